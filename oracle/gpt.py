@@ -1,0 +1,244 @@
+"""Oracle: forward pass, loss and hand-written reverse-mode gradients of the GPT.
+
+TEST INFRASTRUCTURE ONLY (see the package header).
+
+What is computed, following [CT50] "1. Modelo GPT" and "3. Gerenciamento de
+Precisão" (architecture list and the bias-free Linear), with the readings where
+the page is silent:
+
+  x   = wte[tokens]                                   (untied input table)
+  per layer:
+    xn  = rms(x)                                      (pre-norm, no gain)
+    q,k,v = xn Wq^T, xn Wk^T, xn Wv^T, split into 128-wide heads
+    q,k = rope(rms(q)), rope(rms(k))                  (QK-norm per head, then RoPE)
+    o   = causal softmax(q k^T / sqrt(128)) v
+    x   = x + o Wo^T
+    x   = x + relu(rms(x) Wfc^T)^2 Wproj^T            (ReLU^2 MLP)
+  z    = rms(x) Wlm^T                                 (final norm, untied head)
+  loss = mean over valid targets of (logsumexp(z) - z[target])
+
+Readings (the pages do not print these): RMSNorm eps = 1e-6 with statistics
+over the last axis; RoPE pairs element j with j+64, angle t * 10000^(-j/64),
+positions restart at 0 for every row; no biases, no softcap, no dropout;
+targets equal to -1 are ignored in the mean.
+
+The backward pass is derived by hand per operation (no autodiff library), so
+the finite-difference tests in tests/ check it against the forward pass.
+
+Parity pins (tests/test_oracle_model.py): central finite differences in fp64 on
+depth-1 and depth-2 models; loss = ln V and a closed-form lm_head gradient for a
+zero unembedding; causal invariance; attention closed forms (T = 1, q = 0);
+RMSNorm / RoPE invariants; cross-entropy row sums; embedding-gradient support.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+EPS_NORM = 1e-6
+ROPE_BASE = 10000.0
+HEAD_DIM = 128
+
+
+# ----------------------------------------------------------------------------
+# Elementary operations and their adjoints
+# ----------------------------------------------------------------------------
+def rms_norm(x, eps=EPS_NORM):
+    """y = x / sqrt(mean(x^2) + eps) over the last axis; returns (y, rstd)."""
+    rstd = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    return x * rstd, rstd
+
+
+def rms_norm_bwd(dy, y, rstd):
+    """Adjoint of rms_norm: dx = rstd * (dy - y * mean(dy * y))."""
+    return rstd * (dy - y * np.mean(dy * y, axis=-1, keepdims=True))
+
+
+def rope_tables(seq, head_dim=HEAD_DIM, base=ROPE_BASE, dtype=np.float64):
+    """cos/sin of angle t * base^(-j/half) for t < seq, j < head_dim / 2."""
+    half = head_dim // 2
+    theta = base ** (-np.arange(half, dtype=np.float64) / half)
+    phi = np.arange(seq, dtype=np.float64)[:, None] * theta[None, :]
+    return np.cos(phi).astype(dtype), np.sin(phi).astype(dtype)
+
+
+def rope(x, cos, sin):
+    """Rotate pairs (j, j + half) of x [T, H, hd] by the per-position angle."""
+    half = x.shape[-1] // 2
+    x1, x2 = x[..., :half], x[..., half:]
+    c, s = cos[:, None, :], sin[:, None, :]
+    return np.concatenate([x1 * c - x2 * s, x1 * s + x2 * c], axis=-1)
+
+
+def rope_bwd(dy, cos, sin):
+    """Adjoint of rope: rotation by the opposite angle."""
+    half = dy.shape[-1] // 2
+    d1, d2 = dy[..., :half], dy[..., half:]
+    c, s = cos[:, None, :], sin[:, None, :]
+    return np.concatenate([d1 * c + d2 * s, -d1 * s + d2 * c], axis=-1)
+
+
+def causal_attention(q, k, v):
+    """Softmax attention with mask j <= i; q, k, v are [T, H, hd].
+
+    Returns o [T, H, hd] and the probabilities P [H, T, T].
+    """
+    T, _H, hd = q.shape
+    scale = 1.0 / np.sqrt(hd)
+    qh, kh, vh = (a.transpose(1, 0, 2) for a in (q, k, v))  # [H, T, hd]
+    s = np.matmul(qh, kh.transpose(0, 2, 1)) * scale
+    mask = np.tril(np.ones((T, T), dtype=bool))
+    s = np.where(mask[None], s, -np.inf)
+    s = s - s.max(axis=-1, keepdims=True)
+    e = np.exp(s)
+    p = e / e.sum(axis=-1, keepdims=True)
+    o = np.matmul(p, vh).transpose(1, 0, 2)
+    return o, p
+
+
+def causal_attention_bwd(do, q, k, v, p):
+    """Adjoint of causal_attention given the saved probabilities p."""
+    hd = q.shape[-1]
+    scale = 1.0 / np.sqrt(hd)
+    qh, kh, vh, doh = (a.transpose(1, 0, 2) for a in (q, k, v, do))
+    dp = np.matmul(doh, vh.transpose(0, 2, 1))
+    dv = np.matmul(p.transpose(0, 2, 1), doh)
+    ds = p * (dp - np.sum(dp * p, axis=-1, keepdims=True))
+    dq = np.matmul(ds, kh) * scale
+    dk = np.matmul(ds.transpose(0, 2, 1), qh) * scale
+    return dq.transpose(1, 0, 2), dk.transpose(1, 0, 2), dv.transpose(1, 0, 2)
+
+
+def log_softmax_rows(z):
+    """Row-wise logsumexp of z [T, V]."""
+    m = z.max(axis=-1, keepdims=True)
+    return (m + np.log(np.sum(np.exp(z - m), axis=-1, keepdims=True)))[:, 0]
+
+
+# ----------------------------------------------------------------------------
+# Model
+# ----------------------------------------------------------------------------
+def _depth(weights):
+    n = 0
+    while f"h{n}.wq" in weights:
+        n += 1
+    return n
+
+
+def _forward_sequence(weights, tok, cos, sin, final_norm=True):
+    """Forward pass of one sequence; returns the logits and the saved values."""
+    L = _depth(weights)
+    wte = weights["wte"]
+    d = wte.shape[1]
+    H = d // HEAD_DIM
+    T = tok.shape[0]
+    x = wte[tok]
+    layers = []
+    for layer in range(L):
+        w = {n: weights[f"h{layer}.{n}"] for n in ("wq", "wk", "wv", "wo", "wfc", "wproj")}
+        xn1, r1 = rms_norm(x)
+        q = (xn1 @ w["wq"].T).reshape(T, H, HEAD_DIM)
+        k = (xn1 @ w["wk"].T).reshape(T, H, HEAD_DIM)
+        v = (xn1 @ w["wv"].T).reshape(T, H, HEAD_DIM)
+        qn, rq = rms_norm(q)
+        kn, rk = rms_norm(k)
+        qr, kr = rope(qn, cos, sin), rope(kn, cos, sin)
+        o, p = causal_attention(qr, kr, v)
+        o2 = o.reshape(T, d)
+        x_mid = x + o2 @ w["wo"].T
+        xn2, r2 = rms_norm(x_mid)
+        u = xn2 @ w["wfc"].T
+        a = np.maximum(u, 0.0) ** 2
+        x = x_mid + a @ w["wproj"].T
+        layers.append(dict(xn1=xn1, r1=r1, qn=qn, rq=rq, kn=kn, rk=rk, qr=qr, kr=kr,
+                           v=v, p=p, o2=o2, xn2=xn2, r2=r2, u=u, a=a))
+    if final_norm:
+        xnf, rf = rms_norm(x)
+    else:
+        xnf, rf = x, None
+    z = xnf @ weights["lm_head"].T
+    return z, dict(layers=layers, xnf=xnf, rf=rf)
+
+
+def forward_logits(weights, tokens, final_norm=True):
+    """Logits [B, T, V] for int tokens [B, T] (no loss, no gradients)."""
+    tokens = np.asarray(tokens)
+    T = tokens.shape[1]
+    dt = weights["wte"].dtype
+    cos, sin = rope_tables(T, dtype=dt)
+    return np.stack([_forward_sequence(weights, tokens[b], cos, sin, final_norm)[0]
+                     for b in range(tokens.shape[0])])
+
+
+def per_position_loss(weights, tokens, targets, final_norm=True):
+    """lse(z) - z[target] at every position (0 where the target is ignored)."""
+    z = forward_logits(weights, tokens, final_norm)
+    out = np.zeros(targets.shape, dtype=z.dtype)
+    for b in range(z.shape[0]):
+        lse = log_softmax_rows(z[b])
+        valid = targets[b] >= 0
+        t = np.where(valid, targets[b], 0)
+        out[b] = np.where(valid, lse - z[b][np.arange(z.shape[1]), t], 0.0)
+    return out
+
+
+def forward_backward(weights, tokens, targets, final_norm=True, want_grads=True):
+    """Mean cross-entropy loss and the gradient of every tensor.
+
+    Sequences are independent, so the batch is processed one row at a time and
+    the per-row contributions are summed (this bounds memory; it is exact).
+    Returns (loss, grads) with grads a dict shaped like ``weights``.
+    """
+    tokens = np.asarray(tokens)
+    targets = np.asarray(targets)
+    B, T = tokens.shape
+    dt = weights["wte"].dtype
+    cos, sin = rope_tables(T, dtype=dt)
+    n_valid = int(np.count_nonzero(targets >= 0))
+    grads = {k: np.zeros_like(v) for k, v in weights.items()} if want_grads else None
+    loss_sum = 0.0
+    L = _depth(weights)
+    d = weights["wte"].shape[1]
+    H = d // HEAD_DIM
+    for b in range(B):
+        tok, tgt = tokens[b], targets[b]
+        z, c = _forward_sequence(weights, tok, cos, sin, final_norm)
+        lse = log_softmax_rows(z)
+        valid = tgt >= 0
+        t = np.where(valid, tgt, 0)
+        rows = np.arange(T)
+        loss_sum += float(np.sum(np.where(valid, lse - z[rows, t], 0.0)))
+        if not want_grads or n_valid == 0:
+            continue
+        # Cross-entropy: d loss / d z = (softmax(z) - onehot(target)) / n_valid.
+        dz = np.exp(z - lse[:, None])
+        dz[rows, t] -= 1.0
+        dz *= (valid.astype(dt) / n_valid)[:, None]
+        grads["lm_head"] += dz.T @ c["xnf"]
+        dx = dz @ weights["lm_head"]
+        if final_norm:
+            dx = rms_norm_bwd(dx, c["xnf"], c["rf"])
+        for layer in reversed(range(L)):
+            s = c["layers"][layer]
+            w = {n: weights[f"h{layer}.{n}"] for n in ("wq", "wk", "wv", "wo", "wfc", "wproj")}
+            g = {n: f"h{layer}.{n}" for n in w}
+            # x_out = x_mid + relu(u)^2 Wproj^T
+            grads[g["wproj"]] += dx.T @ s["a"]
+            da = dx @ w["wproj"]
+            du = da * 2.0 * np.maximum(s["u"], 0.0)
+            grads[g["wfc"]] += du.T @ s["xn2"]
+            dx_mid = dx + rms_norm_bwd(du @ w["wfc"], s["xn2"], s["r2"])
+            # x_mid = x_in + o Wo^T
+            grads[g["wo"]] += dx_mid.T @ s["o2"]
+            do = (dx_mid @ w["wo"]).reshape(T, H, HEAD_DIM)
+            dqr, dkr, dv = causal_attention_bwd(do, s["qr"], s["kr"], s["v"], s["p"])
+            dq = rms_norm_bwd(rope_bwd(dqr, cos, sin), s["qn"], s["rq"]).reshape(T, d)
+            dk = rms_norm_bwd(rope_bwd(dkr, cos, sin), s["kn"], s["rk"]).reshape(T, d)
+            dv = dv.reshape(T, d)
+            grads[g["wq"]] += dq.T @ s["xn1"]
+            grads[g["wk"]] += dk.T @ s["xn1"]
+            grads[g["wv"]] += dv.T @ s["xn1"]
+            dxn1 = dq @ w["wq"] + dk @ w["wk"] + dv @ w["wv"]
+            dx = dx_mid + rms_norm_bwd(dxn1, s["xn1"], s["r1"])
+        np.add.at(grads["wte"], tok, dx)
+    loss = loss_sum / n_valid if n_valid else 0.0
+    return loss, grads

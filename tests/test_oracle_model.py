@@ -1,0 +1,272 @@
+"""Pins of the oracle's model (forward, loss, backward) against facts other than itself.
+
+Every check here uses something the oracle does not: finite differences of its
+own forward pass, closed forms, brute-force loops on tiny inputs, or
+invariants that the mathematics fixes.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import gpt as og
+from gpt_pretraining_step_bf16_amd import synthetic as syn
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def _tiny_weights(depth, vocab, seed, std):
+    w = syn.init_weights(depth, vocab, seed=seed, std=std)
+    return {k: v.astype(np.float64) for k, v in w.items()}
+
+
+def _ids(batch, seq, vocab, seed):
+    return syn.split_tokens(syn.zipf_ids(batch, seq, vocab, seed=seed))
+
+
+# ----------------------------------------------------------------------------
+# Whole-model gradient: central finite differences in fp64
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("depth", [1, 2])
+def test_gradients_match_central_differences(depth):
+    vocab, seq, batch = 96, 12, 2
+    w = _tiny_weights(depth, vocab, seed=3, std=0.15)
+    tok, tgt = _ids(batch, seq, vocab, seed=5)
+    tgt = tgt.copy()
+    tgt[0, 3] = -1  # one ignored target exercises the valid-count normalisation
+    loss, grads = oracle.forward_backward(w, tok, tgt)
+    assert np.isfinite(loss)
+    rng = np.random.default_rng(11)
+    h = 1e-4
+
+    def f(ww):
+        return oracle.forward_backward(ww, tok, tgt, want_grads=False)[0]
+
+    for name in w:
+        # Directional derivative along a random direction.
+        u = rng.standard_normal(w[name].shape)
+        u /= np.linalg.norm(u)
+        wp = dict(w); wp[name] = w[name] + h * u
+        wm = dict(w); wm[name] = w[name] - h * u
+        fd = (f(wp) - f(wm)) / (2 * h)
+        an = float(np.sum(grads[name] * u))
+        assert abs(fd - an) <= 1e-6 * abs(an) + 1e-9, (name, fd, an)
+        # A few single coordinates, taken where the gradient is largest.
+        flat = np.argsort(np.abs(grads[name]).ravel())[-3:]
+        for idx in flat:
+            pos = np.unravel_index(idx, w[name].shape)
+            hc = 1e-5
+            wp = dict(w); wp[name] = w[name].copy(); wp[name][pos] += hc
+            wm = dict(w); wm[name] = w[name].copy(); wm[name][pos] -= hc
+            fd = (f(wp) - f(wm)) / (2 * hc)
+            an = grads[name][pos]
+            assert abs(fd - an) <= 1e-6 * max(1e-3, abs(an)) + 1e-10, (name, pos, fd, an)
+
+
+# ----------------------------------------------------------------------------
+# Zero unembedding: loss = ln V exactly, closed-form lm_head gradient
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("vocab,expected", [(2048, 7.6246189861593985), (32768, 10.397207708399179)])
+def test_zero_unembedding_gives_log_vocab(vocab, expected):
+    assert math.log(vocab) == pytest.approx(expected, abs=1e-12)
+    depth, seq, batch = 1, 8, 2
+    w = _tiny_weights(depth, vocab, seed=1, std=0.1)
+    w["lm_head"][:] = 0.0
+    # With the output projections zeroed every block is the identity on the
+    # residual, so the final normalised state is rms(wte[tokens]), computed
+    # here without the oracle.
+    w["h0.wo"][:] = 0.0
+    w["h0.wproj"][:] = 0.0
+    tok, tgt = _ids(batch, seq, vocab, seed=2)
+    loss, grads = oracle.forward_backward(w, tok, tgt)
+    assert loss == pytest.approx(expected, abs=1e-12)
+    for name, g in grads.items():
+        if name != "lm_head":
+            assert not np.any(g), name
+    x = w["wte"][tok.ravel()]
+    xnf = x / np.sqrt((x * x).mean(axis=1, keepdims=True) + 1e-6)
+    onehot = np.zeros((tok.size, vocab))
+    onehot[np.arange(tok.size), tgt.ravel()] = 1.0
+    expect = (1.0 / vocab - onehot).T @ xnf / tok.size
+    np.testing.assert_allclose(grads["lm_head"], expect, rtol=1e-12, atol=1e-15)
+
+
+def test_initial_loss_band():
+    depth, vocab, seq, batch = 2, 2048, 16, 2
+    w = _tiny_weights(depth, vocab, seed=0, std=0.02)
+    tok, tgt = _ids(batch, seq, vocab, seed=1)
+    loss, _ = oracle.forward_backward(w, tok, tgt, want_grads=False)
+    # Logits are ~N(0, 0.02^2 d) at this init, so loss ~ ln V + 0.02^2 d / 2.
+    d = w["wte"].shape[1]
+    assert abs(loss - (math.log(vocab) + 0.5 * 0.02 ** 2 * d)) < 0.05
+
+
+# ----------------------------------------------------------------------------
+# Causal invariance
+# ----------------------------------------------------------------------------
+def test_future_tokens_do_not_change_past_logits():
+    depth, vocab, seq = 2, 128, 16
+    w = _tiny_weights(depth, vocab, seed=4, std=0.1)
+    tok, _ = _ids(1, seq, vocab, seed=6)
+    t_cut = 9
+    tok2 = tok.copy()
+    tok2[0, t_cut + 1:] = (tok2[0, t_cut + 1:] + 17) % vocab
+    z1 = oracle.forward_logits(w, tok)
+    z2 = oracle.forward_logits(w, tok2)
+    np.testing.assert_allclose(z1[0, : t_cut + 1], z2[0, : t_cut + 1], rtol=0, atol=1e-13)
+    assert np.abs(z1[0, t_cut + 1:] - z2[0, t_cut + 1:]).max() > 1e-6
+
+
+# ----------------------------------------------------------------------------
+# Attention special cases and brute force
+# ----------------------------------------------------------------------------
+def test_attention_single_position_returns_v():
+    rng = np.random.default_rng(0)
+    q, k, v = (rng.standard_normal((1, 2, 128)) for _ in range(3))
+    o, _ = oracle.causal_attention(q, k, v)
+    np.testing.assert_allclose(o, v, rtol=0, atol=1e-15)
+
+
+def test_attention_zero_query_is_prefix_mean():
+    rng = np.random.default_rng(1)
+    T = 7
+    q = np.zeros((T, 1, 128))
+    k, v = (rng.standard_normal((T, 1, 128)) for _ in range(2))
+    o, _ = oracle.causal_attention(q, k, v)
+    expect = np.cumsum(v, axis=0) / np.arange(1, T + 1)[:, None, None]
+    np.testing.assert_allclose(o, expect, rtol=1e-13, atol=1e-14)
+
+
+def test_attention_matches_scalar_loops():
+    rng = np.random.default_rng(2)
+    T, H, hd = 5, 2, 128
+    q, k, v = (rng.standard_normal((T, H, hd)) for _ in range(3))
+    o, _ = oracle.causal_attention(q, k, v)
+    for h in range(H):
+        for i in range(T):
+            scores = [sum(q[i, h, e] * k[j, h, e] for e in range(hd)) / math.sqrt(hd) for j in range(i + 1)]
+            m = max(scores)
+            ex = [math.exp(s - m) for s in scores]
+            tot = sum(ex)
+            for e in range(0, hd, 17):
+                val = sum(ex[j] / tot * v[j, h, e] for j in range(i + 1))
+                assert abs(val - o[i, h, e]) < 1e-12
+
+
+def test_attention_backward_matches_finite_differences():
+    rng = np.random.default_rng(3)
+    T, H, hd = 6, 2, 128
+    q, k, v = (rng.standard_normal((T, H, hd)) * 0.3 for _ in range(3))
+    w = rng.standard_normal((T, H, hd))
+    o, p = oracle.causal_attention(q, k, v)
+    dq, dk, dv = oracle.causal_attention_bwd(w, q, k, v, p)
+    h = 1e-6
+    for arr, grad in ((q, dq), (k, dk), (v, dv)):
+        u = rng.standard_normal(arr.shape)
+        arr += h * u
+        fp = np.sum(w * oracle.causal_attention(q, k, v)[0])
+        arr -= 2 * h * u
+        fm = np.sum(w * oracle.causal_attention(q, k, v)[0])
+        arr += h * u
+        assert abs((fp - fm) / (2 * h) - np.sum(grad * u)) < 1e-7
+
+
+# ----------------------------------------------------------------------------
+# RMSNorm and RoPE invariants
+# ----------------------------------------------------------------------------
+def test_rms_norm_output_rms_and_scale_invariance():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((9, 256)) * 3.0
+    y, _ = oracle.rms_norm(x)
+    ms = (x * x).mean(axis=1)
+    np.testing.assert_allclose((y * y).mean(axis=1), ms / (ms + 1e-6), rtol=1e-13)
+    y2, _ = oracle.rms_norm(x * 1000.0, eps=0.0)
+    y3, _ = oracle.rms_norm(x, eps=0.0)
+    np.testing.assert_allclose(y2, y3, rtol=1e-13)
+
+
+def test_rope_is_a_rotation():
+    rng = np.random.default_rng(5)
+    T = 33
+    cos, sin = oracle.rope_tables(T)
+    x = rng.standard_normal((T, 3, 128))
+    y = oracle.rope(x, cos, sin)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+    np.testing.assert_allclose(y[0], x[0], rtol=0, atol=0)  # position 0 is the identity
+    np.testing.assert_allclose(oracle.rope_bwd(y, cos, sin), x, rtol=1e-12, atol=1e-13)
+    # The angle of pair j at position t is t * 10000^(-j/64).
+    e = np.zeros((T, 1, 128)); e[:, 0, 5] = 1.0
+    ye = oracle.rope(e, cos, sin)
+    ang = np.arange(T) * 10000.0 ** (-5 / 64)
+    np.testing.assert_allclose(ye[:, 0, 5], np.cos(ang), atol=1e-13)
+    np.testing.assert_allclose(ye[:, 0, 69], np.sin(ang), atol=1e-13)
+
+
+def test_rope_scores_depend_only_on_offset():
+    rng = np.random.default_rng(6)
+    T = 40
+    cos, sin = oracle.rope_tables(T)
+    q0, k0 = rng.standard_normal(128), rng.standard_normal(128)
+    q = np.broadcast_to(q0, (T, 1, 128)).copy()
+    k = np.broadcast_to(k0, (T, 1, 128)).copy()
+    qr, kr = oracle.rope(q, cos, sin)[:, 0], oracle.rope(k, cos, sin)[:, 0]
+    for off in (0, 3, 11):
+        s = [qr[i] @ kr[i - off] for i in range(off, T)]
+        np.testing.assert_allclose(s, s[0], rtol=1e-11, atol=1e-11)
+
+
+def test_qk_norm_commutes_with_rope():
+    rng = np.random.default_rng(7)
+    T = 10
+    cos, sin = oracle.rope_tables(T)
+    x = rng.standard_normal((T, 2, 128))
+    a = oracle.rope(oracle.rms_norm(x)[0], cos, sin)
+    b = oracle.rms_norm(oracle.rope(x, cos, sin))[0]
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------
+# Cross-entropy and embedding gradient structure
+# ----------------------------------------------------------------------------
+def test_lm_head_gradient_columns_sum_to_zero_and_embedding_support():
+    depth, vocab, seq, batch = 1, 300, 10, 3
+    w = _tiny_weights(depth, vocab, seed=8, std=0.1)
+    tok, tgt = _ids(batch, seq, vocab, seed=9)
+    _, g = oracle.forward_backward(w, tok, tgt)
+    np.testing.assert_allclose(g["lm_head"].sum(axis=0), 0.0, atol=1e-15)
+    absent = np.setdiff1d(np.arange(vocab), tok.ravel())
+    assert absent.size > 0
+    assert not np.any(g["wte"][absent])
+    present = np.unique(tok)
+    assert np.all(np.abs(g["wte"][present]).sum(axis=1) > 0)
+
+
+# ----------------------------------------------------------------------------
+# Synthetic inputs
+# ----------------------------------------------------------------------------
+def test_zipf_ids_range_and_head_frequency():
+    from scipy.special import zeta
+
+    for vocab in (2048, 32768):
+        ids = syn.zipf_ids(50, 4000, vocab, seed=1)
+        assert ids.dtype == np.int32 and ids.min() >= 0 and ids.max() < vocab
+        # p(id 0) = 1 / sum_{k<=V} k^-1.1, with the partial sum from Hurwitz zeta.
+        p0 = 1.0 / (zeta(1.1) - zeta(1.1, vocab + 1))
+        f0 = np.mean(ids == 0)
+        assert abs(f0 - p0) < 4 * math.sqrt(p0 * (1 - p0) / ids.size) + 1e-4
+    assert abs(1.0 / (zeta(1.1) - zeta(1.1, 32769)) - 0.14187) < 5e-5
+
+
+def test_targets_are_inputs_shifted_by_one():
+    ids = syn.zipf_ids(3, 20, 500, seed=4)
+    tok, tgt = syn.split_tokens(ids)
+    np.testing.assert_array_equal(tok[:, 1:], tgt[:, :-1])
+    assert tok.shape == (3, 20) and tgt.shape == (3, 20)
+
+
+def test_depth_rule_matches_configs():
+    for name, width in (("d12", 768), ("d20", 1280), ("d26", 1664), ("d32", 2048)):
+        dm = syn.model_dims(syn.CONFIGS[name]["depth"])
+        assert dm["d"] == width and dm["heads"] * 128 == width and dm["mlp"] == 4 * width
+    assert syn.model_dims(1)["d"] == 128 and syn.model_dims(3)["d"] == 256
