@@ -1,0 +1,193 @@
+#!/usr/bin/env python3
+"""Training-step throughput of the depth-parameterised GPT on one MI355X.
+
+One step = gpt_fwd_bwd (embedding, blocks, head + cross-entropy, full
+backward) + muon_step (momentum, Newton-Schulz, update of every block matrix)
+on one microbatch of seeded synthetic tokens, with inputs and weights resident
+in HBM before the timed region. Prints one JSON line:
+
+  value        training tokens/s (B*T*steps / wall time of the timed steps)
+  mfu          value * F_tok / MI355X dense-bf16 peak, with
+               F_tok = 6 (12 L d^2 + V d) + 6 L d T (causal attention once)
+  roofline     the GEMM kernel family (the dominant kernel): algorithmic FLOPs
+               of its launches / their summed durations, from HIP events
+               recorded around each launch on its stream during the timed steps
+  cpu_baseline the CPU oracle on a bounded sample of the same workload
+
+Metric definitions follow the page's train/mfu and train/tok_per_sec
+("Como treinar seu próprio ChatGPT por 50 dólares", section "Métricas para
+Monitorar"); the page prints no value for them.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+from gpt_pretraining_step_bf16_amd import synthetic as syn
+
+PEAK_BF16_FLOPS = 2.5166e15  # MI355X dense bf16 MFMA
+METRIC = "training tokens/sec + MFU, d20 GPT fwd+bwd+Muon step on 1 MI355X"
+
+
+def flops_per_token(L, d, V, T):
+    return 6.0 * (12.0 * L * d * d + V * d) + 6.0 * L * d * T
+
+
+def ns_flops(L, d, steps=5):
+    # Per iteration per layer: four d x d matrices (6 d^3 each) and two 4d x d (18 d^3 each).
+    return steps * L * (4 * 6.0 + 2 * 18.0) * d ** 3
+
+
+def cpu_baseline(cfg, weights, tok, tgt):
+    """Time the oracle on a bounded sample and scale it to one full step."""
+    import oracle  # test infrastructure: used here only for the CPU baseline leg
+
+    cores = len(os.sched_getaffinity(0))
+    L, B, T = cfg["depth"], cfg["batch"], cfg["seq"]
+    t0 = time.perf_counter()
+    oracle.forward_backward(weights, tok[:1], tgt[:1])
+    t_seq = time.perf_counter() - t0
+    names = [f"h0.{n}" for n in ("wq", "wk", "wv", "wo", "wfc", "wproj")]
+    sub_w = {k: weights[k] for k in names}
+    rng = np.random.default_rng(9)
+    sub_g = {k: (rng.standard_normal(sub_w[k].shape, dtype=np.float32) * 1e-3) for k in names}
+    sub_m = {k: np.zeros_like(v) for k, v in sub_w.items()}
+    t0 = time.perf_counter()
+    oracle.muon_step(sub_w, sub_g, sub_m, syn.MUON_LR, syn.MUON_MOMENTUM, syn.NS_COEFFS)
+    t_muon_layer = time.perf_counter() - t0
+    t_step = B * t_seq + L * t_muon_layer
+    return {
+        "value": round(B * T / t_step, 3),
+        "unit": "tokens/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"fp32 NumPy oracle: fwd+bwd of 1 of {B} sequences ({T} tokens, {t_seq:.2f} s) and "
+                   f"Muon of 1 of {L} layers ({t_muon_layer:.2f} s), scaled to the full step "
+                   f"(sequences and layers are independent units of equal cost)"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="d20", choices=sorted(syn.CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the single-GPU step only: this build has no multi-GPU path "
+              "(see DESIGN.md for how the step would shard). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from gpt_pretraining_step_bf16_amd.step import TrainState
+
+    cfg = syn.CONFIGS[args.config]
+    L, V, T, B = cfg["depth"], cfg["vocab"], cfg["seq"], cfg["batch"]
+    dims = syn.model_dims(L)
+    d = dims["d"]
+    print(f"[bench] config {args.config}: depth {L} width {d} vocab {V} seq {T} batch {B}",
+          file=sys.stderr, flush=True)
+    weights = syn.init_weights(L, V, seed=0)
+    tok, tgt = syn.split_tokens(syn.zipf_ids(B, T, V, seed=1))
+    st = TrainState(L, V, T, B)
+    st.load_weights(weights)
+    tok_d = torch.from_numpy(tok).cuda()
+    tgt_d = torch.from_numpy(tgt).cuda()
+
+    def step():
+        st.fwd_bwd(tok_d, tgt_d)
+        st.muon(syn.MUON_LR, syn.MUON_MOMENTUM, syn.NS_COEFFS)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        print(f"[bench] warmup step {i} loss {float(st.loss.item()):.5f}", file=sys.stderr, flush=True)
+    if st.check() != 0:
+        raise RuntimeError("device reported an out-of-range token")
+
+    st.model.profile_enable(True)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record()
+    for _ in range(args.steps):
+        step()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    elapsed_ms = t_start.elapsed_time(t_end)
+    prof = {name: st.model.profile_read(cat) for name, cat in
+            (("gemm", 0), ("attn_fwd", 1), ("attn_bwd", 2), ("ns_gemm", 3))}
+    st.model.profile_enable(False)
+    loss = float(st.loss.item())
+    if not np.isfinite(loss):
+        raise RuntimeError(f"non-finite loss {loss}")
+
+    ms_step = elapsed_ms / args.steps
+    tokens_per_s = B * T * args.steps / (elapsed_ms / 1e3)
+    f_tok = flops_per_token(L, d, V, T)
+    mfu = tokens_per_s * f_tok / PEAK_BF16_FLOPS
+    mfma_work = (tokens_per_s * f_tok + ns_flops(L, d) / (ms_step / 1e3)) / PEAK_BF16_FLOPS
+    for name, (ms, fl, n) in prof.items():
+        tf = fl / (ms / 1e3) / 1e12 if ms > 0 else 0.0
+        print(f"[bench] {name:9s} {ms / args.steps:9.2f} ms/step  {n // max(args.steps, 1):5d} launches/step"
+              f"  {tf:8.1f} TFLOP/s", file=sys.stderr, flush=True)
+    g_ms, g_fl, g_n = prof["gemm"]
+    achieved = g_fl / (g_ms / 1e3) / 1e12 if g_ms > 0 else 0.0
+    roofline = {
+        "kernel": "gemm_bf16_kernel (projection, head and weight-gradient GEMMs of fwd+bwd)",
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": PEAK_BF16_FLOPS / 1e12,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / (PEAK_BF16_FLOPS / 1e12), 4),
+        "traffic": None,
+        "launches_per_step": g_n // max(args.steps, 1),
+        "ms_per_step": round(g_ms / args.steps, 3),
+    }
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Zipf(1.1) token ids, N(0, 0.02) weights)",
+        "config": {
+            "workload": f"{args.config}: depth {L}, width {d}, {dims['heads']} heads x 128, MLP {4 * d}, "
+                        f"vocab {V}, seq {T}, microbatch {B}; fwd+bwd+Muon (5 Newton-Schulz steps)",
+            "global_batch": B,
+            "seq_len": T,
+            "parallelism": "none (1 GPU)",
+        },
+        "mfu": round(mfu, 4),
+        "mfma_work_utilisation": round(mfma_work, 4),
+        "loss": round(loss, 5),
+        "wall_s_timed": round(wall, 3),
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cfg, weights, tok, tgt)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,236 @@
+"""ctypes binding of the C ABI in include/gpt.h (argument marshalling only).
+
+Every compute call runs in the HIP library libgptstep.so; torch tensors only
+supply device pointers and the current stream. If the library has not been
+built, ``lib()`` raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgptstep.so")
+
+GPT_OK, GPT_EINVAL, GPT_ESHAPE, GPT_EHIP, GPT_ETOKEN, GPT_EWORKSPACE = 0, -1, -2, -3, -4, -5
+KIND_NAMES = {0: "emb", 1: "matrix", 2: "lm_head"}
+
+# gpt_op_gemm out_mode values
+OUT_F32, OUT_F32_ACC, OUT_BF16, OUT_RELU_BF16, OUT_RESID_BF16 = 0, 1, 2, 3, 4
+
+
+class GptTensor(C.Structure):
+    _fields_ = [
+        ("name", C.c_char * 32),
+        ("offset", C.c_int64),
+        ("rows", C.c_int32),
+        ("cols", C.c_int32),
+        ("kind", C.c_int32),
+        ("layer", C.c_int32),
+    ]
+
+
+class GptError(RuntimeError):
+    def __init__(self, status, what=""):
+        self.status = status
+        super().__init__(f"{what}: {status_str(status)} ({status})")
+
+
+_lib = None
+_P = C.c_void_p
+_I = C.c_int32
+_L = C.c_int64
+_S = C.c_size_t
+_F = C.c_float
+
+
+def _sig(lib, name, res, args):
+    f = getattr(lib, name)
+    f.restype = res
+    f.argtypes = args
+
+
+EXPORTS = {
+    "gpt_create": (C.c_int, [_I, _I, _I, C.POINTER(_P)]),
+    "gpt_destroy": (None, [_P]),
+    "gpt_dims": (C.c_int, [_P, C.POINTER(C.c_int32)]),
+    "gpt_num_params": (C.c_int64, [_P]),
+    "gpt_num_tensors": (C.c_int32, [_P]),
+    "gpt_tensor_info": (C.c_int, [_P, _I, C.POINTER(GptTensor)]),
+    "gpt_workspace_bytes": (C.c_size_t, [_P, _I, _I]),
+    "gpt_fwd_bwd": (C.c_int, [_P, _P, _P, _P, _I, _I, _P, _P, _I, _P, _S, _P]),
+    "muon_workspace_bytes": (C.c_size_t, [_P]),
+    "muon_step": (C.c_int, [_P, _P, _P, _P, _P, _F, _F, C.POINTER(C.c_float), _I, _P, _S, _P]),
+    "gpt_refresh_bf16": (C.c_int, [_P, _P, _P, _P]),
+    "gpt_check": (C.c_int, [_P, _P, _P]),
+    "gpt_status_str": (C.c_char_p, [C.c_int]),
+    "gpt_op_gemm": (C.c_int, [_I, _I, _I, _I, _P, _L, _L, _I, _P, _L, _L, _I, _P, _L, _L, _I, _P]),
+    "gpt_op_attention_fwd": (C.c_int, [_P, _P, _P, _I, _I, _I, _P]),
+    "gpt_op_attention_bwd": (C.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
+    "gpt_op_ns_scratch_bytes": (C.c_size_t, [_I, _I, _I]),
+    "gpt_op_newton_schulz": (C.c_int, [_P, _I, _I, _I, C.POINTER(C.c_float), _I, _P, _S, _P]),
+    "gpt_profile_enable": (C.c_int, [_P, _I]),
+    "gpt_profile_reset": (C.c_int, [_P]),
+    "gpt_profile_read": (C.c_int, [_P, _I, C.POINTER(C.c_double), C.POINTER(C.c_double),
+                                   C.POINTER(C.c_int64)]),
+}
+
+PROF_GEMM, PROF_ATTN_FWD, PROF_ATTN_BWD, PROF_NS = 0, 1, 2, 3
+
+
+def lib():
+    """Load libgptstep.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m gpt_pretraining_step_bf16_amd.build`"
+            )
+        handle = C.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            _sig(handle, name, res, args)
+        _lib = handle
+    return _lib
+
+
+def status_str(status) -> str:
+    return lib().gpt_status_str(int(status)).decode()
+
+
+def _check(status, what):
+    if status != GPT_OK:
+        raise GptError(status, what)
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is not None:
+        return C.c_void_p(stream)
+    import torch
+
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _coeffs(table):
+    arr = np.ascontiguousarray(np.asarray(table, dtype=np.float32).reshape(-1, 3))
+    buf = (C.c_float * arr.size)(*arr.ravel().tolist())
+    return buf, arr.shape[0]
+
+
+class GptModel:
+    """Host-side plan of a model (no device memory)."""
+
+    def __init__(self, depth: int, vocab: int, max_seq: int):
+        h = C.c_void_p()
+        _check(lib().gpt_create(depth, vocab, max_seq, C.byref(h)), "gpt_create")
+        self._h = h
+        dims = (C.c_int32 * 6)()
+        _check(lib().gpt_dims(h, dims), "gpt_dims")
+        self.depth, self.d, self.heads, self.mlp, self.vocab, self.max_seq = list(dims)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().gpt_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def handle(self):
+        return self._h
+
+    @property
+    def num_params(self) -> int:
+        return int(lib().gpt_num_params(self._h))
+
+    def tensors(self):
+        out = []
+        for i in range(lib().gpt_num_tensors(self._h)):
+            t = GptTensor()
+            _check(lib().gpt_tensor_info(self._h, i, C.byref(t)), "gpt_tensor_info")
+            out.append(dict(name=t.name.decode(), offset=int(t.offset), rows=int(t.rows),
+                            cols=int(t.cols), kind=KIND_NAMES[int(t.kind)], layer=int(t.layer)))
+        return out
+
+    def workspace_bytes(self, batch: int, seq: int) -> int:
+        return int(lib().gpt_workspace_bytes(self._h, batch, seq))
+
+    def muon_workspace_bytes(self) -> int:
+        return int(lib().muon_workspace_bytes(self._h))
+
+    # -- compute (torch device tensors) -------------------------------------
+    def fwd_bwd(self, params_bf16, tokens, targets, loss, grads, workspace, accumulate=False,
+                stream=None):
+        batch, seq = tokens.shape
+        st = lib().gpt_fwd_bwd(self._h, _ptr(params_bf16), _ptr(tokens), _ptr(targets), batch, seq,
+                               _ptr(loss), _ptr(grads), 1 if accumulate else 0, _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream))
+        _check(st, "gpt_fwd_bwd")
+
+    def muon_step(self, params, params_bf16, grads, momentum, lr, momentum_coef, ns_coeffs,
+                  workspace, stream=None):
+        buf, steps = _coeffs(ns_coeffs)
+        st = lib().muon_step(self._h, _ptr(params), _ptr(params_bf16), _ptr(grads), _ptr(momentum),
+                             float(lr), float(momentum_coef), buf, steps, _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(stream))
+        _check(st, "muon_step")
+
+    def refresh_bf16(self, params, params_bf16, stream=None):
+        _check(lib().gpt_refresh_bf16(self._h, _ptr(params), _ptr(params_bf16), _stream(stream)),
+               "gpt_refresh_bf16")
+
+    def check(self, workspace, stream=None) -> int:
+        return int(lib().gpt_check(self._h, _ptr(workspace), _stream(stream)))
+
+    # -- launch timing ----------------------------------------------------------
+    def profile_enable(self, on: bool = True):
+        _check(lib().gpt_profile_enable(self._h, 1 if on else 0), "gpt_profile_enable")
+
+    def profile_reset(self):
+        _check(lib().gpt_profile_reset(self._h), "gpt_profile_reset")
+
+    def profile_read(self, category: int):
+        ms, fl, n = C.c_double(), C.c_double(), C.c_int64()
+        _check(lib().gpt_profile_read(self._h, category, C.byref(ms), C.byref(fl), C.byref(n)),
+               "gpt_profile_read")
+        return ms.value, fl.value, n.value
+
+
+# -- step-level entry points ---------------------------------------------------
+def op_gemm(M, N, K, A, lda, a_kmajor, B, ldb, b_kmajor, Cout, ldc, out_mode, batch=1, stride_a=0,
+            stride_b=0, stride_c=0, stream=None):
+    st = lib().gpt_op_gemm(M, N, K, batch, _ptr(A), lda, stride_a, int(a_kmajor), _ptr(B), ldb,
+                           stride_b, int(b_kmajor), _ptr(Cout), ldc, stride_c, out_mode,
+                           _stream(stream))
+    _check(st, "gpt_op_gemm")
+
+
+def op_attention_fwd(qkv, o, lse, batch, seq, heads, stream=None):
+    _check(lib().gpt_op_attention_fwd(_ptr(qkv), _ptr(o), _ptr(lse), batch, seq, heads,
+                                      _stream(stream)), "gpt_op_attention_fwd")
+
+
+def op_attention_bwd(qkv, o, lse, dO, dqkv, scratch, batch, seq, heads, stream=None):
+    _check(lib().gpt_op_attention_bwd(_ptr(qkv), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dqkv),
+                                      _ptr(scratch), batch, seq, heads, _stream(stream)),
+           "gpt_op_attention_bwd")
+
+
+def ns_scratch_bytes(count, rows, cols) -> int:
+    return int(lib().gpt_op_ns_scratch_bytes(count, rows, cols))
+
+
+def op_newton_schulz(X, count, rows, cols, ns_coeffs, scratch, stream=None):
+    buf, steps = _coeffs(ns_coeffs)
+    st = lib().gpt_op_newton_schulz(_ptr(X), count, rows, cols, buf, steps, _ptr(scratch),
+                                    scratch.numel() * scratch.element_size(), _stream(stream))
+    _check(st, "gpt_op_newton_schulz")

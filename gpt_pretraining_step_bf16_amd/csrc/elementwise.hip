@@ -1,0 +1,598 @@
+// Memory-bound kernels of the step on gfx950: embedding gather/scatter,
+// parameter-free RMSNorm forward/backward, QK-norm + RoPE forward/backward,
+// the softmax cross-entropy row pass, and the Muon elementwise passes.
+//
+// Sources (cited by page title and section):
+//   [CT50] dev.to, "Como treinar seu próprio ChatGPT por 50 dólares".
+//
+// All row kernels use one wave64 per row and 16-byte accesses; statistics and
+// reductions are fp32 and reduced with wave shuffles in a fixed order, so
+// results are run-to-run deterministic.
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr float RMS_EPS = 1e-6f;
+
+__device__ __forceinline__ void unpack8(const uint4& u, float* f) {
+  f[0] = bf_lo(u.x); f[1] = bf_hi(u.x);
+  f[2] = bf_lo(u.y); f[3] = bf_hi(u.y);
+  f[4] = bf_lo(u.z); f[5] = bf_hi(u.z);
+  f[6] = bf_lo(u.w); f[7] = bf_hi(u.w);
+}
+__device__ __forceinline__ uint4 pack8(const float* f) {
+  return make_uint4(pack_bf2(f[0], f[1]), pack_bf2(f[2], f[3]), pack_bf2(f[4], f[5]),
+                    pack_bf2(f[6], f[7]));
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, uint32_t value, long n) {
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x)
+    p[i] = value;
+}
+
+__global__ void f32_to_bf16_kernel(const float* __restrict__ in, uint16_t* __restrict__ out, long n) {
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x)
+    out[i] = (uint16_t)f2bf(in[i]);
+}
+
+// cs[t][j] = (cos, sin) of t * 10000^(-j/64), angle formed in fp64.
+// ([CT50] "1. Modelo GPT" lists RoPE; base 10000 and the half-split pairing
+// (j, j + 64) are this library's reading.)
+__global__ void rope_table_kernel(float* cs, int T) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= T * 64) return;
+  const int t = i >> 6;
+  const int j = i & 63;
+  const double theta = exp(-(double)j / 64.0 * log(10000.0));
+  double s, c;
+  sincos((double)t * theta, &s, &c);
+  cs[2 * i] = (float)c;
+  cs[2 * i + 1] = (float)s;
+}
+
+// x[i] = wte[tok[i]] ([CT50] "1. Modelo GPT": untied input embedding).
+__global__ void embed_fwd_kernel(const int32_t* __restrict__ tok, const uint16_t* __restrict__ wte,
+                                 uint16_t* __restrict__ x, int* err, long N, int d, int V) {
+  const int chunks = d / 8;
+  for (long c = blockIdx.x * (long)blockDim.x + threadIdx.x; c < N * chunks;
+       c += (long)gridDim.x * blockDim.x) {
+    const long i = c / chunks;
+    const int k = (int)(c - i * chunks);
+    const int t = tok[i];
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (t >= 0 && t < V) {
+      v = *reinterpret_cast<const uint4*>(wte + (long)t * d + 8 * k);
+    } else if (k == 0) {
+      atomicOr(err, GPT_DEV_ETOKEN);
+    }
+    *reinterpret_cast<uint4*>(x + i * d + 8 * k) = v;
+  }
+}
+
+// dwte[tok[i]] += dx[i]; rows of absent tokens are untouched (zeroed before).
+__global__ void embed_bwd_kernel(const int32_t* __restrict__ tok, const float* __restrict__ dx,
+                                 float* __restrict__ dwte, long N, int d, int V) {
+  const int chunks = d / 4;
+  for (long c = blockIdx.x * (long)blockDim.x + threadIdx.x; c < N * chunks;
+       c += (long)gridDim.x * blockDim.x) {
+    const long i = c / chunks;
+    const int k = (int)(c - i * chunks);
+    const int t = tok[i];
+    if (t < 0 || t >= V) continue;
+    const float4 g = *reinterpret_cast<const float4*>(dx + i * d + 4 * k);
+    float* dst = dwte + (long)t * d + 4 * k;
+    unsafeAtomicAdd(dst + 0, g.x);
+    unsafeAtomicAdd(dst + 1, g.y);
+    unsafeAtomicAdd(dst + 2, g.z);
+    unsafeAtomicAdd(dst + 3, g.w);
+  }
+}
+
+// Parameter-free RMSNorm: xn = x * rstd, rstd = (mean(x^2) + eps)^-1/2.
+__global__ void rmsnorm_fwd_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ xn,
+                                   float* __restrict__ rstd, long N, int d) {
+  const int lane = threadIdx.x & 63;
+  const long row = blockIdx.x * (long)(blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (row >= N) return;
+  const uint16_t* xr = x + row * d;
+  const int chunks = d / 8;
+  float ss = 0.f;
+  for (int c = lane; c < chunks; c += 64) {
+    float f[8];
+    unpack8(*reinterpret_cast<const uint4*>(xr + 8 * c), f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+  }
+  ss = warp_sum(ss);
+  const float r = rsqrtf(ss / (float)d + RMS_EPS);
+  uint16_t* yr = xn + row * d;
+  for (int c = lane; c < chunks; c += 64) {
+    float f[8];
+    unpack8(*reinterpret_cast<const uint4*>(xr + 8 * c), f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] *= r;
+    *reinterpret_cast<uint4*>(yr + 8 * c) = pack8(f);
+  }
+  if (lane == 0) rstd[row] = r;
+}
+
+// dx (+)= rstd * (dxn - xn * mean(dxn * xn)); dx_bf16 = bf16(dx).
+__global__ void rmsnorm_bwd_kernel(const float* __restrict__ dxn, const uint16_t* __restrict__ xn,
+                                   const float* __restrict__ rstd, float* __restrict__ dx,
+                                   uint16_t* __restrict__ dxb, long N, int d, int accumulate) {
+  const int lane = threadIdx.x & 63;
+  const long row = blockIdx.x * (long)(blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (row >= N) return;
+  const float* gr = dxn + row * d;
+  const uint16_t* yr = xn + row * d;
+  const int chunks = d / 8;
+  float dot = 0.f;
+  for (int c = lane; c < chunks; c += 64) {
+    float y[8];
+    unpack8(*reinterpret_cast<const uint4*>(yr + 8 * c), y);
+    const float4 g0 = *reinterpret_cast<const float4*>(gr + 8 * c);
+    const float4 g1 = *reinterpret_cast<const float4*>(gr + 8 * c + 4);
+    dot += g0.x * y[0] + g0.y * y[1] + g0.z * y[2] + g0.w * y[3] + g1.x * y[4] + g1.y * y[5] +
+           g1.z * y[6] + g1.w * y[7];
+  }
+  dot = warp_sum(dot) / (float)d;
+  const float r = rstd[row];
+  float* dr = dx + row * d;
+  uint16_t* br = dxb + row * d;
+  for (int c = lane; c < chunks; c += 64) {
+    float y[8];
+    unpack8(*reinterpret_cast<const uint4*>(yr + 8 * c), y);
+    const float4 g0 = *reinterpret_cast<const float4*>(gr + 8 * c);
+    const float4 g1 = *reinterpret_cast<const float4*>(gr + 8 * c + 4);
+    const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    float o[8];
+    if (accumulate) {
+      const float4 a0 = *reinterpret_cast<const float4*>(dr + 8 * c);
+      const float4 a1 = *reinterpret_cast<const float4*>(dr + 8 * c + 4);
+      const float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = a[e] + r * (g[e] - y[e] * dot);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = r * (g[e] - y[e] * dot);
+    }
+    *reinterpret_cast<float4*>(dr + 8 * c) = make_float4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<float4*>(dr + 8 * c + 4) = make_float4(o[4], o[5], o[6], o[7]);
+    *reinterpret_cast<uint4*>(br + 8 * c) = pack8(o);
+  }
+}
+
+// QK normalisation per 128-wide head then RoPE ([CT50] "1. Modelo GPT" lists
+// both). One wave per (token, head); lane j holds the rotation pair
+// (j, j + 64), so the rotation is in-lane. rstd per head is saved.
+__global__ void qknorm_rope_fwd_kernel(uint16_t* __restrict__ qkv, float* __restrict__ rstd_qk,
+                                       const float* __restrict__ cs, long N, int T, int H) {
+  const int lane = threadIdx.x & 63;
+  const long idx = blockIdx.x * (long)(blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (idx >= N * 2 * H) return;
+  const long row = idx / (2 * H);
+  const int hh = (int)(idx - row * 2 * H);  // 0..H-1 q heads, H..2H-1 k heads
+  const int t = (int)(row % T);
+  uint16_t* p = qkv + row * 3L * H * 128 + hh * 128;
+  const float x1 = bf2f(p[lane]);
+  const float x2 = bf2f(p[lane + 64]);
+  const float ss = warp_sum(x1 * x1 + x2 * x2);
+  const float r = rsqrtf(ss / 128.f + RMS_EPS);
+  const float n1 = x1 * r, n2 = x2 * r;
+  const float c = cs[2 * (t * 64 + lane)];
+  const float s = cs[2 * (t * 64 + lane) + 1];
+  p[lane] = (uint16_t)f2bf(n1 * c - n2 * s);
+  p[lane + 64] = (uint16_t)f2bf(n1 * s + n2 * c);
+  if (lane == 0) rstd_qk[idx] = r;
+}
+
+// Backward of the above. dy = d loss / d rope(norm(x)); y = rope(norm(x)) saved.
+// dn = rope^-1(dy); n = rope^-1(y); dx = rstd * (dn - n * mean(dn * n)), and
+// mean(dn * n) = mean(dy * y) because the rotation preserves dot products.
+__global__ void qknorm_rope_bwd_kernel(uint16_t* __restrict__ dqkv, const uint16_t* __restrict__ qkv,
+                                       const float* __restrict__ rstd_qk, const float* __restrict__ cs,
+                                       long N, int T, int H) {
+  const int lane = threadIdx.x & 63;
+  const long idx = blockIdx.x * (long)(blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (idx >= N * 2 * H) return;
+  const long row = idx / (2 * H);
+  const int hh = (int)(idx - row * 2 * H);
+  const int t = (int)(row % T);
+  const long off = row * 3L * H * 128 + hh * 128;
+  uint16_t* g = dqkv + off;
+  const uint16_t* y = qkv + off;
+  const float g1 = bf2f(g[lane]), g2 = bf2f(g[lane + 64]);
+  const float y1 = bf2f(y[lane]), y2 = bf2f(y[lane + 64]);
+  const float dot = warp_sum(g1 * y1 + g2 * y2) / 128.f;
+  const float c = cs[2 * (t * 64 + lane)];
+  const float s = cs[2 * (t * 64 + lane) + 1];
+  const float dn1 = g1 * c + g2 * s, dn2 = -g1 * s + g2 * c;
+  const float n1 = y1 * c + y2 * s, n2 = -y1 * s + y2 * c;
+  const float r = rstd_qk[idx];
+  g[lane] = (uint16_t)f2bf(r * (dn1 - n1 * dot));
+  g[lane + 64] = (uint16_t)f2bf(r * (dn2 - n2 * dot));
+}
+
+__global__ void count_targets_kernel(const int32_t* __restrict__ tgt, long N, int V, int* counter,
+                                     int* err) {
+  int local = 0;
+  bool bad = false;
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < N; i += (long)gridDim.x * blockDim.x) {
+    const int t = tgt[i];
+    if (t >= 0 && t < V) {
+      ++local;
+    } else if (t != -1) {
+      bad = true;
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) local += __shfl_xor(local, o, 64);
+  if ((threadIdx.x & 63) == 0 && local) atomicAdd(counter, local);
+  if (bad) atomicOr(err, GPT_DEV_ETOKEN);
+}
+
+// Softmax cross-entropy over one row of bf16 logits, in place:
+//   lse = log sum_j exp(z_j); loss_row = lse - z_t;
+//   dz_j = (exp(z_j - lse) - [j == t]) / n_valid, written as bf16.
+// Rows whose target is ignored (or invalid) get loss 0 and dz 0.
+__global__ void __launch_bounds__(256) ce_softmax_kernel(uint16_t* __restrict__ logits,
+                                                         const int32_t* __restrict__ tgt,
+                                                         float* __restrict__ loss_rows, int V,
+                                                         const int* __restrict__ n_valid) {
+  __shared__ float red[2][4];
+  const long row = blockIdx.x;
+  uint16_t* z = logits + row * (long)V;
+  const int t = tgt[row];
+  const bool valid = t >= 0 && t < V;
+  const int chunks = V / 8;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  float m = -INFINITY, s = 0.f;
+  for (int c = tid; c < chunks; c += 256) {
+    float f[8];
+    unpack8(*reinterpret_cast<const uint4*>(z + 8 * c), f);
+    float cm = f[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) cm = fmaxf(cm, f[e]);
+    const float nm = fmaxf(m, cm);
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += exp2f((f[e] - nm) * GPT_LOG2E);
+    s = s * exp2f((m - nm) * GPT_LOG2E) + acc;
+    m = nm;
+  }
+  // Combine (m, s) across the wave, then across the 4 waves.
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float om = __shfl_xor(m, o, 64);
+    const float os = __shfl_xor(s, o, 64);
+    const float nm = fmaxf(m, om);
+    s = s * exp2f((m - nm) * GPT_LOG2E) + os * exp2f((om - nm) * GPT_LOG2E);
+    m = nm;
+  }
+  if (lane == 0) {
+    red[0][wave] = m;
+    red[1][wave] = s;
+  }
+  __syncthreads();
+  float M = red[0][0], S = 0.f;
+  for (int w = 1; w < 4; ++w) M = fmaxf(M, red[0][w]);
+  for (int w = 0; w < 4; ++w) S += red[1][w] * exp2f((red[0][w] - M) * GPT_LOG2E);
+  const float lse = M + logf(S);
+  const int nv = *n_valid;
+  const float scale = (valid && nv > 0) ? 1.f / (float)nv : 0.f;
+  if (tid == 0) loss_rows[row] = valid ? lse - bf2f(z[t]) : 0.f;
+  __syncthreads();  // z[t] read before it is overwritten
+  for (int c = tid; c < chunks; c += 256) {
+    float f[8];
+    unpack8(*reinterpret_cast<const uint4*>(z + 8 * c), f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float p = exp2f((f[e] - lse) * GPT_LOG2E);
+      if (8 * c + e == t) p -= 1.f;
+      f[e] = p * scale;
+    }
+    *reinterpret_cast<uint4*>(z + 8 * c) = pack8(f);
+  }
+}
+
+// loss = sum(loss_rows) / n_valid, one workgroup, fixed order.
+__global__ void loss_reduce_kernel(const float* __restrict__ rows, long N, const int* n_valid,
+                                   float* loss) {
+  __shared__ float red[4];
+  float s = 0.f;
+  for (long i = threadIdx.x; i < N; i += blockDim.x) s += rows[i];
+  s = warp_sum(s);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float tot = red[0] + red[1] + red[2] + red[3];
+    const int nv = *n_valid;
+    *loss = nv > 0 ? tot / (float)nv : 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Muon ([CT50] "2. Otimizador Muon")
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ long muon_mat_offset(const MuonGroup& g, int j) {
+  const int layer = j / g.per_layer;
+  const int k = j - layer * g.per_layer;
+  return g.base + layer * g.layer_stride + k * g.mat_stride;
+}
+
+// M <- mu M + G over matrix blockIdx.y; partial sum of squares of the new M.
+__global__ void muon_momentum_kernel(const MuonGroup g, const float* __restrict__ grads,
+                                     float* __restrict__ mom, float mu, float* __restrict__ partials) {
+  __shared__ float red[4];
+  const int j = blockIdx.y;
+  const long off = muon_mat_offset(g, j);
+  const long n4 = (long)g.rows * g.cols / 4;
+  const float4* gp = reinterpret_cast<const float4*>(grads + off);
+  float4* mp = reinterpret_cast<float4*>(mom + off);
+  float ss = 0.f;
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n4; i += (long)gridDim.x * blockDim.x) {
+    float4 m = mp[i];
+    const float4 gv = gp[i];
+    m.x = mu * m.x + gv.x;
+    m.y = mu * m.y + gv.y;
+    m.z = mu * m.z + gv.z;
+    m.w = mu * m.w + gv.w;
+    mp[i] = m;
+    ss += m.x * m.x + m.y * m.y + m.z * m.z + m.w * m.w;
+  }
+  ss = warp_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) partials[(long)j * gridDim.x + blockIdx.x] = red[0] + red[1] + red[2] + red[3];
+}
+
+__device__ __forceinline__ float sum_partials(const float* partials, int j, int nb) {
+  float s = 0.f;
+  for (int i = 0; i < nb; ++i) s += partials[(long)j * nb + i];
+  return s;
+}
+
+__device__ __forceinline__ void split_store(float v, float* x32, uint16_t* xh, uint16_t* xl, long i) {
+  const uint32_t h = f2bf(v);
+  x32[i] = v;
+  xh[i] = (uint16_t)h;
+  xl[i] = (uint16_t)f2bf(v - bf2f(h));
+}
+
+// X = M / (||M||_F + 1e-7) in the tall orientation, as fp32 and bf16 hi/lo.
+// X is [x_rows, x_cols]. A matrix flagged in transposed_mask is stored wide,
+// as [x_cols, x_rows]; it is transposed through a 32x33 LDS tile.
+// Grid: (x_cols / 32, x_rows / 32, count); 256 threads.
+__global__ void muon_pack_kernel(const MuonGroup g, const float* __restrict__ mom,
+                                 const float* __restrict__ partials, int nb, float* __restrict__ x32,
+                                 uint16_t* __restrict__ xh, uint16_t* __restrict__ xl) {
+  __shared__ float tile[32][33];
+  const int j = blockIdx.z;
+  const long off = muon_mat_offset(g, j);
+  const int k = j % g.per_layer;
+  const bool tr = (g.transposed_mask >> k) & 1;
+  const float inv = 1.f / (sqrtf(sum_partials(partials, j, nb)) + 1e-7f);
+  const long xr = g.x_rows, xc = g.x_cols;
+  const long xoff = (long)j * xr * xc;
+  const float* src = mom + off;
+  const int tx = threadIdx.x & 31;
+  const int ty = threadIdx.x >> 5;  // 0..7
+  const long r0 = blockIdx.y * 32L, c0 = blockIdx.x * 32L;  // X tile origin
+  if (!tr) {
+    for (int rr = ty; rr < 32; rr += 8) {
+      const long idx = (r0 + rr) * xc + c0 + tx;
+      split_store(src[idx] * inv, x32 + xoff, xh + xoff, xl + xoff, idx);
+    }
+  } else {
+    // Stored M[c][r] = X[r][c]; stored rows have x_rows elements.
+    for (int cc = ty; cc < 32; cc += 8) tile[cc][tx] = src[(c0 + cc) * xr + r0 + tx];
+    __syncthreads();
+    for (int rr = ty; rr < 32; rr += 8) {
+      const long idx = (r0 + rr) * xc + c0 + tx;
+      split_store(tile[tx][rr] * inv, x32 + xoff, xh + xoff, xl + xoff, idx);
+    }
+  }
+}
+
+// W <- W - lr * sqrt(max(1, rows/cols)) * X in the stored orientation (rows =
+// fan-out of the stored matrix); refresh bf16. Grid as muon_pack_kernel.
+__global__ void muon_update_kernel(const MuonGroup g, const float* __restrict__ x32,
+                                   float* __restrict__ params, uint16_t* __restrict__ pbf, float lr) {
+  __shared__ float tile[32][33];
+  const int j = blockIdx.z;
+  const long off = muon_mat_offset(g, j);
+  const int k = j % g.per_layer;
+  const bool tr = (g.transposed_mask >> k) & 1;
+  const long xr = g.x_rows, xc = g.x_cols;
+  const float srows = (float)(tr ? xc : xr), scols = (float)(tr ? xr : xc);
+  const float scale = lr * sqrtf(fmaxf(1.f, srows / scols));
+  const long xoff = (long)j * xr * xc;
+  const int tx = threadIdx.x & 31;
+  const int ty = threadIdx.x >> 5;
+  const long r0 = blockIdx.y * 32L, c0 = blockIdx.x * 32L;  // X tile origin
+  float* w = params + off;
+  uint16_t* wb = pbf + off;
+  if (!tr) {
+    for (int rr = ty; rr < 32; rr += 8) {
+      const long idx = (r0 + rr) * xc + c0 + tx;
+      const float v = w[idx] - scale * x32[xoff + idx];
+      w[idx] = v;
+      wb[idx] = (uint16_t)f2bf(v);
+    }
+  } else {
+    for (int rr = ty; rr < 32; rr += 8) tile[rr][tx] = x32[xoff + (r0 + rr) * xc + c0 + tx];
+    __syncthreads();
+    // Stored W[c][r] with c in the X-column tile, r in the X-row tile.
+    for (int cc = ty; cc < 32; cc += 8) {
+      const long idx = (c0 + cc) * xr + r0 + tx;
+      const float v = w[idx] - scale * tile[tx][cc];
+      w[idx] = v;
+      wb[idx] = (uint16_t)f2bf(v);
+    }
+  }
+}
+
+// Sum of squares of each of `count` contiguous matrices of n elements.
+__global__ void sumsq_kernel(const float* __restrict__ x, long n, float* __restrict__ partials) {
+  __shared__ float red[4];
+  const int j = blockIdx.y;
+  const float* p = x + (long)j * n;
+  float ss = 0.f;
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x)
+    ss += p[i] * p[i];
+  ss = warp_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) partials[(long)j * gridDim.x + blockIdx.x] = red[0] + red[1] + red[2] + red[3];
+}
+
+__global__ void ns_normalize_kernel(float* __restrict__ x32, uint16_t* __restrict__ xh,
+                                    uint16_t* __restrict__ xl, long n, const float* __restrict__ partials,
+                                    int nb) {
+  const int j = blockIdx.y;
+  const float inv = 1.f / (sqrtf(sum_partials(partials, j, nb)) + 1e-7f);
+  const long base = (long)j * n;
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x)
+    split_store(x32[base + i] * inv, x32, xh, xl, base + i);
+}
+
+__global__ void split_hilo_kernel(const float* __restrict__ x32, uint16_t* __restrict__ xh,
+                                  uint16_t* __restrict__ xl, long n) {
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
+    const uint32_t h = f2bf(x32[i]);
+    xh[i] = (uint16_t)h;
+    xl[i] = (uint16_t)f2bf(x32[i] - bf2f(h));
+  }
+}
+
+inline int grid_for(long work, int per_block, int cap = 16384) {
+  long b = (work + per_block - 1) / per_block;
+  if (b < 1) b = 1;
+  if (b > cap) b = cap;
+  return (int)b;
+}
+
+}  // namespace
+
+hipError_t launch_fill_u32(void* p, uint32_t value, long n_words, hipStream_t s) {
+  if (n_words <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_for(n_words, 256)), dim3(256), 0, s,
+                     reinterpret_cast<uint32_t*>(p), value, n_words);
+  return hipGetLastError();
+}
+
+hipError_t launch_f32_to_bf16(const float* in, uint16_t* out, long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(f32_to_bf16_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, in, out, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table(float* cs, int T, hipStream_t s) {
+  hipLaunchKernelGGL(rope_table_kernel, dim3((T * 64 + 255) / 256), dim3(256), 0, s, cs, T);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed_fwd(const int32_t* tok, const uint16_t* wte, uint16_t* x, int* err, long N,
+                            int d, int V, hipStream_t s) {
+  hipLaunchKernelGGL(embed_fwd_kernel, dim3(grid_for(N * (d / 8), 256)), dim3(256), 0, s, tok, wte, x,
+                     err, N, d, V);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed_bwd(const int32_t* tok, const float* dx, float* dwte, long N, int d, int V,
+                            hipStream_t s) {
+  hipLaunchKernelGGL(embed_bwd_kernel, dim3(grid_for(N * (d / 4), 256)), dim3(256), 0, s, tok, dx,
+                     dwte, N, d, V);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_fwd(const uint16_t* x, uint16_t* xn, float* rstd, long N, int d,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(rmsnorm_fwd_kernel, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s, x, xn, rstd,
+                     N, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_bwd(const float* dxn, const uint16_t* xn, const float* rstd, float* dx,
+                              uint16_t* dx_bf16, long N, int d, int accumulate, hipStream_t s) {
+  hipLaunchKernelGGL(rmsnorm_bwd_kernel, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s, dxn, xn, rstd,
+                     dx, dx_bf16, N, d, accumulate);
+  return hipGetLastError();
+}
+
+hipError_t launch_qknorm_rope_fwd(uint16_t* qkv, float* rstd_qk, const float* cs, long N, int T,
+                                  int H, hipStream_t s) {
+  const long items = N * 2 * H;
+  hipLaunchKernelGGL(qknorm_rope_fwd_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, qkv,
+                     rstd_qk, cs, N, T, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_qknorm_rope_bwd(uint16_t* dqkv, const uint16_t* qkv, const float* rstd_qk,
+                                  const float* cs, long N, int T, int H, hipStream_t s) {
+  const long items = N * 2 * H;
+  hipLaunchKernelGGL(qknorm_rope_bwd_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, dqkv,
+                     qkv, rstd_qk, cs, N, T, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_count_targets(const int32_t* tgt, long N, int V, int* counter, int* err,
+                                hipStream_t s) {
+  hipLaunchKernelGGL(count_targets_kernel, dim3(grid_for(N, 256, 1024)), dim3(256), 0, s, tgt, N, V,
+                     counter, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_ce_softmax(uint16_t* logits, const int32_t* tgt, float* loss_rows, long rows,
+                             int V, const int* n_valid, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(ce_softmax_kernel, dim3((unsigned)rows), dim3(256), 0, s, logits, tgt, loss_rows,
+                     V, n_valid);
+  return hipGetLastError();
+}
+
+hipError_t launch_loss_reduce(const float* loss_rows, long N, const int* n_valid, float* loss,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(256), 0, s, loss_rows, N, n_valid, loss);
+  return hipGetLastError();
+}
+
+hipError_t launch_muon_momentum(const MuonGroup& g, const float* grads, float* mom, float mu,
+                                float* partials, int blocks_per_mat, hipStream_t s) {
+  hipLaunchKernelGGL(muon_momentum_kernel, dim3(blocks_per_mat, g.count), dim3(256), 0, s, g, grads,
+                     mom, mu, partials);
+  return hipGetLastError();
+}
+
+hipError_t launch_muon_pack(const MuonGroup& g, const float* mom, const float* partials,
+                            int blocks_per_mat, float* x32, uint16_t* xh, uint16_t* xl,
+                            hipStream_t s) {
+  dim3 grid((unsigned)(g.x_cols / 32), (unsigned)(g.x_rows / 32), g.count);
+  hipLaunchKernelGGL(muon_pack_kernel, grid, dim3(256), 0, s, g, mom, partials, blocks_per_mat, x32, xh,
+                     xl);
+  return hipGetLastError();
+}
+
+hipError_t launch_muon_update(const MuonGroup& g, const float* x32, float* params,
+                              uint16_t* params_bf16, float lr, hipStream_t s) {
+  dim3 grid((unsigned)(g.x_cols / 32), (unsigned)(g.x_rows / 32), g.count);
+  hipLaunchKernelGGL(muon_update_kernel, grid, dim3(256), 0, s, g, x32, params, params_bf16, lr);
+  return hipGetLastError();
+}
+
+hipError_t launch_ns_prepare(float* x32, uint16_t* xh, uint16_t* xl, int count, long n,
+                             float* partials, int blocks_per_mat, hipStream_t s) {
+  hipLaunchKernelGGL(sumsq_kernel, dim3(blocks_per_mat, count), dim3(256), 0, s, x32, n, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(ns_normalize_kernel, dim3(grid_for(n, 256, 1024), count), dim3(256), 0, s, x32, xh,
+                     xl, n, partials, blocks_per_mat);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_hilo(const float* x32, uint16_t* xh, uint16_t* xl, long n, hipStream_t s) {
+  hipLaunchKernelGGL(split_hilo_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, x32, xh, xl, n);
+  return hipGetLastError();
+}

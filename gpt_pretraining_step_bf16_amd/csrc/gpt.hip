@@ -1,0 +1,792 @@
+// Host runtime of the pretraining step: the model plan (shapes and flat
+// parameter layout), workspace carving, the launch sequences of gpt_fwd_bwd
+// and muon_step, and the C ABI declared in include/gpt.h.
+//
+// Sources (cited by page title and section):
+//   [CT50] dev.to, "Como treinar seu próprio ChatGPT por 50 dólares".
+//   [HADA] GeekNews (hada.io) summary of the nanochat launch README.
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/gpt.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+// One timed launch: events recorded on the launch stream around it.
+struct ProfSlot {
+  hipEvent_t start = nullptr, stop = nullptr;
+  int cat = 0;
+  double flops = 0.0;
+};
+
+}  // namespace
+
+struct gpt_model {
+  int depth = 0, d = 0, H = 0, F = 0, V = 0, max_seq = 0;
+  std::vector<gpt_tensor> tensors;
+  int64_t nparams = 0;
+  int64_t off_wte = 0, off_layer0 = 0, layer_stride = 0, off_lm = 0;
+  // Opt-in launch timing (gpt_profile_*): a pool of event pairs, reused.
+  bool prof_on = false;
+  std::vector<ProfSlot> prof;
+  size_t prof_used = 0;
+  ~gpt_model() {
+    for (auto& s : prof) {
+      if (s.start) (void)hipEventDestroy(s.start);
+      if (s.stop) (void)hipEventDestroy(s.stop);
+    }
+  }
+};
+
+namespace {
+
+// Brackets one launch with events when profiling is on.
+struct ProfScope {
+  gpt_model* m;
+  hipStream_t s;
+  ProfSlot* slot = nullptr;
+  ProfScope(gpt_model* m_, hipStream_t s_, int cat, double flops) : m(m_), s(s_) {
+    if (!m || !m->prof_on) return;
+    if (m->prof_used == m->prof.size()) {
+      ProfSlot ns;
+      if (hipEventCreate(&ns.start) != hipSuccess || hipEventCreate(&ns.stop) != hipSuccess) return;
+      m->prof.push_back(ns);
+    }
+    slot = &m->prof[m->prof_used++];
+    slot->cat = cat;
+    slot->flops = flops;
+    (void)hipEventRecord(slot->start, s);
+  }
+  ~ProfScope() {
+    if (slot) (void)hipEventRecord(slot->stop, s);
+  }
+};
+
+enum { PROF_GEMM = 0, PROF_ATTN_FWD = 1, PROF_ATTN_BWD = 2, PROF_NS = 3, PROF_NCAT = 4 };
+
+// Thread-local current model for the GEMM helpers' profiling.
+thread_local gpt_model* g_prof_model = nullptr;
+
+inline double gemm_flops(const GemmArgs& g) {
+  return 2.0 * g.M * (double)g.N * g.K * g.nseg * g.batch;
+}
+
+hipError_t launch_gemm_prof(const GemmArgs& g, hipStream_t s, int cat = PROF_GEMM) {
+  ProfScope ps(g_prof_model, s, cat, gemm_flops(g));
+  return launch_gemm(g, s);
+}
+
+constexpr size_t ALIGN = 256;
+inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+// Linear carve of one workspace.
+struct Carve {
+  size_t cur = 0;
+  size_t take(size_t bytes) {
+    const size_t o = cur;
+    cur = align_up(cur + bytes);
+    return o;
+  }
+};
+
+// Offsets of the gpt_fwd_bwd workspace for a (batch, seq).
+struct FwdPlan {
+  long N = 0;
+  int T = 0, B = 0;
+  size_t hdr = 0, cs = 0;
+  // per-layer saved activations: base offsets of layer 0 and the stride
+  size_t xn1 = 0, rstd1 = 0, qkv = 0, rstdqk = 0, o = 0, lse = 0, xn2 = 0, rstd2 = 0, r = 0;
+  size_t layer_bytes = 0;
+  size_t x = 0, xnf = 0, rstdf = 0, dx = 0, dxb = 0, dxn = 0, du = 0, dO = 0, delta = 0, dqkv = 0;
+  size_t logits = 0, loss_rows = 0, part = 0;
+  long nc = 0;       // CE chunk rows
+  size_t part_bytes = 0;
+  size_t total = 0;
+};
+
+struct SplitK {
+  int splits = 1;
+  int k_chunk = 0;
+};
+
+// Split-K for the weight-gradient GEMMs (K = tokens, small outputs).
+SplitK plan_splitk(long out_rows, long out_cols, long K) {
+  SplitK s;
+  const long tiles = ((out_rows + 255) / 256) * ((out_cols + 255) / 256);
+  long want = (512 + tiles - 1) / tiles;
+  const long max_by_k = std::max<long>(1, K / 1024);
+  want = std::max<long>(1, std::min(want, max_by_k));
+  long chunk = (K + want - 1) / want;
+  chunk = (chunk + 63) / 64 * 64;
+  s.k_chunk = (int)chunk;
+  s.splits = (int)((K + chunk - 1) / chunk);
+  return s;
+}
+
+FwdPlan plan_fwd(const gpt_model& m, int B, int T) {
+  FwdPlan p;
+  p.B = B;
+  p.T = T;
+  p.N = (long)B * T;
+  const long N = p.N;
+  const long d = m.d, F = m.F, H = m.H, V = m.V;
+  Carve c;
+  p.hdr = c.take(256);
+  p.cs = c.take((size_t)T * 64 * 2 * 4);
+  // Per-layer block, laid out once and repeated.
+  Carve lc;
+  p.xn1 = lc.take(N * d * 2);
+  p.rstd1 = lc.take(N * 4);
+  p.qkv = lc.take(N * 3 * d * 2);
+  p.rstdqk = lc.take(N * 2 * H * 4);
+  p.o = lc.take(N * d * 2);
+  p.lse = lc.take(N * H * 4);
+  p.xn2 = lc.take(N * d * 2);
+  p.rstd2 = lc.take(N * 4);
+  p.r = lc.take(N * F * 2);
+  p.layer_bytes = lc.cur;
+  const size_t layers_base = c.take(p.layer_bytes * m.depth);
+  p.xn1 += layers_base;
+  p.rstd1 += layers_base;
+  p.qkv += layers_base;
+  p.rstdqk += layers_base;
+  p.o += layers_base;
+  p.lse += layers_base;
+  p.xn2 += layers_base;
+  p.rstd2 += layers_base;
+  p.r += layers_base;
+  p.x = c.take(N * d * 2);
+  p.xnf = c.take(N * d * 2);
+  p.rstdf = c.take(N * 4);
+  p.dx = c.take(N * d * 4);
+  p.dxb = c.take(N * d * 2);
+  p.dxn = c.take(N * d * 4);
+  p.du = c.take(N * F * 2);
+  p.dO = c.take(N * d * 2);
+  p.delta = c.take(N * H * 4);
+  p.dqkv = c.take(N * 3 * d * 2);
+  const long cap_rows = std::max<long>(256, (1L << 30) / (2 * V));
+  p.nc = std::min<long>(N, cap_rows);
+  p.logits = c.take((size_t)p.nc * V * 2);
+  p.loss_rows = c.take(N * 4);
+  size_t part = 0;
+  const long shapes[4][2] = {{3 * d, d}, {d, d}, {F, d}, {d, F}};
+  for (auto& sh : shapes) {
+    const SplitK s = plan_splitk(sh[0], sh[1], N);
+    if (s.splits > 1) part = std::max(part, (size_t)s.splits * sh[0] * sh[1] * 4);
+  }
+  p.part_bytes = part;
+  p.part = c.take(std::max<size_t>(part, 256));
+  p.total = c.cur;
+  return p;
+}
+
+// Muon groups of a model: the four d x d matrices of each layer, and the
+// MLP pair (wfc stored [4d, d]; wproj stored [d, 4d], handled transposed).
+void muon_groups(const gpt_model& m, MuonGroup& sq, MuonGroup& tall) {
+  const long d = m.d, F = m.F;
+  sq = MuonGroup{};
+  sq.base = m.off_layer0;
+  sq.layer_stride = m.layer_stride;
+  sq.per_layer = 4;
+  sq.mat_stride = d * d;
+  sq.count = 4 * m.depth;
+  sq.rows = (int)d;
+  sq.cols = (int)d;
+  sq.transposed_mask = 0;
+  sq.x_rows = d;
+  sq.x_cols = d;
+  tall = MuonGroup{};
+  tall.base = m.off_layer0 + 4 * d * d;
+  tall.layer_stride = m.layer_stride;
+  tall.per_layer = 2;
+  tall.mat_stride = F * d;
+  tall.count = 2 * m.depth;
+  tall.rows = (int)F;  // wfc; wproj is the transposed one (mask bit 1)
+  tall.cols = (int)d;
+  tall.transposed_mask = 2;
+  tall.x_rows = F;
+  tall.x_cols = d;
+}
+
+// Newton-Schulz buffers for `count` matrices of xr x xc.
+struct NsPlan {
+  size_t x32 = 0, xh0 = 0, xl0 = 0, xh1 = 0, xl1 = 0, ah = 0, al = 0, bh = 0, bl = 0, part = 0;
+  size_t total = 0;
+  int nb = 0;
+};
+
+NsPlan plan_ns(long count, long xr, long xc, size_t base) {
+  NsPlan p;
+  Carve c;
+  c.cur = base;
+  const long nx = count * xr * xc;
+  const long na = count * xc * xc;
+  p.x32 = c.take(nx * 4);
+  p.xh0 = c.take(nx * 2);
+  p.xl0 = c.take(nx * 2);
+  p.xh1 = c.take(nx * 2);
+  p.xl1 = c.take(nx * 2);
+  p.ah = c.take(na * 2);
+  p.al = c.take(na * 2);
+  p.bh = c.take(na * 2);
+  p.bl = c.take(na * 2);
+  p.nb = 64;
+  p.part = c.take(count * p.nb * 4);
+  p.total = c.cur;
+  return p;
+}
+
+// Run ns_steps iterations on prepared X (x32, xh0, xl0 filled). Result in x32.
+hipError_t run_ns(char* ws, const NsPlan& p, int count, long xr, long xc, const float* coeffs,
+                  int steps, hipStream_t s) {
+  uint16_t* xh[2] = {reinterpret_cast<uint16_t*>(ws + p.xh0), reinterpret_cast<uint16_t*>(ws + p.xh1)};
+  uint16_t* xl[2] = {reinterpret_cast<uint16_t*>(ws + p.xl0), reinterpret_cast<uint16_t*>(ws + p.xl1)};
+  uint16_t* ah = reinterpret_cast<uint16_t*>(ws + p.ah);
+  uint16_t* al = reinterpret_cast<uint16_t*>(ws + p.al);
+  uint16_t* bh = reinterpret_cast<uint16_t*>(ws + p.bh);
+  uint16_t* bl = reinterpret_cast<uint16_t*>(ws + p.bl);
+  float* x32 = reinterpret_cast<float*>(ws + p.x32);
+  int cur = 0;
+  for (int it = 0; it < steps; ++it) {
+    const float a = coeffs[3 * it], b = coeffs[3 * it + 1], c = coeffs[3 * it + 2];
+    // A = X^T X, from hi/lo splits: Xh^T Xh + Xh^T Xl + Xl^T Xh.
+    GemmArgs g;
+    gemm_args_init(g);
+    g.nseg = 3;
+    g.a[0] = xh[cur]; g.b[0] = xh[cur];
+    g.a[1] = xh[cur]; g.b[1] = xl[cur];
+    g.a[2] = xl[cur]; g.b[2] = xh[cur];
+    g.M = (int)xc; g.N = (int)xc; g.K = (int)xr;
+    g.lda = xc; g.ldb = xc; g.sa = xr * xc; g.sb = xr * xc;
+    g.a_kmajor = 0; g.b_kmajor = 0;
+    g.c = ah; g.c2 = al; g.ldc = xc; g.sc = xc * xc;
+    g.batch = count;
+    g.epi = EPI_HILO;
+    hipError_t e = launch_gemm_prof(g, s, PROF_NS);
+    if (e != hipSuccess) return e;
+    // B = b A + c A A (A symmetric, so A A = A A^T).
+    gemm_args_init(g);
+    g.nseg = 3;
+    g.a[0] = ah; g.b[0] = ah;
+    g.a[1] = ah; g.b[1] = al;
+    g.a[2] = al; g.b[2] = ah;
+    g.M = (int)xc; g.N = (int)xc; g.K = (int)xc;
+    g.lda = xc; g.ldb = xc; g.sa = xc * xc; g.sb = xc * xc;
+    g.a_kmajor = 1; g.b_kmajor = 1;
+    g.c = bh; g.c2 = bl; g.ldc = xc; g.sc = xc * xc;
+    g.d = ah; g.d2 = al; g.ldd = xc; g.sd = xc * xc;
+    g.alpha = c; g.beta = b;
+    g.batch = count;
+    g.epi = EPI_NS_POLY;
+    e = launch_gemm_prof(g, s, PROF_NS);
+    if (e != hipSuccess) return e;
+    // X = a X + X B (B symmetric, so X B = X B^T).
+    gemm_args_init(g);
+    g.nseg = 3;
+    g.a[0] = xh[cur]; g.b[0] = bh;
+    g.a[1] = xh[cur]; g.b[1] = bl;
+    g.a[2] = xl[cur]; g.b[2] = bh;
+    g.M = (int)xr; g.N = (int)xc; g.K = (int)xc;
+    g.lda = xc; g.ldb = xc; g.sa = xr * xc; g.sb = xc * xc;
+    g.a_kmajor = 1; g.b_kmajor = 1;
+    g.c = xh[cur ^ 1]; g.c2 = xl[cur ^ 1]; g.c3 = x32; g.ldc = xc; g.sc = xr * xc;
+    g.d = x32; g.ldd = xc; g.sd = xr * xc;
+    g.alpha = 1.f; g.beta = a;
+    g.batch = count;
+    g.epi = EPI_NS_UPDATE;
+    e = launch_gemm_prof(g, s, PROF_NS);
+    if (e != hipSuccess) return e;
+    cur ^= 1;
+  }
+  return hipSuccess;
+}
+
+inline gpt_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return GPT_OK;
+  std::fprintf(stderr, "gpt: HIP error %s\n", hipGetErrorString(e));
+  return GPT_EHIP;
+}
+
+#define HIP_TRY(expr)                                \
+  do {                                               \
+    hipError_t e_ = (expr);                          \
+    if (e_ != hipSuccess) return hip_status(e_);     \
+  } while (0)
+
+// GEMM helpers for the step.
+hipError_t gemm_nt(const uint16_t* A, long lda, const uint16_t* B, long ldb, int M, int N, int K,
+                   void* C, long ldc, int epi, hipStream_t s, const void* D = nullptr, long ldd = 0) {
+  GemmArgs g;
+  gemm_args_init(g);
+  g.a[0] = A; g.b[0] = B;
+  g.M = M; g.N = N; g.K = K;
+  g.lda = lda; g.ldb = ldb;
+  g.a_kmajor = 1; g.b_kmajor = 1;
+  g.c = C; g.ldc = ldc;
+  g.d = D; g.ldd = ldd;
+  g.epi = epi;
+  return launch_gemm_prof(g, s);
+}
+
+// C[M,N] = A[M,K] . B where B is stored [K][N] (a weight read along its out dim).
+hipError_t gemm_nn(const uint16_t* A, long lda, const uint16_t* B, long ldb, int M, int N, int K,
+                   void* C, long ldc, int epi, hipStream_t s, const void* D = nullptr, long ldd = 0) {
+  GemmArgs g;
+  gemm_args_init(g);
+  g.a[0] = A; g.b[0] = B;
+  g.M = M; g.N = N; g.K = K;
+  g.lda = lda; g.ldb = ldb;
+  g.a_kmajor = 1; g.b_kmajor = 0;
+  g.c = C; g.ldc = ldc;
+  g.d = D; g.ldd = ldd;
+  g.epi = epi;
+  return launch_gemm_prof(g, s);
+}
+
+// Weight gradient: G[M,N] (+)= sum_t A[t][m] * B[t][n], A stored [K][M], B [K][N].
+hipError_t gemm_wgrad(const uint16_t* A, long lda, const uint16_t* B, long ldb, int M, int N, long K,
+                      float* G, int accumulate, int square_b, float* part, hipStream_t s) {
+  const SplitK sk = plan_splitk(M, N, K);
+  GemmArgs g;
+  gemm_args_init(g);
+  g.a[0] = A; g.b[0] = B;
+  g.M = M; g.N = N; g.K = (int)K;
+  g.lda = lda; g.ldb = ldb;
+  g.a_kmajor = 0; g.b_kmajor = 0;
+  g.square = square_b ? 2 : 0;
+  if (sk.splits > 1) {
+    g.c = part; g.ldc = N;
+    g.splits = sk.splits; g.k_chunk = sk.k_chunk;
+    g.s_split = (long)M * N;
+    g.epi = EPI_SPLITK;
+    hipError_t e = launch_gemm_prof(g, s);
+    if (e != hipSuccess) return e;
+    return launch_splitk_reduce(part, (long)M * N, sk.splits, G, (long)M * N, accumulate, s);
+  }
+  g.c = G; g.ldc = N;
+  g.epi = EPI_F32_ACC;
+  g.alpha = 1.f;
+  g.beta = accumulate ? 1.f : 0.f;
+  return launch_gemm_prof(g, s);
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+const char* gpt_status_str(gpt_status s) {
+  switch (s) {
+    case GPT_OK: return "ok";
+    case GPT_EINVAL: return "invalid argument";
+    case GPT_ESHAPE: return "unsupported shape";
+    case GPT_EHIP: return "HIP runtime error";
+    case GPT_ETOKEN: return "token or target id outside the vocabulary";
+    case GPT_EWORKSPACE: return "workspace missing or too small";
+  }
+  return "unknown status";
+}
+
+gpt_status gpt_create(int32_t depth, int32_t vocab, int32_t max_seq, gpt_model** out) {
+  if (!out) return GPT_EINVAL;
+  *out = nullptr;
+  if (depth < 1 || depth > 64) return GPT_EINVAL;
+  if (vocab < 64 || vocab > 262144 || vocab % 64 != 0) return GPT_EINVAL;
+  if (max_seq < 1 || max_seq > 16384) return GPT_EINVAL;
+  gpt_model* m = new (std::nothrow) gpt_model();
+  if (!m) return GPT_EINVAL;
+  m->depth = depth;
+  m->d = 128 * ((64 * depth + 127) / 128);
+  m->H = m->d / 128;
+  m->F = 4 * m->d;
+  m->V = vocab;
+  m->max_seq = max_seq;
+  const int64_t d = m->d, F = m->F;
+  int64_t off = 0;
+  auto add = [&](const std::string& name, int32_t rows, int32_t cols, int32_t kind, int32_t layer) {
+    gpt_tensor t{};
+    std::snprintf(t.name, sizeof(t.name), "%s", name.c_str());
+    t.offset = off;
+    t.rows = rows;
+    t.cols = cols;
+    t.kind = kind;
+    t.layer = layer;
+    m->tensors.push_back(t);
+    off += (int64_t)rows * cols;
+  };
+  m->off_wte = 0;
+  add("wte", vocab, (int32_t)d, GPT_KIND_EMB, -1);
+  m->off_layer0 = off;
+  for (int l = 0; l < depth; ++l) {
+    const std::string p = "h" + std::to_string(l) + ".";
+    add(p + "wq", (int32_t)d, (int32_t)d, GPT_KIND_MATRIX, l);
+    add(p + "wk", (int32_t)d, (int32_t)d, GPT_KIND_MATRIX, l);
+    add(p + "wv", (int32_t)d, (int32_t)d, GPT_KIND_MATRIX, l);
+    add(p + "wo", (int32_t)d, (int32_t)d, GPT_KIND_MATRIX, l);
+    add(p + "wfc", (int32_t)F, (int32_t)d, GPT_KIND_MATRIX, l);
+    add(p + "wproj", (int32_t)d, (int32_t)F, GPT_KIND_MATRIX, l);
+  }
+  m->layer_stride = 4 * d * d + 2 * F * d;
+  m->off_lm = off;
+  add("lm_head", vocab, (int32_t)d, GPT_KIND_LM_HEAD, -1);
+  m->nparams = off;
+  *out = m;
+  return GPT_OK;
+}
+
+void gpt_destroy(gpt_model* m) { delete m; }
+
+gpt_status gpt_dims(const gpt_model* m, int32_t dims[6]) {
+  if (!m || !dims) return GPT_EINVAL;
+  dims[0] = m->depth;
+  dims[1] = m->d;
+  dims[2] = m->H;
+  dims[3] = m->F;
+  dims[4] = m->V;
+  dims[5] = m->max_seq;
+  return GPT_OK;
+}
+
+int64_t gpt_num_params(const gpt_model* m) { return m ? m->nparams : 0; }
+int32_t gpt_num_tensors(const gpt_model* m) { return m ? (int32_t)m->tensors.size() : 0; }
+
+gpt_status gpt_tensor_info(const gpt_model* m, int32_t i, gpt_tensor* out) {
+  if (!m || !out || i < 0 || i >= (int32_t)m->tensors.size()) return GPT_EINVAL;
+  *out = m->tensors[i];
+  return GPT_OK;
+}
+
+size_t gpt_workspace_bytes(const gpt_model* m, int32_t batch, int32_t seq) {
+  if (!m || batch < 1 || seq < 1 || seq > m->max_seq) return 0;
+  return plan_fwd(*m, batch, seq).total;
+}
+
+gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
+                       const int32_t* targets, int32_t batch, int32_t seq, float* loss,
+                       float* grads, int32_t accumulate, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (!m || !pbf || !tokens || !targets || !loss || !grads) return GPT_EINVAL;
+  if (batch < 1 || seq < 1) return GPT_EINVAL;
+  if (seq > m->max_seq) return GPT_ESHAPE;
+  if (accumulate != 0 && accumulate != 1) return GPT_EINVAL;
+  const FwdPlan p = plan_fwd(*m, batch, seq);
+  if (!workspace || workspace_bytes < p.total) return GPT_EWORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return GPT_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  g_prof_model = m;
+  const long N = p.N;
+  const int T = seq, d = m->d, F = m->F, H = m->H, V = m->V, L = m->depth;
+  int* hdr = reinterpret_cast<int*>(ws + p.hdr);
+  int* err = hdr;
+  int* n_valid = hdr + 1;
+  float* cs = reinterpret_cast<float*>(ws + p.cs);
+  auto lay = [&](size_t base, int l) { return ws + base + (size_t)l * p.layer_bytes; };
+  uint16_t* x = reinterpret_cast<uint16_t*>(ws + p.x);
+  uint16_t* xnf = reinterpret_cast<uint16_t*>(ws + p.xnf);
+  float* rstdf = reinterpret_cast<float*>(ws + p.rstdf);
+  float* dx = reinterpret_cast<float*>(ws + p.dx);
+  uint16_t* dxb = reinterpret_cast<uint16_t*>(ws + p.dxb);
+  float* dxn = reinterpret_cast<float*>(ws + p.dxn);
+  uint16_t* du = reinterpret_cast<uint16_t*>(ws + p.du);
+  uint16_t* dO = reinterpret_cast<uint16_t*>(ws + p.dO);
+  float* delta = reinterpret_cast<float*>(ws + p.delta);
+  uint16_t* dqkv = reinterpret_cast<uint16_t*>(ws + p.dqkv);
+  uint16_t* logits = reinterpret_cast<uint16_t*>(ws + p.logits);
+  float* loss_rows = reinterpret_cast<float*>(ws + p.loss_rows);
+  float* part = reinterpret_cast<float*>(ws + p.part);
+  const uint16_t* wte = pbf + m->off_wte;
+  const uint16_t* wlm = pbf + m->off_lm;
+
+  // ---- prologue
+  HIP_TRY(launch_fill_u32(hdr, 0, 2, s));
+  HIP_TRY(launch_rope_table(cs, T, s));
+  HIP_TRY(launch_count_targets(targets, N, V, n_valid, err, s));
+  HIP_TRY(launch_embed_fwd(tokens, wte, x, err, N, d, V, s));
+
+  // ---- forward through the blocks
+  for (int l = 0; l < L; ++l) {
+    const uint16_t* W = pbf + m->off_layer0 + (long)l * m->layer_stride;
+    const uint16_t* wqkv = W;
+    const uint16_t* wo = W + 3L * d * d;
+    const uint16_t* wfc = W + 4L * d * d;
+    const uint16_t* wproj = wfc + (long)F * d;
+    uint16_t* xn1 = reinterpret_cast<uint16_t*>(lay(p.xn1, l));
+    float* rstd1 = reinterpret_cast<float*>(lay(p.rstd1, l));
+    uint16_t* qkv = reinterpret_cast<uint16_t*>(lay(p.qkv, l));
+    float* rstdqk = reinterpret_cast<float*>(lay(p.rstdqk, l));
+    uint16_t* o = reinterpret_cast<uint16_t*>(lay(p.o, l));
+    float* lse = reinterpret_cast<float*>(lay(p.lse, l));
+    uint16_t* xn2 = reinterpret_cast<uint16_t*>(lay(p.xn2, l));
+    float* rstd2 = reinterpret_cast<float*>(lay(p.rstd2, l));
+    uint16_t* r = reinterpret_cast<uint16_t*>(lay(p.r, l));
+    HIP_TRY(launch_rmsnorm_fwd(x, xn1, rstd1, N, d, s));
+    HIP_TRY(gemm_nt(xn1, d, wqkv, d, (int)N, 3 * d, d, qkv, 3L * d, EPI_BF16, s));
+    HIP_TRY(launch_qknorm_rope_fwd(qkv, rstdqk, cs, N, T, H, s));
+    {
+      ProfScope ps(m, s, PROF_ATTN_FWD, 4.0 * batch * H * 128.0 * T * (T + 1) / 2.0);
+      HIP_TRY(launch_attention_fwd(qkv, o, lse, batch, T, H, s));
+    }
+    HIP_TRY(gemm_nt(o, d, wo, d, (int)N, d, d, x, d, EPI_RESID_BF16, s));
+    HIP_TRY(launch_rmsnorm_fwd(x, xn2, rstd2, N, d, s));
+    HIP_TRY(gemm_nt(xn2, d, wfc, d, (int)N, F, d, r, F, EPI_RELU_BF16, s));
+    {
+      GemmArgs g;
+      gemm_args_init(g);
+      g.a[0] = r; g.b[0] = wproj;
+      g.M = (int)N; g.N = d; g.K = F;
+      g.lda = F; g.ldb = F;
+      g.a_kmajor = 1; g.b_kmajor = 1;
+      g.square = 1;
+      g.c = x; g.ldc = d;
+      g.epi = EPI_RESID_BF16;
+      HIP_TRY(launch_gemm_prof(g, s));
+    }
+  }
+  HIP_TRY(launch_rmsnorm_fwd(x, xnf, rstdf, N, d, s));
+
+  // ---- head: logits, softmax cross-entropy, and its backward, by token chunks
+  float* g_lm = grads + m->off_lm;
+  for (long r0 = 0; r0 < N; r0 += p.nc) {
+    const int nc = (int)std::min<long>(p.nc, N - r0);
+    HIP_TRY(gemm_nt(xnf + r0 * d, d, wlm, d, nc, V, d, logits, V, EPI_BF16, s));
+    HIP_TRY(launch_ce_softmax(logits, targets + r0, loss_rows + r0, nc, V, n_valid, s));
+    HIP_TRY(gemm_nn(logits, V, wlm, d, nc, d, V, dxn + r0 * d, d, EPI_F32, s));
+    {
+      GemmArgs g;
+      gemm_args_init(g);
+      g.a[0] = logits; g.b[0] = xnf + r0 * d;
+      g.M = V; g.N = d; g.K = nc;
+      g.lda = V; g.ldb = d;
+      g.a_kmajor = 0; g.b_kmajor = 0;
+      g.c = g_lm; g.ldc = d;
+      g.epi = EPI_F32_ACC;
+      g.beta = (r0 > 0 || accumulate) ? 1.f : 0.f;
+      HIP_TRY(launch_gemm_prof(g, s));
+    }
+  }
+  HIP_TRY(launch_loss_reduce(loss_rows, N, n_valid, loss, s));
+  HIP_TRY(launch_rmsnorm_bwd(dxn, xnf, rstdf, dx, dxb, N, d, 0, s));
+
+  // ---- backward through the blocks
+  for (int l = L - 1; l >= 0; --l) {
+    const long woff = m->off_layer0 + (long)l * m->layer_stride;
+    const uint16_t* W = pbf + woff;
+    const uint16_t* wqkv = W;
+    const uint16_t* wo = W + 3L * d * d;
+    const uint16_t* wfc = W + 4L * d * d;
+    const uint16_t* wproj = wfc + (long)F * d;
+    float* G = grads + woff;
+    float* gqkv = G;
+    float* go = G + 3L * d * d;
+    float* gfc = G + 4L * d * d;
+    float* gproj = gfc + (long)F * d;
+    const uint16_t* xn1 = reinterpret_cast<const uint16_t*>(lay(p.xn1, l));
+    const float* rstd1 = reinterpret_cast<const float*>(lay(p.rstd1, l));
+    const uint16_t* qkv = reinterpret_cast<const uint16_t*>(lay(p.qkv, l));
+    const float* rstdqk = reinterpret_cast<const float*>(lay(p.rstdqk, l));
+    const uint16_t* o = reinterpret_cast<const uint16_t*>(lay(p.o, l));
+    const float* lse = reinterpret_cast<const float*>(lay(p.lse, l));
+    const uint16_t* xn2 = reinterpret_cast<const uint16_t*>(lay(p.xn2, l));
+    const float* rstd2 = reinterpret_cast<const float*>(lay(p.rstd2, l));
+    const uint16_t* r = reinterpret_cast<const uint16_t*>(lay(p.r, l));
+    // MLP: x_out = x_mid + relu(u)^2 Wproj^T
+    HIP_TRY(gemm_nn(dxb, d, wproj, F, (int)N, F, d, du, F, EPI_DRELU2_BF16, s, r, F));
+    HIP_TRY(gemm_wgrad(dxb, d, r, F, d, F, N, gproj, accumulate, 1, part, s));
+    HIP_TRY(gemm_nn(du, F, wfc, d, (int)N, d, F, dxn, d, EPI_F32, s));
+    HIP_TRY(gemm_wgrad(du, F, xn2, d, F, d, N, gfc, accumulate, 0, part, s));
+    HIP_TRY(launch_rmsnorm_bwd(dxn, xn2, rstd2, dx, dxb, N, d, 1, s));
+    // Attention: x_mid = x_in + o Wo^T
+    HIP_TRY(gemm_nn(dxb, d, wo, d, (int)N, d, d, dO, d, EPI_BF16, s));
+    HIP_TRY(gemm_wgrad(dxb, d, o, d, d, d, N, go, accumulate, 0, part, s));
+    {
+      ProfScope ps(m, s, PROF_ATTN_BWD, 10.0 * batch * H * 128.0 * T * (T + 1) / 2.0);
+      HIP_TRY(launch_attention_bwd(qkv, o, lse, dO, dqkv, delta, batch, T, H, s));
+    }
+    HIP_TRY(launch_qknorm_rope_bwd(dqkv, qkv, rstdqk, cs, N, T, H, s));
+    HIP_TRY(gemm_nn(dqkv, 3L * d, wqkv, d, (int)N, d, 3 * d, dxn, d, EPI_F32, s));
+    HIP_TRY(gemm_wgrad(dqkv, 3L * d, xn1, d, 3 * d, d, N, gqkv, accumulate, 0, part, s));
+    HIP_TRY(launch_rmsnorm_bwd(dxn, xn1, rstd1, dx, dxb, N, d, 1, s));
+  }
+
+  // ---- embedding gradient
+  float* gwte = grads + m->off_wte;
+  if (!accumulate) HIP_TRY(launch_fill_u32(gwte, 0, (long)V * d, s));
+  HIP_TRY(launch_embed_bwd(tokens, dx, gwte, N, d, V, s));
+  return GPT_OK;
+}
+
+size_t muon_workspace_bytes(const gpt_model* m) {
+  if (!m) return 0;
+  MuonGroup sq, tall;
+  muon_groups(*m, sq, tall);
+  const size_t a = plan_ns(sq.count, sq.x_rows, sq.x_cols, 0).total;
+  const size_t b = plan_ns(tall.count, tall.x_rows, tall.x_cols, 0).total;
+  return std::max(a, b);
+}
+
+gpt_status muon_step(gpt_model* m, float* params, uint16_t* params_bf16, const float* grads,
+                     float* momentum, float lr, float momentum_coef, const float* ns_coeffs,
+                     int32_t ns_steps, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!m || !params || !params_bf16 || !grads || !momentum || !ns_coeffs) return GPT_EINVAL;
+  if (ns_steps < 1 || ns_steps > 8) return GPT_EINVAL;
+  if (!workspace || workspace_bytes < muon_workspace_bytes(m)) return GPT_EWORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return GPT_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  g_prof_model = m;
+  MuonGroup groups[2];
+  muon_groups(*m, groups[0], groups[1]);
+  for (const MuonGroup& g : groups) {
+    const NsPlan p = plan_ns(g.count, g.x_rows, g.x_cols, 0);
+    float* part = reinterpret_cast<float*>(ws + p.part);
+    float* x32 = reinterpret_cast<float*>(ws + p.x32);
+    HIP_TRY(launch_muon_momentum(g, grads, momentum, momentum_coef, part, p.nb, s));
+    HIP_TRY(launch_muon_pack(g, momentum, part, p.nb, x32, reinterpret_cast<uint16_t*>(ws + p.xh0),
+                             reinterpret_cast<uint16_t*>(ws + p.xl0), s));
+    HIP_TRY(run_ns(ws, p, g.count, g.x_rows, g.x_cols, ns_coeffs, ns_steps, s));
+    HIP_TRY(launch_muon_update(g, x32, params, params_bf16, lr, s));
+  }
+  return GPT_OK;
+}
+
+gpt_status gpt_refresh_bf16(const gpt_model* m, const float* params, uint16_t* params_bf16,
+                            void* stream) {
+  if (!m || !params || !params_bf16) return GPT_EINVAL;
+  HIP_TRY(launch_f32_to_bf16(params, params_bf16, m->nparams, reinterpret_cast<hipStream_t>(stream)));
+  return GPT_OK;
+}
+
+gpt_status gpt_check(const gpt_model* m, void* workspace, void* stream) {
+  if (!m || !workspace) return GPT_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  HIP_TRY(hipStreamSynchronize(s));
+  int flag = 0;
+  HIP_TRY(hipMemcpy(&flag, workspace, sizeof(int), hipMemcpyDeviceToHost));
+  if (flag) {
+    const int zero = 0;
+    HIP_TRY(hipMemcpy(workspace, &zero, sizeof(int), hipMemcpyHostToDevice));
+    return GPT_ETOKEN;
+  }
+  return GPT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Step-level entry points
+// ---------------------------------------------------------------------------
+gpt_status gpt_op_gemm(int32_t M, int32_t N, int32_t K, int32_t batch, const uint16_t* A,
+                       int64_t lda, int64_t stride_a, int32_t a_kmajor, const uint16_t* B,
+                       int64_t ldb, int64_t stride_b, int32_t b_kmajor, void* C, int64_t ldc,
+                       int64_t stride_c, int32_t out_mode, void* stream) {
+  if (!A || !B || !C || M < 1 || N < 1 || K < 1 || batch < 1) return GPT_EINVAL;
+  if (N % 4 != 0 || ldc % 4 != 0) return GPT_ESHAPE;
+  if ((a_kmajor ? K : M) % 8 != 0 || (b_kmajor ? K : N) % 8 != 0) return GPT_ESHAPE;
+  if (lda % 8 != 0 || ldb % 8 != 0) return GPT_ESHAPE;
+  static const int modes[5] = {EPI_F32, EPI_F32_ACC, EPI_BF16, EPI_RELU_BF16, EPI_RESID_BF16};
+  if (out_mode < 0 || out_mode > 4) return GPT_EINVAL;
+  g_prof_model = nullptr;
+  GemmArgs g;
+  gemm_args_init(g);
+  g.a[0] = A; g.b[0] = B;
+  g.M = M; g.N = N; g.K = K;
+  g.lda = lda; g.ldb = ldb; g.sa = stride_a; g.sb = stride_b;
+  g.a_kmajor = a_kmajor ? 1 : 0; g.b_kmajor = b_kmajor ? 1 : 0;
+  g.c = C; g.ldc = ldc; g.sc = stride_c;
+  g.batch = batch;
+  g.epi = modes[out_mode];
+  g.alpha = 1.f;
+  g.beta = 1.f;
+  HIP_TRY(launch_gemm_prof(g, reinterpret_cast<hipStream_t>(stream)));
+  return GPT_OK;
+}
+
+gpt_status gpt_op_attention_fwd(const uint16_t* qkv, uint16_t* o, float* lse, int32_t batch,
+                                int32_t seq, int32_t heads, void* stream) {
+  if (!qkv || !o || !lse || batch < 1 || seq < 1 || heads < 1) return GPT_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  HIP_TRY(launch_attention_fwd(qkv, o, lse, batch, seq, heads, s));
+  return GPT_OK;
+}
+
+gpt_status gpt_op_attention_bwd(const uint16_t* qkv, const uint16_t* o, const float* lse,
+                                const uint16_t* dO, uint16_t* dqkv, float* scratch,
+                                int32_t batch, int32_t seq, int32_t heads, void* stream) {
+  if (!qkv || !o || !lse || !dO || !dqkv || !scratch || batch < 1 || seq < 1 || heads < 1)
+    return GPT_EINVAL;
+  HIP_TRY(launch_attention_bwd(qkv, o, lse, dO, dqkv, scratch, batch, seq, heads,
+                               reinterpret_cast<hipStream_t>(stream)));
+  return GPT_OK;
+}
+
+size_t gpt_op_ns_scratch_bytes(int32_t count, int32_t rows, int32_t cols) {
+  if (count < 1 || rows < 1 || cols < 1) return 0;
+  return plan_ns(count, rows, cols, 0).total;
+}
+
+gpt_status gpt_op_newton_schulz(float* X, int32_t count, int32_t rows, int32_t cols,
+                                const float* ns_coeffs, int32_t ns_steps, void* scratch,
+                                size_t scratch_bytes, void* stream) {
+  if (!X || !ns_coeffs || count < 1 || rows < 1 || cols < 1 || ns_steps < 1 || ns_steps > 8)
+    return GPT_EINVAL;
+  if (rows < cols || cols % 8 != 0 || rows % 8 != 0) return GPT_ESHAPE;
+  const NsPlan p = plan_ns(count, rows, cols, 0);
+  if (!scratch || scratch_bytes < p.total) return GPT_EWORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(scratch);
+  g_prof_model = nullptr;
+  float* x32 = reinterpret_cast<float*>(ws + p.x32);
+  const long n = (long)rows * cols;
+  HIP_TRY(hipMemcpyAsync(x32, X, (size_t)count * n * 4, hipMemcpyDeviceToDevice, s));
+  HIP_TRY(launch_ns_prepare(x32, reinterpret_cast<uint16_t*>(ws + p.xh0),
+                            reinterpret_cast<uint16_t*>(ws + p.xl0), count, n,
+                            reinterpret_cast<float*>(ws + p.part), p.nb, s));
+  HIP_TRY(run_ns(ws, p, count, rows, cols, ns_coeffs, ns_steps, s));
+  HIP_TRY(hipMemcpyAsync(X, x32, (size_t)count * n * 4, hipMemcpyDeviceToDevice, s));
+  return GPT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Launch timing
+// ---------------------------------------------------------------------------
+gpt_status gpt_profile_enable(gpt_model* m, int32_t enable) {
+  if (!m) return GPT_EINVAL;
+  m->prof_on = enable != 0;
+  m->prof_used = 0;
+  return GPT_OK;
+}
+
+gpt_status gpt_profile_read(gpt_model* m, int32_t category, double* ms, double* flops,
+                            int64_t* launches) {
+  if (!m || !ms || !flops || !launches || category < 0 || category >= PROF_NCAT) return GPT_EINVAL;
+  *ms = 0.0;
+  *flops = 0.0;
+  *launches = 0;
+  for (size_t i = 0; i < m->prof_used; ++i) {
+    ProfSlot& sl = m->prof[i];
+    if (sl.cat != category) continue;
+    HIP_TRY(hipEventSynchronize(sl.stop));
+    float t = 0.f;
+    HIP_TRY(hipEventElapsedTime(&t, sl.start, sl.stop));
+    *ms += t;
+    *flops += sl.flops;
+    *launches += 1;
+  }
+  return GPT_OK;
+}
+
+gpt_status gpt_profile_reset(gpt_model* m) {
+  if (!m) return GPT_EINVAL;
+  m->prof_used = 0;
+  return GPT_OK;
+}
+
+}  // extern "C"

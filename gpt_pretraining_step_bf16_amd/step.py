@@ -1,0 +1,68 @@
+"""Device buffers for repeated training steps (torch allocates, the HIP library computes).
+
+``TrainState`` owns the flat fp32 parameters, their bf16 shadow, gradients,
+Muon momentum and the two workspaces, laid out as the library's tensor table
+says. A step is ``fwd_bwd`` (loss + gradients) followed by ``muon``.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import binding
+
+
+class TrainState:
+    def __init__(self, depth: int, vocab: int, seq: int, batch: int, device="cuda"):
+        import torch
+
+        self.torch = torch
+        self.model = binding.GptModel(depth, vocab, seq)
+        self.batch, self.seq = batch, seq
+        self.device = device
+        n = self.model.num_params
+        self.tensors = self.model.tensors()
+        self.params = torch.zeros(n, dtype=torch.float32, device=device)
+        self.params_bf16 = torch.zeros(n, dtype=torch.int16, device=device)
+        self.grads = torch.zeros(n, dtype=torch.float32, device=device)
+        self.momentum = torch.zeros(n, dtype=torch.float32, device=device)
+        self.loss = torch.zeros(1, dtype=torch.float32, device=device)
+        self.ws = torch.empty(self.model.workspace_bytes(batch, seq), dtype=torch.uint8, device=device)
+        self.muon_ws = torch.empty(self.model.muon_workspace_bytes(), dtype=torch.uint8, device=device)
+
+    # -- host <-> device ------------------------------------------------------
+    def flatten(self, arrays: dict) -> np.ndarray:
+        flat = np.empty(self.model.num_params, dtype=np.float32)
+        for t in self.tensors:
+            a = arrays[t["name"]]
+            assert a.shape == (t["rows"], t["cols"]), (t["name"], a.shape)
+            flat[t["offset"]: t["offset"] + a.size] = a.ravel()
+        return flat
+
+    def unflatten(self, flat: np.ndarray) -> dict:
+        return {t["name"]: flat[t["offset"]: t["offset"] + t["rows"] * t["cols"]].reshape(t["rows"], t["cols"])
+                for t in self.tensors}
+
+    def load_weights(self, weights: dict):
+        self.params.copy_(self.torch.from_numpy(self.flatten(weights)))
+        self.model.refresh_bf16(self.params, self.params_bf16)
+
+    def load_momentum(self, momentum: dict):
+        self.momentum.copy_(self.torch.from_numpy(self.flatten(momentum)))
+
+    def load_grads(self, grads: dict):
+        self.grads.copy_(self.torch.from_numpy(self.flatten(grads)))
+
+    def to_host(self, t) -> dict:
+        return self.unflatten(t.detach().cpu().numpy())
+
+    # -- compute --------------------------------------------------------------
+    def fwd_bwd(self, tokens, targets, accumulate=False):
+        self.model.fwd_bwd(self.params_bf16, tokens, targets, self.loss, self.grads, self.ws,
+                           accumulate=accumulate)
+
+    def muon(self, lr, momentum_coef, ns_coeffs):
+        self.model.muon_step(self.params, self.params_bf16, self.grads, self.momentum, lr,
+                             momentum_coef, ns_coeffs, self.muon_ws)
+
+    def check(self) -> int:
+        return self.model.check(self.ws)

@@ -1,0 +1,205 @@
+/*
+ * gpt.h -- C ABI of the MI355X (gfx950) pretraining step of the
+ * depth-parameterised GPT: one forward + backward pass over a microbatch and
+ * one Muon update of the block matrices.
+ *
+ * Sources (cited by page title and section):
+ *   [CT50] dev.to, "Como treinar seu próprio ChatGPT por 50 dólares".
+ *   [HADA] GeekNews (hada.io) summary of the nanochat launch README.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Plain C types only. Device buffers are raw device pointers; `stream` is a
+ *   hipStream_t passed as void* (NULL = the null stream).
+ * - The caller allocates and owns every device buffer (parameters, bf16
+ *   shadow, gradients, momentum, tokens, loss, workspaces). The library never
+ *   allocates device memory and keeps no device state between calls; a
+ *   gpt_model is a host-side plan (shapes and the flat parameter layout).
+ * - Matrices are row-major [out, in] as in a bias-free Linear layer
+ *   ([CT50] "3. Gerenciamento de Precisão": weights are kept in full precision
+ *   and cast to the activation type on use). Flat buffers hold the tensors in
+ *   canonical order: wte; per layer wq, wk, wv, wo, wfc, wproj; lm_head.
+ * - bf16 buffers hold raw bfloat16 bits (uint16_t), round-to-nearest-even.
+ * - All compute calls are asynchronous on `stream`; results are valid after
+ *   the stream is synchronised. One model handle serves one stream at a time.
+ * - Host-side validation happens before any launch and returns a status; on a
+ *   non-OK status nothing was launched. Errors found on the device (a token
+ *   or target outside the vocabulary) set a flag in the first word of the
+ *   gpt_fwd_bwd workspace; each gpt_fwd_bwd call clears it first, and
+ *   gpt_check() reports it. Nothing crosses the ABI as a C++ exception.
+ */
+#ifndef GPT_STEP_GPT_H
+#define GPT_STEP_GPT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct gpt_model gpt_model;
+
+typedef enum {
+  GPT_OK = 0,
+  GPT_EINVAL = -1,     /* bad argument: null pointer, depth/vocab/seq/batch out of range */
+  GPT_ESHAPE = -2,     /* shape not supported (e.g. seq > the plan's max_seq) */
+  GPT_EHIP = -3,       /* a HIP runtime call failed */
+  GPT_ETOKEN = -4,     /* a token id or target outside [0, vocab) (target -1 = ignore) */
+  GPT_EWORKSPACE = -5  /* workspace missing or smaller than the *_workspace_bytes() value */
+} gpt_status;
+
+enum { GPT_KIND_EMB = 0, GPT_KIND_MATRIX = 1, GPT_KIND_LM_HEAD = 2 };
+
+typedef struct {
+  char name[32];   /* "wte", "h<l>.wq" ... "h<l>.wproj", "lm_head" */
+  int64_t offset;  /* element offset into every flat buffer (params, bf16, grads, momentum) */
+  int32_t rows;    /* out features (vocab for wte / lm_head) */
+  int32_t cols;    /* in features */
+  int32_t kind;    /* GPT_KIND_* */
+  int32_t layer;   /* block index, -1 for wte and lm_head */
+} gpt_tensor;
+
+/*
+ * Plan a model from the depth knob ([CT50] "Filosofia: Um Único Seletor Para
+ * Controlar Tudo": width, heads and the rest follow from --depth). The rule is
+ * not printed on the page; this library uses width d = 64*depth rounded up to
+ * a multiple of 128, heads H = d/128 of size 128, MLP hidden 4d.
+ *   depth   1..64
+ *   vocab   64..262144, multiple of 64 (the pages' tokenizer has 32768)
+ *   max_seq 1..16384, the longest sequence later calls may pass
+ * On success *out receives a handle to release with gpt_destroy().
+ */
+gpt_status gpt_create(int32_t depth, int32_t vocab, int32_t max_seq, gpt_model** out);
+void gpt_destroy(gpt_model* m);
+
+/* dims[6] <- {depth, width, heads, mlp_hidden, vocab, max_seq}. */
+gpt_status gpt_dims(const gpt_model* m, int32_t dims[6]);
+
+/* Total element count of the flat parameter layout (also of grads / momentum). */
+int64_t gpt_num_params(const gpt_model* m);
+int32_t gpt_num_tensors(const gpt_model* m);
+/* Describe tensor i (0 <= i < gpt_num_tensors) of the canonical order. */
+gpt_status gpt_tensor_info(const gpt_model* m, int32_t i, gpt_tensor* out);
+
+/* Bytes of device workspace gpt_fwd_bwd needs for `batch` sequences of length `seq`. */
+size_t gpt_workspace_bytes(const gpt_model* m, int32_t batch, int32_t seq);
+
+/*
+ * One forward and backward pass over a microbatch ([CT50] "1. Modelo GPT":
+ * untied token embedding, pre-norm blocks with RoPE, QK normalisation, causal
+ * attention and a ReLU^2 MLP, then the untied head and softmax cross-entropy).
+ *   params_bf16  device, [gpt_num_params] bf16 shadow of the fp32 parameters
+ *   tokens       device, int32 [batch, seq], ids in [0, vocab)
+ *   targets      device, int32 [batch, seq], ids in [0, vocab) or -1 (ignored)
+ *   loss         device, 1 float: mean cross-entropy over non-ignored targets
+ *   grads        device, fp32 [gpt_num_params], same layout as the parameters
+ *   accumulate   0: grads are overwritten; 1: grads are added to (gradient
+ *                accumulation over microbatches, as the single-GPU mode in
+ *                [HADA] "Requisitos do ambiente de computação" does)
+ *   workspace    device, >= gpt_workspace_bytes(m, batch, seq) bytes,
+ *                256-byte aligned; holds activations and the sticky error flag
+ * Ids outside the vocabulary set GPT_ETOKEN in the workspace flag; such tokens
+ * embed as zeros and such targets are ignored, so the call still completes.
+ */
+gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* params_bf16, const int32_t* tokens,
+                       const int32_t* targets, int32_t batch, int32_t seq, float* loss,
+                       float* grads, int32_t accumulate, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace muon_step needs. */
+size_t muon_workspace_bytes(const gpt_model* m);
+
+/*
+ * One Muon update of every block matrix ([CT50] "2. Otimizador Muon": 2-D
+ * matrices take momentum orthogonalised by a Newton-Schulz iteration
+ * A = X^T X, B = b A + c A A, X = a X + X B over a table of (a, b, c)).
+ * wte and lm_head belong to the page's AdamW group and are left unchanged.
+ *   params       device fp32 [gpt_num_params], updated in place
+ *   params_bf16  device bf16 shadow, refreshed for the updated matrices
+ *   grads        device fp32 gradients
+ *   momentum     device fp32 [gpt_num_params], M <- momentum_coef * M + G
+ *   ns_coeffs    HOST pointer to ns_steps rows of (a, b, c) floats
+ *   ns_steps     1..8
+ * Per matrix: X0 = M / (||M||_F + 1e-7), oriented so rows >= cols, ns_steps
+ * iterations, W <- W - lr * sqrt(max(1, rows/cols)) * X. The iteration runs
+ * with fp32 accumulation and fp32 master X; each matrix product is formed
+ * from bf16 hi/lo splits of its operands (three MFMA products).
+ */
+gpt_status muon_step(gpt_model* m, float* params, uint16_t* params_bf16, const float* grads,
+                     float* momentum, float lr, float momentum_coef, const float* ns_coeffs,
+                     int32_t ns_steps, void* workspace, size_t workspace_bytes, void* stream);
+
+/* params_bf16 <- round-to-nearest-even bf16 of params, every tensor. */
+gpt_status gpt_refresh_bf16(const gpt_model* m, const float* params, uint16_t* params_bf16,
+                            void* stream);
+
+/* Synchronise `stream`, then return the device error flag of a gpt_fwd_bwd
+ * workspace (GPT_OK or GPT_ETOKEN) from its most recent call, and clear it. */
+gpt_status gpt_check(const gpt_model* m, void* workspace, void* stream);
+
+const char* gpt_status_str(gpt_status s);
+
+/*
+ * Launch timing (measurement of [CT50] "Métricas para Monitorar": train/mfu
+ * and train/tok_per_sec need per-kernel time). When enabled, gpt_fwd_bwd and
+ * muon_step record a pair of HIP events on `stream` around every matrix
+ * product and attention launch (the events are host runtime objects the
+ * model creates once and reuses; no device memory). gpt_profile_read waits
+ * for the recorded events and sums, for one category, the elapsed time in
+ * milliseconds, the algorithmic FLOPs and the launch count since the last
+ * enable/reset. Categories: 0 projection / head / weight-gradient GEMMs,
+ * 1 attention forward, 2 attention backward (causal FLOPs, recompute not
+ * counted), 3 Newton-Schulz GEMMs (hi/lo products counted).
+ */
+gpt_status gpt_profile_enable(gpt_model* m, int32_t enable);
+gpt_status gpt_profile_reset(gpt_model* m);
+gpt_status gpt_profile_read(gpt_model* m, int32_t category, double* ms, double* flops,
+                            int64_t* launches);
+
+/*
+ * Step-level entry points. Each runs one step of the path above on caller
+ * buffers with the same kernels gpt_fwd_bwd / muon_step launch; the test
+ * suite uses them to compare single steps with the oracle.
+ */
+
+/* C[b] (op)= sum_k A[b](m,k) * B[b](n,k) in bf16 x bf16 -> fp32.
+ *   a_kmajor: 1 -> A element (m,k) at A[m*lda + k]; 0 -> at A[k*lda + m]
+ *   b_kmajor: 1 -> B element (n,k) at B[n*ldb + k]; 0 -> at B[k*ldb + n]
+ *   The contiguous dimension of each operand must be a multiple of 8 and
+ *   every row 16-byte aligned. N must be a multiple of 4.
+ *   out_mode 0: C fp32 = acc; 1: C fp32 += acc; 2: C bf16 = acc;
+ *            3: C bf16 = max(acc, 0); 4: C bf16 += acc (bf16 in place).
+ *   batch strides are in elements. */
+gpt_status gpt_op_gemm(int32_t M, int32_t N, int32_t K, int32_t batch, const uint16_t* A,
+                       int64_t lda, int64_t stride_a, int32_t a_kmajor, const uint16_t* B,
+                       int64_t ldb, int64_t stride_b, int32_t b_kmajor, void* C, int64_t ldc,
+                       int64_t stride_c, int32_t out_mode, void* stream);
+
+/* Causal attention forward over qkv [batch*seq, 3*heads*128] bf16 (q | k | v
+ * column blocks, 128 columns per head). Writes o [batch*seq, heads*128] bf16
+ * and lse [batch, heads, seq] fp32: the base-2 logarithm of the softmax
+ * normaliser sum_j 2^(s_ij), where s_ij = (q_i . k_j) * log2(e) / sqrt(128). */
+gpt_status gpt_op_attention_fwd(const uint16_t* qkv, uint16_t* o, float* lse, int32_t batch,
+                                int32_t seq, int32_t heads, void* stream);
+
+/* Causal attention backward: from qkv, o, lse (as written by the forward) and
+ * dO [batch*seq, heads*128] bf16, write dqkv [batch*seq, 3*heads*128] bf16.
+ * scratch: device, >= batch*heads*seq floats. */
+gpt_status gpt_op_attention_bwd(const uint16_t* qkv, const uint16_t* o, const float* lse,
+                                const uint16_t* dO, uint16_t* dqkv, float* scratch,
+                                int32_t batch, int32_t seq, int32_t heads, void* stream);
+
+/* Newton-Schulz on `count` fp32 matrices X [count, rows, cols] (rows >= cols)
+ * in place: X0 = X / (||X||_F + 1e-7), then ns_steps iterations with the
+ * host table ns_coeffs. scratch >= gpt_op_ns_scratch_bytes(count, rows, cols). */
+size_t gpt_op_ns_scratch_bytes(int32_t count, int32_t rows, int32_t cols);
+gpt_status gpt_op_newton_schulz(float* X, int32_t count, int32_t rows, int32_t cols,
+                                const float* ns_coeffs, int32_t ns_steps, void* scratch,
+                                size_t scratch_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPT_STEP_GPT_H */

@@ -1,0 +1,161 @@
+"""Whole-path parity on the GPU: gpt_fwd_bwd and muon_step against the oracle.
+
+Tolerances: loss |delta| <= 1e-2; every gradient tensor and every Muon update
+relative L2 <= 2e-2 (bf16 operands, fp32 accumulation against an fp64 oracle).
+Token handling is bit-exact: embedding-gradient rows of absent tokens are 0.
+"""
+import numpy as np
+import pytest
+
+from gpu_util import bits_to_f32, bf16_bits, log, rel_l2
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import oracle  # noqa: E402
+from gpt_pretraining_step_bf16_amd import synthetic as syn  # noqa: E402
+from gpt_pretraining_step_bf16_amd.step import TrainState  # noqa: E402
+
+LOSS_TOL = 1e-2
+REL_TOL = 2e-2
+
+
+def _run_case(depth, vocab, seq, batch, seed_w=0, seed_t=1, ignore=()):
+    log(f"fwd_bwd depth={depth} vocab={vocab} seq={seq} batch={batch}")
+    w = syn.init_weights(depth, vocab, seed=seed_w)
+    ids = syn.zipf_ids(batch, seq, vocab, seed=seed_t)
+    tok, tgt = syn.split_tokens(ids)
+    tgt = tgt.copy()
+    for (b, t) in ignore:
+        tgt[b, t] = -1
+    st = TrainState(depth, vocab, seq, batch)
+    st.load_weights(w)
+    tok_d = torch.from_numpy(tok).cuda()
+    tgt_d = torch.from_numpy(tgt).cuda()
+    st.fwd_bwd(tok_d, tgt_d)
+    torch.cuda.synchronize()
+    assert st.check() == 0
+    loss = float(st.loss.cpu()[0])
+    grads = st.to_host(st.grads)
+    w64 = {k: v.astype(np.float64) for k, v in w.items()}
+    ref_loss, ref_grads = oracle.forward_backward(w64, tok, tgt)
+    return st, tok, tgt, loss, grads, ref_loss, ref_grads
+
+
+def _assert_grads(grads, ref_grads, tok, vocab):
+    worst = []
+    for name, ref in ref_grads.items():
+        e = rel_l2(grads[name], ref)
+        worst.append((e, name))
+        assert e < REL_TOL, (name, e)
+    flat_g = np.concatenate([grads[k].ravel() for k in ref_grads])
+    flat_r = np.concatenate([ref_grads[k].ravel() for k in ref_grads])
+    assert rel_l2(flat_g, flat_r) < REL_TOL
+    absent = np.setdiff1d(np.arange(vocab), tok.ravel())
+    assert not np.any(grads["wte"][absent])
+    log(f"  worst grad rel-L2: {sorted(worst)[-3:]}")
+
+
+def test_tiny_fwd_bwd_matches_oracle():
+    cfg = syn.CONFIGS["tiny"]
+    st, tok, tgt, loss, grads, ref_loss, ref_grads = _run_case(cfg["depth"], cfg["vocab"], cfg["seq"],
+                                                                cfg["batch"])
+    log(f"  loss gpu={loss:.6f} oracle={ref_loss:.6f}")
+    assert abs(loss - ref_loss) <= LOSS_TOL
+    _assert_grads(grads, ref_grads, tok, cfg["vocab"])
+
+
+def test_ragged_fwd_bwd_with_ignored_targets():
+    # seq 200 is not a multiple of the 64/128/256 tiles; 3 sequences -> 600 tokens.
+    st, tok, tgt, loss, grads, ref_loss, ref_grads = _run_case(3, 2048, 200, 3, seed_w=5, seed_t=6,
+                                                                ignore=[(0, 0), (1, 199), (2, 50)])
+    log(f"  loss gpu={loss:.6f} oracle={ref_loss:.6f}")
+    assert abs(loss - ref_loss) <= LOSS_TOL
+    _assert_grads(grads, ref_grads, tok, 2048)
+
+
+def test_gradient_accumulation_adds():
+    cfg = syn.CONFIGS["tiny"]
+    w = syn.init_weights(cfg["depth"], cfg["vocab"], seed=0)
+    st = TrainState(cfg["depth"], cfg["vocab"], cfg["seq"], cfg["batch"])
+    st.load_weights(w)
+    outs = []
+    for seed in (1, 2):
+        tok, tgt = syn.split_tokens(syn.zipf_ids(cfg["batch"], cfg["seq"], cfg["vocab"], seed=seed))
+        st.fwd_bwd(torch.from_numpy(tok).cuda(), torch.from_numpy(tgt).cuda())
+        outs.append(st.grads.clone())
+    tok, tgt = syn.split_tokens(syn.zipf_ids(cfg["batch"], cfg["seq"], cfg["vocab"], seed=1))
+    st.fwd_bwd(torch.from_numpy(tok).cuda(), torch.from_numpy(tgt).cuda())
+    tok, tgt = syn.split_tokens(syn.zipf_ids(cfg["batch"], cfg["seq"], cfg["vocab"], seed=2))
+    st.fwd_bwd(torch.from_numpy(tok).cuda(), torch.from_numpy(tgt).cuda(), accumulate=True)
+    torch.cuda.synchronize()
+    want = (outs[0] + outs[1]).cpu().numpy()
+    got = st.grads.cpu().numpy()
+    assert rel_l2(got, want) < 1e-5
+
+
+def test_out_of_range_token_sets_flag():
+    cfg = syn.CONFIGS["tiny"]
+    st = TrainState(cfg["depth"], cfg["vocab"], cfg["seq"], cfg["batch"])
+    st.load_weights(syn.init_weights(cfg["depth"], cfg["vocab"], seed=0))
+    tok, tgt = syn.split_tokens(syn.zipf_ids(cfg["batch"], cfg["seq"], cfg["vocab"], seed=1))
+    tok = tok.copy()
+    tok[1, 7] = cfg["vocab"] + 3
+    st.fwd_bwd(torch.from_numpy(tok).cuda(), torch.from_numpy(tgt).cuda())
+    assert st.check() == -4  # GPT_ETOKEN
+    assert st.check() == 0   # cleared
+    tok[1, 7] = 0
+    st.fwd_bwd(torch.from_numpy(tok).cuda(), torch.from_numpy(tgt).cuda())
+    assert st.check() == 0
+
+
+def test_deterministic_loss_and_causal_invariance():
+    cfg = syn.CONFIGS["tiny"]
+    st = TrainState(cfg["depth"], cfg["vocab"], cfg["seq"], 1)
+    st.load_weights(syn.init_weights(cfg["depth"], cfg["vocab"], seed=0))
+    tok, tgt = syn.split_tokens(syn.zipf_ids(1, cfg["seq"], cfg["vocab"], seed=3))
+    # Only the target at position 10 counts: the loss then depends on tokens
+    # 0..10 alone, so changing tokens after 10 must leave it bit-identical.
+    tgt_one = np.full_like(tgt, -1)
+    tgt_one[0, 10] = tgt[0, 10]
+    st.fwd_bwd(torch.from_numpy(tok).cuda(), torch.from_numpy(tgt_one).cuda())
+    l1 = st.loss.clone()
+    st.fwd_bwd(torch.from_numpy(tok).cuda(), torch.from_numpy(tgt_one).cuda())
+    l2 = st.loss.clone()
+    tok2 = tok.copy()
+    tok2[0, 11:] = (tok2[0, 11:] + 101) % cfg["vocab"]
+    st.fwd_bwd(torch.from_numpy(tok2).cuda(), torch.from_numpy(tgt_one).cuda())
+    l3 = st.loss.clone()
+    torch.cuda.synchronize()
+    assert l1.item() == l2.item() == l3.item()
+
+
+def test_muon_step_matches_oracle_on_identical_inputs():
+    cfg = syn.CONFIGS["tiny"]
+    depth, vocab = cfg["depth"], cfg["vocab"]
+    log("muon tiny")
+    w = syn.init_weights(depth, vocab, seed=0)
+    g = syn.random_like_grads(depth, vocab, seed=7, scale=1e-2)
+    m0 = syn.random_like_grads(depth, vocab, seed=8, scale=1e-2)
+    st = TrainState(depth, vocab, cfg["seq"], cfg["batch"])
+    st.load_weights(w)
+    st.load_grads(g)
+    st.load_momentum(m0)
+    st.muon(syn.MUON_LR, syn.MUON_MOMENTUM, syn.NS_COEFFS)
+    torch.cuda.synchronize()
+    new_w = st.to_host(st.params)
+    new_m = st.to_host(st.momentum)
+    new_bf = st.params_bf16.cpu().numpy()
+    f64 = lambda d: {k: v.astype(np.float64) for k, v in d.items()}
+    ref_w, ref_m, ref_upd = oracle.muon_step(f64(w), f64(g), f64(m0), syn.MUON_LR, syn.MUON_MOMENTUM,
+                                             syn.NS_COEFFS)
+    for name in w:
+        if name in ("wte", "lm_head"):
+            np.testing.assert_array_equal(new_w[name], w[name])
+            continue
+        assert rel_l2(new_m[name], ref_m[name]) < 1e-6
+        upd = w[name].astype(np.float64) - new_w[name]
+        e = rel_l2(upd, ref_upd[name])
+        assert e < REL_TOL, (name, e)
+    # The bf16 shadow is the rounded fp32 master.
+    np.testing.assert_array_equal(new_bf, bf16_bits(st.params.cpu().numpy()))
