@@ -1,0 +1,484 @@
+// bf16 MFMA GEMM kernel for gfx950 (device code; instantiated per operand
+// layout in gemm_*.hip): every dense contraction of the step (QKV, O, MLP
+// and head projections forward and backward, weight gradients, Newton-Schulz).
+//
+// Design
+//  * Macro tile 256 x 256, 256 threads = 4 wave64s in a 2 x 2 grid, each wave
+//    owning a 128 x 128 sub-tile as 4 x 4 v_mfma_f32_32x32x16_bf16 tiles
+//    (256 fp32 accumulators per lane, held in AGPRs).
+//  * Operands go from HBM straight into LDS with 16-byte global_load_lds
+//    (no register staging), through a 4-stage ring of 32-wide k-blocks
+//    (4 x 32 KB): three k-blocks are in flight while one is consumed, which
+//    covers the load latency that a one-block register prefetch left exposed.
+//  * Each operand keeps its memory layout in LDS. A K-contiguous operand is
+//    staged [row][32 k] (64 B rows) and read with ds_read_b128. A K-strided
+//    operand (activations read along tokens for weight gradients, weights
+//    read along their out dimension) is staged [32 k][256 rows] (512 B rows)
+//    and read with ds_read_b64_tr_b16, the gfx950 transposing LDS read, which
+//    hands each lane the same 8-element k-run a K-contiguous read would.
+//    16-byte chunks are XOR-swizzled per row so fragment reads are
+//    bank-conflict free; the swizzle is applied by choosing which global
+//    chunk each lane fetches (lane l of a direct load lands at base + 16 l).
+//  * Fragments of the next 16-wide k-step are read before the MFMAs of the
+//    current one (sched_barrier keeps that order), so LDS latency hides
+//    under 16 MFMAs.
+//  * Partial tiles: rows past M / N load clamped (valid) addresses and are
+//    never stored; a k-block past the end of K is zeroed in LDS before use.
+//  * The MFMA computes the transposed tile (B fragment as the A input), so a
+//    lane holds 4 consecutive output columns, stored straight from the
+//    accumulators (8-byte bf16 / 16-byte fp32 stores).
+//  * Workgroup ids are remapped so consecutive tiles run on one XCD (ids are
+//    dealt round-robin over the 8 XCDs), then grouped 4 tile-rows at a time so
+//    an XCD's tiles share A rows and B columns in its L2.
+//  * Up to three K segments with their own operand bases are summed into one
+//    accumulator: Newton-Schulz uses it for hi/lo split products.
+#pragma once
+
+#include "common.h"
+#include "kernels.h"
+
+namespace gemm_impl {
+
+constexpr int BM = 256;
+constexpr int BN = 256;
+constexpr int BKD = 32;                 // k per stage
+constexpr int NST = 4;                  // stages in the ring
+constexpr int NTHR = 256;
+constexpr int OP_BYTES = BM * BKD * 2;  // one operand's stage: 16 KB
+constexpr int STAGE_BYTES = 2 * OP_BYTES;
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+#define LDS_V4S(p) ((__attribute__((address_space(3))) v4s*)(p))
+
+__device__ __forceinline__ uint32_t sq2(uint32_t w) {
+  float lo = bf_lo(w), hi = bf_hi(w);
+  return pack_bf2(lo * lo, hi * hi);
+}
+
+// Byte offset of (row r, 16-byte k-chunk c) in a K-contiguous stage [256][32].
+__device__ __forceinline__ int koff(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+// Byte offset of (k-row kr, 16-byte row-chunk c) in a K-strided stage [32][256].
+__device__ __forceinline__ int toff(int kr, int c) { return kr * 512 + ((c ^ ((kr & 3) << 2)) << 4); }
+
+// LDS byte address of a pointer into shared memory, as a wave-uniform value.
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p);
+}
+
+// One 16-byte-per-lane direct load: lane l's 16 bytes at gsrc land at
+// LDS lds_base + 16 l. Issued from asm so that the compiler does not add a
+// full vmcnt(0) drain before every transposing LDS read (it cannot tell
+// which LDS bytes a direct load writes); the ring's explicit vmcnt waits
+// and barriers order these loads instead. M0 carries the LDS base and is
+// restored afterwards. The asm has no output registers.
+__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gsrc), "s"(lds_base)
+      : "memory");
+}
+
+// Issue 1 KB block `blk` (0..15) of one operand's k-block [k0, k0 + 32) into
+// an LDS stage buffer; the 4 waves issue blocks 4 wave .. 4 wave + 3.
+template <bool KMAJ>
+__device__ __forceinline__ void issue_one(const uint16_t* __restrict__ base, long ld, int row0,
+                                          int rows, int k0, int kend, char* lds_op, int blk,
+                                          int lane) {
+  {
+    const uint16_t* src;
+    if (KMAJ) {
+      // 1 KB = rows 16 blk .. +15, 64 B each; lane l -> row 16 blk + l/4, slot l%4.
+      const int r = 16 * blk + (lane >> 2);
+      const int c = (lane & 3) ^ ((r >> 2) & 3);
+      const int gr = min(row0 + r, rows - 1);
+      const int kk = min(k0 + 8 * c, kend - 8);
+      src = base + (long)gr * ld + kk;
+    } else {
+      // 1 KB = k-rows 2 blk, 2 blk + 1, 512 B each; lane l -> k-row 2 blk + l/32, slot l%32.
+      const int kr = 2 * blk + (lane >> 5);
+      const int c = (lane & 31) ^ ((kr & 3) << 2);
+      const int gk = min(k0 + kr, kend - 1);
+      const int gm = min(row0 + 8 * c, rows - 8);
+      src = base + (long)gk * ld + gm;
+    }
+    dma16(src, lds_addr(lds_op + blk * 1024));
+  }
+}
+
+template <bool KMAJ>
+__device__ __forceinline__ void issue_operand(const uint16_t* __restrict__ base, long ld, int row0,
+                                              int rows, int k0, int kend, char* lds_op, int wave,
+                                              int lane) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) issue_one<KMAJ>(base, ld, row0, rows, k0, kend, lds_op, wave * 4 + j, lane);
+}
+
+// Zero the k-range [kvalid, 32) of one operand's stage (tail k-block).
+template <bool KMAJ>
+__device__ __forceinline__ void zero_tail(char* lds_op, int kvalid, int tid) {
+  if (KMAJ) {
+    // 256 rows x 4 chunks; chunk c holds k 8c..8c+7.
+    for (int i = tid; i < BM * 4; i += NTHR) {
+      const int r = i >> 2, c = i & 3;
+      if (8 * c >= kvalid) *reinterpret_cast<uint4*>(lds_op + koff(r, c)) = make_uint4(0, 0, 0, 0);
+    }
+  } else {
+    for (int i = tid; i < BKD * 32; i += NTHR) {
+      const int kr = i >> 5, c = i & 31;
+      if (kr >= kvalid) *reinterpret_cast<uint4*>(lds_op + toff(kr, c)) = make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+// 32 x 16 fragment (rows rb + lane%32, k-step ks of the stage) as 8 bf16.
+template <bool KMAJ>
+__device__ __forceinline__ bf16x8 read_frag(const char* lds_op, int rb, int ks, int lane) {
+  if (KMAJ) {
+    const int r = rb + (lane & 31);
+    const int c = 2 * ks + (lane >> 5);
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(lds_op + koff(r, c)));
+  } else {
+    // Group g = lane/16 covers rows rb + 16 (g & 1) .. +15 and k 16 ks + 8 (g >> 1) .. +7.
+    // Group-lane p addresses k-row (base + p/4) at row offset 4 (p % 4); two reads
+    // (k base and k base + 4) give the lane's 8 k values for its row.
+    const int g = lane >> 4, p = lane & 15;
+    const int m = rb + 16 * (g & 1) + 4 * (p & 3);
+    const int kr = 16 * ks + 8 * (g >> 1) + (p >> 2);
+    const int c = m >> 3, within = (m & 7) * 2;
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_V4S(lds_op + toff(kr, c) + within));
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_V4S(lds_op + toff(kr + 4, c) + within));
+    const uint2 a = __builtin_bit_cast(uint2, lo);
+    const uint2 b = __builtin_bit_cast(uint2, hi);
+    return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+  }
+}
+
+__device__ __forceinline__ bf16x8 square_frag(bf16x8 f) {
+  uint4 u = __builtin_bit_cast(uint4, f);
+  u = make_uint4(sq2(u.x), sq2(u.y), sq2(u.z), sq2(u.w));
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// Wait until at most `n` of this wave's direct loads are outstanding (they
+// complete in issue order), then barrier. Both are compiler memory barriers,
+// so no LDS access moves across them.
+__device__ __forceinline__ void ring_sync(int n) {
+  if (n >= 16) {
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  } else if (n >= 8) {
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  asm volatile("s_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ void store_bf16x4(void* p, float v0, float v1, float v2, float v3) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf2(v0, v1), pack_bf2(v2, v3));
+}
+
+// hi = bf16(v), lo = bf16(v - hi)
+__device__ __forceinline__ void store_hilo4(void* ph, void* pl, const float* v) {
+  float hi[4], lo[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    hi[r] = bf2f(f2bf(v[r]));
+    lo[r] = v[r] - hi[r];
+  }
+  store_bf16x4(ph, hi[0], hi[1], hi[2], hi[3]);
+  store_bf16x4(pl, lo[0], lo[1], lo[2], lo[3]);
+}
+
+__device__ __forceinline__ void load_bf16x4(const void* p, float* v) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  v[0] = bf_lo(u.x);
+  v[1] = bf_hi(u.x);
+  v[2] = bf_lo(u.y);
+  v[3] = bf_hi(u.y);
+}
+
+// Epilogue of one output group C(m, n..n+3) for a compile-time mode.
+template <int E>
+__device__ __forceinline__ void epi4(const GemmArgs& p, int bi, int si, int m, int n, const float* v) {
+  const long off = (long)bi * p.sc + (long)m * p.ldc + n;
+  const long doff = (long)bi * p.sd + (long)m * p.ldd + n;
+  if constexpr (E == EPI_F32) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.c) + off) =
+        make_float4(p.alpha * v[0], p.alpha * v[1], p.alpha * v[2], p.alpha * v[3]);
+  } else if constexpr (E == EPI_F32_ACC) {
+    float* c = reinterpret_cast<float*>(p.c) + off;
+    float4 o = *reinterpret_cast<const float4*>(c);
+    o.x = p.beta * o.x + p.alpha * v[0];
+    o.y = p.beta * o.y + p.alpha * v[1];
+    o.z = p.beta * o.z + p.alpha * v[2];
+    o.w = p.beta * o.w + p.alpha * v[3];
+    *reinterpret_cast<float4*>(c) = o;
+  } else if constexpr (E == EPI_BF16) {
+    store_bf16x4(reinterpret_cast<uint16_t*>(p.c) + off, p.alpha * v[0], p.alpha * v[1], p.alpha * v[2],
+                 p.alpha * v[3]);
+  } else if constexpr (E == EPI_RELU_BF16) {
+    store_bf16x4(reinterpret_cast<uint16_t*>(p.c) + off, fmaxf(v[0], 0.f), fmaxf(v[1], 0.f),
+                 fmaxf(v[2], 0.f), fmaxf(v[3], 0.f));
+  } else if constexpr (E == EPI_RESID_BF16) {
+    uint16_t* c = reinterpret_cast<uint16_t*>(p.c) + off;
+    float o[4];
+    load_bf16x4(c, o);
+    store_bf16x4(c, o[0] + v[0], o[1] + v[1], o[2] + v[2], o[3] + v[3]);
+  } else if constexpr (E == EPI_DRELU2_BF16) {
+    // d relu(u)^2 / du = 2 relu(u) = 2 sqrt(h), h = relu(u)^2 as stored.
+    float hh[4];
+    load_bf16x4(reinterpret_cast<const uint16_t*>(p.d) + doff, hh);
+    store_bf16x4(reinterpret_cast<uint16_t*>(p.c) + off, 2.f * v[0] * sqrtf(hh[0]), 2.f * v[1] * sqrtf(hh[1]),
+                 2.f * v[2] * sqrtf(hh[2]), 2.f * v[3] * sqrtf(hh[3]));
+  } else if constexpr (E == EPI_RELU2_BF16) {
+    const float r0 = fmaxf(v[0], 0.f), r1 = fmaxf(v[1], 0.f), r2 = fmaxf(v[2], 0.f), r3 = fmaxf(v[3], 0.f);
+    store_bf16x4(reinterpret_cast<uint16_t*>(p.c) + off, r0 * r0, r1 * r1, r2 * r2, r3 * r3);
+  } else if constexpr (E == EPI_SPLITK) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.c) + off + (long)si * p.s_split) =
+        make_float4(v[0], v[1], v[2], v[3]);
+  } else if constexpr (E == EPI_HILO) {
+    float w[4] = {p.alpha * v[0], p.alpha * v[1], p.alpha * v[2], p.alpha * v[3]};
+    store_hilo4(reinterpret_cast<uint16_t*>(p.c) + off, reinterpret_cast<uint16_t*>(p.c2) + off, w);
+  } else if constexpr (E == EPI_NS_POLY) {
+    float h[4], l[4], w[4];
+    load_bf16x4(reinterpret_cast<const uint16_t*>(p.d) + doff, h);
+    load_bf16x4(reinterpret_cast<const uint16_t*>(p.d2) + doff, l);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) w[r] = p.alpha * v[r] + p.beta * (h[r] + l[r]);
+    store_hilo4(reinterpret_cast<uint16_t*>(p.c) + off, reinterpret_cast<uint16_t*>(p.c2) + off, w);
+  } else if constexpr (E == EPI_NS_UPDATE) {
+    const float4 x = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.d) + doff);
+    float w[4] = {p.alpha * v[0] + p.beta * x.x, p.alpha * v[1] + p.beta * x.y,
+                  p.alpha * v[2] + p.beta * x.z, p.alpha * v[3] + p.beta * x.w};
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.c3) + doff) = make_float4(w[0], w[1], w[2], w[3]);
+    store_hilo4(reinterpret_cast<uint16_t*>(p.c) + off, reinterpret_cast<uint16_t*>(p.c2) + off, w);
+  }
+}
+
+// Store a finished 256 x 256 tile straight from the accumulators.
+// acc[i][j][4g + r] is C(m, n) with m = m0 + wm*128 + i*32 + lane%32 and
+// n = n0 + wn*128 + j*32 + 8g + 4*(lane/32) + r.
+template <int E>
+__device__ __forceinline__ void store_tile(const GemmArgs& p, const f32x16 (&acc)[4][4], int bi, int si,
+                                           int m0, int n0, int wm, int wn, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + wm * 128 + i * 32 + (lane & 31);
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * 128 + j * 32 + 8 * g + 4 * (lane >> 5);
+        if (n < p.N) {
+          const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                              acc[i][j][4 * g + 3]};
+          epi4<E>(p, bi, si, m, n, v);
+        }
+      }
+  }
+}
+
+template <bool AK, bool BK_, int SQ, int EPI>
+__global__ void __launch_bounds__(NTHR, 1) gemm_bf16_kernel(const GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+
+  // Tile coordinates: XCD-aware remap, then grouped order along M.
+  const int tiles_m = (p.M + BM - 1) / BM;
+  const int tiles_n = (p.N + BN - 1) / BN;
+  const int ntiles = tiles_m * tiles_n;
+  int bid = blockIdx.x;
+  if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);
+  constexpr int GM = 4;
+  const int group = bid / (GM * tiles_n);
+  const int first_m = group * GM;
+  const int gm = min(tiles_m - first_m, GM);
+  const int in_group = bid - group * GM * tiles_n;
+  const int tm = first_m + in_group % gm;
+  const int tn = in_group / gm;
+  const int m0 = tm * BM;
+  const int n0 = tn * BN;
+
+  const int z = blockIdx.y;
+  const int bi = z / p.splits;
+  const int si = z - bi * p.splits;
+  const int kbeg = si * p.k_chunk;
+  const int kend = min(p.K, kbeg + p.k_chunk);
+  const int kiters = (kend - kbeg + BKD - 1) / BKD;
+  const int nk = kiters * p.nseg;
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  auto stage_a = [&](int it) { return smem + (it % NST) * STAGE_BYTES; };
+  auto issue = [&](int it) {
+    const int seg = it / kiters;
+    const int k0 = kbeg + (it - seg * kiters) * BKD;
+    char* st = stage_a(it);
+    issue_operand<AK>(p.a[seg] + (long)bi * p.sa, p.lda, m0, p.M, k0, kend, st, wave, lane);
+    issue_operand<BK_>(p.b[seg] + (long)bi * p.sb, p.ldb, n0, p.N, k0, kend, st + OP_BYTES, wave, lane);
+  };
+
+  struct Frags {
+    bf16x8 a[4], b[4];
+  };
+  auto read_frags = [&](int it, int ks, Frags& f) {
+    const char* st = stage_a(it);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f.a[i] = read_frag<AK>(st, wm * 128 + i * 32, ks, lane);
+      if (SQ == 1) f.a[i] = square_frag(f.a[i]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f.b[j] = read_frag<BK_>(st + OP_BYTES, wn * 128 + j * 32, ks, lane);
+      if (SQ == 2) f.b[j] = square_frag(f.b[j]);
+    }
+  };
+  auto mfma_step = [&](const Frags& f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+  };
+
+  // Interleave a k-step's 16 MFMAs with the NR LDS reads of the next
+  // fragments (NR = 8 / 12 / 16 by operand layout), so that fewer than 16
+  // reads are ever outstanding (the LDS counter tracks 15) and their latency
+  // hides under the MFMAs.
+  constexpr int NR = (AK ? 4 : 8) + (BK_ ? 4 : 8);
+  auto interleave = [&]() {
+    // mask 0x100: one DS read; mask 0x008: MFMAs.
+    if constexpr (NR == 8) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      }
+    } else if constexpr (NR == 12) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+    }
+  };
+  // Zero the part of k-block `it` past the end of K (tail block only).
+  auto tail_fix = [&](int it) {
+    const int seg = it / kiters;
+    const int kvalid = kend - (kbeg + (it - seg * kiters) * BKD);
+    if (kvalid < BKD) {
+      zero_tail<AK>(stage_a(it), kvalid, tid);
+      zero_tail<BK_>(stage_a(it) + OP_BYTES, kvalid, tid);
+      __syncthreads();
+    }
+  };
+  // Number of k-blocks issued after block j once blocks 0..last are issued.
+  auto pending_after = [&](int j, int last) { return max(0, min(nk - 1, last) - j) * 8; };
+
+  // Ring of NST k-blocks, one barrier per iteration, placed mid-iteration:
+  //   iteration it: MFMAs of k-step 0 of block it (reads of its k-step 1
+  //   interleaved) | wait for block it+1, barrier, issue block it+NST-1 into
+  //   the slot of block it-1 | MFMAs of k-step 1 of block it (reads of k-step
+  //   0 of block it+1 interleaved).
+  // Every read of block it-1 precedes the previous barrier, so its slot is
+  // free; block it+1 is visible to all waves after this barrier.
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < nk) issue(s);
+  Frags f0, f1;
+  if (nk > 0) {
+    ring_sync(pending_after(0, NST - 2));
+    tail_fix(0);
+    read_frags(0, 0, f0);
+  }
+  for (int it = 0; it < nk; ++it) {
+    read_frags(it, 1, f1);
+    mfma_step(f0);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    if (it + 1 < nk) {
+      ring_sync(pending_after(it + 1, it + NST - 2));
+      tail_fix(it + 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // Phase B in 8 chunks: one direct load (4 of A, then 4 of B), one
+    // fragment of block it+1 and two MFMAs on k-step 1 of block it per
+    // chunk, so the in-order wave never stalls on a burst of loads while the
+    // MFMA pipe drains. Past the last block the fragment reads hit a stale
+    // slot and are unused.
+    const bool more = it + NST - 1 < nk;
+    const int nx = it + NST - 1;
+    const int nseg_i = nx / kiters;
+    const int nk0 = kbeg + (nx - nseg_i * kiters) * BKD;
+    const uint16_t* na = p.a[more ? nseg_i : 0] + (long)bi * p.sa;
+    const uint16_t* nb = p.b[more ? nseg_i : 0] + (long)bi * p.sb;
+    char* nst = stage_a(nx);
+    const char* rst = stage_a(it + 1);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (more) {
+        if (q < 4) {
+          issue_one<AK>(na, p.lda, m0, p.M, nk0, kend, nst, wave * 4 + q, lane);
+        } else {
+          issue_one<BK_>(nb, p.ldb, n0, p.N, nk0, kend, nst + OP_BYTES, wave * 4 + q - 4, lane);
+        }
+      }
+      if (q < 4) {
+        f0.a[q] = read_frag<AK>(rst, wm * 128 + q * 32, 0, lane);
+        if (SQ == 1) f0.a[q] = square_frag(f0.a[q]);
+      } else {
+        f0.b[q - 4] = read_frag<BK_>(rst + OP_BYTES, wn * 128 + (q - 4) * 32, 0, lane);
+        if (SQ == 2) f0.b[q - 4] = square_frag(f0.b[q - 4]);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int t = 2 * q + u;
+        acc[t >> 2][t & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1.b[t & 3], f1.a[t >> 2],
+                                                                     acc[t >> 2][t & 3], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __syncthreads();
+
+  store_tile<EPI>(p, acc, bi, si, m0, n0, wm, wn, lane);
+}
+
+}  // namespace gemm_impl
+
+// Launch one instantiation: one workgroup per 256 x 256 tile and (batch, split).
+#define GEMM_LAUNCH(AK, BK, SQ, EPI) \
+  hipLaunchKernelGGL((gemm_impl::gemm_bf16_kernel<AK, BK, SQ, EPI>), grid, dim3(gemm_impl::NTHR), 0, s, g)

@@ -149,7 +149,7 @@ FwdPlan plan_fwd(const gpt_model& m, int B, int T) {
   p.lse = lc.take(N * H * 4);
   p.xn2 = lc.take(N * d * 2);
   p.rstd2 = lc.take(N * 4);
-  p.r = lc.take(N * F * 2);
+  p.r = lc.take(N * F * 2);  // h = relu(u)^2, bf16
   p.layer_bytes = lc.cur;
   const size_t layers_base = c.take(p.layer_bytes * m.depth);
   p.xn1 += layers_base;
@@ -352,7 +352,7 @@ hipError_t gemm_nn(const uint16_t* A, long lda, const uint16_t* B, long ldb, int
 
 // Weight gradient: G[M,N] (+)= sum_t A[t][m] * B[t][n], A stored [K][M], B [K][N].
 hipError_t gemm_wgrad(const uint16_t* A, long lda, const uint16_t* B, long ldb, int M, int N, long K,
-                      float* G, int accumulate, int square_b, float* part, hipStream_t s) {
+                      float* G, int accumulate, float* part, hipStream_t s) {
   const SplitK sk = plan_splitk(M, N, K);
   GemmArgs g;
   gemm_args_init(g);
@@ -360,7 +360,6 @@ hipError_t gemm_wgrad(const uint16_t* A, long lda, const uint16_t* B, long ldb, 
   g.M = M; g.N = N; g.K = (int)K;
   g.lda = lda; g.ldb = ldb;
   g.a_kmajor = 0; g.b_kmajor = 0;
-  g.square = square_b ? 2 : 0;
   if (sk.splits > 1) {
     g.c = part; g.ldc = N;
     g.splits = sk.splits; g.k_chunk = sk.k_chunk;
@@ -538,19 +537,9 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
     }
     HIP_TRY(gemm_nt(o, d, wo, d, (int)N, d, d, x, d, EPI_RESID_BF16, s));
     HIP_TRY(launch_rmsnorm_fwd(x, xn2, rstd2, N, d, s));
-    HIP_TRY(gemm_nt(xn2, d, wfc, d, (int)N, F, d, r, F, EPI_RELU_BF16, s));
-    {
-      GemmArgs g;
-      gemm_args_init(g);
-      g.a[0] = r; g.b[0] = wproj;
-      g.M = (int)N; g.N = d; g.K = F;
-      g.lda = F; g.ldb = F;
-      g.a_kmajor = 1; g.b_kmajor = 1;
-      g.square = 1;
-      g.c = x; g.ldc = d;
-      g.epi = EPI_RESID_BF16;
-      HIP_TRY(launch_gemm_prof(g, s));
-    }
+    // h = relu(u)^2 is stored once; the down projection reads it directly.
+    HIP_TRY(gemm_nt(xn2, d, wfc, d, (int)N, F, d, r, F, EPI_RELU2_BF16, s));
+    HIP_TRY(gemm_nt(r, F, wproj, F, (int)N, d, F, x, d, EPI_RESID_BF16, s));
   }
   HIP_TRY(launch_rmsnorm_fwd(x, xnf, rstdf, N, d, s));
 
@@ -601,20 +590,20 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
     const uint16_t* r = reinterpret_cast<const uint16_t*>(lay(p.r, l));
     // MLP: x_out = x_mid + relu(u)^2 Wproj^T
     HIP_TRY(gemm_nn(dxb, d, wproj, F, (int)N, F, d, du, F, EPI_DRELU2_BF16, s, r, F));
-    HIP_TRY(gemm_wgrad(dxb, d, r, F, d, F, N, gproj, accumulate, 1, part, s));
+    HIP_TRY(gemm_wgrad(dxb, d, r, F, d, F, N, gproj, accumulate, part, s));
     HIP_TRY(gemm_nn(du, F, wfc, d, (int)N, d, F, dxn, d, EPI_F32, s));
-    HIP_TRY(gemm_wgrad(du, F, xn2, d, F, d, N, gfc, accumulate, 0, part, s));
+    HIP_TRY(gemm_wgrad(du, F, xn2, d, F, d, N, gfc, accumulate, part, s));
     HIP_TRY(launch_rmsnorm_bwd(dxn, xn2, rstd2, dx, dxb, N, d, 1, s));
     // Attention: x_mid = x_in + o Wo^T
     HIP_TRY(gemm_nn(dxb, d, wo, d, (int)N, d, d, dO, d, EPI_BF16, s));
-    HIP_TRY(gemm_wgrad(dxb, d, o, d, d, d, N, go, accumulate, 0, part, s));
+    HIP_TRY(gemm_wgrad(dxb, d, o, d, d, d, N, go, accumulate, part, s));
     {
       ProfScope ps(m, s, PROF_ATTN_BWD, 10.0 * batch * H * 128.0 * T * (T + 1) / 2.0);
       HIP_TRY(launch_attention_bwd(qkv, o, lse, dO, dqkv, delta, batch, T, H, s));
     }
     HIP_TRY(launch_qknorm_rope_bwd(dqkv, qkv, rstdqk, cs, N, T, H, s));
     HIP_TRY(gemm_nn(dqkv, 3L * d, wqkv, d, (int)N, d, 3 * d, dxn, d, EPI_F32, s));
-    HIP_TRY(gemm_wgrad(dqkv, 3L * d, xn1, d, 3 * d, d, N, gqkv, accumulate, 0, part, s));
+    HIP_TRY(gemm_wgrad(dqkv, 3L * d, xn1, d, 3 * d, d, N, gqkv, accumulate, part, s));
     HIP_TRY(launch_rmsnorm_bwd(dxn, xn1, rstd1, dx, dxb, N, d, 1, s));
   }
 

@@ -13,11 +13,12 @@ enum GemmEpilogue {
   EPI_BF16 = 2,         // C bf16 = alpha*acc
   EPI_RELU_BF16 = 3,    // C bf16 = max(acc, 0)
   EPI_RESID_BF16 = 4,   // C bf16 = C + acc (in place)
-  EPI_DRELU2_BF16 = 5,  // C bf16 = acc * 2 * D (D bf16, same shape as C, ldd)
+  EPI_DRELU2_BF16 = 5,  // C bf16 = acc * 2 * sqrt(D) (D = relu(u)^2 bf16, same shape as C, ldd)
   EPI_SPLITK = 6,       // C f32 [split] = acc (partials, reduced later)
   EPI_HILO = 7,         // v = alpha*acc -> C bf16 hi(v), C2 bf16 lo(v)
   EPI_NS_POLY = 8,      // v = alpha*acc + beta*(D + D2) (D, D2 bf16 hi/lo) -> C hi, C2 lo
   EPI_NS_UPDATE = 9,    // v = alpha*acc + beta*D (D f32) -> C3 f32 v, C hi, C2 lo
+  EPI_RELU2_BF16 = 10,  // C bf16 = max(acc, 0)^2
 };
 
 struct GemmArgs {
@@ -28,7 +29,7 @@ struct GemmArgs {
   long lda, ldb;         // leading dimensions (elements)
   long sa, sb;           // batch strides (elements)
   int a_kmajor, b_kmajor;
-  int square;            // 1: A is squared on load, 2: B is squared on load
+  int square;            // must be 0 (no operand transform on load)
   void* c;
   long ldc, sc;
   void* c2;
@@ -113,3 +114,10 @@ hipError_t launch_muon_update(const MuonGroup& g, const float* x32, float* param
 hipError_t launch_ns_prepare(float* x32, uint16_t* xh, uint16_t* xl, int count, long n,
                              float* partials, int blocks_per_mat, hipStream_t s);
 hipError_t launch_split_hilo(const float* x32, uint16_t* xh, uint16_t* xl, long n, hipStream_t s);
+
+// Per-layout GEMM instantiation launchers (gemm_*.hip); grid is the
+// persistent grid chosen by launch_gemm.
+hipError_t launch_gemm_kk_fwd(const GemmArgs& g, dim3 grid, hipStream_t s);
+hipError_t launch_gemm_kk_aux(const GemmArgs& g, dim3 grid, hipStream_t s);
+hipError_t launch_gemm_kt(const GemmArgs& g, dim3 grid, hipStream_t s);
+hipError_t launch_gemm_tt(const GemmArgs& g, dim3 grid, hipStream_t s);
