@@ -43,10 +43,17 @@ constexpr int NTHR = 256;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Row-major [rows][128] tile in 16-byte chunks (16 per row), swizzled.
-__device__ __forceinline__ int rswz(int row, int chunk) { return row * 16 + (chunk ^ (row & 7)); }
-// Transposed [128 dims][64 rows] tile in 8-byte units of 4 rows (16 per dim).
+// Row-major [rows][128] tile in 16-byte chunks (16 per row), swizzled so the
+// 16 lanes a 256-byte LDS cycle serves (16 rows, same logical chunk) hit 16
+// distinct chunk positions.
+__device__ __forceinline__ int rswz(int row, int chunk) { return row * 16 + (chunk ^ (row & 15)); }
+// Transposed [128 dims][64 rows] tile in 8-byte units of 4 rows (16 per dim),
+// with the unit position rotated by the dim so that consecutive dims reading
+// the same logical unit land on different banks (measured best of the
+// row/dim-parity variants).
 __device__ __forceinline__ int tswz(int dim, int unit) { return dim * 16 + (unit ^ (dim & 15)); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Load a [64 rows][128] bf16 block (rows r0.. of a strided buffer) as 4 rows x
 // 8 columns per thread: rows 4*(t%16)+i, columns 8*(t/16)..+7.
@@ -195,26 +202,40 @@ __global__ void __launch_bounds__(NTHR, 2)
       }
       // s[t][v]: key kb*64 + 32t + 8(v/4) + 4hl + v%4, query qpos.
       float mloc = -INFINITY;
+      // Masking is needed only where the block reaches past the wave's first
+      // query (causal diagonal) or past the end of the sequence.
+      const bool need_mask = (kb * KB + KB - 1 > q0) || (kb * KB + KB > T);
+      if (need_mask) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = kb * KB + 32 * t + 8 * (v >> 2) + 4 * hl + (v & 3);
-          float x = s[t][v] * sc;
-          if (key > qpos || key >= T) x = -INFINITY;
-          s[t][v] = x;
-          mloc = fmaxf(mloc, x);
-        }
+          for (int v = 0; v < 16; ++v) {
+            const int key = kb * KB + 32 * t + 8 * (v >> 2) + 4 * hl + (v & 3);
+            float x = s[t][v] * sc;
+            if (key > qpos || key >= T) x = -INFINITY;
+            s[t][v] = x;
+            mloc = fmaxf(mloc, x);
+          }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const float x = s[t][v] * sc;
+            s[t][v] = x;
+            mloc = fmaxf(mloc, x);
+          }
+      }
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
       const float m_new = fmaxf(m_run, mloc);
       const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(m_run - m_ref);
+      const float alpha = fast_exp2(m_run - m_ref);
       float lsum = 0.f;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const float pv = exp2f(s[t][v] - m_ref);
+          const float pv = fast_exp2(s[t][v] - m_ref);
           s[t][v] = pv;
           lsum += pv;
         }
@@ -392,6 +413,9 @@ __global__ void __launch_bounds__(NTHR, 1)
         }
       }
       // s[t][v]: query qb*64 + 32t + 8(v/4) + 4hl + v%4, key kpos.
+      // Mask where some query of the block precedes a key of the wave, or the
+      // block runs past the end of the sequence.
+      const bool need_mask = (qb * QBW < k0 + 31) || (qb * QBW + QBW > T);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -405,8 +429,8 @@ __global__ void __launch_bounds__(NTHR, 1)
           for (int r = 0; r < 4; ++r) {
             const int q = qb * QBW + ql + r;
             const int v = 4 * g + r;
-            float p = exp2f(s[t][v] * sc - lq[r]);
-            if (kpos > q || q >= T) p = 0.f;
+            float p = fast_exp2(fmaf(s[t][v], sc, -lq[r]));
+            if (need_mask && (kpos > q || q >= T)) p = 0.f;
             s[t][v] = p;
             dp[t][v] = p * (dp[t][v] - dq[r]);
           }
@@ -542,13 +566,14 @@ __global__ void __launch_bounds__(NTHR, 1)
         }
       }
       // s[t][v]: key kb*64 + 32t + 8(v/4) + 4hl + v%4, query qpos.
+      const bool need_mask = (kb * KB + KB - 1 > q0) || (kb * KB + KB > T) || (q0 + 32 > T);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = kb * KB + 32 * t + 8 * (v >> 2) + 4 * hl + (v & 3);
-          float p = exp2f(s[t][v] * sc - lq);
-          if (key > qpos || key >= T || !qok) p = 0.f;
+          float p = fast_exp2(fmaf(s[t][v], sc, -lq));
+          if (need_mask && (key > qpos || key >= T || !qok)) p = 0.f;
           dp[t][v] = p * (dp[t][v] - dq_);
         }
       bf16x8 dsf[4];

@@ -35,6 +35,7 @@
 #pragma once
 
 #include "common.h"
+#include "lds_dma.h"
 #include "kernels.h"
 
 namespace gemm_impl {
@@ -47,9 +48,6 @@ constexpr int NTHR = 256;
 constexpr int OP_BYTES = BM * BKD * 2;  // one operand's stage: 16 KB
 constexpr int STAGE_BYTES = 2 * OP_BYTES;
 
-typedef short v4s __attribute__((ext_vector_type(4)));
-#define LDS_V4S(p) ((__attribute__((address_space(3))) v4s*)(p))
-
 __device__ __forceinline__ uint32_t sq2(uint32_t w) {
   float lo = bf_lo(w), hi = bf_hi(w);
   return pack_bf2(lo * lo, hi * hi);
@@ -59,31 +57,6 @@ __device__ __forceinline__ uint32_t sq2(uint32_t w) {
 __device__ __forceinline__ int koff(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
 // Byte offset of (k-row kr, 16-byte row-chunk c) in a K-strided stage [32][256].
 __device__ __forceinline__ int toff(int kr, int c) { return kr * 512 + ((c ^ ((kr & 3) << 2)) << 4); }
-
-// LDS byte address of a pointer into shared memory, as a wave-uniform value.
-__device__ __forceinline__ uint32_t lds_addr(const char* p) {
-  return __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p);
-}
-
-// One 16-byte-per-lane direct load: lane l's 16 bytes at gsrc land at
-// LDS lds_base + 16 l. Issued from asm so that the compiler does not add a
-// full vmcnt(0) drain before every transposing LDS read (it cannot tell
-// which LDS bytes a direct load writes); the ring's explicit vmcnt waits
-// and barriers order these loads instead. M0 carries the LDS base and is
-// restored afterwards. The asm has no output registers.
-__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(gsrc), "s"(lds_base)
-      : "memory");
-}
 
 // Issue 1 KB block `blk` (0..15) of one operand's k-block [k0, k0 + 32) into
 // an LDS stage buffer; the 4 waves issue blocks 4 wave .. 4 wave + 3.

@@ -1,0 +1,51 @@
+// Direct global -> LDS loads and the transposing LDS read of gfx950, shared
+// by the GEMM and attention kernels.
+#pragma once
+
+#include "common.h"
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+#define LDS_V4S(p) ((__attribute__((address_space(3))) v4s*)(p))
+
+// LDS byte address of a pointer into shared memory, as a wave-uniform value.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p);
+}
+
+// One 16-byte-per-lane direct load: lane l's 16 bytes at gsrc land at LDS
+// lds_base + 16 l. Issued from asm so that the compiler does not add a full
+// vmcnt(0) drain before every transposing LDS read (it cannot tell which
+// LDS bytes a direct load writes); the callers' explicit vmcnt waits and
+// barriers order these loads instead. M0 carries the LDS base and is
+// restored afterwards. The asm has no output registers.
+__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gsrc), "s"(lds_base)
+      : "memory");
+}
+
+// 4-byte variant: lane l's dword lands at lds_base + 4 l (active lanes only).
+__device__ __forceinline__ void dma4(const void* gsrc, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gsrc), "s"(lds_base)
+      : "memory");
+}
+
+// s_waitcnt vmcnt(N) for the immediate N, then s_barrier; both act as
+// compiler memory barriers so no LDS access moves across them.
+#define VMCNT_BARRIER(N) asm volatile("s_waitcnt vmcnt(" #N ")\n\ts_barrier" ::: "memory")
