@@ -38,9 +38,52 @@ def flops_per_token(L, d, V, T):
     return 6.0 * (12.0 * L * d * d + V * d) + 6.0 * L * d * T
 
 
+def gemm_bytes_per_step(L, d, V, N, chunk):
+    """Algorithmic HBM bytes of the fwd/bwd GEMM launches of one step: bf16 operands
+    read once, outputs written once (fp32 for dX feeding a norm and for weight
+    gradients), epilogue operands (residual, relu^2 activations) read once."""
+    F = 4 * d
+    layer = (N * d * 2 + 3 * d * d * 2 + N * 3 * d * 2            # QKV
+             + N * d * 2 + d * d * 2 + 2 * N * d * 2              # O + residual
+             + N * d * 2 + F * d * 2 + N * F * 2                  # FC, relu^2
+             + N * F * 2 + F * d * 2 + 2 * N * d * 2              # proj + residual
+             + N * d * 2 + d * F * 2 + 2 * N * F * 2              # dH, relu^2' epilogue
+             + N * d * 2 + N * F * 2 + F * d * 4                  # dW_proj
+             + N * F * 2 + F * d * 2 + N * d * 4                  # dXn2
+             + N * F * 2 + N * d * 2 + F * d * 4                  # dW_fc
+             + N * d * 2 + d * d * 2 + N * d * 2                  # dO
+             + 2 * N * d * 2 + d * d * 4                          # dWo
+             + N * 3 * d * 2 + 3 * d * d * 2 + N * d * 4          # dXn
+             + N * 3 * d * 2 + N * d * 2 + 3 * d * d * 4)         # dW_qkv
+    nchunks = -(-N // chunk)
+    head = nchunks * ((chunk * d * 2 + V * d * 2 + chunk * V * 2)
+                      + (chunk * V * 2 + V * d * 2 + chunk * d * 4)
+                      + (chunk * V * 2 + chunk * d * 2 + 2 * V * d * 4))
+    return L * layer + head, 12 * L + 3 * nchunks
+
+
 def ns_flops(L, d, steps=5):
     # Per iteration per layer: four d x d matrices (6 d^3 each) and two 4d x d (18 d^3 each).
     return steps * L * (4 * 6.0 + 2 * 18.0) * d ** 3
+
+
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "gemm_bf16_kernel_d20_hbm_traffic.txt")
+
+
+def gemm_traffic():
+    """HBM bytes per launch of the fwd/bwd GEMM family from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary, or None when the GEMM sources changed since."""
+    from gpt_pretraining_step_bf16_amd.profile_summary import gemm_source_hash
+
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    vals = dict(line.split(": ", 1) for line in text.splitlines() if ": " in line and not line.startswith("#"))
+    if vals.get("source_sha256", "").strip() != gemm_source_hash():
+        return None
+    return float(vals["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(cfg, weights, tok, tgt):
@@ -79,6 +122,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="d20", choices=sorted(syn.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="launch one plain device copy of this many MiB before the steps "
+                         "(the calibration kernel for rocprofv3 FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -103,6 +149,15 @@ def main():
     st.load_weights(weights)
     tok_d = torch.from_numpy(tok).cuda()
     tgt_d = torch.from_numpy(tgt).cuda()
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy probe: {n * 4} bytes read and written", file=sys.stderr, flush=True)
+        del src, dst
 
     def step():
         st.fwd_bwd(tok_d, tgt_d)
@@ -144,6 +199,9 @@ def main():
         print(f"[bench] {name:9s} {ms / args.steps:9.2f} ms/step  {n // max(args.steps, 1):5d} launches/step"
               f"  {tf:8.1f} TFLOP/s", file=sys.stderr, flush=True)
     g_ms, g_fl, g_n = prof["gemm"]
+    # The head runs over token chunks of at most 1 GiB of bf16 logits (at least 256 rows).
+    head_chunk = min(B * T, max(256, (1 << 30) // (2 * V)))
+    g_bytes, g_launches = gemm_bytes_per_step(L, d, V, B * T, head_chunk)
     achieved = g_fl / (g_ms / 1e3) / 1e12 if g_ms > 0 else 0.0
     roofline = {
         "kernel": "gemm_bf16_kernel (projection, head and weight-gradient GEMMs of fwd+bwd)",
@@ -152,7 +210,9 @@ def main():
         "peak": PEAK_BF16_FLOPS / 1e12,
         "unit": "TFLOP/s",
         "frac": round(achieved / (PEAK_BF16_FLOPS / 1e12), 4),
-        "traffic": None,
+        "traffic": gemm_traffic(),
+        "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+        "algorithmic_bytes_per_launch": round(g_bytes / g_launches),
         "launches_per_step": g_n // max(args.steps, 1),
         "ms_per_step": round(g_ms / args.steps, 3),
     }
