@@ -7,111 +7,130 @@
 // Layout: q, k, v live in one packed buffer qkv [B*T, 3*H*128] bf16 (q heads,
 // then k heads, then v heads; 128 columns per head), o is [B*T, H*128].
 //
-// Forward (per workgroup: 128 queries of one (b, h); 4 waves x 32 queries):
-//  * Scores are computed transposed, S^T = K Q^T, with
-//    v_mfma_f32_32x32x16_bf16 (A = 32 keys from LDS, B = the wave's 32
-//    queries held in registers). A lane then holds one query and 32 of the 64
-//    keys of a block, so the online-softmax max/sum are in-lane, plus one
-//    exchange with lane ^ 32.
-//  * O^T += V^T P^T: P^T is already in the B-operand layout (the 8 k-slots
-//    of a lane are two groups of 4 consecutive keys), V^T comes from LDS
-//    where V is stored transposed as [dim][key] in 8-byte units of 4 keys,
-//    XOR-swizzled by dim so 16 consecutive dims hit distinct banks. The
-//    accumulator O^T keeps one query per lane, so the rescale is in-lane too.
-//  * K/V blocks of 64 keys are double-buffered in LDS (2 x 32 KB).
-//  * Softmax runs in the log2 domain: scores are scaled by log2(e)/sqrt(128),
-//    exp2 is used, and the saved normaliser lse2 is log2-based.
+// Every K, V, Q or dO tile that more than one wave reads goes global -> LDS
+// by direct loads (global_load_lds_dwordx4), row-major [64 rows][128] with
+// the 16-byte chunk c of row r at position c ^ (r & 15). MFMA operands come
+// out of that one copy two ways: row fragments (32 rows x 8 dims per lane
+// half) by ds_read_b128, and transposed fragments (32 dims x 4+4 rows) by
+// ds_read_b64_tr_b16. No wave transposes through registers.
+//
+// All products are v_mfma_f32_32x32x16_bf16. A 32x32 accumulator lane holds
+// one column (lane % 32) and the 16 rows 8g + 4(lane / 32) + r, g, r < 4; a
+// pair of row groups (g = 2m, 2m+1) is exactly the k-slot order of a
+// transposed fragment read at rows 16m + 4(lane / 32) + {0..3, 8..11}, so a
+// packed accumulator feeds the next product as a B operand with no shuffle.
+//
+// Forward (workgroup: 128 queries of one (b, h); 4 waves x 32 queries):
+//  * S^T = K Q^T (A = K rows from LDS, B = the wave's queries in registers):
+//    a lane holds one query, so the online-softmax state is per lane, plus
+//    one exchange with lane ^ 32 for the block max.
+//  * O^T += V^T P^T (A = V transposed from LDS, B = P^T packed in place).
+//  * Softmax in the log2 domain with the scale folded into one FMA. The
+//    reference max is only moved (and O, l rescaled) when a block exceeds it
+//    by more than 8 in log2 units; probabilities then stay below 2^8, so
+//    nothing overflows and the normalised result is unchanged.
 //
 // Backward (deterministic, no atomics):
 //  * delta = rowsum(dO * O) per (b, h, t).
-//  * dK/dV kernel: a workgroup owns 128 keys, walks query blocks of 64 from
-//    the diagonal; recomputes S = Q K^T and dP = dO V^T with the keys as the
-//    lane index, then dV^T += dO^T P and dK^T += Q^T dS with Q and dO staged
-//    in LDS both row-major and transposed.
-//  * dQ kernel: a workgroup owns 128 queries, walks key blocks up to the
-//    diagonal; recomputes S^T and dP^T with the queries as the lane index,
-//    then dQ^T += K^T dS^T with K^T staged in LDS.
+//  * dK/dV: a workgroup owns 128 keys (32 per wave, K and V in registers) and
+//    walks 64-query tiles of Q and dO from the diagonal: S = Q K^T and
+//    dP = dO V^T (A = Q, dO rows), then dV^T += dO^T P and dK^T += Q^T dS
+//    (A = dO, Q transposed).
+//  * dQ: a workgroup owns 128 queries (Q, dO in registers) and walks 64-key
+//    tiles up to the diagonal: S^T = K Q^T, dP^T = V dO^T, then
+//    dQ^T += K^T dS^T (A = K transposed).
 #include "common.h"
 #include "kernels.h"
+#include "lds_dma.h"
 
 namespace {
 
 constexpr int HD = 128;
 constexpr int QB = 128;   // queries per forward / dQ workgroup
-constexpr int KB = 64;    // keys per K/V block
+constexpr int KB = 64;    // keys per K/V tile
+constexpr int KBW = 128;  // keys per dK/dV workgroup
+constexpr int QBW = 64;   // queries per Q/dO tile of the dK/dV kernel
 constexpr int NTHR = 256;
+constexpr int TILE = 64 * HD * 2;  // bytes of one [64][128] bf16 tile
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-// Row-major [rows][128] tile in 16-byte chunks (16 per row), swizzled so the
-// 16 lanes a 256-byte LDS cycle serves (16 rows, same logical chunk) hit 16
-// distinct chunk positions.
-__device__ __forceinline__ int rswz(int row, int chunk) { return row * 16 + (chunk ^ (row & 15)); }
-// Transposed [128 dims][64 rows] tile in 8-byte units of 4 rows (16 per dim),
-// with the unit position rotated by the dim so that consecutive dims reading
-// the same logical unit land on different banks (measured best of the
-// row/dim-parity variants).
-__device__ __forceinline__ int tswz(int dim, int unit) { return dim * 16 + (unit ^ (dim & 15)); }
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Load a [64 rows][128] bf16 block (rows r0.. of a strided buffer) as 4 rows x
-// 8 columns per thread: rows 4*(t%16)+i, columns 8*(t/16)..+7.
-__device__ __forceinline__ void load_rows4x8(const uint16_t* __restrict__ base, long ld, int r0,
-                                             int nrows, int tid, uint4 (&r)[4]) {
-  const int kg = tid & 15;
-  const int dc = tid >> 4;
+// Per-lane byte offsets, within a tile, of the fragments a lane reads.
+struct FragAddr {
+  uint32_t row[8];    // row fragment of k-step k: row lane % 32, chunk 2k + lane / 32
+  uint32_t tr[4][2];  // transposed fragment of dim tile dt, read r (rows +8r)
+};
+
+__device__ __forceinline__ void frag_addr(int lane, FragAddr& a) {
+  const int hl = lane >> 5;
+  const int r = lane & 31;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) a.row[k] = r * 256 + (((2 * k + hl) ^ (r & 15)) << 4);
+  // Transposed read: group g = lane / 16, group-lane p = 4 j + q addresses row
+  // base + 8 rr + 4 (g >> 1) + j at dims 32 dt + 16 (g & 1) + 4 q .. +3; the
+  // lane receives dim 32 dt + 16 (g & 1) + p at the four rows of its group.
+  const int g = lane >> 4, p = lane & 15, j = p >> 2, q = p & 3;
+  const int c0 = 2 * (g & 1) + (q >> 1);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const int x = 8 * rr + 4 * (g >> 1) + j;  // row within the 16-row group (base % 16 == 0)
+      a.tr[dt][rr] = x * 256 + (((4 * dt + c0) ^ x) << 4) + (q & 1) * 8;
+    }
+}
+
+// Row fragment: rows rbase + lane % 32 (rbase % 16 == 0), dims 16k + 8 (lane / 32) .. +7.
+__device__ __forceinline__ bf16x8 row_frag(const char* tile, const FragAddr& a, int rbase, int k) {
+  return as_bf16x8(*reinterpret_cast<const uint4*>(tile + rbase * 256 + a.row[k]));
+}
+
+// Transposed fragment: dims 32 dt + lane % 32; k-slots rows
+// rbase + 4 (lane / 32) + {0..3} and rbase + 8 + 4 (lane / 32) + {0..3} (rbase % 16 == 0).
+__device__ __forceinline__ bf16x8 tr_frag(const char* tile, const FragAddr& a, int rbase, int dt) {
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_V4S(tile + rbase * 256 + a.tr[dt][0]));
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_V4S(tile + rbase * 256 + a.tr[dt][1]));
+  const uint2 x = __builtin_bit_cast(uint2, lo);
+  const uint2 y = __builtin_bit_cast(uint2, hi);
+  return as_bf16x8(make_uint4(x.x, x.y, y.x, y.y));
+}
+
+// Direct load of rows r0 .. r0+63 (row stride ld elements, rows past nrows - 1
+// read row nrows - 1) into a swizzled LDS tile; wave w issues 1 KB blocks
+// 4w .. 4w+3 (4 rows each).
+__device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ base, long ld, int r0, int nrows,
+                                         char* tile, int wave, int lane) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int row = r0 + 4 * kg + i;
-    if (row < nrows) {
-      r[i] = *reinterpret_cast<const uint4*>(base + (long)row * ld + dc * 8);
-    } else {
-      r[i] = make_uint4(0, 0, 0, 0);
-    }
+    const int blk = 4 * wave + i;
+    const int row = 4 * blk + (lane >> 4);
+    const int chunk = (lane & 15) ^ (row & 15);
+    const int gr = min(r0 + row, nrows - 1);
+    dma16(base + (long)gr * ld + chunk * 8, lds_addr(tile + blk * 1024));
   }
 }
 
-__device__ __forceinline__ uint32_t w4(const uint4& v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+// 64 floats v[r0 .. r0+63] (indices past n - 1 read v[n - 1]) into LDS.
+__device__ __forceinline__ void dma_vec64(const float* __restrict__ v, int r0, int n, float* dst,
+                                          int lane) {
+  dma4(v + min(r0 + lane, n - 1), lds_addr(dst));
 }
 
-// Store the 4x8 block transposed: unit (dim 8dc+j, rows 4kg..4kg+3).
-__device__ __forceinline__ void store_t4x8(uint2* __restrict__ lt, int tid, const uint4 (&r)[4]) {
-  const int kg = tid & 15;
-  const int dc = tid >> 4;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int sh = (j & 1) * 16;
-    const uint32_t e0 = (w4(r[0], j >> 1) >> sh) & 0xffffu;
-    const uint32_t e1 = (w4(r[1], j >> 1) >> sh) & 0xffffu;
-    const uint32_t e2 = (w4(r[2], j >> 1) >> sh) & 0xffffu;
-    const uint32_t e3 = (w4(r[3], j >> 1) >> sh) & 0xffffu;
-    lt[tswz(dc * 8 + j, kg)] = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
-  }
-}
-
-// Store the 4x8 block row-major.
-__device__ __forceinline__ void store_r4x8(uint4* __restrict__ lr, int tid, const uint4 (&r)[4]) {
-  const int kg = tid & 15;
-  const int dc = tid >> 4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) lr[rswz(4 * kg + i, dc)] = r[i];
-}
-
-// A-operand fragment from a transposed tile: dim `dim`, k-slots = rows
-// {base4, base4+1, base4+2, base4+3, base4+8, ..., base4+11} where
-// base4 = 32t + 16(s%2) + 4h (rows relative to the tile).
-__device__ __forceinline__ bf16x8 tfrag(const uint2* __restrict__ lt, int dim, int unit) {
-  const uint2 a = lt[tswz(dim, unit)];
-  const uint2 b = lt[tswz(dim, unit + 2)];
-  return as_bf16x8(make_uint4(a.x, a.y, b.x, b.y));
-}
-
-// Pack accumulator registers v0..v0+7 of a 32x32 tile into a bf16 B fragment.
 __device__ __forceinline__ bf16x8 pack_frag(const f32x16& x, int v0) {
   return as_bf16x8(make_uint4(pack_bf2(x[v0 + 0], x[v0 + 1]), pack_bf2(x[v0 + 2], x[v0 + 3]),
                               pack_bf2(x[v0 + 4], x[v0 + 5]), pack_bf2(x[v0 + 6], x[v0 + 7])));
+}
+
+// Work item of a (blocks_per_head x heads) grid, remapped so that the blocks
+// of one head run on the same XCD (they share its K/V or Q/dO in L2).
+__device__ __forceinline__ void head_block(int& blk, int& bh) {
+  const int nb = gridDim.x;
+  const int total = nb * gridDim.y;
+  int lin = blockIdx.x + nb * blockIdx.y;
+  if ((total & 7) == 0) lin = (lin & 7) * (total >> 3) + (lin >> 3);
+  bh = lin / nb;
+  blk = lin - bh * nb;
 }
 
 // ===========================================================================
@@ -120,16 +139,16 @@ __device__ __forceinline__ bf16x8 pack_frag(const f32x16& x, int v0) {
 __global__ void __launch_bounds__(NTHR, 2)
     attn_fwd_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ out,
                     float* __restrict__ lse2, int T, int H) {
-  __shared__ uint4 ks[2][KB * 16];
-  __shared__ uint2 vt[2][HD * 16];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];  // [stage][K, V]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int hl = lane >> 5;
+  int xb, bh;
+  head_block(xb, bh);
   const int nqb = (T + QB - 1) / QB;
-  const int qblk = nqb - 1 - blockIdx.x;  // heaviest blocks first
-  const int bh = blockIdx.y;
+  const int qblk = nqb - 1 - xb;  // heaviest blocks first
   const int b = bh / H;
   const int h = bh - b * H;
   const int d = H * HD;
@@ -137,17 +156,21 @@ __global__ void __launch_bounds__(NTHR, 2)
   const uint16_t* qbase = qkv + (long)b * T * ld + h * HD;
   const uint16_t* kbase = qbase + d;
   const uint16_t* vbase = qbase + 2 * d;
-
   const int q0 = qblk * QB + wave * 32;
   const int qpos = q0 + (lane & 31);
   const float sc = GPT_LOG2E * 0.08838834764831845f;  // log2(e) / sqrt(128)
+  // Rescale only when the block max exceeds the reference by 8 in log2 units.
+  const float lazy = 8.f / sc;
 
-  // Q fragments (B operand): query qpos, dims 16ks + 8hl .. +7.
+  FragAddr fa;
+  frag_addr(lane, fa);
+
+  // Q fragments (B operand): query qpos, dims 16k + 8hl .. +7.
   uint4 qf[8];
+  {
+    const uint16_t* qrow = qbase + (long)min(qpos, T - 1) * ld + 8 * hl;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    qf[k] = qpos < T ? *reinterpret_cast<const uint4*>(qbase + (long)qpos * ld + 16 * k + 8 * hl)
-                     : make_uint4(0, 0, 0, 0);
+    for (int k = 0; k < 8; ++k) qf[k] = *reinterpret_cast<const uint4*>(qrow + 16 * k);
   }
 
   f32x16 o[4];
@@ -155,117 +178,95 @@ __global__ void __launch_bounds__(NTHR, 2)
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[i][v] = 0.f;
-  float m_run = -INFINITY;
-  float l_run = 0.f;
+  float m_ref = -INFINITY;  // raw-score reference max (the same in both lane halves)
+  float l_run = 0.f;        // this lane half's share of the normaliser
 
   const int qmax = min(T - 1, qblk * QB + QB - 1);
   const int nkb = qmax / KB + 1;
 
-  uint4 kr[4], vr[4];
-  auto load_kv = [&](int kb) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + NTHR * i;
-      const int key = kb * KB + (c >> 4);
-      kr[i] = key < T ? *reinterpret_cast<const uint4*>(kbase + (long)key * ld + (c & 15) * 8)
-                      : make_uint4(0, 0, 0, 0);
-    }
-    load_rows4x8(vbase, ld, kb * KB, T, tid, vr);
-  };
-  auto store_kv = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + NTHR * i;
-      ks[st][rswz(c >> 4, c & 15)] = kr[i];
-    }
-    store_t4x8(vt[st], tid, vr);
+  auto issue = [&](int kb, int st) {
+    char* ks = smem + st * 2 * TILE;
+    dma_tile(kbase, ld, kb * KB, T, ks, wave, lane);
+    dma_tile(vbase, ld, kb * KB, T, ks + TILE, wave, lane);
   };
 
-  load_kv(0);
-  store_kv(0);
-  __syncthreads();
-
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int st = kb & 1;
-    if (kb + 1 < nkb) load_kv(kb + 1);
-    if (kb * KB <= q0 + 31) {  // some key of this block is visible to the wave
-      f32x16 s[2];
+  auto block = [&](int kb, int st) {
+    const char* ks = smem + st * 2 * TILE;
+    const char* vs = ks + TILE;
+    if (kb * KB > q0 + 31) return;  // no key of this block is visible to the wave
+    f32x16 s[2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < 2; ++t) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) s[t][v] = 0.f;
+      for (int v = 0; v < 16; ++v) s[t][v] = 0.f;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const bf16x8 a = as_bf16x8(ks[st][rswz(32 * t + (lane & 31), 2 * k + hl)]);
-          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(qf[k]), s[t], 0, 0, 0);
-        }
-      }
-      // s[t][v]: key kb*64 + 32t + 8(v/4) + 4hl + v%4, query qpos.
-      float mloc = -INFINITY;
-      // Masking is needed only where the block reaches past the wave's first
-      // query (causal diagonal) or past the end of the sequence.
-      const bool need_mask = (kb * KB + KB - 1 > q0) || (kb * KB + KB > T);
-      if (need_mask) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int key = kb * KB + 32 * t + 8 * (v >> 2) + 4 * hl + (v & 3);
-            float x = s[t][v] * sc;
-            if (key > qpos || key >= T) x = -INFINITY;
-            s[t][v] = x;
-            mloc = fmaxf(mloc, x);
-          }
-      } else {
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const float x = s[t][v] * sc;
-            s[t][v] = x;
-            mloc = fmaxf(mloc, x);
-          }
-      }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-      const float m_new = fmaxf(m_run, mloc);
-      const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_ref);
-      float lsum = 0.f;
+      for (int k = 0; k < 8; ++k)
+        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(ks, fa, 32 * t, k), as_bf16x8(qf[k]),
+                                                       s[t], 0, 0, 0);
+    }
+    // s[t][v]: key kb*64 + 32t + 8(v/4) + 4hl + v%4, query qpos (raw q.k).
+    const bool need_mask = (kb * KB + KB - 1 > q0) || (kb * KB + KB > T);
+    if (need_mask) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const float pv = fast_exp2(s[t][v] - m_ref);
-          s[t][v] = pv;
-          lsum += pv;
+          const int key = kb * KB + 32 * t + 8 * (v >> 2) + 4 * hl + (v & 3);
+          if (key > qpos || key >= T) s[t][v] = -INFINITY;
         }
-      lsum += __shfl_xor(lsum, 32, 64);
-      l_run = alpha * l_run + lsum;
-      m_run = m_new;
+    }
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, s[t][v]);
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    if (__builtin_amdgcn_ballot_w64(mloc > m_ref + lazy) != 0) {
+      const float m_new = fmaxf(m_ref, mloc);
+      const float alpha = m_ref == -INFINITY ? 0.f : fast_exp2((m_ref - m_new) * sc);
+      l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
-      bf16x8 pf[4];
-#pragma unroll
-      for (int sidx = 0; sidx < 4; ++sidx) pf[sidx] = pack_frag(s[sidx >> 1], 8 * (sidx & 1));
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const int dim = 32 * dt + (lane & 31);
-#pragma unroll
-        for (int sidx = 0; sidx < 4; ++sidx) {
-          const int unit = 8 * (sidx >> 1) + 4 * (sidx & 1) + hl;
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tfrag(vt[st], dim, unit), pf[sidx], o[dt], 0,
-                                                          0, 0);
-        }
-      }
+      m_ref = m_new;
     }
-    if (kb + 1 < nkb) store_kv(st ^ 1);
-    __syncthreads();
+    const float msc = m_ref == -INFINITY ? 0.f : m_ref * sc;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float pv = fast_exp2(fmaf(s[t][v], sc, -msc));
+        s[t][v] = pv;
+        l_run += pv;
+      }
+    bf16x8 pf[4];
+#pragma unroll
+    for (int si = 0; si < 4; ++si) pf[si] = pack_frag(s[si >> 1], 8 * (si & 1));
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int si = 0; si < 4; ++si)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(vs, fa, 16 * si, dt), pf[si], o[dt], 0,
+                                                        0, 0);
+  };
+
+  issue(0, 0);
+  VMCNT_BARRIER(0);
+  for (int kb = 0; kb < nkb; kb += 2) {
+    if (kb + 1 < nkb) issue(kb + 1, 1);
+    block(kb, 0);
+    VMCNT_BARRIER(0);
+    if (kb + 1 < nkb) {
+      if (kb + 2 < nkb) issue(kb + 2, 0);
+      block(kb + 1, 1);
+      VMCNT_BARRIER(0);
+    }
   }
 
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (qpos < T) {
-    const float inv = 1.f / l_run;
+    const float inv = 1.f / l_tot;
     uint16_t* orow = out + ((long)b * T + qpos) * d + h * HD;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -276,7 +277,7 @@ __global__ void __launch_bounds__(NTHR, 2)
             make_uint2(pack_bf2(o[dt][4 * g + 0] * inv, o[dt][4 * g + 1] * inv),
                        pack_bf2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv));
       }
-    if (hl == 0) lse2[(long)bh * T + qpos] = m_run + log2f(l_run);
+    if (hl == 0) lse2[(long)bh * T + qpos] = m_ref * sc + log2f(l_tot);
   }
 }
 
@@ -305,26 +306,20 @@ __global__ void attn_bwd_delta_kernel(const uint16_t* __restrict__ o, const uint
 // ===========================================================================
 // Backward: dK, dV
 // ===========================================================================
-constexpr int KBW = 128;  // keys per dK/dV workgroup
-constexpr int QBW = 64;   // queries per block walked
+constexpr int DKDV_STAGE = 2 * TILE + 2 * QBW * 4;  // Q tile, dO tile, lse, delta
 
 __global__ void __launch_bounds__(NTHR, 1)
     attn_bwd_dkdv_kernel(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dO,
                          const float* __restrict__ lse2, const float* __restrict__ delta,
                          uint16_t* __restrict__ dqkv, int T, int H) {
-  __shared__ uint4 qs[2][QBW * 16];
-  __shared__ uint4 dos[2][QBW * 16];
-  __shared__ uint2 qt[2][HD * 16];
-  __shared__ uint2 dot_[2][HD * 16];
-  __shared__ __attribute__((aligned(16))) float ls[2][QBW];
-  __shared__ __attribute__((aligned(16))) float ds_[2][QBW];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * DKDV_STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int hl = lane >> 5;
-  const int kblk = blockIdx.x;
-  const int bh = blockIdx.y;
+  int kblk, bh;
+  head_block(kblk, bh);
   const int b = bh / H;
   const int h = bh - b * H;
   const int d = H * HD;
@@ -340,15 +335,18 @@ __global__ void __launch_bounds__(NTHR, 1)
   const int k0 = kblk * KBW + wave * 32;
   const int kpos = k0 + (lane & 31);
 
+  FragAddr fa;
+  frag_addr(lane, fa);
+
   // K and V fragments as B operands: key kpos, dims 16k + 8hl .. +7.
   uint4 kf[8], vf[8];
+  {
+    const long kr = (long)min(kpos, T - 1) * ld + 8 * hl;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const bool ok = kpos < T;
-    kf[k] = ok ? *reinterpret_cast<const uint4*>(kbase + (long)kpos * ld + 16 * k + 8 * hl)
-               : make_uint4(0, 0, 0, 0);
-    vf[k] = ok ? *reinterpret_cast<const uint4*>(vbase + (long)kpos * ld + 16 * k + 8 * hl)
-               : make_uint4(0, 0, 0, 0);
+    for (int k = 0; k < 8; ++k) {
+      kf[k] = *reinterpret_cast<const uint4*>(kbase + kr + 16 * k);
+      vf[k] = *reinterpret_cast<const uint4*>(vbase + kr + 16 * k);
+    }
   }
 
   f32x16 dk[4], dv[4];
@@ -363,99 +361,87 @@ __global__ void __launch_bounds__(NTHR, 1)
   const int qb_first = (kblk * KBW) / QBW;
   const int qb_end = (T + QBW - 1) / QBW;
 
-  uint4 qr[4], gr[4];
-  float lv = 0.f, dvv = 0.f;
-  auto load_q = [&](int qb) {
-    load_rows4x8(qbase, ld, qb * QBW, T, tid, qr);
-    load_rows4x8(dobase, d, qb * QBW, T, tid, gr);
-    if (tid < QBW) {
-      const int q = qb * QBW + tid;
-      lv = q < T ? lrow[q] : 0.f;
-      dvv = q < T ? drow[q] : 0.f;
-    }
+  auto issue = [&](int qb, int st) {
+    char* base = smem + st * DKDV_STAGE;
+    dma_tile(qbase, ld, qb * QBW, T, base, wave, lane);
+    dma_tile(dobase, d, qb * QBW, T, base + TILE, wave, lane);
+    if (wave == 0) dma_vec64(lrow, qb * QBW, T, reinterpret_cast<float*>(base + 2 * TILE), lane);
+    if (wave == 1) dma_vec64(drow, qb * QBW, T, reinterpret_cast<float*>(base + 2 * TILE + QBW * 4), lane);
   };
-  auto store_q = [&](int st) {
-    store_r4x8(qs[st], tid, qr);
-    store_t4x8(qt[st], tid, qr);
-    store_r4x8(dos[st], tid, gr);
-    store_t4x8(dot_[st], tid, gr);
-    if (tid < QBW) {
-      ls[st][tid] = lv;
-      ds_[st][tid] = dvv;
+
+  auto block = [&](int qb, int st) {
+    const char* qs = smem + st * DKDV_STAGE;
+    const char* gs = qs + TILE;
+    const float* ls = reinterpret_cast<const float*>(qs + 2 * TILE);
+    const float* ds = ls + QBW;
+    if (qb * QBW + QBW - 1 < k0 || k0 >= T) return;  // every query precedes the wave's keys
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        s[t][v] = 0.f;
+        dp[t][v] = 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(qs, fa, 32 * t, k), as_bf16x8(kf[k]), s[t],
+                                                       0, 0, 0);
+        dp[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(gs, fa, 32 * t, k), as_bf16x8(vf[k]),
+                                                        dp[t], 0, 0, 0);
+      }
     }
+    // s[t][v]: query qb*64 + 32t + 8(v/4) + 4hl + v%4, key kpos.
+    const bool need_mask = (qb * QBW < k0 + 31) || (qb * QBW + QBW > T);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int ql = 32 * t + 8 * g + 4 * hl;
+        const float4 l4 = *reinterpret_cast<const float4*>(ls + ql);
+        const float4 d4 = *reinterpret_cast<const float4*>(ds + ql);
+        const float lq[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dq[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int q = qb * QBW + ql + r;
+          const int v = 4 * g + r;
+          float p = fast_exp2(fmaf(s[t][v], sc, -lq[r]));
+          if (need_mask && (kpos > q || q >= T)) p = 0.f;
+          s[t][v] = p;
+          dp[t][v] = p * (dp[t][v] - dq[r]);
+        }
+      }
+    bf16x8 pf[4], dsf[4];
+#pragma unroll
+    for (int si = 0; si < 4; ++si) {
+      pf[si] = pack_frag(s[si >> 1], 8 * (si & 1));
+      dsf[si] = pack_frag(dp[si >> 1], 8 * (si & 1));
+    }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int si = 0; si < 4; ++si) {
+        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(gs, fa, 16 * si, dt), pf[si], dv[dt], 0, 0,
+                                                         0);
+        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(qs, fa, 16 * si, dt), dsf[si], dk[dt], 0,
+                                                         0, 0);
+      }
   };
 
   if (qb_first < qb_end) {
-    load_q(qb_first);
-    store_q(0);
+    issue(qb_first, 0);
+    VMCNT_BARRIER(0);
   }
-  __syncthreads();
-
-  for (int qb = qb_first; qb < qb_end; ++qb) {
-    const int st = (qb - qb_first) & 1;
-    if (qb + 1 < qb_end) load_q(qb + 1);
-    if (qb * QBW + QBW - 1 >= k0 && k0 < T) {
-      f32x16 s[2], dp[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          s[t][v] = 0.f;
-          dp[t][v] = 0.f;
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int row = 32 * t + (lane & 31);
-          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qs[st][rswz(row, 2 * k + hl)]),
-                                                         as_bf16x8(kf[k]), s[t], 0, 0, 0);
-          dp[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(dos[st][rswz(row, 2 * k + hl)]),
-                                                          as_bf16x8(vf[k]), dp[t], 0, 0, 0);
-        }
-      }
-      // s[t][v]: query qb*64 + 32t + 8(v/4) + 4hl + v%4, key kpos.
-      // Mask where some query of the block precedes a key of the wave, or the
-      // block runs past the end of the sequence.
-      const bool need_mask = (qb * QBW < k0 + 31) || (qb * QBW + QBW > T);
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int ql = 32 * t + 8 * g + 4 * hl;
-          const float4 l4 = *reinterpret_cast<const float4*>(&ls[st][ql]);
-          const float4 d4 = *reinterpret_cast<const float4*>(&ds_[st][ql]);
-          const float lq[4] = {l4.x, l4.y, l4.z, l4.w};
-          const float dq[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int q = qb * QBW + ql + r;
-            const int v = 4 * g + r;
-            float p = fast_exp2(fmaf(s[t][v], sc, -lq[r]));
-            if (need_mask && (kpos > q || q >= T)) p = 0.f;
-            s[t][v] = p;
-            dp[t][v] = p * (dp[t][v] - dq[r]);
-          }
-        }
-      bf16x8 pf[4], dsf[4];
-#pragma unroll
-      for (int sidx = 0; sidx < 4; ++sidx) {
-        pf[sidx] = pack_frag(s[sidx >> 1], 8 * (sidx & 1));
-        dsf[sidx] = pack_frag(dp[sidx >> 1], 8 * (sidx & 1));
-      }
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const int dim = 32 * dt + (lane & 31);
-#pragma unroll
-        for (int sidx = 0; sidx < 4; ++sidx) {
-          const int unit = 8 * (sidx >> 1) + 4 * (sidx & 1) + hl;
-          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tfrag(dot_[st], dim, unit), pf[sidx], dv[dt],
-                                                           0, 0, 0);
-          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tfrag(qt[st], dim, unit), dsf[sidx], dk[dt],
-                                                           0, 0, 0);
-        }
-      }
+  for (int qb = qb_first; qb < qb_end; qb += 2) {
+    if (qb + 1 < qb_end) issue(qb + 1, 1);
+    block(qb, 0);
+    VMCNT_BARRIER(0);
+    if (qb + 1 < qb_end) {
+      if (qb + 2 < qb_end) issue(qb + 2, 0);
+      block(qb + 1, 1);
+      VMCNT_BARRIER(0);
     }
-    if (qb + 1 < qb_end) store_q(st ^ 1);
-    __syncthreads();
   }
 
   if (kpos < T) {
@@ -480,21 +466,20 @@ __global__ void __launch_bounds__(NTHR, 1)
 // ===========================================================================
 // Backward: dQ
 // ===========================================================================
-__global__ void __launch_bounds__(NTHR, 1)
+__global__ void __launch_bounds__(NTHR, 2)
     attn_bwd_dq_kernel(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dO,
                        const float* __restrict__ lse2, const float* __restrict__ delta,
                        uint16_t* __restrict__ dqkv, int T, int H) {
-  __shared__ uint4 ks[2][KB * 16];
-  __shared__ uint4 vs[2][KB * 16];
-  __shared__ uint2 kt[2][HD * 16];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];  // [stage][K, V]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int hl = lane >> 5;
+  int xb, bh;
+  head_block(xb, bh);
   const int nqb = (T + QB - 1) / QB;
-  const int qblk = nqb - 1 - blockIdx.x;
-  const int bh = blockIdx.y;
+  const int qblk = nqb - 1 - xb;
   const int b = bh / H;
   const int h = bh - b * H;
   const int d = H * HD;
@@ -508,17 +493,19 @@ __global__ void __launch_bounds__(NTHR, 1)
   const int q0 = qblk * QB + wave * 32;
   const int qpos = q0 + (lane & 31);
   const bool qok = qpos < T;
+  const int qc = min(qpos, T - 1);
+
+  FragAddr fa;
+  frag_addr(lane, fa);
 
   uint4 qf[8], gf[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    qf[k] = qok ? *reinterpret_cast<const uint4*>(qbase + (long)qpos * ld + 16 * k + 8 * hl)
-                : make_uint4(0, 0, 0, 0);
-    gf[k] = qok ? *reinterpret_cast<const uint4*>(dobase + (long)qpos * d + 16 * k + 8 * hl)
-                : make_uint4(0, 0, 0, 0);
+    qf[k] = *reinterpret_cast<const uint4*>(qbase + (long)qc * ld + 16 * k + 8 * hl);
+    gf[k] = *reinterpret_cast<const uint4*>(dobase + (long)qc * d + 16 * k + 8 * hl);
   }
-  const float lq = qok ? lse2[(long)bh * T + qpos] : 0.f;
-  const float dq_ = qok ? delta[(long)bh * T + qpos] : 0.f;
+  const float lq = lse2[(long)bh * T + qc];
+  const float dq_ = delta[(long)bh * T + qc];
 
   f32x16 acc[4];
 #pragma unroll
@@ -529,69 +516,63 @@ __global__ void __launch_bounds__(NTHR, 1)
   const int qmax = min(T - 1, qblk * QB + QB - 1);
   const int nkb = qmax / KB + 1;
 
-  uint4 kr[4], vr[4];
-  auto load_kv = [&](int kb) {
-    load_rows4x8(kbase, ld, kb * KB, T, tid, kr);
-    load_rows4x8(vbase, ld, kb * KB, T, tid, vr);
-  };
-  auto store_kv = [&](int st) {
-    store_r4x8(ks[st], tid, kr);
-    store_t4x8(kt[st], tid, kr);
-    store_r4x8(vs[st], tid, vr);
+  auto issue = [&](int kb, int st) {
+    char* ks = smem + st * 2 * TILE;
+    dma_tile(kbase, ld, kb * KB, T, ks, wave, lane);
+    dma_tile(vbase, ld, kb * KB, T, ks + TILE, wave, lane);
   };
 
-  load_kv(0);
-  store_kv(0);
-  __syncthreads();
-
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int st = kb & 1;
-    if (kb + 1 < nkb) load_kv(kb + 1);
-    if (kb * KB <= q0 + 31) {
-      f32x16 s[2], dp[2];
+  auto block = [&](int kb, int st) {
+    const char* ks = smem + st * 2 * TILE;
+    const char* vs = ks + TILE;
+    if (kb * KB > q0 + 31) return;
+    const bool need_mask = (kb * KB + KB - 1 > q0) || (kb * KB + KB > T) || (q0 + 32 > T);
+    // One 32-key half of the tile at a time (keeps two accumulators live, not four).
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < 2; ++t) {
+      f32x16 s, dp;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          s[t][v] = 0.f;
-          dp[t][v] = 0.f;
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int row = 32 * t + (lane & 31);
-          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ks[st][rswz(row, 2 * k + hl)]),
-                                                         as_bf16x8(qf[k]), s[t], 0, 0, 0);
-          dp[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vs[st][rswz(row, 2 * k + hl)]),
-                                                          as_bf16x8(gf[k]), dp[t], 0, 0, 0);
-        }
+      for (int v = 0; v < 16; ++v) {
+        s[v] = 0.f;
+        dp[v] = 0.f;
       }
-      // s[t][v]: key kb*64 + 32t + 8(v/4) + 4hl + v%4, query qpos.
-      const bool need_mask = (kb * KB + KB - 1 > q0) || (kb * KB + KB > T) || (q0 + 32 > T);
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int k = 0; k < 8; ++k) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(ks, fa, 32 * t, k), as_bf16x8(qf[k]), s, 0, 0,
+                                                    0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(vs, fa, 32 * t, k), as_bf16x8(gf[k]), dp, 0,
+                                                     0, 0);
+      }
+      // s[v]: key kb*64 + 32t + 8(v/4) + 4hl + v%4, query qpos.
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = kb * KB + 32 * t + 8 * (v >> 2) + 4 * hl + (v & 3);
-          float p = fast_exp2(fmaf(s[t][v], sc, -lq));
-          if (need_mask && (key > qpos || key >= T || !qok)) p = 0.f;
-          dp[t][v] = p * (dp[t][v] - dq_);
-        }
-      bf16x8 dsf[4];
-#pragma unroll
-      for (int sidx = 0; sidx < 4; ++sidx) dsf[sidx] = pack_frag(dp[sidx >> 1], 8 * (sidx & 1));
+      for (int v = 0; v < 16; ++v) {
+        const int key = kb * KB + 32 * t + 8 * (v >> 2) + 4 * hl + (v & 3);
+        float p = fast_exp2(fmaf(s[v], sc, -lq));
+        if (need_mask && (key > qpos || key >= T || !qok)) p = 0.f;
+        dp[v] = p * (dp[v] - dq_);
+      }
+      const bf16x8 ds0 = pack_frag(dp, 0);
+      const bf16x8 ds1 = pack_frag(dp, 8);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const int dim = 32 * dt + (lane & 31);
-#pragma unroll
-        for (int sidx = 0; sidx < 4; ++sidx) {
-          const int unit = 8 * (sidx >> 1) + 4 * (sidx & 1) + hl;
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tfrag(kt[st], dim, unit), dsf[sidx],
-                                                            acc[dt], 0, 0, 0);
-        }
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(ks, fa, 32 * t, dt), ds0, acc[dt], 0, 0, 0);
+        acc[dt] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(ks, fa, 32 * t + 16, dt), ds1, acc[dt], 0, 0, 0);
       }
     }
-    if (kb + 1 < nkb) store_kv(st ^ 1);
-    __syncthreads();
+  };
+
+  issue(0, 0);
+  VMCNT_BARRIER(0);
+  for (int kb = 0; kb < nkb; kb += 2) {
+    if (kb + 1 < nkb) issue(kb + 1, 1);
+    block(kb, 0);
+    VMCNT_BARRIER(0);
+    if (kb + 1 < nkb) {
+      if (kb + 2 < nkb) issue(kb + 2, 0);
+      block(kb + 1, 1);
+      VMCNT_BARRIER(0);
+    }
   }
 
   if (qok) {
