@@ -9,7 +9,10 @@
 //
 // Every K, V, Q or dO tile that more than one wave reads goes global -> LDS
 // by direct loads (global_load_lds_dwordx4), row-major [64 rows][128] with
-// the 16-byte chunk c of row r at position c ^ (r & 15). MFMA operands come
+// the 16-byte chunk c of row r at position c ^ swz(r), swz swapping the two
+// 2-bit fields of r % 16: 16 consecutive rows of one chunk, and 4 consecutive
+// rows of 4 consecutive chunks, each land on 16 distinct bank groups, which
+// makes both read kinds below free of bank conflicts. MFMA operands come
 // out of that one copy two ways: row fragments (32 rows x 8 dims per lane
 // half) by ds_read_b128, and transposed fragments (32 dims x 4+4 rows) by
 // ds_read_b64_tr_b16. No wave transposes through registers.
@@ -56,6 +59,9 @@ constexpr int TILE = 64 * HD * 2;  // bytes of one [64][128] bf16 tile
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Chunk swizzle of row r (only r % 16 matters; tile fragments start at rows % 16 == 0).
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
 // Per-lane byte offsets, within a tile, of the fragments a lane reads.
 struct FragAddr {
   uint32_t row[8];    // row fragment of k-step k: row lane % 32, chunk 2k + lane / 32
@@ -66,7 +72,7 @@ __device__ __forceinline__ void frag_addr(int lane, FragAddr& a) {
   const int hl = lane >> 5;
   const int r = lane & 31;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) a.row[k] = r * 256 + (((2 * k + hl) ^ (r & 15)) << 4);
+  for (int k = 0; k < 8; ++k) a.row[k] = r * 256 + (((2 * k + hl) ^ swz(r)) << 4);
   // Transposed read: group g = lane / 16, group-lane p = 4 j + q addresses row
   // base + 8 rr + 4 (g >> 1) + j at dims 32 dt + 16 (g & 1) + 4 q .. +3; the
   // lane receives dim 32 dt + 16 (g & 1) + p at the four rows of its group.
@@ -77,7 +83,7 @@ __device__ __forceinline__ void frag_addr(int lane, FragAddr& a) {
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
       const int x = 8 * rr + 4 * (g >> 1) + j;  // row within the 16-row group (base % 16 == 0)
-      a.tr[dt][rr] = x * 256 + (((4 * dt + c0) ^ x) << 4) + (q & 1) * 8;
+      a.tr[dt][rr] = x * 256 + (((4 * dt + c0) ^ swz(x)) << 4) + (q & 1) * 8;
     }
 }
 
@@ -105,9 +111,36 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ base, long
   for (int i = 0; i < 4; ++i) {
     const int blk = 4 * wave + i;
     const int row = 4 * blk + (lane >> 4);
-    const int chunk = (lane & 15) ^ (row & 15);
+    const int chunk = (lane & 15) ^ swz(row);
     const int gr = min(r0 + row, nrows - 1);
     dma16(base + (long)gr * ld + chunk * 8, lds_addr(tile + blk * 1024));
+  }
+}
+
+// Per-lane byte offsets of the four 1 KB blocks a wave loads from a row-major
+// source with row stride ld elements (rows 16 wave + 4 i + lane / 16).
+struct TileDma {
+  uint32_t off[4];
+};
+
+__device__ __forceinline__ void tile_dma_init(TileDma& t, long ld, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * wave + 4 * i + (lane >> 4);
+    const int chunk = (lane & 15) ^ swz(row);
+    t.off[i] = (uint32_t)(((long)row * ld + chunk * 8) * 2);
+  }
+}
+
+// dma_tile with a scalar base and precomputed offsets when all 64 rows exist.
+__device__ __forceinline__ void dma_tile_fast(const uint16_t* __restrict__ base, long ld, int r0, int nrows,
+                                              char* tile, int wave, int lane, const TileDma& t) {
+  if (r0 + 64 <= nrows) {
+    const uint16_t* sb = base + (long)r0 * ld;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16_sv(sb, t.off[i], lds_addr(tile + (4 * wave + i) * 1024));
+  } else {
+    dma_tile(base, ld, r0, nrows, tile, wave, lane);
   }
 }
 
@@ -184,10 +217,14 @@ __global__ void __launch_bounds__(NTHR, 2)
   const int qmax = min(T - 1, qblk * QB + QB - 1);
   const int nkb = qmax / KB + 1;
 
+  TileDma td;
+  tile_dma_init(td, ld, wave, lane);
+  const int klim = min(qpos, T - 1);  // last key visible to this lane's query
+
   auto issue = [&](int kb, int st) {
     char* ks = smem + st * 2 * TILE;
-    dma_tile(kbase, ld, kb * KB, T, ks, wave, lane);
-    dma_tile(vbase, ld, kb * KB, T, ks + TILE, wave, lane);
+    dma_tile_fast(kbase, ld, kb * KB, T, ks, wave, lane, td);
+    dma_tile_fast(vbase, ld, kb * KB, T, ks + TILE, wave, lane, td);
   };
 
   auto block = [&](int kb, int st) {
@@ -212,7 +249,7 @@ __global__ void __launch_bounds__(NTHR, 2)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = kb * KB + 32 * t + 8 * (v >> 2) + 4 * hl + (v & 3);
-          if (key > qpos || key >= T) s[t][v] = -INFINITY;
+          if (key > klim) s[t][v] = -INFINITY;
         }
     }
     float mloc = -INFINITY;
@@ -361,10 +398,14 @@ __global__ void __launch_bounds__(NTHR, 1)
   const int qb_first = (kblk * KBW) / QBW;
   const int qb_end = (T + QBW - 1) / QBW;
 
+  TileDma tq, tg;
+  tile_dma_init(tq, ld, wave, lane);
+  tile_dma_init(tg, d, wave, lane);
+
   auto issue = [&](int qb, int st) {
     char* base = smem + st * DKDV_STAGE;
-    dma_tile(qbase, ld, qb * QBW, T, base, wave, lane);
-    dma_tile(dobase, d, qb * QBW, T, base + TILE, wave, lane);
+    dma_tile_fast(qbase, ld, qb * QBW, T, base, wave, lane, tq);
+    dma_tile_fast(dobase, d, qb * QBW, T, base + TILE, wave, lane, tg);
     if (wave == 0) dma_vec64(lrow, qb * QBW, T, reinterpret_cast<float*>(base + 2 * TILE), lane);
     if (wave == 1) dma_vec64(drow, qb * QBW, T, reinterpret_cast<float*>(base + 2 * TILE + QBW * 4), lane);
   };
@@ -407,7 +448,8 @@ __global__ void __launch_bounds__(NTHR, 1)
           const int q = qb * QBW + ql + r;
           const int v = 4 * g + r;
           float p = fast_exp2(fmaf(s[t][v], sc, -lq[r]));
-          if (need_mask && (kpos > q || q >= T)) p = 0.f;
+          // Visible iff kpos <= q <= T - 1 (one unsigned compare).
+          if (need_mask && (uint32_t)(q - kpos) > (uint32_t)(T - 1 - kpos)) p = 0.f;
           s[t][v] = p;
           dp[t][v] = p * (dp[t][v] - dq[r]);
         }
@@ -516,10 +558,14 @@ __global__ void __launch_bounds__(NTHR, 2)
   const int qmax = min(T - 1, qblk * QB + QB - 1);
   const int nkb = qmax / KB + 1;
 
+  TileDma td;
+  tile_dma_init(td, ld, wave, lane);
+  const int klim = min(qpos, T - 1);  // last visible key (lanes past T are discarded)
+
   auto issue = [&](int kb, int st) {
     char* ks = smem + st * 2 * TILE;
-    dma_tile(kbase, ld, kb * KB, T, ks, wave, lane);
-    dma_tile(vbase, ld, kb * KB, T, ks + TILE, wave, lane);
+    dma_tile_fast(kbase, ld, kb * KB, T, ks, wave, lane, td);
+    dma_tile_fast(vbase, ld, kb * KB, T, ks + TILE, wave, lane, td);
   };
 
   auto block = [&](int kb, int st) {
@@ -548,7 +594,7 @@ __global__ void __launch_bounds__(NTHR, 2)
       for (int v = 0; v < 16; ++v) {
         const int key = kb * KB + 32 * t + 8 * (v >> 2) + 4 * hl + (v & 3);
         float p = fast_exp2(fmaf(s[v], sc, -lq));
-        if (need_mask && (key > qpos || key >= T || !qok)) p = 0.f;
+        if (need_mask && key > klim) p = 0.f;
         dp[v] = p * (dp[v] - dq_);
       }
       const bf16x8 ds0 = pack_frag(dp, 0);

@@ -32,6 +32,21 @@ __device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
       : "memory");
 }
 
+// Same load with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit
+// byte offset: lane l's 16 bytes at sbase + voff land at LDS lds_base + 16 l.
+__device__ __forceinline__ void dma16_sv(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds_base)
+      : "memory");
+}
+
 // 4-byte variant: lane l's dword lands at lds_base + 4 l (active lanes only).
 __device__ __forceinline__ void dma4(const void* gsrc, uint32_t lds_base) {
   uint32_t saved;
