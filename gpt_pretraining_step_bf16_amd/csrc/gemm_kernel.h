@@ -34,6 +34,8 @@
 //    accumulator: Newton-Schulz uses it for hi/lo split products.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 #include "lds_dma.h"
 #include "kernels.h"
@@ -179,86 +181,167 @@ __device__ __forceinline__ void load_bf16x4(const void* p, float* v) {
   v[3] = bf_hi(u.y);
 }
 
-// Epilogue of one output group C(m, n..n+3) for a compile-time mode.
+// Whether an epilogue reads memory besides the accumulators.
 template <int E>
-__device__ __forceinline__ void epi4(const GemmArgs& p, int bi, int si, int m, int n, const float* v) {
-  const long off = (long)bi * p.sc + (long)m * p.ldc + n;
-  const long doff = (long)bi * p.sd + (long)m * p.ldd + n;
-  if constexpr (E == EPI_F32) {
-    *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.c) + off) =
-        make_float4(p.alpha * v[0], p.alpha * v[1], p.alpha * v[2], p.alpha * v[3]);
-  } else if constexpr (E == EPI_F32_ACC) {
-    float* c = reinterpret_cast<float*>(p.c) + off;
-    float4 o = *reinterpret_cast<const float4*>(c);
-    o.x = p.beta * o.x + p.alpha * v[0];
-    o.y = p.beta * o.y + p.alpha * v[1];
-    o.z = p.beta * o.z + p.alpha * v[2];
-    o.w = p.beta * o.w + p.alpha * v[3];
-    *reinterpret_cast<float4*>(c) = o;
-  } else if constexpr (E == EPI_BF16) {
-    store_bf16x4(reinterpret_cast<uint16_t*>(p.c) + off, p.alpha * v[0], p.alpha * v[1], p.alpha * v[2],
-                 p.alpha * v[3]);
-  } else if constexpr (E == EPI_RELU_BF16) {
-    store_bf16x4(reinterpret_cast<uint16_t*>(p.c) + off, fmaxf(v[0], 0.f), fmaxf(v[1], 0.f),
-                 fmaxf(v[2], 0.f), fmaxf(v[3], 0.f));
+constexpr bool epi_reads() {
+  return E == EPI_F32_ACC || E == EPI_RESID_BF16 || E == EPI_DRELU2_BF16 || E == EPI_NS_POLY ||
+         E == EPI_NS_UPDATE;
+}
+
+// Per-lane output pointers of one wave's tile: element (row m, column n) of
+// C / C2 / C3 / D / D2 for the lane's rows m = mb + 32 i and columns
+// n = nb + 32 j + 8 g + r (mb, nb the lane's first row and column).
+struct EpiPtrs {
+  float* cf;            // C as fp32 (F32, F32_ACC, SPLITK)
+  uint16_t* cb;         // C as bf16
+  uint16_t* c2;         // lo half of hi/lo outputs
+  float* c3;            // fp32 X (NS_UPDATE; D layout)
+  const uint16_t* db;   // D as bf16
+  const uint16_t* d2;   // D2 as bf16
+  const float* df;      // D as fp32
+  long ldc, ldd;
+  float alpha, beta;
+};
+
+// What the epilogue of group (i, j, g) reads, in one 16-byte slot.
+template <int E>
+__device__ __forceinline__ uint4 epi_load(const EpiPtrs& e, int i, int j, int g) {
+  const long co = 32L * i * e.ldc + 32 * j + 8 * g;
+  const long dof = 32L * i * e.ldd + 32 * j + 8 * g;
+  uint4 r = make_uint4(0, 0, 0, 0);
+  if constexpr (E == EPI_F32_ACC) {
+    if (e.beta != 0.f) r = *reinterpret_cast<const uint4*>(e.cf + co);
   } else if constexpr (E == EPI_RESID_BF16) {
-    uint16_t* c = reinterpret_cast<uint16_t*>(p.c) + off;
-    float o[4];
-    load_bf16x4(c, o);
-    store_bf16x4(c, o[0] + v[0], o[1] + v[1], o[2] + v[2], o[3] + v[3]);
+    const uint2 u = *reinterpret_cast<const uint2*>(e.cb + co);
+    r.x = u.x;
+    r.y = u.y;
   } else if constexpr (E == EPI_DRELU2_BF16) {
-    // d relu(u)^2 / du = 2 relu(u) = 2 sqrt(h), h = relu(u)^2 as stored.
-    float hh[4];
-    load_bf16x4(reinterpret_cast<const uint16_t*>(p.d) + doff, hh);
-    store_bf16x4(reinterpret_cast<uint16_t*>(p.c) + off, 2.f * v[0] * sqrtf(hh[0]), 2.f * v[1] * sqrtf(hh[1]),
-                 2.f * v[2] * sqrtf(hh[2]), 2.f * v[3] * sqrtf(hh[3]));
+    const uint2 u = *reinterpret_cast<const uint2*>(e.db + dof);
+    r.x = u.x;
+    r.y = u.y;
+  } else if constexpr (E == EPI_NS_POLY) {
+    const uint2 h = *reinterpret_cast<const uint2*>(e.db + dof);
+    const uint2 l = *reinterpret_cast<const uint2*>(e.d2 + dof);
+    r = make_uint4(h.x, h.y, l.x, l.y);
+  } else if constexpr (E == EPI_NS_UPDATE) {
+    r = *reinterpret_cast<const uint4*>(e.df + dof);
+  }
+  return r;
+}
+
+// Epilogue of group (i, j, g) for a compile-time mode; v are the four
+// accumulators, `in` what epi_load returned.
+template <int E>
+__device__ __forceinline__ void epi4(const EpiPtrs& e, int i, int j, int g, const float* v, const uint4& in) {
+  const long co = 32L * i * e.ldc + 32 * j + 8 * g;
+  const long dof = 32L * i * e.ldd + 32 * j + 8 * g;
+  if constexpr (E == EPI_F32 || E == EPI_SPLITK) {
+    *reinterpret_cast<float4*>(e.cf + co) =
+        make_float4(e.alpha * v[0], e.alpha * v[1], e.alpha * v[2], e.alpha * v[3]);
+  } else if constexpr (E == EPI_F32_ACC) {
+    const float4 o = __builtin_bit_cast(float4, in);
+    *reinterpret_cast<float4*>(e.cf + co) =
+        make_float4(e.beta * o.x + e.alpha * v[0], e.beta * o.y + e.alpha * v[1],
+                    e.beta * o.z + e.alpha * v[2], e.beta * o.w + e.alpha * v[3]);
+  } else if constexpr (E == EPI_BF16) {
+    store_bf16x4(e.cb + co, e.alpha * v[0], e.alpha * v[1], e.alpha * v[2], e.alpha * v[3]);
+  } else if constexpr (E == EPI_RELU_BF16) {
+    store_bf16x4(e.cb + co, fmaxf(v[0], 0.f), fmaxf(v[1], 0.f), fmaxf(v[2], 0.f), fmaxf(v[3], 0.f));
+  } else if constexpr (E == EPI_RESID_BF16) {
+    store_bf16x4(e.cb + co, bf_lo(in.x) + v[0], bf_hi(in.x) + v[1], bf_lo(in.y) + v[2], bf_hi(in.y) + v[3]);
+  } else if constexpr (E == EPI_DRELU2_BF16) {
+    // d relu(u)^2 / du = 2 relu(u) = 2 sqrt(h), h = relu(u)^2 as stored
+    // (v_sqrt_f32 directly: its ~1 ulp is far below the bf16 output's).
+    store_bf16x4(e.cb + co, 2.f * v[0] * __builtin_amdgcn_sqrtf(bf_lo(in.x)),
+                 2.f * v[1] * __builtin_amdgcn_sqrtf(bf_hi(in.x)), 2.f * v[2] * __builtin_amdgcn_sqrtf(bf_lo(in.y)),
+                 2.f * v[3] * __builtin_amdgcn_sqrtf(bf_hi(in.y)));
   } else if constexpr (E == EPI_RELU2_BF16) {
     const float r0 = fmaxf(v[0], 0.f), r1 = fmaxf(v[1], 0.f), r2 = fmaxf(v[2], 0.f), r3 = fmaxf(v[3], 0.f);
-    store_bf16x4(reinterpret_cast<uint16_t*>(p.c) + off, r0 * r0, r1 * r1, r2 * r2, r3 * r3);
-  } else if constexpr (E == EPI_SPLITK) {
-    *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.c) + off + (long)si * p.s_split) =
-        make_float4(v[0], v[1], v[2], v[3]);
+    store_bf16x4(e.cb + co, r0 * r0, r1 * r1, r2 * r2, r3 * r3);
   } else if constexpr (E == EPI_HILO) {
-    float w[4] = {p.alpha * v[0], p.alpha * v[1], p.alpha * v[2], p.alpha * v[3]};
-    store_hilo4(reinterpret_cast<uint16_t*>(p.c) + off, reinterpret_cast<uint16_t*>(p.c2) + off, w);
+    float w[4] = {e.alpha * v[0], e.alpha * v[1], e.alpha * v[2], e.alpha * v[3]};
+    store_hilo4(e.cb + co, e.c2 + co, w);
   } else if constexpr (E == EPI_NS_POLY) {
-    float h[4], l[4], w[4];
-    load_bf16x4(reinterpret_cast<const uint16_t*>(p.d) + doff, h);
-    load_bf16x4(reinterpret_cast<const uint16_t*>(p.d2) + doff, l);
+    const float h[4] = {bf_lo(in.x), bf_hi(in.x), bf_lo(in.y), bf_hi(in.y)};
+    const float l[4] = {bf_lo(in.z), bf_hi(in.z), bf_lo(in.w), bf_hi(in.w)};
+    float w[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) w[r] = p.alpha * v[r] + p.beta * (h[r] + l[r]);
-    store_hilo4(reinterpret_cast<uint16_t*>(p.c) + off, reinterpret_cast<uint16_t*>(p.c2) + off, w);
+    for (int r = 0; r < 4; ++r) w[r] = e.alpha * v[r] + e.beta * (h[r] + l[r]);
+    store_hilo4(e.cb + co, e.c2 + co, w);
   } else if constexpr (E == EPI_NS_UPDATE) {
-    const float4 x = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.d) + doff);
-    float w[4] = {p.alpha * v[0] + p.beta * x.x, p.alpha * v[1] + p.beta * x.y,
-                  p.alpha * v[2] + p.beta * x.z, p.alpha * v[3] + p.beta * x.w};
-    *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.c3) + doff) = make_float4(w[0], w[1], w[2], w[3]);
-    store_hilo4(reinterpret_cast<uint16_t*>(p.c) + off, reinterpret_cast<uint16_t*>(p.c2) + off, w);
+    const float4 x = __builtin_bit_cast(float4, in);
+    float w[4] = {e.alpha * v[0] + e.beta * x.x, e.alpha * v[1] + e.beta * x.y,
+                  e.alpha * v[2] + e.beta * x.z, e.alpha * v[3] + e.beta * x.w};
+    *reinterpret_cast<float4*>(e.c3 + dof) = make_float4(w[0], w[1], w[2], w[3]);
+    store_hilo4(e.cb + co, e.c2 + co, w);
   }
 }
 
 // Store a finished 256 x 256 tile straight from the accumulators.
 // acc[i][j][4g + r] is C(m, n) with m = m0 + wm*128 + i*32 + lane%32 and
 // n = n0 + wn*128 + j*32 + 8g + 4*(lane/32) + r.
+// Epilogues that read memory load a whole 32-row block's inputs at once and
+// issue the next block's loads before the current block's stores (the
+// blocks touch disjoint rows), so load latency is paid about once per block
+// instead of once per group. Interior tiles skip the bounds checks.
 template <int E>
 __device__ __forceinline__ void store_tile(const GemmArgs& p, const f32x16 (&acc)[4][4], int bi, int si,
                                            int m0, int n0, int wm, int wn, int lane) {
+  const int mb = m0 + wm * 128 + (lane & 31);
+  const int nb = n0 + wn * 128 + 4 * (lane >> 5);
+  const long co = (long)bi * p.sc + (long)mb * p.ldc + nb;
+  const long dof = (long)bi * p.sd + (long)mb * p.ldd + nb;
+  EpiPtrs e;
+  e.cf = reinterpret_cast<float*>(p.c) + co + (E == EPI_SPLITK ? (long)si * p.s_split : 0L);
+  e.cb = reinterpret_cast<uint16_t*>(p.c) + co;
+  e.c2 = reinterpret_cast<uint16_t*>(p.c2) + co;
+  e.c3 = reinterpret_cast<float*>(p.c3) + dof;
+  e.db = reinterpret_cast<const uint16_t*>(p.d) + dof;
+  e.d2 = reinterpret_cast<const uint16_t*>(p.d2) + dof;
+  e.df = reinterpret_cast<const float*>(p.d) + dof;
+  e.ldc = p.ldc;
+  e.ldd = p.ldd;
+  e.alpha = (E == EPI_SPLITK) ? 1.f : p.alpha;
+  e.beta = p.beta;
+  const int M = p.M, N = p.N;
+  // Straight-line code for interior tiles: with no branches between them the
+  // loads and stores keep exact wait counts instead of a full drain per group.
+  auto run = [&](auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    auto ok = [&](int i, int j, int g) { return FULL || (mb + 32 * i < M && nb + 32 * j + 8 * g < N); };
+    uint4 in[2][4][4];
+    auto load_block = [&](int i, uint4 (&dst)[4][4]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + wm * 128 + i * 32 + (lane & 31);
-    if (m >= p.M) continue;
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+        for (int g = 0; g < 4; ++g) dst[j][g] = ok(i, j, g) ? epi_load<E>(e, i, j, g) : make_uint4(0, 0, 0, 0);
+    };
+    // 16-byte inputs (fp32 or hi/lo pairs) load block by block; 8-byte ones
+    // also prefetch the next block (registers allow it).
+    constexpr bool WIDE = E == EPI_F32_ACC || E == EPI_NS_POLY || E == EPI_NS_UPDATE;
+    if constexpr (epi_reads<E>()) load_block(0, in[0]);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * 128 + j * 32 + 8 * g + 4 * (lane >> 5);
-        if (n < p.N) {
-          const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                              acc[i][j][4 * g + 3]};
-          epi4<E>(p, bi, si, m, n, v);
-        }
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (epi_reads<E>()) {
+        if (i + 1 < 4 && !WIDE) load_block(i + 1, in[(i + 1) & 1]);
+        if (i > 0 && WIDE) load_block(i, in[i & 1]);
       }
-  }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          if (ok(i, j, g)) {
+            const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                acc[i][j][4 * g + 3]};
+            epi4<E>(e, i, j, g, v, in[i & 1][j][g]);
+          }
+        }
+    }
+  };
+  if ((m0 + BM <= M) && (n0 + BN <= N))
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 }
 
 template <bool AK, bool BK_, int SQ, int EPI>
