@@ -115,14 +115,32 @@ struct SplitK {
   int k_chunk = 0;
 };
 
-// Split-K for the weight-gradient GEMMs (K = tokens, small outputs).
+// Split-K for the weight-gradient GEMMs (K = tokens, small outputs). The
+// split count fills whole rounds of workgroups over the chip's compute units
+// (one 256 x 256 workgroup per CU at a time): it maximises
+// tiles * splits / (rounds * CUs), the busy fraction of the last round
+// included, preferring fewer splits (less partial-sum traffic) on ties, with
+// at least 1024 k per split.
+constexpr int kPlanCUs = 256;  // MI355X compute units
+
 SplitK plan_splitk(long out_rows, long out_cols, long K) {
   SplitK s;
   const long tiles = ((out_rows + 255) / 256) * ((out_cols + 255) / 256);
-  long want = (512 + tiles - 1) / tiles;
   const long max_by_k = std::max<long>(1, K / 1024);
-  want = std::max<long>(1, std::min(want, max_by_k));
-  long chunk = (K + want - 1) / want;
+  long best = 1;
+  double best_eff = -1.0;
+  for (long sp = 1; sp <= std::min<long>(16, max_by_k); ++sp) {
+    const long chunk = ((K + sp - 1) / sp + 63) / 64 * 64;
+    const long real = (K + chunk - 1) / chunk;
+    const long wgs = tiles * real;
+    const long rounds = (wgs + kPlanCUs - 1) / kPlanCUs;
+    const double eff = (double)wgs / (double)(rounds * kPlanCUs);
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best = sp;
+    }
+  }
+  long chunk = (K + best - 1) / best;
   chunk = (chunk + 63) / 64 * 64;
   s.k_chunk = (int)chunk;
   s.splits = (int)((K + chunk - 1) / chunk);
