@@ -163,55 +163,101 @@ __global__ void rmsnorm_bwd_kernel(const float* __restrict__ dxn, const uint16_t
   }
 }
 
-// QK normalisation per 128-wide head then RoPE ([CT50] "1. Modelo GPT" lists
-// both). One wave per (token, head); lane j holds the rotation pair
-// (j, j + 64), so the rotation is in-lane. rstd per head is saved.
-__global__ void qknorm_rope_fwd_kernel(uint16_t* __restrict__ qkv, float* __restrict__ rstd_qk,
-                                       const float* __restrict__ cs, long N, int T, int H) {
-  const int lane = threadIdx.x & 63;
-  const long idx = blockIdx.x * (long)(blockDim.x >> 6) + (threadIdx.x >> 6);
-  if (idx >= N * 2 * H) return;
-  const long row = idx / (2 * H);
-  const int hh = (int)(idx - row * 2 * H);  // 0..H-1 q heads, H..2H-1 k heads
+// Eight lanes per (row, head): lane q of a group holds dims 8q..8q+7 and
+// 64+8q..64+8q+7, i.e. exactly its RoPE pairs (j, j+64), as two 16-byte
+// vectors; the head's sum of squares is reduced over the group's 8 lanes.
+__device__ __forceinline__ float group8_sum(float v) {
+  v += __shfl_xor(v, 1, 64);
+  v += __shfl_xor(v, 2, 64);
+  v += __shfl_xor(v, 4, 64);
+  return v;
+}
+// cos / sin of pairs 8q .. 8q+7 at position t (table rows of 64 (cos, sin)).
+__device__ __forceinline__ void rope8(const float* __restrict__ cs, int t, int q, float* c, float* sn) {
+  const float4* p = reinterpret_cast<const float4*>(cs + 2 * (t * 64 + 8 * q));
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float4 v = p[k];
+    c[2 * k] = v.x;
+    sn[2 * k] = v.y;
+    c[2 * k + 1] = v.z;
+    sn[2 * k + 1] = v.w;
+  }
+}
+
+// In-place QK-norm then RoPE on the q and k heads of qkv ([CT50] "1. Modelo
+// GPT": QK normalisation and rotary embeddings): per (token, head) of 128,
+// n = x * rstd with rstd = (mean x^2 + eps)^-1/2, then pair (j, j+64) is
+// rotated by angle t * 10000^(-j/64). rstd is saved for the backward.
+__global__ void __launch_bounds__(256) qknorm_rope_fwd_kernel(uint16_t* __restrict__ qkv,
+                                                             float* __restrict__ rstd_qk,
+                                                             const float* __restrict__ cs, long N, int T,
+                                                             int H) {
+  const long item = (blockIdx.x * (long)blockDim.x + threadIdx.x) >> 3;  // (row, head)
+  const int q = threadIdx.x & 7;
+  if (item >= N * 2 * H) return;  // whole groups of 8 leave together
+  const long row = item / (2 * H);
+  const int hh = (int)(item - row * 2 * H);  // 0..H-1 q heads, H..2H-1 k heads
   const int t = (int)(row % T);
   uint16_t* p = qkv + row * 3L * H * 128 + hh * 128;
-  const float x1 = bf2f(p[lane]);
-  const float x2 = bf2f(p[lane + 64]);
-  const float ss = warp_sum(x1 * x1 + x2 * x2);
-  const float r = rsqrtf(ss / 128.f + RMS_EPS);
-  const float n1 = x1 * r, n2 = x2 * r;
-  const float c = cs[2 * (t * 64 + lane)];
-  const float s = cs[2 * (t * 64 + lane) + 1];
-  p[lane] = (uint16_t)f2bf(n1 * c - n2 * s);
-  p[lane + 64] = (uint16_t)f2bf(n1 * s + n2 * c);
-  if (lane == 0) rstd_qk[idx] = r;
+  float x1[8], x2[8];
+  unpack8(*reinterpret_cast<const uint4*>(p + 8 * q), x1);
+  unpack8(*reinterpret_cast<const uint4*>(p + 64 + 8 * q), x2);
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss += x1[e] * x1[e] + x2[e] * x2[e];
+  const float r = rsqrtf(group8_sum(ss) / 128.f + RMS_EPS);
+  float c[8], sn[8], o1[8], o2[8];
+  rope8(cs, t, q, c, sn);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float n1 = x1[e] * r, n2 = x2[e] * r;
+    o1[e] = n1 * c[e] - n2 * sn[e];
+    o2[e] = n1 * sn[e] + n2 * c[e];
+  }
+  *reinterpret_cast<uint4*>(p + 8 * q) = pack8(o1);
+  *reinterpret_cast<uint4*>(p + 64 + 8 * q) = pack8(o2);
+  if (q == 0) rstd_qk[item] = r;
 }
 
 // Backward of the above. dy = d loss / d rope(norm(x)); y = rope(norm(x)) saved.
 // dn = rope^-1(dy); n = rope^-1(y); dx = rstd * (dn - n * mean(dn * n)), and
 // mean(dn * n) = mean(dy * y) because the rotation preserves dot products.
-__global__ void qknorm_rope_bwd_kernel(uint16_t* __restrict__ dqkv, const uint16_t* __restrict__ qkv,
-                                       const float* __restrict__ rstd_qk, const float* __restrict__ cs,
-                                       long N, int T, int H) {
-  const int lane = threadIdx.x & 63;
-  const long idx = blockIdx.x * (long)(blockDim.x >> 6) + (threadIdx.x >> 6);
-  if (idx >= N * 2 * H) return;
-  const long row = idx / (2 * H);
-  const int hh = (int)(idx - row * 2 * H);
+__global__ void __launch_bounds__(256) qknorm_rope_bwd_kernel(uint16_t* __restrict__ dqkv,
+                                                             const uint16_t* __restrict__ qkv,
+                                                             const float* __restrict__ rstd_qk,
+                                                             const float* __restrict__ cs, long N, int T,
+                                                             int H) {
+  const long item = (blockIdx.x * (long)blockDim.x + threadIdx.x) >> 3;
+  const int q = threadIdx.x & 7;
+  if (item >= N * 2 * H) return;
+  const long row = item / (2 * H);
+  const int hh = (int)(item - row * 2 * H);
   const int t = (int)(row % T);
   const long off = row * 3L * H * 128 + hh * 128;
   uint16_t* g = dqkv + off;
   const uint16_t* y = qkv + off;
-  const float g1 = bf2f(g[lane]), g2 = bf2f(g[lane + 64]);
-  const float y1 = bf2f(y[lane]), y2 = bf2f(y[lane + 64]);
-  const float dot = warp_sum(g1 * y1 + g2 * y2) / 128.f;
-  const float c = cs[2 * (t * 64 + lane)];
-  const float s = cs[2 * (t * 64 + lane) + 1];
-  const float dn1 = g1 * c + g2 * s, dn2 = -g1 * s + g2 * c;
-  const float n1 = y1 * c + y2 * s, n2 = -y1 * s + y2 * c;
-  const float r = rstd_qk[idx];
-  g[lane] = (uint16_t)f2bf(r * (dn1 - n1 * dot));
-  g[lane + 64] = (uint16_t)f2bf(r * (dn2 - n2 * dot));
+  float g1[8], g2[8], y1[8], y2[8];
+  unpack8(*reinterpret_cast<const uint4*>(g + 8 * q), g1);
+  unpack8(*reinterpret_cast<const uint4*>(g + 64 + 8 * q), g2);
+  unpack8(*reinterpret_cast<const uint4*>(y + 8 * q), y1);
+  unpack8(*reinterpret_cast<const uint4*>(y + 64 + 8 * q), y2);
+  float dot = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dot += g1[e] * y1[e] + g2[e] * y2[e];
+  dot = group8_sum(dot) / 128.f;
+  const float r = rstd_qk[item];
+  float c[8], sn[8], o1[8], o2[8];
+  rope8(cs, t, q, c, sn);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float dn1 = g1[e] * c[e] + g2[e] * sn[e], dn2 = -g1[e] * sn[e] + g2[e] * c[e];
+    const float n1 = y1[e] * c[e] + y2[e] * sn[e], n2 = -y1[e] * sn[e] + y2[e] * c[e];
+    o1[e] = r * (dn1 - n1 * dot);
+    o2[e] = r * (dn2 - n2 * dot);
+  }
+  *reinterpret_cast<uint4*>(g + 8 * q) = pack8(o1);
+  *reinterpret_cast<uint4*>(g + 64 + 8 * q) = pack8(o2);
 }
 
 __global__ void count_targets_kernel(const int32_t* __restrict__ tgt, long N, int V, int* counter,
@@ -525,7 +571,7 @@ hipError_t launch_rmsnorm_bwd(const float* dxn, const uint16_t* xn, const float*
 hipError_t launch_qknorm_rope_fwd(uint16_t* qkv, float* rstd_qk, const float* cs, long N, int T,
                                   int H, hipStream_t s) {
   const long items = N * 2 * H;
-  hipLaunchKernelGGL(qknorm_rope_fwd_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, qkv,
+  hipLaunchKernelGGL(qknorm_rope_fwd_kernel, dim3((unsigned)((items * 8 + 255) / 256)), dim3(256), 0, s, qkv,
                      rstd_qk, cs, N, T, H);
   return hipGetLastError();
 }
@@ -533,7 +579,7 @@ hipError_t launch_qknorm_rope_fwd(uint16_t* qkv, float* rstd_qk, const float* cs
 hipError_t launch_qknorm_rope_bwd(uint16_t* dqkv, const uint16_t* qkv, const float* rstd_qk,
                                   const float* cs, long N, int T, int H, hipStream_t s) {
   const long items = N * 2 * H;
-  hipLaunchKernelGGL(qknorm_rope_bwd_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, dqkv,
+  hipLaunchKernelGGL(qknorm_rope_bwd_kernel, dim3((unsigned)((items * 8 + 255) / 256)), dim3(256), 0, s, dqkv,
                      qkv, rstd_qk, cs, N, T, H);
   return hipGetLastError();
 }

@@ -61,10 +61,11 @@ __device__ __forceinline__ int koff(int r, int c) { return r * 64 + ((c ^ ((r >>
 __device__ __forceinline__ int toff(int kr, int c) { return kr * 512 + ((c ^ ((kr & 3) << 2)) << 4); }
 
 // Issue 1 KB block `blk` (0..15) of one operand's k-block [k0, k0 + 32) into
-// an LDS stage buffer; the 4 waves issue blocks 4 wave .. 4 wave + 3.
+// the LDS stage buffer at byte address lds_op (wave-uniform); the 4 waves
+// issue blocks 4 wave .. 4 wave + 3. Rows and k past the operand are clamped.
 template <bool KMAJ>
 __device__ __forceinline__ void issue_one(const uint16_t* __restrict__ base, long ld, int row0,
-                                          int rows, int k0, int kend, char* lds_op, int blk,
+                                          int rows, int k0, int kend, uint32_t lds_op, int blk,
                                           int lane) {
   {
     const uint16_t* src;
@@ -83,16 +84,27 @@ __device__ __forceinline__ void issue_one(const uint16_t* __restrict__ base, lon
       const int gm = min(row0 + 8 * c, rows - 8);
       src = base + (long)gk * ld + gm;
     }
-    dma16(src, lds_addr(lds_op + blk * 1024));
+    dma16(src, lds_op + blk * 1024);
   }
 }
 
+// Per-lane byte offsets, relative to a full k-block's scalar base, of the
+// four 1 KB blocks wave `wave` loads (same layout as issue_one).
 template <bool KMAJ>
-__device__ __forceinline__ void issue_operand(const uint16_t* __restrict__ base, long ld, int row0,
-                                              int rows, int k0, int kend, char* lds_op, int wave,
-                                              int lane) {
+__device__ __forceinline__ void block_offsets(long ld, int wave, int lane, uint32_t (&off)[4]) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) issue_one<KMAJ>(base, ld, row0, rows, k0, kend, lds_op, wave * 4 + j, lane);
+  for (int j = 0; j < 4; ++j) {
+    const int blk = 4 * wave + j;
+    if (KMAJ) {
+      const int r = 16 * blk + (lane >> 2);
+      const int c = (lane & 3) ^ ((r >> 2) & 3);
+      off[j] = (uint32_t)(((long)r * ld + 8 * c) * 2);
+    } else {
+      const int kr = 2 * blk + (lane >> 5);
+      const int c = (lane & 31) ^ ((kr & 3) << 2);
+      off[j] = (uint32_t)(((long)kr * ld + 8 * c) * 2);
+    }
+  }
 }
 
 // Zero the k-range [kvalid, 32) of one operand's stage (tail k-block).
@@ -350,7 +362,7 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_bf16_kernel(const GemmArgs p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1;
   const int wn = wave & 1;
 
@@ -387,12 +399,56 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_bf16_kernel(const GemmArgs p) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   auto stage_a = [&](int it) { return smem + (it % NST) * STAGE_BYTES; };
-  auto issue = [&](int it) {
+  // LDS byte address of the ring, taken once; direct-load destinations are
+  // formed from it with scalar arithmetic only.
+  const uint32_t lds0 = lds_addr(smem);
+  auto stage_l = [&](int it) { return lds0 + (uint32_t)((it % NST) * STAGE_BYTES); };
+
+  // A k-block inside both operands (every tile of the d20 shapes) loads with
+  // a scalar base and per-lane offsets computed once; edge tiles and a
+  // partial last k-block take the clamping path.
+  uint32_t offa[4], offb[4];
+  block_offsets<AK>(p.lda, wave, lane, offa);
+  block_offsets<BK_>(p.ldb, wave, lane, offb);
+  const bool interior = (m0 + BM <= p.M) && (n0 + BN <= p.N);
+  struct KBlk {
+    const uint16_t* a;  // operand bases of the block's segment and batch
+    const uint16_t* b;
+    const uint16_t* sa;  // scalar bases of the block (fast path)
+    const uint16_t* sb;
+    int k0;
+    bool fast;
+  };
+  auto kblk = [&](int it) {
+    KBlk kb;
     const int seg = it / kiters;
-    const int k0 = kbeg + (it - seg * kiters) * BKD;
-    char* st = stage_a(it);
-    issue_operand<AK>(p.a[seg] + (long)bi * p.sa, p.lda, m0, p.M, k0, kend, st, wave, lane);
-    issue_operand<BK_>(p.b[seg] + (long)bi * p.sb, p.ldb, n0, p.N, k0, kend, st + OP_BYTES, wave, lane);
+    kb.k0 = kbeg + (it - seg * kiters) * BKD;
+    kb.a = p.a[seg] + (long)bi * p.sa;
+    kb.b = p.b[seg] + (long)bi * p.sb;
+    kb.sa = AK ? kb.a + (long)m0 * p.lda + kb.k0 : kb.a + (long)kb.k0 * p.lda + m0;
+    kb.sb = BK_ ? kb.b + (long)n0 * p.ldb + kb.k0 : kb.b + (long)kb.k0 * p.ldb + n0;
+    kb.fast = interior && (kb.k0 + BKD <= kend);
+    return kb;
+  };
+  // Load q (0..3: A blocks, 4..7: B blocks) of this wave's share of kb into
+  // the stage at lds_st (kb.fast is wave-uniform: a scalar branch).
+  auto load_q = [&](const KBlk& kb, uint32_t lds_st, int q) {
+    if (q < 4) {
+      if (kb.fast)
+        dma16_sv(kb.sa, offa[q], lds_st + (wave * 4 + q) * 1024);
+      else
+        issue_one<AK>(kb.a, p.lda, m0, p.M, kb.k0, kend, lds_st, wave * 4 + q, lane);
+    } else {
+      if (kb.fast)
+        dma16_sv(kb.sb, offb[q - 4], lds_st + OP_BYTES + (wave * 4 + q - 4) * 1024);
+      else
+        issue_one<BK_>(kb.b, p.ldb, n0, p.N, kb.k0, kend, lds_st + OP_BYTES, wave * 4 + q - 4, lane);
+    }
+  };
+  auto issue = [&](int it) {
+    const KBlk kb = kblk(it);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) load_q(kb, stage_l(it), q);
   };
 
   struct Frags {
@@ -496,22 +552,12 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_bf16_kernel(const GemmArgs p) {
     // MFMA pipe drains. Past the last block the fragment reads hit a stale
     // slot and are unused.
     const bool more = it + NST - 1 < nk;
-    const int nx = it + NST - 1;
-    const int nseg_i = nx / kiters;
-    const int nk0 = kbeg + (nx - nseg_i * kiters) * BKD;
-    const uint16_t* na = p.a[more ? nseg_i : 0] + (long)bi * p.sa;
-    const uint16_t* nb = p.b[more ? nseg_i : 0] + (long)bi * p.sb;
-    char* nst = stage_a(nx);
+    const KBlk kb = kblk(more ? it + NST - 1 : 0);
+    const uint32_t nst = stage_l(it + NST - 1);
     const char* rst = stage_a(it + 1);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      if (more) {
-        if (q < 4) {
-          issue_one<AK>(na, p.lda, m0, p.M, nk0, kend, nst, wave * 4 + q, lane);
-        } else {
-          issue_one<BK_>(nb, p.ldb, n0, p.N, nk0, kend, nst + OP_BYTES, wave * 4 + q - 4, lane);
-        }
-      }
+      if (more) load_q(kb, nst, q);
       if (q < 4) {
         f0.a[q] = read_frag<AK>(rst, wm * 128 + q * 32, 0, lane);
         if (SQ == 1) f0.a[q] = square_frag(f0.a[q]);
