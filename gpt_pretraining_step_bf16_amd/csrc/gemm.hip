@@ -41,7 +41,8 @@ hipError_t launch_gemm(const GemmArgs& g0, hipStream_t s) {
   if (g.splits < 1) g.splits = 1;
   if (g.k_chunk <= 0) g.k_chunk = g.K;
   if (g.splits == 1) g.k_chunk = g.K > 0 ? g.K : 1;
-  const int tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256);
+  const int tside = (g.M + 255) / 256;
+  const int tiles = g.sym ? tside * (tside + 1) / 2 : tside * ((g.N + 255) / 256);
   const dim3 grid(tiles, g.batch * g.splits);
   if (g.a_kmajor && g.b_kmajor) {
     if (g.epi == EPI_BF16 || g.epi == EPI_RELU_BF16 || g.epi == EPI_RELU2_BF16 || g.epi == EPI_RESID_BF16)

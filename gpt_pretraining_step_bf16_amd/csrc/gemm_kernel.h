@@ -211,6 +211,9 @@ struct EpiPtrs {
   const uint16_t* db;   // D as bf16
   const uint16_t* d2;   // D2 as bf16
   const float* df;      // D as fp32
+  uint16_t* cbt;        // transposed C / C2 of a symmetric output: element (n, m)
+  uint16_t* c2t;        //   at cbt[(n - nb) * ldc + (m - mb)]
+  bool tr;              // also store the tile transposed (off-diagonal symmetric tile)
   long ldc, ldd;
   float alpha, beta;
 };
@@ -239,6 +242,19 @@ __device__ __forceinline__ uint4 epi_load(const EpiPtrs& e, int i, int j, int g)
     r = *reinterpret_cast<const uint4*>(e.df + dof);
   }
   return r;
+}
+
+// Transposed hi/lo store of group (i, j, g) of a symmetric output:
+// C(n + r, m) for the lane's row m and columns n .. n+3 (consecutive lanes
+// hold consecutive m, so each store coalesces across the wave).
+__device__ __forceinline__ void store_hilo4_t(const EpiPtrs& e, int i, int j, int g, const float* w) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const long o = (long)(32 * j + 8 * g + r) * e.ldc + 32 * i;
+    const uint32_t h = f2bf(w[r]);
+    e.cbt[o] = (uint16_t)h;
+    e.c2t[o] = (uint16_t)f2bf(w[r] - bf2f(h));
+  }
 }
 
 // Epilogue of group (i, j, g) for a compile-time mode; v are the four
@@ -273,6 +289,7 @@ __device__ __forceinline__ void epi4(const EpiPtrs& e, int i, int j, int g, cons
   } else if constexpr (E == EPI_HILO) {
     float w[4] = {e.alpha * v[0], e.alpha * v[1], e.alpha * v[2], e.alpha * v[3]};
     store_hilo4(e.cb + co, e.c2 + co, w);
+    if (e.tr) store_hilo4_t(e, i, j, g, w);
   } else if constexpr (E == EPI_NS_POLY) {
     const float h[4] = {bf_lo(in.x), bf_hi(in.x), bf_lo(in.y), bf_hi(in.y)};
     const float l[4] = {bf_lo(in.z), bf_hi(in.z), bf_lo(in.w), bf_hi(in.w)};
@@ -280,6 +297,7 @@ __device__ __forceinline__ void epi4(const EpiPtrs& e, int i, int j, int g, cons
 #pragma unroll
     for (int r = 0; r < 4; ++r) w[r] = e.alpha * v[r] + e.beta * (h[r] + l[r]);
     store_hilo4(e.cb + co, e.c2 + co, w);
+    if (e.tr) store_hilo4_t(e, i, j, g, w);
   } else if constexpr (E == EPI_NS_UPDATE) {
     const float4 x = __builtin_bit_cast(float4, in);
     float w[4] = {e.alpha * v[0] + e.beta * x.x, e.alpha * v[1] + e.beta * x.y,
@@ -311,6 +329,10 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const f32x16 (&acc
   e.db = reinterpret_cast<const uint16_t*>(p.d) + dof;
   e.d2 = reinterpret_cast<const uint16_t*>(p.d2) + dof;
   e.df = reinterpret_cast<const float*>(p.d) + dof;
+  const long cot = (long)bi * p.sc + (long)nb * p.ldc + mb;
+  e.cbt = reinterpret_cast<uint16_t*>(p.c) + cot;
+  e.c2t = reinterpret_cast<uint16_t*>(p.c2) + cot;
+  e.tr = p.sym && (m0 != n0);
   e.ldc = p.ldc;
   e.ldd = p.ldd;
   e.alpha = (E == EPI_SPLITK) ? 1.f : p.alpha;
@@ -370,15 +392,27 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_bf16_kernel(const GemmArgs p) {
   const int tiles_m = (p.M + BM - 1) / BM;
   const int tiles_n = (p.N + BN - 1) / BN;
   const int ntiles = tiles_m * tiles_n;
-  int bid = blockIdx.x;
-  if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);
-  constexpr int GM = 4;
-  const int group = bid / (GM * tiles_n);
-  const int first_m = group * GM;
-  const int gm = min(tiles_m - first_m, GM);
-  const int in_group = bid - group * GM * tiles_n;
-  const int tm = first_m + in_group % gm;
-  const int tn = in_group / gm;
+  int tm, tn;
+  if (p.sym) {
+    // Upper triangle tm <= tn, row by row.
+    int r = blockIdx.x;
+    tm = 0;
+    while (r >= tiles_m - tm) {
+      r -= tiles_m - tm;
+      ++tm;
+    }
+    tn = tm + r;
+  } else {
+    int bid = blockIdx.x;
+    if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);
+    constexpr int GM = 4;
+    const int group = bid / (GM * tiles_n);
+    const int first_m = group * GM;
+    const int gm = min(tiles_m - first_m, GM);
+    const int in_group = bid - group * GM * tiles_n;
+    tm = first_m + in_group % gm;
+    tn = in_group / gm;
+  }
   const int m0 = tm * BM;
   const int n0 = tn * BN;
 

@@ -3,7 +3,7 @@
 #include "gemm_kernel.h"
 
 hipError_t launch_gemm_kk_aux(const GemmArgs& g, dim3 grid, hipStream_t s) {
-  if (g.square != 0) return hipErrorInvalidValue;
+  if (g.sym != 0 && (g.epi != EPI_NS_POLY || g.M != g.N)) return hipErrorInvalidValue;
   switch (g.epi) {
     case EPI_F32: GEMM_LAUNCH(true, true, 0, EPI_F32); break;
     case EPI_F32_ACC: GEMM_LAUNCH(true, true, 0, EPI_F32_ACC); break;

@@ -2,7 +2,7 @@
 #include "gemm_kernel.h"
 
 hipError_t launch_gemm_kk_fwd(const GemmArgs& g, dim3 grid, hipStream_t s) {
-  if (g.square != 0) return hipErrorInvalidValue;
+  if (g.sym != 0) return hipErrorInvalidValue;
   switch (g.epi) {
     case EPI_BF16: GEMM_LAUNCH(true, true, 0, EPI_BF16); break;
     case EPI_RELU_BF16: GEMM_LAUNCH(true, true, 0, EPI_RELU_BF16); break;

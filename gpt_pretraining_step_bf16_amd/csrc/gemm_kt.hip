@@ -3,7 +3,7 @@
 #include "gemm_kernel.h"
 
 hipError_t launch_gemm_kt(const GemmArgs& g, dim3 grid, hipStream_t s) {
-  if (g.square != 0) return hipErrorInvalidValue;
+  if (g.sym != 0) return hipErrorInvalidValue;
   if (g.a_kmajor) {
     switch (g.epi) {
       case EPI_DRELU2_BF16: GEMM_LAUNCH(true, false, 0, EPI_DRELU2_BF16); break;

@@ -73,8 +73,15 @@ enum { PROF_GEMM = 0, PROF_ATTN_FWD = 1, PROF_ATTN_BWD = 2, PROF_NS = 3, PROF_NC
 // Thread-local current model for the GEMM helpers' profiling.
 thread_local gpt_model* g_prof_model = nullptr;
 
+// MFMA work a launch executes (all K segments; a symmetric launch computes
+// only the T (T + 1) / 2 upper-triangle tiles of its T x T tile grid).
 inline double gemm_flops(const GemmArgs& g) {
-  return 2.0 * g.M * (double)g.N * g.K * g.nseg * g.batch;
+  double f = 2.0 * g.M * (double)g.N * g.K * g.nseg * g.batch;
+  if (g.sym) {
+    const double t = (g.M + 255) / 256;
+    f *= (t + 1) / (2.0 * t);
+  }
+  return f;
 }
 
 hipError_t launch_gemm_prof(const GemmArgs& g, hipStream_t s, int cat = PROF_GEMM) {
@@ -286,6 +293,7 @@ hipError_t run_ns(char* ws, const NsPlan& p, int count, long xr, long xc, const 
     g.a_kmajor = 0; g.b_kmajor = 0;
     g.c = ah; g.c2 = al; g.ldc = xc; g.sc = xc * xc;
     g.batch = count;
+    g.sym = 1;  // A is symmetric: upper-triangle tiles only, mirrored on store
     g.epi = EPI_HILO;
     hipError_t e = launch_gemm_prof(g, s, PROF_NS);
     if (e != hipSuccess) return e;
@@ -302,6 +310,7 @@ hipError_t run_ns(char* ws, const NsPlan& p, int count, long xr, long xc, const 
     g.d = ah; g.d2 = al; g.ldd = xc; g.sd = xc * xc;
     g.alpha = c; g.beta = b;
     g.batch = count;
+    g.sym = 1;  // B = bA + cA^2 is symmetric too
     g.epi = EPI_NS_POLY;
     e = launch_gemm_prof(g, s, PROF_NS);
     if (e != hipSuccess) return e;

@@ -29,7 +29,8 @@ struct GemmArgs {
   long lda, ldb;         // leading dimensions (elements)
   long sa, sb;           // batch strides (elements)
   int a_kmajor, b_kmajor;
-  int square;            // must be 0 (no operand transform on load)
+  int sym;               // 1: C is symmetric (M == N; HILO / NS_POLY only): only tiles
+                         //    tm <= tn are computed, off-diagonal ones also stored transposed
   void* c;
   long ldc, sc;
   void* c2;
