@@ -42,6 +42,8 @@
 //  * dQ: a workgroup owns 128 queries (Q, dO in registers) and walks 64-key
 //    tiles up to the diagonal: S^T = K Q^T, dP^T = V dO^T, then
 //    dQ^T += K^T dS^T (A = K transposed).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "lds_dma.h"
@@ -344,12 +346,20 @@ __global__ void attn_bwd_delta_kernel(const uint16_t* __restrict__ o, const uint
 // Backward: dK, dV
 // ===========================================================================
 constexpr int DKDV_STAGE = 2 * TILE + 2 * QBW * 4;  // Q tile, dO tile, lse, delta
+constexpr int DKDV_NST = 4;                         // stages of the Q/dO ring
 
+// Software-pipelined over the query tiles: while the softmax / dS VALU work
+// of tile n runs, the MFMAs of S and dP for tile n+1 are issued from the same
+// wave, then dV and dK of tile n; the Q/dO ring holds tiles n .. n+2. Every
+// wave walks every tile of the workgroup (tiles entirely before a wave's keys
+// are masked to zero), so all waves keep one schedule. Each wave issues the
+// same number of direct loads per tile (waves 2 and 3 load a dummy row), so a
+// single vmcnt(0) + barrier per tile orders the ring.
 __global__ void __launch_bounds__(NTHR, 1)
     attn_bwd_dkdv_kernel(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dO,
                          const float* __restrict__ lse2, const float* __restrict__ delta,
                          uint16_t* __restrict__ dqkv, int T, int H) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * DKDV_STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[DKDV_NST * DKDV_STAGE + 256];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -396,94 +406,150 @@ __global__ void __launch_bounds__(NTHR, 1)
     }
 
   const int qb_first = (kblk * KBW) / QBW;
-  const int qb_end = (T + QBW - 1) / QBW;
+  const int ntile = (T + QBW - 1) / QBW - qb_first;
 
   TileDma tq, tg;
   tile_dma_init(tq, ld, wave, lane);
   tile_dma_init(tg, d, wave, lane);
+  float* dummy = reinterpret_cast<float*>(smem + DKDV_NST * DKDV_STAGE);
 
-  auto issue = [&](int qb, int st) {
-    char* base = smem + st * DKDV_STAGE;
-    dma_tile_fast(qbase, ld, qb * QBW, T, base, wave, lane, tq);
-    dma_tile_fast(dobase, d, qb * QBW, T, base + TILE, wave, lane, tg);
-    if (wave == 0) dma_vec64(lrow, qb * QBW, T, reinterpret_cast<float*>(base + 2 * TILE), lane);
-    if (wave == 1) dma_vec64(drow, qb * QBW, T, reinterpret_cast<float*>(base + 2 * TILE + QBW * 4), lane);
+  auto stage = [&](int st) { return smem + st * DKDV_STAGE; };
+  auto issue = [&](int n, int st) {
+    char* base = stage(st);
+    const int q0 = (qb_first + n) * QBW;
+    dma_tile_fast(qbase, ld, q0, T, base, wave, lane, tq);
+    dma_tile_fast(dobase, d, q0, T, base + TILE, wave, lane, tg);
+    float* dst = wave == 0 ? reinterpret_cast<float*>(base + 2 * TILE)
+               : wave == 1 ? reinterpret_cast<float*>(base + 2 * TILE + QBW * 4)
+                           : dummy;
+    dma_vec64(wave == 1 ? drow : lrow, q0, T, dst, lane);
   };
 
-  auto block = [&](int qb, int st) {
-    const char* qs = smem + st * DKDV_STAGE;
+  // Work unit: one 32-query half t of a 64-query tile.
+  // S = Q K^T and dP = dO V^T of half t of the tile in stage st. Fragments are
+  // read two k-steps ahead of their MFMAs (sched_group_barrier pins the
+  // order), so LDS latency hides under the previous MFMAs.
+  auto sdp = [&](int st, int t, f32x16& s, f32x16& dp) {
+    const char* qs = stage(st);
     const char* gs = qs + TILE;
-    const float* ls = reinterpret_cast<const float*>(qs + 2 * TILE);
-    const float* ds = ls + QBW;
-    if (qb * QBW + QBW - 1 < k0 || k0 >= T) return;  // every query precedes the wave's keys
-    f32x16 s[2], dp[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int v = 0; v < 16; ++v) {
+      s[v] = 0.f;
+      dp[v] = 0.f;
+    }
+    bf16x8 fq[8], fg[8];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        s[t][v] = 0.f;
-        dp[t][v] = 0.f;
+    for (int k = 0; k < 2; ++k) {
+      fq[k] = row_frag(qs, fa, 32 * t, k);
+      fg[k] = row_frag(gs, fa, 32 * t, k);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (k + 2 < 8) {
+        fq[k + 2] = row_frag(qs, fa, 32 * t, k + 2);
+        fg[k + 2] = row_frag(gs, fa, 32 * t, k + 2);
       }
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[k], as_bf16x8(kf[k]), s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fg[k], as_bf16x8(vf[k]), dp, 0, 0, 0);
+    }
+    // mask 0x100: DS read, 0x008: MFMA.
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(qs, fa, 32 * t, k), as_bf16x8(kf[k]), s[t],
-                                                       0, 0, 0);
-        dp[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(gs, fa, 32 * t, k), as_bf16x8(vf[k]),
-                                                        dp[t], 0, 0, 0);
+    for (int k = 0; k < 6; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  };
+  // P and dS of half t of tile n (stage st), packed as B operands.
+  auto softmax = [&](int n, int st, int t, f32x16& s, f32x16& dp, bf16x8 (&pf)[2], bf16x8 (&dsf)[2]) {
+    const float* ls = reinterpret_cast<const float*>(stage(st) + 2 * TILE);
+    const float* ds = ls + QBW;
+    const int qb = qb_first + n;
+    // s[v]: query qb*64 + 32t + 8(v/4) + 4hl + v%4, key kpos.
+    const bool need_mask = (qb * QBW + 32 * t < k0 + 31) || (qb * QBW + 32 * t + 32 > T);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int ql = 32 * t + 8 * g + 4 * hl;
+      const float4 l4 = *reinterpret_cast<const float4*>(ls + ql);
+      const float4 d4 = *reinterpret_cast<const float4*>(ds + ql);
+      const float lq[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float dq[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int q = qb * QBW + ql + r;
+        const int v = 4 * g + r;
+        float p = fast_exp2(fmaf(s[v], sc, -lq[r]));
+        // Visible iff kpos <= q <= T - 1 (one unsigned compare).
+        if (need_mask && (uint32_t)(q - kpos) > (uint32_t)(T - 1 - kpos)) p = 0.f;
+        s[v] = p;
+        dp[v] = p * (dp[v] - dq[r]);
       }
     }
-    // s[t][v]: query qb*64 + 32t + 8(v/4) + 4hl + v%4, key kpos.
-    const bool need_mask = (qb * QBW < k0 + 31) || (qb * QBW + QBW > T);
+    pf[0] = pack_frag(s, 0);
+    pf[1] = pack_frag(s, 8);
+    dsf[0] = pack_frag(dp, 0);
+    dsf[1] = pack_frag(dp, 8);
+  };
+  // dV^T += dO^T P and dK^T += Q^T dS for half t of the tile in stage st;
+  // the transposed fragments of dim tile dt+1 are read during the MFMAs of dt.
+  auto dvdk = [&](int st, int t, const bf16x8 (&pf)[2], const bf16x8 (&dsf)[2]) {
+    const char* qs = stage(st);
+    const char* gs = qs + TILE;
+    bf16x8 ag[2][2], aq[2][2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int u = 0; u < 2; ++u) {
+      ag[0][u] = tr_frag(gs, fa, 32 * t + 16 * u, 0);
+      aq[0][u] = tr_frag(qs, fa, 32 * t + 16 * u, 0);
+    }
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int ql = 32 * t + 8 * g + 4 * hl;
-        const float4 l4 = *reinterpret_cast<const float4*>(ls + ql);
-        const float4 d4 = *reinterpret_cast<const float4*>(ds + ql);
-        const float lq[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dq[4] = {d4.x, d4.y, d4.z, d4.w};
+    for (int dt = 0; dt < 4; ++dt) {
+      const int cb = dt & 1;
+      if (dt + 1 < 4) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int q = qb * QBW + ql + r;
-          const int v = 4 * g + r;
-          float p = fast_exp2(fmaf(s[t][v], sc, -lq[r]));
-          // Visible iff kpos <= q <= T - 1 (one unsigned compare).
-          if (need_mask && (uint32_t)(q - kpos) > (uint32_t)(T - 1 - kpos)) p = 0.f;
-          s[t][v] = p;
-          dp[t][v] = p * (dp[t][v] - dq[r]);
+        for (int u = 0; u < 2; ++u) {
+          ag[cb ^ 1][u] = tr_frag(gs, fa, 32 * t + 16 * u, dt + 1);
+          aq[cb ^ 1][u] = tr_frag(qs, fa, 32 * t + 16 * u, dt + 1);
         }
       }
-    bf16x8 pf[4], dsf[4];
 #pragma unroll
-    for (int si = 0; si < 4; ++si) {
-      pf[si] = pack_frag(s[si >> 1], 8 * (si & 1));
-      dsf[si] = pack_frag(dp[si >> 1], 8 * (si & 1));
-    }
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int si = 0; si < 4; ++si) {
-        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(gs, fa, 16 * si, dt), pf[si], dv[dt], 0, 0,
-                                                         0);
-        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(qs, fa, 16 * si, dt), dsf[si], dk[dt], 0,
-                                                         0, 0);
+      for (int u = 0; u < 2; ++u) {
+        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag[cb][u], pf[u], dv[dt], 0, 0, 0);
+        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[cb][u], dsf[u], dk[dt], 0, 0, 0);
       }
+    }
+    // Each tr_frag is two DS reads.
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int dt = 0; dt < 3; ++dt) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   };
 
-  if (qb_first < qb_end) {
-    issue(qb_first, 0);
+  // Pipeline over halves: the S / dP MFMAs of the next half are issued while
+  // the softmax of the current half runs (set A holds halves t = 0, set B
+  // halves t = 1). Tile n lives in stage n % 4; tile n+2 is loaded during
+  // tile n into the stage of tile n-2.
+  f32x16 sa, da, sb, db;
+  if (ntile > 0) {
+    issue(0, 0);
+    if (ntile > 1) issue(1, 1);
     VMCNT_BARRIER(0);
+    sdp(0, 0, sa, da);
   }
-  for (int qb = qb_first; qb < qb_end; qb += 2) {
-    if (qb + 1 < qb_end) issue(qb + 1, 1);
-    block(qb, 0);
-    VMCNT_BARRIER(0);
-    if (qb + 1 < qb_end) {
-      if (qb + 2 < qb_end) issue(qb + 2, 0);
-      block(qb + 1, 1);
-      VMCNT_BARRIER(0);
-    }
+  for (int n = 0; n < ntile; ++n) {
+    const int st = n & (DKDV_NST - 1);
+    if (n > 0) VMCNT_BARRIER(0);  // tile n+1 is in LDS; every wave is past tile n-1
+    if (n + 2 < ntile) issue(n + 2, (n + 2) & (DKDV_NST - 1));
+    bf16x8 pf[2], dsf[2];
+    softmax(n, st, 0, sa, da, pf, dsf);
+    sdp(st, 1, sb, db);
+    dvdk(st, 0, pf, dsf);
+    softmax(n, st, 1, sb, db, pf, dsf);
+    if (n + 1 < ntile) sdp((n + 1) & (DKDV_NST - 1), 0, sa, da);
+    dvdk(st, 1, pf, dsf);
   }
 
   if (kpos < T) {
