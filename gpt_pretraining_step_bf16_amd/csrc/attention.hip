@@ -33,15 +33,15 @@
 //    by more than 8 in log2 units; probabilities then stay below 2^8, so
 //    nothing overflows and the normalised result is unchanged.
 //
-// Backward (deterministic, no atomics):
-//  * delta = rowsum(dO * O) per (b, h, t).
+// Backward (deterministic, no atomics), two kernels in this order:
+//  * dQ: a workgroup owns 128 queries (Q, dO in registers) and walks 64-key
+//    tiles up to the diagonal: S^T = K Q^T, dP^T = V dO^T, then
+//    dQ^T += K^T dS^T (A = K transposed). It first forms
+//    delta = rowsum(dO * O) for its queries and writes it out.
 //  * dK/dV: a workgroup owns 128 keys (32 per wave, K and V in registers) and
 //    walks 64-query tiles of Q and dO from the diagonal: S = Q K^T and
 //    dP = dO V^T (A = Q, dO rows), then dV^T += dO^T P and dK^T += Q^T dS
-//    (A = dO, Q transposed).
-//  * dQ: a workgroup owns 128 queries (Q, dO in registers) and walks 64-key
-//    tiles up to the diagonal: S^T = K Q^T, dP^T = V dO^T, then
-//    dQ^T += K^T dS^T (A = K transposed).
+//    (A = dO, Q transposed), using the delta written by dQ.
 #include <type_traits>
 
 #include "common.h"
@@ -235,14 +235,24 @@ __global__ void __launch_bounds__(NTHR, 2)
     if (kb * KB > q0 + 31) return;  // no key of this block is visible to the wave
     f32x16 s[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[t][v] = 0.f;
+    // K fragments are read one step ahead of their MFMA.
+    bf16x8 fk[16];
+    fk[0] = row_frag(ks, fa, 0, 0);
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(ks, fa, 32 * t, k), as_bf16x8(qf[k]),
-                                                       s[t], 0, 0, 0);
+    for (int i = 0; i < 16; ++i) {
+      if (i + 1 < 16) fk[i + 1] = row_frag(ks, fa, 32 * ((i + 1) >> 3), (i + 1) & 7);
+      s[i >> 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[i], as_bf16x8(qf[i & 7]), s[i >> 3], 0, 0, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = 0; i < 15; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     // s[t][v]: key kb*64 + 32t + 8(v/4) + 4hl + v%4, query qpos (raw q.k).
     const bool need_mask = (kb * KB + KB - 1 > q0) || (kb * KB + KB > T);
     if (need_mask) {
@@ -282,12 +292,21 @@ __global__ void __launch_bounds__(NTHR, 2)
     bf16x8 pf[4];
 #pragma unroll
     for (int si = 0; si < 4; ++si) pf[si] = pack_frag(s[si >> 1], 8 * (si & 1));
+    // V^T fragments of dim tile dt+1 are read during the MFMAs of dt.
+    bf16x8 av[2][4];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int si = 0; si < 4; ++si) av[0][si] = tr_frag(vs, fa, 16 * si, 0);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int cb = dt & 1;
+      if (dt + 1 < 4) {
+#pragma unroll
+        for (int si = 0; si < 4; ++si) av[cb ^ 1][si] = tr_frag(vs, fa, 16 * si, dt + 1);
+      }
 #pragma unroll
       for (int si = 0; si < 4; ++si)
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(vs, fa, 16 * si, dt), pf[si], o[dt], 0,
-                                                        0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[cb][si], pf[si], o[dt], 0, 0, 0);
+    }
   };
 
   issue(0, 0);
@@ -317,28 +336,6 @@ __global__ void __launch_bounds__(NTHR, 2)
                        pack_bf2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv));
       }
     if (hl == 0) lse2[(long)bh * T + qpos] = m_ref * sc + log2f(l_tot);
-  }
-}
-
-// ===========================================================================
-// Backward: delta = rowsum(dO * O)
-// ===========================================================================
-__global__ void attn_bwd_delta_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dO,
-                                      float* __restrict__ delta, int T, int H, long rows) {
-  const int lane = threadIdx.x & 63;
-  const long idx = blockIdx.x * 4L + (threadIdx.x >> 6);  // (row, head)
-  if (idx >= rows * H) return;
-  const long row = idx / H;
-  const int h = (int)(idx - row * H);
-  const long off = row * (long)H * HD + h * HD + 2 * lane;
-  const uint32_t a = *reinterpret_cast<const uint32_t*>(o + off);
-  const uint32_t g = *reinterpret_cast<const uint32_t*>(dO + off);
-  float s = bf_lo(a) * bf_lo(g) + bf_hi(a) * bf_hi(g);
-  s = warp_sum(s);
-  if (lane == 0) {
-    const long b = row / T;
-    const long t = row - b * T;
-    delta[(b * H + h) * T + t] = s;
   }
 }
 
@@ -575,9 +572,9 @@ __global__ void __launch_bounds__(NTHR, 1)
 // Backward: dQ
 // ===========================================================================
 __global__ void __launch_bounds__(NTHR, 2)
-    attn_bwd_dq_kernel(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dO,
-                       const float* __restrict__ lse2, const float* __restrict__ delta,
-                       uint16_t* __restrict__ dqkv, int T, int H) {
+    attn_bwd_dq_kernel(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ o,
+                       const uint16_t* __restrict__ dO, const float* __restrict__ lse2,
+                       float* __restrict__ delta, uint16_t* __restrict__ dqkv, int T, int H) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];  // [stage][K, V]
 
   const int tid = threadIdx.x;
@@ -613,7 +610,22 @@ __global__ void __launch_bounds__(NTHR, 2)
     gf[k] = *reinterpret_cast<const uint4*>(dobase + (long)qc * d + 16 * k + 8 * hl);
   }
   const float lq = lse2[(long)bh * T + qc];
-  const float dq_ = delta[(long)bh * T + qc];
+  // delta = rowsum(dO * O) of this lane's query (the lane holds half the
+  // dims, lane ^ 32 the other half); also written out for the dK/dV kernel.
+  float dq_ = 0.f;
+  {
+    const uint16_t* orow = o + ((long)b * T + qc) * d + h * HD + 8 * hl;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint4 ov = *reinterpret_cast<const uint4*>(orow + 16 * k);
+      const uint32_t ow[4] = {ov.x, ov.y, ov.z, ov.w};
+      const uint32_t gw[4] = {gf[k].x, gf[k].y, gf[k].z, gf[k].w};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) dq_ += bf_lo(ow[w]) * bf_lo(gw[w]) + bf_hi(ow[w]) * bf_hi(gw[w]);
+    }
+    dq_ += __shfl_xor(dq_, 32, 64);
+    if (hl == 0 && qok) delta[(long)bh * T + qpos] = dq_;
+  }
 
   f32x16 acc[4];
 #pragma unroll
@@ -639,37 +651,57 @@ __global__ void __launch_bounds__(NTHR, 2)
     const char* vs = ks + TILE;
     if (kb * KB > q0 + 31) return;
     const bool need_mask = (kb * KB + KB - 1 > q0) || (kb * KB + KB > T) || (q0 + 32 > T);
-    // One 32-key half of the tile at a time (keeps two accumulators live, not four).
+    // One 32-key half of the tile at a time (keeps two accumulators live, not
+    // four); fragments are read one k-step (or one dim tile) ahead.
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      f32x16 s, dp;
+      f32x16 sv, dp;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        s[v] = 0.f;
+        sv[v] = 0.f;
         dp[v] = 0.f;
       }
+      bf16x8 fk[8], fv[8];
+      fk[0] = row_frag(ks, fa, 32 * t, 0);
+      fv[0] = row_frag(vs, fa, 32 * t, 0);
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(ks, fa, 32 * t, k), as_bf16x8(qf[k]), s, 0, 0,
-                                                    0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(vs, fa, 32 * t, k), as_bf16x8(gf[k]), dp, 0,
-                                                     0, 0);
+        if (k + 1 < 8) {
+          fk[k + 1] = row_frag(ks, fa, 32 * t, k + 1);
+          fv[k + 1] = row_frag(vs, fa, 32 * t, k + 1);
+        }
+        sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[k], as_bf16x8(qf[k]), sv, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fv[k], as_bf16x8(gf[k]), dp, 0, 0, 0);
       }
-      // s[v]: key kb*64 + 32t + 8(v/4) + 4hl + v%4, query qpos.
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int k = 0; k < 7; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      // sv[v]: key kb*64 + 32t + 8(v/4) + 4hl + v%4, query qpos.
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int key = kb * KB + 32 * t + 8 * (v >> 2) + 4 * hl + (v & 3);
-        float p = fast_exp2(fmaf(s[v], sc, -lq));
+        float p = fast_exp2(fmaf(sv[v], sc, -lq));
         if (need_mask && key > klim) p = 0.f;
         dp[v] = p * (dp[v] - dq_);
       }
       const bf16x8 ds0 = pack_frag(dp, 0);
       const bf16x8 ds1 = pack_frag(dp, 8);
+      bf16x8 ak[2][2];
+      ak[0][0] = tr_frag(ks, fa, 32 * t, 0);
+      ak[0][1] = tr_frag(ks, fa, 32 * t + 16, 0);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(ks, fa, 32 * t, dt), ds0, acc[dt], 0, 0, 0);
-        acc[dt] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(ks, fa, 32 * t + 16, dt), ds1, acc[dt], 0, 0, 0);
+        const int cb = dt & 1;
+        if (dt + 1 < 4) {
+          ak[cb ^ 1][0] = tr_frag(ks, fa, 32 * t, dt + 1);
+          ak[cb ^ 1][1] = tr_frag(ks, fa, 32 * t + 16, dt + 1);
+        }
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[cb][0], ds0, acc[dt], 0, 0, 0);
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[cb][1], ds1, acc[dt], 0, 0, 0);
       }
     }
   };
@@ -716,16 +748,12 @@ hipError_t launch_attention_bwd(const uint16_t* qkv, const uint16_t* o, const fl
                                 const uint16_t* dO, uint16_t* dqkv, float* delta, int B, int T,
                                 int H, hipStream_t s) {
   if (B <= 0 || T <= 0 || H <= 0) return hipSuccess;
-  const long rows = (long)B * T;
-  hipLaunchKernelGGL(attn_bwd_delta_kernel, dim3((unsigned)((rows * H + 3) / 4)), dim3(256), 0, s, o,
-                     dO, delta, T, H, rows);
+  // dQ first: it also writes delta = rowsum(dO * O), which dK/dV reads.
+  hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((T + QB - 1) / QB, B * H), dim3(NTHR), 0, s, qkv, o, dO,
+                     lse2, delta, dqkv, T, H);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((T + KBW - 1) / KBW, B * H), dim3(NTHR), 0, s, qkv,
                      dO, lse2, delta, dqkv, T, H);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((T + QB - 1) / QB, B * H), dim3(NTHR), 0, s, qkv, dO,
-                     lse2, delta, dqkv, T, H);
   return hipGetLastError();
 }
