@@ -314,11 +314,11 @@ __device__ __forceinline__ void epi4(const EpiPtrs& e, int i, int j, int g, cons
 // issue the next block's loads before the current block's stores (the
 // blocks touch disjoint rows), so load latency is paid about once per block
 // instead of once per group. Interior tiles skip the bounds checks.
-template <int E>
-__device__ __forceinline__ void store_tile(const GemmArgs& p, const f32x16 (&acc)[4][4], int bi, int si,
-                                           int m0, int n0, int wm, int wn, int lane) {
-  const int mb = m0 + wm * 128 + (lane & 31);
-  const int nb = n0 + wn * 128 + 4 * (lane >> 5);
+template <int E, int NJ>
+__device__ __forceinline__ void store_tile(const GemmArgs& p, const f32x16 (&acc)[4][NJ], int bi, int si,
+                                           int m0, int n0, int row_off, int col_off, int lane) {
+  const int mb = m0 + row_off + (lane & 31);
+  const int nb = n0 + col_off + 4 * (lane >> 5);
   const long co = (long)bi * p.sc + (long)mb * p.ldc + nb;
   const long dof = (long)bi * p.sd + (long)mb * p.ldd + nb;
   EpiPtrs e;
@@ -343,10 +343,10 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const f32x16 (&acc
   auto run = [&](auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
     auto ok = [&](int i, int j, int g) { return FULL || (mb + 32 * i < M && nb + 32 * j + 8 * g < N); };
-    uint4 in[2][4][4];
-    auto load_block = [&](int i, uint4 (&dst)[4][4]) {
+    uint4 in[2][NJ][4];
+    auto load_block = [&](int i, uint4 (&dst)[NJ][4]) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) dst[j][g] = ok(i, j, g) ? epi_load<E>(e, i, j, g) : make_uint4(0, 0, 0, 0);
     };
@@ -361,7 +361,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const f32x16 (&acc
         if (i > 0 && WIDE) load_block(i, in[i & 1]);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           if (ok(i, j, g)) {
@@ -610,11 +610,196 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_bf16_kernel(const GemmArgs p) {
   }
   __syncthreads();
 
-  store_tile<EPI>(p, acc, bi, si, m0, n0, wm, wn, lane);
+  store_tile<EPI, 4>(p, acc, bi, si, m0, n0, wm * 128, wn * 128, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Ping-pong variant: 8 waves in two groups of 4 (one wave of each group per
+// SIMD). Group g owns rows 128 g .. 128 g + 127 of the 256 x 256 tile; wave
+// w of a group owns 64 columns (4 x 2 MFMA tiles, 128 accumulators). The
+// groups alternate phases: while one group runs a burst of 16 MFMAs on
+// fragments already in registers, the other reads its fragments of the next
+// k-block from LDS and issues its half of a later k-block's direct loads
+// (group 0 the A operand, group 1 the B operand). Each SIMD thus always has
+// one wave issuing only MFMAs and one wave issuing only memory instructions.
+//   phase 2j:   group 0 reads k-block j (+ loads A of j+2); group 1 computes j-1
+//   phase 2j+1: group 0 computes j;  group 1 reads j (+ loads B of j+2)
+// A barrier closes every phase after vmcnt(4) (vmcnt(0) once no further
+// batch follows): each wave keeps only its most recent batch of 4 direct
+// loads in flight, so a k-block is complete before its first read, and its
+// slot (k-block j-2 in a 4-stage ring) was last read two phases earlier.
+// K (and each split's k range) must be a multiple of 32: there is no tail
+// k-block.
+// ---------------------------------------------------------------------------
+constexpr int PP_THR = 512;
+
+template <bool AK, bool BK_, int EPI>
+__global__ void __launch_bounds__(PP_THR, 1) gemm_pp_kernel(const GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int w4 = wave & 3;
+
+  const int tiles_m = (p.M + BM - 1) / BM;
+  const int tiles_n = (p.N + BN - 1) / BN;
+  const int ntiles = tiles_m * tiles_n;
+  int tm, tn;
+  if (p.sym) {
+    int r = blockIdx.x;
+    tm = 0;
+    while (r >= tiles_m - tm) {
+      r -= tiles_m - tm;
+      ++tm;
+    }
+    tn = tm + r;
+  } else {
+    int bid = blockIdx.x;
+    if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);
+    constexpr int GM = 4;
+    const int group = bid / (GM * tiles_n);
+    const int first_m = group * GM;
+    const int gm = min(tiles_m - first_m, GM);
+    const int in_group = bid - group * GM * tiles_n;
+    tm = first_m + in_group % gm;
+    tn = in_group / gm;
+  }
+  const int m0 = tm * BM;
+  const int n0 = tn * BN;
+
+  const int z = blockIdx.y;
+  const int bi = z / p.splits;
+  const int si = z - bi * p.splits;
+  const int kbeg = si * p.k_chunk;
+  const int kend = min(p.K, kbeg + p.k_chunk);
+  const int kiters = (kend - kbeg + BKD - 1) / BKD;
+  const int nk = kiters * p.nseg;
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  auto stage_a = [&](int it) { return smem + (it % NST) * STAGE_BYTES; };
+  const uint32_t lds0 = lds_addr(smem);
+  auto stage_l = [&](int it) { return lds0 + (uint32_t)((it % NST) * STAGE_BYTES); };
+
+  uint32_t off[4];
+  if (grp == 0)
+    block_offsets<AK>(p.lda, w4, lane, off);
+  else
+    block_offsets<BK_>(p.ldb, w4, lane, off);
+  const bool interior = (m0 + BM <= p.M) && (n0 + BN <= p.N);
+
+  // This wave's 4 blocks of its group's operand of k-block it.
+  auto dma_part = [&](int it) {
+    const int seg = it / kiters;
+    const int k0 = kbeg + (it - seg * kiters) * BKD;
+    const bool fast = interior && (k0 + BKD <= kend);
+    const uint32_t st = stage_l(it);
+    if (grp == 0) {
+      const uint16_t* a = p.a[seg] + (long)bi * p.sa;
+      const uint16_t* sa = AK ? a + (long)m0 * p.lda + k0 : a + (long)k0 * p.lda + m0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (fast)
+          dma16_sv(sa, off[q], st + (w4 * 4 + q) * 1024);
+        else
+          issue_one<AK>(a, p.lda, m0, p.M, k0, kend, st, w4 * 4 + q, lane);
+      }
+    } else {
+      const uint16_t* b = p.b[seg] + (long)bi * p.sb;
+      const uint16_t* sb = BK_ ? b + (long)n0 * p.ldb + k0 : b + (long)k0 * p.ldb + n0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (fast)
+          dma16_sv(sb, off[q], st + OP_BYTES + (w4 * 4 + q) * 1024);
+        else
+          issue_one<BK_>(b, p.ldb, n0, p.N, k0, kend, st + OP_BYTES, w4 * 4 + q, lane);
+      }
+    }
+  };
+
+  bf16x8 fa[2][4], fb[2][2];
+  auto load_frags = [&](int it) {
+    const char* st = stage_a(it);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[ks][i] = read_frag<AK>(st, 128 * grp + 32 * i, ks, lane);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) fb[ks][j] = read_frag<BK_>(st + OP_BYTES, 64 * w4 + 32 * j, ks, lane);
+    }
+  };
+  auto compute = [&]() {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][j], fa[ks][i], acc[i][j], 0, 0, 0);
+  };
+  // Phases: each group runs the same straight-line loop (fragment loads,
+  // barrier, MFMA burst, barrier); group 1 starts one barrier later. Every
+  // k-block is full (the launcher only uses this kernel when K, and each
+  // split's k range, are multiples of 32).
+  // A phase ends with vmcnt(4) (this wave's newest batch may stay in flight)
+  // while batches keep coming, and with vmcnt(0) once none follows: the last
+  // batch must have landed before its k-block's first read.
+  auto phase_end = [&](bool more) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (more)
+      asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto run = [&]() {
+#pragma nounroll
+    for (int j = 0; j < nk; ++j) {
+      const bool more = j + 2 < nk;
+      load_frags(j);
+      if (more) dma_part(j + 2);
+      phase_end(more);
+      compute();
+      phase_end(more);
+    }
+  };
+  if (nk > 0) dma_part(0);
+  if (nk > 1) dma_part(1);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  if (grp == 0) {
+    run();
+    phase_end(false);
+  } else {
+    phase_end(false);
+    run();
+  }
+  __syncthreads();
+
+  store_tile<EPI, 2>(p, acc, bi, si, m0, n0, 128 * grp, 64 * w4, lane);
 }
 
 }  // namespace gemm_impl
 
-// Launch one instantiation: one workgroup per 256 x 256 tile and (batch, split).
-#define GEMM_LAUNCH(AK, BK, SQ, EPI) \
-  hipLaunchKernelGGL((gemm_impl::gemm_bf16_kernel<AK, BK, SQ, EPI>), grid, dim3(gemm_impl::NTHR), 0, s, g)
+// Launch one instantiation: one workgroup per 256 x 256 tile and (batch,
+// split). The ping-pong kernel needs whole 32-wide k-blocks; otherwise the
+// single-group kernel (which zeroes a partial last k-block) runs.
+inline bool gemm_pp_ok(const GemmArgs& g) {
+  return g.K % gemm_impl::BKD == 0 && (g.splits == 1 || g.k_chunk % gemm_impl::BKD == 0);
+}
+#define GEMM_LAUNCH(AK, BK, SQ, EPI)                                                                  \
+  do {                                                                                                \
+    if (gemm_pp_ok(g))                                                                                \
+      hipLaunchKernelGGL((gemm_impl::gemm_pp_kernel<AK, BK, EPI>), grid, dim3(gemm_impl::PP_THR), 0, s, \
+                         g);                                                                          \
+    else                                                                                              \
+      hipLaunchKernelGGL((gemm_impl::gemm_bf16_kernel<AK, BK, SQ, EPI>), grid, dim3(gemm_impl::NTHR), 0, \
+                         s, g);                                                                       \
+  } while (0)

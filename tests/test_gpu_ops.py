@@ -23,9 +23,12 @@ def _rand_bf16(rng, shape, scale=1.0):
 # ----------------------------------------------------------------------------
 # GEMM: every operand layout, several epilogues, ragged M / N / K tails
 # ----------------------------------------------------------------------------
+# K = 328 has a partial last k-block (single-group kernel); K = 320 has whole
+# k-blocks (ping-pong kernel, with ragged M / N edge tiles).
+@pytest.mark.parametrize("K", [328, 320])
 @pytest.mark.parametrize("a_kmajor,b_kmajor", [(1, 1), (1, 0), (0, 1), (0, 0)])
-def test_gemm_layouts_fp32_out(a_kmajor, b_kmajor):
-    M, N, K, batch = 520, 264, 328, 2
+def test_gemm_layouts_fp32_out(a_kmajor, b_kmajor, K):
+    M, N, batch = 520, 264, 2
     log(f"gemm layouts a_kmajor={a_kmajor} b_kmajor={b_kmajor} M={M} N={N} K={K}")
     rng = np.random.default_rng(10 + 2 * a_kmajor + b_kmajor)
     Ab, Af = _rand_bf16(rng, (batch, M, K))
