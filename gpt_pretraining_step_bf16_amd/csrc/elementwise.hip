@@ -51,22 +51,25 @@ __global__ void rope_table_kernel(float* cs, int T) {
   cs[2 * i + 1] = (float)s;
 }
 
-// x[i] = wte[tok[i]] ([CT50] "1. Modelo GPT": untied input embedding).
+// x[i] = wte[tok[i]] ([CT50] "1. Modelo GPT": untied input embedding). The
+// residual stream x is kept in fp32.
 __global__ void embed_fwd_kernel(const int32_t* __restrict__ tok, const uint16_t* __restrict__ wte,
-                                 uint16_t* __restrict__ x, int* err, long N, int d, int V) {
+                                 float* __restrict__ x, int* err, long N, int d, int V) {
   const int chunks = d / 8;
   for (long c = blockIdx.x * (long)blockDim.x + threadIdx.x; c < N * chunks;
        c += (long)gridDim.x * blockDim.x) {
     const long i = c / chunks;
     const int k = (int)(c - i * chunks);
     const int t = tok[i];
-    uint4 v = make_uint4(0, 0, 0, 0);
+    float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (t >= 0 && t < V) {
-      v = *reinterpret_cast<const uint4*>(wte + (long)t * d + 8 * k);
+      unpack8(*reinterpret_cast<const uint4*>(wte + (long)t * d + 8 * k), f);
     } else if (k == 0) {
       atomicOr(err, GPT_DEV_ETOKEN);
     }
-    *reinterpret_cast<uint4*>(x + i * d + 8 * k) = v;
+    float4* dst = reinterpret_cast<float4*>(x + i * d + 8 * k);
+    dst[0] = make_float4(f[0], f[1], f[2], f[3]);
+    dst[1] = make_float4(f[4], f[5], f[6], f[7]);
   }
 }
 
@@ -89,29 +92,27 @@ __global__ void embed_bwd_kernel(const int32_t* __restrict__ tok, const float* _
   }
 }
 
-// Parameter-free RMSNorm: xn = x * rstd, rstd = (mean(x^2) + eps)^-1/2.
-__global__ void rmsnorm_fwd_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ xn,
+// Parameter-free RMSNorm of the fp32 residual stream: xn = bf16(x * rstd),
+// rstd = (mean(x^2) + eps)^-1/2.
+__global__ void rmsnorm_fwd_kernel(const float* __restrict__ x, uint16_t* __restrict__ xn,
                                    float* __restrict__ rstd, long N, int d) {
   const int lane = threadIdx.x & 63;
   const long row = blockIdx.x * (long)(blockDim.x >> 6) + (threadIdx.x >> 6);
   if (row >= N) return;
-  const uint16_t* xr = x + row * d;
+  const float4* xr = reinterpret_cast<const float4*>(x + row * d);
   const int chunks = d / 8;
   float ss = 0.f;
   for (int c = lane; c < chunks; c += 64) {
-    float f[8];
-    unpack8(*reinterpret_cast<const uint4*>(xr + 8 * c), f);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+    const float4 a = xr[2 * c], b = xr[2 * c + 1];
+    ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+    ss += b.x * b.x + b.y * b.y + b.z * b.z + b.w * b.w;
   }
   ss = warp_sum(ss);
   const float r = rsqrtf(ss / (float)d + RMS_EPS);
   uint16_t* yr = xn + row * d;
   for (int c = lane; c < chunks; c += 64) {
-    float f[8];
-    unpack8(*reinterpret_cast<const uint4*>(xr + 8 * c), f);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] *= r;
+    const float4 a = xr[2 * c], b = xr[2 * c + 1];
+    float f[8] = {a.x * r, a.y * r, a.z * r, a.w * r, b.x * r, b.y * r, b.z * r, b.w * r};
     *reinterpret_cast<uint4*>(yr + 8 * c) = pack8(f);
   }
   if (lane == 0) rstd[row] = r;
@@ -540,7 +541,7 @@ hipError_t launch_rope_table(float* cs, int T, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_embed_fwd(const int32_t* tok, const uint16_t* wte, uint16_t* x, int* err, long N,
+hipError_t launch_embed_fwd(const int32_t* tok, const uint16_t* wte, float* x, int* err, long N,
                             int d, int V, hipStream_t s) {
   hipLaunchKernelGGL(embed_fwd_kernel, dim3(grid_for(N * (d / 8), 256)), dim3(256), 0, s, tok, wte, x,
                      err, N, d, V);
@@ -554,7 +555,7 @@ hipError_t launch_embed_bwd(const int32_t* tok, const float* dx, float* dwte, lo
   return hipGetLastError();
 }
 
-hipError_t launch_rmsnorm_fwd(const uint16_t* x, uint16_t* xn, float* rstd, long N, int d,
+hipError_t launch_rmsnorm_fwd(const float* x, uint16_t* xn, float* rstd, long N, int d,
                               hipStream_t s) {
   hipLaunchKernelGGL(rmsnorm_fwd_kernel, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s, x, xn, rstd,
                      N, d);

@@ -186,7 +186,7 @@ FwdPlan plan_fwd(const gpt_model& m, int B, int T) {
   p.xn2 += layers_base;
   p.rstd2 += layers_base;
   p.r += layers_base;
-  p.x = c.take(N * d * 2);
+  p.x = c.take(N * d * 4);
   p.xnf = c.take(N * d * 2);
   p.rstdf = c.take(N * 4);
   p.dx = c.take(N * d * 4);
@@ -362,6 +362,21 @@ hipError_t gemm_nt(const uint16_t* A, long lda, const uint16_t* B, long ldb, int
   return launch_gemm_prof(g, s);
 }
 
+// C[M,N] (fp32) += A[M,K] . B[N,K]^T: the update of the fp32 residual stream.
+hipError_t gemm_nt_add_f32(const uint16_t* A, long lda, const uint16_t* B, long ldb, int M, int N,
+                           int K, float* C, long ldc, hipStream_t s) {
+  GemmArgs g;
+  gemm_args_init(g);
+  g.a[0] = A; g.b[0] = B;
+  g.M = M; g.N = N; g.K = K;
+  g.lda = lda; g.ldb = ldb;
+  g.a_kmajor = 1; g.b_kmajor = 1;
+  g.c = C; g.ldc = ldc;
+  g.epi = EPI_F32_ACC;
+  g.beta = 1.f;
+  return launch_gemm_prof(g, s);
+}
+
 // C[M,N] = A[M,K] . B where B is stored [K][N] (a weight read along its out dim).
 hipError_t gemm_nn(const uint16_t* A, long lda, const uint16_t* B, long ldb, int M, int N, int K,
                    void* C, long ldc, int epi, hipStream_t s, const void* D = nullptr, long ldd = 0) {
@@ -517,7 +532,7 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
   int* n_valid = hdr + 1;
   float* cs = reinterpret_cast<float*>(ws + p.cs);
   auto lay = [&](size_t base, int l) { return ws + base + (size_t)l * p.layer_bytes; };
-  uint16_t* x = reinterpret_cast<uint16_t*>(ws + p.x);
+  float* x = reinterpret_cast<float*>(ws + p.x);
   uint16_t* xnf = reinterpret_cast<uint16_t*>(ws + p.xnf);
   float* rstdf = reinterpret_cast<float*>(ws + p.rstdf);
   float* dx = reinterpret_cast<float*>(ws + p.dx);
@@ -562,11 +577,11 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
       ProfScope ps(m, s, PROF_ATTN_FWD, 4.0 * batch * H * 128.0 * T * (T + 1) / 2.0);
       HIP_TRY(launch_attention_fwd(qkv, o, lse, batch, T, H, s));
     }
-    HIP_TRY(gemm_nt(o, d, wo, d, (int)N, d, d, x, d, EPI_RESID_BF16, s));
+    HIP_TRY(gemm_nt_add_f32(o, d, wo, d, (int)N, d, d, x, d, s));
     HIP_TRY(launch_rmsnorm_fwd(x, xn2, rstd2, N, d, s));
     // h = relu(u)^2 is stored once; the down projection reads it directly.
     HIP_TRY(gemm_nt(xn2, d, wfc, d, (int)N, F, d, r, F, EPI_RELU2_BF16, s));
-    HIP_TRY(gemm_nt(r, F, wproj, F, (int)N, d, F, x, d, EPI_RESID_BF16, s));
+    HIP_TRY(gemm_nt_add_f32(r, F, wproj, F, (int)N, d, F, x, d, s));
   }
   HIP_TRY(launch_rmsnorm_fwd(x, xnf, rstdf, N, d, s));
 

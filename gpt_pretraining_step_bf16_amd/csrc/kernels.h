@@ -69,11 +69,11 @@ hipError_t launch_attention_bwd(const uint16_t* qkv, const uint16_t* o, const fl
 hipError_t launch_fill_u32(void* p, uint32_t value, long n_words, hipStream_t s);
 hipError_t launch_f32_to_bf16(const float* in, uint16_t* out, long n, hipStream_t s);
 hipError_t launch_rope_table(float* cs, int T, hipStream_t s);  // cs [T][64][2] (cos, sin)
-hipError_t launch_embed_fwd(const int32_t* tok, const uint16_t* wte, uint16_t* x, int* err, long N,
+hipError_t launch_embed_fwd(const int32_t* tok, const uint16_t* wte, float* x, int* err, long N,
                             int d, int V, hipStream_t s);
 hipError_t launch_embed_bwd(const int32_t* tok, const float* dx, float* dwte, long N, int d, int V,
                             hipStream_t s);
-hipError_t launch_rmsnorm_fwd(const uint16_t* x, uint16_t* xn, float* rstd, long N, int d,
+hipError_t launch_rmsnorm_fwd(const float* x, uint16_t* xn, float* rstd, long N, int d,
                               hipStream_t s);
 // dx (+)= rstd * (dxn - xn * mean(dxn * xn)); also writes dx_bf16.
 hipError_t launch_rmsnorm_bwd(const float* dxn, const uint16_t* xn, const float* rstd, float* dx,

@@ -85,7 +85,7 @@ def test_gemm_epilogues():
 # ----------------------------------------------------------------------------
 # Attention forward / backward against the oracle (fp64 on the same bf16 inputs)
 # ----------------------------------------------------------------------------
-@pytest.mark.parametrize("B,T,H", [(2, 200, 2), (1, 64, 1), (1, 1, 1), (1, 333, 3), (1, 1024, 2)])
+@pytest.mark.parametrize("B,T,H", [(2, 200, 2), (1, 64, 1), (1, 1, 1), (1, 333, 3), (1, 1024, 2), (1, 4096, 2)])
 def test_attention_fwd_bwd(B, T, H):
     log(f"attention B={B} T={T} H={H}")
     rng = np.random.default_rng(T + H)

@@ -2,12 +2,15 @@
 
 Tolerances: loss |delta| <= 1e-2; every gradient tensor and every Muon update
 relative L2 <= 2e-2 (bf16 operands, fp32 accumulation against an fp64 oracle).
+gpt_fwd_bwd computes with the bf16 copy of the weights, so the oracle is given
+that copy (widened to fp64); muon_step works on the fp32 master, which both
+sides share.
 Token handling is bit-exact: embedding-gradient rows of absent tokens are 0.
 """
 import numpy as np
 import pytest
 
-from gpu_util import bits_to_f32, bf16_bits, log, rel_l2
+from gpu_util import bits_to_f32, bf16_bits, bf16_round, log, rel_l2
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -37,7 +40,8 @@ def _run_case(depth, vocab, seq, batch, seed_w=0, seed_t=1, ignore=()):
     assert st.check() == 0
     loss = float(st.loss.cpu()[0])
     grads = st.to_host(st.grads)
-    w64 = {k: v.astype(np.float64) for k, v in w.items()}
+    # The oracle gets the inputs gpt_fwd_bwd gets: the bf16 weights.
+    w64 = {k: bf16_round(v).astype(np.float64) for k, v in w.items()}
     ref_loss, ref_grads = oracle.forward_backward(w64, tok, tgt)
     return st, tok, tgt, loss, grads, ref_loss, ref_grads
 
