@@ -40,13 +40,14 @@ def flops_per_token(L, d, V, T):
 
 def gemm_bytes_per_step(L, d, V, N, chunk):
     """Algorithmic HBM bytes of the fwd/bwd GEMM launches of one step: bf16 operands
-    read once, outputs written once (fp32 for dX feeding a norm and for weight
-    gradients), epilogue operands (residual, relu^2 activations) read once."""
+    read once, outputs written once (fp32 for dX feeding a norm, for weight
+    gradients and for the residual stream), epilogue operands (the fp32 residual,
+    relu^2 activations) read once."""
     F = 4 * d
     layer = (N * d * 2 + 3 * d * d * 2 + N * 3 * d * 2            # QKV
-             + N * d * 2 + d * d * 2 + 2 * N * d * 2              # O + residual
+             + N * d * 2 + d * d * 2 + 2 * N * d * 4              # O + fp32 residual
              + N * d * 2 + F * d * 2 + N * F * 2                  # FC, relu^2
-             + N * F * 2 + F * d * 2 + 2 * N * d * 2              # proj + residual
+             + N * F * 2 + F * d * 2 + 2 * N * d * 4              # proj + fp32 residual
              + N * d * 2 + d * F * 2 + 2 * N * F * 2              # dH, relu^2' epilogue
              + N * d * 2 + N * F * 2 + F * d * 4                  # dW_proj
              + N * F * 2 + F * d * 2 + N * d * 4                  # dXn2
@@ -68,7 +69,7 @@ def ns_flops(L, d, steps=5):
 
 
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                            "gemm_bf16_kernel_d20_hbm_traffic.txt")
+                            "gemm_fwd_bwd_d20_hbm_traffic.txt")
 
 
 def gemm_traffic():
@@ -204,7 +205,7 @@ def main():
     g_bytes, g_launches = gemm_bytes_per_step(L, d, V, B * T, head_chunk)
     achieved = g_fl / (g_ms / 1e3) / 1e12 if g_ms > 0 else 0.0
     roofline = {
-        "kernel": "gemm_bf16_kernel (projection, head and weight-gradient GEMMs of fwd+bwd)",
+        "kernel": "gemm_pp_kernel + gemm_bf16_kernel (projection, head and weight-gradient GEMMs of fwd+bwd)",
         "bound": "mfma",
         "achieved": round(achieved, 2),
         "peak": PEAK_BF16_FLOPS / 1e12,

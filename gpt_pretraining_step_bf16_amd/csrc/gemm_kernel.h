@@ -630,6 +630,10 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_bf16_kernel(const GemmArgs p) {
 // slot (k-block j-2 in a 4-stage ring) was last read two phases earlier.
 // K (and each split's k range) must be a multiple of 32: there is no tail
 // k-block.
+// A wave's four direct loads of a k-block go out in one asm block from one
+// scalar pointer that advances by a k-block per issue (no per-load address
+// arithmetic, division or branch in the loop); only edge tiles take the
+// clamped per-load path.
 // ---------------------------------------------------------------------------
 constexpr int PP_THR = 512;
 
@@ -696,32 +700,45 @@ __global__ void __launch_bounds__(PP_THR, 1) gemm_pp_kernel(const GemmArgs p) {
     block_offsets<BK_>(p.ldb, w4, lane, off);
   const bool interior = (m0 + BM <= p.M) && (n0 + BN <= p.N);
 
-  // This wave's 4 blocks of its group's operand of k-block it.
+  // Direct-load state of this wave's operand (group 0: A, group 1: B): a
+  // scalar pointer to (first row, first k) of the next k-block to issue,
+  // advanced by one k-block per issue and reset at each K segment.
+  const bool opA = grp == 0;
+  const long ld = opA ? p.lda : p.ldb;
+  const bool kmaj = opA ? AK : BK_;
+  const long kstep = kmaj ? (long)BKD : (long)BKD * ld;
+  const int rc0 = opA ? m0 : n0;
+  auto seg_ptr = [&](int seg) {
+    const uint16_t* b = opA ? p.a[seg] + (long)bi * p.sa : p.b[seg] + (long)bi * p.sb;
+    return b + (kmaj ? (long)rc0 * ld + kbeg : (long)kbeg * ld + rc0);
+  };
+  const uint16_t* nxt = seg_ptr(0);
+  int nxt_seg = 0, nxt_k = 0;
+  const uint32_t op_off = opA ? 0u : (uint32_t)OP_BYTES;
+
+  // This wave's 4 blocks of its group's operand of k-block it (the next one
+  // in issue order).
   auto dma_part = [&](int it) {
-    const int seg = it / kiters;
-    const int k0 = kbeg + (it - seg * kiters) * BKD;
-    const bool fast = interior && (k0 + BKD <= kend);
-    const uint32_t st = stage_l(it);
-    if (grp == 0) {
-      const uint16_t* a = p.a[seg] + (long)bi * p.sa;
-      const uint16_t* sa = AK ? a + (long)m0 * p.lda + k0 : a + (long)k0 * p.lda + m0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (fast)
-          dma16_sv(sa, off[q], st + (w4 * 4 + q) * 1024);
-        else
-          issue_one<AK>(a, p.lda, m0, p.M, k0, kend, st, w4 * 4 + q, lane);
-      }
+    const uint32_t st = stage_l(it) + op_off;
+    if (interior) {
+      dma16_sv4(nxt, off, st + (uint32_t)(w4 * 4 * 1024));
     } else {
-      const uint16_t* b = p.b[seg] + (long)bi * p.sb;
-      const uint16_t* sb = BK_ ? b + (long)n0 * p.ldb + k0 : b + (long)k0 * p.ldb + n0;
+      const int k0 = kbeg + nxt_k * BKD;
+      if (opA) {
+        const uint16_t* a = p.a[nxt_seg] + (long)bi * p.sa;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (fast)
-          dma16_sv(sb, off[q], st + OP_BYTES + (w4 * 4 + q) * 1024);
-        else
-          issue_one<BK_>(b, p.ldb, n0, p.N, k0, kend, st + OP_BYTES, w4 * 4 + q, lane);
+        for (int q = 0; q < 4; ++q) issue_one<AK>(a, p.lda, m0, p.M, k0, kend, st, w4 * 4 + q, lane);
+      } else {
+        const uint16_t* b = p.b[nxt_seg] + (long)bi * p.sb;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) issue_one<BK_>(b, p.ldb, n0, p.N, k0, kend, st, w4 * 4 + q, lane);
       }
+    }
+    if (++nxt_k == kiters) {
+      nxt_k = 0;
+      if (++nxt_seg < p.nseg) nxt = seg_ptr(nxt_seg);
+    } else {
+      nxt += kstep;
     }
   };
 
@@ -736,23 +753,18 @@ __global__ void __launch_bounds__(PP_THR, 1) gemm_pp_kernel(const GemmArgs p) {
       for (int j = 0; j < 2; ++j) fb[ks][j] = read_frag<BK_>(st + OP_BYTES, 64 * w4 + 32 * j, ks, lane);
     }
   };
-  auto compute = [&]() {
+  auto compute_ks = [&](int ks) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][j], fa[ks][i], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][j], fa[ks][i], acc[i][j], 0, 0, 0);
   };
-  // Phases: each group runs the same straight-line loop (fragment loads,
-  // barrier, MFMA burst, barrier); group 1 starts one barrier later. Every
-  // k-block is full (the launcher only uses this kernel when K, and each
-  // split's k range, are multiples of 32).
-  // A phase ends with vmcnt(4) (this wave's newest batch may stay in flight)
-  // while batches keep coming, and with vmcnt(0) once none follows: the last
-  // batch must have landed before its k-block's first read.
-  auto phase_end = [&](bool more) {
+  auto compute = [&]() {
+    compute_ks(0);
+    compute_ks(1);
+  };
+  auto wait_bar = [&](bool more) {
     __builtin_amdgcn_sched_barrier(0);
     if (more)
       asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
@@ -766,9 +778,9 @@ __global__ void __launch_bounds__(PP_THR, 1) gemm_pp_kernel(const GemmArgs p) {
       const bool more = j + 2 < nk;
       load_frags(j);
       if (more) dma_part(j + 2);
-      phase_end(more);
+      wait_bar(more);
       compute();
-      phase_end(more);
+      wait_bar(more);
     }
   };
   if (nk > 0) dma_part(0);
@@ -776,9 +788,9 @@ __global__ void __launch_bounds__(PP_THR, 1) gemm_pp_kernel(const GemmArgs p) {
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   if (grp == 0) {
     run();
-    phase_end(false);
+    wait_bar(false);
   } else {
-    phase_end(false);
+    wait_bar(false);
     run();
   }
   __syncthreads();

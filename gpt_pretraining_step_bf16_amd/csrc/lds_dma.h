@@ -64,3 +64,28 @@ __device__ __forceinline__ void dma4(const void* gsrc, uint32_t lds_base) {
 // s_waitcnt vmcnt(N) for the immediate N, then s_barrier; both act as
 // compiler memory barriers so no LDS access moves across them.
 #define VMCNT_BARRIER(N) asm volatile("s_waitcnt vmcnt(" #N ")\n\ts_barrier" ::: "memory")
+
+// Four 16-byte-per-lane direct loads from one wave-uniform 64-bit base with
+// per-lane byte offsets v[0..3], landing in four consecutive 1 KB LDS blocks
+// from lds_base. M0 is saved once and restored once.
+__device__ __forceinline__ void dma16_sv4(const void* sbase, const uint32_t (&v)[4], uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %6\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %5\n\t"
+      "s_add_u32 m0, %6, 0x400\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %5\n\t"
+      "s_add_u32 m0, %6, 0x800\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, %5\n\t"
+      "s_add_u32 m0, %6, 0xc00\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %4, %5\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "s"(sbase), "s"(lds_base)
+      : "memory");
+}

@@ -3,9 +3,9 @@
     python -m gpt_pretraining_step_bf16_amd.profile_summary trace  KERNEL_TRACE.csv --steps S
     python -m gpt_pretraining_step_bf16_amd.profile_summary traffic FETCH.csv WRITE.csv --copy-bytes N
 
-`trace` groups the dispatches of a `--kernel-trace` run by kernel (the GEMM
-template is split into its fwd/bwd family and its Newton-Schulz family by the
-epilogue template argument) and prints launches, average duration and time
+`trace` groups the dispatches of a `--kernel-trace` run by kernel (the two GEMM
+templates, gemm_pp_kernel and gemm_bf16_kernel, are split into a fwd/bwd family
+and a Newton-Schulz family by their last template argument, the epilogue) and prints launches, average duration and time
 per step, where S is the number of steps in the traced run (warm-up
 included; every step launches the same kernels).
 
@@ -41,7 +41,7 @@ def gemm_source_hash() -> str:
 
 
 def kernel_family(name: str) -> str:
-    m = re.search(r"gemm_bf16_kernel<([^>]*)>", name)
+    m = re.search(r"gemm_(?:bf16|pp)_kernel<([^>]*)>", name)
     if m:
         args = [a.strip() for a in m.group(1).split(",")]
         epi = int(args[-1]) if args and args[-1].lstrip("-").isdigit() else -1
@@ -69,7 +69,7 @@ def summarise_trace(path: str, steps: int) -> None:
             fam[k][0] += 1
             fam[k][1] += dur
             if k.startswith("gemm"):
-                m = re.search(r"gemm_bf16_kernel<[^>]*>", name)
+                m = re.search(r"gemm_(?:bf16|pp)_kernel<[^>]*>", name)
                 inst[(k, m.group(0) if m else name[:60])][0] += 1
                 inst[(k, m.group(0) if m else name[:60])][1] += dur
     total = sum(v[1] for v in fam.values())
@@ -78,7 +78,7 @@ def summarise_trace(path: str, steps: int) -> None:
     print(f"{'ms/step':>10} {'launch/step':>11} {'avg us':>10} {'share':>6}  kernel")
     for k, (n, d) in sorted(fam.items(), key=lambda kv: -kv[1][1]):
         print(f"{d / 1e6 / steps:10.3f} {n / steps:11.1f} {d / n / 1e3:10.2f} {100 * d / total:5.1f}%  {k}")
-    print("# GEMM instantiations (template args: A k-major, B k-major, 0, epilogue id)")
+    print("# GEMM instantiations (template args: A k-major, B k-major, [0,] epilogue id)")
     for (k, i), (n, d) in sorted(inst.items(), key=lambda kv: -kv[1][1]):
         print(f"{d / 1e6 / steps:10.3f} {n / steps:11.1f} {d / n / 1e3:10.2f}         {k}: {i}")
 
