@@ -28,5 +28,6 @@ from .gpt import (  # noqa: F401
     rope_bwd,
     rope_tables,
 )
+from .adamw import adamw_step, adamw_update  # noqa: F401
 from .muon import muon_step, newton_schulz, newton_schulz_svd  # noqa: F401
 from .polar_express import greedy_minimax_triples  # noqa: F401
