@@ -3,8 +3,10 @@
 
 One step = gpt_fwd_bwd (embedding, blocks, head + cross-entropy, full
 backward) + muon_step (momentum, Newton-Schulz, update of every block matrix)
-on one microbatch of seeded synthetic tokens, with inputs and weights resident
-in HBM before the timed region. Prints one JSON line:
++ adamw_step (wte and lm_head) on one microbatch of seeded synthetic tokens,
+with inputs and weights resident in HBM before the timed region. With
+--accum K a step runs K microbatches (gradient accumulation) before the two
+optimizer calls. Prints one JSON line:
 
   value        training tokens/s (B*T*steps / wall time of the timed steps)
   mfu          value * F_tok / MI355X dense-bf16 peak, with
@@ -32,6 +34,10 @@ from gpt_pretraining_step_bf16_amd import synthetic as syn
 
 PEAK_BF16_FLOPS = 2.5166e15  # MI355X dense bf16 MFMA
 METRIC = "training tokens/sec + MFU, d20 GPT fwd+bwd+Muon step on 1 MI355X"
+# AdamW hyperparameters for wte / lm_head: the page names the optimizer only.
+# PyTorch's default betas and eps, no decay, and a rate well below the 0.02
+# init scale (early Adam steps move every element by about lr).
+ADAMW = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
 
 
 def flops_per_token(L, d, V, T):
@@ -104,15 +110,23 @@ def cpu_baseline(cfg, weights, tok, tgt):
     t0 = time.perf_counter()
     oracle.muon_step(sub_w, sub_g, sub_m, syn.MUON_LR, syn.MUON_MOMENTUM, syn.NS_COEFFS)
     t_muon_layer = time.perf_counter() - t0
-    t_step = B * t_seq + L * t_muon_layer
+    ad_w = {k: weights[k] for k in ("wte", "lm_head")}
+    ad_g = {k: (rng.standard_normal(v.shape, dtype=np.float32) * 1e-3) for k, v in ad_w.items()}
+    ad_z = {k: np.zeros_like(v) for k, v in ad_w.items()}
+    t0 = time.perf_counter()
+    oracle.adamw_step(ad_w, ad_g, ad_z, ad_z, 1, ADAMW["lr"], ADAMW["beta1"], ADAMW["beta2"], ADAMW["eps"],
+                      ADAMW["weight_decay"])
+    t_adamw = time.perf_counter() - t0
+    t_step = B * t_seq + L * t_muon_layer + t_adamw
     return {
         "value": round(B * T / t_step, 3),
         "unit": "tokens/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": (f"fp32 NumPy oracle: fwd+bwd of 1 of {B} sequences ({T} tokens, {t_seq:.2f} s) and "
-                   f"Muon of 1 of {L} layers ({t_muon_layer:.2f} s), scaled to the full step "
-                   f"(sequences and layers are independent units of equal cost)"),
+        "sample": (f"fp32 NumPy oracle: fwd+bwd of 1 of {B} sequences ({T} tokens, {t_seq:.2f} s), "
+                   f"Muon of 1 of {L} layers ({t_muon_layer:.2f} s) and AdamW of wte and lm_head "
+                   f"({t_adamw:.2f} s), scaled to the full step (sequences and layers are "
+                   f"independent units of equal cost)"),
     }
 
 
@@ -122,6 +136,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="d20", choices=sorted(syn.CONFIGS))
+    ap.add_argument("--accum", type=int, default=1,
+                    help="microbatches per optimizer step (gradient accumulation)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="launch one plain device copy of this many MiB before the steps "
@@ -160,9 +176,16 @@ def main():
         print(f"[bench] copy probe: {n * 4} bytes read and written", file=sys.stderr, flush=True)
         del src, dst
 
+    accum = max(1, args.accum)
+    opt_step = [0]
+
     def step():
-        st.fwd_bwd(tok_d, tgt_d)
+        for i in range(accum):
+            st.fwd_bwd(tok_d, tgt_d, accumulate=i > 0)
         st.muon(syn.MUON_LR, syn.MUON_MOMENTUM, syn.NS_COEFFS)
+        opt_step[0] += 1
+        st.adamw(ADAMW["lr"], ADAMW["beta1"], ADAMW["beta2"], ADAMW["eps"], ADAMW["weight_decay"],
+                 opt_step[0])
 
     for i in range(args.warmup):
         step()
@@ -191,10 +214,21 @@ def main():
         raise RuntimeError(f"non-finite loss {loss}")
 
     ms_step = elapsed_ms / args.steps
-    tokens_per_s = B * T * args.steps / (elapsed_ms / 1e3)
+    tokens_per_s = accum * B * T * args.steps / (elapsed_ms / 1e3)
     f_tok = flops_per_token(L, d, V, T)
     mfu = tokens_per_s * f_tok / PEAK_BF16_FLOPS
     mfma_work = (tokens_per_s * f_tok + ns_flops(L, d) / (ms_step / 1e3)) / PEAK_BF16_FLOPS
+    # The AdamW call alone, timed after the steps (HIP events on the current stream).
+    a0 = torch.cuda.Event(enable_timing=True)
+    a1 = torch.cuda.Event(enable_timing=True)
+    a0.record()
+    for _ in range(5):
+        opt_step[0] += 1
+        st.adamw(ADAMW["lr"], ADAMW["beta1"], ADAMW["beta2"], ADAMW["eps"], ADAMW["weight_decay"],
+                 opt_step[0])
+    a1.record()
+    torch.cuda.synchronize()
+    adamw_ms = a0.elapsed_time(a1) / 5
     for name, (ms, fl, n) in prof.items():
         tf = fl / (ms / 1e3) / 1e12 if ms > 0 else 0.0
         print(f"[bench] {name:9s} {ms / args.steps:9.2f} ms/step  {n // max(args.steps, 1):5d} launches/step"
@@ -232,8 +266,10 @@ def main():
         "data": "synthetic (seeded Zipf(1.1) token ids, N(0, 0.02) weights)",
         "config": {
             "workload": f"{args.config}: depth {L}, width {d}, {dims['heads']} heads x 128, MLP {4 * d}, "
-                        f"vocab {V}, seq {T}, microbatch {B}; fwd+bwd+Muon (5 Newton-Schulz steps)",
-            "global_batch": B,
+                        f"vocab {V}, seq {T}, microbatch {B}"
+                        + (f" x {accum} accumulated" if accum > 1 else "")
+                        + "; fwd+bwd+Muon (5 Newton-Schulz steps)+AdamW (wte, lm_head)",
+            "global_batch": accum * B,
             "seq_len": T,
             "parallelism": "none (1 GPU)",
         },
@@ -241,6 +277,7 @@ def main():
         "mfma_work_utilisation": round(mfma_work, 4),
         "loss": round(loss, 5),
         "wall_s_timed": round(wall, 3),
+        "adamw_ms": round(adamw_ms, 3),
         "roofline": roofline,
         "cpu_baseline": None,
     }

@@ -63,6 +63,8 @@ EXPORTS = {
     "gpt_fwd_bwd": (C.c_int, [_P, _P, _P, _P, _I, _I, _P, _P, _I, _P, _S, _P]),
     "muon_workspace_bytes": (C.c_size_t, [_P]),
     "muon_step": (C.c_int, [_P, _P, _P, _P, _P, _F, _F, C.POINTER(C.c_float), _I, _P, _S, _P]),
+    "adamw_state_elems": (C.c_int64, [_P]),
+    "adamw_step": (C.c_int, [_P, _P, _P, _P, _P, _P, _F, _F, _F, _F, _F, _I, _P]),
     "gpt_refresh_bf16": (C.c_int, [_P, _P, _P, _P]),
     "gpt_check": (C.c_int, [_P, _P, _P]),
     "gpt_status_str": (C.c_char_p, [C.c_int]),
@@ -183,6 +185,16 @@ class GptModel:
                              float(lr), float(momentum_coef), buf, steps, _ptr(workspace),
                              workspace.numel() * workspace.element_size(), _stream(stream))
         _check(st, "muon_step")
+
+    def adamw_state_elems(self) -> int:
+        return int(lib().adamw_state_elems(self._h))
+
+    def adamw_step(self, params, params_bf16, grads, exp_avg, exp_avg_sq, lr, beta1, beta2, eps,
+                   weight_decay, step, stream=None):
+        st = lib().adamw_step(self._h, _ptr(params), _ptr(params_bf16), _ptr(grads), _ptr(exp_avg),
+                              _ptr(exp_avg_sq), float(lr), float(beta1), float(beta2), float(eps),
+                              float(weight_decay), int(step), _stream(stream))
+        _check(st, "adamw_step")
 
     def refresh_bf16(self, params, params_bf16, stream=None):
         _check(lib().gpt_refresh_bf16(self._h, _ptr(params), _ptr(params_bf16), _stream(stream)),

@@ -10,6 +10,7 @@
 // results are run-to-run deterministic.
 #include "common.h"
 #include "kernels.h"
+#include "optimizer.h"
 
 namespace {
 
@@ -481,6 +482,54 @@ __global__ void muon_update_kernel(const MuonGroup g, const float* __restrict__ 
   }
 }
 
+// AdamW on one contiguous fp32 tensor and its moments ([CT50] "2. Otimizador
+// Muon": embeddings and lm_head are in the AdamW group). Decoupled decay scaled
+// by lr and taken from the weights before the step; bias corrections
+// bc1 = 1 - beta1^t, bc2 = 1 - beta2^t come from the host. Tensor y of the
+// grid's y dimension is at w + woff[y], with moments at state + y * n.
+struct AdamwArgs {
+  float* w;
+  uint16_t* wb;
+  const float* g;
+  float* m;
+  float* v;
+  long woff[2];
+  long n;
+  float lr, b1, b2, eps, wd, bc1, bc2;
+};
+
+__global__ void adamw_kernel(const AdamwArgs a) {
+  const long base = a.woff[blockIdx.y];
+  float* __restrict__ w = a.w + base;
+  uint16_t* __restrict__ wb = a.wb + base;
+  const float* __restrict__ g = a.g + base;
+  float* __restrict__ m = a.m + (long)blockIdx.y * a.n;
+  float* __restrict__ v = a.v + (long)blockIdx.y * a.n;
+  const long n4 = a.n / 4;
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n4; i += (long)gridDim.x * blockDim.x) {
+    const float4 gg = reinterpret_cast<const float4*>(g)[i];
+    float4 mm = reinterpret_cast<float4*>(m)[i];
+    float4 vv = reinterpret_cast<float4*>(v)[i];
+    float4 ww = reinterpret_cast<float4*>(w)[i];
+    float gv[4] = {gg.x, gg.y, gg.z, gg.w};
+    float mv[4] = {mm.x, mm.y, mm.z, mm.w};
+    float vv4[4] = {vv.x, vv.y, vv.z, vv.w};
+    float wv[4] = {ww.x, ww.y, ww.z, ww.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      mv[e] = a.b1 * mv[e] + (1.f - a.b1) * gv[e];
+      vv4[e] = a.b2 * vv4[e] + (1.f - a.b2) * (gv[e] * gv[e]);
+      const float mhat = mv[e] / a.bc1;
+      const float vhat = vv4[e] / a.bc2;
+      wv[e] = wv[e] - a.lr * a.wd * wv[e] - a.lr * mhat / (sqrtf(vhat) + a.eps);
+    }
+    reinterpret_cast<float4*>(m)[i] = make_float4(mv[0], mv[1], mv[2], mv[3]);
+    reinterpret_cast<float4*>(v)[i] = make_float4(vv4[0], vv4[1], vv4[2], vv4[3]);
+    reinterpret_cast<float4*>(w)[i] = make_float4(wv[0], wv[1], wv[2], wv[3]);
+    reinterpret_cast<uint2*>(wb)[i] = make_uint2(pack_bf2(wv[0], wv[1]), pack_bf2(wv[2], wv[3]));
+  }
+}
+
 // Sum of squares of each of `count` contiguous matrices of n elements.
 __global__ void sumsq_kernel(const float* __restrict__ x, long n, float* __restrict__ partials) {
   __shared__ float red[4];
@@ -626,6 +675,18 @@ hipError_t launch_muon_update(const MuonGroup& g, const float* x32, float* param
                               uint16_t* params_bf16, float lr, hipStream_t s) {
   dim3 grid((unsigned)(g.x_cols / 32), (unsigned)(g.x_rows / 32), g.count);
   hipLaunchKernelGGL(muon_update_kernel, grid, dim3(256), 0, s, g, x32, params, params_bf16, lr);
+  return hipGetLastError();
+}
+
+hipError_t launch_adamw(float* w, uint16_t* wb, const float* g, float* m, float* v, long off0, long off1,
+                        long n, float lr, float b1, float b2, float eps, float wd, float bc1, float bc2,
+                        hipStream_t s) {
+  AdamwArgs a;
+  a.w = w; a.wb = wb; a.g = g; a.m = m; a.v = v;
+  a.woff[0] = off0; a.woff[1] = off1;
+  a.n = n;
+  a.lr = lr; a.b1 = b1; a.b2 = b2; a.eps = eps; a.wd = wd; a.bc1 = bc1; a.bc2 = bc2;
+  hipLaunchKernelGGL(adamw_kernel, dim3(grid_for(n / 4, 256, 2048), 2), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

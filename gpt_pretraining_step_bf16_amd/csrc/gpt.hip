@@ -6,6 +6,7 @@
 //   [CT50] dev.to, "Como treinar seu próprio ChatGPT por 50 dólares".
 //   [HADA] GeekNews (hada.io) summary of the nanochat launch README.
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -15,6 +16,7 @@
 #include "../../include/gpt.h"
 #include "common.h"
 #include "kernels.h"
+#include "optimizer.h"
 
 namespace {
 
@@ -687,6 +689,28 @@ gpt_status muon_step(gpt_model* m, float* params, uint16_t* params_bf16, const f
     HIP_TRY(run_ns(ws, p, g.count, g.x_rows, g.x_cols, ns_coeffs, ns_steps, s));
     HIP_TRY(launch_muon_update(g, x32, params, params_bf16, lr, s));
   }
+  return GPT_OK;
+}
+
+int64_t adamw_state_elems(const gpt_model* m) {
+  if (!m) return 0;
+  return 2L * m->V * m->d;
+}
+
+gpt_status adamw_step(gpt_model* m, float* params, uint16_t* params_bf16, const float* grads,
+                      float* exp_avg, float* exp_avg_sq, float lr, float beta1, float beta2, float eps,
+                      float weight_decay, int32_t step, void* stream) {
+  if (!m || !params || !params_bf16 || !grads || !exp_avg || !exp_avg_sq) return GPT_EINVAL;
+  if (step < 1 || !(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f)) return GPT_EINVAL;
+  if (!(eps >= 0.f) || !std::isfinite(lr) || !std::isfinite(weight_decay)) return GPT_EINVAL;
+  // The moments' bias corrections, formed in double on the host.
+  const double bc1 = 1.0 - std::pow((double)beta1, (double)step);
+  const double bc2 = 1.0 - std::pow((double)beta2, (double)step);
+  if (!(bc1 > 0.0) || !(bc2 > 0.0)) return GPT_EINVAL;
+  const long n = (long)m->V * m->d;
+  HIP_TRY(launch_adamw(params, params_bf16, grads, exp_avg, exp_avg_sq, (long)m->off_wte, (long)m->off_lm,
+                       n, lr, beta1, beta2, eps, weight_decay, (float)bc1, (float)bc2,
+                       reinterpret_cast<hipStream_t>(stream)));
   return GPT_OK;
 }
 

@@ -1,8 +1,9 @@
 """Device buffers for repeated training steps (torch allocates, the HIP library computes).
 
 ``TrainState`` owns the flat fp32 parameters, their bf16 shadow, gradients,
-Muon momentum and the two workspaces, laid out as the library's tensor table
-says. A step is ``fwd_bwd`` (loss + gradients) followed by ``muon``.
+Muon momentum, the AdamW moments of wte and lm_head and the two workspaces,
+laid out as the library's tensor table says. A step is ``fwd_bwd`` (loss +
+gradients) followed by ``muon`` (block matrices) and ``adamw`` (wte, lm_head).
 """
 from __future__ import annotations
 
@@ -28,6 +29,10 @@ class TrainState:
         self.loss = torch.zeros(1, dtype=torch.float32, device=device)
         self.ws = torch.empty(self.model.workspace_bytes(batch, seq), dtype=torch.uint8, device=device)
         self.muon_ws = torch.empty(self.model.muon_workspace_bytes(), dtype=torch.uint8, device=device)
+        # AdamW moments of wte and lm_head (packed: wte, then lm_head).
+        na = self.model.adamw_state_elems()
+        self.exp_avg = torch.zeros(na, dtype=torch.float32, device=device)
+        self.exp_avg_sq = torch.zeros(na, dtype=torch.float32, device=device)
 
     # -- host <-> device ------------------------------------------------------
     def flatten(self, arrays: dict) -> np.ndarray:
@@ -63,6 +68,10 @@ class TrainState:
     def muon(self, lr, momentum_coef, ns_coeffs):
         self.model.muon_step(self.params, self.params_bf16, self.grads, self.momentum, lr,
                              momentum_coef, ns_coeffs, self.muon_ws)
+
+    def adamw(self, lr, beta1, beta2, eps, weight_decay, step):
+        self.model.adamw_step(self.params, self.params_bf16, self.grads, self.exp_avg, self.exp_avg_sq,
+                              lr, beta1, beta2, eps, weight_decay, step)
 
     def check(self) -> int:
         return self.model.check(self.ws)

@@ -130,6 +130,28 @@ gpt_status muon_step(gpt_model* m, float* params, uint16_t* params_bf16, const f
                      float* momentum, float lr, float momentum_coef, const float* ns_coeffs,
                      int32_t ns_steps, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Elements of each AdamW moment buffer: wte then lm_head, 2 * vocab * d. */
+int64_t adamw_state_elems(const gpt_model* m);
+
+/*
+ * One AdamW step of wte and lm_head ([CT50] "2. Otimizador Muon": embeddings
+ * and lm_head are optimised by AdamW; the page gives no hyperparameters, so
+ * all of them are arguments). Per element, with t = step:
+ *   m <- beta1 m + (1 - beta1) g;   v <- beta2 v + (1 - beta2) g^2
+ *   w <- w - lr * weight_decay * w - lr * (m / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps)
+ * (decoupled decay scaled by lr, from the weights before the step).
+ *   params, params_bf16, grads  as for muon_step; only wte and lm_head change,
+ *                               and their bf16 shadow is refreshed
+ *   exp_avg, exp_avg_sq         device fp32 [adamw_state_elems(m)]: the moments
+ *                               of wte, then those of lm_head; zero before step 1
+ *   step                        1-based step count (bias correction)
+ * Returns GPT_EINVAL for null pointers, step < 1, betas outside [0, 1),
+ * eps < 0 or non-finite lr / weight_decay, before any launch.
+ */
+gpt_status adamw_step(gpt_model* m, float* params, uint16_t* params_bf16, const float* grads,
+                      float* exp_avg, float* exp_avg_sq, float lr, float beta1, float beta2, float eps,
+                      float weight_decay, int32_t step, void* stream);
+
 /* params_bf16 <- round-to-nearest-even bf16 of params, every tensor. */
 gpt_status gpt_refresh_bf16(const gpt_model* m, const float* params, uint16_t* params_bf16,
                             void* stream);

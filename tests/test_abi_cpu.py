@@ -21,13 +21,14 @@ def _declared_functions():
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
     skip = {"if", "sizeof", "defined"}
-    return sorted({n for n in names if n.startswith(("gpt_", "muon_")) and n not in skip})
+    return sorted({n for n in names if n.startswith(("gpt_", "muon_", "adamw_")) and n not in skip})
 
 
 def test_every_declared_symbol_is_exported():
     lib = C.CDLL(binding.LIB_PATH)
     declared = _declared_functions()
     assert "gpt_fwd_bwd" in declared and "muon_step" in declared and "gpt_create" in declared
+    assert "adamw_step" in declared
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(binding.EXPORTS), set(declared) ^ set(binding.EXPORTS)
@@ -117,3 +118,21 @@ def test_muon_and_op_validation():
     assert lib.gpt_op_gemm(64, 64, 64, 1, fake, 64, 0, 1, fake, 64, 0, 1, fake, 64, 0, 9, None) == binding.GPT_EINVAL
     assert lib.gpt_op_newton_schulz(fake, 1, 64, 128, buf, 5, ws, 1 << 30, None) == binding.GPT_ESHAPE
     assert binding.status_str(binding.GPT_ETOKEN).startswith("token")
+
+
+def test_adamw_state_and_host_validation_precede_any_launch():
+    m = binding.GptModel(20, 32768, 2048)
+    assert m.adamw_state_elems() == 2 * 32768 * 1280
+    lib = binding.lib()
+    fake = C.c_void_p(1 << 20)
+
+    def call(p=fake, step=1, b1=0.9, b2=0.95, eps=1e-8, lr=0.01, wd=0.0):
+        return lib.adamw_step(m.handle, p, fake, fake, fake, fake, lr, b1, b2, eps, wd, step, None)
+
+    assert call(p=None) == binding.GPT_EINVAL
+    assert call(step=0) == binding.GPT_EINVAL
+    assert call(b1=1.0) == binding.GPT_EINVAL
+    assert call(b2=-0.1) == binding.GPT_EINVAL
+    assert call(eps=-1.0) == binding.GPT_EINVAL
+    assert call(lr=float("nan")) == binding.GPT_EINVAL
+    assert lib.adamw_step(None, fake, fake, fake, fake, fake, 0.01, 0.9, 0.95, 1e-8, 0.0, 1, None) == binding.GPT_EINVAL

@@ -163,3 +163,48 @@ def test_muon_step_matches_oracle_on_identical_inputs():
         assert e < REL_TOL, (name, e)
     # The bf16 shadow is the rounded fp32 master.
     np.testing.assert_array_equal(new_bf, bf16_bits(st.params.cpu().numpy()))
+
+
+ADAMW = dict(lr=0.004, beta1=0.8, beta2=0.95, eps=1e-8, weight_decay=0.01)
+
+
+@pytest.mark.parametrize("cfg_name", ["tiny", "d20"])
+def test_adamw_step_matches_oracle(cfg_name):
+    """Two AdamW steps on wte and lm_head against the oracle from identical fp32
+    inputs: fp32 elementwise arithmetic against fp64, so the updates agree to
+    rel-L2 1e-5 and the moments to 1e-6; block matrices are untouched and the
+    bf16 shadow is the rounded fp32 master."""
+    cfg = syn.CONFIGS[cfg_name]
+    depth, vocab = cfg["depth"], cfg["vocab"]
+    log(f"adamw {cfg_name}")
+    w = syn.init_weights(depth, vocab, seed=0)
+    g1 = syn.random_like_grads(depth, vocab, seed=7, scale=1e-2)
+    g2 = syn.random_like_grads(depth, vocab, seed=9, scale=1e-3)
+    st = TrainState(depth, vocab, cfg["seq"], 1)
+    st.load_weights(w)
+    f64 = lambda d: {k: d[k].astype(np.float64) for k in ("wte", "lm_head")}
+    ref_w = {k: v.astype(np.float64) for k, v in w.items() if k in ("wte", "lm_head")}
+    ref_m = {k: np.zeros_like(v) for k, v in ref_w.items()}
+    ref_v = {k: np.zeros_like(v) for k, v in ref_w.items()}
+    a = ADAMW
+    for step, g in ((1, g1), (2, g2)):
+        st.load_grads(g)
+        st.adamw(a["lr"], a["beta1"], a["beta2"], a["eps"], a["weight_decay"], step)
+        prev = ref_w
+        ref_w, ref_m, ref_v = oracle.adamw_step(ref_w, f64(g), ref_m, ref_v, step, a["lr"], a["beta1"],
+                                                a["beta2"], a["eps"], a["weight_decay"])
+    torch.cuda.synchronize()
+    new_w = st.to_host(st.params)
+    n = vocab * syn.model_dims(depth)["d"]
+    m_dev = st.exp_avg.cpu().numpy()
+    v_dev = st.exp_avg_sq.cpu().numpy()
+    for i, k in enumerate(("wte", "lm_head")):
+        upd = w[k].astype(np.float64) - new_w[k]
+        ref_upd = w[k].astype(np.float64) - ref_w[k]
+        assert rel_l2(upd, ref_upd) < 1e-5, (k, rel_l2(upd, ref_upd))
+        assert rel_l2(m_dev[i * n:(i + 1) * n], ref_m[k].ravel()) < 1e-6
+        assert rel_l2(v_dev[i * n:(i + 1) * n], ref_v[k].ravel()) < 1e-6
+    for k in w:
+        if k not in ("wte", "lm_head"):
+            np.testing.assert_array_equal(new_w[k], w[k])
+    np.testing.assert_array_equal(st.params_bf16.cpu().numpy(), bf16_bits(st.params.cpu().numpy()))
