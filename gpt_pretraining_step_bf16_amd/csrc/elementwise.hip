@@ -119,6 +119,48 @@ __global__ void rmsnorm_fwd_kernel(const float* __restrict__ x, uint16_t* __rest
   if (lane == 0) rstd[row] = r;
 }
 
+// The same with the row held in registers between the two passes (one read of
+// x): lane l holds 8-element chunks l, l + 64, ..., at most MAXC of them.
+template <int MAXC>
+__global__ void rmsnorm_fwd_reg_kernel(const float* __restrict__ x, uint16_t* __restrict__ xn,
+                                       float* __restrict__ rstd, long N, int d) {
+  const int lane = threadIdx.x & 63;
+  const long row = blockIdx.x * (long)(blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (row >= N) return;
+  const float4* xr = reinterpret_cast<const float4*>(x + row * d);
+  const int chunks = d / 8;
+  float4 v[MAXC][2];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = lane + 64 * i;
+    if (c < chunks) {
+      v[i][0] = xr[2 * c];
+      v[i][1] = xr[2 * c + 1];
+    } else {
+      v[i][0] = v[i][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      ss += v[i][h].x * v[i][h].x + v[i][h].y * v[i][h].y + v[i][h].z * v[i][h].z + v[i][h].w * v[i][h].w;
+  ss = warp_sum(ss);
+  const float r = rsqrtf(ss / (float)d + RMS_EPS);
+  uint16_t* yr = xn + row * d;
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = lane + 64 * i;
+    if (c < chunks) {
+      const float4 a = v[i][0], bq = v[i][1];
+      float f[8] = {a.x * r, a.y * r, a.z * r, a.w * r, bq.x * r, bq.y * r, bq.z * r, bq.w * r};
+      *reinterpret_cast<uint4*>(yr + 8 * c) = pack8(f);
+    }
+  }
+  if (lane == 0) rstd[row] = r;
+}
+
 // dx (+)= rstd * (dxn - xn * mean(dxn * xn)); dx_bf16 = bf16(dx).
 __global__ void rmsnorm_bwd_kernel(const float* __restrict__ dxn, const uint16_t* __restrict__ xn,
                                    const float* __restrict__ rstd, float* __restrict__ dx,
@@ -161,6 +203,66 @@ __global__ void rmsnorm_bwd_kernel(const float* __restrict__ dxn, const uint16_t
     }
     *reinterpret_cast<float4*>(dr + 8 * c) = make_float4(o[0], o[1], o[2], o[3]);
     *reinterpret_cast<float4*>(dr + 8 * c + 4) = make_float4(o[4], o[5], o[6], o[7]);
+    *reinterpret_cast<uint4*>(br + 8 * c) = pack8(o);
+  }
+}
+
+// The backward with the row held in registers between the two passes (one
+// read of dxn and xn); lane l holds chunks l, l + 64, ..., at most MAXC.
+template <int MAXC>
+__global__ void rmsnorm_bwd_reg_kernel(const float* __restrict__ dxn, const uint16_t* __restrict__ xn,
+                                       const float* __restrict__ rstd, float* __restrict__ dx,
+                                       uint16_t* __restrict__ dxb, long N, int d, int accumulate) {
+  const int lane = threadIdx.x & 63;
+  const long row = blockIdx.x * (long)(blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (row >= N) return;
+  const float4* gr = reinterpret_cast<const float4*>(dxn + row * d);
+  const uint16_t* yr = xn + row * d;
+  const int chunks = d / 8;
+  float4 g[MAXC][2];
+  uint4 yb[MAXC];
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = lane + 64 * i;
+    if (c < chunks) {
+      yb[i] = *reinterpret_cast<const uint4*>(yr + 8 * c);
+      g[i][0] = gr[2 * c];
+      g[i][1] = gr[2 * c + 1];
+    } else {
+      yb[i] = make_uint4(0, 0, 0, 0);
+      g[i][0] = g[i][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  float dot = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    float y[8];
+    unpack8(yb[i], y);
+    dot += g[i][0].x * y[0] + g[i][0].y * y[1] + g[i][0].z * y[2] + g[i][0].w * y[3] +
+           g[i][1].x * y[4] + g[i][1].y * y[5] + g[i][1].z * y[6] + g[i][1].w * y[7];
+  }
+  dot = warp_sum(dot) / (float)d;
+  const float r = rstd[row];
+  float4* dr = reinterpret_cast<float4*>(dx + row * d);
+  uint16_t* br = dxb + row * d;
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = lane + 64 * i;
+    if (c >= chunks) continue;
+    float y[8];
+    unpack8(yb[i], y);
+    const float gg[8] = {g[i][0].x, g[i][0].y, g[i][0].z, g[i][0].w,
+                         g[i][1].x, g[i][1].y, g[i][1].z, g[i][1].w};
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = r * (gg[e] - y[e] * dot);
+    if (accumulate) {
+      const float4 a0 = dr[2 * c], a1 = dr[2 * c + 1];
+      o[0] += a0.x; o[1] += a0.y; o[2] += a0.z; o[3] += a0.w;
+      o[4] += a1.x; o[5] += a1.y; o[6] += a1.z; o[7] += a1.w;
+    }
+    dr[2 * c] = make_float4(o[0], o[1], o[2], o[3]);
+    dr[2 * c + 1] = make_float4(o[4], o[5], o[6], o[7]);
     *reinterpret_cast<uint4*>(br + 8 * c) = pack8(o);
   }
 }
@@ -606,15 +708,33 @@ hipError_t launch_embed_bwd(const int32_t* tok, const float* dx, float* dwte, lo
 
 hipError_t launch_rmsnorm_fwd(const float* x, uint16_t* xn, float* rstd, long N, int d,
                               hipStream_t s) {
-  hipLaunchKernelGGL(rmsnorm_fwd_kernel, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s, x, xn, rstd,
-                     N, d);
+  const dim3 grid((unsigned)((N + 3) / 4));
+  switch ((d / 8 + 63) / 64) {
+    case 1: hipLaunchKernelGGL(rmsnorm_fwd_reg_kernel<1>, grid, dim3(256), 0, s, x, xn, rstd, N, d); break;
+    case 2: hipLaunchKernelGGL(rmsnorm_fwd_reg_kernel<2>, grid, dim3(256), 0, s, x, xn, rstd, N, d); break;
+    case 3: hipLaunchKernelGGL(rmsnorm_fwd_reg_kernel<3>, grid, dim3(256), 0, s, x, xn, rstd, N, d); break;
+    case 4: hipLaunchKernelGGL(rmsnorm_fwd_reg_kernel<4>, grid, dim3(256), 0, s, x, xn, rstd, N, d); break;
+    default: hipLaunchKernelGGL(rmsnorm_fwd_kernel, grid, dim3(256), 0, s, x, xn, rstd, N, d); break;
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_rmsnorm_bwd(const float* dxn, const uint16_t* xn, const float* rstd, float* dx,
                               uint16_t* dx_bf16, long N, int d, int accumulate, hipStream_t s) {
-  hipLaunchKernelGGL(rmsnorm_bwd_kernel, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s, dxn, xn, rstd,
-                     dx, dx_bf16, N, d, accumulate);
+  const dim3 grid((unsigned)((N + 3) / 4));
+#define RMSB(C) hipLaunchKernelGGL(rmsnorm_bwd_reg_kernel<C>, grid, dim3(256), 0, s, dxn, xn, rstd, dx, dx_bf16, \
+                                   N, d, accumulate)
+  switch ((d / 8 + 63) / 64) {
+    case 1: RMSB(1); break;
+    case 2: RMSB(2); break;
+    case 3: RMSB(3); break;
+    case 4: RMSB(4); break;
+    default:
+      hipLaunchKernelGGL(rmsnorm_bwd_kernel, grid, dim3(256), 0, s, dxn, xn, rstd, dx, dx_bf16, N, d,
+                         accumulate);
+      break;
+  }
+#undef RMSB
   return hipGetLastError();
 }
 
