@@ -60,6 +60,39 @@ __device__ __forceinline__ int koff(int r, int c) { return r * 64 + ((c ^ ((r >>
 // Byte offset of (k-row kr, 16-byte row-chunk c) in a K-strided stage [32][256].
 __device__ __forceinline__ int toff(int kr, int c) { return kr * 512 + ((c ^ ((kr & 3) << 2)) << 4); }
 
+// Work item of this workgroup: output tile (tm, tn) and batch / split index z.
+// Workgroups are dealt round-robin over the 8 XCDs in launch order, so the
+// linear launch index is remapped to give consecutive work items (the tiles of
+// one matrix, then those of the next) to one XCD, whose L2 then holds their
+// shared operand panels; within a matrix, tiles go 4 tile-rows at a time along
+// N. A symmetric output enumerates its upper triangle tm <= tn.
+__device__ __forceinline__ void tile_coords(const GemmArgs& p, int& tm, int& tn, int& z) {
+  const int tiles_m = (p.M + BM - 1) / BM;
+  const int tiles_n = (p.N + BN - 1) / BN;
+  const int per = gridDim.x;
+  const int total = per * gridDim.y;
+  int lin = blockIdx.x + per * blockIdx.y;
+  if ((total & 7) == 0) lin = (lin & 7) * (total >> 3) + (lin >> 3);
+  z = lin / per;
+  int t = lin - z * per;
+  if (p.sym) {
+    tm = 0;
+    while (t >= tiles_m - tm) {
+      t -= tiles_m - tm;
+      ++tm;
+    }
+    tn = tm + t;
+  } else {
+    constexpr int GM = 4;
+    const int group = t / (GM * tiles_n);
+    const int first_m = group * GM;
+    const int gm = min(tiles_m - first_m, GM);
+    const int in_group = t - group * GM * tiles_n;
+    tm = first_m + in_group % gm;
+    tn = in_group / gm;
+  }
+}
+
 // Issue 1 KB block `blk` (0..15) of one operand's k-block [k0, k0 + 32) into
 // the LDS stage buffer at byte address lds_op (wave-uniform); the 4 waves
 // issue blocks 4 wave .. 4 wave + 3. Rows and k past the operand are clamped.
@@ -388,35 +421,11 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_bf16_kernel(const GemmArgs p) {
   const int wm = wave >> 1;
   const int wn = wave & 1;
 
-  // Tile coordinates: XCD-aware remap, then grouped order along M.
-  const int tiles_m = (p.M + BM - 1) / BM;
-  const int tiles_n = (p.N + BN - 1) / BN;
-  const int ntiles = tiles_m * tiles_n;
-  int tm, tn;
-  if (p.sym) {
-    // Upper triangle tm <= tn, row by row.
-    int r = blockIdx.x;
-    tm = 0;
-    while (r >= tiles_m - tm) {
-      r -= tiles_m - tm;
-      ++tm;
-    }
-    tn = tm + r;
-  } else {
-    int bid = blockIdx.x;
-    if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);
-    constexpr int GM = 4;
-    const int group = bid / (GM * tiles_n);
-    const int first_m = group * GM;
-    const int gm = min(tiles_m - first_m, GM);
-    const int in_group = bid - group * GM * tiles_n;
-    tm = first_m + in_group % gm;
-    tn = in_group / gm;
-  }
+  int tm, tn, z;
+  tile_coords(p, tm, tn, z);
   const int m0 = tm * BM;
   const int n0 = tn * BN;
 
-  const int z = blockIdx.y;
   const int bi = z / p.splits;
   const int si = z - bi * p.splits;
   const int kbeg = si * p.k_chunk;
@@ -647,33 +656,11 @@ __global__ void __launch_bounds__(PP_THR, 1) gemm_pp_kernel(const GemmArgs p) {
   const int grp = wave >> 2;
   const int w4 = wave & 3;
 
-  const int tiles_m = (p.M + BM - 1) / BM;
-  const int tiles_n = (p.N + BN - 1) / BN;
-  const int ntiles = tiles_m * tiles_n;
-  int tm, tn;
-  if (p.sym) {
-    int r = blockIdx.x;
-    tm = 0;
-    while (r >= tiles_m - tm) {
-      r -= tiles_m - tm;
-      ++tm;
-    }
-    tn = tm + r;
-  } else {
-    int bid = blockIdx.x;
-    if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);
-    constexpr int GM = 4;
-    const int group = bid / (GM * tiles_n);
-    const int first_m = group * GM;
-    const int gm = min(tiles_m - first_m, GM);
-    const int in_group = bid - group * GM * tiles_n;
-    tm = first_m + in_group % gm;
-    tn = in_group / gm;
-  }
+  int tm, tn, z;
+  tile_coords(p, tm, tn, z);
   const int m0 = tm * BM;
   const int n0 = tn * BN;
 
-  const int z = blockIdx.y;
   const int bi = z / p.splits;
   const int si = z - bi * p.splits;
   const int kbeg = si * p.k_chunk;

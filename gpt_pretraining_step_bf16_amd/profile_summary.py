@@ -2,6 +2,8 @@
 
     python -m gpt_pretraining_step_bf16_amd.profile_summary trace  KERNEL_TRACE.csv --steps S
     python -m gpt_pretraining_step_bf16_amd.profile_summary traffic FETCH.csv WRITE.csv --copy-bytes N
+    python -m gpt_pretraining_step_bf16_amd.profile_summary roofline TRACE.csv FETCH.csv WRITE.csv UTIL.csv \
+        --steps S --copy-bytes N
 
 `trace` groups the dispatches of a `--kernel-trace` run by kernel (the two GEMM
 templates, gemm_pp_kernel and gemm_bf16_kernel, are split into a fwd/bwd family
@@ -13,6 +15,11 @@ included; every step launches the same kernels).
 dispatch), calibrates each counter against the plain copy kernel of N bytes
 that `bench.py --copy-probe-mib` launches (it reads N and writes N bytes),
 and prints the calibrated HBM bytes per launch of the fwd/bwd GEMM family.
+
+`roofline` joins the kernel trace (durations) with the two traffic runs and a
+`--pmc MfmaUtil LdsUtil` run and prints, per kernel family, the calibrated HBM
+bytes per launch, the achieved GB/s against the 8 TB/s HBM peak, and the MFMA
+and LDS utilisation the counters report.
 """
 from __future__ import annotations
 
@@ -118,6 +125,70 @@ def summarise_traffic(fetch_csv: str, write_csv: str, copy_bytes: int) -> None:
     print(f"source_sha256: {gemm_source_hash()}")
 
 
+HBM_PEAK_GBS = 8000.0
+
+
+def _per_dispatch_all(path):
+    """{counter: {dispatch id: (kernel name, value)}} of a --pmc run."""
+    out = collections.defaultdict(dict)
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            c = _col(row, "Counter_Name")
+            did = _col(row, "Dispatch_Id", "Correlation_Id")
+            name = _col(row, "Kernel_Name")
+            val = float(_col(row, "Counter_Value"))
+            prev = out[c].get(did)
+            out[c][did] = (name, val + (prev[1] if prev else 0.0))
+    return out
+
+
+def summarise_roofline(trace_csv, fetch_csv, write_csv, util_csv, steps, copy_bytes) -> None:
+    dur = collections.defaultdict(lambda: [0, 0.0])
+    with open(trace_csv, newline="") as f:
+        for row in csv.DictReader(f):
+            k = kernel_family(_col(row, "Kernel_Name", "Name"))
+            dur[k][0] += 1
+            dur[k][1] += float(_col(row, "End_Timestamp")) - float(_col(row, "Start_Timestamp"))
+    scale = {}
+    traffic = collections.defaultdict(lambda: [0, 0.0, 0.0])  # dispatches, fetch B, write B
+    for label, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        d = _per_dispatch(path, counter)
+        copies = [v for n, v in d.values() if "copy" in n.lower()]
+        if not copies:
+            sys.exit(f"no copy kernel dispatch in {path}: run bench.py with --copy-probe-mib")
+        scale[label] = (copy_bytes / 1024.0) / max(copies)
+        for n, v in d.values():
+            if "copy" in n.lower():
+                continue
+            k = kernel_family(n)
+            if label == "fetch":
+                traffic[k][0] += 1
+                traffic[k][1] += v * 1024.0 * scale[label]
+            else:
+                traffic[k][2] += v * 1024.0 * scale[label]
+    util = collections.defaultdict(lambda: collections.defaultdict(list))
+    for c, d in _per_dispatch_all(util_csv).items():
+        for n, v in d.values():
+            util[kernel_family(n)][c].append(v)
+    print(f"# counter scales: FETCH_SIZE x{scale['fetch']:.4f}, WRITE_SIZE x{scale['write']:.4f} "
+          f"(plain copy of {copy_bytes} bytes); HBM peak {HBM_PEAK_GBS:.0f} GB/s")
+    print(f"{'ms/step':>9} {'launch':>6} {'avg us':>9} {'HBM MB/launch':>13} {'GB/s':>7} {'%HBM':>5} "
+          f"{'MFMA%':>6} {'LDS%':>5}  kernel")
+    for k, (n, t) in sorted(dur.items(), key=lambda kv: -kv[1][1]):
+        avg_us = t / n / 1e3
+        tr = traffic.get(k)
+        if tr and tr[0]:
+            mb = (tr[1] + tr[2]) / tr[0] / 1e6
+            gbs = mb / 1e3 / (avg_us / 1e6)
+            mb_s, gbs_s, pct_s = f"{mb:13.1f}", f"{gbs:7.0f}", f"{100 * gbs / HBM_PEAK_GBS:5.1f}"
+        else:
+            mb_s, gbs_s, pct_s = f"{'-':>13}", f"{'-':>7}", f"{'-':>5}"
+        u = util.get(k, {})
+        mf = f"{sum(u['MfmaUtil']) / len(u['MfmaUtil']):6.1f}" if u.get("MfmaUtil") else f"{'-':>6}"
+        ls = f"{sum(u['LdsUtil']) / len(u['LdsUtil']):5.1f}" if u.get("LdsUtil") else f"{'-':>5}"
+        print(f"{t / 1e6 / steps:9.3f} {n / steps:6.1f} {avg_us:9.1f} {mb_s} {gbs_s} {pct_s} {mf} {ls}  {k}")
+
+
 def main(argv=None) -> None:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -128,11 +199,20 @@ def main(argv=None) -> None:
     p.add_argument("fetch_csv")
     p.add_argument("write_csv")
     p.add_argument("--copy-bytes", type=int, required=True)
+    r = sub.add_parser("roofline")
+    r.add_argument("trace_csv")
+    r.add_argument("fetch_csv")
+    r.add_argument("write_csv")
+    r.add_argument("util_csv")
+    r.add_argument("--steps", type=int, required=True)
+    r.add_argument("--copy-bytes", type=int, required=True)
     a = ap.parse_args(argv)
     if a.cmd == "trace":
         summarise_trace(a.csv, a.steps)
-    else:
+    elif a.cmd == "traffic":
         summarise_traffic(a.fetch_csv, a.write_csv, a.copy_bytes)
+    else:
+        summarise_roofline(a.trace_csv, a.fetch_csv, a.write_csv, a.util_csv, a.steps, a.copy_bytes)
 
 
 if __name__ == "__main__":
