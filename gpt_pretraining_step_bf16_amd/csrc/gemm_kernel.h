@@ -93,6 +93,33 @@ __device__ __forceinline__ void tile_coords(const GemmArgs& p, int& tm, int& tn,
   }
 }
 
+// Work item `lin` of `total` (per tiles per batch / split): output tile
+// (tm, tn) and batch / split index z, with the same XCD-aware remap as
+// tile_coords (a persistent workgroup on XCD x walks lin = x, x + G, ... with
+// G a multiple of 8).
+__device__ __forceinline__ void tile_coords_lin(const GemmArgs& p, int lin, int per, int total, int tiles_m,
+                                                int tiles_n, int& tm, int& tn, int& z) {
+  if ((total & 7) == 0) lin = (lin & 7) * (total >> 3) + (lin >> 3);
+  z = lin / per;
+  int t = lin - z * per;
+  if (p.sym) {
+    tm = 0;
+    while (t >= tiles_m - tm) {
+      t -= tiles_m - tm;
+      ++tm;
+    }
+    tn = tm + t;
+  } else {
+    constexpr int GM = 4;
+    const int group = t / (GM * tiles_n);
+    const int first_m = group * GM;
+    const int gm = min(tiles_m - first_m, GM);
+    const int in_group = t - group * GM * tiles_n;
+    tm = first_m + in_group % gm;
+    tn = in_group / gm;
+  }
+}
+
 // Issue 1 KB block `blk` (0..15) of one operand's k-block [k0, k0 + 32) into
 // the LDS stage buffer at byte address lds_op (wave-uniform); the 4 waves
 // issue blocks 4 wave .. 4 wave + 3. Rows and k past the operand are clamped.
@@ -411,6 +438,71 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const f32x16 (&acc
     run(std::false_type{});
 }
 
+// ---------------------------------------------------------------------------
+// Epilogue through LDS for bf16 outputs of the ping-pong kernel (128 x 64 per
+// wave). The accumulator layout gives a lane 4 consecutive columns of one row,
+// so direct bf16 stores write 16 bytes per row per instruction. Instead, per
+// 32-row block, each wave applies the element-wise math, writes the bf16
+// 32 x 64 block into a private LDS region (rows padded to 144 bytes, which
+// keeps the writes free of bank conflicts), reads it back row-contiguous and
+// stores whole 128-byte row segments (8 lanes per row). Edge tiles check
+// every row segment against M and N (N a multiple of 4).
+// ---------------------------------------------------------------------------
+template <int E>
+constexpr bool lds_epi() {
+  return E == EPI_BF16 || E == EPI_RELU_BF16 || E == EPI_RELU2_BF16;
+}
+constexpr int STG_RS = 144;  // padded row stride of a staging block (bytes)
+
+template <int E, bool FULL>
+__device__ __forceinline__ void store_tile_lds(const GemmArgs& p, const f32x16 (&acc)[4][2], int bi, int m0,
+                                               int n0, int row_off, int col_off, int lane, int wave, char* smem) {
+  const int rows_left = p.M - (m0 + row_off), cols_left = p.N - (n0 + col_off);
+  char* wreg = smem + wave * (32 * STG_RS);
+  const int r = lane & 31, hl = lane >> 5;
+  const long ldc = p.ldc;
+  uint16_t* cb = reinterpret_cast<uint16_t*>(p.c) + (long)bi * p.sc + (long)(m0 + row_off) * ldc + (n0 + col_off);
+  const float alpha = p.alpha;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // (Scheduling barriers keep each block's registers from being hoisted
+    // across blocks.)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = 32 * j + 8 * g + 4 * hl;
+        float o[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float v = acc[i][j][4 * g + t];
+          if constexpr (E == EPI_BF16) {
+            o[t] = alpha * v;
+          } else if constexpr (E == EPI_RELU_BF16) {
+            o[t] = fmaxf(v, 0.f);
+          } else {
+            const float u = fmaxf(v, 0.f);
+            o[t] = u * u;
+          }
+        }
+        *reinterpret_cast<uint2*>(wreg + r * STG_RS + col * 2) = make_uint2(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]));
+      }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int rr = 8 * q + (lane >> 3), cc = lane & 7;
+      const uint4 val = *reinterpret_cast<const uint4*>(wreg + rr * STG_RS + cc * 16);
+      uint16_t* dst = cb + (long)(32 * i + rr) * ldc + cc * 8;
+      if (FULL || (32 * i + rr < rows_left && cc * 8 + 8 <= cols_left)) {
+        *reinterpret_cast<uint4*>(dst) = val;
+      } else if (32 * i + rr < rows_left && cc * 8 + 4 <= cols_left) {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(val.x, val.y);
+      }
+    }
+  }
+}
+
 template <bool AK, bool BK_, int SQ, int EPI>
 __global__ void __launch_bounds__(NTHR, 1) gemm_bf16_kernel(const GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE_BYTES];
@@ -643,6 +735,12 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_bf16_kernel(const GemmArgs p) {
 // scalar pointer that advances by a k-block per issue (no per-load address
 // arithmetic, division or branch in the loop); only edge tiles take the
 // clamped per-load path.
+// The kernel is persistent: one workgroup per CU walks the (batch / split,
+// tile) work items with stride gridDim.x, so a tile's epilogue stores drain
+// while the next tile's first k-blocks load, instead of each workgroup
+// draining its stores before the next one may start. Epilogues that write
+// bf16 without reading an input go through LDS (store_tile_lds) so that
+// every store instruction writes whole 128-byte row segments.
 // ---------------------------------------------------------------------------
 constexpr int PP_THR = 512;
 
@@ -656,28 +754,14 @@ __global__ void __launch_bounds__(PP_THR, 1) gemm_pp_kernel(const GemmArgs p) {
   const int grp = wave >> 2;
   const int w4 = wave & 3;
 
-  int tm, tn, z;
-  tile_coords(p, tm, tn, z);
-  const int m0 = tm * BM;
-  const int n0 = tn * BN;
+  // Work items: (batch / split, tile) pairs, walked with stride gridDim.x.
+  const int tiles_m = (p.M + BM - 1) / BM;
+  const int tiles_n = (p.N + BN - 1) / BN;
+  const int per = p.sym ? tiles_m * (tiles_m + 1) / 2 : tiles_m * tiles_n;
+  const int total = per * p.batch * p.splits;
 
-  const int bi = z / p.splits;
-  const int si = z - bi * p.splits;
-  const int kbeg = si * p.k_chunk;
-  const int kend = min(p.K, kbeg + p.k_chunk);
-  const int kiters = (kend - kbeg + BKD - 1) / BKD;
-  const int nk = kiters * p.nseg;
-
-  f32x16 acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-  auto stage_a = [&](int it) { return smem + (it % NST) * STAGE_BYTES; };
   const uint32_t lds0 = lds_addr(smem);
+  auto stage_a = [&](int it) { return smem + (it % NST) * STAGE_BYTES; };
   auto stage_l = [&](int it) { return lds0 + (uint32_t)((it % NST) * STAGE_BYTES); };
 
   uint32_t off[4];
@@ -685,23 +769,38 @@ __global__ void __launch_bounds__(PP_THR, 1) gemm_pp_kernel(const GemmArgs p) {
     block_offsets<AK>(p.lda, w4, lane, off);
   else
     block_offsets<BK_>(p.ldb, w4, lane, off);
-  const bool interior = (m0 + BM <= p.M) && (n0 + BN <= p.N);
-
-  // Direct-load state of this wave's operand (group 0: A, group 1: B): a
-  // scalar pointer to (first row, first k) of the next k-block to issue,
-  // advanced by one k-block per issue and reset at each K segment.
   const bool opA = grp == 0;
   const long ld = opA ? p.lda : p.ldb;
   const bool kmaj = opA ? AK : BK_;
   const long kstep = kmaj ? (long)BKD : (long)BKD * ld;
-  const int rc0 = opA ? m0 : n0;
+  const uint32_t op_off = opA ? 0u : (uint32_t)OP_BYTES;
+
+  // Per-tile state.
+  int m0, n0, bi, si, kbeg, kend, kiters, nk;
+  bool interior;
+  const uint16_t* nxt;
+  int nxt_seg, nxt_k;
   auto seg_ptr = [&](int seg) {
+    const int rc0 = opA ? m0 : n0;
     const uint16_t* b = opA ? p.a[seg] + (long)bi * p.sa : p.b[seg] + (long)bi * p.sb;
     return b + (kmaj ? (long)rc0 * ld + kbeg : (long)kbeg * ld + rc0);
   };
-  const uint16_t* nxt = seg_ptr(0);
-  int nxt_seg = 0, nxt_k = 0;
-  const uint32_t op_off = opA ? 0u : (uint32_t)OP_BYTES;
+  auto setup = [&](int lin) {
+    int tm, tn, z;
+    tile_coords_lin(p, lin, per, total, tiles_m, tiles_n, tm, tn, z);
+    m0 = tm * BM;
+    n0 = tn * BN;
+    bi = z / p.splits;
+    si = z - bi * p.splits;
+    kbeg = si * p.k_chunk;
+    kend = min(p.K, kbeg + p.k_chunk);
+    kiters = (kend - kbeg + BKD - 1) / BKD;
+    nk = kiters * p.nseg;
+    interior = (m0 + BM <= p.M) && (n0 + BN <= p.N);
+    nxt = seg_ptr(0);
+    nxt_seg = 0;
+    nxt_k = 0;
+  };
 
   // This wave's 4 blocks of its group's operand of k-block it (the next one
   // in issue order).
@@ -729,6 +828,7 @@ __global__ void __launch_bounds__(PP_THR, 1) gemm_pp_kernel(const GemmArgs p) {
     }
   };
 
+  f32x16 acc[4][2];
   bf16x8 fa[2][4], fb[2][2];
   auto load_frags = [&](int it) {
     const char* st = stage_a(it);
@@ -759,6 +859,12 @@ __global__ void __launch_bounds__(PP_THR, 1) gemm_pp_kernel(const GemmArgs p) {
       asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
+  // Barrier that orders LDS accesses only (stores may stay in flight).
+  auto lds_bar = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
   auto run = [&]() {
 #pragma nounroll
     for (int j = 0; j < nk; ++j) {
@@ -770,19 +876,46 @@ __global__ void __launch_bounds__(PP_THR, 1) gemm_pp_kernel(const GemmArgs p) {
       wait_bar(more);
     }
   };
+
+  int lin = blockIdx.x;
+  if (lin >= total) return;
+  setup(lin);
   if (nk > 0) dma_part(0);
   if (nk > 1) dma_part(1);
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-  if (grp == 0) {
-    run();
-    wait_bar(false);
-  } else {
-    wait_bar(false);
-    run();
+#pragma nounroll
+  while (true) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    if (grp == 0) {
+      run();
+      wait_bar(false);
+    } else {
+      wait_bar(false);
+      run();
+    }
+    lds_bar();  // every LDS read of this tile is done
+    if constexpr (lds_epi<EPI>()) {
+      if (interior)
+        store_tile_lds<EPI, true>(p, acc, bi, m0, n0, 128 * grp, 64 * w4, lane, wave, smem);
+      else
+        store_tile_lds<EPI, false>(p, acc, bi, m0, n0, 128 * grp, 64 * w4, lane, wave, smem);
+    } else {
+      store_tile<EPI, 2>(p, acc, bi, si, m0, n0, 128 * grp, 64 * w4, lane);
+    }
+    const int lin_next = lin + gridDim.x;
+    if (lin_next >= total) break;
+    lds_bar();  // the epilogue's LDS staging is done before direct loads overwrite it
+    lin = lin_next;
+    setup(lin);
+    if (nk > 0) dma_part(0);
+    if (nk > 1) dma_part(1);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   }
-  __syncthreads();
-
-  store_tile<EPI, 2>(p, acc, bi, si, m0, n0, 128 * grp, 64 * w4, lane);
 }
 
 }  // namespace gemm_impl
@@ -793,11 +926,17 @@ __global__ void __launch_bounds__(PP_THR, 1) gemm_pp_kernel(const GemmArgs p) {
 inline bool gemm_pp_ok(const GemmArgs& g) {
   return g.K % gemm_impl::BKD == 0 && (g.splits == 1 || g.k_chunk % gemm_impl::BKD == 0);
 }
+// Persistent grid of the ping-pong kernel: one workgroup per CU (its LDS
+// allows one), each walking work items with stride gridDim.x.
+inline unsigned gemm_pp_grid(const dim3& work) {
+  const unsigned total = work.x * work.y;
+  return total < 256u ? total : 256u;
+}
 #define GEMM_LAUNCH(AK, BK, SQ, EPI)                                                                  \
   do {                                                                                                \
     if (gemm_pp_ok(g))                                                                                \
-      hipLaunchKernelGGL((gemm_impl::gemm_pp_kernel<AK, BK, EPI>), grid, dim3(gemm_impl::PP_THR), 0, s, \
-                         g);                                                                          \
+      hipLaunchKernelGGL((gemm_impl::gemm_pp_kernel<AK, BK, EPI>), dim3(gemm_pp_grid(grid)),              \
+                         dim3(gemm_impl::PP_THR), 0, s, g);                                                 \
     else                                                                                              \
       hipLaunchKernelGGL((gemm_impl::gemm_bf16_kernel<AK, BK, SQ, EPI>), grid, dim3(gemm_impl::NTHR), 0, \
                          s, g);                                                                       \

@@ -50,6 +50,30 @@ def test_gemm_layouts_fp32_out(a_kmajor, b_kmajor, K):
     assert err < 2e-6, err
 
 
+# bf16 outputs go through the LDS-staged epilogue (interior tiles, and edge
+# tiles with a column count that is a multiple of 8 or only of 4), in a
+# persistent launch that walks several tiles per workgroup.
+# The layouts with bf16 epilogues: both operands K-major, and K-major A with a
+# K-strided B (N = 260 needs a K-major B: K-strided rows must be 16-byte aligned).
+@pytest.mark.parametrize("a_kmajor,b_kmajor,N", [(1, 1, 264), (1, 1, 260), (1, 0, 264)])
+def test_gemm_layouts_bf16_out(a_kmajor, b_kmajor, N):
+    M, K = 776, 320
+    log(f"gemm bf16 out a_kmajor={a_kmajor} b_kmajor={b_kmajor} M={M} N={N} K={K}")
+    rng = np.random.default_rng(40 + 2 * a_kmajor + b_kmajor + N)
+    Ab, Af = _rand_bf16(rng, (M, K))
+    Bb, Bf = _rand_bf16(rng, (N, K))
+    A = dev(torch, Ab if a_kmajor else np.ascontiguousarray(Ab.T))
+    B = dev(torch, Bb if b_kmajor else np.ascontiguousarray(Bb.T))
+    C = torch.full((M, N), 0x7FC0, dtype=torch.int16, device="cuda")  # NaN fill: unwritten shows
+    binding.op_gemm(M, N, K, A, K if a_kmajor else M, a_kmajor, B, K if b_kmajor else N, b_kmajor, C, N,
+                    binding.OUT_BF16)
+    torch.cuda.synchronize()
+    got = bits_to_f32(C.cpu().numpy()).reshape(M, N)
+    ref = Af @ Bf.T
+    assert np.all(np.isfinite(got))
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-4)
+
+
 def test_gemm_epilogues():
     M, N, K = 300, 392, 256
     log(f"gemm epilogues M={M} N={N} K={K}")
