@@ -31,3 +31,4 @@ from .gpt import (  # noqa: F401
 from .adamw import adamw_step, adamw_update  # noqa: F401
 from .muon import muon_step, newton_schulz, newton_schulz_svd  # noqa: F401
 from .polar_express import greedy_minimax_triples  # noqa: F401
+from .normuon import normuon_step, variance_reduction  # noqa: F401
