@@ -6,7 +6,9 @@ backward) + muon_step (momentum, Newton-Schulz, update of every block matrix)
 + adamw_step (wte and lm_head) on one microbatch of seeded synthetic tokens,
 with inputs and weights resident in HBM before the timed region. With
 --accum K a step runs K microbatches (gradient accumulation) before the two
-optimizer calls. Prints one JSON line:
+optimizer calls; with --normuon the block matrices take normuon_step (Muon
+with NorMuon variance reduction, beta2 0.95) in place of muon_step. Prints one
+JSON line:
 
   value        training tokens/s (B*T*steps / wall time of the timed steps)
   mfu          value * F_tok / MI355X dense-bf16 peak, with
@@ -38,6 +40,8 @@ METRIC = "training tokens/sec + MFU, d20 GPT fwd+bwd+Muon step on 1 MI355X"
 # PyTorch's default betas and eps, no decay, and a rate well below the 0.02
 # init scale (early Adam steps move every element by about lr).
 ADAMW = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
+# NorMuon second-moment decay (the pages give none; the NorMuon method's usual value).
+NORMUON_BETA2 = 0.95
 
 
 def flops_per_token(L, d, V, T):
@@ -93,7 +97,7 @@ def gemm_traffic():
     return float(vals["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(cfg, weights, tok, tgt):
+def cpu_baseline(cfg, weights, tok, tgt, normuon=False):
     """Time the oracle on a bounded sample and scale it to one full step."""
     import oracle  # test infrastructure: used here only for the CPU baseline leg
 
@@ -108,7 +112,12 @@ def cpu_baseline(cfg, weights, tok, tgt):
     sub_g = {k: (rng.standard_normal(sub_w[k].shape, dtype=np.float32) * 1e-3) for k in names}
     sub_m = {k: np.zeros_like(v) for k, v in sub_w.items()}
     t0 = time.perf_counter()
-    oracle.muon_step(sub_w, sub_g, sub_m, syn.MUON_LR, syn.MUON_MOMENTUM, syn.NS_COEFFS)
+    if normuon:
+        sub_v = {k: np.zeros(max(v.shape), dtype=np.float32) for k, v in sub_w.items()}
+        oracle.normuon_step(sub_w, sub_g, sub_m, sub_v, syn.MUON_LR, syn.MUON_MOMENTUM, NORMUON_BETA2,
+                            syn.NS_COEFFS)
+    else:
+        oracle.muon_step(sub_w, sub_g, sub_m, syn.MUON_LR, syn.MUON_MOMENTUM, syn.NS_COEFFS)
     t_muon_layer = time.perf_counter() - t0
     ad_w = {k: weights[k] for k in ("wte", "lm_head")}
     ad_g = {k: (rng.standard_normal(v.shape, dtype=np.float32) * 1e-3) for k, v in ad_w.items()}
@@ -124,7 +133,7 @@ def cpu_baseline(cfg, weights, tok, tgt):
         "cores": cores,
         "kind": "oracle",
         "sample": (f"fp32 NumPy oracle: fwd+bwd of 1 of {B} sequences ({T} tokens, {t_seq:.2f} s), "
-                   f"Muon of 1 of {L} layers ({t_muon_layer:.2f} s) and AdamW of wte and lm_head "
+                   f"{'NorMuon' if normuon else 'Muon'} of 1 of {L} layers ({t_muon_layer:.2f} s) and AdamW of wte and lm_head "
                    f"({t_adamw:.2f} s), scaled to the full step (sequences and layers are "
                    f"independent units of equal cost)"),
     }
@@ -138,6 +147,8 @@ def main():
     ap.add_argument("--config", default="d20", choices=sorted(syn.CONFIGS))
     ap.add_argument("--accum", type=int, default=1,
                     help="microbatches per optimizer step (gradient accumulation)")
+    ap.add_argument("--normuon", action="store_true",
+                    help="NorMuon variance reduction after Newton-Schulz (normuon_step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="launch one plain device copy of this many MiB before the steps "
@@ -179,10 +190,16 @@ def main():
     accum = max(1, args.accum)
     opt_step = [0]
 
+    def block_update():
+        if args.normuon:
+            st.normuon(syn.MUON_LR, syn.MUON_MOMENTUM, NORMUON_BETA2, syn.NS_COEFFS)
+        else:
+            st.muon(syn.MUON_LR, syn.MUON_MOMENTUM, syn.NS_COEFFS)
+
     def step():
         for i in range(accum):
             st.fwd_bwd(tok_d, tgt_d, accumulate=i > 0)
-        st.muon(syn.MUON_LR, syn.MUON_MOMENTUM, syn.NS_COEFFS)
+        block_update()
         opt_step[0] += 1
         st.adamw(ADAMW["lr"], ADAMW["beta1"], ADAMW["beta2"], ADAMW["eps"], ADAMW["weight_decay"],
                  opt_step[0])
@@ -229,6 +246,13 @@ def main():
     a1.record()
     torch.cuda.synchronize()
     adamw_ms = a0.elapsed_time(a1) / 5
+    # The block-matrix update alone (muon_step or normuon_step), timed the same way.
+    a0.record()
+    for _ in range(3):
+        block_update()
+    a1.record()
+    torch.cuda.synchronize()
+    block_ms = a0.elapsed_time(a1) / 3
     for name, (ms, fl, n) in prof.items():
         tf = fl / (ms / 1e3) / 1e12 if ms > 0 else 0.0
         print(f"[bench] {name:9s} {ms / args.steps:9.2f} ms/step  {n // max(args.steps, 1):5d} launches/step"
@@ -268,7 +292,8 @@ def main():
             "workload": f"{args.config}: depth {L}, width {d}, {dims['heads']} heads x 128, MLP {4 * d}, "
                         f"vocab {V}, seq {T}, microbatch {B}"
                         + (f" x {accum} accumulated" if accum > 1 else "")
-                        + "; fwd+bwd+Muon (5 Newton-Schulz steps)+AdamW (wte, lm_head)",
+                        + "; fwd+bwd+" + ("NorMuon" if args.normuon else "Muon")
+                        + " (5 Newton-Schulz steps)+AdamW (wte, lm_head)",
             "global_batch": accum * B,
             "seq_len": T,
             "parallelism": "none (1 GPU)",
@@ -278,12 +303,13 @@ def main():
         "loss": round(loss, 5),
         "wall_s_timed": round(wall, 3),
         "adamw_ms": round(adamw_ms, 3),
+        ("normuon_ms" if args.normuon else "muon_ms"): round(block_ms, 3),
         "roofline": roofline,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(cfg, weights, tok, tgt)
+        out["cpu_baseline"] = cpu_baseline(cfg, weights, tok, tgt, args.normuon)
     print(json.dumps(out), flush=True)
 
 

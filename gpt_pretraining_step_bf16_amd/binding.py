@@ -63,6 +63,8 @@ EXPORTS = {
     "gpt_fwd_bwd": (C.c_int, [_P, _P, _P, _P, _I, _I, _P, _P, _I, _P, _S, _P]),
     "muon_workspace_bytes": (C.c_size_t, [_P]),
     "muon_step": (C.c_int, [_P, _P, _P, _P, _P, _F, _F, C.POINTER(C.c_float), _I, _P, _S, _P]),
+    "normuon_state_elems": (C.c_int64, [_P]),
+    "normuon_step": (C.c_int, [_P, _P, _P, _P, _P, _P, _F, _F, _F, C.POINTER(C.c_float), _I, _P, _S, _P]),
     "adamw_state_elems": (C.c_int64, [_P]),
     "adamw_step": (C.c_int, [_P, _P, _P, _P, _P, _P, _F, _F, _F, _F, _F, _I, _P]),
     "gpt_refresh_bf16": (C.c_int, [_P, _P, _P, _P]),
@@ -185,6 +187,18 @@ class GptModel:
                              float(lr), float(momentum_coef), buf, steps, _ptr(workspace),
                              workspace.numel() * workspace.element_size(), _stream(stream))
         _check(st, "muon_step")
+
+    def normuon_state_elems(self) -> int:
+        return int(lib().normuon_state_elems(self._h))
+
+    def normuon_step(self, params, params_bf16, grads, momentum, second_moment, lr, momentum_coef, beta2,
+                     ns_coeffs, workspace, stream=None):
+        buf, steps = _coeffs(ns_coeffs)
+        st = lib().normuon_step(self._h, _ptr(params), _ptr(params_bf16), _ptr(grads), _ptr(momentum),
+                                _ptr(second_moment), float(lr), float(momentum_coef), float(beta2), buf,
+                                steps, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _stream(stream))
+        _check(st, "normuon_step")
 
     def adamw_state_elems(self) -> int:
         return int(lib().adamw_state_elems(self._h))

@@ -547,9 +547,12 @@ __global__ void muon_pack_kernel(const MuonGroup g, const float* __restrict__ mo
 }
 
 // W <- W - lr * sqrt(max(1, rows/cols)) * X in the stored orientation (rows =
-// fan-out of the stored matrix); refresh bf16. Grid as muon_pack_kernel.
+// fan-out of the stored matrix); refresh bf16. With row_scale (NorMuon), row r
+// of X is first multiplied by row_scale[j * x_rows + r]. Grid as
+// muon_pack_kernel.
 __global__ void muon_update_kernel(const MuonGroup g, const float* __restrict__ x32,
-                                   float* __restrict__ params, uint16_t* __restrict__ pbf, float lr) {
+                                   float* __restrict__ params, uint16_t* __restrict__ pbf, float lr,
+                                   const float* __restrict__ row_scale) {
   __shared__ float tile[32][33];
   const int j = blockIdx.z;
   const long off = muon_mat_offset(g, j);
@@ -564,15 +567,18 @@ __global__ void muon_update_kernel(const MuonGroup g, const float* __restrict__ 
   const long r0 = blockIdx.y * 32L, c0 = blockIdx.x * 32L;  // X tile origin
   float* w = params + off;
   uint16_t* wb = pbf + off;
+  const float* rsc = row_scale ? row_scale + (long)j * xr + r0 : nullptr;
   if (!tr) {
     for (int rr = ty; rr < 32; rr += 8) {
       const long idx = (r0 + rr) * xc + c0 + tx;
-      const float v = w[idx] - scale * x32[xoff + idx];
+      const float sr = rsc ? scale * rsc[rr] : scale;
+      const float v = w[idx] - sr * x32[xoff + idx];
       w[idx] = v;
       wb[idx] = (uint16_t)f2bf(v);
     }
   } else {
-    for (int rr = ty; rr < 32; rr += 8) tile[rr][tx] = x32[xoff + (r0 + rr) * xc + c0 + tx];
+    for (int rr = ty; rr < 32; rr += 8)
+      tile[rr][tx] = (rsc ? rsc[rr] : 1.f) * x32[xoff + (r0 + rr) * xc + c0 + tx];
     __syncthreads();
     // Stored W[c][r] with c in the X-column tile, r in the X-row tile.
     for (int cc = ty; cc < 32; cc += 8) {
@@ -582,6 +588,69 @@ __global__ void muon_update_kernel(const MuonGroup g, const float* __restrict__ 
       wb[idx] = (uint16_t)f2bf(v);
     }
   }
+}
+
+// NorMuon ([CT50] "2. Otimizador Muon", variance reduction after the
+// iteration). Statistics are per row of X, the tall orientation, i.e. per
+// element of the stored matrix's longer side; the mean runs over x_cols.
+// Pass 1, one wave per X row: v_mean = mean(X_r^2); the moving average
+// v <- beta2 v + (1 - beta2) v_mean; step_r = 1 / sqrt(max(v, 1e-10)).
+// Writes step_r to rs and the row's terms of the two norms (v_mean and
+// v_mean * step_r^2) to terms[0] / terms[1] ([count, x_rows] each).
+// Grid: (x_rows / 4, count); 256 threads.
+__global__ void normuon_stats_kernel(const MuonGroup g, const float* __restrict__ x32,
+                                     float* __restrict__ state, float beta2, float* __restrict__ rs,
+                                     float* __restrict__ terms) {
+  const int j = blockIdx.y;
+  const long xr = g.x_rows, xc = g.x_cols;
+  const long r = blockIdx.x * 4L + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const float4* row = reinterpret_cast<const float4*>(x32 + ((long)j * xr + r) * xc);
+  float ss = 0.f;
+  for (long c = lane; c < xc / 4; c += 64) {
+    const float4 v = row[c];
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = warp_sum(ss);
+  if (lane == 0) {
+    const long i = (long)j * xr + r;
+    const float vmean = ss / (float)xc;
+    const float v = beta2 * state[i] + (1.f - beta2) * vmean;
+    state[i] = v;
+    const float st = 1.f / sqrtf(fmaxf(v, 1e-10f));
+    rs[i] = st;
+    terms[i] = vmean;
+    terms[(long)g.count * xr + i] = vmean * st * st;
+  }
+}
+
+// Pass 2, one workgroup per matrix: v_norm = sqrt(sum v_mean), v_norm_new =
+// sqrt(sum v_mean step^2); rs_r <- step_r * v_norm / max(v_norm_new, 1e-10).
+// Each thread sums a fixed stride of rows, so the result is deterministic.
+// Grid: (count); 256 threads.
+__global__ void normuon_scale_kernel(const MuonGroup g, float* __restrict__ rs,
+                                     const float* __restrict__ terms) {
+  __shared__ float red[2][4];
+  const int j = blockIdx.x;
+  const long xr = g.x_rows;
+  const float* a = terms + (long)j * xr;
+  const float* b = terms + ((long)g.count + j) * xr;
+  float sa = 0.f, sb = 0.f;
+  for (long r = threadIdx.x; r < xr; r += blockDim.x) {
+    sa += a[r];
+    sb += b[r];
+  }
+  sa = warp_sum(sa);
+  sb = warp_sum(sb);
+  if ((threadIdx.x & 63) == 0) {
+    red[0][threadIdx.x >> 6] = sa;
+    red[1][threadIdx.x >> 6] = sb;
+  }
+  __syncthreads();
+  const float ta = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+  const float tb = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  const float ratio = sqrtf(ta) / fmaxf(sqrtf(tb), 1e-10f);
+  for (long r = threadIdx.x; r < xr; r += blockDim.x) rs[(long)j * xr + r] *= ratio;
 }
 
 // AdamW on one contiguous fp32 tensor and its moments ([CT50] "2. Otimizador
@@ -794,7 +863,26 @@ hipError_t launch_muon_pack(const MuonGroup& g, const float* mom, const float* p
 hipError_t launch_muon_update(const MuonGroup& g, const float* x32, float* params,
                               uint16_t* params_bf16, float lr, hipStream_t s) {
   dim3 grid((unsigned)(g.x_cols / 32), (unsigned)(g.x_rows / 32), g.count);
-  hipLaunchKernelGGL(muon_update_kernel, grid, dim3(256), 0, s, g, x32, params, params_bf16, lr);
+  hipLaunchKernelGGL(muon_update_kernel, grid, dim3(256), 0, s, g, x32, params, params_bf16, lr,
+                     static_cast<const float*>(nullptr));
+  return hipGetLastError();
+}
+
+hipError_t launch_normuon(const MuonGroup& g, const float* x32, float* state, float beta2, float* rs,
+                          float* terms, hipStream_t s) {
+  hipLaunchKernelGGL(normuon_stats_kernel, dim3((unsigned)(g.x_rows / 4), g.count), dim3(256), 0, s, g, x32,
+                     state, beta2, rs, terms);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(normuon_scale_kernel, dim3(g.count), dim3(256), 0, s, g, rs,
+                     static_cast<const float*>(terms));
+  return hipGetLastError();
+}
+
+hipError_t launch_muon_update_scaled(const MuonGroup& g, const float* x32, float* params,
+                                     uint16_t* params_bf16, float lr, const float* row_scale, hipStream_t s) {
+  dim3 grid((unsigned)(g.x_cols / 32), (unsigned)(g.x_rows / 32), g.count);
+  hipLaunchKernelGGL(muon_update_kernel, grid, dim3(256), 0, s, g, x32, params, params_bf16, lr, row_scale);
   return hipGetLastError();
 }
 

@@ -658,27 +658,48 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
   return GPT_OK;
 }
 
+// NorMuon scratch after the Newton-Schulz buffers: per X row of the larger
+// group, the scale and the two norm terms.
+static size_t ns_workspace_bytes(const gpt_model& m, size_t* normuon_off) {
+  MuonGroup sq, tall;
+  muon_groups(m, sq, tall);
+  const size_t a = plan_ns(sq.count, sq.x_rows, sq.x_cols, 0).total;
+  const size_t b = plan_ns(tall.count, tall.x_rows, tall.x_cols, 0).total;
+  const size_t off = (std::max(a, b) + 255) / 256 * 256;
+  if (normuon_off) *normuon_off = off;
+  const size_t rows = std::max((size_t)sq.count * sq.x_rows, (size_t)tall.count * tall.x_rows);
+  return off + (3 * rows * 4 + 255) / 256 * 256;
+}
+
 size_t muon_workspace_bytes(const gpt_model* m) {
+  if (!m) return 0;
+  return ns_workspace_bytes(*m, nullptr);
+}
+
+int64_t normuon_state_elems(const gpt_model* m) {
   if (!m) return 0;
   MuonGroup sq, tall;
   muon_groups(*m, sq, tall);
-  const size_t a = plan_ns(sq.count, sq.x_rows, sq.x_cols, 0).total;
-  const size_t b = plan_ns(tall.count, tall.x_rows, tall.x_cols, 0).total;
-  return std::max(a, b);
+  return (int64_t)sq.count * sq.x_rows + (int64_t)tall.count * tall.x_rows;
 }
 
-gpt_status muon_step(gpt_model* m, float* params, uint16_t* params_bf16, const float* grads,
-                     float* momentum, float lr, float momentum_coef, const float* ns_coeffs,
-                     int32_t ns_steps, void* workspace, size_t workspace_bytes, void* stream) {
+// Momentum, Newton-Schulz and the update for both groups; with second_moment,
+// NorMuon rescales each group's orthogonalised update before the update.
+static gpt_status muon_impl(gpt_model* m, float* params, uint16_t* params_bf16, const float* grads,
+                            float* momentum, float* second_moment, float lr, float momentum_coef, float beta2,
+                            const float* ns_coeffs, int32_t ns_steps, void* workspace, size_t workspace_bytes,
+                            void* stream) {
   if (!m || !params || !params_bf16 || !grads || !momentum || !ns_coeffs) return GPT_EINVAL;
   if (ns_steps < 1 || ns_steps > 8) return GPT_EINVAL;
-  if (!workspace || workspace_bytes < muon_workspace_bytes(m)) return GPT_EWORKSPACE;
+  size_t nm_off = 0;
+  if (!workspace || workspace_bytes < ns_workspace_bytes(*m, &nm_off)) return GPT_EWORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return GPT_EINVAL;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = reinterpret_cast<char*>(workspace);
   g_prof_model = m;
   MuonGroup groups[2];
   muon_groups(*m, groups[0], groups[1]);
+  float* state = second_moment;
   for (const MuonGroup& g : groups) {
     const NsPlan p = plan_ns(g.count, g.x_rows, g.x_cols, 0);
     float* part = reinterpret_cast<float*>(ws + p.part);
@@ -687,9 +708,33 @@ gpt_status muon_step(gpt_model* m, float* params, uint16_t* params_bf16, const f
     HIP_TRY(launch_muon_pack(g, momentum, part, p.nb, x32, reinterpret_cast<uint16_t*>(ws + p.xh0),
                              reinterpret_cast<uint16_t*>(ws + p.xl0), s));
     HIP_TRY(run_ns(ws, p, g.count, g.x_rows, g.x_cols, ns_coeffs, ns_steps, s));
-    HIP_TRY(launch_muon_update(g, x32, params, params_bf16, lr, s));
+    if (state) {
+      const long rows = (long)g.count * g.x_rows;
+      float* rs = reinterpret_cast<float*>(ws + nm_off);
+      HIP_TRY(launch_normuon(g, x32, state, beta2, rs, rs + rows, s));
+      HIP_TRY(launch_muon_update_scaled(g, x32, params, params_bf16, lr, rs, s));
+      state += rows;
+    } else {
+      HIP_TRY(launch_muon_update(g, x32, params, params_bf16, lr, s));
+    }
   }
   return GPT_OK;
+}
+
+gpt_status muon_step(gpt_model* m, float* params, uint16_t* params_bf16, const float* grads,
+                     float* momentum, float lr, float momentum_coef, const float* ns_coeffs,
+                     int32_t ns_steps, void* workspace, size_t workspace_bytes, void* stream) {
+  return muon_impl(m, params, params_bf16, grads, momentum, nullptr, lr, momentum_coef, 0.f, ns_coeffs,
+                   ns_steps, workspace, workspace_bytes, stream);
+}
+
+gpt_status normuon_step(gpt_model* m, float* params, uint16_t* params_bf16, const float* grads,
+                        float* momentum, float* second_moment, float lr, float momentum_coef, float beta2,
+                        const float* ns_coeffs, int32_t ns_steps, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (!second_moment || !(beta2 >= 0.f && beta2 < 1.f)) return GPT_EINVAL;
+  return muon_impl(m, params, params_bf16, grads, momentum, second_moment, lr, momentum_coef, beta2,
+                   ns_coeffs, ns_steps, workspace, workspace_bytes, stream);
 }
 
 int64_t adamw_state_elems(const gpt_model* m) {

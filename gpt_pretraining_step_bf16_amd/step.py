@@ -1,9 +1,10 @@
 """Device buffers for repeated training steps (torch allocates, the HIP library computes).
 
 ``TrainState`` owns the flat fp32 parameters, their bf16 shadow, gradients,
-Muon momentum, the AdamW moments of wte and lm_head and the two workspaces,
-laid out as the library's tensor table says. A step is ``fwd_bwd`` (loss +
-gradients) followed by ``muon`` (block matrices) and ``adamw`` (wte, lm_head).
+Muon momentum, the NorMuon second moments, the AdamW moments of wte and
+lm_head and the two workspaces, laid out as the library's tensor table says. A
+step is ``fwd_bwd`` (loss + gradients) followed by ``muon`` or ``normuon``
+(block matrices) and ``adamw`` (wte, lm_head).
 """
 from __future__ import annotations
 
@@ -33,6 +34,8 @@ class TrainState:
         na = self.model.adamw_state_elems()
         self.exp_avg = torch.zeros(na, dtype=torch.float32, device=device)
         self.exp_avg_sq = torch.zeros(na, dtype=torch.float32, device=device)
+        self.second_moment = torch.zeros(self.model.normuon_state_elems(), dtype=torch.float32,
+                                         device=device)
 
     # -- host <-> device ------------------------------------------------------
     def flatten(self, arrays: dict) -> np.ndarray:
@@ -68,6 +71,10 @@ class TrainState:
     def muon(self, lr, momentum_coef, ns_coeffs):
         self.model.muon_step(self.params, self.params_bf16, self.grads, self.momentum, lr,
                              momentum_coef, ns_coeffs, self.muon_ws)
+
+    def normuon(self, lr, momentum_coef, beta2, ns_coeffs):
+        self.model.normuon_step(self.params, self.params_bf16, self.grads, self.momentum,
+                                self.second_moment, lr, momentum_coef, beta2, ns_coeffs, self.muon_ws)
 
     def adamw(self, lr, beta1, beta2, eps, weight_decay, step):
         self.model.adamw_step(self.params, self.params_bf16, self.grads, self.exp_avg, self.exp_avg_sq,

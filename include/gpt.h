@@ -107,7 +107,7 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* params_bf16, const int32_t*
                        float* grads, int32_t accumulate, void* workspace,
                        size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace muon_step needs. */
+/* Bytes of device workspace muon_step and normuon_step need. */
 size_t muon_workspace_bytes(const gpt_model* m);
 
 /*
@@ -129,6 +129,39 @@ size_t muon_workspace_bytes(const gpt_model* m);
 gpt_status muon_step(gpt_model* m, float* params, uint16_t* params_bf16, const float* grads,
                      float* momentum, float lr, float momentum_coef, const float* ns_coeffs,
                      int32_t ns_steps, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Elements of the NorMuon second-moment state: one fp32 per element of the
+ * longer side of each block matrix (per row of wq, wk, wv, wo and wfc, per
+ * column of wproj). Layout: the d x d matrices in the order layer 0 wq, wk,
+ * wv, wo, layer 1 wq, ... (d each), then layer 0 wfc, wproj, layer 1 wfc, ...
+ * (4d each).
+ */
+int64_t normuon_state_elems(const gpt_model* m);
+
+/*
+ * muon_step with NorMuon variance reduction ([CT50] "2. Otimizador Muon", the
+ * NorMuon paragraph after the iteration). After the iteration, per matrix,
+ * with O the orthogonalised update in the stored orientation:
+ *   v_mean_i     = mean of O^2 over the shorter side, one per neuron i
+ *   state_i     <- beta2 * state_i + (1 - beta2) * v_mean_i
+ *   step_i       = 1 / sqrt(max(state_i, 1e-10))
+ *   v_norm       = sqrt(sum v_mean_i),  v_norm_new = sqrt(sum v_mean_i step_i^2)
+ *   O_i         <- O_i * step_i * v_norm / max(v_norm_new, 1e-10)
+ * then W <- W - lr * sqrt(max(1, rows/cols)) * O as in muon_step (the
+ * rescaled O keeps its Frobenius norm). The page prints only part of this
+ * rule; the averaged dimension, the moving average and v_norm_new are the
+ * readings stated here.
+ *   second_moment  device fp32 [normuon_state_elems(m)], zero before the
+ *                  first step, updated in place
+ *   beta2          in [0, 1)
+ * Other arguments as for muon_step (same workspace size). Returns GPT_EINVAL
+ * for a null second_moment or beta2 outside [0, 1), before any launch.
+ */
+gpt_status normuon_step(gpt_model* m, float* params, uint16_t* params_bf16, const float* grads,
+                        float* momentum, float* second_moment, float lr, float momentum_coef, float beta2,
+                        const float* ns_coeffs, int32_t ns_steps, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /* Elements of each AdamW moment buffer: wte then lm_head, 2 * vocab * d. */
 int64_t adamw_state_elems(const gpt_model* m);

@@ -21,14 +21,14 @@ def _declared_functions():
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
     skip = {"if", "sizeof", "defined"}
-    return sorted({n for n in names if n.startswith(("gpt_", "muon_", "adamw_")) and n not in skip})
+    return sorted({n for n in names if n.startswith(("gpt_", "muon_", "normuon_", "adamw_")) and n not in skip})
 
 
 def test_every_declared_symbol_is_exported():
     lib = C.CDLL(binding.LIB_PATH)
     declared = _declared_functions()
     assert "gpt_fwd_bwd" in declared and "muon_step" in declared and "gpt_create" in declared
-    assert "adamw_step" in declared
+    assert "adamw_step" in declared and "normuon_step" in declared
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(binding.EXPORTS), set(declared) ^ set(binding.EXPORTS)
@@ -136,3 +136,23 @@ def test_adamw_state_and_host_validation_precede_any_launch():
     assert call(eps=-1.0) == binding.GPT_EINVAL
     assert call(lr=float("nan")) == binding.GPT_EINVAL
     assert lib.adamw_step(None, fake, fake, fake, fake, fake, 0.01, 0.9, 0.95, 1e-8, 0.0, 1, None) == binding.GPT_EINVAL
+
+
+def test_normuon_state_and_host_validation_precede_any_launch():
+    m = binding.GptModel(20, 32768, 2048)
+    # One value per element of each block matrix's longer side.
+    assert m.normuon_state_elems() == 20 * (4 * 1280 + 2 * 5120)
+    lib = binding.lib()
+    fake = C.c_void_p(1 << 20)
+    buf, _ = binding._coeffs(syn.NS_COEFFS)
+    need = m.muon_workspace_bytes()
+
+    def call(v=fake, b2=0.95, ws=C.c_void_p(1 << 20), wsb=need, steps=5):
+        return lib.normuon_step(m.handle, fake, fake, fake, fake, v, 0.02, 0.95, b2, buf, steps, ws, wsb, None)
+
+    assert call(v=None) == binding.GPT_EINVAL
+    assert call(b2=1.0) == binding.GPT_EINVAL
+    assert call(b2=-0.5) == binding.GPT_EINVAL
+    assert call(b2=float("nan")) == binding.GPT_EINVAL
+    assert call(steps=0) == binding.GPT_EINVAL
+    assert call(wsb=need - 1) == binding.GPT_EWORKSPACE

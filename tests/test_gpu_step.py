@@ -208,3 +208,116 @@ def test_adamw_step_matches_oracle(cfg_name):
         if k not in ("wte", "lm_head"):
             np.testing.assert_array_equal(new_w[k], w[k])
     np.testing.assert_array_equal(st.params_bf16.cpu().numpy(), bf16_bits(st.params.cpu().numpy()))
+
+
+NORMUON_BETA2 = 0.95
+
+
+def _normuon_slices(depth):
+    """Slice of each block matrix in the NorMuon state (layout of include/gpt.h)."""
+    dm = syn.model_dims(depth)
+    d, f = dm["d"], dm["mlp"]
+    out = {}
+    for l in range(depth):
+        for k, n in enumerate(("wq", "wk", "wv", "wo")):
+            o = (4 * l + k) * d
+            out[f"h{l}.{n}"] = slice(o, o + d)
+        for k, n in enumerate(("wfc", "wproj")):
+            o = 4 * depth * d + (2 * l + k) * f
+            out[f"h{l}.{n}"] = slice(o, o + f)
+    return out
+
+
+def _row_scaled_grads(depth, vocab, seed):
+    """Gradients whose neurons (rows; columns of wproj) differ in scale by up to 15x,
+    so the per-neuron rescaling is far from uniform."""
+    g = syn.random_like_grads(depth, vocab, seed=seed, scale=1e-2)
+    rng = np.random.default_rng(seed + 100)
+    for k, v in g.items():
+        if k.endswith("wproj"):
+            v *= rng.uniform(0.2, 3.0, size=(1, v.shape[1])).astype(np.float32)
+        else:
+            v *= rng.uniform(0.2, 3.0, size=(v.shape[0], 1)).astype(np.float32)
+    return g
+
+
+@pytest.mark.parametrize("cfg_name", ["tiny", "d20"])
+def test_normuon_step_matches_oracle(cfg_name):
+    """Two NorMuon steps from a seeded non-uniform second-moment state, against the
+    oracle on identical fp32 inputs. Each step's update: rel-L2 < 2e-2 as for
+    muon_step; momentum 1e-6; state 1e-3 (means of squares of the orthogonalised
+    update, whose error is near 1e-4); wte and lm_head untouched; bf16 shadow is
+    the rounded master. d20 checks layer 0 (the oracle's iteration in fp64 on all
+    120 matrices would take minutes); the device updates every layer."""
+    cfg = syn.CONFIGS[cfg_name]
+    depth, vocab = cfg["depth"], cfg["vocab"]
+    log(f"normuon {cfg_name}")
+    w = syn.init_weights(depth, vocab, seed=0)
+    grads = [_row_scaled_grads(depth, vocab, 7), _row_scaled_grads(depth, vocab, 9)]
+    st = TrainState(depth, vocab, cfg["seq"], 1)
+    st.load_weights(w)
+    slices = _normuon_slices(depth)
+    n_state = st.model.normuon_state_elems()
+    assert n_state == max(s.stop for s in slices.values())
+    d = syn.model_dims(depth)["d"]
+    v0 = np.random.default_rng(11).uniform(0.2, 2.0, size=n_state).astype(np.float32) / np.float32(d)
+    st.second_moment.copy_(torch.from_numpy(v0))
+    names = list(slices) if cfg_name == "tiny" else [k for k in slices if k.startswith("h0.")]
+    f64 = lambda dd: {k: dd[k].astype(np.float64) for k in names}
+    ref_w = f64(w)
+    ref_m = {k: np.zeros_like(v) for k, v in ref_w.items()}
+    ref_v = {k: v0[slices[k]].astype(np.float64) for k in names}
+    prev = st.to_host(st.params)
+    for step, g in enumerate(grads, 1):
+        st.load_grads(g)
+        st.normuon(syn.MUON_LR, syn.MUON_MOMENTUM, NORMUON_BETA2, syn.NS_COEFFS)
+        ref_w, ref_m, ref_v, ref_upd = oracle.normuon_step(ref_w, f64(g), ref_m, ref_v, syn.MUON_LR,
+                                                           syn.MUON_MOMENTUM, NORMUON_BETA2, syn.NS_COEFFS,
+                                                           names=names)
+        torch.cuda.synchronize()
+        cur = st.to_host(st.params)
+        mom = st.to_host(st.momentum)
+        state = st.second_moment.cpu().numpy()
+        worst = []
+        for k in names:
+            e = rel_l2(prev[k].astype(np.float64) - cur[k], ref_upd[k])
+            worst.append((e, k))
+            assert e < REL_TOL, (step, k, e)
+            assert rel_l2(mom[k], ref_m[k]) < 1e-6, (step, k)
+            ev = rel_l2(state[slices[k]], ref_v[k])
+            assert ev < 1e-3, (step, k, ev)
+        log(f"  step {step} worst update rel-L2 " + " ".join(f"{k}:{e:.2e}" for e, k in sorted(worst)[-3:]))
+        for k in ("wte", "lm_head"):
+            np.testing.assert_array_equal(cur[k], w[k])
+        prev = cur
+    np.testing.assert_array_equal(st.params_bf16.cpu().numpy(), bf16_bits(st.params.cpu().numpy()))
+
+
+def test_normuon_differs_from_muon_only_by_neuron_scales():
+    """Same inputs through muon_step and normuon_step on the device: for every
+    block matrix the two updates have equal Frobenius norms (to fp32 rounding) and
+    their ratio is constant along each neuron."""
+    cfg = syn.CONFIGS["tiny"]
+    depth, vocab = cfg["depth"], cfg["vocab"]
+    log("normuon vs muon tiny")
+    w = syn.init_weights(depth, vocab, seed=0)
+    g = _row_scaled_grads(depth, vocab, 3)
+    out = []
+    for use_nm in (False, True):
+        st = TrainState(depth, vocab, cfg["seq"], 1)
+        st.load_weights(w)
+        st.load_grads(g)
+        if use_nm:
+            st.normuon(syn.MUON_LR, syn.MUON_MOMENTUM, 0.0, syn.NS_COEFFS)
+        else:
+            st.muon(syn.MUON_LR, syn.MUON_MOMENTUM, syn.NS_COEFFS)
+        torch.cuda.synchronize()
+        out.append(st.to_host(st.params))
+    for k in _normuon_slices(depth):
+        u_mu = w[k].astype(np.float64) - out[0][k]
+        u_nm = w[k].astype(np.float64) - out[1][k]
+        assert abs(np.linalg.norm(u_nm) / np.linalg.norm(u_mu) - 1) < 1e-3, k
+        # beta2 = 0: every neuron of the NorMuon update has the same norm.
+        axis = 0 if k.endswith("wproj") else 1
+        nrm = np.linalg.norm(u_nm, axis=axis)
+        assert np.ptp(nrm) < 2e-3 * nrm.mean(), (k, np.ptp(nrm) / nrm.mean())
