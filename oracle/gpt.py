@@ -11,7 +11,7 @@ the page is silent:
     xn  = rms(x)                                      (pre-norm, no gain)
     q,k,v = xn Wq^T, xn Wk^T, xn Wv^T, split into 128-wide heads
     q,k = rope(rms(q)), rope(rms(k))                  (QK-norm per head, then RoPE)
-    o   = causal softmax(q k^T / sqrt(128)) v
+    o   = causal softmax(q k^T / sqrt(128)) v        (optionally windowed per layer)
     x   = x + o Wo^T
     x   = x + relu(rms(x) Wfc^T)^2 Wproj^T            (ReLU^2 MLP)
   z    = rms(x) Wlm^T                                 (final norm, untied head)
@@ -25,10 +25,17 @@ targets equal to -1 are ignored in the mean.
 The backward pass is derived by hand per operation (no autodiff library), so
 the finite-difference tests in tests/ check it against the forward pass.
 
+Window attention (optional, per layer): the pages list alternating short and
+long attention windows but give no sizes, so the windows are an input; a
+window W lets query i see keys i - W .. i.
+
 Parity pins (tests/test_oracle_model.py): central finite differences in fp64 on
-depth-1 and depth-2 models; loss = ln V and a closed-form lm_head gradient for a
-zero unembedding; causal invariance; attention closed forms (T = 1, q = 0);
-RMSNorm / RoPE invariants; cross-entropy row sums; embedding-gradient support.
+depth-1 and depth-2 models (one with a windowed layer); loss = ln V and a
+closed-form lm_head gradient for a zero unembedding; causal invariance;
+attention closed forms (T = 1, q = 0, window 0 returns v); a window equals
+causal attention over the trailing slice; a window covering the sequence is
+the causal mask; RMSNorm / RoPE invariants; cross-entropy row sums;
+embedding-gradient support.
 """
 from __future__ import annotations
 
@@ -77,9 +84,14 @@ def rope_bwd(dy, cos, sin):
     return np.concatenate([d1 * c + d2 * s, -d1 * s + d2 * c], axis=-1)
 
 
-def causal_attention(q, k, v):
+def causal_attention(q, k, v, window=None):
     """Softmax attention with mask j <= i; q, k, v are [T, H, hd].
 
+    With a window W (an int >= 0) key j is visible to query i only when
+    i - W <= j <= i as well ([CT50] "1. Modelo GPT" lists short/long window
+    attention, and "5. Flash Attention Unificado" passes a window_size to the
+    attention call; W keys to the left of the query plus the query itself).
+    None is the plain causal mask.
     Returns o [T, H, hd] and the probabilities P [H, T, T].
     """
     T, _H, hd = q.shape
@@ -87,6 +99,8 @@ def causal_attention(q, k, v):
     qh, kh, vh = (a.transpose(1, 0, 2) for a in (q, k, v))  # [H, T, hd]
     s = np.matmul(qh, kh.transpose(0, 2, 1)) * scale
     mask = np.tril(np.ones((T, T), dtype=bool))
+    if window is not None:
+        mask &= np.triu(np.ones((T, T), dtype=bool), -int(window))
     s = np.where(mask[None], s, -np.inf)
     s = s - s.max(axis=-1, keepdims=True)
     e = np.exp(s)
@@ -124,8 +138,16 @@ def _depth(weights):
     return n
 
 
-def _forward_sequence(weights, tok, cos, sin, final_norm=True):
-    """Forward pass of one sequence; returns the logits and the saved values."""
+def _layer_window(windows, layer):
+    return None if windows is None else windows[layer]
+
+
+def _forward_sequence(weights, tok, cos, sin, final_norm=True, windows=None):
+    """Forward pass of one sequence; returns the logits and the saved values.
+
+    windows: None, or one attention window per layer (an int, or None for the
+    full causal context).
+    """
     L = _depth(weights)
     wte = weights["wte"]
     d = wte.shape[1]
@@ -142,7 +164,7 @@ def _forward_sequence(weights, tok, cos, sin, final_norm=True):
         qn, rq = rms_norm(q)
         kn, rk = rms_norm(k)
         qr, kr = rope(qn, cos, sin), rope(kn, cos, sin)
-        o, p = causal_attention(qr, kr, v)
+        o, p = causal_attention(qr, kr, v, _layer_window(windows, layer))
         o2 = o.reshape(T, d)
         x_mid = x + o2 @ w["wo"].T
         xn2, r2 = rms_norm(x_mid)
@@ -159,19 +181,19 @@ def _forward_sequence(weights, tok, cos, sin, final_norm=True):
     return z, dict(layers=layers, xnf=xnf, rf=rf)
 
 
-def forward_logits(weights, tokens, final_norm=True):
+def forward_logits(weights, tokens, final_norm=True, windows=None):
     """Logits [B, T, V] for int tokens [B, T] (no loss, no gradients)."""
     tokens = np.asarray(tokens)
     T = tokens.shape[1]
     dt = weights["wte"].dtype
     cos, sin = rope_tables(T, dtype=dt)
-    return np.stack([_forward_sequence(weights, tokens[b], cos, sin, final_norm)[0]
+    return np.stack([_forward_sequence(weights, tokens[b], cos, sin, final_norm, windows)[0]
                      for b in range(tokens.shape[0])])
 
 
-def per_position_loss(weights, tokens, targets, final_norm=True):
+def per_position_loss(weights, tokens, targets, final_norm=True, windows=None):
     """lse(z) - z[target] at every position (0 where the target is ignored)."""
-    z = forward_logits(weights, tokens, final_norm)
+    z = forward_logits(weights, tokens, final_norm, windows)
     out = np.zeros(targets.shape, dtype=z.dtype)
     for b in range(z.shape[0]):
         lse = log_softmax_rows(z[b])
@@ -181,8 +203,10 @@ def per_position_loss(weights, tokens, targets, final_norm=True):
     return out
 
 
-def forward_backward(weights, tokens, targets, final_norm=True, want_grads=True):
+def forward_backward(weights, tokens, targets, final_norm=True, want_grads=True, windows=None):
     """Mean cross-entropy loss and the gradient of every tensor.
+
+    windows: None, or one attention window per layer (see causal_attention).
 
     Sequences are independent, so the batch is processed one row at a time and
     the per-row contributions are summed (this bounds memory; it is exact).
@@ -201,7 +225,7 @@ def forward_backward(weights, tokens, targets, final_norm=True, want_grads=True)
     H = d // HEAD_DIM
     for b in range(B):
         tok, tgt = tokens[b], targets[b]
-        z, c = _forward_sequence(weights, tok, cos, sin, final_norm)
+        z, c = _forward_sequence(weights, tok, cos, sin, final_norm, windows)
         lse = log_softmax_rows(z)
         valid = tgt >= 0
         t = np.where(valid, tgt, 0)

@@ -28,20 +28,20 @@ def _ids(batch, seq, vocab, seed):
 # ----------------------------------------------------------------------------
 # Whole-model gradient: central finite differences in fp64
 # ----------------------------------------------------------------------------
-@pytest.mark.parametrize("depth", [1, 2])
-def test_gradients_match_central_differences(depth):
+@pytest.mark.parametrize("depth,windows", [(1, None), (2, None), (2, [3, None])])
+def test_gradients_match_central_differences(depth, windows):
     vocab, seq, batch = 96, 12, 2
     w = _tiny_weights(depth, vocab, seed=3, std=0.15)
     tok, tgt = _ids(batch, seq, vocab, seed=5)
     tgt = tgt.copy()
     tgt[0, 3] = -1  # one ignored target exercises the valid-count normalisation
-    loss, grads = oracle.forward_backward(w, tok, tgt)
+    loss, grads = oracle.forward_backward(w, tok, tgt, windows=windows)
     assert np.isfinite(loss)
     rng = np.random.default_rng(11)
     h = 1e-4
 
     def f(ww):
-        return oracle.forward_backward(ww, tok, tgt, want_grads=False)[0]
+        return oracle.forward_backward(ww, tok, tgt, want_grads=False, windows=windows)[0]
 
     for name in w:
         # Directional derivative along a random direction.
@@ -170,6 +170,67 @@ def test_attention_backward_matches_finite_differences():
         fm = np.sum(w * oracle.causal_attention(q, k, v)[0])
         arr += h * u
         assert abs((fp - fm) / (2 * h) - np.sum(grad * u)) < 1e-7
+
+
+# ----------------------------------------------------------------------------
+# Window attention: special cases and an independent formulation
+# ----------------------------------------------------------------------------
+def test_window_zero_sees_only_itself():
+    rng = np.random.default_rng(20)
+    q, k, v = (rng.standard_normal((9, 2, 128)) for _ in range(3))
+    o, p = oracle.causal_attention(q, k, v, window=0)
+    np.testing.assert_allclose(o, v, rtol=0, atol=1e-15)
+    np.testing.assert_array_equal(p, np.broadcast_to(np.eye(9), p.shape))
+
+
+@pytest.mark.parametrize("window", [8, 9, 50])
+def test_window_covering_the_sequence_is_causal(window):
+    rng = np.random.default_rng(21)
+    q, k, v = (rng.standard_normal((9, 2, 128)) for _ in range(3))
+    np.testing.assert_array_equal(oracle.causal_attention(q, k, v, window=window)[0],
+                                  oracle.causal_attention(q, k, v)[0])
+
+
+@pytest.mark.parametrize("window", [1, 3, 6])
+def test_window_is_causal_attention_on_the_trailing_slice(window):
+    # Attention has no positions of its own, so query i under window W equals
+    # the last row of plain causal attention over rows max(0, i - W) .. i.
+    rng = np.random.default_rng(22)
+    T = 13
+    q, k, v = (rng.standard_normal((T, 2, 128)) * 0.5 for _ in range(3))
+    o, _ = oracle.causal_attention(q, k, v, window=window)
+    for i in range(T):
+        lo = max(0, i - window)
+        oi, _ = oracle.causal_attention(q[lo:i + 1], k[lo:i + 1], v[lo:i + 1])
+        np.testing.assert_allclose(o[i], oi[-1], rtol=1e-13, atol=1e-14)
+
+
+def test_window_backward_matches_finite_differences():
+    rng = np.random.default_rng(23)
+    T, H, hd, W = 10, 2, 128, 3
+    q, k, v = (rng.standard_normal((T, H, hd)) * 0.3 for _ in range(3))
+    w = rng.standard_normal((T, H, hd))
+    o, p = oracle.causal_attention(q, k, v, window=W)
+    dq, dk, dv = oracle.causal_attention_bwd(w, q, k, v, p)
+    h = 1e-6
+    for arr, grad in ((q, dq), (k, dk), (v, dv)):
+        u = rng.standard_normal(arr.shape)
+        arr += h * u
+        fp = np.sum(w * oracle.causal_attention(q, k, v, window=W)[0])
+        arr -= 2 * h * u
+        fm = np.sum(w * oracle.causal_attention(q, k, v, window=W)[0])
+        arr += h * u
+        assert abs((fp - fm) / (2 * h) - np.sum(grad * u)) < 1e-7
+
+
+def test_windowed_model_matches_full_model_until_the_window_binds():
+    depth, vocab, seq, W = 2, 128, 16, 5
+    w = _tiny_weights(depth, vocab, seed=4, std=0.1)
+    tok, _ = _ids(1, seq, vocab, seed=6)
+    z_full = oracle.forward_logits(w, tok)
+    z_win = oracle.forward_logits(w, tok, windows=[W, None])
+    np.testing.assert_allclose(z_win[0, : W + 1], z_full[0, : W + 1], rtol=0, atol=1e-13)
+    assert np.abs(z_win[0, W + 1:] - z_full[0, W + 1:]).max() > 1e-6
 
 
 # ----------------------------------------------------------------------------
