@@ -44,8 +44,18 @@ ADAMW = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
 NORMUON_BETA2 = 0.95
 
 
-def flops_per_token(L, d, V, T):
-    return 6.0 * (12.0 * L * d * d + V * d) + 6.0 * L * d * T
+def flops_per_token(L, d, V, T, windows=None):
+    """Model FLOPs per token; causal attention counts T per layer (half of the
+    T^2 score matrix, fwd+bwd). A windowed layer counts 2 * (visible pairs) / T."""
+    att = 0.0
+    for l in range(L):
+        w = -1 if windows is None else windows[l]
+        if w < 0 or w >= T - 1:
+            att += T
+        else:
+            pairs = 0.5 * (w + 1) * (w + 2) + (T - 1 - w) * (w + 1)
+            att += 2.0 * pairs / T
+    return 6.0 * (12.0 * L * d * d + V * d) + 6.0 * d * att
 
 
 def gemm_bytes_per_step(L, d, V, N, chunk):
@@ -97,14 +107,15 @@ def gemm_traffic():
     return float(vals["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(cfg, weights, tok, tgt, normuon=False):
+def cpu_baseline(cfg, weights, tok, tgt, normuon=False, windows=None):
     """Time the oracle on a bounded sample and scale it to one full step."""
     import oracle  # test infrastructure: used here only for the CPU baseline leg
 
     cores = len(os.sched_getaffinity(0))
     L, B, T = cfg["depth"], cfg["batch"], cfg["seq"]
     t0 = time.perf_counter()
-    oracle.forward_backward(weights, tok[:1], tgt[:1])
+    oracle.forward_backward(weights, tok[:1], tgt[:1],
+                            windows=None if windows is None else [None if w < 0 else w for w in windows])
     t_seq = time.perf_counter() - t0
     names = [f"h0.{n}" for n in ("wq", "wk", "wv", "wo", "wfc", "wproj")]
     sub_w = {k: weights[k] for k in names}
@@ -147,6 +158,8 @@ def main():
     ap.add_argument("--config", default="d20", choices=sorted(syn.CONFIGS))
     ap.add_argument("--accum", type=int, default=1,
                     help="microbatches per optimizer step (gradient accumulation)")
+    ap.add_argument("--window-pattern", default=None,
+                    help="per-layer attention windows, e.g. SSSL (S: seq/2 keys, L: full causal)")
     ap.add_argument("--normuon", action="store_true",
                     help="NorMuon variance reduction after Newton-Schulz (normuon_step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -163,7 +176,7 @@ def main():
 
     import torch
 
-    from gpt_pretraining_step_bf16_amd.step import TrainState
+    from gpt_pretraining_step_bf16_amd.step import TrainState, window_pattern
 
     cfg = syn.CONFIGS[args.config]
     L, V, T, B = cfg["depth"], cfg["vocab"], cfg["seq"], cfg["batch"]
@@ -175,6 +188,8 @@ def main():
     tok, tgt = syn.split_tokens(syn.zipf_ids(B, T, V, seed=1))
     st = TrainState(L, V, T, B)
     st.load_weights(weights)
+    windows = window_pattern(L, T, args.window_pattern) if args.window_pattern else None
+    st.set_windows(windows)
     tok_d = torch.from_numpy(tok).cuda()
     tgt_d = torch.from_numpy(tgt).cuda()
     if args.copy_probe_mib > 0:
@@ -232,7 +247,7 @@ def main():
 
     ms_step = elapsed_ms / args.steps
     tokens_per_s = accum * B * T * args.steps / (elapsed_ms / 1e3)
-    f_tok = flops_per_token(L, d, V, T)
+    f_tok = flops_per_token(L, d, V, T, windows)
     mfu = tokens_per_s * f_tok / PEAK_BF16_FLOPS
     mfma_work = (tokens_per_s * f_tok + ns_flops(L, d) / (ms_step / 1e3)) / PEAK_BF16_FLOPS
     # The AdamW call alone, timed after the steps (HIP events on the current stream).
@@ -292,6 +307,8 @@ def main():
             "workload": f"{args.config}: depth {L}, width {d}, {dims['heads']} heads x 128, MLP {4 * d}, "
                         f"vocab {V}, seq {T}, microbatch {B}"
                         + (f" x {accum} accumulated" if accum > 1 else "")
+                        + (f"; attention windows {args.window_pattern.upper()} (S = {T // 2} keys)"
+                           if args.window_pattern else "")
                         + "; fwd+bwd+" + ("NorMuon" if args.normuon else "Muon")
                         + " (5 Newton-Schulz steps)+AdamW (wte, lm_head)",
             "global_batch": accum * B,
@@ -309,7 +326,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(cfg, weights, tok, tgt, args.normuon)
+        out["cpu_baseline"] = cpu_baseline(cfg, weights, tok, tgt, args.normuon, windows)
     print(json.dumps(out), flush=True)
 
 

@@ -71,8 +71,10 @@ EXPORTS = {
     "gpt_check": (C.c_int, [_P, _P, _P]),
     "gpt_status_str": (C.c_char_p, [C.c_int]),
     "gpt_op_gemm": (C.c_int, [_I, _I, _I, _I, _P, _L, _L, _I, _P, _L, _L, _I, _P, _L, _L, _I, _P]),
-    "gpt_op_attention_fwd": (C.c_int, [_P, _P, _P, _I, _I, _I, _P]),
-    "gpt_op_attention_bwd": (C.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
+    "gpt_op_attention_fwd": (C.c_int, [_P, _P, _P, _I, _I, _I, _I, _P]),
+    "gpt_op_attention_bwd": (C.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
+    "gpt_set_attention_windows": (C.c_int, [_P, C.POINTER(C.c_int32), _I]),
+    "gpt_get_attention_windows": (C.c_int, [_P, C.POINTER(C.c_int32), _I]),
     "gpt_op_ns_scratch_bytes": (C.c_size_t, [_I, _I, _I]),
     "gpt_op_newton_schulz": (C.c_int, [_P, _I, _I, _I, C.POINTER(C.c_float), _I, _P, _S, _P]),
     "gpt_profile_enable": (C.c_int, [_P, _I]),
@@ -165,6 +167,20 @@ class GptModel:
                             cols=int(t.cols), kind=KIND_NAMES[int(t.kind)], layer=int(t.layer)))
         return out
 
+    def set_windows(self, windows):
+        """Per-layer attention windows (None entries or -1: full causal context)."""
+        if windows is None:
+            _check(lib().gpt_set_attention_windows(self._h, None, 0), "gpt_set_attention_windows")
+            return
+        vals = [-1 if w is None else int(w) for w in windows]
+        arr = (C.c_int32 * len(vals))(*vals)
+        _check(lib().gpt_set_attention_windows(self._h, arr, len(vals)), "gpt_set_attention_windows")
+
+    def windows(self):
+        arr = (C.c_int32 * self.depth)()
+        _check(lib().gpt_get_attention_windows(self._h, arr, self.depth), "gpt_get_attention_windows")
+        return list(arr)
+
     def workspace_bytes(self, batch: int, seq: int) -> int:
         return int(lib().gpt_workspace_bytes(self._h, batch, seq))
 
@@ -240,14 +256,14 @@ def op_gemm(M, N, K, A, lda, a_kmajor, B, ldb, b_kmajor, Cout, ldc, out_mode, ba
     _check(st, "gpt_op_gemm")
 
 
-def op_attention_fwd(qkv, o, lse, batch, seq, heads, stream=None):
-    _check(lib().gpt_op_attention_fwd(_ptr(qkv), _ptr(o), _ptr(lse), batch, seq, heads,
+def op_attention_fwd(qkv, o, lse, batch, seq, heads, window=-1, stream=None):
+    _check(lib().gpt_op_attention_fwd(_ptr(qkv), _ptr(o), _ptr(lse), batch, seq, heads, int(window),
                                       _stream(stream)), "gpt_op_attention_fwd")
 
 
-def op_attention_bwd(qkv, o, lse, dO, dqkv, scratch, batch, seq, heads, stream=None):
+def op_attention_bwd(qkv, o, lse, dO, dqkv, scratch, batch, seq, heads, window=-1, stream=None):
     _check(lib().gpt_op_attention_bwd(_ptr(qkv), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dqkv),
-                                      _ptr(scratch), batch, seq, heads, _stream(stream)),
+                                      _ptr(scratch), batch, seq, heads, int(window), _stream(stream)),
            "gpt_op_attention_bwd")
 
 

@@ -1,0 +1,14 @@
+// Launchers of the flash-attention kernels with an attention window (defined
+// in attention.hip): key j is visible to query i when i - window <= j <= i; a
+// negative window (or one of at least T) is the plain causal mask.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+hipError_t launch_attention_fwd_window(const uint16_t* qkv, uint16_t* o, float* lse2, int B, int T, int H,
+                                       int window, hipStream_t s);
+hipError_t launch_attention_bwd_window(const uint16_t* qkv, const uint16_t* o, const float* lse2,
+                                       const uint16_t* dO, uint16_t* dqkv, float* delta, int B, int T, int H,
+                                       int window, hipStream_t s);

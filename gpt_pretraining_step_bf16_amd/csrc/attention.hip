@@ -2,7 +2,10 @@
 //
 // [CT50] "1. Modelo GPT" and "5. Flash Attention Unificado": causal softmax
 // attention computed by a fused flash-attention kernel (the page's FA3 is
-// written for Hopper; this is a gfx950 design).
+// written for Hopper; this is a gfx950 design), optionally with a window W
+// (short/long window attention): key j is visible to query i when
+// i - W <= j <= i. W >= T - 1 is the plain causal mask. Tiles wholly outside
+// the band are skipped, not masked.
 //
 // Layout: q, k, v live in one packed buffer qkv [B*T, 3*H*128] bf16 (q heads,
 // then k heads, then v heads; 128 columns per head), o is [B*T, H*128].
@@ -45,6 +48,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "attention.h"
 #include "kernels.h"
 #include "lds_dma.h"
 
@@ -173,7 +177,7 @@ __device__ __forceinline__ void head_block(int& blk, int& bh) {
 // ===========================================================================
 __global__ void __launch_bounds__(NTHR, 2)
     attn_fwd_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ out,
-                    float* __restrict__ lse2, int T, int H) {
+                    float* __restrict__ lse2, int T, int H, int W) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];  // [stage][K, V]
 
   const int tid = threadIdx.x;
@@ -218,10 +222,14 @@ __global__ void __launch_bounds__(NTHR, 2)
 
   const int qmax = min(T - 1, qblk * QB + QB - 1);
   const int nkb = qmax / KB + 1;
+  const int kb_lo = max(0, qblk * QB - W) / KB;  // first tile inside the window of the block
 
   TileDma td;
   tile_dma_init(td, ld, wave, lane);
-  const int klim = min(qpos, T - 1);  // last key visible to this lane's query
+  // Keys visible to this lane's query: kwin .. kwin + kspan, i.e.
+  // qpos - W .. min(qpos, T - 1).
+  const int kwin = qpos - W;
+  const uint32_t kspan = (uint32_t)(min(qpos, T - 1) - kwin);
 
   auto issue = [&](int kb, int st) {
     char* ks = smem + st * 2 * TILE;
@@ -232,7 +240,9 @@ __global__ void __launch_bounds__(NTHR, 2)
   auto block = [&](int kb, int st) {
     const char* ks = smem + st * 2 * TILE;
     const char* vs = ks + TILE;
-    if (kb * KB > q0 + 31) return;  // no key of this block is visible to the wave
+    // No key of this block is visible to the wave: past its last query, or
+    // before the window of its first query.
+    if (kb * KB > q0 + 31 || kb * KB + KB - 1 < q0 - W) return;
     f32x16 s[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -254,14 +264,14 @@ __global__ void __launch_bounds__(NTHR, 2)
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     // s[t][v]: key kb*64 + 32t + 8(v/4) + 4hl + v%4, query qpos (raw q.k).
-    const bool need_mask = (kb * KB + KB - 1 > q0) || (kb * KB + KB > T);
+    const bool need_mask = (kb * KB + KB - 1 > q0) || (kb * KB + KB > T) || (kb * KB < q0 + 31 - W);
     if (need_mask) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = kb * KB + 32 * t + 8 * (v >> 2) + 4 * hl + (v & 3);
-          if (key > klim) s[t][v] = -INFINITY;
+          if ((uint32_t)(key - kwin) > kspan) s[t][v] = -INFINITY;
         }
     }
     float mloc = -INFINITY;
@@ -309,9 +319,9 @@ __global__ void __launch_bounds__(NTHR, 2)
     }
   };
 
-  issue(0, 0);
+  issue(kb_lo, 0);
   VMCNT_BARRIER(0);
-  for (int kb = 0; kb < nkb; kb += 2) {
+  for (int kb = kb_lo; kb < nkb; kb += 2) {
     if (kb + 1 < nkb) issue(kb + 1, 1);
     block(kb, 0);
     VMCNT_BARRIER(0);
@@ -355,7 +365,7 @@ constexpr int DKDV_NST = 4;                         // stages of the Q/dO ring
 __global__ void __launch_bounds__(NTHR, 1)
     attn_bwd_dkdv_kernel(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dO,
                          const float* __restrict__ lse2, const float* __restrict__ delta,
-                         uint16_t* __restrict__ dqkv, int T, int H) {
+                         uint16_t* __restrict__ dqkv, int T, int H, int W) {
   __shared__ __attribute__((aligned(1024))) char smem[DKDV_NST * DKDV_STAGE + 256];
 
   const int tid = threadIdx.x;
@@ -402,8 +412,12 @@ __global__ void __launch_bounds__(NTHR, 1)
       dv[i][v] = 0.f;
     }
 
+  // Query tiles from the block's first key to the last query that sees its
+  // last key (query i sees key j for j <= i <= j + W).
   const int qb_first = (kblk * KBW) / QBW;
-  const int ntile = (T + QBW - 1) / QBW - qb_first;
+  const int qb_end = min((T + QBW - 1) / QBW, (min(T - 1, kblk * KBW + KBW - 1 + W)) / QBW + 1);
+  const int ntile = qb_end - qb_first;
+  const int qlim = min(T - 1 - kpos, W);  // last visible query - kpos (negative past T)
 
   TileDma tq, tg;
   tile_dma_init(tq, ld, wave, lane);
@@ -464,7 +478,8 @@ __global__ void __launch_bounds__(NTHR, 1)
     const float* ds = ls + QBW;
     const int qb = qb_first + n;
     // s[v]: query qb*64 + 32t + 8(v/4) + 4hl + v%4, key kpos.
-    const bool need_mask = (qb * QBW + 32 * t < k0 + 31) || (qb * QBW + 32 * t + 32 > T);
+    const bool need_mask = (qb * QBW + 32 * t < k0 + 31) || (qb * QBW + 32 * t + 32 > T) ||
+                           (qb * QBW + 32 * t + 31 > k0 + W);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int ql = 32 * t + 8 * g + 4 * hl;
@@ -477,8 +492,8 @@ __global__ void __launch_bounds__(NTHR, 1)
         const int q = qb * QBW + ql + r;
         const int v = 4 * g + r;
         float p = fast_exp2(fmaf(s[v], sc, -lq[r]));
-        // Visible iff kpos <= q <= T - 1 (one unsigned compare).
-        if (need_mask && (uint32_t)(q - kpos) > (uint32_t)(T - 1 - kpos)) p = 0.f;
+        // Visible iff kpos <= q <= min(T - 1, kpos + W) (one unsigned compare).
+        if (need_mask && (uint32_t)(q - kpos) > (uint32_t)qlim) p = 0.f;
         s[v] = p;
         dp[v] = p * (dp[v] - dq[r]);
       }
@@ -574,7 +589,7 @@ __global__ void __launch_bounds__(NTHR, 1)
 __global__ void __launch_bounds__(NTHR, 2)
     attn_bwd_dq_kernel(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ o,
                        const uint16_t* __restrict__ dO, const float* __restrict__ lse2,
-                       float* __restrict__ delta, uint16_t* __restrict__ dqkv, int T, int H) {
+                       float* __restrict__ delta, uint16_t* __restrict__ dqkv, int T, int H, int W) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];  // [stage][K, V]
 
   const int tid = threadIdx.x;
@@ -635,10 +650,14 @@ __global__ void __launch_bounds__(NTHR, 2)
 
   const int qmax = min(T - 1, qblk * QB + QB - 1);
   const int nkb = qmax / KB + 1;
+  const int kb_lo = max(0, qblk * QB - W) / KB;
 
   TileDma td;
   tile_dma_init(td, ld, wave, lane);
-  const int klim = min(qpos, T - 1);  // last visible key (lanes past T are discarded)
+  // Visible keys: kwin .. kwin + kspan, i.e. qpos - W .. min(qpos, T - 1)
+  // (lanes past T are discarded).
+  const int kwin = qpos - W;
+  const uint32_t kspan = (uint32_t)(min(qpos, T - 1) - kwin);
 
   auto issue = [&](int kb, int st) {
     char* ks = smem + st * 2 * TILE;
@@ -649,8 +668,9 @@ __global__ void __launch_bounds__(NTHR, 2)
   auto block = [&](int kb, int st) {
     const char* ks = smem + st * 2 * TILE;
     const char* vs = ks + TILE;
-    if (kb * KB > q0 + 31) return;
-    const bool need_mask = (kb * KB + KB - 1 > q0) || (kb * KB + KB > T) || (q0 + 32 > T);
+    if (kb * KB > q0 + 31 || kb * KB + KB - 1 < q0 - W) return;
+    const bool need_mask =
+        (kb * KB + KB - 1 > q0) || (kb * KB + KB > T) || (q0 + 32 > T) || (kb * KB < q0 + 31 - W);
     // One 32-key half of the tile at a time (keeps two accumulators live, not
     // four); fragments are read one k-step (or one dim tile) ahead.
 #pragma unroll
@@ -685,7 +705,7 @@ __global__ void __launch_bounds__(NTHR, 2)
       for (int v = 0; v < 16; ++v) {
         const int key = kb * KB + 32 * t + 8 * (v >> 2) + 4 * hl + (v & 3);
         float p = fast_exp2(fmaf(sv[v], sc, -lq));
-        if (need_mask && key > klim) p = 0.f;
+        if (need_mask && (uint32_t)(key - kwin) > kspan) p = 0.f;
         dp[v] = p * (dp[v] - dq_);
       }
       const bf16x8 ds0 = pack_frag(dp, 0);
@@ -706,9 +726,9 @@ __global__ void __launch_bounds__(NTHR, 2)
     }
   };
 
-  issue(0, 0);
+  issue(kb_lo, 0);
   VMCNT_BARRIER(0);
-  for (int kb = 0; kb < nkb; kb += 2) {
+  for (int kb = kb_lo; kb < nkb; kb += 2) {
     if (kb + 1 < nkb) issue(kb + 1, 1);
     block(kb, 0);
     VMCNT_BARRIER(0);
@@ -736,24 +756,37 @@ __global__ void __launch_bounds__(NTHR, 2)
 
 }  // namespace
 
+hipError_t launch_attention_fwd_window(const uint16_t* qkv, uint16_t* o, float* lse2, int B, int T, int H,
+                                       int window, hipStream_t s) {
+  if (B <= 0 || T <= 0 || H <= 0) return hipSuccess;
+  const int W = (window < 0 || window > T) ? T : window;
+  dim3 grid((T + QB - 1) / QB, B * H);
+  hipLaunchKernelGGL(attn_fwd_kernel, grid, dim3(NTHR), 0, s, qkv, o, lse2, T, H, W);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_bwd_window(const uint16_t* qkv, const uint16_t* o, const float* lse2,
+                                       const uint16_t* dO, uint16_t* dqkv, float* delta, int B, int T, int H,
+                                       int window, hipStream_t s) {
+  if (B <= 0 || T <= 0 || H <= 0) return hipSuccess;
+  const int W = (window < 0 || window > T) ? T : window;
+  // dQ first: it also writes delta = rowsum(dO * O), which dK/dV reads.
+  hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((T + QB - 1) / QB, B * H), dim3(NTHR), 0, s, qkv, o, dO,
+                     lse2, delta, dqkv, T, H, W);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((T + KBW - 1) / KBW, B * H), dim3(NTHR), 0, s, qkv,
+                     dO, lse2, delta, dqkv, T, H, W);
+  return hipGetLastError();
+}
+
 hipError_t launch_attention_fwd(const uint16_t* qkv, uint16_t* o, float* lse2, int B, int T, int H,
                                 hipStream_t s) {
-  if (B <= 0 || T <= 0 || H <= 0) return hipSuccess;
-  dim3 grid((T + QB - 1) / QB, B * H);
-  hipLaunchKernelGGL(attn_fwd_kernel, grid, dim3(NTHR), 0, s, qkv, o, lse2, T, H);
-  return hipGetLastError();
+  return launch_attention_fwd_window(qkv, o, lse2, B, T, H, -1, s);
 }
 
 hipError_t launch_attention_bwd(const uint16_t* qkv, const uint16_t* o, const float* lse2,
                                 const uint16_t* dO, uint16_t* dqkv, float* delta, int B, int T,
                                 int H, hipStream_t s) {
-  if (B <= 0 || T <= 0 || H <= 0) return hipSuccess;
-  // dQ first: it also writes delta = rowsum(dO * O), which dK/dV reads.
-  hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((T + QB - 1) / QB, B * H), dim3(NTHR), 0, s, qkv, o, dO,
-                     lse2, delta, dqkv, T, H);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((T + KBW - 1) / KBW, B * H), dim3(NTHR), 0, s, qkv,
-                     dO, lse2, delta, dqkv, T, H);
-  return hipGetLastError();
+  return launch_attention_bwd_window(qkv, o, lse2, dO, dqkv, delta, B, T, H, -1, s);
 }

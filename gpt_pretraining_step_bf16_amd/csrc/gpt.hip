@@ -16,6 +16,7 @@
 #include "../../include/gpt.h"
 #include "common.h"
 #include "kernels.h"
+#include "attention.h"
 #include "optimizer.h"
 
 namespace {
@@ -34,6 +35,8 @@ struct gpt_model {
   std::vector<gpt_tensor> tensors;
   int64_t nparams = 0;
   int64_t off_wte = 0, off_layer0 = 0, layer_stride = 0, off_lm = 0;
+  // Attention window per layer (-1: the full causal context).
+  std::vector<int32_t> windows;
   // Opt-in launch timing (gpt_profile_*): a pool of event pairs, reused.
   bool prof_on = false;
   std::vector<ProfSlot> prof;
@@ -71,6 +74,12 @@ struct ProfScope {
 };
 
 enum { PROF_GEMM = 0, PROF_ATTN_FWD = 1, PROF_ATTN_BWD = 2, PROF_NS = 3, PROF_NCAT = 4 };
+
+// Visible (query, key) pairs of one sequence of T under window w (-1: causal).
+double attn_pairs(long T, long w) {
+  if (w < 0 || w >= T - 1) return 0.5 * T * (T + 1);
+  return 0.5 * (w + 1) * (w + 2) + (double)(T - 1 - w) * (w + 1);
+}
 
 // Thread-local current model for the GEMM helpers' profiling.
 thread_local gpt_model* g_prof_model = nullptr;
@@ -453,6 +462,7 @@ gpt_status gpt_create(int32_t depth, int32_t vocab, int32_t max_seq, gpt_model**
   m->F = 4 * m->d;
   m->V = vocab;
   m->max_seq = max_seq;
+  m->windows.assign(depth, -1);
   const int64_t d = m->d, F = m->F;
   int64_t off = 0;
   auto add = [&](const std::string& name, int32_t rows, int32_t cols, int32_t kind, int32_t layer) {
@@ -576,8 +586,8 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
     HIP_TRY(gemm_nt(xn1, d, wqkv, d, (int)N, 3 * d, d, qkv, 3L * d, EPI_BF16, s));
     HIP_TRY(launch_qknorm_rope_fwd(qkv, rstdqk, cs, N, T, H, s));
     {
-      ProfScope ps(m, s, PROF_ATTN_FWD, 4.0 * batch * H * 128.0 * T * (T + 1) / 2.0);
-      HIP_TRY(launch_attention_fwd(qkv, o, lse, batch, T, H, s));
+      ProfScope ps(m, s, PROF_ATTN_FWD, 4.0 * batch * H * 128.0 * attn_pairs(T, m->windows[l]));
+      HIP_TRY(launch_attention_fwd_window(qkv, o, lse, batch, T, H, m->windows[l], s));
     }
     HIP_TRY(gemm_nt_add_f32(o, d, wo, d, (int)N, d, d, x, d, s));
     HIP_TRY(launch_rmsnorm_fwd(x, xn2, rstd2, N, d, s));
@@ -642,8 +652,8 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
     HIP_TRY(gemm_nn(dxb, d, wo, d, (int)N, d, d, dO, d, EPI_BF16, s));
     HIP_TRY(gemm_wgrad(dxb, d, o, d, d, d, N, go, accumulate, part, s));
     {
-      ProfScope ps(m, s, PROF_ATTN_BWD, 10.0 * batch * H * 128.0 * T * (T + 1) / 2.0);
-      HIP_TRY(launch_attention_bwd(qkv, o, lse, dO, dqkv, delta, batch, T, H, s));
+      ProfScope ps(m, s, PROF_ATTN_BWD, 10.0 * batch * H * 128.0 * attn_pairs(T, m->windows[l]));
+      HIP_TRY(launch_attention_bwd_window(qkv, o, lse, dO, dqkv, delta, batch, T, H, m->windows[l], s));
     }
     HIP_TRY(launch_qknorm_rope_bwd(dqkv, qkv, rstdqk, cs, N, T, H, s));
     HIP_TRY(gemm_nn(dqkv, 3L * d, wqkv, d, (int)N, d, 3 * d, dxn, d, EPI_F32, s));
@@ -810,20 +820,40 @@ gpt_status gpt_op_gemm(int32_t M, int32_t N, int32_t K, int32_t batch, const uin
 }
 
 gpt_status gpt_op_attention_fwd(const uint16_t* qkv, uint16_t* o, float* lse, int32_t batch,
-                                int32_t seq, int32_t heads, void* stream) {
-  if (!qkv || !o || !lse || batch < 1 || seq < 1 || heads < 1) return GPT_EINVAL;
+                                int32_t seq, int32_t heads, int32_t window, void* stream) {
+  if (!qkv || !o || !lse || batch < 1 || seq < 1 || heads < 1 || window < -1) return GPT_EINVAL;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  HIP_TRY(launch_attention_fwd(qkv, o, lse, batch, seq, heads, s));
+  HIP_TRY(launch_attention_fwd_window(qkv, o, lse, batch, seq, heads, window, s));
   return GPT_OK;
 }
 
 gpt_status gpt_op_attention_bwd(const uint16_t* qkv, const uint16_t* o, const float* lse,
                                 const uint16_t* dO, uint16_t* dqkv, float* scratch,
-                                int32_t batch, int32_t seq, int32_t heads, void* stream) {
-  if (!qkv || !o || !lse || !dO || !dqkv || !scratch || batch < 1 || seq < 1 || heads < 1)
+                                int32_t batch, int32_t seq, int32_t heads, int32_t window, void* stream) {
+  if (!qkv || !o || !lse || !dO || !dqkv || !scratch || batch < 1 || seq < 1 || heads < 1 || window < -1)
     return GPT_EINVAL;
-  HIP_TRY(launch_attention_bwd(qkv, o, lse, dO, dqkv, scratch, batch, seq, heads,
-                               reinterpret_cast<hipStream_t>(stream)));
+  HIP_TRY(launch_attention_bwd_window(qkv, o, lse, dO, dqkv, scratch, batch, seq, heads, window,
+                                      reinterpret_cast<hipStream_t>(stream)));
+  return GPT_OK;
+}
+
+gpt_status gpt_set_attention_windows(gpt_model* m, const int32_t* windows, int32_t n) {
+  if (!m) return GPT_EINVAL;
+  if (!windows) {
+    m->windows.assign(m->depth, -1);
+    return GPT_OK;
+  }
+  if (n != m->depth) return GPT_ESHAPE;
+  for (int i = 0; i < n; ++i)
+    if (windows[i] < -1) return GPT_EINVAL;
+  m->windows.assign(windows, windows + n);
+  return GPT_OK;
+}
+
+gpt_status gpt_get_attention_windows(const gpt_model* m, int32_t* windows, int32_t n) {
+  if (!m || !windows) return GPT_EINVAL;
+  if (n != m->depth) return GPT_ESHAPE;
+  for (int i = 0; i < n; ++i) windows[i] = m->windows[i];
   return GPT_OK;
 }
 

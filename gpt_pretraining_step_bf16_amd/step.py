@@ -13,6 +13,20 @@ import numpy as np
 from . import binding
 
 
+def window_pattern(depth: int, seq: int, pattern: str = "SSSL", short_window=None):
+    """Per-layer attention windows from a short/long pattern string.
+
+    Layer l takes pattern[l % len(pattern)]: "L" is the full causal context
+    (-1), "S" a window of short_window keys to the left of each query
+    (default seq // 2).
+    """
+    pattern = pattern.upper()
+    if not pattern or set(pattern) - {"S", "L"}:
+        raise ValueError(f"window pattern must be made of S and L: {pattern!r}")
+    short = seq // 2 if short_window is None else int(short_window)
+    return [short if pattern[l % len(pattern)] == "S" else -1 for l in range(depth)]
+
+
 class TrainState:
     def __init__(self, depth: int, vocab: int, seq: int, batch: int, device="cuda"):
         import torch
@@ -64,6 +78,10 @@ class TrainState:
         return self.unflatten(t.detach().cpu().numpy())
 
     # -- compute --------------------------------------------------------------
+    def set_windows(self, windows):
+        """Per-layer attention windows for later fwd_bwd calls (None: all causal)."""
+        self.model.set_windows(windows)
+
     def fwd_bwd(self, tokens, targets, accumulate=False):
         self.model.fwd_bwd(self.params_bf16, tokens, targets, self.loss, self.grads, self.ws,
                            accumulate=accumulate)

@@ -76,6 +76,20 @@ void gpt_destroy(gpt_model* m);
 /* dims[6] <- {depth, width, heads, mlp_hidden, vocab, max_seq}. */
 gpt_status gpt_dims(const gpt_model* m, int32_t dims[6]);
 
+/*
+ * Attention window of every layer ([CT50] "1. Modelo GPT" lists window
+ * attention that alternates short and long context, e.g. "SSSL", and
+ * "5. Flash Attention Unificado" passes a window_size to the attention call;
+ * the page gives no sizes). windows is a HOST array of n == depth entries:
+ * layer l's queries i see keys i - windows[l] .. i; -1 is the full causal
+ * context (the default after gpt_create). NULL resets every layer to -1.
+ * Returns GPT_ESHAPE if n != depth, GPT_EINVAL for an entry below -1.
+ * Later gpt_fwd_bwd calls on this model use the windows.
+ */
+gpt_status gpt_set_attention_windows(gpt_model* m, const int32_t* windows, int32_t n);
+/* windows[0 .. n-1] <- the model's windows (n == depth). */
+gpt_status gpt_get_attention_windows(const gpt_model* m, int32_t* windows, int32_t n);
+
 /* Total element count of the flat parameter layout (also of grads / momentum). */
 int64_t gpt_num_params(const gpt_model* m);
 int32_t gpt_num_tensors(const gpt_model* m);
@@ -234,16 +248,17 @@ gpt_status gpt_op_gemm(int32_t M, int32_t N, int32_t K, int32_t batch, const uin
 /* Causal attention forward over qkv [batch*seq, 3*heads*128] bf16 (q | k | v
  * column blocks, 128 columns per head). Writes o [batch*seq, heads*128] bf16
  * and lse [batch, heads, seq] fp32: the base-2 logarithm of the softmax
- * normaliser sum_j 2^(s_ij), where s_ij = (q_i . k_j) * log2(e) / sqrt(128). */
+ * normaliser sum_j 2^(s_ij), where s_ij = (q_i . k_j) * log2(e) / sqrt(128).
+ * window: -1 for the causal mask, else W >= 0: query i sees keys i - W .. i. */
 gpt_status gpt_op_attention_fwd(const uint16_t* qkv, uint16_t* o, float* lse, int32_t batch,
-                                int32_t seq, int32_t heads, void* stream);
+                                int32_t seq, int32_t heads, int32_t window, void* stream);
 
-/* Causal attention backward: from qkv, o, lse (as written by the forward) and
- * dO [batch*seq, heads*128] bf16, write dqkv [batch*seq, 3*heads*128] bf16.
- * scratch: device, >= batch*heads*seq floats. */
+/* Causal attention backward: from qkv, o, lse (as written by the forward with
+ * the same window) and dO [batch*seq, heads*128] bf16, write dqkv
+ * [batch*seq, 3*heads*128] bf16. scratch: device, >= batch*heads*seq floats. */
 gpt_status gpt_op_attention_bwd(const uint16_t* qkv, const uint16_t* o, const float* lse,
                                 const uint16_t* dO, uint16_t* dqkv, float* scratch,
-                                int32_t batch, int32_t seq, int32_t heads, void* stream);
+                                int32_t batch, int32_t seq, int32_t heads, int32_t window, void* stream);
 
 /* Newton-Schulz on `count` fp32 matrices X [count, rows, cols] (rows >= cols)
  * in place: X0 = X / (||X||_F + 1e-7), then ns_steps iterations with the

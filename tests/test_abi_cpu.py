@@ -156,3 +156,26 @@ def test_normuon_state_and_host_validation_precede_any_launch():
     assert call(b2=float("nan")) == binding.GPT_EINVAL
     assert call(steps=0) == binding.GPT_EINVAL
     assert call(wsb=need - 1) == binding.GPT_EWORKSPACE
+
+
+def test_attention_windows_are_host_state_with_validation():
+    from gpt_pretraining_step_bf16_amd.step import window_pattern
+
+    m = binding.GptModel(6, 2048, 256)
+    assert m.windows() == [-1] * 6
+    pat = window_pattern(6, 256, "SSSL")
+    assert pat == [128, 128, 128, -1, 128, 128]
+    m.set_windows(pat)
+    assert m.windows() == pat
+    lib = binding.lib()
+    bad = (C.c_int32 * 6)(1, 2, 3, -2, 5, 6)
+    assert lib.gpt_set_attention_windows(m.handle, bad, 6) == binding.GPT_EINVAL
+    short = (C.c_int32 * 5)(1, 2, 3, 4, 5)
+    assert lib.gpt_set_attention_windows(m.handle, short, 5) == binding.GPT_ESHAPE
+    assert m.windows() == pat  # a rejected call changes nothing
+    m.set_windows(None)
+    assert m.windows() == [-1] * 6
+    with pytest.raises(ValueError):
+        window_pattern(4, 64, "SXL")
+    fake = C.c_void_p(4096)
+    assert lib.gpt_op_attention_fwd(fake, fake, fake, 1, 64, 1, -2, None) == binding.GPT_EINVAL

@@ -7,7 +7,8 @@ Weights are the seeded N(0, 0.02) draws, tokens seeded Zipf(1.1).
 
 For each depth:
 * One sequence through the whole model against the fp64 oracle, which is
-  given the bf16 weights gpt_fwd_bwd computes with: loss |delta| <= 1e-2,
+  given the bf16 weights gpt_fwd_bwd computes with (at d12 and d20 also with
+  the "SSSL" window pattern, short window seq / 2): loss |delta| <= 1e-2,
   every gradient tensor rel-L2 <= 2e-2, embedding rows of absent tokens exactly
   zero. The sequence is the workload's full length except at d32, where it is
   1024 tokens: the fp64 oracle of a 32-layer model at 4096 tokens needs about
@@ -39,7 +40,7 @@ pytestmark = pytest.mark.gpu
 
 import oracle  # noqa: E402
 from gpt_pretraining_step_bf16_amd import synthetic as syn  # noqa: E402
-from gpt_pretraining_step_bf16_amd.step import TrainState  # noqa: E402
+from gpt_pretraining_step_bf16_amd.step import TrainState, window_pattern  # noqa: E402
 
 LOSS_TOL = 1e-2
 REL_TOL = 2e-2
@@ -61,15 +62,18 @@ def _cuda(a):
 # The fp64 oracle needs from a few seconds (d12) to about a minute (d26) of
 # host time for one sequence.
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ["d12", "d20", "d26", "d32"])
-def test_one_sequence_matches_oracle(name):
+@pytest.mark.parametrize("name,pattern", [("d12", None), ("d20", None), ("d26", None), ("d32", None),
+                                          ("d12", "SSSL"), ("d20", "SSSL")])
+def test_one_sequence_matches_oracle(name, pattern):
     L, V, _, _ = _cfg(name)
     T = ORACLE_SEQ[name]
-    log(f"{name} one sequence of {T} vs oracle")
+    windows = None if pattern is None else window_pattern(L, T, pattern)
+    log(f"{name} one sequence of {T} vs oracle" + (f", windows {pattern} (short {T // 2})" if pattern else ""))
     w = syn.init_weights(L, V, seed=0)
     tok, tgt = syn.split_tokens(syn.zipf_ids(1, T, V, seed=1))
     st = TrainState(L, V, T, 1)
     st.load_weights(w)
+    st.set_windows(windows)
     st.fwd_bwd(_cuda(tok), _cuda(tgt))
     torch.cuda.synchronize()
     assert st.check() == 0
@@ -79,7 +83,8 @@ def test_one_sequence_matches_oracle(name):
     torch.cuda.empty_cache()
     w64 = {k: bf16_round(v).astype(np.float64) for k, v in w.items()}
     del w
-    ref_loss, ref_grads = oracle.forward_backward(w64, tok, tgt)
+    ref_loss, ref_grads = oracle.forward_backward(
+        w64, tok, tgt, windows=None if windows is None else [None if x < 0 else x for x in windows])
     del w64
     errs = sorted(((rel_l2(grads[k], ref_grads[k]), k) for k in ref_grads), reverse=True)
     log(f"  loss {loss:.6f} oracle {ref_loss:.6f}; worst grad rel-L2 "

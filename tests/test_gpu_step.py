@@ -23,8 +23,8 @@ LOSS_TOL = 1e-2
 REL_TOL = 2e-2
 
 
-def _run_case(depth, vocab, seq, batch, seed_w=0, seed_t=1, ignore=()):
-    log(f"fwd_bwd depth={depth} vocab={vocab} seq={seq} batch={batch}")
+def _run_case(depth, vocab, seq, batch, seed_w=0, seed_t=1, ignore=(), windows=None):
+    log(f"fwd_bwd depth={depth} vocab={vocab} seq={seq} batch={batch} windows={windows}")
     w = syn.init_weights(depth, vocab, seed=seed_w)
     ids = syn.zipf_ids(batch, seq, vocab, seed=seed_t)
     tok, tgt = syn.split_tokens(ids)
@@ -33,6 +33,7 @@ def _run_case(depth, vocab, seq, batch, seed_w=0, seed_t=1, ignore=()):
         tgt[b, t] = -1
     st = TrainState(depth, vocab, seq, batch)
     st.load_weights(w)
+    st.set_windows(windows)
     tok_d = torch.from_numpy(tok).cuda()
     tgt_d = torch.from_numpy(tgt).cuda()
     st.fwd_bwd(tok_d, tgt_d)
@@ -42,7 +43,8 @@ def _run_case(depth, vocab, seq, batch, seed_w=0, seed_t=1, ignore=()):
     grads = st.to_host(st.grads)
     # The oracle gets the inputs gpt_fwd_bwd gets: the bf16 weights.
     w64 = {k: bf16_round(v).astype(np.float64) for k, v in w.items()}
-    ref_loss, ref_grads = oracle.forward_backward(w64, tok, tgt)
+    ref_loss, ref_grads = oracle.forward_backward(
+        w64, tok, tgt, windows=None if windows is None else [None if x < 0 else x for x in windows])
     return st, tok, tgt, loss, grads, ref_loss, ref_grads
 
 
@@ -67,6 +69,27 @@ def test_tiny_fwd_bwd_matches_oracle():
     log(f"  loss gpu={loss:.6f} oracle={ref_loss:.6f}")
     assert abs(loss - ref_loss) <= LOSS_TOL
     _assert_grads(grads, ref_grads, tok, cfg["vocab"])
+
+
+@pytest.mark.parametrize("windows", [[0, 20], [63, -1], [7, 1]])
+def test_windowed_fwd_bwd_matches_oracle(windows):
+    """Per-layer attention windows: the degenerate window 0 (each token sees
+    only itself), one that covers the sequence, and short ones that cut every
+    key tile."""
+    cfg = syn.CONFIGS["tiny"]
+    st, tok, tgt, loss, grads, ref_loss, ref_grads = _run_case(
+        cfg["depth"], cfg["vocab"], cfg["seq"], cfg["batch"], windows=windows)
+    assert st.model.windows() == windows
+    assert abs(loss - ref_loss) <= LOSS_TOL
+    _assert_grads(grads, ref_grads, tok, cfg["vocab"])
+
+
+def test_ragged_windowed_fwd_bwd():
+    # seq 200 with windows that end inside key tiles, plus one causal layer.
+    st, tok, tgt, loss, grads, ref_loss, ref_grads = _run_case(3, 2048, 200, 3, seed_w=5, seed_t=6,
+                                                                windows=[50, -1, 130])
+    assert abs(loss - ref_loss) <= LOSS_TOL
+    _assert_grads(grads, ref_grads, tok, 2048)
 
 
 def test_ragged_fwd_bwd_with_ignored_targets():
