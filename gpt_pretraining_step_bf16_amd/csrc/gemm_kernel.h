@@ -503,6 +503,173 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& p, const f32x16 (
   }
 }
 
+// The same staging for the epilogues that read an operand: the fp32 residual
+// add (read-modify-write of fp32 C) and the ReLU^2 backward (reads bf16 D). Per 32-row block: the block's inputs (old C, or D) are read
+// row-contiguous into the wave's LDS region; each lane combines its
+// accumulators with the inputs at its own positions, in place; the results
+// leave row-contiguous (256-byte fp32 or 128-byte bf16 row segments). The
+// next block's inputs are loaded while the current block is processed.
+// Global accesses go through buffer instructions on the wave's tile base:
+// one per-lane 32-bit offset for the whole epilogue, the row-group offset
+// in a scalar register. fp32 rows are padded to 272 bytes in LDS.
+template <int E>
+constexpr bool lds_epi_io() {
+  // (Plain fp32 outputs and split-K partials measured no faster staged: their
+  // GEMMs have long K, and the register path already writes 16 bytes a lane.)
+  return E == EPI_F32_ACC || E == EPI_DRELU2_BF16;
+}
+constexpr int STG_RS_F = 272;  // padded row stride of an fp32 staging block (bytes)
+static_assert(8 * 32 * STG_RS_F <= NST * STAGE_BYTES, "staging regions must fit in the ring");
+
+// Orders this wave's LDS accesses as written: lanes read what other lanes of
+// the wave wrote, which the compiler cannot see.
+__device__ __forceinline__ void wave_lds_order() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Raw buffer resource over a wave-uniform base (range 2 GiB; gfx9 dword 3).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0,
+                                           0x7fffffff, 0x00020000);
+}
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+template <int E, bool FULL>
+__device__ __forceinline__ void store_tile_lds_io(const GemmArgs& p, const f32x16 (&acc)[4][2], int bi,
+                                                  int m0, int n0, int row_off, int col_off, int lane, int wave,
+                                                  char* smem) {
+  const int rows_left = p.M - (m0 + row_off), cols_left = p.N - (n0 + col_off);
+  char* wreg = smem + wave * (32 * STG_RS_F);
+  const int r = lane & 31, hl = lane >> 5;
+  const int ldc = (int)p.ldc;
+  const long cbase = (long)bi * p.sc + (long)(m0 + row_off) * p.ldc + (n0 + col_off);
+  if constexpr (E == EPI_DRELU2_BF16) {
+    // bf16 rows: 8 lanes per 128-byte segment, 8 rows per instruction.
+    constexpr int RS = STG_RS;
+    const int ldd = (int)p.ldd;
+    const auto drs =
+        wave_rsrc(reinterpret_cast<const uint16_t*>(p.d) + (long)bi * p.sd + (long)(m0 + row_off) * p.ldd + (n0 + col_off));
+    const auto crs = wave_rsrc(reinterpret_cast<uint16_t*>(p.c) + cbase);
+    const int rq = lane >> 3, cc = lane & 7;
+    const int dvo = (rq * ldd + cc * 8) * 2, cvo = (rq * ldc + cc * 8) * 2;
+    u32x4_t din[4];
+    auto load_d = [&](int i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = 32 * i + 8 * q + rq;
+        const int so = (32 * i + 8 * q) * ldd * 2;
+        if (FULL || (row < rows_left && cc * 8 + 8 <= cols_left)) {
+          din[q] = __builtin_amdgcn_raw_buffer_load_b128(drs, dvo, so, 0);
+        } else if (row < rows_left && cc * 8 + 4 <= cols_left) {
+          const u32x2_t u = __builtin_amdgcn_raw_buffer_load_b64(drs, dvo, so, 0);
+          din[q] = u32x4_t{u.x, u.y, 0u, 0u};
+        } else {
+          din[q] = u32x4_t{0u, 0u, 0u, 0u};
+        }
+      }
+    };
+    load_d(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4_t*>(wreg + (8 * q + rq) * RS + cc * 16) = din[q];
+      if (i + 1 < 4) load_d(i + 1);
+      wave_lds_order();
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          char* a = wreg + r * RS + (32 * j + 8 * g + 4 * hl) * 2;
+          const uint2 h = *reinterpret_cast<const uint2*>(a);
+          // d relu(u)^2 / du = 2 relu(u) = 2 sqrt(h), h = relu(u)^2 as stored.
+          const f32x16& v = acc[i][j];
+          *reinterpret_cast<uint2*>(a) =
+              make_uint2(pack_bf2(2.f * v[4 * g] * __builtin_amdgcn_sqrtf(bf_lo(h.x)),
+                                  2.f * v[4 * g + 1] * __builtin_amdgcn_sqrtf(bf_hi(h.x))),
+                         pack_bf2(2.f * v[4 * g + 2] * __builtin_amdgcn_sqrtf(bf_lo(h.y)),
+                                  2.f * v[4 * g + 3] * __builtin_amdgcn_sqrtf(bf_hi(h.y))));
+        }
+      wave_lds_order();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = 32 * i + 8 * q + rq;
+        const int so = (32 * i + 8 * q) * ldc * 2;
+        const u32x4_t val = *reinterpret_cast<const u32x4_t*>(wreg + (8 * q + rq) * RS + cc * 16);
+        if (FULL || (row < rows_left && cc * 8 + 8 <= cols_left)) {
+          __builtin_amdgcn_raw_buffer_store_b128(val, crs, cvo, so, 0);
+        } else if (row < rows_left && cc * 8 + 4 <= cols_left) {
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{val.x, val.y}, crs, cvo, so, 0);
+        }
+      }
+      wave_lds_order();
+    }
+  } else {
+    // fp32 rows: 16 lanes per 256-byte segment, 4 rows per instruction.
+    constexpr int RS = STG_RS_F;
+    const auto crs = wave_rsrc(reinterpret_cast<float*>(p.c) + cbase);
+    const float alpha = p.alpha;
+    const float beta = p.beta;
+    const bool reads = (E == EPI_F32_ACC) && beta != 0.f;
+    const int rq = lane >> 4, cc = lane & 15;
+    const int cvo = (rq * ldc + cc * 4) * 4;
+    auto ok = [&](int row) { return FULL || (row < rows_left && cc * 4 < cols_left); };
+    u32x4_t cin[8];
+    auto load_c = [&](int i) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int row = 32 * i + 4 * q + rq;
+        cin[q] = ok(row) ? __builtin_amdgcn_raw_buffer_load_b128(crs, cvo, (32 * i + 4 * q) * ldc * 4, 0)
+                         : u32x4_t{0u, 0u, 0u, 0u};
+      }
+    };
+    if constexpr (E == EPI_F32_ACC) {
+      if (reads) load_c(0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (E == EPI_F32_ACC) {
+        if (reads) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) *reinterpret_cast<u32x4_t*>(wreg + (4 * q + rq) * RS + cc * 16) = cin[q];
+          if (i + 1 < 4) load_c(i + 1);
+        }
+      }
+      wave_lds_order();
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float* a = reinterpret_cast<float*>(wreg + r * RS + (32 * j + 8 * g + 4 * hl) * 4);
+          const f32x16& v = acc[i][j];
+          float4 o = make_float4(alpha * v[4 * g], alpha * v[4 * g + 1], alpha * v[4 * g + 2], alpha * v[4 * g + 3]);
+          if constexpr (E == EPI_F32_ACC) {
+            if (reads) {
+              const float4 c = *reinterpret_cast<const float4*>(a);
+              o = make_float4(beta * c.x + o.x, beta * c.y + o.y, beta * c.z + o.z, beta * c.w + o.w);
+            }
+          }
+          *reinterpret_cast<float4*>(a) = o;
+        }
+      wave_lds_order();
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int row = 32 * i + 4 * q + rq;
+        const u32x4_t val = *reinterpret_cast<const u32x4_t*>(wreg + (4 * q + rq) * RS + cc * 16);
+        if (ok(row)) __builtin_amdgcn_raw_buffer_store_b128(val, crs, cvo, (32 * i + 4 * q) * ldc * 4, 0);
+      }
+      wave_lds_order();
+    }
+  }
+}
+
 template <bool AK, bool BK_, int SQ, int EPI>
 __global__ void __launch_bounds__(NTHR, 1) gemm_bf16_kernel(const GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE_BYTES];
@@ -904,6 +1071,11 @@ __global__ void __launch_bounds__(PP_THR, 1) gemm_pp_kernel(const GemmArgs p) {
         store_tile_lds<EPI, true>(p, acc, bi, m0, n0, 128 * grp, 64 * w4, lane, wave, smem);
       else
         store_tile_lds<EPI, false>(p, acc, bi, m0, n0, 128 * grp, 64 * w4, lane, wave, smem);
+    } else if constexpr (lds_epi_io<EPI>()) {
+      if (interior)
+        store_tile_lds_io<EPI, true>(p, acc, bi, m0, n0, 128 * grp, 64 * w4, lane, wave, smem);
+      else
+        store_tile_lds_io<EPI, false>(p, acc, bi, m0, n0, 128 * grp, 64 * w4, lane, wave, smem);
     } else {
       store_tile<EPI, 2>(p, acc, bi, si, m0, n0, 128 * grp, 64 * w4, lane);
     }
