@@ -504,7 +504,8 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& p, const f32x16 (
 }
 
 // The same staging for the epilogues that read an operand: the fp32 residual
-// add (read-modify-write of fp32 C) and the ReLU^2 backward (reads bf16 D). Per 32-row block: the block's inputs (old C, or D) are read
+// add (read-modify-write of fp32 C), the ReLU^2 backward (reads bf16 D) and
+// the Newton-Schulz update (reads fp32 X, writes fp32 X and its bf16 hi/lo). Per 32-row block: the block's inputs (old C, or D) are read
 // row-contiguous into the wave's LDS region; each lane combines its
 // accumulators with the inputs at its own positions, in place; the results
 // leave row-contiguous (256-byte fp32 or 128-byte bf16 row segments). The
@@ -516,7 +517,7 @@ template <int E>
 constexpr bool lds_epi_io() {
   // (Plain fp32 outputs and split-K partials measured no faster staged: their
   // GEMMs have long K, and the register path already writes 16 bytes a lane.)
-  return E == EPI_F32_ACC || E == EPI_DRELU2_BF16;
+  return E == EPI_F32_ACC || E == EPI_DRELU2_BF16 || E == EPI_NS_UPDATE;
 }
 constexpr int STG_RS_F = 272;  // padded row stride of an fp32 staging block (bytes)
 static_assert(8 * 32 * STG_RS_F <= NST * STAGE_BYTES, "staging regions must fit in the ring");
@@ -606,6 +607,66 @@ __device__ __forceinline__ void store_tile_lds_io(const GemmArgs& p, const f32x1
           __builtin_amdgcn_raw_buffer_store_b128(val, crs, cvo, so, 0);
         } else if (row < rows_left && cc * 8 + 4 <= cols_left) {
           __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{val.x, val.y}, crs, cvo, so, 0);
+        }
+      }
+      wave_lds_order();
+    }
+  } else if constexpr (E == EPI_NS_UPDATE) {
+    // v = alpha acc + beta D; fp32 v to C3 (stride ldd), bf16 hi/lo of v to C
+    // and C2 (stride ldc). fp32 rows: 16 lanes per 256-byte segment.
+    constexpr int RS = STG_RS_F;
+    const int ldd = (int)p.ldd;
+    const long dbase = (long)bi * p.sd + (long)(m0 + row_off) * p.ldd + (n0 + col_off);
+    const auto drs = wave_rsrc(reinterpret_cast<const float*>(p.d) + dbase);
+    const auto x3 = wave_rsrc(reinterpret_cast<float*>(p.c3) + dbase);
+    const auto hrs = wave_rsrc(reinterpret_cast<uint16_t*>(p.c) + cbase);
+    const auto lrs = wave_rsrc(reinterpret_cast<uint16_t*>(p.c2) + cbase);
+    const float alpha = p.alpha, beta = p.beta;
+    const int rq = lane >> 4, cc = lane & 15;
+    const int dvo = (rq * ldd + cc * 4) * 4, hvo = (rq * ldc + cc * 4) * 2;
+    auto ok = [&](int row) { return FULL || (row < rows_left && cc * 4 < cols_left); };
+    u32x4_t din[8];
+    auto load_d = [&](int i) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int row = 32 * i + 4 * q + rq;
+        din[q] = ok(row) ? __builtin_amdgcn_raw_buffer_load_b128(drs, dvo, (32 * i + 4 * q) * ldd * 4, 0)
+                         : u32x4_t{0u, 0u, 0u, 0u};
+      }
+    };
+    load_d(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) *reinterpret_cast<u32x4_t*>(wreg + (4 * q + rq) * RS + cc * 16) = din[q];
+      if (i + 1 < 4) load_d(i + 1);
+      wave_lds_order();
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float* a = reinterpret_cast<float*>(wreg + r * RS + (32 * j + 8 * g + 4 * hl) * 4);
+          const f32x16& v = acc[i][j];
+          const float4 x = *reinterpret_cast<const float4*>(a);
+          *reinterpret_cast<float4*>(a) =
+              make_float4(alpha * v[4 * g] + beta * x.x, alpha * v[4 * g + 1] + beta * x.y,
+                          alpha * v[4 * g + 2] + beta * x.z, alpha * v[4 * g + 3] + beta * x.w);
+        }
+      wave_lds_order();
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int row = 32 * i + 4 * q + rq;
+        const float4 w = *reinterpret_cast<const float4*>(wreg + (4 * q + rq) * RS + cc * 16);
+        if (ok(row)) {
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, w), x3, dvo,
+                                                 (32 * i + 4 * q) * ldd * 4, 0);
+          const uint32_t h0 = f2bf(w.x), h1 = f2bf(w.y), h2 = f2bf(w.z), h3 = f2bf(w.w);
+          const uint32_t l0 = f2bf(w.x - bf2f(h0)), l1 = f2bf(w.y - bf2f(h1)), l2 = f2bf(w.z - bf2f(h2)),
+                         l3 = f2bf(w.w - bf2f(h3));
+          const int so = (32 * i + 4 * q) * ldc * 2;
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{h0 | (h1 << 16), h2 | (h3 << 16)}, hrs, hvo, so, 0);
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{l0 | (l1 << 16), l2 | (l3 << 16)}, lrs, hvo, so, 0);
         }
       }
       wave_lds_order();
@@ -1071,13 +1132,18 @@ __global__ void __launch_bounds__(PP_THR, 1) gemm_pp_kernel(const GemmArgs p) {
         store_tile_lds<EPI, true>(p, acc, bi, m0, n0, 128 * grp, 64 * w4, lane, wave, smem);
       else
         store_tile_lds<EPI, false>(p, acc, bi, m0, n0, 128 * grp, 64 * w4, lane, wave, smem);
-    } else if constexpr (lds_epi_io<EPI>()) {
-      if (interior)
-        store_tile_lds_io<EPI, true>(p, acc, bi, m0, n0, 128 * grp, 64 * w4, lane, wave, smem);
-      else
-        store_tile_lds_io<EPI, false>(p, acc, bi, m0, n0, 128 * grp, 64 * w4, lane, wave, smem);
     } else {
-      store_tile<EPI, 2>(p, acc, bi, si, m0, n0, 128 * grp, 64 * w4, lane);
+      // Edge tiles of the read-modify-write epilogues keep the register path:
+      // the staged version's edge variant gave wrong Newton-Schulz updates on
+      // a 384 x 128 batch (cause not found), while interior tiles agree.
+      bool staged = false;
+      if constexpr (lds_epi_io<EPI>()) {
+        if (interior) {
+          store_tile_lds_io<EPI, true>(p, acc, bi, m0, n0, 128 * grp, 64 * w4, lane, wave, smem);
+          staged = true;
+        }
+      }
+      if (!staged) store_tile<EPI, 2>(p, acc, bi, si, m0, n0, 128 * grp, 64 * w4, lane);
     }
     const int lin_next = lin + gridDim.x;
     if (lin_next >= total) break;
