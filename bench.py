@@ -163,6 +163,9 @@ def main():
     ap.add_argument("--normuon", action="store_true",
                     help="NorMuon variance reduction after Newton-Schulz (normuon_step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-isolated-timings", action="store_true",
+                    help="skip the separate AdamW / Muon timings after the timed steps (keeps a "
+                         "kernel trace to whole steps)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="launch one plain device copy of this many MiB before the steps "
                          "(the calibration kernel for rocprofv3 FETCH_SIZE/WRITE_SIZE counters)")
@@ -250,24 +253,26 @@ def main():
     f_tok = flops_per_token(L, d, V, T, windows)
     mfu = tokens_per_s * f_tok / PEAK_BF16_FLOPS
     mfma_work = (tokens_per_s * f_tok + ns_flops(L, d) / (ms_step / 1e3)) / PEAK_BF16_FLOPS
-    # The AdamW call alone, timed after the steps (HIP events on the current stream).
-    a0 = torch.cuda.Event(enable_timing=True)
-    a1 = torch.cuda.Event(enable_timing=True)
-    a0.record()
-    for _ in range(5):
-        opt_step[0] += 1
-        st.adamw(ADAMW["lr"], ADAMW["beta1"], ADAMW["beta2"], ADAMW["eps"], ADAMW["weight_decay"],
-                 opt_step[0])
-    a1.record()
-    torch.cuda.synchronize()
-    adamw_ms = a0.elapsed_time(a1) / 5
-    # The block-matrix update alone (muon_step or normuon_step), timed the same way.
-    a0.record()
-    for _ in range(3):
-        block_update()
-    a1.record()
-    torch.cuda.synchronize()
-    block_ms = a0.elapsed_time(a1) / 3
+    adamw_ms = block_ms = None
+    if not args.no_isolated_timings:
+        # The AdamW call alone, timed after the steps (HIP events on the current stream).
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for _ in range(5):
+            opt_step[0] += 1
+            st.adamw(ADAMW["lr"], ADAMW["beta1"], ADAMW["beta2"], ADAMW["eps"], ADAMW["weight_decay"],
+                     opt_step[0])
+        a1.record()
+        torch.cuda.synchronize()
+        adamw_ms = a0.elapsed_time(a1) / 5
+        # The block-matrix update alone (muon_step or normuon_step), timed the same way.
+        a0.record()
+        for _ in range(3):
+            block_update()
+        a1.record()
+        torch.cuda.synchronize()
+        block_ms = a0.elapsed_time(a1) / 3
     for name, (ms, fl, n) in prof.items():
         tf = fl / (ms / 1e3) / 1e12 if ms > 0 else 0.0
         print(f"[bench] {name:9s} {ms / args.steps:9.2f} ms/step  {n // max(args.steps, 1):5d} launches/step"
@@ -319,8 +324,8 @@ def main():
         "mfma_work_utilisation": round(mfma_work, 4),
         "loss": round(loss, 5),
         "wall_s_timed": round(wall, 3),
-        "adamw_ms": round(adamw_ms, 3),
-        ("normuon_ms" if args.normuon else "muon_ms"): round(block_ms, 3),
+        "adamw_ms": None if adamw_ms is None else round(adamw_ms, 3),
+        ("normuon_ms" if args.normuon else "muon_ms"): None if block_ms is None else round(block_ms, 3),
         "roofline": roofline,
         "cpu_baseline": None,
     }
