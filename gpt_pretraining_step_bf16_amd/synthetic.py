@@ -65,20 +65,23 @@ def model_dims(depth: int) -> dict:
     return dict(depth=depth, d=d, heads=d // HEAD_DIM, mlp=4 * d)
 
 
-def tensor_specs(depth: int, vocab: int):
+def tensor_specs(depth: int, vocab: int, kv_heads=None):
     """Canonical tensor order: wte; per layer wq, wk, wv, wo, wfc, wproj; lm_head.
 
     Each entry is (name, rows, cols, kind, layer) with kind in
     {"emb", "matrix", "lm_head"}; matrices are [out, in] as in a Linear layer.
+    kv_heads (default: every head) sets the rows of wk and wv to kv_heads * 128
+    (grouped-query attention).
     """
     dm = model_dims(depth)
     d, f = dm["d"], dm["mlp"]
+    dkv = d if kv_heads is None else HEAD_DIM * int(kv_heads)
     specs = [("wte", vocab, d, "emb", -1)]
     for layer in range(depth):
         specs += [
             (f"h{layer}.wq", d, d, "matrix", layer),
-            (f"h{layer}.wk", d, d, "matrix", layer),
-            (f"h{layer}.wv", d, d, "matrix", layer),
+            (f"h{layer}.wk", dkv, d, "matrix", layer),
+            (f"h{layer}.wv", dkv, d, "matrix", layer),
             (f"h{layer}.wo", d, d, "matrix", layer),
             (f"h{layer}.wfc", f, d, "matrix", layer),
             (f"h{layer}.wproj", d, f, "matrix", layer),
@@ -87,11 +90,11 @@ def tensor_specs(depth: int, vocab: int):
     return specs
 
 
-def init_weights(depth: int, vocab: int, seed: int = 0, std: float = INIT_STD) -> dict:
+def init_weights(depth: int, vocab: int, seed: int = 0, std: float = INIT_STD, kv_heads=None) -> dict:
     """Every tensor N(0, std^2), float32, drawn in canonical order from one seed."""
     rng = np.random.default_rng(seed)
     out = {}
-    for name, rows, cols, _kind, _layer in tensor_specs(depth, vocab):
+    for name, rows, cols, _kind, _layer in tensor_specs(depth, vocab, kv_heads):
         w = rng.standard_normal((rows, cols), dtype=np.float32)
         w *= np.float32(std)
         out[name] = w
@@ -120,11 +123,11 @@ def split_tokens(ids: np.ndarray):
     return np.ascontiguousarray(ids[:, :-1]), np.ascontiguousarray(ids[:, 1:])
 
 
-def random_like_grads(depth: int, vocab: int, seed: int, scale: float = 1e-3) -> dict:
+def random_like_grads(depth: int, vocab: int, seed: int, scale: float = 1e-3, kv_heads=None) -> dict:
     """Seeded Gaussian arrays shaped like the parameters (for optimizer-only cases)."""
     rng = np.random.default_rng(seed)
     out = {}
-    for name, rows, cols, _kind, _layer in tensor_specs(depth, vocab):
+    for name, rows, cols, _kind, _layer in tensor_specs(depth, vocab, kv_heads):
         g = rng.standard_normal((rows, cols), dtype=np.float32)
         g *= np.float32(scale)
         out[name] = g

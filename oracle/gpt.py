@@ -29,6 +29,10 @@ Window attention (optional, per layer): the pages list alternating short and
 long attention windows but give no sizes, so the windows are an input; a
 window W lets query i see keys i - W .. i.
 
+Grouped-query attention (optional): the pages list "fewer KV heads". When wk
+and wv have Hkv * 128 rows (Hkv dividing H), query head h attends with key and
+value head h // (H / Hkv); QK-norm and RoPE act per head as before.
+
 Parity pins (tests/test_oracle_model.py): central finite differences in fp64 on
 depth-1 and depth-2 models (one with a windowed layer); loss = ln V and a
 closed-form lm_head gradient for a zero unembedding; causal invariance;
@@ -84,8 +88,22 @@ def rope_bwd(dy, cos, sin):
     return np.concatenate([d1 * c + d2 * s, -d1 * s + d2 * c], axis=-1)
 
 
+def _repeat_kv(x, heads):
+    """Grouped-query attention ([CT50] "1. Modelo GPT": fewer key/value heads):
+    with Hkv key/value heads, query head h reads key/value head h // (H / Hkv)."""
+    hkv = x.shape[1]
+    return x if hkv == heads else np.repeat(x, heads // hkv, axis=1)
+
+
+def _sum_kv_groups(dx, hkv):
+    """Adjoint of _repeat_kv: sum the gradients of each group of query heads."""
+    T, H, hd = dx.shape
+    return dx if hkv == H else dx.reshape(T, hkv, H // hkv, hd).sum(axis=2)
+
+
 def causal_attention(q, k, v, window=None):
-    """Softmax attention with mask j <= i; q, k, v are [T, H, hd].
+    """Softmax attention with mask j <= i; q is [T, H, hd], k and v [T, Hkv, hd]
+    with Hkv dividing H (grouped-query attention when Hkv < H).
 
     With a window W (an int >= 0) key j is visible to query i only when
     i - W <= j <= i as well ([CT50] "1. Modelo GPT" lists short/long window
@@ -94,7 +112,8 @@ def causal_attention(q, k, v, window=None):
     None is the plain causal mask.
     Returns o [T, H, hd] and the probabilities P [H, T, T].
     """
-    T, _H, hd = q.shape
+    T, H, hd = q.shape
+    k, v = _repeat_kv(k, H), _repeat_kv(v, H)
     scale = 1.0 / np.sqrt(hd)
     qh, kh, vh = (a.transpose(1, 0, 2) for a in (q, k, v))  # [H, T, hd]
     s = np.matmul(qh, kh.transpose(0, 2, 1)) * scale
@@ -110,8 +129,11 @@ def causal_attention(q, k, v, window=None):
 
 
 def causal_attention_bwd(do, q, k, v, p):
-    """Adjoint of causal_attention given the saved probabilities p."""
+    """Adjoint of causal_attention given the saved probabilities p; dk and dv
+    have k's and v's head count."""
     hd = q.shape[-1]
+    hkv = k.shape[1]
+    k, v = _repeat_kv(k, q.shape[1]), _repeat_kv(v, q.shape[1])
     scale = 1.0 / np.sqrt(hd)
     qh, kh, vh, doh = (a.transpose(1, 0, 2) for a in (q, k, v, do))
     dp = np.matmul(doh, vh.transpose(0, 2, 1))
@@ -119,7 +141,8 @@ def causal_attention_bwd(do, q, k, v, p):
     ds = p * (dp - np.sum(dp * p, axis=-1, keepdims=True))
     dq = np.matmul(ds, kh) * scale
     dk = np.matmul(ds.transpose(0, 2, 1), qh) * scale
-    return dq.transpose(1, 0, 2), dk.transpose(1, 0, 2), dv.transpose(1, 0, 2)
+    return (dq.transpose(1, 0, 2), _sum_kv_groups(dk.transpose(1, 0, 2), hkv),
+            _sum_kv_groups(dv.transpose(1, 0, 2), hkv))
 
 
 def log_softmax_rows(z):
@@ -159,8 +182,8 @@ def _forward_sequence(weights, tok, cos, sin, final_norm=True, windows=None):
         w = {n: weights[f"h{layer}.{n}"] for n in ("wq", "wk", "wv", "wo", "wfc", "wproj")}
         xn1, r1 = rms_norm(x)
         q = (xn1 @ w["wq"].T).reshape(T, H, HEAD_DIM)
-        k = (xn1 @ w["wk"].T).reshape(T, H, HEAD_DIM)
-        v = (xn1 @ w["wv"].T).reshape(T, H, HEAD_DIM)
+        k = (xn1 @ w["wk"].T).reshape(T, -1, HEAD_DIM)
+        v = (xn1 @ w["wv"].T).reshape(T, -1, HEAD_DIM)
         qn, rq = rms_norm(q)
         kn, rk = rms_norm(k)
         qr, kr = rope(qn, cos, sin), rope(kn, cos, sin)
@@ -256,8 +279,8 @@ def forward_backward(weights, tokens, targets, final_norm=True, want_grads=True,
             do = (dx_mid @ w["wo"]).reshape(T, H, HEAD_DIM)
             dqr, dkr, dv = causal_attention_bwd(do, s["qr"], s["kr"], s["v"], s["p"])
             dq = rms_norm_bwd(rope_bwd(dqr, cos, sin), s["qn"], s["rq"]).reshape(T, d)
-            dk = rms_norm_bwd(rope_bwd(dkr, cos, sin), s["kn"], s["rk"]).reshape(T, d)
-            dv = dv.reshape(T, d)
+            dk = rms_norm_bwd(rope_bwd(dkr, cos, sin), s["kn"], s["rk"]).reshape(T, -1)
+            dv = dv.reshape(T, -1)
             grads[g["wq"]] += dq.T @ s["xn1"]
             grads[g["wk"]] += dk.T @ s["xn1"]
             grads[g["wv"]] += dv.T @ s["xn1"]

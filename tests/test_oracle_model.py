@@ -16,8 +16,8 @@ from gpt_pretraining_step_bf16_amd import synthetic as syn
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
 
 
-def _tiny_weights(depth, vocab, seed, std):
-    w = syn.init_weights(depth, vocab, seed=seed, std=std)
+def _tiny_weights(depth, vocab, seed, std, kv_heads=None):
+    w = syn.init_weights(depth, vocab, seed=seed, std=std, kv_heads=kv_heads)
     return {k: v.astype(np.float64) for k, v in w.items()}
 
 
@@ -28,10 +28,11 @@ def _ids(batch, seq, vocab, seed):
 # ----------------------------------------------------------------------------
 # Whole-model gradient: central finite differences in fp64
 # ----------------------------------------------------------------------------
-@pytest.mark.parametrize("depth,windows", [(1, None), (2, None), (2, [3, None])])
-def test_gradients_match_central_differences(depth, windows):
+@pytest.mark.parametrize("depth,windows,kv_heads", [(1, None, None), (2, None, None), (2, [3, None], None),
+                                                    (4, [None, 5, None, None], 1)])
+def test_gradients_match_central_differences(depth, windows, kv_heads):
     vocab, seq, batch = 96, 12, 2
-    w = _tiny_weights(depth, vocab, seed=3, std=0.15)
+    w = _tiny_weights(depth, vocab, seed=3, std=0.15, kv_heads=kv_heads)
     tok, tgt = _ids(batch, seq, vocab, seed=5)
     tgt = tgt.copy()
     tgt[0, 3] = -1  # one ignored target exercises the valid-count normalisation
@@ -231,6 +232,50 @@ def test_windowed_model_matches_full_model_until_the_window_binds():
     z_win = oracle.forward_logits(w, tok, windows=[W, None])
     np.testing.assert_allclose(z_win[0, : W + 1], z_full[0, : W + 1], rtol=0, atol=1e-13)
     assert np.abs(z_win[0, W + 1:] - z_full[0, W + 1:]).max() > 1e-6
+
+
+# ----------------------------------------------------------------------------
+# Grouped-query attention: equal to full multi-head attention whose key/value
+# weights repeat each group's rows (an independent path: no head sharing)
+# ----------------------------------------------------------------------------
+def _expand_kv(w, depth, heads, kv_heads):
+    g = heads // kv_heads
+    out = dict(w)
+    for layer in range(depth):
+        for n in ("wk", "wv"):
+            blocks = w[f"h{layer}.{n}"].reshape(kv_heads, 128, -1)
+            out[f"h{layer}.{n}"] = np.repeat(blocks, g, axis=0).reshape(heads * 128, -1)
+    return out
+
+
+@pytest.mark.parametrize("kv_heads", [1, 2])
+def test_gqa_equals_mha_with_repeated_kv_weights(kv_heads):
+    depth, vocab, seq, heads = 8, 128, 10, 4  # width 512, 4 heads
+    w = _tiny_weights(depth, vocab, seed=7, std=0.1, kv_heads=kv_heads)
+    w_full = _expand_kv(w, depth, heads, kv_heads)
+    tok, tgt = _ids(2, seq, vocab, seed=8)
+    loss_g, grads_g = oracle.forward_backward(w, tok, tgt, windows=[None, 4] * 4)
+    loss_f, grads_f = oracle.forward_backward(w_full, tok, tgt, windows=[None, 4] * 4)
+    assert loss_g == pytest.approx(loss_f, rel=1e-13)
+    g = heads // kv_heads
+    for k in grads_g:
+        if k.endswith(".wk") or k.endswith(".wv"):
+            # A shared row receives the sum of its copies' gradients.
+            summed = grads_f[k].reshape(kv_heads, g, 128, -1).sum(axis=1).reshape(kv_heads * 128, -1)
+            np.testing.assert_allclose(grads_g[k], summed, rtol=1e-10, atol=1e-14)
+        else:
+            np.testing.assert_allclose(grads_g[k], grads_f[k], rtol=1e-10, atol=1e-14)
+
+
+def test_gqa_attention_reads_the_group_head():
+    rng = np.random.default_rng(30)
+    T, H, Hkv = 6, 4, 2
+    q = rng.standard_normal((T, H, 128))
+    k, v = (rng.standard_normal((T, Hkv, 128)) for _ in range(2))
+    o, _ = oracle.causal_attention(q, k, v)
+    for h in range(H):
+        oh, _ = oracle.causal_attention(q[:, h:h + 1], k[:, h // 2:h // 2 + 1], v[:, h // 2:h // 2 + 1])
+        np.testing.assert_allclose(o[:, h], oh[:, 0], rtol=1e-14, atol=1e-15)
 
 
 # ----------------------------------------------------------------------------
