@@ -44,9 +44,11 @@ ADAMW = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
 NORMUON_BETA2 = 0.95
 
 
-def flops_per_token(L, d, V, T, windows=None):
+def flops_per_token(L, d, V, T, windows=None, dkv=None):
     """Model FLOPs per token; causal attention counts T per layer (half of the
-    T^2 score matrix, fwd+bwd). A windowed layer counts 2 * (visible pairs) / T."""
+    T^2 score matrix, fwd+bwd). A windowed layer counts 2 * (visible pairs) / T.
+    dkv: width of the key/value projections (d unless grouped-query)."""
+    dkv = d if dkv is None else dkv
     att = 0.0
     for l in range(L):
         w = -1 if windows is None else windows[l]
@@ -55,16 +57,17 @@ def flops_per_token(L, d, V, T, windows=None):
         else:
             pairs = 0.5 * (w + 1) * (w + 2) + (T - 1 - w) * (w + 1)
             att += 2.0 * pairs / T
-    return 6.0 * (12.0 * L * d * d + V * d) + 6.0 * d * att
+    return 6.0 * (L * (10.0 * d * d + 2.0 * dkv * d) + V * d) + 6.0 * d * att
 
 
-def gemm_bytes_per_step(L, d, V, N, chunk):
+def gemm_bytes_per_step(L, d, V, N, chunk, dkv=None):
     """Algorithmic HBM bytes of the fwd/bwd GEMM launches of one step: bf16 operands
     read once, outputs written once (fp32 for dX feeding a norm, for weight
     gradients and for the residual stream), epilogue operands (the fp32 residual,
-    relu^2 activations) read once."""
+    relu^2 activations) read once. The qkv width is d + 2 dkv."""
     F = 4 * d
-    layer = (N * d * 2 + 3 * d * d * 2 + N * 3 * d * 2            # QKV
+    Q = d + 2 * (d if dkv is None else dkv)
+    layer = (N * d * 2 + Q * d * 2 + N * Q * 2                    # QKV
              + N * d * 2 + d * d * 2 + 2 * N * d * 4              # O + fp32 residual
              + N * d * 2 + F * d * 2 + N * F * 2                  # FC, relu^2
              + N * F * 2 + F * d * 2 + 2 * N * d * 4              # proj + fp32 residual
@@ -74,8 +77,8 @@ def gemm_bytes_per_step(L, d, V, N, chunk):
              + N * F * 2 + N * d * 2 + F * d * 4                  # dW_fc
              + N * d * 2 + d * d * 2 + N * d * 2                  # dO
              + 2 * N * d * 2 + d * d * 4                          # dWo
-             + N * 3 * d * 2 + 3 * d * d * 2 + N * d * 4          # dXn
-             + N * 3 * d * 2 + N * d * 2 + 3 * d * d * 4)         # dW_qkv
+             + N * Q * 2 + Q * d * 2 + N * d * 4                  # dXn
+             + N * Q * 2 + N * d * 2 + Q * d * 4)                 # dW_qkv
     nchunks = -(-N // chunk)
     head = nchunks * ((chunk * d * 2 + V * d * 2 + chunk * V * 2)
                       + (chunk * V * 2 + V * d * 2 + chunk * d * 4)
@@ -83,9 +86,13 @@ def gemm_bytes_per_step(L, d, V, N, chunk):
     return L * layer + head, 12 * L + 3 * nchunks
 
 
-def ns_flops(L, d, steps=5):
-    # Per iteration per layer: four d x d matrices (6 d^3 each) and two 4d x d (18 d^3 each).
-    return steps * L * (4 * 6.0 + 2 * 18.0) * d ** 3
+def ns_flops(L, d, steps=5, dkv=None):
+    # Per iteration, an r x c matrix (r >= c) costs 4 r c^2 + 2 c^3: the Gram
+    # matrix, its square and the update. Per layer: wq, wo (d x d, 6 d^3 each),
+    # wk, wv (d x dkv once oriented tall), wfc and wproj (4d x d, 18 d^3 each).
+    dkv = d if dkv is None else dkv
+    kv = 4.0 * d * dkv ** 2 + 2.0 * dkv ** 3
+    return steps * L * (2 * 6.0 * d ** 3 + 2 * kv + 2 * 18.0 * d ** 3)
 
 
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
@@ -160,6 +167,8 @@ def main():
                     help="microbatches per optimizer step (gradient accumulation)")
     ap.add_argument("--window-pattern", default=None,
                     help="per-layer attention windows, e.g. SSSL (S: seq/2 keys, L: full causal)")
+    ap.add_argument("--kv-heads", type=int, default=None,
+                    help="key/value heads (grouped-query attention; default: every head)")
     ap.add_argument("--normuon", action="store_true",
                     help="NorMuon variance reduction after Newton-Schulz (normuon_step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -187,9 +196,9 @@ def main():
     d = dims["d"]
     print(f"[bench] config {args.config}: depth {L} width {d} vocab {V} seq {T} batch {B}",
           file=sys.stderr, flush=True)
-    weights = syn.init_weights(L, V, seed=0)
+    weights = syn.init_weights(L, V, seed=0, kv_heads=args.kv_heads)
     tok, tgt = syn.split_tokens(syn.zipf_ids(B, T, V, seed=1))
-    st = TrainState(L, V, T, B)
+    st = TrainState(L, V, T, B, kv_heads=args.kv_heads)
     st.load_weights(weights)
     windows = window_pattern(L, T, args.window_pattern) if args.window_pattern else None
     st.set_windows(windows)
@@ -250,9 +259,10 @@ def main():
 
     ms_step = elapsed_ms / args.steps
     tokens_per_s = accum * B * T * args.steps / (elapsed_ms / 1e3)
-    f_tok = flops_per_token(L, d, V, T, windows)
+    dkv = 128 * st.model.kv_heads
+    f_tok = flops_per_token(L, d, V, T, windows, dkv)
     mfu = tokens_per_s * f_tok / PEAK_BF16_FLOPS
-    mfma_work = (tokens_per_s * f_tok + ns_flops(L, d) / (ms_step / 1e3)) / PEAK_BF16_FLOPS
+    mfma_work = (tokens_per_s * f_tok + ns_flops(L, d, dkv=dkv) / (ms_step / 1e3)) / PEAK_BF16_FLOPS
     adamw_ms = block_ms = None
     if not args.no_isolated_timings:
         # The AdamW call alone, timed after the steps (HIP events on the current stream).
@@ -280,7 +290,7 @@ def main():
     g_ms, g_fl, g_n = prof["gemm"]
     # The head runs over token chunks of at most 1 GiB of bf16 logits (at least 256 rows).
     head_chunk = min(B * T, max(256, (1 << 30) // (2 * V)))
-    g_bytes, g_launches = gemm_bytes_per_step(L, d, V, B * T, head_chunk)
+    g_bytes, g_launches = gemm_bytes_per_step(L, d, V, B * T, head_chunk, dkv)
     achieved = g_fl / (g_ms / 1e3) / 1e12 if g_ms > 0 else 0.0
     roofline = {
         "kernel": "gemm_pp_kernel + gemm_bf16_kernel (projection, head and weight-gradient GEMMs of fwd+bwd)",
@@ -314,6 +324,7 @@ def main():
                         + (f" x {accum} accumulated" if accum > 1 else "")
                         + (f"; attention windows {args.window_pattern.upper()} (S = {T // 2} keys)"
                            if args.window_pattern else "")
+                        + (f"; {args.kv_heads} key/value heads" if args.kv_heads else "")
                         + "; fwd+bwd+" + ("NorMuon" if args.normuon else "Muon")
                         + " (5 Newton-Schulz steps)+AdamW (wte, lm_head)",
             "global_batch": accum * B,

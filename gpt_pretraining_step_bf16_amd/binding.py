@@ -54,6 +54,8 @@ def _sig(lib, name, res, args):
 
 EXPORTS = {
     "gpt_create": (C.c_int, [_I, _I, _I, C.POINTER(_P)]),
+    "gpt_create_gqa": (C.c_int, [_I, _I, _I, _I, C.POINTER(_P)]),
+    "gpt_kv_heads": (C.c_int32, [_P]),
     "gpt_destroy": (None, [_P]),
     "gpt_dims": (C.c_int, [_P, C.POINTER(C.c_int32)]),
     "gpt_num_params": (C.c_int64, [_P]),
@@ -71,8 +73,8 @@ EXPORTS = {
     "gpt_check": (C.c_int, [_P, _P, _P]),
     "gpt_status_str": (C.c_char_p, [C.c_int]),
     "gpt_op_gemm": (C.c_int, [_I, _I, _I, _I, _P, _L, _L, _I, _P, _L, _L, _I, _P, _L, _L, _I, _P]),
-    "gpt_op_attention_fwd": (C.c_int, [_P, _P, _P, _I, _I, _I, _I, _P]),
-    "gpt_op_attention_bwd": (C.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
+    "gpt_op_attention_fwd": (C.c_int, [_P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "gpt_op_attention_bwd": (C.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "gpt_set_attention_windows": (C.c_int, [_P, C.POINTER(C.c_int32), _I]),
     "gpt_get_attention_windows": (C.c_int, [_P, C.POINTER(C.c_int32), _I]),
     "gpt_op_ns_scratch_bytes": (C.c_size_t, [_I, _I, _I]),
@@ -131,13 +133,17 @@ def _coeffs(table):
 class GptModel:
     """Host-side plan of a model (no device memory)."""
 
-    def __init__(self, depth: int, vocab: int, max_seq: int):
+    def __init__(self, depth: int, vocab: int, max_seq: int, kv_heads=None):
         h = C.c_void_p()
-        _check(lib().gpt_create(depth, vocab, max_seq, C.byref(h)), "gpt_create")
+        if kv_heads is None:
+            _check(lib().gpt_create(depth, vocab, max_seq, C.byref(h)), "gpt_create")
+        else:
+            _check(lib().gpt_create_gqa(depth, vocab, max_seq, int(kv_heads), C.byref(h)), "gpt_create_gqa")
         self._h = h
         dims = (C.c_int32 * 6)()
         _check(lib().gpt_dims(h, dims), "gpt_dims")
         self.depth, self.d, self.heads, self.mlp, self.vocab, self.max_seq = list(dims)
+        self.kv_heads = int(lib().gpt_kv_heads(h))
 
     def close(self):
         if getattr(self, "_h", None):
@@ -256,14 +262,17 @@ def op_gemm(M, N, K, A, lda, a_kmajor, B, ldb, b_kmajor, Cout, ldc, out_mode, ba
     _check(st, "gpt_op_gemm")
 
 
-def op_attention_fwd(qkv, o, lse, batch, seq, heads, window=-1, stream=None):
-    _check(lib().gpt_op_attention_fwd(_ptr(qkv), _ptr(o), _ptr(lse), batch, seq, heads, int(window),
+def op_attention_fwd(qkv, o, lse, batch, seq, heads, window=-1, kv_heads=None, stream=None):
+    kvh = heads if kv_heads is None else int(kv_heads)
+    _check(lib().gpt_op_attention_fwd(_ptr(qkv), _ptr(o), _ptr(lse), batch, seq, heads, kvh, int(window),
                                       _stream(stream)), "gpt_op_attention_fwd")
 
 
-def op_attention_bwd(qkv, o, lse, dO, dqkv, scratch, batch, seq, heads, window=-1, stream=None):
+def op_attention_bwd(qkv, o, lse, dO, dqkv, scratch, batch, seq, heads, window=-1, kv_heads=None,
+                     stream=None):
+    kvh = heads if kv_heads is None else int(kv_heads)
     _check(lib().gpt_op_attention_bwd(_ptr(qkv), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dqkv),
-                                      _ptr(scratch), batch, seq, heads, int(window), _stream(stream)),
+                                      _ptr(scratch), batch, seq, heads, kvh, int(window), _stream(stream)),
            "gpt_op_attention_bwd")
 
 

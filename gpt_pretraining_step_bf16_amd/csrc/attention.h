@@ -1,6 +1,8 @@
-// Launchers of the flash-attention kernels with an attention window (defined
-// in attention.hip): key j is visible to query i when i - window <= j <= i; a
-// negative window (or one of at least T) is the plain causal mask.
+// Launchers of the flash-attention kernels (defined in attention.hip).
+// qkv is [B*T, (H + 2*Hkv)*128] bf16 (q heads, k heads, v heads); Hkv divides
+// H (grouped-query attention when Hkv < H). window: key j is visible to query
+// i when i - window <= j <= i; a negative window (or one of at least T) is the
+// plain causal mask. lse2 and delta are [B, H, T].
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -8,7 +10,7 @@
 #include <cstdint>
 
 hipError_t launch_attention_fwd_window(const uint16_t* qkv, uint16_t* o, float* lse2, int B, int T, int H,
-                                       int window, hipStream_t s);
+                                       int Hkv, int window, hipStream_t s);
 hipError_t launch_attention_bwd_window(const uint16_t* qkv, const uint16_t* o, const float* lse2,
                                        const uint16_t* dO, uint16_t* dqkv, float* delta, int B, int T, int H,
-                                       int window, hipStream_t s);
+                                       int Hkv, int window, hipStream_t s);

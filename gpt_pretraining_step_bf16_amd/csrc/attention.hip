@@ -7,8 +7,11 @@
 // i - W <= j <= i. W >= T - 1 is the plain causal mask. Tiles wholly outside
 // the band are skipped, not masked.
 //
-// Layout: q, k, v live in one packed buffer qkv [B*T, 3*H*128] bf16 (q heads,
-// then k heads, then v heads; 128 columns per head), o is [B*T, H*128].
+// Layout: q, k, v live in one packed buffer qkv [B*T, (H + 2*Hkv)*128] bf16
+// (H query heads, then Hkv key heads, then Hkv value heads; 128 columns per
+// head), o is [B*T, H*128]. With Hkv < H (grouped-query attention, [CT50]
+// "1. Modelo GPT": fewer KV heads) query head h reads key/value head
+// h / (H / Hkv); the dK/dV kernel sums over the query heads of its group.
 //
 // Every K, V, Q or dO tile that more than one wave reads goes global -> LDS
 // by direct loads (global_load_lds_dwordx4), row-major [64 rows][128] with
@@ -177,7 +180,7 @@ __device__ __forceinline__ void head_block(int& blk, int& bh) {
 // ===========================================================================
 __global__ void __launch_bounds__(NTHR, 2)
     attn_fwd_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ out,
-                    float* __restrict__ lse2, int T, int H, int W) {
+                    float* __restrict__ lse2, int T, int H, int Hkv, int W) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];  // [stage][K, V]
 
   const int tid = threadIdx.x;
@@ -191,10 +194,11 @@ __global__ void __launch_bounds__(NTHR, 2)
   const int b = bh / H;
   const int h = bh - b * H;
   const int d = H * HD;
-  const long ld = 3L * d;
+  const int dkv = Hkv * HD;
+  const long ld = (long)d + 2L * dkv;
   const uint16_t* qbase = qkv + (long)b * T * ld + h * HD;
-  const uint16_t* kbase = qbase + d;
-  const uint16_t* vbase = qbase + 2 * d;
+  const uint16_t* kbase = qkv + (long)b * T * ld + d + (h / (H / Hkv)) * HD;
+  const uint16_t* vbase = kbase + dkv;
   const int q0 = qblk * QB + wave * 32;
   const int qpos = q0 + (lane & 31);
   const float sc = GPT_LOG2E * 0.08838834764831845f;  // log2(e) / sqrt(128)
@@ -365,25 +369,28 @@ constexpr int DKDV_NST = 4;                         // stages of the Q/dO ring
 __global__ void __launch_bounds__(NTHR, 1)
     attn_bwd_dkdv_kernel(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dO,
                          const float* __restrict__ lse2, const float* __restrict__ delta,
-                         uint16_t* __restrict__ dqkv, int T, int H, int W) {
+                         uint16_t* __restrict__ dqkv, int T, int H, int Hkv, int W) {
   __shared__ __attribute__((aligned(1024))) char smem[DKDV_NST * DKDV_STAGE + 256];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int hl = lane >> 5;
-  int kblk, bh;
-  head_block(kblk, bh);
-  const int b = bh / H;
-  const int h = bh - b * H;
+  int kblk, bkv;
+  head_block(kblk, bkv);  // bkv = b * Hkv + key/value head
+  const int b = bkv / Hkv;
+  const int hk = bkv - b * Hkv;
+  const int G = H / Hkv;  // query heads per key/value head
   const int d = H * HD;
-  const long ld = 3L * d;
-  const uint16_t* qbase = qkv + (long)b * T * ld + h * HD;
-  const uint16_t* kbase = qbase + d;
-  const uint16_t* vbase = qbase + 2 * d;
-  const uint16_t* dobase = dO + (long)b * T * d + h * HD;
-  const float* lrow = lse2 + (long)bh * T;
-  const float* drow = delta + (long)bh * T;
+  const int dkv = Hkv * HD;
+  const long ld = (long)d + 2L * dkv;
+  const uint16_t* kbase = qkv + (long)b * T * ld + d + hk * HD;
+  const uint16_t* vbase = kbase + dkv;
+  // Query head g of the group: its q columns, dO columns, lse and delta rows.
+  auto qbase = [&](int g) { return qkv + (long)b * T * ld + (hk * G + g) * HD; };
+  auto dobase = [&](int g) { return dO + (long)b * T * d + (hk * G + g) * HD; };
+  auto lrow = [&](int g) { return lse2 + ((long)b * H + hk * G + g) * T; };
+  auto drow = [&](int g) { return delta + ((long)b * H + hk * G + g) * T; };
   const float sc = GPT_LOG2E * 0.08838834764831845f;
 
   const int k0 = kblk * KBW + wave * 32;
@@ -416,7 +423,8 @@ __global__ void __launch_bounds__(NTHR, 1)
   // last key (query i sees key j for j <= i <= j + W).
   const int qb_first = (kblk * KBW) / QBW;
   const int qb_end = min((T + QBW - 1) / QBW, (min(T - 1, kblk * KBW + KBW - 1 + W)) / QBW + 1);
-  const int ntile = qb_end - qb_first;
+  const int nqt = qb_end - qb_first;  // query tiles per query head
+  const int ntile = G * nqt;          // tile n: head n / nqt, query tile n % nqt
   const int qlim = min(T - 1 - kpos, W);  // last visible query - kpos (negative past T)
 
   TileDma tq, tg;
@@ -427,13 +435,14 @@ __global__ void __launch_bounds__(NTHR, 1)
   auto stage = [&](int st) { return smem + st * DKDV_STAGE; };
   auto issue = [&](int n, int st) {
     char* base = stage(st);
-    const int q0 = (qb_first + n) * QBW;
-    dma_tile_fast(qbase, ld, q0, T, base, wave, lane, tq);
-    dma_tile_fast(dobase, d, q0, T, base + TILE, wave, lane, tg);
+    const int g = n / nqt;
+    const int q0 = (qb_first + n - g * nqt) * QBW;
+    dma_tile_fast(qbase(g), ld, q0, T, base, wave, lane, tq);
+    dma_tile_fast(dobase(g), d, q0, T, base + TILE, wave, lane, tg);
     float* dst = wave == 0 ? reinterpret_cast<float*>(base + 2 * TILE)
                : wave == 1 ? reinterpret_cast<float*>(base + 2 * TILE + QBW * 4)
                            : dummy;
-    dma_vec64(wave == 1 ? drow : lrow, q0, T, dst, lane);
+    dma_vec64(wave == 1 ? drow(g) : lrow(g), q0, T, dst, lane);
   };
 
   // Work unit: one 32-query half t of a 64-query tile.
@@ -476,7 +485,7 @@ __global__ void __launch_bounds__(NTHR, 1)
   auto softmax = [&](int n, int st, int t, f32x16& s, f32x16& dp, bf16x8 (&pf)[2], bf16x8 (&dsf)[2]) {
     const float* ls = reinterpret_cast<const float*>(stage(st) + 2 * TILE);
     const float* ds = ls + QBW;
-    const int qb = qb_first + n;
+    const int qb = qb_first + n % nqt;
     // s[v]: query qb*64 + 32t + 8(v/4) + 4hl + v%4, key kpos.
     const bool need_mask = (qb * QBW + 32 * t < k0 + 31) || (qb * QBW + 32 * t + 32 > T) ||
                            (qb * QBW + 32 * t + 31 > k0 + W);
@@ -566,8 +575,8 @@ __global__ void __launch_bounds__(NTHR, 1)
 
   if (kpos < T) {
     const float scale = 0.08838834764831845f;
-    uint16_t* krow = dqkv + ((long)b * T + kpos) * ld + d + h * HD;
-    uint16_t* vrow = krow + d;
+    uint16_t* krow = dqkv + ((long)b * T + kpos) * ld + d + hk * HD;
+    uint16_t* vrow = krow + dkv;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -589,7 +598,8 @@ __global__ void __launch_bounds__(NTHR, 1)
 __global__ void __launch_bounds__(NTHR, 2)
     attn_bwd_dq_kernel(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ o,
                        const uint16_t* __restrict__ dO, const float* __restrict__ lse2,
-                       float* __restrict__ delta, uint16_t* __restrict__ dqkv, int T, int H, int W) {
+                       float* __restrict__ delta, uint16_t* __restrict__ dqkv, int T, int H, int Hkv,
+                       int W) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];  // [stage][K, V]
 
   const int tid = threadIdx.x;
@@ -603,10 +613,11 @@ __global__ void __launch_bounds__(NTHR, 2)
   const int b = bh / H;
   const int h = bh - b * H;
   const int d = H * HD;
-  const long ld = 3L * d;
+  const int dkv = Hkv * HD;
+  const long ld = (long)d + 2L * dkv;
   const uint16_t* qbase = qkv + (long)b * T * ld + h * HD;
-  const uint16_t* kbase = qbase + d;
-  const uint16_t* vbase = qbase + 2 * d;
+  const uint16_t* kbase = qkv + (long)b * T * ld + d + (h / (H / Hkv)) * HD;
+  const uint16_t* vbase = kbase + dkv;
   const uint16_t* dobase = dO + (long)b * T * d + h * HD;
   const float sc = GPT_LOG2E * 0.08838834764831845f;
 
@@ -757,36 +768,27 @@ __global__ void __launch_bounds__(NTHR, 2)
 }  // namespace
 
 hipError_t launch_attention_fwd_window(const uint16_t* qkv, uint16_t* o, float* lse2, int B, int T, int H,
-                                       int window, hipStream_t s) {
+                                       int Hkv, int window, hipStream_t s) {
   if (B <= 0 || T <= 0 || H <= 0) return hipSuccess;
+  if (Hkv <= 0 || H % Hkv != 0) return hipErrorInvalidValue;
   const int W = (window < 0 || window > T) ? T : window;
   dim3 grid((T + QB - 1) / QB, B * H);
-  hipLaunchKernelGGL(attn_fwd_kernel, grid, dim3(NTHR), 0, s, qkv, o, lse2, T, H, W);
+  hipLaunchKernelGGL(attn_fwd_kernel, grid, dim3(NTHR), 0, s, qkv, o, lse2, T, H, Hkv, W);
   return hipGetLastError();
 }
 
 hipError_t launch_attention_bwd_window(const uint16_t* qkv, const uint16_t* o, const float* lse2,
                                        const uint16_t* dO, uint16_t* dqkv, float* delta, int B, int T, int H,
-                                       int window, hipStream_t s) {
+                                       int Hkv, int window, hipStream_t s) {
   if (B <= 0 || T <= 0 || H <= 0) return hipSuccess;
+  if (Hkv <= 0 || H % Hkv != 0) return hipErrorInvalidValue;
   const int W = (window < 0 || window > T) ? T : window;
   // dQ first: it also writes delta = rowsum(dO * O), which dK/dV reads.
   hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((T + QB - 1) / QB, B * H), dim3(NTHR), 0, s, qkv, o, dO,
-                     lse2, delta, dqkv, T, H, W);
+                     lse2, delta, dqkv, T, H, Hkv, W);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((T + KBW - 1) / KBW, B * H), dim3(NTHR), 0, s, qkv,
-                     dO, lse2, delta, dqkv, T, H, W);
+  hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((T + KBW - 1) / KBW, B * Hkv), dim3(NTHR), 0, s, qkv,
+                     dO, lse2, delta, dqkv, T, H, Hkv, W);
   return hipGetLastError();
-}
-
-hipError_t launch_attention_fwd(const uint16_t* qkv, uint16_t* o, float* lse2, int B, int T, int H,
-                                hipStream_t s) {
-  return launch_attention_fwd_window(qkv, o, lse2, B, T, H, -1, s);
-}
-
-hipError_t launch_attention_bwd(const uint16_t* qkv, const uint16_t* o, const float* lse2,
-                                const uint16_t* dO, uint16_t* dqkv, float* delta, int B, int T,
-                                int H, hipStream_t s) {
-  return launch_attention_bwd_window(qkv, o, lse2, dO, dqkv, delta, B, T, H, -1, s);
 }

@@ -296,14 +296,15 @@ __device__ __forceinline__ void rope8(const float* __restrict__ cs, int t, int q
 __global__ void __launch_bounds__(256) qknorm_rope_fwd_kernel(uint16_t* __restrict__ qkv,
                                                              float* __restrict__ rstd_qk,
                                                              const float* __restrict__ cs, long N, int T,
-                                                             int H) {
+                                                             int H, int Hkv) {
+  const int NH = H + Hkv;  // normalised heads per row: H q heads, then Hkv k heads
   const long item = (blockIdx.x * (long)blockDim.x + threadIdx.x) >> 3;  // (row, head)
   const int q = threadIdx.x & 7;
-  if (item >= N * 2 * H) return;  // whole groups of 8 leave together
-  const long row = item / (2 * H);
-  const int hh = (int)(item - row * 2 * H);  // 0..H-1 q heads, H..2H-1 k heads
+  if (item >= N * NH) return;  // whole groups of 8 leave together
+  const long row = item / NH;
+  const int hh = (int)(item - row * NH);
   const int t = (int)(row % T);
-  uint16_t* p = qkv + row * 3L * H * 128 + hh * 128;
+  uint16_t* p = qkv + row * (long)(H + 2 * Hkv) * 128 + hh * 128;
   float x1[8], x2[8];
   unpack8(*reinterpret_cast<const uint4*>(p + 8 * q), x1);
   unpack8(*reinterpret_cast<const uint4*>(p + 64 + 8 * q), x2);
@@ -331,14 +332,15 @@ __global__ void __launch_bounds__(256) qknorm_rope_bwd_kernel(uint16_t* __restri
                                                              const uint16_t* __restrict__ qkv,
                                                              const float* __restrict__ rstd_qk,
                                                              const float* __restrict__ cs, long N, int T,
-                                                             int H) {
+                                                             int H, int Hkv) {
+  const int NH = H + Hkv;
   const long item = (blockIdx.x * (long)blockDim.x + threadIdx.x) >> 3;
   const int q = threadIdx.x & 7;
-  if (item >= N * 2 * H) return;
-  const long row = item / (2 * H);
-  const int hh = (int)(item - row * 2 * H);
+  if (item >= N * NH) return;
+  const long row = item / NH;
+  const int hh = (int)(item - row * NH);
   const int t = (int)(row % T);
-  const long off = row * 3L * H * 128 + hh * 128;
+  const long off = row * (long)(H + 2 * Hkv) * 128 + hh * 128;
   uint16_t* g = dqkv + off;
   const uint16_t* y = qkv + off;
   float g1[8], g2[8], y1[8], y2[8];
@@ -808,18 +810,18 @@ hipError_t launch_rmsnorm_bwd(const float* dxn, const uint16_t* xn, const float*
 }
 
 hipError_t launch_qknorm_rope_fwd(uint16_t* qkv, float* rstd_qk, const float* cs, long N, int T,
-                                  int H, hipStream_t s) {
-  const long items = N * 2 * H;
+                                  int H, int Hkv, hipStream_t s) {
+  const long items = N * (H + Hkv);
   hipLaunchKernelGGL(qknorm_rope_fwd_kernel, dim3((unsigned)((items * 8 + 255) / 256)), dim3(256), 0, s, qkv,
-                     rstd_qk, cs, N, T, H);
+                     rstd_qk, cs, N, T, H, Hkv);
   return hipGetLastError();
 }
 
 hipError_t launch_qknorm_rope_bwd(uint16_t* dqkv, const uint16_t* qkv, const float* rstd_qk,
-                                  const float* cs, long N, int T, int H, hipStream_t s) {
-  const long items = N * 2 * H;
+                                  const float* cs, long N, int T, int H, int Hkv, hipStream_t s) {
+  const long items = N * (H + Hkv);
   hipLaunchKernelGGL(qknorm_rope_bwd_kernel, dim3((unsigned)((items * 8 + 255) / 256)), dim3(256), 0, s, dqkv,
-                     qkv, rstd_qk, cs, N, T, H);
+                     qkv, rstd_qk, cs, N, T, H, Hkv);
   return hipGetLastError();
 }
 

@@ -4,7 +4,7 @@
 #include <algorithm>
 
 #include "common.h"
-#include "kernels.h"
+#include "gemm.h"
 
 namespace {
 

@@ -38,7 +38,7 @@
 
 #include "common.h"
 #include "lds_dma.h"
-#include "kernels.h"
+#include "gemm.h"
 
 namespace gemm_impl {
 

@@ -32,6 +32,7 @@ struct ProfSlot {
 
 struct gpt_model {
   int depth = 0, d = 0, H = 0, F = 0, V = 0, max_seq = 0;
+  int Hkv = 0, dkv = 0;  // key/value heads (Hkv < H: grouped-query attention) and their width
   std::vector<gpt_tensor> tensors;
   int64_t nparams = 0;
   int64_t off_wte = 0, off_layer0 = 0, layer_stride = 0, off_lm = 0;
@@ -172,6 +173,7 @@ FwdPlan plan_fwd(const gpt_model& m, int B, int T) {
   p.N = (long)B * T;
   const long N = p.N;
   const long d = m.d, F = m.F, H = m.H, V = m.V;
+  const long Q = d + 2L * m.dkv;  // qkv row: H q heads, Hkv k heads, Hkv v heads
   Carve c;
   p.hdr = c.take(256);
   p.cs = c.take((size_t)T * 64 * 2 * 4);
@@ -179,8 +181,8 @@ FwdPlan plan_fwd(const gpt_model& m, int B, int T) {
   Carve lc;
   p.xn1 = lc.take(N * d * 2);
   p.rstd1 = lc.take(N * 4);
-  p.qkv = lc.take(N * 3 * d * 2);
-  p.rstdqk = lc.take(N * 2 * H * 4);
+  p.qkv = lc.take(N * Q * 2);
+  p.rstdqk = lc.take(N * (H + m.Hkv) * 4);
   p.o = lc.take(N * d * 2);
   p.lse = lc.take(N * H * 4);
   p.xn2 = lc.take(N * d * 2);
@@ -206,13 +208,13 @@ FwdPlan plan_fwd(const gpt_model& m, int B, int T) {
   p.du = c.take(N * F * 2);
   p.dO = c.take(N * d * 2);
   p.delta = c.take(N * H * 4);
-  p.dqkv = c.take(N * 3 * d * 2);
+  p.dqkv = c.take(N * Q * 2);
   const long cap_rows = std::max<long>(256, (1L << 30) / (2 * V));
   p.nc = std::min<long>(N, cap_rows);
   p.logits = c.take((size_t)p.nc * V * 2);
   p.loss_rows = c.take(N * 4);
   size_t part = 0;
-  const long shapes[4][2] = {{3 * d, d}, {d, d}, {F, d}, {d, F}};
+  const long shapes[4][2] = {{Q, d}, {d, d}, {F, d}, {d, F}};
   for (auto& sh : shapes) {
     const SplitK s = plan_splitk(sh[0], sh[1], N);
     if (s.splits > 1) part = std::max(part, (size_t)s.splits * sh[0] * sh[1] * 4);
@@ -223,23 +225,56 @@ FwdPlan plan_fwd(const gpt_model& m, int B, int T) {
   return p;
 }
 
-// Muon groups of a model: the four d x d matrices of each layer, and the
-// MLP pair (wfc stored [4d, d]; wproj stored [d, 4d], handled transposed).
-void muon_groups(const gpt_model& m, MuonGroup& sq, MuonGroup& tall) {
-  const long d = m.d, F = m.F;
-  sq = MuonGroup{};
-  sq.base = m.off_layer0;
-  sq.layer_stride = m.layer_stride;
-  sq.per_layer = 4;
-  sq.mat_stride = d * d;
-  sq.count = 4 * m.depth;
-  sq.rows = (int)d;
-  sq.cols = (int)d;
-  sq.transposed_mask = 0;
-  sq.x_rows = d;
-  sq.x_cols = d;
-  tall = MuonGroup{};
-  tall.base = m.off_layer0 + 4 * d * d;
+// Muon groups of a model, each a batch of same-shaped matrices for the
+// Newton-Schulz iteration. Without grouped-query attention: the four d x d
+// matrices of each layer (wq, wk, wv, wo), then the MLP pair (wfc stored
+// [4d, d]; wproj stored [d, 4d], handled transposed). With Hkv < H: wq and
+// wo, then wk and wv ([dkv, d], handled transposed), then the MLP pair.
+// Layer layout: wq [d, d], wk [dkv, d], wv [dkv, d], wo [d, d], wfc, wproj.
+int muon_groups(const gpt_model& m, MuonGroup* out) {
+  const long d = m.d, F = m.F, dkv = m.dkv;
+  int n = 0;
+  if (dkv == d) {
+    MuonGroup sq{};
+    sq.base = m.off_layer0;
+    sq.layer_stride = m.layer_stride;
+    sq.per_layer = 4;
+    sq.mat_stride = d * d;
+    sq.count = 4 * m.depth;
+    sq.rows = (int)d;
+    sq.cols = (int)d;
+    sq.transposed_mask = 0;
+    sq.x_rows = d;
+    sq.x_cols = d;
+    out[n++] = sq;
+  } else {
+    MuonGroup qo{};  // wq at 0, wo after wk and wv
+    qo.base = m.off_layer0;
+    qo.layer_stride = m.layer_stride;
+    qo.per_layer = 2;
+    qo.mat_stride = d * d + 2 * dkv * d;
+    qo.count = 2 * m.depth;
+    qo.rows = (int)d;
+    qo.cols = (int)d;
+    qo.transposed_mask = 0;
+    qo.x_rows = d;
+    qo.x_cols = d;
+    out[n++] = qo;
+    MuonGroup kv{};  // wk, wv: [dkv, d], wide
+    kv.base = m.off_layer0 + d * d;
+    kv.layer_stride = m.layer_stride;
+    kv.per_layer = 2;
+    kv.mat_stride = dkv * d;
+    kv.count = 2 * m.depth;
+    kv.rows = (int)dkv;
+    kv.cols = (int)d;
+    kv.transposed_mask = 3;
+    kv.x_rows = d;
+    kv.x_cols = dkv;
+    out[n++] = kv;
+  }
+  MuonGroup tall{};
+  tall.base = m.off_layer0 + 2 * d * d + 2 * dkv * d;
   tall.layer_stride = m.layer_stride;
   tall.per_layer = 2;
   tall.mat_stride = F * d;
@@ -249,7 +284,10 @@ void muon_groups(const gpt_model& m, MuonGroup& sq, MuonGroup& tall) {
   tall.transposed_mask = 2;
   tall.x_rows = F;
   tall.x_cols = d;
+  out[n++] = tall;
+  return n;
 }
+constexpr int kMaxMuonGroups = 3;
 
 // Newton-Schulz buffers for `count` matrices of xr x xc.
 struct NsPlan {
@@ -449,21 +487,30 @@ const char* gpt_status_str(gpt_status s) {
 }
 
 gpt_status gpt_create(int32_t depth, int32_t vocab, int32_t max_seq, gpt_model** out) {
+  return gpt_create_gqa(depth, vocab, max_seq, 0, out);
+}
+
+gpt_status gpt_create_gqa(int32_t depth, int32_t vocab, int32_t max_seq, int32_t kv_heads, gpt_model** out) {
   if (!out) return GPT_EINVAL;
   *out = nullptr;
   if (depth < 1 || depth > 64) return GPT_EINVAL;
   if (vocab < 64 || vocab > 262144 || vocab % 64 != 0) return GPT_EINVAL;
   if (max_seq < 1 || max_seq > 16384) return GPT_EINVAL;
+  const int d_ = 128 * ((64 * depth + 127) / 128);
+  const int H_ = d_ / 128;
+  if (kv_heads < 0 || kv_heads > H_ || (kv_heads > 0 && H_ % kv_heads != 0)) return GPT_EINVAL;
   gpt_model* m = new (std::nothrow) gpt_model();
   if (!m) return GPT_EINVAL;
   m->depth = depth;
-  m->d = 128 * ((64 * depth + 127) / 128);
-  m->H = m->d / 128;
+  m->d = d_;
+  m->H = H_;
+  m->Hkv = kv_heads > 0 ? kv_heads : H_;
+  m->dkv = 128 * m->Hkv;
   m->F = 4 * m->d;
   m->V = vocab;
   m->max_seq = max_seq;
   m->windows.assign(depth, -1);
-  const int64_t d = m->d, F = m->F;
+  const int64_t d = m->d, F = m->F, dkv = m->dkv;
   int64_t off = 0;
   auto add = [&](const std::string& name, int32_t rows, int32_t cols, int32_t kind, int32_t layer) {
     gpt_tensor t{};
@@ -482,13 +529,13 @@ gpt_status gpt_create(int32_t depth, int32_t vocab, int32_t max_seq, gpt_model**
   for (int l = 0; l < depth; ++l) {
     const std::string p = "h" + std::to_string(l) + ".";
     add(p + "wq", (int32_t)d, (int32_t)d, GPT_KIND_MATRIX, l);
-    add(p + "wk", (int32_t)d, (int32_t)d, GPT_KIND_MATRIX, l);
-    add(p + "wv", (int32_t)d, (int32_t)d, GPT_KIND_MATRIX, l);
+    add(p + "wk", (int32_t)dkv, (int32_t)d, GPT_KIND_MATRIX, l);
+    add(p + "wv", (int32_t)dkv, (int32_t)d, GPT_KIND_MATRIX, l);
     add(p + "wo", (int32_t)d, (int32_t)d, GPT_KIND_MATRIX, l);
     add(p + "wfc", (int32_t)F, (int32_t)d, GPT_KIND_MATRIX, l);
     add(p + "wproj", (int32_t)d, (int32_t)F, GPT_KIND_MATRIX, l);
   }
-  m->layer_stride = 4 * d * d + 2 * F * d;
+  m->layer_stride = 2 * d * d + 2 * dkv * d + 2 * F * d;
   m->off_lm = off;
   add("lm_head", vocab, (int32_t)d, GPT_KIND_LM_HEAD, -1);
   m->nparams = off;
@@ -508,6 +555,8 @@ gpt_status gpt_dims(const gpt_model* m, int32_t dims[6]) {
   dims[5] = m->max_seq;
   return GPT_OK;
 }
+
+int32_t gpt_kv_heads(const gpt_model* m) { return m ? m->Hkv : 0; }
 
 int64_t gpt_num_params(const gpt_model* m) { return m ? m->nparams : 0; }
 int32_t gpt_num_tensors(const gpt_model* m) { return m ? (int32_t)m->tensors.size() : 0; }
@@ -538,7 +587,8 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
   char* ws = reinterpret_cast<char*>(workspace);
   g_prof_model = m;
   const long N = p.N;
-  const int T = seq, d = m->d, F = m->F, H = m->H, V = m->V, L = m->depth;
+  const int T = seq, d = m->d, F = m->F, H = m->H, V = m->V, L = m->depth, Hkv = m->Hkv;
+  const int Q = d + 2 * m->dkv;  // qkv row width
   int* hdr = reinterpret_cast<int*>(ws + p.hdr);
   int* err = hdr;
   int* n_valid = hdr + 1;
@@ -570,8 +620,8 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
   for (int l = 0; l < L; ++l) {
     const uint16_t* W = pbf + m->off_layer0 + (long)l * m->layer_stride;
     const uint16_t* wqkv = W;
-    const uint16_t* wo = W + 3L * d * d;
-    const uint16_t* wfc = W + 4L * d * d;
+    const uint16_t* wo = W + (long)Q * d;
+    const uint16_t* wfc = wo + (long)d * d;
     const uint16_t* wproj = wfc + (long)F * d;
     uint16_t* xn1 = reinterpret_cast<uint16_t*>(lay(p.xn1, l));
     float* rstd1 = reinterpret_cast<float*>(lay(p.rstd1, l));
@@ -583,11 +633,11 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
     float* rstd2 = reinterpret_cast<float*>(lay(p.rstd2, l));
     uint16_t* r = reinterpret_cast<uint16_t*>(lay(p.r, l));
     HIP_TRY(launch_rmsnorm_fwd(x, xn1, rstd1, N, d, s));
-    HIP_TRY(gemm_nt(xn1, d, wqkv, d, (int)N, 3 * d, d, qkv, 3L * d, EPI_BF16, s));
-    HIP_TRY(launch_qknorm_rope_fwd(qkv, rstdqk, cs, N, T, H, s));
+    HIP_TRY(gemm_nt(xn1, d, wqkv, d, (int)N, Q, d, qkv, Q, EPI_BF16, s));
+    HIP_TRY(launch_qknorm_rope_fwd(qkv, rstdqk, cs, N, T, H, Hkv, s));
     {
       ProfScope ps(m, s, PROF_ATTN_FWD, 4.0 * batch * H * 128.0 * attn_pairs(T, m->windows[l]));
-      HIP_TRY(launch_attention_fwd_window(qkv, o, lse, batch, T, H, m->windows[l], s));
+      HIP_TRY(launch_attention_fwd_window(qkv, o, lse, batch, T, H, Hkv, m->windows[l], s));
     }
     HIP_TRY(gemm_nt_add_f32(o, d, wo, d, (int)N, d, d, x, d, s));
     HIP_TRY(launch_rmsnorm_fwd(x, xn2, rstd2, N, d, s));
@@ -625,13 +675,13 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
     const long woff = m->off_layer0 + (long)l * m->layer_stride;
     const uint16_t* W = pbf + woff;
     const uint16_t* wqkv = W;
-    const uint16_t* wo = W + 3L * d * d;
-    const uint16_t* wfc = W + 4L * d * d;
+    const uint16_t* wo = W + (long)Q * d;
+    const uint16_t* wfc = wo + (long)d * d;
     const uint16_t* wproj = wfc + (long)F * d;
     float* G = grads + woff;
     float* gqkv = G;
-    float* go = G + 3L * d * d;
-    float* gfc = G + 4L * d * d;
+    float* go = G + (long)Q * d;
+    float* gfc = go + (long)d * d;
     float* gproj = gfc + (long)F * d;
     const uint16_t* xn1 = reinterpret_cast<const uint16_t*>(lay(p.xn1, l));
     const float* rstd1 = reinterpret_cast<const float*>(lay(p.rstd1, l));
@@ -653,11 +703,11 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
     HIP_TRY(gemm_wgrad(dxb, d, o, d, d, d, N, go, accumulate, part, s));
     {
       ProfScope ps(m, s, PROF_ATTN_BWD, 10.0 * batch * H * 128.0 * attn_pairs(T, m->windows[l]));
-      HIP_TRY(launch_attention_bwd_window(qkv, o, lse, dO, dqkv, delta, batch, T, H, m->windows[l], s));
+      HIP_TRY(launch_attention_bwd_window(qkv, o, lse, dO, dqkv, delta, batch, T, H, Hkv, m->windows[l], s));
     }
-    HIP_TRY(launch_qknorm_rope_bwd(dqkv, qkv, rstdqk, cs, N, T, H, s));
-    HIP_TRY(gemm_nn(dqkv, 3L * d, wqkv, d, (int)N, d, 3 * d, dxn, d, EPI_F32, s));
-    HIP_TRY(gemm_wgrad(dqkv, 3L * d, xn1, d, 3 * d, d, N, gqkv, accumulate, part, s));
+    HIP_TRY(launch_qknorm_rope_bwd(dqkv, qkv, rstdqk, cs, N, T, H, Hkv, s));
+    HIP_TRY(gemm_nn(dqkv, Q, wqkv, d, (int)N, d, Q, dxn, d, EPI_F32, s));
+    HIP_TRY(gemm_wgrad(dqkv, Q, xn1, d, Q, d, N, gqkv, accumulate, part, s));
     HIP_TRY(launch_rmsnorm_bwd(dxn, xn1, rstd1, dx, dxb, N, d, 1, s));
   }
 
@@ -671,13 +721,16 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
 // NorMuon scratch after the Newton-Schulz buffers: per X row of the larger
 // group, the scale and the two norm terms.
 static size_t ns_workspace_bytes(const gpt_model& m, size_t* normuon_off) {
-  MuonGroup sq, tall;
-  muon_groups(m, sq, tall);
-  const size_t a = plan_ns(sq.count, sq.x_rows, sq.x_cols, 0).total;
-  const size_t b = plan_ns(tall.count, tall.x_rows, tall.x_cols, 0).total;
-  const size_t off = (std::max(a, b) + 255) / 256 * 256;
+  MuonGroup groups[kMaxMuonGroups];
+  const int ng = muon_groups(m, groups);
+  size_t ns = 0, rows = 0;
+  for (int i = 0; i < ng; ++i) {
+    const MuonGroup& g = groups[i];
+    ns = std::max(ns, plan_ns(g.count, g.x_rows, g.x_cols, 0).total);
+    rows = std::max(rows, (size_t)g.count * g.x_rows);
+  }
+  const size_t off = (ns + 255) / 256 * 256;
   if (normuon_off) *normuon_off = off;
-  const size_t rows = std::max((size_t)sq.count * sq.x_rows, (size_t)tall.count * tall.x_rows);
   return off + (3 * rows * 4 + 255) / 256 * 256;
 }
 
@@ -688,9 +741,11 @@ size_t muon_workspace_bytes(const gpt_model* m) {
 
 int64_t normuon_state_elems(const gpt_model* m) {
   if (!m) return 0;
-  MuonGroup sq, tall;
-  muon_groups(*m, sq, tall);
-  return (int64_t)sq.count * sq.x_rows + (int64_t)tall.count * tall.x_rows;
+  MuonGroup groups[kMaxMuonGroups];
+  const int ng = muon_groups(*m, groups);
+  int64_t n = 0;
+  for (int i = 0; i < ng; ++i) n += (int64_t)groups[i].count * groups[i].x_rows;
+  return n;
 }
 
 // Momentum, Newton-Schulz and the update for both groups; with second_moment,
@@ -707,10 +762,11 @@ static gpt_status muon_impl(gpt_model* m, float* params, uint16_t* params_bf16, 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = reinterpret_cast<char*>(workspace);
   g_prof_model = m;
-  MuonGroup groups[2];
-  muon_groups(*m, groups[0], groups[1]);
+  MuonGroup groups[kMaxMuonGroups];
+  const int ng = muon_groups(*m, groups);
   float* state = second_moment;
-  for (const MuonGroup& g : groups) {
+  for (int gi = 0; gi < ng; ++gi) {
+    const MuonGroup& g = groups[gi];
     const NsPlan p = plan_ns(g.count, g.x_rows, g.x_cols, 0);
     float* part = reinterpret_cast<float*>(ws + p.part);
     float* x32 = reinterpret_cast<float*>(ws + p.x32);
@@ -820,19 +876,21 @@ gpt_status gpt_op_gemm(int32_t M, int32_t N, int32_t K, int32_t batch, const uin
 }
 
 gpt_status gpt_op_attention_fwd(const uint16_t* qkv, uint16_t* o, float* lse, int32_t batch,
-                                int32_t seq, int32_t heads, int32_t window, void* stream) {
+                                int32_t seq, int32_t heads, int32_t kv_heads, int32_t window, void* stream) {
   if (!qkv || !o || !lse || batch < 1 || seq < 1 || heads < 1 || window < -1) return GPT_EINVAL;
+  if (kv_heads < 1 || heads % kv_heads != 0) return GPT_EINVAL;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  HIP_TRY(launch_attention_fwd_window(qkv, o, lse, batch, seq, heads, window, s));
+  HIP_TRY(launch_attention_fwd_window(qkv, o, lse, batch, seq, heads, kv_heads, window, s));
   return GPT_OK;
 }
 
 gpt_status gpt_op_attention_bwd(const uint16_t* qkv, const uint16_t* o, const float* lse,
-                                const uint16_t* dO, uint16_t* dqkv, float* scratch,
-                                int32_t batch, int32_t seq, int32_t heads, int32_t window, void* stream) {
+                                const uint16_t* dO, uint16_t* dqkv, float* scratch, int32_t batch,
+                                int32_t seq, int32_t heads, int32_t kv_heads, int32_t window, void* stream) {
   if (!qkv || !o || !lse || !dO || !dqkv || !scratch || batch < 1 || seq < 1 || heads < 1 || window < -1)
     return GPT_EINVAL;
-  HIP_TRY(launch_attention_bwd_window(qkv, o, lse, dO, dqkv, scratch, batch, seq, heads, window,
+  if (kv_heads < 1 || heads % kv_heads != 0) return GPT_EINVAL;
+  HIP_TRY(launch_attention_bwd_window(qkv, o, lse, dO, dqkv, scratch, batch, seq, heads, kv_heads, window,
                                       reinterpret_cast<hipStream_t>(stream)));
   return GPT_OK;
 }

@@ -33,7 +33,7 @@ import sys
 
 # Epilogue ids (GemmEpilogue in csrc/kernels.h) that only Newton-Schulz uses.
 NS_EPILOGUES = {7, 8, 9}
-GEMM_SOURCES = ("common.h", "lds_dma.h", "kernels.h", "gemm_kernel.h", "gemm.hip",
+GEMM_SOURCES = ("common.h", "lds_dma.h", "gemm.h", "gemm_kernel.h", "gemm.hip",
                 "gemm_kk_fwd.hip", "gemm_kk_aux.hip", "gemm_kt.hip", "gemm_tt.hip")
 
 

@@ -28,11 +28,11 @@ def window_pattern(depth: int, seq: int, pattern: str = "SSSL", short_window=Non
 
 
 class TrainState:
-    def __init__(self, depth: int, vocab: int, seq: int, batch: int, device="cuda"):
+    def __init__(self, depth: int, vocab: int, seq: int, batch: int, device="cuda", kv_heads=None):
         import torch
 
         self.torch = torch
-        self.model = binding.GptModel(depth, vocab, seq)
+        self.model = binding.GptModel(depth, vocab, seq, kv_heads)
         self.batch, self.seq = batch, seq
         self.device = device
         n = self.model.num_params

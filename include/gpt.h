@@ -71,7 +71,19 @@ typedef struct {
  * On success *out receives a handle to release with gpt_destroy().
  */
 gpt_status gpt_create(int32_t depth, int32_t vocab, int32_t max_seq, gpt_model** out);
+
+/*
+ * gpt_create with grouped-query attention ([CT50] "1. Modelo GPT" lists
+ * attention with fewer KV heads): kv_heads key/value heads of 128, dividing
+ * the H query heads; query head h attends with key/value head h / (H / kv_heads).
+ * wk and wv become [kv_heads*128, d]. kv_heads = 0 means H (plain multi-head).
+ * Returns GPT_EINVAL when kv_heads does not divide H.
+ */
+gpt_status gpt_create_gqa(int32_t depth, int32_t vocab, int32_t max_seq, int32_t kv_heads, gpt_model** out);
 void gpt_destroy(gpt_model* m);
+
+/* Key/value heads of the model (H unless created with fewer). */
+int32_t gpt_kv_heads(const gpt_model* m);
 
 /* dims[6] <- {depth, width, heads, mlp_hidden, vocab, max_seq}. */
 gpt_status gpt_dims(const gpt_model* m, int32_t dims[6]);
@@ -146,10 +158,13 @@ gpt_status muon_step(gpt_model* m, float* params, uint16_t* params_bf16, const f
 
 /*
  * Elements of the NorMuon second-moment state: one fp32 per element of the
- * longer side of each block matrix (per row of wq, wk, wv, wo and wfc, per
- * column of wproj). Layout: the d x d matrices in the order layer 0 wq, wk,
- * wv, wo, layer 1 wq, ... (d each), then layer 0 wfc, wproj, layer 1 wfc, ...
- * (4d each).
+ * longer side of each block matrix (per row of wq, wo and wfc, per column of
+ * wproj; per row of wk and wv, or per column when they have fewer rows than
+ * columns under grouped-query attention). Layout: the d x d matrices in the
+ * order layer 0 wq, wk, wv, wo, layer 1 wq, ... (d each), then layer 0 wfc,
+ * wproj, layer 1 wfc, ... (4d each). With kv_heads < H the first block is
+ * layer 0 wq, wo, layer 1 wq, wo, ... (d each), then layer 0 wk, wv, ... (d
+ * each), then the MLP pairs.
  */
 int64_t normuon_state_elems(const gpt_model* m);
 
@@ -249,16 +264,19 @@ gpt_status gpt_op_gemm(int32_t M, int32_t N, int32_t K, int32_t batch, const uin
  * column blocks, 128 columns per head). Writes o [batch*seq, heads*128] bf16
  * and lse [batch, heads, seq] fp32: the base-2 logarithm of the softmax
  * normaliser sum_j 2^(s_ij), where s_ij = (q_i . k_j) * log2(e) / sqrt(128).
- * window: -1 for the causal mask, else W >= 0: query i sees keys i - W .. i. */
+ * window: -1 for the causal mask, else W >= 0: query i sees keys i - W .. i.
+ * kv_heads: key/value heads (dividing heads); qkv is then
+ * [batch*seq, (heads + 2*kv_heads)*128]. */
 gpt_status gpt_op_attention_fwd(const uint16_t* qkv, uint16_t* o, float* lse, int32_t batch,
-                                int32_t seq, int32_t heads, int32_t window, void* stream);
+                                int32_t seq, int32_t heads, int32_t kv_heads, int32_t window, void* stream);
 
 /* Causal attention backward: from qkv, o, lse (as written by the forward with
  * the same window) and dO [batch*seq, heads*128] bf16, write dqkv
- * [batch*seq, 3*heads*128] bf16. scratch: device, >= batch*heads*seq floats. */
+ * [batch*seq, (heads + 2*kv_heads)*128] bf16. scratch: device, >= batch*heads*seq
+ * floats. */
 gpt_status gpt_op_attention_bwd(const uint16_t* qkv, const uint16_t* o, const float* lse,
-                                const uint16_t* dO, uint16_t* dqkv, float* scratch,
-                                int32_t batch, int32_t seq, int32_t heads, int32_t window, void* stream);
+                                const uint16_t* dO, uint16_t* dqkv, float* scratch, int32_t batch,
+                                int32_t seq, int32_t heads, int32_t kv_heads, int32_t window, void* stream);
 
 /* Newton-Schulz on `count` fp32 matrices X [count, rows, cols] (rows >= cols)
  * in place: X0 = X / (||X||_F + 1e-7), then ns_steps iterations with the

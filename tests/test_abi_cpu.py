@@ -178,4 +178,34 @@ def test_attention_windows_are_host_state_with_validation():
     with pytest.raises(ValueError):
         window_pattern(4, 64, "SXL")
     fake = C.c_void_p(4096)
-    assert lib.gpt_op_attention_fwd(fake, fake, fake, 1, 64, 1, -2, None) == binding.GPT_EINVAL
+    assert lib.gpt_op_attention_fwd(fake, fake, fake, 1, 64, 1, 1, -2, None) == binding.GPT_EINVAL
+    assert lib.gpt_op_attention_fwd(fake, fake, fake, 1, 64, 4, 3, -1, None) == binding.GPT_EINVAL
+
+
+@pytest.mark.parametrize("depth,kv_heads", [(4, 1), (20, 2), (20, 5), (12, 6)])
+def test_gqa_layout_matches_canonical_specs(depth, kv_heads):
+    m = binding.GptModel(depth, 2048, 128, kv_heads)
+    assert m.kv_heads == kv_heads
+    specs = syn.tensor_specs(depth, 2048, kv_heads)
+    got = m.tensors()
+    assert [t["name"] for t in got] == [sp[0] for sp in specs]
+    off = 0
+    for t, (name, rows, cols, _kind, _layer) in zip(got, specs):
+        assert (t["rows"], t["cols"], t["offset"]) == (rows, cols, off), name
+        off += rows * cols
+    assert m.num_params == off
+    d, f = m.d, m.mlp
+    dkv = 128 * kv_heads
+    # One value per element of each block matrix's longer side.
+    assert m.normuon_state_elems() == depth * (2 * d + 2 * max(dkv, d) + f + f)
+    assert m.muon_workspace_bytes() > 0 and m.workspace_bytes(2, 128) > 0
+
+
+def test_gqa_create_rejects_kv_heads_that_do_not_divide():
+    lib = binding.lib()
+    h = C.c_void_p()
+    assert lib.gpt_create_gqa(20, 2048, 128, 3, C.byref(h)) == binding.GPT_EINVAL  # 10 heads
+    assert lib.gpt_create_gqa(20, 2048, 128, 11, C.byref(h)) == binding.GPT_EINVAL
+    assert lib.gpt_create_gqa(20, 2048, 128, -1, C.byref(h)) == binding.GPT_EINVAL
+    m = binding.GptModel(20, 2048, 128, 0)  # 0: every head
+    assert m.kv_heads == m.heads == 10

@@ -8,7 +8,8 @@ Weights are the seeded N(0, 0.02) draws, tokens seeded Zipf(1.1).
 For each depth:
 * One sequence through the whole model against the fp64 oracle, which is
   given the bf16 weights gpt_fwd_bwd computes with (at d12 and d20 also with
-  the "SSSL" window pattern, short window seq / 2): loss |delta| <= 1e-2,
+  the "SSSL" window pattern, short window seq / 2, and at d20 with 2 key/value
+  heads for the 10 query heads): loss |delta| <= 1e-2,
   every gradient tensor rel-L2 <= 2e-2, embedding rows of absent tokens exactly
   zero. The sequence is the workload's full length except at d32, where it is
   1024 tokens: the fp64 oracle of a 32-layer model at 4096 tokens needs about
@@ -62,16 +63,18 @@ def _cuda(a):
 # The fp64 oracle needs from a few seconds (d12) to about a minute (d26) of
 # host time for one sequence.
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name,pattern", [("d12", None), ("d20", None), ("d26", None), ("d32", None),
-                                          ("d12", "SSSL"), ("d20", "SSSL")])
-def test_one_sequence_matches_oracle(name, pattern):
+@pytest.mark.parametrize("name,pattern,kv_heads", [("d12", None, None), ("d20", None, None), ("d26", None, None),
+                                                   ("d32", None, None), ("d12", "SSSL", None),
+                                                   ("d20", "SSSL", None), ("d20", None, 2)])
+def test_one_sequence_matches_oracle(name, pattern, kv_heads):
     L, V, _, _ = _cfg(name)
     T = ORACLE_SEQ[name]
     windows = None if pattern is None else window_pattern(L, T, pattern)
-    log(f"{name} one sequence of {T} vs oracle" + (f", windows {pattern} (short {T // 2})" if pattern else ""))
-    w = syn.init_weights(L, V, seed=0)
+    log(f"{name} one sequence of {T} vs oracle" + (f", windows {pattern} (short {T // 2})" if pattern else "")
+        + (f", {kv_heads} kv heads" if kv_heads else ""))
+    w = syn.init_weights(L, V, seed=0, kv_heads=kv_heads)
     tok, tgt = syn.split_tokens(syn.zipf_ids(1, T, V, seed=1))
-    st = TrainState(L, V, T, 1)
+    st = TrainState(L, V, T, 1, kv_heads=kv_heads)
     st.load_weights(w)
     st.set_windows(windows)
     st.fwd_bwd(_cuda(tok), _cuda(tgt))

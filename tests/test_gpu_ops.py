@@ -109,38 +109,44 @@ def test_gemm_epilogues():
 # ----------------------------------------------------------------------------
 # Attention forward / backward against the oracle (fp64 on the same bf16 inputs)
 # ----------------------------------------------------------------------------
-@pytest.mark.parametrize("B,T,H,W", [(2, 200, 2, -1), (1, 64, 1, -1), (1, 1, 1, -1), (1, 333, 3, -1),
-                                     (1, 1024, 2, -1), (1, 4096, 2, -1),
-                                     # windows: only the diagonal, odd sizes across tile edges,
-                                     # exactly one tile, and the short window of a 4096 sequence
-                                     (2, 200, 2, 0), (1, 333, 3, 37), (1, 300, 2, 63), (1, 300, 2, 64),
-                                     (1, 1000, 1, 129), (1, 1024, 2, 200), (1, 4096, 2, 2048)])
-def test_attention_fwd_bwd(B, T, H, W):
-    log(f"attention B={B} T={T} H={H} window={W}")
+@pytest.mark.parametrize("B,T,H,W,HKV", [(2, 200, 2, -1, 2), (1, 64, 1, -1, 1), (1, 1, 1, -1, 1),
+                                         (1, 333, 3, -1, 3), (1, 1024, 2, -1, 2), (1, 4096, 2, -1, 2),
+                                         # windows: only the diagonal, odd sizes across tile edges,
+                                         # exactly one tile, and the short window of a 4096 sequence
+                                         (2, 200, 2, 0, 2), (1, 333, 3, 37, 3), (1, 300, 2, 63, 2),
+                                         (1, 300, 2, 64, 2), (1, 1000, 1, 129, 1), (1, 1024, 2, 200, 2),
+                                         (1, 4096, 2, 2048, 2),
+                                         # grouped-query attention: groups of 2, 4 and 3 query heads
+                                         (1, 333, 4, -1, 2), (2, 200, 4, 37, 1), (1, 1024, 6, -1, 2),
+                                         (1, 2048, 4, 1024, 2)])
+def test_attention_fwd_bwd(B, T, H, W, HKV):
+    log(f"attention B={B} T={T} H={H} window={W} kv_heads={HKV}")
     rng = np.random.default_rng(T + H)
-    d = H * 128
-    qkv_b, qkv_f = _rand_bf16(rng, (B * T, 3 * d))
+    d, dkv = H * 128, HKV * 128
+    qkv_b, qkv_f = _rand_bf16(rng, (B * T, d + 2 * dkv))
     do_b, do_f = _rand_bf16(rng, (B * T, d))
     qkv = dev(torch, qkv_b)
     o = torch.zeros(B * T, d, dtype=torch.int16, device="cuda")
     lse = torch.zeros(B * H * T, dtype=torch.float32, device="cuda")
-    binding.op_attention_fwd(qkv, o, lse, B, T, H, W)
+    binding.op_attention_fwd(qkv, o, lse, B, T, H, W, kv_heads=HKV)
     dO = dev(torch, do_b)
-    dqkv = torch.zeros(B * T, 3 * d, dtype=torch.int16, device="cuda")
+    dqkv = torch.zeros(B * T, d + 2 * dkv, dtype=torch.int16, device="cuda")
     scratch = torch.zeros(B * H * T, dtype=torch.float32, device="cuda")
-    binding.op_attention_bwd(qkv, o, lse, dO, dqkv, scratch, B, T, H, W)
+    binding.op_attention_bwd(qkv, o, lse, dO, dqkv, scratch, B, T, H, W, kv_heads=HKV)
     torch.cuda.synchronize()
     o_got = bits_to_f32(o.cpu().numpy()).reshape(B, T, H, 128)
     lse_got = lse.cpu().numpy().reshape(B, H, T)
-    dq_got = bits_to_f32(dqkv.cpu().numpy()).reshape(B, T, 3, H, 128)
-    o_bf = bits_to_f32(o.cpu().numpy()).reshape(B, T, H, 128).astype(np.float64)
+    dqkv_got = bits_to_f32(dqkv.cpu().numpy()).reshape(B, T, d + 2 * dkv)
     for b in range(B):
-        blk = qkv_f[b * T:(b + 1) * T].reshape(T, 3, H, 128)
-        q, k, v = blk[:, 0], blk[:, 1], blk[:, 2]
+        blk = qkv_f[b * T:(b + 1) * T]
+        q = blk[:, :d].reshape(T, H, 128)
+        k = blk[:, d:d + dkv].reshape(T, HKV, 128)
+        v = blk[:, d + dkv:].reshape(T, HKV, 128)
         o_ref, p = oracle.causal_attention(q, k, v, None if W < 0 else W)
         assert rel_l2(o_got[b], o_ref) < 1e-2
         # lse: base-2 log of sum_j exp(q.k_j / sqrt(128)) over the visible j.
-        s = np.einsum("ihd,jhd->hij", q, k) / np.sqrt(128.0)
+        kr = np.repeat(k, H // HKV, axis=1)
+        s = np.einsum("ihd,jhd->hij", q, kr) / np.sqrt(128.0)
         vis = np.tril(np.ones((T, T), bool))
         if W >= 0:
             vis &= np.triu(np.ones((T, T), bool), -W)
@@ -152,7 +158,10 @@ def test_attention_fwd_bwd(B, T, H, W):
         # The backward takes the kernel's own o (as the fused kernels do), so
         # the reference gradient is formed with the same o via rowsum(dO * o).
         dq_ref, dk_ref, dv_ref = oracle.causal_attention_bwd(do, q, k, v, p)
-        for got, ref in ((dq_got[b, :, 0], dq_ref), (dq_got[b, :, 1], dk_ref), (dq_got[b, :, 2], dv_ref)):
+        got_q = dqkv_got[b, :, :d].reshape(T, H, 128)
+        got_k = dqkv_got[b, :, d:d + dkv].reshape(T, HKV, 128)
+        got_v = dqkv_got[b, :, d + dkv:].reshape(T, HKV, 128)
+        for got, ref in ((got_q, dq_ref), (got_k, dk_ref), (got_v, dv_ref)):
             if np.linalg.norm(ref) == 0:
                 # Window 0: P is the identity, so dS = 0 exactly in the oracle;
                 # the kernel's dP - delta is a difference of two fp32 sums.

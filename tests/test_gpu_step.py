@@ -23,15 +23,15 @@ LOSS_TOL = 1e-2
 REL_TOL = 2e-2
 
 
-def _run_case(depth, vocab, seq, batch, seed_w=0, seed_t=1, ignore=(), windows=None):
-    log(f"fwd_bwd depth={depth} vocab={vocab} seq={seq} batch={batch} windows={windows}")
-    w = syn.init_weights(depth, vocab, seed=seed_w)
+def _run_case(depth, vocab, seq, batch, seed_w=0, seed_t=1, ignore=(), windows=None, kv_heads=None):
+    log(f"fwd_bwd depth={depth} vocab={vocab} seq={seq} batch={batch} windows={windows} kv_heads={kv_heads}")
+    w = syn.init_weights(depth, vocab, seed=seed_w, kv_heads=kv_heads)
     ids = syn.zipf_ids(batch, seq, vocab, seed=seed_t)
     tok, tgt = syn.split_tokens(ids)
     tgt = tgt.copy()
     for (b, t) in ignore:
         tgt[b, t] = -1
-    st = TrainState(depth, vocab, seq, batch)
+    st = TrainState(depth, vocab, seq, batch, kv_heads=kv_heads)
     st.load_weights(w)
     st.set_windows(windows)
     tok_d = torch.from_numpy(tok).cuda()
@@ -82,6 +82,67 @@ def test_windowed_fwd_bwd_matches_oracle(windows):
     assert st.model.windows() == windows
     assert abs(loss - ref_loss) <= LOSS_TOL
     _assert_grads(grads, ref_grads, tok, cfg["vocab"])
+
+
+@pytest.mark.parametrize("depth,kv_heads,seq,batch,windows", [(4, 1, 64, 2, None), (8, 2, 200, 2, [-1, 50] * 4),
+                                                              (8, 1, 128, 1, None)])
+def test_gqa_fwd_bwd_matches_oracle(depth, kv_heads, seq, batch, windows):
+    """Grouped-query attention through the whole model: 2 query heads on 1
+    key/value head, 4 on 2 (with windows and a ragged length), 4 on 1."""
+    st, tok, tgt, loss, grads, ref_loss, ref_grads = _run_case(depth, 2048, seq, batch, seed_w=3, seed_t=4,
+                                                                windows=windows, kv_heads=kv_heads)
+    assert st.model.kv_heads == kv_heads
+    assert grads["h0.wk"].shape == (128 * kv_heads, st.model.d)
+    assert abs(loss - ref_loss) <= LOSS_TOL
+    _assert_grads(grads, ref_grads, tok, 2048)
+
+
+@pytest.mark.parametrize("normuon", [False, True])
+def test_gqa_muon_matches_oracle(normuon):
+    """Muon / NorMuon on a grouped-query model: wk and wv ([128, 512], wide)
+    form their own Newton-Schulz batch, apart from wq and wo."""
+    depth, vocab, kvh = 8, 2048, 1
+    log(f"gqa {'normuon' if normuon else 'muon'} depth={depth} kv_heads={kvh}")
+    w = syn.init_weights(depth, vocab, seed=0, kv_heads=kvh)
+    g = syn.random_like_grads(depth, vocab, seed=7, scale=1e-2, kv_heads=kvh)
+    st = TrainState(depth, vocab, 64, 1, kv_heads=kvh)
+    st.load_weights(w)
+    st.load_grads(g)
+    f64 = lambda dd: {k: v.astype(np.float64) for k, v in dd.items()}
+    m0 = {k: np.zeros_like(v) for k, v in f64(w).items()}
+    names = [k for k in w if k.startswith("h")]
+    if normuon:
+        st.normuon(syn.MUON_LR, syn.MUON_MOMENTUM, NORMUON_BETA2, syn.NS_COEFFS)
+        v0 = {k: np.zeros(max(w[k].shape)) for k in names}
+        _, _, ref_v, ref_upd = oracle.normuon_step(f64(w), f64(g), m0, v0, syn.MUON_LR, syn.MUON_MOMENTUM,
+                                                   NORMUON_BETA2, syn.NS_COEFFS, names=names)
+    else:
+        st.muon(syn.MUON_LR, syn.MUON_MOMENTUM, syn.NS_COEFFS)
+        _, _, ref_upd = oracle.muon_step(f64(w), f64(g), m0, syn.MUON_LR, syn.MUON_MOMENTUM, syn.NS_COEFFS,
+                                         names=names)
+    torch.cuda.synchronize()
+    new_w = st.to_host(st.params)
+    worst = []
+    for k in names:
+        e = rel_l2(w[k].astype(np.float64) - new_w[k], ref_upd[k])
+        worst.append((e, k))
+        assert e < REL_TOL, (k, e)
+    log("  worst update rel-L2 " + " ".join(f"{k}:{e:.2e}" for e, k in sorted(worst)[-3:]))
+    if normuon:
+        # State layout with kv_heads < H: (wq, wo) per layer, then (wk, wv), then (wfc, wproj).
+        d, f = st.model.d, st.model.mlp
+        state = st.second_moment.cpu().numpy()
+        order = ([f"h{l}.{n}" for l in range(depth) for n in ("wq", "wo")]
+                 + [f"h{l}.{n}" for l in range(depth) for n in ("wk", "wv")]
+                 + [f"h{l}.{n}" for l in range(depth) for n in ("wfc", "wproj")])
+        off = 0
+        for k in order:
+            n = max(w[k].shape)
+            assert rel_l2(state[off:off + n], ref_v[k]) < 1e-3, k
+            off += n
+        assert off == state.size
+    for k in ("wte", "lm_head"):
+        np.testing.assert_array_equal(new_w[k], w[k])
 
 
 def test_ragged_windowed_fwd_bwd():
