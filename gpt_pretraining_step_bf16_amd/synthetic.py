@@ -65,13 +65,15 @@ def model_dims(depth: int) -> dict:
     return dict(depth=depth, d=d, heads=d // HEAD_DIM, mlp=4 * d)
 
 
-def tensor_specs(depth: int, vocab: int, kv_heads=None):
-    """Canonical tensor order: wte; per layer wq, wk, wv, wo, wfc, wproj; lm_head.
+def tensor_specs(depth: int, vocab: int, kv_heads=None, resid_scalars=False, backout=False):
+    """Canonical tensor order: wte; per layer wq, wk, wv, wo, wfc, wproj; lm_head;
+    then the optional scalar tensors resid_lambdas [1, depth], x0_lambdas
+    [1, depth] and backout_lambda [1, 1].
 
     Each entry is (name, rows, cols, kind, layer) with kind in
-    {"emb", "matrix", "lm_head"}; matrices are [out, in] as in a Linear layer.
-    kv_heads (default: every head) sets the rows of wk and wv to kv_heads * 128
-    (grouped-query attention).
+    {"emb", "matrix", "lm_head", "scalar"}; matrices are [out, in] as in a
+    Linear layer. kv_heads (default: every head) sets the rows of wk and wv to
+    kv_heads * 128 (grouped-query attention).
     """
     dm = model_dims(depth)
     d, f = dm["d"], dm["mlp"]
@@ -87,14 +89,28 @@ def tensor_specs(depth: int, vocab: int, kv_heads=None):
             (f"h{layer}.wproj", d, f, "matrix", layer),
         ]
     specs.append(("lm_head", vocab, d, "lm_head", -1))
+    if resid_scalars:
+        specs += [("resid_lambdas", 1, depth, "scalar", -1), ("x0_lambdas", 1, depth, "scalar", -1)]
+    if backout:
+        specs.append(("backout_lambda", 1, 1, "scalar", -1))
     return specs
 
 
-def init_weights(depth: int, vocab: int, seed: int = 0, std: float = INIT_STD, kv_heads=None) -> dict:
-    """Every tensor N(0, std^2), float32, drawn in canonical order from one seed."""
+# Start values of the scalar tensors: the plain residual stream (no x0 mix, no
+# backout). The pages give none; tests set other values explicitly.
+SCALAR_INIT = {"resid_lambdas": 1.0, "x0_lambdas": 0.0, "backout_lambda": 0.0}
+
+
+def init_weights(depth: int, vocab: int, seed: int = 0, std: float = INIT_STD, kv_heads=None,
+                 resid_scalars=False, backout=False) -> dict:
+    """Every matrix N(0, std^2), float32, drawn in canonical order from one seed;
+    scalar tensors take SCALAR_INIT (no draw)."""
     rng = np.random.default_rng(seed)
     out = {}
-    for name, rows, cols, _kind, _layer in tensor_specs(depth, vocab, kv_heads):
+    for name, rows, cols, kind, _layer in tensor_specs(depth, vocab, kv_heads, resid_scalars, backout):
+        if kind == "scalar":
+            out[name] = np.full((rows, cols), SCALAR_INIT[name], dtype=np.float32)
+            continue
         w = rng.standard_normal((rows, cols), dtype=np.float32)
         w *= np.float32(std)
         out[name] = w
@@ -123,11 +139,12 @@ def split_tokens(ids: np.ndarray):
     return np.ascontiguousarray(ids[:, :-1]), np.ascontiguousarray(ids[:, 1:])
 
 
-def random_like_grads(depth: int, vocab: int, seed: int, scale: float = 1e-3, kv_heads=None) -> dict:
+def random_like_grads(depth: int, vocab: int, seed: int, scale: float = 1e-3, kv_heads=None,
+                      resid_scalars=False, backout=False) -> dict:
     """Seeded Gaussian arrays shaped like the parameters (for optimizer-only cases)."""
     rng = np.random.default_rng(seed)
     out = {}
-    for name, rows, cols, _kind, _layer in tensor_specs(depth, vocab, kv_heads):
+    for name, rows, cols, _kind, _layer in tensor_specs(depth, vocab, kv_heads, resid_scalars, backout):
         g = rng.standard_normal((rows, cols), dtype=np.float32)
         g *= np.float32(scale)
         out[name] = g

@@ -29,6 +29,12 @@ Window attention (optional, per layer): the pages list alternating short and
 long attention windows but give no sizes, so the windows are an input; a
 window W lets query i see keys i - W .. i.
 
+Residual scalars (optional): with tensors resid_lambdas and x0_lambdas [1, L],
+block i reads resid_lambdas[i] * x + x0_lambdas[i] * x0 (x0 the embedding
+output) as its input stream; with backout_lambda [1, 1] and a backout layer k,
+backout_lambda times the stream entering block k is subtracted before the
+final norm. The pages print these two lines and nothing around them.
+
 Grouped-query attention (optional): the pages list "fewer KV heads". When wk
 and wv have Hkv * 128 rows (Hkv dividing H), query head h attends with key and
 value head h // (H / Hkv); QK-norm and RoPE act per head as before.
@@ -165,21 +171,42 @@ def _layer_window(windows, layer):
     return None if windows is None else windows[layer]
 
 
-def _forward_sequence(weights, tok, cos, sin, final_norm=True, windows=None):
+def _scalars(weights):
+    """Per-layer residual scalars and the backout scalar, when the model has them."""
+    rl = weights["resid_lambdas"][0] if "resid_lambdas" in weights else None
+    xl = weights["x0_lambdas"][0] if "x0_lambdas" in weights else None
+    bl = float(weights["backout_lambda"][0, 0]) if "backout_lambda" in weights else None
+    return rl, xl, bl
+
+
+def _forward_sequence(weights, tok, cos, sin, final_norm=True, windows=None, backout_layer=None):
     """Forward pass of one sequence; returns the logits and the saved values.
 
     windows: None, or one attention window per layer (an int, or None for the
     full causal context).
+    Residual scalars ([CT50] "Truques de Eficiência", items 1 and 3), when the
+    weights hold them: before block i the stream becomes
+    resid_lambdas[i] * x + x0_lambdas[i] * x0, x0 being the embedding output;
+    with backout_layer k, the stream entering block k (after its mix) is kept
+    and backout_lambda times it is subtracted before the final norm.
     """
     L = _depth(weights)
     wte = weights["wte"]
     d = wte.shape[1]
     H = d // HEAD_DIM
     T = tok.shape[0]
+    rl, xl, bl = _scalars(weights)
     x = wte[tok]
+    x0 = x
+    x_backout = None
     layers = []
     for layer in range(L):
         w = {n: weights[f"h{layer}.{n}"] for n in ("wq", "wk", "wv", "wo", "wfc", "wproj")}
+        x_prev = x
+        if rl is not None:
+            x = rl[layer] * x + xl[layer] * x0
+        if backout_layer == layer:
+            x_backout = x
         xn1, r1 = rms_norm(x)
         q = (xn1 @ w["wq"].T).reshape(T, H, HEAD_DIM)
         k = (xn1 @ w["wk"].T).reshape(T, -1, HEAD_DIM)
@@ -195,22 +222,24 @@ def _forward_sequence(weights, tok, cos, sin, final_norm=True, windows=None):
         a = np.maximum(u, 0.0) ** 2
         x = x_mid + a @ w["wproj"].T
         layers.append(dict(xn1=xn1, r1=r1, qn=qn, rq=rq, kn=kn, rk=rk, qr=qr, kr=kr,
-                           v=v, p=p, o2=o2, xn2=xn2, r2=r2, u=u, a=a))
+                           v=v, p=p, o2=o2, xn2=xn2, r2=r2, u=u, a=a, x_prev=x_prev))
+    if backout_layer is not None:
+        x = x - bl * x_backout
     if final_norm:
         xnf, rf = rms_norm(x)
     else:
         xnf, rf = x, None
     z = xnf @ weights["lm_head"].T
-    return z, dict(layers=layers, xnf=xnf, rf=rf)
+    return z, dict(layers=layers, xnf=xnf, rf=rf, x0=x0, x_backout=x_backout)
 
 
-def forward_logits(weights, tokens, final_norm=True, windows=None):
+def forward_logits(weights, tokens, final_norm=True, windows=None, backout_layer=None):
     """Logits [B, T, V] for int tokens [B, T] (no loss, no gradients)."""
     tokens = np.asarray(tokens)
     T = tokens.shape[1]
     dt = weights["wte"].dtype
     cos, sin = rope_tables(T, dtype=dt)
-    return np.stack([_forward_sequence(weights, tokens[b], cos, sin, final_norm, windows)[0]
+    return np.stack([_forward_sequence(weights, tokens[b], cos, sin, final_norm, windows, backout_layer)[0]
                      for b in range(tokens.shape[0])])
 
 
@@ -226,10 +255,14 @@ def per_position_loss(weights, tokens, targets, final_norm=True, windows=None):
     return out
 
 
-def forward_backward(weights, tokens, targets, final_norm=True, want_grads=True, windows=None):
+def forward_backward(weights, tokens, targets, final_norm=True, want_grads=True, windows=None,
+                     backout_layer=None):
     """Mean cross-entropy loss and the gradient of every tensor.
 
     windows: None, or one attention window per layer (see causal_attention).
+    backout_layer: the layer whose input stream the backout subtracts (the
+    weights then hold backout_lambda); residual scalars apply when the weights
+    hold resid_lambdas and x0_lambdas (see _forward_sequence).
 
     Sequences are independent, so the batch is processed one row at a time and
     the per-row contributions are summed (this bounds memory; it is exact).
@@ -248,7 +281,7 @@ def forward_backward(weights, tokens, targets, final_norm=True, want_grads=True,
     H = d // HEAD_DIM
     for b in range(B):
         tok, tgt = tokens[b], targets[b]
-        z, c = _forward_sequence(weights, tok, cos, sin, final_norm, windows)
+        z, c = _forward_sequence(weights, tok, cos, sin, final_norm, windows, backout_layer)
         lse = log_softmax_rows(z)
         valid = tgt >= 0
         t = np.where(valid, tgt, 0)
@@ -264,6 +297,12 @@ def forward_backward(weights, tokens, targets, final_norm=True, want_grads=True,
         dx = dz @ weights["lm_head"]
         if final_norm:
             dx = rms_norm_bwd(dx, c["xnf"], c["rf"])
+        rl, xl, bl = _scalars(weights)
+        if backout_layer is not None:
+            # x_final = x_L - bl * x_backout
+            grads["backout_lambda"][0, 0] -= float(np.sum(dx * c["x_backout"]))
+            d_backout = -bl * dx
+        dx0 = np.zeros_like(dx)
         for layer in reversed(range(L)):
             s = c["layers"][layer]
             w = {n: weights[f"h{layer}.{n}"] for n in ("wq", "wk", "wv", "wo", "wfc", "wproj")}
@@ -286,6 +325,15 @@ def forward_backward(weights, tokens, targets, final_norm=True, want_grads=True,
             grads[g["wv"]] += dv.T @ s["xn1"]
             dxn1 = dq @ w["wq"] + dk @ w["wk"] + dv @ w["wv"]
             dx = dx_mid + rms_norm_bwd(dxn1, s["xn1"], s["r1"])
-        np.add.at(grads["wte"], tok, dx)
+            # dx is now the gradient of the stream entering block `layer`.
+            if backout_layer == layer:
+                dx = dx + d_backout
+            if rl is not None:
+                # x_in = rl * x_prev + xl * x0
+                grads["resid_lambdas"][0, layer] += float(np.sum(dx * s["x_prev"]))
+                grads["x0_lambdas"][0, layer] += float(np.sum(dx * c["x0"]))
+                dx0 += xl[layer] * dx
+                dx = rl[layer] * dx
+        np.add.at(grads["wte"], tok, dx + dx0)
     loss = loss_sum / n_valid if n_valid else 0.0
     return loss, grads

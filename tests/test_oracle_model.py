@@ -235,6 +235,79 @@ def test_windowed_model_matches_full_model_until_the_window_binds():
 
 
 # ----------------------------------------------------------------------------
+# Residual scalars and backout
+# ----------------------------------------------------------------------------
+def _scalar_weights(depth, vocab, seed, std, rng_seed, backout=True):
+    w = syn.init_weights(depth, vocab, seed=seed, std=std, resid_scalars=True, backout=backout)
+    w = {k: v.astype(np.float64) for k, v in w.items()}
+    rng = np.random.default_rng(rng_seed)
+    w["resid_lambdas"] = rng.uniform(0.5, 1.5, size=(1, depth))
+    w["x0_lambdas"] = rng.uniform(-0.5, 0.5, size=(1, depth))
+    if backout:
+        w["backout_lambda"] = np.array([[rng.uniform(0.1, 0.6)]])
+    return w
+
+
+def test_identity_scalars_equal_the_plain_model():
+    depth, vocab, seq = 3, 128, 10
+    w = _tiny_weights(depth, vocab, seed=4, std=0.1)
+    ws = dict(w)
+    ws.update({k: v.astype(np.float64) for k, v in syn.init_weights(
+        depth, vocab, resid_scalars=True, backout=True).items() if k not in w})
+    tok, tgt = _ids(2, seq, vocab, seed=6)
+    loss, grads = oracle.forward_backward(w, tok, tgt)
+    loss_s, grads_s = oracle.forward_backward(ws, tok, tgt, backout_layer=1)
+    assert loss_s == loss
+    for k in grads:
+        np.testing.assert_array_equal(grads_s[k], grads[k])
+
+
+def test_scalars_with_zero_blocks_scale_the_embedding():
+    # With wo = wproj = 0 the blocks add nothing, so the stream is
+    # x_(i+1) = rl_i x_i + xl_i x0 (alpha_(i+1) = rl_i alpha_i + xl_i, alpha_0 = 1)
+    # and the head sees (alpha_L - bl alpha_k) x0, with alpha_k the mixed stream
+    # entering block k: the plain model with wte scaled by that factor.
+    depth, vocab, seq, k = 4, 128, 9, 2
+    w = _scalar_weights(depth, vocab, seed=5, std=0.1, rng_seed=9)
+    for l in range(depth):
+        w[f"h{l}.wo"] = np.zeros_like(w[f"h{l}.wo"])
+        w[f"h{l}.wproj"] = np.zeros_like(w[f"h{l}.wproj"])
+    alpha, alpha_k = 1.0, None
+    for l in range(depth):
+        alpha = w["resid_lambdas"][0, l] * alpha + w["x0_lambdas"][0, l]
+        if l == k:
+            alpha_k = alpha
+    scale = alpha - w["backout_lambda"][0, 0] * alpha_k
+    plain = {n: v for n, v in w.items() if n not in syn.SCALAR_INIT}
+    plain["wte"] = w["wte"] * scale
+    tok, _ = _ids(1, seq, vocab, seed=3)
+    np.testing.assert_allclose(oracle.forward_logits(w, tok, backout_layer=k),
+                               oracle.forward_logits(plain, tok), rtol=1e-11, atol=1e-13)
+
+
+@pytest.mark.parametrize("backout_layer", [None, 0, 2])
+def test_scalar_gradients_match_central_differences(backout_layer):
+    depth, vocab, seq, batch = 3, 96, 10, 2
+    w = _scalar_weights(depth, vocab, seed=3, std=0.15, rng_seed=4, backout=backout_layer is not None)
+    tok, tgt = _ids(batch, seq, vocab, seed=5)
+    loss, grads = oracle.forward_backward(w, tok, tgt, backout_layer=backout_layer)
+    rng = np.random.default_rng(12)
+    h = 1e-5
+
+    def f(ww):
+        return oracle.forward_backward(ww, tok, tgt, want_grads=False, backout_layer=backout_layer)[0]
+
+    for name in w:
+        u = rng.standard_normal(w[name].shape)
+        u /= np.linalg.norm(u)
+        wp = dict(w); wp[name] = w[name] + h * u
+        wm = dict(w); wm[name] = w[name] - h * u
+        fd = (f(wp) - f(wm)) / (2 * h)
+        an = float(np.sum(grads[name] * u))
+        assert abs(fd - an) <= 1e-6 * abs(an) + 1e-9, (name, fd, an)
+
+
+# ----------------------------------------------------------------------------
 # Grouped-query attention: equal to full multi-head attention whose key/value
 # weights repeat each group's rows (an independent path: no head sharing)
 # ----------------------------------------------------------------------------
