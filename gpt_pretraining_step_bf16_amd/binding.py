@@ -15,7 +15,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgptstep.so")
 
 GPT_OK, GPT_EINVAL, GPT_ESHAPE, GPT_EHIP, GPT_ETOKEN, GPT_EWORKSPACE = 0, -1, -2, -3, -4, -5
-KIND_NAMES = {0: "emb", 1: "matrix", 2: "lm_head"}
+KIND_NAMES = {0: "emb", 1: "matrix", 2: "lm_head", 3: "scalar"}
 
 # gpt_op_gemm out_mode values
 OUT_F32, OUT_F32_ACC, OUT_BF16, OUT_RELU_BF16, OUT_RESID_BF16 = 0, 1, 2, 3, 4
@@ -29,6 +29,17 @@ class GptTensor(C.Structure):
         ("cols", C.c_int32),
         ("kind", C.c_int32),
         ("layer", C.c_int32),
+    ]
+
+
+class GptConfig(C.Structure):
+    _fields_ = [
+        ("depth", C.c_int32),
+        ("vocab", C.c_int32),
+        ("max_seq", C.c_int32),
+        ("kv_heads", C.c_int32),
+        ("resid_scalars", C.c_int32),
+        ("backout_layer", C.c_int32),
     ]
 
 
@@ -56,6 +67,8 @@ EXPORTS = {
     "gpt_create": (C.c_int, [_I, _I, _I, C.POINTER(_P)]),
     "gpt_create_gqa": (C.c_int, [_I, _I, _I, _I, C.POINTER(_P)]),
     "gpt_kv_heads": (C.c_int32, [_P]),
+    "gpt_create_config": (C.c_int, [C.POINTER(GptConfig), C.POINTER(_P)]),
+    "gpt_backout_layer": (C.c_int32, [_P]),
     "gpt_destroy": (None, [_P]),
     "gpt_dims": (C.c_int, [_P, C.POINTER(C.c_int32)]),
     "gpt_num_params": (C.c_int64, [_P]),
@@ -133,17 +146,25 @@ def _coeffs(table):
 class GptModel:
     """Host-side plan of a model (no device memory)."""
 
-    def __init__(self, depth: int, vocab: int, max_seq: int, kv_heads=None):
+    def __init__(self, depth: int, vocab: int, max_seq: int, kv_heads=None, resid_scalars=False,
+                 backout_layer=None):
         h = C.c_void_p()
-        if kv_heads is None:
-            _check(lib().gpt_create(depth, vocab, max_seq, C.byref(h)), "gpt_create")
+        if not resid_scalars and backout_layer is None:
+            if kv_heads is None:
+                _check(lib().gpt_create(depth, vocab, max_seq, C.byref(h)), "gpt_create")
+            else:
+                _check(lib().gpt_create_gqa(depth, vocab, max_seq, int(kv_heads), C.byref(h)), "gpt_create_gqa")
         else:
-            _check(lib().gpt_create_gqa(depth, vocab, max_seq, int(kv_heads), C.byref(h)), "gpt_create_gqa")
+            cfg = GptConfig(depth, vocab, max_seq, 0 if kv_heads is None else int(kv_heads),
+                            1 if resid_scalars else 0, -1 if backout_layer is None else int(backout_layer))
+            _check(lib().gpt_create_config(C.byref(cfg), C.byref(h)), "gpt_create_config")
         self._h = h
         dims = (C.c_int32 * 6)()
         _check(lib().gpt_dims(h, dims), "gpt_dims")
         self.depth, self.d, self.heads, self.mlp, self.vocab, self.max_seq = list(dims)
         self.kv_heads = int(lib().gpt_kv_heads(h))
+        bl = int(lib().gpt_backout_layer(h))
+        self.backout_layer = None if bl < 0 else bl
 
     def close(self):
         if getattr(self, "_h", None):

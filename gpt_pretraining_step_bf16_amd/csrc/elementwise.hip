@@ -655,6 +655,145 @@ __global__ void normuon_scale_kernel(const MuonGroup g, float* __restrict__ rs,
   for (long r = threadIdx.x; r < xr; r += blockDim.x) rs[(long)j * xr + r] *= ratio;
 }
 
+// ---------------------------------------------------------------------------
+// Residual scalars and backout ([CT50] "Truques de Eficiência", items 1 and
+// 3). The scalars are read from the bf16 weight copy the step computes with.
+// ---------------------------------------------------------------------------
+// Before block i: x_prev <- x; x <- a x + b x0 (a = resid_lambdas[i],
+// b = x0_lambdas[i]). n4 float4 groups.
+__global__ void resid_mix_fwd_kernel(float* __restrict__ x, const float* __restrict__ x0,
+                                     float* __restrict__ x_prev, const uint16_t* __restrict__ pa,
+                                     const uint16_t* __restrict__ pb, long n4) {
+  const float a = bf2f(*pa), b = bf2f(*pb);
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n4; i += (long)gridDim.x * blockDim.x) {
+    const float4 v = reinterpret_cast<const float4*>(x)[i];
+    const float4 z = reinterpret_cast<const float4*>(x0)[i];
+    reinterpret_cast<float4*>(x_prev)[i] = v;
+    reinterpret_cast<float4*>(x)[i] =
+        make_float4(a * v.x + b * z.x, a * v.y + b * z.y, a * v.z + b * z.z, a * v.w + b * z.w);
+  }
+}
+
+// y <- y + c * x over n4 float4 groups, c = scale * (bf16 scalar at pc, or 1
+// when pc is null).
+__global__ void axpy_f32_kernel(float* __restrict__ y, const float* __restrict__ x,
+                                const uint16_t* __restrict__ pc, float scale, long n4) {
+  const float c = scale * (pc ? bf2f(*pc) : 1.f);
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n4; i += (long)gridDim.x * blockDim.x) {
+    float4 v = reinterpret_cast<float4*>(y)[i];
+    const float4 u = reinterpret_cast<const float4*>(x)[i];
+    v.x += c * u.x;
+    v.y += c * u.y;
+    v.z += c * u.z;
+    v.w += c * u.w;
+    reinterpret_cast<float4*>(y)[i] = v;
+  }
+}
+
+// Fixed-order block sum of two values; thread 0 writes both to out[blockIdx.x].
+__device__ __forceinline__ void block_sum2(float s0, float s1, float2* out) {
+  __shared__ float red[2][4];
+  s0 = warp_sum(s0);
+  s1 = warp_sum(s1);
+  if ((threadIdx.x & 63) == 0) {
+    red[0][threadIdx.x >> 6] = s0;
+    red[1][threadIdx.x >> 6] = s1;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0)
+    out[blockIdx.x] = make_float2(red[0][0] + red[0][1] + red[0][2] + red[0][3],
+                                  red[1][0] + red[1][1] + red[1][2] + red[1][3]);
+}
+
+// Backward of the mix before block i, with g = dx (gradient of the mixed
+// stream): partial sums of g . x_prev (d a) and g . x0 (d b); dx0 += b g;
+// dx <- a g and its bf16 copy. 256 threads per block; partials[blockIdx.x].
+__global__ void __launch_bounds__(256) resid_mix_bwd_kernel(float* __restrict__ dx, uint16_t* __restrict__ dxb,
+                                                            const float* __restrict__ x_prev,
+                                                            const float* __restrict__ x0, float* __restrict__ dx0,
+                                                            const uint16_t* __restrict__ pa,
+                                                            const uint16_t* __restrict__ pb, long n4,
+                                                            float2* __restrict__ partials) {
+  const float a = bf2f(*pa), b = bf2f(*pb);
+  float s0 = 0.f, s1 = 0.f;
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n4; i += (long)gridDim.x * blockDim.x) {
+    const float4 g = reinterpret_cast<const float4*>(dx)[i];
+    const float4 xp = reinterpret_cast<const float4*>(x_prev)[i];
+    const float4 z = reinterpret_cast<const float4*>(x0)[i];
+    float4 d0 = reinterpret_cast<float4*>(dx0)[i];
+    s0 += g.x * xp.x + g.y * xp.y + g.z * xp.z + g.w * xp.w;
+    s1 += g.x * z.x + g.y * z.y + g.z * z.z + g.w * z.w;
+    d0.x += b * g.x;
+    d0.y += b * g.y;
+    d0.z += b * g.z;
+    d0.w += b * g.w;
+    reinterpret_cast<float4*>(dx0)[i] = d0;
+    const float o[4] = {a * g.x, a * g.y, a * g.z, a * g.w};
+    reinterpret_cast<float4*>(dx)[i] = make_float4(o[0], o[1], o[2], o[3]);
+    reinterpret_cast<uint2*>(dxb)[i] = make_uint2(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]));
+  }
+  block_sum2(s0, s1, partials);
+}
+
+// Backout, top of the backward (g = dx, gradient of the final stream):
+// partial sums of g . x_backout; keep dback <- g.
+__global__ void __launch_bounds__(256) backout_bwd_kernel(const float* __restrict__ dx,
+                                                          const float* __restrict__ xbo, float* __restrict__ dback,
+                                                          long n4, float2* __restrict__ partials) {
+  float s0 = 0.f;
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n4; i += (long)gridDim.x * blockDim.x) {
+    const float4 g = reinterpret_cast<const float4*>(dx)[i];
+    const float4 v = reinterpret_cast<const float4*>(xbo)[i];
+    s0 += g.x * v.x + g.y * v.y + g.z * v.z + g.w * v.w;
+    reinterpret_cast<float4*>(dback)[i] = g;
+  }
+  block_sum2(s0, 0.f, partials);
+}
+
+// At the backout block: dx += -c dback (c = backout_lambda) and refresh dxb.
+__global__ void backout_add_kernel(float* __restrict__ dx, uint16_t* __restrict__ dxb,
+                                   const float* __restrict__ dback, const uint16_t* __restrict__ pc, long n4) {
+  const float c = -bf2f(*pc);
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n4; i += (long)gridDim.x * blockDim.x) {
+    float4 v = reinterpret_cast<float4*>(dx)[i];
+    const float4 u = reinterpret_cast<const float4*>(dback)[i];
+    const float o[4] = {v.x + c * u.x, v.y + c * u.y, v.z + c * u.z, v.w + c * u.w};
+    reinterpret_cast<float4*>(dx)[i] = make_float4(o[0], o[1], o[2], o[3]);
+    reinterpret_cast<uint2*>(dxb)[i] = make_uint2(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]));
+  }
+}
+
+// Scalar gradients from the partials, summed in block order by one thread
+// per output: out0 (+)= sign0 * sum .x, out1 (+)= sign1 * sum .y (out1 may be
+// null).
+__global__ void scalar_grads_kernel(const float2* __restrict__ partials, int nb, float* out0, float sign0,
+                                    float* out1, float sign1, int accumulate) {
+  if (threadIdx.x > 1) return;
+  float* out = threadIdx.x == 0 ? out0 : out1;
+  if (!out) return;
+  float t = 0.f;
+  for (int i = 0; i < nb; ++i) t += threadIdx.x == 0 ? partials[i].x : partials[i].y;
+  t *= threadIdx.x == 0 ? sign0 : sign1;
+  *out = accumulate ? *out + t : t;
+}
+
+// AdamW on a small contiguous fp32 tensor (the scalars), one element per
+// thread, no alignment assumed; same update as adamw_kernel.
+__global__ void adamw_small_kernel(float* __restrict__ w, uint16_t* __restrict__ wb, const float* __restrict__ g,
+                                   float* __restrict__ m, float* __restrict__ v, long n, float lr, float b1,
+                                   float b2, float eps, float wd, float bc1, float bc2) {
+  const long i = blockIdx.x * (long)blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float gv = g[i];
+  const float mv = b1 * m[i] + (1.f - b1) * gv;
+  const float vv = b2 * v[i] + (1.f - b2) * (gv * gv);
+  m[i] = mv;
+  v[i] = vv;
+  const float wv = w[i] - lr * wd * w[i] - lr * (mv / bc1) / (sqrtf(vv / bc2) + eps);
+  w[i] = wv;
+  wb[i] = (uint16_t)f2bf(wv);
+}
+
 // AdamW on one contiguous fp32 tensor and its moments ([CT50] "2. Otimizador
 // Muon": embeddings and lm_head are in the AdamW group). Decoupled decay scaled
 // by lr and taken from the weights before the step; bias corrections
@@ -912,5 +1051,59 @@ hipError_t launch_ns_prepare(float* x32, uint16_t* xh, uint16_t* xl, int count, 
 
 hipError_t launch_split_hilo(const float* x32, uint16_t* xh, uint16_t* xl, long n, hipStream_t s) {
   hipLaunchKernelGGL(split_hilo_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, x32, xh, xl, n);
+  return hipGetLastError();
+}
+
+// ---- residual scalars and backout
+namespace {
+constexpr int kRedBlocks = 1024;  // blocks of the two-value reductions (partials buffer size)
+}
+int resid_partials_count() { return kRedBlocks; }
+
+hipError_t launch_resid_mix_fwd(float* x, const float* x0, float* x_prev, const uint16_t* pa, const uint16_t* pb,
+                                long n, hipStream_t s) {
+  hipLaunchKernelGGL(resid_mix_fwd_kernel, dim3(grid_for(n / 4, 256)), dim3(256), 0, s, x, x0, x_prev, pa, pb,
+                     n / 4);
+  return hipGetLastError();
+}
+
+hipError_t launch_axpy_f32(float* y, const float* x, const uint16_t* pc, float scale, long n, hipStream_t s) {
+  hipLaunchKernelGGL(axpy_f32_kernel, dim3(grid_for(n / 4, 256)), dim3(256), 0, s, y, x, pc, scale, n / 4);
+  return hipGetLastError();
+}
+
+hipError_t launch_resid_mix_bwd(float* dx, uint16_t* dxb, const float* x_prev, const float* x0, float* dx0,
+                                const uint16_t* pa, const uint16_t* pb, long n, float2* partials, float* ga,
+                                float* gb, int accumulate, hipStream_t s) {
+  hipLaunchKernelGGL(resid_mix_bwd_kernel, dim3(kRedBlocks), dim3(256), 0, s, dx, dxb, x_prev, x0, dx0, pa, pb,
+                     n / 4, partials);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(scalar_grads_kernel, dim3(1), dim3(64), 0, s, static_cast<const float2*>(partials),
+                     kRedBlocks, ga, 1.f, gb, 1.f, accumulate);
+  return hipGetLastError();
+}
+
+hipError_t launch_backout_bwd(const float* dx, const float* xbo, float* dback, long n, float2* partials,
+                              float* gc, int accumulate, hipStream_t s) {
+  hipLaunchKernelGGL(backout_bwd_kernel, dim3(kRedBlocks), dim3(256), 0, s, dx, xbo, dback, n / 4, partials);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(scalar_grads_kernel, dim3(1), dim3(64), 0, s, static_cast<const float2*>(partials),
+                     kRedBlocks, gc, -1.f, static_cast<float*>(nullptr), 0.f, accumulate);
+  return hipGetLastError();
+}
+
+hipError_t launch_backout_add(float* dx, uint16_t* dxb, const float* dback, const uint16_t* pc, long n,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(backout_add_kernel, dim3(grid_for(n / 4, 256)), dim3(256), 0, s, dx, dxb, dback, pc, n / 4);
+  return hipGetLastError();
+}
+
+hipError_t launch_adamw_small(float* w, uint16_t* wb, const float* g, float* m, float* v, long n, float lr,
+                              float b1, float b2, float eps, float wd, float bc1, float bc2, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(adamw_small_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, w, wb, g, m, v, n, lr,
+                     b1, b2, eps, wd, bc1, bc2);
   return hipGetLastError();
 }

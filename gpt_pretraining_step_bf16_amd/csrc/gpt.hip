@@ -33,6 +33,10 @@ struct ProfSlot {
 struct gpt_model {
   int depth = 0, d = 0, H = 0, F = 0, V = 0, max_seq = 0;
   int Hkv = 0, dkv = 0;  // key/value heads (Hkv < H: grouped-query attention) and their width
+  // Residual scalars and backout: element offsets of resid_lambdas [L],
+  // x0_lambdas [L], backout_lambda (-1 when absent); the backout layer.
+  int64_t off_rl = -1, off_xl = -1, off_bl = -1, off_scalars = -1, n_scalars = 0;
+  int backout_layer = -1;
   std::vector<gpt_tensor> tensors;
   int64_t nparams = 0;
   int64_t off_wte = 0, off_layer0 = 0, layer_stride = 0, off_lm = 0;
@@ -124,6 +128,8 @@ struct FwdPlan {
   size_t layer_bytes = 0;
   size_t x = 0, xnf = 0, rstdf = 0, dx = 0, dxb = 0, dxn = 0, du = 0, dO = 0, delta = 0, dqkv = 0;
   size_t logits = 0, loss_rows = 0, part = 0;
+  // residual scalars / backout (0 when the model has none)
+  size_t x0 = 0, dx0 = 0, red = 0, xprev = 0, xbo = 0, dback = 0;
   long nc = 0;       // CE chunk rows
   size_t part_bytes = 0;
   size_t total = 0;
@@ -213,6 +219,16 @@ FwdPlan plan_fwd(const gpt_model& m, int B, int T) {
   p.nc = std::min<long>(N, cap_rows);
   p.logits = c.take((size_t)p.nc * V * 2);
   p.loss_rows = c.take(N * 4);
+  if (m.off_rl >= 0 || m.off_bl >= 0) {
+    p.x0 = c.take(N * d * 4);
+    p.dx0 = c.take(N * d * 4);
+    p.red = c.take((size_t)resid_partials_count() * 8);
+  }
+  if (m.off_rl >= 0) p.xprev = c.take((size_t)m.depth * N * d * 4);
+  if (m.off_bl >= 0) {
+    p.xbo = c.take(N * d * 4);
+    p.dback = c.take(N * d * 4);
+  }
   size_t part = 0;
   const long shapes[4][2] = {{Q, d}, {d, d}, {F, d}, {d, F}};
   for (auto& sh : shapes) {
@@ -491,8 +507,26 @@ gpt_status gpt_create(int32_t depth, int32_t vocab, int32_t max_seq, gpt_model**
 }
 
 gpt_status gpt_create_gqa(int32_t depth, int32_t vocab, int32_t max_seq, int32_t kv_heads, gpt_model** out) {
+  gpt_config c{};
+  c.depth = depth;
+  c.vocab = vocab;
+  c.max_seq = max_seq;
+  c.kv_heads = kv_heads;
+  c.resid_scalars = 0;
+  c.backout_layer = -1;
+  return gpt_create_config(&c, out);
+}
+
+gpt_status gpt_create_config(const gpt_config* cfg, gpt_model** out) {
   if (!out) return GPT_EINVAL;
+  if (!cfg) {
+    *out = nullptr;
+    return GPT_EINVAL;
+  }
+  const int32_t depth = cfg->depth, vocab = cfg->vocab, max_seq = cfg->max_seq, kv_heads = cfg->kv_heads;
   *out = nullptr;
+  if (cfg->resid_scalars != 0 && cfg->resid_scalars != 1) return GPT_EINVAL;
+  if (cfg->backout_layer < -1 || cfg->backout_layer >= depth) return GPT_EINVAL;
   if (depth < 1 || depth > 64) return GPT_EINVAL;
   if (vocab < 64 || vocab > 262144 || vocab % 64 != 0) return GPT_EINVAL;
   if (max_seq < 1 || max_seq > 16384) return GPT_EINVAL;
@@ -538,6 +572,19 @@ gpt_status gpt_create_gqa(int32_t depth, int32_t vocab, int32_t max_seq, int32_t
   m->layer_stride = 2 * d * d + 2 * dkv * d + 2 * F * d;
   m->off_lm = off;
   add("lm_head", vocab, (int32_t)d, GPT_KIND_LM_HEAD, -1);
+  m->off_scalars = off;
+  if (cfg->resid_scalars) {
+    m->off_rl = off;
+    add("resid_lambdas", 1, depth, GPT_KIND_SCALAR, -1);
+    m->off_xl = off;
+    add("x0_lambdas", 1, depth, GPT_KIND_SCALAR, -1);
+  }
+  if (cfg->backout_layer >= 0) {
+    m->backout_layer = cfg->backout_layer;
+    m->off_bl = off;
+    add("backout_lambda", 1, 1, GPT_KIND_SCALAR, -1);
+  }
+  m->n_scalars = off - m->off_scalars;
   m->nparams = off;
   *out = m;
   return GPT_OK;
@@ -557,6 +604,7 @@ gpt_status gpt_dims(const gpt_model* m, int32_t dims[6]) {
 }
 
 int32_t gpt_kv_heads(const gpt_model* m) { return m ? m->Hkv : 0; }
+int32_t gpt_backout_layer(const gpt_model* m) { return m ? m->backout_layer : -1; }
 
 int64_t gpt_num_params(const gpt_model* m) { return m ? m->nparams : 0; }
 int32_t gpt_num_tensors(const gpt_model* m) { return m ? (int32_t)m->tensors.size() : 0; }
@@ -615,6 +663,17 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
   HIP_TRY(launch_rope_table(cs, T, s));
   HIP_TRY(launch_count_targets(targets, N, V, n_valid, err, s));
   HIP_TRY(launch_embed_fwd(tokens, wte, x, err, N, d, V, s));
+  const long Nd = N * d;
+  float* x0 = p.x0 ? reinterpret_cast<float*>(ws + p.x0) : nullptr;
+  float* dx0 = p.dx0 ? reinterpret_cast<float*>(ws + p.dx0) : nullptr;
+  float2* red = p.red ? reinterpret_cast<float2*>(ws + p.red) : nullptr;
+  float* xbo = p.xbo ? reinterpret_cast<float*>(ws + p.xbo) : nullptr;
+  float* dback = p.dback ? reinterpret_cast<float*>(ws + p.dback) : nullptr;
+  auto xprev = [&](int l) { return reinterpret_cast<float*>(ws + p.xprev) + (size_t)l * Nd; };
+  const uint16_t* prl = m->off_rl >= 0 ? pbf + m->off_rl : nullptr;
+  const uint16_t* pxl = m->off_xl >= 0 ? pbf + m->off_xl : nullptr;
+  const uint16_t* pbl = m->off_bl >= 0 ? pbf + m->off_bl : nullptr;
+  if (x0) HIP_TRY(hipMemcpyAsync(x0, x, Nd * 4, hipMemcpyDeviceToDevice, s));
 
   // ---- forward through the blocks
   for (int l = 0; l < L; ++l) {
@@ -632,6 +691,9 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
     uint16_t* xn2 = reinterpret_cast<uint16_t*>(lay(p.xn2, l));
     float* rstd2 = reinterpret_cast<float*>(lay(p.rstd2, l));
     uint16_t* r = reinterpret_cast<uint16_t*>(lay(p.r, l));
+    // Residual scalars: the block reads resid_lambdas[l] x + x0_lambdas[l] x0.
+    if (prl) HIP_TRY(launch_resid_mix_fwd(x, x0, xprev(l), prl + l, pxl + l, Nd, s));
+    if (l == m->backout_layer) HIP_TRY(hipMemcpyAsync(xbo, x, Nd * 4, hipMemcpyDeviceToDevice, s));
     HIP_TRY(launch_rmsnorm_fwd(x, xn1, rstd1, N, d, s));
     HIP_TRY(gemm_nt(xn1, d, wqkv, d, (int)N, Q, d, qkv, Q, EPI_BF16, s));
     HIP_TRY(launch_qknorm_rope_fwd(qkv, rstdqk, cs, N, T, H, Hkv, s));
@@ -645,6 +707,8 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
     HIP_TRY(gemm_nt(xn2, d, wfc, d, (int)N, F, d, r, F, EPI_RELU2_BF16, s));
     HIP_TRY(gemm_nt_add_f32(r, F, wproj, F, (int)N, d, F, x, d, s));
   }
+  // Backout: subtract backout_lambda times the stream kept at the backout block.
+  if (pbl) HIP_TRY(launch_axpy_f32(x, xbo, pbl, -1.f, Nd, s));
   HIP_TRY(launch_rmsnorm_fwd(x, xnf, rstdf, N, d, s));
 
   // ---- head: logits, softmax cross-entropy, and its backward, by token chunks
@@ -669,6 +733,8 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
   }
   HIP_TRY(launch_loss_reduce(loss_rows, N, n_valid, loss, s));
   HIP_TRY(launch_rmsnorm_bwd(dxn, xnf, rstdf, dx, dxb, N, d, 0, s));
+  if (pbl) HIP_TRY(launch_backout_bwd(dx, xbo, dback, Nd, red, grads + m->off_bl, accumulate, s));
+  if (dx0) HIP_TRY(launch_fill_u32(dx0, 0, Nd, s));
 
   // ---- backward through the blocks
   for (int l = L - 1; l >= 0; --l) {
@@ -709,9 +775,15 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
     HIP_TRY(gemm_nn(dqkv, Q, wqkv, d, (int)N, d, Q, dxn, d, EPI_F32, s));
     HIP_TRY(gemm_wgrad(dqkv, Q, xn1, d, Q, d, N, gqkv, accumulate, part, s));
     HIP_TRY(launch_rmsnorm_bwd(dxn, xn1, rstd1, dx, dxb, N, d, 1, s));
+    // dx is now the gradient of the stream entering block l.
+    if (l == m->backout_layer) HIP_TRY(launch_backout_add(dx, dxb, dback, pbl, Nd, s));
+    if (prl)
+      HIP_TRY(launch_resid_mix_bwd(dx, dxb, xprev(l), x0, dx0, prl + l, pxl + l, Nd, red, grads + m->off_rl + l,
+                                   grads + m->off_xl + l, accumulate, s));
   }
 
-  // ---- embedding gradient
+  // ---- embedding gradient (the embedding output is also x0 of every mix)
+  if (dx0) HIP_TRY(launch_axpy_f32(dx, dx0, nullptr, 1.f, Nd, s));
   float* gwte = grads + m->off_wte;
   if (!accumulate) HIP_TRY(launch_fill_u32(gwte, 0, (long)V * d, s));
   HIP_TRY(launch_embed_bwd(tokens, dx, gwte, N, d, V, s));
@@ -805,7 +877,7 @@ gpt_status normuon_step(gpt_model* m, float* params, uint16_t* params_bf16, cons
 
 int64_t adamw_state_elems(const gpt_model* m) {
   if (!m) return 0;
-  return 2L * m->V * m->d;
+  return 2L * m->V * m->d + m->n_scalars;
 }
 
 gpt_status adamw_step(gpt_model* m, float* params, uint16_t* params_bf16, const float* grads,
@@ -819,9 +891,14 @@ gpt_status adamw_step(gpt_model* m, float* params, uint16_t* params_bf16, const 
   const double bc2 = 1.0 - std::pow((double)beta2, (double)step);
   if (!(bc1 > 0.0) || !(bc2 > 0.0)) return GPT_EINVAL;
   const long n = (long)m->V * m->d;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   HIP_TRY(launch_adamw(params, params_bf16, grads, exp_avg, exp_avg_sq, (long)m->off_wte, (long)m->off_lm,
-                       n, lr, beta1, beta2, eps, weight_decay, (float)bc1, (float)bc2,
-                       reinterpret_cast<hipStream_t>(stream)));
+                       n, lr, beta1, beta2, eps, weight_decay, (float)bc1, (float)bc2, s));
+  if (m->n_scalars > 0) {
+    const long o = m->off_scalars;
+    HIP_TRY(launch_adamw_small(params + o, params_bf16 + o, grads + o, exp_avg + 2 * n, exp_avg_sq + 2 * n,
+                               (long)m->n_scalars, lr, beta1, beta2, eps, weight_decay, (float)bc1, (float)bc2, s));
+  }
   return GPT_OK;
 }
 

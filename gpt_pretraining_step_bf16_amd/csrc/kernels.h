@@ -57,3 +57,27 @@ hipError_t launch_muon_update(const MuonGroup& g, const float* x32, float* param
 hipError_t launch_ns_prepare(float* x32, uint16_t* xh, uint16_t* xl, int count, long n,
                              float* partials, int blocks_per_mat, hipStream_t s);
 hipError_t launch_split_hilo(const float* x32, uint16_t* xh, uint16_t* xl, long n, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Residual scalars and backout (all arrays fp32 [n], n % 4 == 0; scalars are
+// device pointers to bf16 weights)
+// ---------------------------------------------------------------------------
+int resid_partials_count();  // float2 partials the two reductions below need
+// x_prev <- x; x <- a x + b x0
+hipError_t launch_resid_mix_fwd(float* x, const float* x0, float* x_prev, const uint16_t* pa, const uint16_t* pb,
+                                long n, hipStream_t s);
+// y <- y + scale * c * x (c = *pc, or 1 if pc is null)
+hipError_t launch_axpy_f32(float* y, const float* x, const uint16_t* pc, float scale, long n, hipStream_t s);
+// With g = dx: *ga (+)= g . x_prev, *gb (+)= g . x0, dx0 += b g, dx <- a g, dxb <- bf16(a g)
+hipError_t launch_resid_mix_bwd(float* dx, uint16_t* dxb, const float* x_prev, const float* x0, float* dx0,
+                                const uint16_t* pa, const uint16_t* pb, long n, float2* partials, float* ga,
+                                float* gb, int accumulate, hipStream_t s);
+// *gc (+)= -(dx . xbo); dback <- dx
+hipError_t launch_backout_bwd(const float* dx, const float* xbo, float* dback, long n, float2* partials,
+                              float* gc, int accumulate, hipStream_t s);
+// dx += -c dback, dxb <- bf16(dx)
+hipError_t launch_backout_add(float* dx, uint16_t* dxb, const float* dback, const uint16_t* pc, long n,
+                              hipStream_t s);
+// AdamW on n contiguous elements (no alignment assumed)
+hipError_t launch_adamw_small(float* w, uint16_t* wb, const float* g, float* m, float* v, long n, float lr,
+                              float b1, float b2, float eps, float wd, float bc1, float bc2, hipStream_t s);

@@ -49,7 +49,7 @@ typedef enum {
   GPT_EWORKSPACE = -5  /* workspace missing or smaller than the *_workspace_bytes() value */
 } gpt_status;
 
-enum { GPT_KIND_EMB = 0, GPT_KIND_MATRIX = 1, GPT_KIND_LM_HEAD = 2 };
+enum { GPT_KIND_EMB = 0, GPT_KIND_MATRIX = 1, GPT_KIND_LM_HEAD = 2, GPT_KIND_SCALAR = 3 };
 
 typedef struct {
   char name[32];   /* "wte", "h<l>.wq" ... "h<l>.wproj", "lm_head" */
@@ -84,6 +84,32 @@ void gpt_destroy(gpt_model* m);
 
 /* Key/value heads of the model (H unless created with fewer). */
 int32_t gpt_kv_heads(const gpt_model* m);
+
+/*
+ * A model with the optional architecture features of [CT50] "1. Modelo GPT"
+ * ("Truques de Eficiência" items 1 and 3; the page prints one line for each):
+ *   kv_heads       as for gpt_create_gqa (0: every head)
+ *   resid_scalars  1: tensors resid_lambdas [1, depth] and x0_lambdas
+ *                  [1, depth]; block i reads resid_lambdas[i] * x +
+ *                  x0_lambdas[i] * x0 as its input stream, x0 being the
+ *                  embedding output
+ *   backout_layer  -1, or k in [0, depth): tensor backout_lambda [1, 1];
+ *                  backout_lambda times the stream entering block k (after its
+ *                  mix) is subtracted before the final norm
+ * Scalar tensors (kind GPT_KIND_SCALAR) follow lm_head in the flat layout and
+ * belong to the AdamW group; gpt_fwd_bwd reads them from params_bf16 like
+ * every weight and writes their gradients. Returns GPT_EINVAL for values out
+ * of range.
+ */
+typedef struct {
+  int32_t depth, vocab, max_seq;
+  int32_t kv_heads;
+  int32_t resid_scalars;
+  int32_t backout_layer;
+} gpt_config;
+gpt_status gpt_create_config(const gpt_config* cfg, gpt_model** out);
+/* The backout layer, or -1. */
+int32_t gpt_backout_layer(const gpt_model* m);
 
 /* dims[6] <- {depth, width, heads, mlp_hidden, vocab, max_seq}. */
 gpt_status gpt_dims(const gpt_model* m, int32_t dims[6]);
@@ -192,20 +218,22 @@ gpt_status normuon_step(gpt_model* m, float* params, uint16_t* params_bf16, cons
                         const float* ns_coeffs, int32_t ns_steps, void* workspace, size_t workspace_bytes,
                         void* stream);
 
-/* Elements of each AdamW moment buffer: wte then lm_head, 2 * vocab * d. */
+/* Elements of each AdamW moment buffer: wte, lm_head, then the scalar tensors
+ * (2 * vocab * d + their count). */
 int64_t adamw_state_elems(const gpt_model* m);
 
 /*
- * One AdamW step of wte and lm_head ([CT50] "2. Otimizador Muon": embeddings
- * and lm_head are optimised by AdamW; the page gives no hyperparameters, so
- * all of them are arguments). Per element, with t = step:
+ * One AdamW step of wte, lm_head and the scalar tensors ([CT50] "2. Otimizador
+ * Muon": embeddings, lm_head and scalars are optimised by AdamW; the page gives
+ * no hyperparameters, so all of them are arguments). Per element, with t = step:
  *   m <- beta1 m + (1 - beta1) g;   v <- beta2 v + (1 - beta2) g^2
  *   w <- w - lr * weight_decay * w - lr * (m / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps)
  * (decoupled decay scaled by lr, from the weights before the step).
- *   params, params_bf16, grads  as for muon_step; only wte and lm_head change,
- *                               and their bf16 shadow is refreshed
+ *   params, params_bf16, grads  as for muon_step; only wte, lm_head and the
+ *                               scalars change, and their bf16 shadow is refreshed
  *   exp_avg, exp_avg_sq         device fp32 [adamw_state_elems(m)]: the moments
- *                               of wte, then those of lm_head; zero before step 1
+ *                               of wte, then lm_head, then the scalars (in
+ *                               layout order); zero before step 1
  *   step                        1-based step count (bias correction)
  * Returns GPT_EINVAL for null pointers, step < 1, betas outside [0, 1),
  * eps < 0 or non-finite lr / weight_decay, before any launch.

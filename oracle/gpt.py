@@ -255,14 +255,22 @@ def per_position_loss(weights, tokens, targets, final_norm=True, windows=None):
     return out
 
 
+def _cs(a, b):
+    """Cauchy-Schwarz bound of sum(a * b): sum over rows of |a_row| |b_row|."""
+    return float(np.sum(np.linalg.norm(a, axis=-1) * np.linalg.norm(b, axis=-1)))
+
+
 def forward_backward(weights, tokens, targets, final_norm=True, want_grads=True, windows=None,
-                     backout_layer=None):
+                     backout_layer=None, scalar_scales=None):
     """Mean cross-entropy loss and the gradient of every tensor.
 
     windows: None, or one attention window per layer (see causal_attention).
     backout_layer: the layer whose input stream the backout subtracts (the
     weights then hold backout_lambda); residual scalars apply when the weights
     hold resid_lambdas and x0_lambdas (see _forward_sequence).
+    scalar_scales: optional dict; for each scalar tensor it receives, shaped
+    like the tensor, the Cauchy-Schwarz bound of the dot product that forms
+    its gradient (a tolerance scale for comparisons; not part of the step).
 
     Sequences are independent, so the batch is processed one row at a time and
     the per-row contributions are summed (this bounds memory; it is exact).
@@ -298,9 +306,16 @@ def forward_backward(weights, tokens, targets, final_norm=True, want_grads=True,
         if final_norm:
             dx = rms_norm_bwd(dx, c["xnf"], c["rf"])
         rl, xl, bl = _scalars(weights)
+        sc = scalar_scales
+        if sc is not None:
+            for k in ("resid_lambdas", "x0_lambdas", "backout_lambda"):
+                if k in weights:
+                    sc.setdefault(k, np.zeros_like(weights[k]))
         if backout_layer is not None:
             # x_final = x_L - bl * x_backout
             grads["backout_lambda"][0, 0] -= float(np.sum(dx * c["x_backout"]))
+            if sc is not None:
+                sc["backout_lambda"][0, 0] += _cs(dx, c["x_backout"])
             d_backout = -bl * dx
         dx0 = np.zeros_like(dx)
         for layer in reversed(range(L)):
@@ -332,6 +347,9 @@ def forward_backward(weights, tokens, targets, final_norm=True, want_grads=True,
                 # x_in = rl * x_prev + xl * x0
                 grads["resid_lambdas"][0, layer] += float(np.sum(dx * s["x_prev"]))
                 grads["x0_lambdas"][0, layer] += float(np.sum(dx * c["x0"]))
+                if sc is not None:
+                    sc["resid_lambdas"][0, layer] += _cs(dx, s["x_prev"])
+                    sc["x0_lambdas"][0, layer] += _cs(dx, c["x0"])
                 dx0 += xl[layer] * dx
                 dx = rl[layer] * dx
         np.add.at(grads["wte"], tok, dx + dx0)

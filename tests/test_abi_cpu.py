@@ -209,3 +209,26 @@ def test_gqa_create_rejects_kv_heads_that_do_not_divide():
     assert lib.gpt_create_gqa(20, 2048, 128, -1, C.byref(h)) == binding.GPT_EINVAL
     m = binding.GptModel(20, 2048, 128, 0)  # 0: every head
     assert m.kv_heads == m.heads == 10
+
+
+@pytest.mark.parametrize("resid,backout", [(True, None), (False, 1), (True, 0)])
+def test_scalar_tensors_follow_lm_head(resid, backout):
+    depth, vocab = 3, 2048
+    m = binding.GptModel(depth, vocab, 128, None, resid, backout)
+    assert m.backout_layer == backout
+    specs = syn.tensor_specs(depth, vocab, None, resid, backout is not None)
+    got = m.tensors()
+    assert [(t["name"], t["rows"], t["cols"], t["kind"]) for t in got] == [sp[:4] for sp in specs]
+    n_scal = (2 * depth if resid else 0) + (1 if backout is not None else 0)
+    assert m.adamw_state_elems() == 2 * vocab * m.d + n_scal
+    assert m.num_params == sum(r * c for _, r, c, _, _ in specs)
+
+
+def test_config_validation():
+    lib = binding.lib()
+    h = C.c_void_p()
+    bad = [binding.GptConfig(3, 2048, 128, 0, 2, -1), binding.GptConfig(3, 2048, 128, 0, 0, 3),
+           binding.GptConfig(3, 2048, 128, 0, 0, -2), binding.GptConfig(0, 2048, 128, 0, 1, -1)]
+    for cfg in bad:
+        assert lib.gpt_create_config(C.byref(cfg), C.byref(h)) == binding.GPT_EINVAL
+    assert lib.gpt_create_config(None, C.byref(h)) == binding.GPT_EINVAL

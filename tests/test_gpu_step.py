@@ -10,7 +10,7 @@ Token handling is bit-exact: embedding-gradient rows of absent tokens are 0.
 import numpy as np
 import pytest
 
-from gpu_util import bits_to_f32, bf16_bits, bf16_round, log, rel_l2
+from gpu_util import assert_scalar_grads, bits_to_f32, bf16_bits, bf16_round, log, rel_l2
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -23,15 +23,31 @@ LOSS_TOL = 1e-2
 REL_TOL = 2e-2
 
 
-def _run_case(depth, vocab, seq, batch, seed_w=0, seed_t=1, ignore=(), windows=None, kv_heads=None):
-    log(f"fwd_bwd depth={depth} vocab={vocab} seq={seq} batch={batch} windows={windows} kv_heads={kv_heads}")
-    w = syn.init_weights(depth, vocab, seed=seed_w, kv_heads=kv_heads)
+def _random_scalars(w, depth, seed, backout_value=None):
+    rng = np.random.default_rng(seed)
+    if "resid_lambdas" in w:
+        w["resid_lambdas"] = rng.uniform(0.5, 1.5, size=(1, depth)).astype(np.float32)
+        w["x0_lambdas"] = rng.uniform(-0.5, 0.5, size=(1, depth)).astype(np.float32)
+    if "backout_lambda" in w:
+        v = rng.uniform(0.1, 0.6) if backout_value is None else backout_value
+        w["backout_lambda"] = np.array([[v]], dtype=np.float32)
+    return w
+
+
+def _run_case(depth, vocab, seq, batch, seed_w=0, seed_t=1, ignore=(), windows=None, kv_heads=None,
+              resid_scalars=False, backout_layer=None, std=syn.INIT_STD, backout_value=None):
+    log(f"fwd_bwd depth={depth} vocab={vocab} seq={seq} batch={batch} windows={windows} kv_heads={kv_heads}"
+        f" resid_scalars={resid_scalars} backout_layer={backout_layer}")
+    w = syn.init_weights(depth, vocab, seed=seed_w, std=std, kv_heads=kv_heads, resid_scalars=resid_scalars,
+                         backout=backout_layer is not None)
+    w = _random_scalars(w, depth, seed_w + 50, backout_value)
     ids = syn.zipf_ids(batch, seq, vocab, seed=seed_t)
     tok, tgt = syn.split_tokens(ids)
     tgt = tgt.copy()
     for (b, t) in ignore:
         tgt[b, t] = -1
-    st = TrainState(depth, vocab, seq, batch, kv_heads=kv_heads)
+    st = TrainState(depth, vocab, seq, batch, kv_heads=kv_heads, resid_scalars=resid_scalars,
+                    backout_layer=backout_layer)
     st.load_weights(w)
     st.set_windows(windows)
     tok_d = torch.from_numpy(tok).cuda()
@@ -43,14 +59,19 @@ def _run_case(depth, vocab, seq, batch, seed_w=0, seed_t=1, ignore=(), windows=N
     grads = st.to_host(st.grads)
     # The oracle gets the inputs gpt_fwd_bwd gets: the bf16 weights.
     w64 = {k: bf16_round(v).astype(np.float64) for k, v in w.items()}
+    scales = {}
     ref_loss, ref_grads = oracle.forward_backward(
-        w64, tok, tgt, windows=None if windows is None else [None if x < 0 else x for x in windows])
+        w64, tok, tgt, windows=None if windows is None else [None if x < 0 else x for x in windows],
+        backout_layer=backout_layer, scalar_scales=scales)
+    _run_case.scales = scales
     return st, tok, tgt, loss, grads, ref_loss, ref_grads
 
 
-def _assert_grads(grads, ref_grads, tok, vocab):
+def _assert_grads(grads, ref_grads, tok, vocab, skip=()):
     worst = []
     for name, ref in ref_grads.items():
+        if name in skip:
+            continue
         e = rel_l2(grads[name], ref)
         worst.append((e, name))
         assert e < REL_TOL, (name, e)
@@ -143,6 +164,58 @@ def test_gqa_muon_matches_oracle(normuon):
         assert off == state.size
     for k in ("wte", "lm_head"):
         np.testing.assert_array_equal(new_w[k], w[k])
+
+
+@pytest.mark.parametrize("depth,vocab,seq,batch,resid,backout", [(2, 2048, 64, 2, True, 1), (3, 2048, 200, 3, True, 0),
+                                                                (4, 2048, 128, 2, False, 2), (4, 2048, 128, 2, True, None)])
+def test_scalars_fwd_bwd_matches_oracle(depth, vocab, seq, batch, resid, backout):
+    """Residual scalars (random values) and backout at various layers, with a
+    ragged length; the scalar gradients are full reductions over tokens, checked
+    against their Cauchy-Schwarz scale (gpu_util.assert_scalar_grads). Weights
+    of std 0.1 and backout_lambda 0.9 keep the kept stream far from parallel to
+    the final one, so the backout gradient is not cancelled to noise."""
+    st, tok, tgt, loss, grads, ref_loss, ref_grads = _run_case(depth, vocab, seq, batch, seed_w=2, seed_t=3,
+                                                                resid_scalars=resid, backout_layer=backout,
+                                                                std=0.1, backout_value=0.9)
+    assert abs(loss - ref_loss) <= LOSS_TOL
+    scalars = ("resid_lambdas", "x0_lambdas", "backout_lambda")
+    _assert_grads(grads, ref_grads, tok, vocab, skip=scalars)
+    assert_scalar_grads(grads, ref_grads, _run_case.scales, log)
+    if backout is not None:  # the backout gradient is well above its noise floor here
+        assert abs(ref_grads["backout_lambda"][0, 0]) > 1e-3 * _run_case.scales["backout_lambda"][0, 0]
+    # Accumulation: a second identical call with accumulate=1 doubles every gradient.
+    toks = torch.from_numpy(tok).cuda()
+    tgts = torch.from_numpy(tgt).cuda()
+    st.fwd_bwd(toks, tgts, accumulate=True)
+    torch.cuda.synchronize()
+    g2 = st.to_host(st.grads)
+    for k in ("resid_lambdas", "x0_lambdas", "backout_lambda"):
+        if k in grads:
+            np.testing.assert_allclose(g2[k], 2 * grads[k], rtol=1e-5, atol=1e-9)
+
+
+def test_adamw_updates_scalar_tensors():
+    depth, vocab = 3, 2048
+    w = _random_scalars(syn.init_weights(depth, vocab, seed=0, resid_scalars=True, backout=True), depth, 1)
+    g = syn.random_like_grads(depth, vocab, seed=7, scale=1e-2, resid_scalars=True, backout=True)
+    st = TrainState(depth, vocab, 64, 1, resid_scalars=True, backout_layer=1)
+    st.load_weights(w)
+    st.load_grads(g)
+    a = ADAMW
+    st.adamw(a["lr"], a["beta1"], a["beta2"], a["eps"], a["weight_decay"], 1)
+    torch.cuda.synchronize()
+    new_w = st.to_host(st.params)
+    names = ("wte", "lm_head", "resid_lambdas", "x0_lambdas", "backout_lambda")
+    f64 = lambda dd: {k: v.astype(np.float64) for k, v in dd.items()}
+    z = {k: np.zeros(w[k].shape) for k in names}
+    ref_w, _, _ = oracle.adamw_step(f64(w), f64(g), z, z, 1, a["lr"], a["beta1"], a["beta2"], a["eps"],
+                                    a["weight_decay"])
+    for k in names:
+        assert rel_l2(w[k].astype(np.float64) - new_w[k], w[k].astype(np.float64) - ref_w[k]) < 1e-5, k
+    for k in w:
+        if k not in names:
+            np.testing.assert_array_equal(new_w[k], w[k])
+    np.testing.assert_array_equal(st.params_bf16.cpu().numpy(), bf16_bits(st.params.cpu().numpy()))
 
 
 def test_ragged_windowed_fwd_bwd():

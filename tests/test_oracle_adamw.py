@@ -75,3 +75,21 @@ def test_only_embedding_and_head_change():
     np.testing.assert_array_equal(new_w["h0.wq"], weights["h0.wq"])
     assert set(new_m) == set(new_v) == {"wte", "lm_head"}
     assert not np.array_equal(new_w["wte"], weights["wte"])
+
+
+def test_scalar_tensors_join_the_adamw_group():
+    from gpt_pretraining_step_bf16_amd import synthetic as syn
+
+    w = {k: v.astype(np.float64) for k, v in syn.init_weights(2, 64, resid_scalars=True, backout=True).items()}
+    rng = np.random.default_rng(5)
+    g = {k: rng.standard_normal(v.shape) for k, v in w.items()}
+    names = ("wte", "lm_head", "resid_lambdas", "x0_lambdas", "backout_lambda")
+    z = {k: np.zeros_like(w[k]) for k in names}
+    new_w, m1, _ = adamw_step(w, g, z, z, 1, 0.01, 0.9, 0.95, 1e-8, 0.0)
+    for k in w:
+        if k in names:
+            # First step from zero moments: a normalised-gradient step.
+            np.testing.assert_allclose(w[k] - new_w[k], 0.01 * g[k] / (np.abs(g[k]) + 1e-8), rtol=1e-9)
+            assert k in m1
+        else:
+            np.testing.assert_array_equal(new_w[k], w[k])
