@@ -65,10 +65,10 @@ def model_dims(depth: int) -> dict:
     return dict(depth=depth, d=d, heads=d // HEAD_DIM, mlp=4 * d)
 
 
-def tensor_specs(depth: int, vocab: int, kv_heads=None, resid_scalars=False, backout=False):
+def tensor_specs(depth: int, vocab: int, kv_heads=None, resid_scalars=False, backout=False, smear=False):
     """Canonical tensor order: wte; per layer wq, wk, wv, wo, wfc, wproj; lm_head;
     then the optional scalar tensors resid_lambdas [1, depth], x0_lambdas
-    [1, depth] and backout_lambda [1, 1].
+    [1, depth], backout_lambda [1, 1], smear_gate [1, 24] and smear_lambda [1, 1].
 
     Each entry is (name, rows, cols, kind, layer) with kind in
     {"emb", "matrix", "lm_head", "scalar"}; matrices are [out, in] as in a
@@ -93,21 +93,24 @@ def tensor_specs(depth: int, vocab: int, kv_heads=None, resid_scalars=False, bac
         specs += [("resid_lambdas", 1, depth, "scalar", -1), ("x0_lambdas", 1, depth, "scalar", -1)]
     if backout:
         specs.append(("backout_lambda", 1, 1, "scalar", -1))
+    if smear:
+        specs += [("smear_gate", 1, 24, "scalar", -1), ("smear_lambda", 1, 1, "scalar", -1)]
     return specs
 
 
 # Start values of the scalar tensors: the plain residual stream (no x0 mix, no
 # backout). The pages give none; tests set other values explicitly.
-SCALAR_INIT = {"resid_lambdas": 1.0, "x0_lambdas": 0.0, "backout_lambda": 0.0}
+SCALAR_INIT = {"resid_lambdas": 1.0, "x0_lambdas": 0.0, "backout_lambda": 0.0, "smear_gate": 0.0,
+               "smear_lambda": 0.0}
 
 
 def init_weights(depth: int, vocab: int, seed: int = 0, std: float = INIT_STD, kv_heads=None,
-                 resid_scalars=False, backout=False) -> dict:
+                 resid_scalars=False, backout=False, smear=False) -> dict:
     """Every matrix N(0, std^2), float32, drawn in canonical order from one seed;
     scalar tensors take SCALAR_INIT (no draw)."""
     rng = np.random.default_rng(seed)
     out = {}
-    for name, rows, cols, kind, _layer in tensor_specs(depth, vocab, kv_heads, resid_scalars, backout):
+    for name, rows, cols, kind, _layer in tensor_specs(depth, vocab, kv_heads, resid_scalars, backout, smear):
         if kind == "scalar":
             out[name] = np.full((rows, cols), SCALAR_INIT[name], dtype=np.float32)
             continue
@@ -140,11 +143,11 @@ def split_tokens(ids: np.ndarray):
 
 
 def random_like_grads(depth: int, vocab: int, seed: int, scale: float = 1e-3, kv_heads=None,
-                      resid_scalars=False, backout=False) -> dict:
+                      resid_scalars=False, backout=False, smear=False) -> dict:
     """Seeded Gaussian arrays shaped like the parameters (for optimizer-only cases)."""
     rng = np.random.default_rng(seed)
     out = {}
-    for name, rows, cols, _kind, _layer in tensor_specs(depth, vocab, kv_heads, resid_scalars, backout):
+    for name, rows, cols, _kind, _layer in tensor_specs(depth, vocab, kv_heads, resid_scalars, backout, smear):
         g = rng.standard_normal((rows, cols), dtype=np.float32)
         g *= np.float32(scale)
         out[name] = g

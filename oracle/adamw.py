@@ -45,7 +45,7 @@ def adamw_update(w, g, m, v, step, lr, beta1, beta2, eps, wd):
     return w, m, v
 
 
-SCALAR_TENSORS = ("resid_lambdas", "x0_lambdas", "backout_lambda")
+SCALAR_TENSORS = ("resid_lambdas", "x0_lambdas", "backout_lambda", "smear_gate", "smear_lambda")
 
 
 def adamw_step(weights, grads, exp_avg, exp_avg_sq, step, lr, beta1, beta2, eps, wd):

@@ -35,6 +35,11 @@ output) as its input stream; with backout_lambda [1, 1] and a backout layer k,
 backout_lambda times the stream entering block k is subtracted before the
 final norm. The pages print these two lines and nothing around them.
 
+Smear (optional): with tensors smear_gate [1, 24] and smear_lambda [1, 1] the
+embedding output becomes x_t + smear_lambda * sigmoid(smear_gate . x_t[:24])
+* x_(t-1) (zero before a sequence's first token); this is the x0 that the
+residual scalars mix in.
+
 Grouped-query attention (optional): the pages list "fewer KV heads". When wk
 and wv have Hkv * 128 rows (Hkv dividing H), query head h attends with key and
 value head h // (H / Hkv); QK-norm and RoPE act per head as before.
@@ -179,6 +184,44 @@ def _scalars(weights):
     return rl, xl, bl
 
 
+SMEAR_CHANNELS = 24
+
+
+def _smear(x, weights):
+    """Smear ([CT50] "Truques de Eficiência", item 2: mix in the previous
+    token's embedding): gate_t = smear_lambda * sigmoid(smear_gate . x_t[:24]),
+    y_t = x_t + gate_t * x_(t-1), with x_(-1) = 0 (the first token of a
+    sequence has no previous one). Returns y and the saved (gate logits)."""
+    w = weights["smear_gate"][0]
+    lam = float(weights["smear_lambda"][0, 0])
+    a = x[:, :SMEAR_CHANNELS] @ w
+    prev = np.concatenate([np.zeros_like(x[:1]), x[:-1]], axis=0)
+    g = lam / (1.0 + np.exp(-a))
+    return x + g[:, None] * prev, a
+
+
+def _smear_bwd(dy, x, a, weights, grads, sc=None):
+    """Adjoint of _smear: returns dx and adds the gate's gradients (and, with
+    sc, the Cauchy-Schwarz bounds of the sums that form them)."""
+    w = weights["smear_gate"][0]
+    lam = float(weights["smear_lambda"][0, 0])
+    sig = 1.0 / (1.0 + np.exp(-a))
+    prev = np.concatenate([np.zeros_like(x[:1]), x[:-1]], axis=0)
+    s = np.sum(dy * prev, axis=1)             # d loss / d gate_t
+    grads["smear_lambda"][0, 0] += float(np.sum(sig * s))
+    c = lam * sig * (1.0 - sig) * s           # d loss / d a_t
+    grads["smear_gate"][0] += c @ x[:, :SMEAR_CHANNELS]
+    if sc is not None:
+        bound = np.linalg.norm(dy, axis=1) * np.linalg.norm(prev, axis=1)
+        sc["smear_lambda"][0, 0] += float(np.sum(sig * bound))
+        sc["smear_gate"][0] += (np.abs(lam) * sig * (1.0 - sig) * bound) @ np.abs(x[:, :SMEAR_CHANNELS])
+    g = lam * sig
+    dx = dy.copy()
+    dx[:-1] += g[1:, None] * dy[1:]           # x_t is the previous token of t + 1
+    dx[:, :SMEAR_CHANNELS] += c[:, None] * w[None, :]
+    return dx
+
+
 def _forward_sequence(weights, tok, cos, sin, final_norm=True, windows=None, backout_layer=None):
     """Forward pass of one sequence; returns the logits and the saved values.
 
@@ -197,6 +240,9 @@ def _forward_sequence(weights, tok, cos, sin, final_norm=True, windows=None, bac
     T = tok.shape[0]
     rl, xl, bl = _scalars(weights)
     x = wte[tok]
+    x_emb, smear_a = x, None
+    if "smear_gate" in weights:
+        x, smear_a = _smear(x, weights)
     x0 = x
     x_backout = None
     layers = []
@@ -230,7 +276,7 @@ def _forward_sequence(weights, tok, cos, sin, final_norm=True, windows=None, bac
     else:
         xnf, rf = x, None
     z = xnf @ weights["lm_head"].T
-    return z, dict(layers=layers, xnf=xnf, rf=rf, x0=x0, x_backout=x_backout)
+    return z, dict(layers=layers, xnf=xnf, rf=rf, x0=x0, x_backout=x_backout, x_emb=x_emb, smear_a=smear_a)
 
 
 def forward_logits(weights, tokens, final_norm=True, windows=None, backout_layer=None):
@@ -308,7 +354,7 @@ def forward_backward(weights, tokens, targets, final_norm=True, want_grads=True,
         rl, xl, bl = _scalars(weights)
         sc = scalar_scales
         if sc is not None:
-            for k in ("resid_lambdas", "x0_lambdas", "backout_lambda"):
+            for k in ("resid_lambdas", "x0_lambdas", "backout_lambda", "smear_gate", "smear_lambda"):
                 if k in weights:
                     sc.setdefault(k, np.zeros_like(weights[k]))
         if backout_layer is not None:
@@ -352,6 +398,9 @@ def forward_backward(weights, tokens, targets, final_norm=True, want_grads=True,
                     sc["x0_lambdas"][0, layer] += _cs(dx, c["x0"])
                 dx0 += xl[layer] * dx
                 dx = rl[layer] * dx
-        np.add.at(grads["wte"], tok, dx + dx0)
+        dx = dx + dx0
+        if "smear_gate" in weights:
+            dx = _smear_bwd(dx, c["x_emb"], c["smear_a"], weights, grads, sc)
+        np.add.at(grads["wte"], tok, dx)
     loss = loss_sum / n_valid if n_valid else 0.0
     return loss, grads

@@ -308,6 +308,61 @@ def test_scalar_gradients_match_central_differences(backout_layer):
 
 
 # ----------------------------------------------------------------------------
+# Smear
+# ----------------------------------------------------------------------------
+def test_smear_matches_a_token_loop():
+    rng = np.random.default_rng(40)
+    T, d = 7, 128
+    x = rng.standard_normal((T, d))
+    w = {"smear_gate": rng.standard_normal((1, 24)) * 0.3, "smear_lambda": np.array([[0.7]])}
+    y, _ = og._smear(x, w)
+    for t in range(T):
+        a = sum(w["smear_gate"][0, j] * x[t, j] for j in range(24))
+        gate = 0.7 / (1.0 + math.exp(-a))
+        for e in range(0, d, 9):
+            want = x[t, e] + (gate * x[t - 1, e] if t > 0 else 0.0)
+            assert abs(y[t, e] - want) < 1e-12
+
+
+def test_smear_lambda_zero_is_the_plain_model():
+    depth, vocab, seq = 2, 128, 10
+    w = _tiny_weights(depth, vocab, seed=4, std=0.1)
+    ws = dict(w)
+    ws["smear_gate"] = np.random.default_rng(1).standard_normal((1, 24))
+    ws["smear_lambda"] = np.zeros((1, 1))
+    tok, tgt = _ids(2, seq, vocab, seed=6)
+    loss, grads = oracle.forward_backward(w, tok, tgt)
+    loss_s, grads_s = oracle.forward_backward(ws, tok, tgt)
+    assert loss_s == loss
+    for k in grads:
+        np.testing.assert_array_equal(grads_s[k], grads[k])
+    assert not np.any(grads_s["smear_gate"])  # the gate's slope carries the factor lambda
+
+
+def test_smear_gradients_match_central_differences():
+    depth, vocab, seq, batch = 2, 96, 10, 2
+    w = _scalar_weights(depth, vocab, seed=3, std=0.15, rng_seed=4, backout=True)
+    rng = np.random.default_rng(41)
+    w["smear_gate"] = rng.standard_normal((1, 24)) * 0.5
+    w["smear_lambda"] = np.array([[0.6]])
+    tok, tgt = _ids(batch, seq, vocab, seed=5)
+    loss, grads = oracle.forward_backward(w, tok, tgt, backout_layer=1)
+    h = 1e-5
+
+    def f(ww):
+        return oracle.forward_backward(ww, tok, tgt, want_grads=False, backout_layer=1)[0]
+
+    for name in w:
+        u = rng.standard_normal(w[name].shape)
+        u /= np.linalg.norm(u)
+        wp = dict(w); wp[name] = w[name] + h * u
+        wm = dict(w); wm[name] = w[name] - h * u
+        fd = (f(wp) - f(wm)) / (2 * h)
+        an = float(np.sum(grads[name] * u))
+        assert abs(fd - an) <= 1e-6 * abs(an) + 1e-9, (name, fd, an)
+
+
+# ----------------------------------------------------------------------------
 # Grouped-query attention: equal to full multi-head attention whose key/value
 # weights repeat each group's rows (an independent path: no head sharing)
 # ----------------------------------------------------------------------------
