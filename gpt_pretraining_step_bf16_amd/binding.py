@@ -40,6 +40,7 @@ class GptConfig(C.Structure):
         ("kv_heads", C.c_int32),
         ("resid_scalars", C.c_int32),
         ("backout_layer", C.c_int32),
+        ("smear", C.c_int32),
     ]
 
 
@@ -147,16 +148,17 @@ class GptModel:
     """Host-side plan of a model (no device memory)."""
 
     def __init__(self, depth: int, vocab: int, max_seq: int, kv_heads=None, resid_scalars=False,
-                 backout_layer=None):
+                 backout_layer=None, smear=False):
         h = C.c_void_p()
-        if not resid_scalars and backout_layer is None:
+        if not resid_scalars and backout_layer is None and not smear:
             if kv_heads is None:
                 _check(lib().gpt_create(depth, vocab, max_seq, C.byref(h)), "gpt_create")
             else:
                 _check(lib().gpt_create_gqa(depth, vocab, max_seq, int(kv_heads), C.byref(h)), "gpt_create_gqa")
         else:
             cfg = GptConfig(depth, vocab, max_seq, 0 if kv_heads is None else int(kv_heads),
-                            1 if resid_scalars else 0, -1 if backout_layer is None else int(backout_layer))
+                            1 if resid_scalars else 0, -1 if backout_layer is None else int(backout_layer),
+                            1 if smear else 0)
             _check(lib().gpt_create_config(C.byref(cfg), C.byref(h)), "gpt_create_config")
         self._h = h
         dims = (C.c_int32 * 6)()

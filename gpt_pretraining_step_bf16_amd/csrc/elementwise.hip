@@ -794,6 +794,110 @@ __global__ void adamw_small_kernel(float* __restrict__ w, uint16_t* __restrict__
   wb[i] = (uint16_t)f2bf(wv);
 }
 
+// Smear ([CT50] "Truques de Eficiência", item 2): y_t = x_t + gate_t x_(t-1),
+// gate_t = lambda * sigmoid(w . x_t[0:24]), x_(-1) = 0 at a sequence's first
+// token. One wave per row (token); rows are b * T + t.
+constexpr int SMEAR_CH = 24;
+
+__global__ void __launch_bounds__(256) smear_fwd_kernel(const float* __restrict__ xe, float* __restrict__ x,
+                                                        float* __restrict__ a_out, const uint16_t* __restrict__ pw,
+                                                        const uint16_t* __restrict__ plam, long N, int T, int d) {
+  const long row = blockIdx.x * 4L + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= N) return;
+  const int t = (int)(row % T);
+  const float4* xr = reinterpret_cast<const float4*>(xe + row * d);
+  float part = 0.f;
+  if (lane < SMEAR_CH / 4) {
+    const float4 v = xr[lane];
+    part = v.x * bf2f(pw[4 * lane]) + v.y * bf2f(pw[4 * lane + 1]) + v.z * bf2f(pw[4 * lane + 2]) +
+           v.w * bf2f(pw[4 * lane + 3]);
+  }
+  const float a = warp_sum(part);
+  const float g = t > 0 ? bf2f(*plam) / (1.f + __expf(-a)) : 0.f;
+  const float4* pr = reinterpret_cast<const float4*>(xe + (row - (t > 0 ? 1 : 0)) * d);
+  float4* yr = reinterpret_cast<float4*>(x + row * d);
+  for (int c = lane; c < d / 4; c += 64) {
+    const float4 v = xr[c], u = pr[c];
+    yr[c] = make_float4(v.x + g * u.x, v.y + g * u.y, v.z + g * u.z, v.w + g * u.w);
+  }
+  if (lane == 0) a_out[row] = a;
+}
+
+// Backward, with dy the gradient of the smeared stream: per row,
+// s_t = dy_t . x_(t-1), c_t = lambda sig(a_t) (1 - sig(a_t)) s_t,
+// dx_t = dy_t + gate_(t+1) dy_(t+1) + c_t w (on channels 0..23). Block
+// partials of d lambda = sum sig(a_t) s_t and d w = sum c_t x_t[0:24] go to
+// partials[blockIdx.x][25]. Grid-stride over rows, 4 waves per block.
+__global__ void __launch_bounds__(256) smear_bwd_kernel(const float* __restrict__ dy, const float* __restrict__ xe,
+                                                        const float* __restrict__ a_in, float* __restrict__ dxo,
+                                                        const uint16_t* __restrict__ pw,
+                                                        const uint16_t* __restrict__ plam, long N, int T, int d,
+                                                        float* __restrict__ partials) {
+  __shared__ float red[4][SMEAR_CH + 1];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const float lam = bf2f(*plam);
+  float acc_l = 0.f;
+  float acc_w[4] = {0.f, 0.f, 0.f, 0.f};  // channels 4 lane .. 4 lane + 3 (lanes < 6)
+  for (long row = blockIdx.x * 4L + wave; row < N; row += gridDim.x * 4L) {
+    const int t = (int)(row % T);
+    const float4* g0 = reinterpret_cast<const float4*>(dy + row * d);
+    float s = 0.f;
+    if (t > 0) {
+      const float4* xp = reinterpret_cast<const float4*>(xe + (row - 1) * d);
+      for (int c = lane; c < d / 4; c += 64) {
+        const float4 u = g0[c], v = xp[c];
+        s += u.x * v.x + u.y * v.y + u.z * v.z + u.w * v.w;
+      }
+    }
+    s = warp_sum(s);
+    const float sig = 1.f / (1.f + __expf(-a_in[row]));
+    const float cc = lam * sig * (1.f - sig) * s;
+    const bool has_next = t + 1 < T && row + 1 < N;
+    const float gn = has_next ? lam / (1.f + __expf(-a_in[row + 1])) : 0.f;
+    const float4* g1 = reinterpret_cast<const float4*>(dy + (row + (has_next ? 1 : 0)) * d);
+    float4* out = reinterpret_cast<float4*>(dxo + row * d);
+    for (int c = lane; c < d / 4; c += 64) {
+      const float4 u = g0[c], v = g1[c];
+      float4 o = make_float4(u.x + gn * v.x, u.y + gn * v.y, u.z + gn * v.z, u.w + gn * v.w);
+      if (c < SMEAR_CH / 4) {
+        o.x += cc * bf2f(pw[4 * c]);
+        o.y += cc * bf2f(pw[4 * c + 1]);
+        o.z += cc * bf2f(pw[4 * c + 2]);
+        o.w += cc * bf2f(pw[4 * c + 3]);
+      }
+      out[c] = o;
+    }
+    acc_l += sig * s;
+    if (lane < SMEAR_CH / 4) {
+      const float4 xv = reinterpret_cast<const float4*>(xe + row * d)[lane];
+      acc_w[0] += cc * xv.x;
+      acc_w[1] += cc * xv.y;
+      acc_w[2] += cc * xv.z;
+      acc_w[3] += cc * xv.w;
+    }
+  }
+  // Every lane of a wave holds the same acc_l (s and sig are wave-uniform).
+  if (lane == 0) red[wave][SMEAR_CH] = acc_l;
+  if (lane < SMEAR_CH / 4)
+    for (int k = 0; k < 4; ++k) red[wave][4 * lane + k] = acc_w[k];
+  __syncthreads();
+  if (threadIdx.x < SMEAR_CH + 1)
+    partials[blockIdx.x * (SMEAR_CH + 1) + threadIdx.x] =
+        red[0][threadIdx.x] + red[1][threadIdx.x] + red[2][threadIdx.x] + red[3][threadIdx.x];
+}
+
+// grads (+)= column sums of partials [nb][25]: smear_gate (24) then smear_lambda.
+__global__ void smear_grads_kernel(const float* __restrict__ partials, int nb, float* gw, float* glam,
+                                   int accumulate) {
+  const int k = threadIdx.x;
+  if (k > SMEAR_CH) return;
+  float t = 0.f;
+  for (int i = 0; i < nb; ++i) t += partials[i * (SMEAR_CH + 1) + k];
+  float* out = k < SMEAR_CH ? gw + k : glam;
+  *out = accumulate ? *out + t : t;
+}
+
 // AdamW on one contiguous fp32 tensor and its moments ([CT50] "2. Otimizador
 // Muon": embeddings and lm_head are in the AdamW group). Decoupled decay scaled
 // by lr and taken from the weights before the step; bias corrections
@@ -1105,5 +1209,29 @@ hipError_t launch_adamw_small(float* w, uint16_t* wb, const float* g, float* m, 
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(adamw_small_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, w, wb, g, m, v, n, lr,
                      b1, b2, eps, wd, bc1, bc2);
+  return hipGetLastError();
+}
+
+// ---- smear
+namespace {
+constexpr int kSmearBlocks = 256;
+}
+int smear_partials_floats() { return kSmearBlocks * (SMEAR_CH + 1); }
+
+hipError_t launch_smear_fwd(const float* xe, float* x, float* a, const uint16_t* pw, const uint16_t* plam, long N,
+                            int T, int d, hipStream_t s) {
+  hipLaunchKernelGGL(smear_fwd_kernel, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s, xe, x, a, pw, plam, N, T, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_smear_bwd(const float* dy, const float* xe, const float* a, float* dxo, const uint16_t* pw,
+                            const uint16_t* plam, long N, int T, int d, float* partials, float* gw, float* glam,
+                            int accumulate, hipStream_t s) {
+  hipLaunchKernelGGL(smear_bwd_kernel, dim3(kSmearBlocks), dim3(256), 0, s, dy, xe, a, dxo, pw, plam, N, T, d,
+                     partials);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(smear_grads_kernel, dim3(1), dim3(64), 0, s, static_cast<const float*>(partials), kSmearBlocks,
+                     gw, glam, accumulate);
   return hipGetLastError();
 }

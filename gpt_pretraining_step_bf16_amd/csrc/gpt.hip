@@ -36,6 +36,7 @@ struct gpt_model {
   // Residual scalars and backout: element offsets of resid_lambdas [L],
   // x0_lambdas [L], backout_lambda (-1 when absent); the backout layer.
   int64_t off_rl = -1, off_xl = -1, off_bl = -1, off_scalars = -1, n_scalars = 0;
+  int64_t off_sg = -1, off_sl = -1;  // smear_gate [24], smear_lambda (-1 when absent)
   int backout_layer = -1;
   std::vector<gpt_tensor> tensors;
   int64_t nparams = 0;
@@ -130,6 +131,7 @@ struct FwdPlan {
   size_t logits = 0, loss_rows = 0, part = 0;
   // residual scalars / backout (0 when the model has none)
   size_t x0 = 0, dx0 = 0, red = 0, xprev = 0, xbo = 0, dback = 0;
+  size_t xe = 0, sa = 0, sred = 0;  // smear: embedding output, gate logits, partials
   long nc = 0;       // CE chunk rows
   size_t part_bytes = 0;
   size_t total = 0;
@@ -228,6 +230,11 @@ FwdPlan plan_fwd(const gpt_model& m, int B, int T) {
   if (m.off_bl >= 0) {
     p.xbo = c.take(N * d * 4);
     p.dback = c.take(N * d * 4);
+  }
+  if (m.off_sg >= 0) {
+    p.xe = c.take(N * d * 4);
+    p.sa = c.take(N * 4);
+    p.sred = c.take((size_t)smear_partials_floats() * 4);
   }
   size_t part = 0;
   const long shapes[4][2] = {{Q, d}, {d, d}, {F, d}, {d, F}};
@@ -514,6 +521,7 @@ gpt_status gpt_create_gqa(int32_t depth, int32_t vocab, int32_t max_seq, int32_t
   c.kv_heads = kv_heads;
   c.resid_scalars = 0;
   c.backout_layer = -1;
+  c.smear = 0;
   return gpt_create_config(&c, out);
 }
 
@@ -527,6 +535,7 @@ gpt_status gpt_create_config(const gpt_config* cfg, gpt_model** out) {
   *out = nullptr;
   if (cfg->resid_scalars != 0 && cfg->resid_scalars != 1) return GPT_EINVAL;
   if (cfg->backout_layer < -1 || cfg->backout_layer >= depth) return GPT_EINVAL;
+  if (cfg->smear != 0 && cfg->smear != 1) return GPT_EINVAL;
   if (depth < 1 || depth > 64) return GPT_EINVAL;
   if (vocab < 64 || vocab > 262144 || vocab % 64 != 0) return GPT_EINVAL;
   if (max_seq < 1 || max_seq > 16384) return GPT_EINVAL;
@@ -583,6 +592,12 @@ gpt_status gpt_create_config(const gpt_config* cfg, gpt_model** out) {
     m->backout_layer = cfg->backout_layer;
     m->off_bl = off;
     add("backout_lambda", 1, 1, GPT_KIND_SCALAR, -1);
+  }
+  if (cfg->smear) {
+    m->off_sg = off;
+    add("smear_gate", 1, 24, GPT_KIND_SCALAR, -1);
+    m->off_sl = off;
+    add("smear_lambda", 1, 1, GPT_KIND_SCALAR, -1);
   }
   m->n_scalars = off - m->off_scalars;
   m->nparams = off;
@@ -662,7 +677,13 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
   HIP_TRY(launch_fill_u32(hdr, 0, 2, s));
   HIP_TRY(launch_rope_table(cs, T, s));
   HIP_TRY(launch_count_targets(targets, N, V, n_valid, err, s));
-  HIP_TRY(launch_embed_fwd(tokens, wte, x, err, N, d, V, s));
+  float* xe = p.xe ? reinterpret_cast<float*>(ws + p.xe) : nullptr;
+  float* sa = p.sa ? reinterpret_cast<float*>(ws + p.sa) : nullptr;
+  const uint16_t* psg = m->off_sg >= 0 ? pbf + m->off_sg : nullptr;
+  const uint16_t* psl = m->off_sl >= 0 ? pbf + m->off_sl : nullptr;
+  HIP_TRY(launch_embed_fwd(tokens, wte, xe ? xe : x, err, N, d, V, s));
+  // Smear: x_t = xe_t + lambda sigmoid(w . xe_t[0:24]) xe_(t-1).
+  if (xe) HIP_TRY(launch_smear_fwd(xe, x, sa, psg, psl, N, T, d, s));
   const long Nd = N * d;
   float* x0 = p.x0 ? reinterpret_cast<float*>(ws + p.x0) : nullptr;
   float* dx0 = p.dx0 ? reinterpret_cast<float*>(ws + p.dx0) : nullptr;
@@ -784,6 +805,12 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
 
   // ---- embedding gradient (the embedding output is also x0 of every mix)
   if (dx0) HIP_TRY(launch_axpy_f32(dx, dx0, nullptr, 1.f, Nd, s));
+  if (xe) {
+    // Through the smear into the raw embedding rows (dxn is free here).
+    HIP_TRY(launch_smear_bwd(dx, xe, sa, dxn, psg, psl, N, T, d, reinterpret_cast<float*>(ws + p.sred),
+                             grads + m->off_sg, grads + m->off_sl, accumulate, s));
+    dx = dxn;
+  }
   float* gwte = grads + m->off_wte;
   if (!accumulate) HIP_TRY(launch_fill_u32(gwte, 0, (long)V * d, s));
   HIP_TRY(launch_embed_bwd(tokens, dx, gwte, N, d, V, s));

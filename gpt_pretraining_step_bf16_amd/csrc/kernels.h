@@ -81,3 +81,15 @@ hipError_t launch_backout_add(float* dx, uint16_t* dxb, const float* dback, cons
 // AdamW on n contiguous elements (no alignment assumed)
 hipError_t launch_adamw_small(float* w, uint16_t* wb, const float* g, float* m, float* v, long n, float lr,
                               float b1, float b2, float eps, float wd, float bc1, float bc2, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Smear (x fp32 [N, d], rows b * T + t; gate weights and lambda are bf16)
+// ---------------------------------------------------------------------------
+int smear_partials_floats();
+// x <- smear(xe); a <- gate logits [N]
+hipError_t launch_smear_fwd(const float* xe, float* x, float* a, const uint16_t* pw, const uint16_t* plam, long N,
+                            int T, int d, hipStream_t s);
+// dxo <- gradient of xe from dy; *gw [24], *glam (+)= the gate's gradients
+hipError_t launch_smear_bwd(const float* dy, const float* xe, const float* a, float* dxo, const uint16_t* pw,
+                            const uint16_t* plam, long N, int T, int d, float* partials, float* gw, float* glam,
+                            int accumulate, hipStream_t s);

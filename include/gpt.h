@@ -96,6 +96,11 @@ int32_t gpt_kv_heads(const gpt_model* m);
  *   backout_layer  -1, or k in [0, depth): tensor backout_lambda [1, 1];
  *                  backout_lambda times the stream entering block k (after its
  *                  mix) is subtracted before the final norm
+ *   smear          1: tensors smear_gate [1, 24] and smear_lambda [1, 1]
+ *                  ("Truques de Eficiência" item 2); the embedding output
+ *                  becomes x_t + smear_lambda * sigmoid(smear_gate . x_t[0:24])
+ *                  * x_(t-1), x_(-1) = 0 at a sequence's first token (this is
+ *                  the x0 of the residual scalars)
  * Scalar tensors (kind GPT_KIND_SCALAR) follow lm_head in the flat layout and
  * belong to the AdamW group; gpt_fwd_bwd reads them from params_bf16 like
  * every weight and writes their gradients. Returns GPT_EINVAL for values out
@@ -106,6 +111,7 @@ typedef struct {
   int32_t kv_heads;
   int32_t resid_scalars;
   int32_t backout_layer;
+  int32_t smear;
 } gpt_config;
 gpt_status gpt_create_config(const gpt_config* cfg, gpt_model** out);
 /* The backout layer, or -1. */

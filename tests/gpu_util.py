@@ -45,8 +45,9 @@ def assert_scalar_grads(grads, ref_grads, scales, log=None):
     S = sum over rows of |g_row| |v_row| (the oracle reports S per scalar).
     Their error is at most |delta g| |v| <= eps S, eps being the relative error
     of the device's stream gradient (bounded by the 2e-2 gradient bar); the
-    errors measured on these models stay below 5e-5 S, so per scalar:
-    |delta| <= 2e-2 |ref| + 5e-4 S. A sign error or a wrong kept stream also
+    errors measured on these models stay below 5e-5 S, except the smear gate
+    at the end of the backward chain (up to 2.6e-4 S), so per scalar:
+    |delta| <= 2e-2 |ref| + 1e-3 S. A sign error or a wrong kept stream also
     breaks the matrix and embedding gradients that the same stream gradient
     feeds, which the rel-L2 checks catch."""
     for k, s in scales.items():
@@ -55,5 +56,5 @@ def assert_scalar_grads(grads, ref_grads, scales, log=None):
         sv = np.asarray(s).ravel()
         if log is not None:
             log(f"  {k}: |delta|/S = {np.max(np.abs(got - ref) / sv):.2e}")
-        tol = 2e-2 * np.abs(ref) + 5e-4 * sv
+        tol = 2e-2 * np.abs(ref) + 1e-3 * sv
         assert np.all(np.abs(got - ref) <= tol), (k, got, ref, sv)

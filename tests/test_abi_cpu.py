@@ -211,15 +211,16 @@ def test_gqa_create_rejects_kv_heads_that_do_not_divide():
     assert m.kv_heads == m.heads == 10
 
 
-@pytest.mark.parametrize("resid,backout", [(True, None), (False, 1), (True, 0)])
-def test_scalar_tensors_follow_lm_head(resid, backout):
+@pytest.mark.parametrize("resid,backout,smear", [(True, None, False), (False, 1, False), (True, 0, True),
+                                                (False, None, True)])
+def test_scalar_tensors_follow_lm_head(resid, backout, smear):
     depth, vocab = 3, 2048
-    m = binding.GptModel(depth, vocab, 128, None, resid, backout)
+    m = binding.GptModel(depth, vocab, 128, None, resid, backout, smear)
     assert m.backout_layer == backout
-    specs = syn.tensor_specs(depth, vocab, None, resid, backout is not None)
+    specs = syn.tensor_specs(depth, vocab, None, resid, backout is not None, smear)
     got = m.tensors()
     assert [(t["name"], t["rows"], t["cols"], t["kind"]) for t in got] == [sp[:4] for sp in specs]
-    n_scal = (2 * depth if resid else 0) + (1 if backout is not None else 0)
+    n_scal = (2 * depth if resid else 0) + (1 if backout is not None else 0) + (25 if smear else 0)
     assert m.adamw_state_elems() == 2 * vocab * m.d + n_scal
     assert m.num_params == sum(r * c for _, r, c, _, _ in specs)
 
@@ -228,7 +229,8 @@ def test_config_validation():
     lib = binding.lib()
     h = C.c_void_p()
     bad = [binding.GptConfig(3, 2048, 128, 0, 2, -1), binding.GptConfig(3, 2048, 128, 0, 0, 3),
-           binding.GptConfig(3, 2048, 128, 0, 0, -2), binding.GptConfig(0, 2048, 128, 0, 1, -1)]
+           binding.GptConfig(3, 2048, 128, 0, 0, -2), binding.GptConfig(0, 2048, 128, 0, 1, -1),
+           binding.GptConfig(3, 2048, 128, 0, 0, -1, 2)]
     for cfg in bad:
         assert lib.gpt_create_config(C.byref(cfg), C.byref(h)) == binding.GPT_EINVAL
     assert lib.gpt_create_config(None, C.byref(h)) == binding.GPT_EINVAL

@@ -9,8 +9,8 @@ For each depth:
 * One sequence through the whole model against the fp64 oracle, which is
   given the bf16 weights gpt_fwd_bwd computes with (at d12 and d20 also with
   the "SSSL" window pattern, short window seq / 2, and at d20 with 2 key/value
-  heads for the 10 query heads, and with residual scalars and a backout at layer
-  10): loss |delta| <= 1e-2,
+  heads for the 10 query heads, and with residual scalars, a backout at layer
+  10 and smear): loss |delta| <= 1e-2,
   every gradient tensor rel-L2 <= 2e-2, embedding rows of absent tokens exactly
   zero. The sequence is the workload's full length except at d32, where it is
   1024 tokens: the fp64 oracle of a 32-layer model at 4096 tokens needs about
@@ -74,14 +74,16 @@ def test_one_sequence_matches_oracle(name, pattern, kv_heads, scalars):
     log(f"{name} one sequence of {T} vs oracle" + (f", windows {pattern} (short {T // 2})" if pattern else "")
         + (f", {kv_heads} kv heads" if kv_heads else ""))
     backout = L // 2 if scalars else None
-    w = syn.init_weights(L, V, seed=0, kv_heads=kv_heads, resid_scalars=scalars, backout=scalars)
+    w = syn.init_weights(L, V, seed=0, kv_heads=kv_heads, resid_scalars=scalars, backout=scalars, smear=scalars)
     if scalars:
+        w["smear_gate"] = (np.random.default_rng(4).standard_normal((1, 24)) * 2.0).astype(np.float32)
+        w["smear_lambda"] = np.array([[0.5]], dtype=np.float32)
         rng = np.random.default_rng(3)
         w["resid_lambdas"] = rng.uniform(0.7, 1.3, size=(1, L)).astype(np.float32)
         w["x0_lambdas"] = rng.uniform(-0.3, 0.3, size=(1, L)).astype(np.float32)
         w["backout_lambda"] = np.array([[0.9]], dtype=np.float32)
     tok, tgt = syn.split_tokens(syn.zipf_ids(1, T, V, seed=1))
-    st = TrainState(L, V, T, 1, kv_heads=kv_heads, resid_scalars=scalars, backout_layer=backout)
+    st = TrainState(L, V, T, 1, kv_heads=kv_heads, resid_scalars=scalars, backout_layer=backout, smear=scalars)
     st.load_weights(w)
     st.set_windows(windows)
     st.fwd_bwd(_cuda(tok), _cuda(tgt))

@@ -31,15 +31,18 @@ def _random_scalars(w, depth, seed, backout_value=None):
     if "backout_lambda" in w:
         v = rng.uniform(0.1, 0.6) if backout_value is None else backout_value
         w["backout_lambda"] = np.array([[v]], dtype=np.float32)
+    if "smear_gate" in w:
+        w["smear_gate"] = (rng.standard_normal((1, 24)) * 2.0).astype(np.float32)
+        w["smear_lambda"] = np.array([[rng.uniform(0.3, 0.9)]], dtype=np.float32)
     return w
 
 
 def _run_case(depth, vocab, seq, batch, seed_w=0, seed_t=1, ignore=(), windows=None, kv_heads=None,
-              resid_scalars=False, backout_layer=None, std=syn.INIT_STD, backout_value=None):
+              resid_scalars=False, backout_layer=None, std=syn.INIT_STD, backout_value=None, smear=False):
     log(f"fwd_bwd depth={depth} vocab={vocab} seq={seq} batch={batch} windows={windows} kv_heads={kv_heads}"
         f" resid_scalars={resid_scalars} backout_layer={backout_layer}")
     w = syn.init_weights(depth, vocab, seed=seed_w, std=std, kv_heads=kv_heads, resid_scalars=resid_scalars,
-                         backout=backout_layer is not None)
+                         backout=backout_layer is not None, smear=smear)
     w = _random_scalars(w, depth, seed_w + 50, backout_value)
     ids = syn.zipf_ids(batch, seq, vocab, seed=seed_t)
     tok, tgt = syn.split_tokens(ids)
@@ -47,7 +50,7 @@ def _run_case(depth, vocab, seq, batch, seed_w=0, seed_t=1, ignore=(), windows=N
     for (b, t) in ignore:
         tgt[b, t] = -1
     st = TrainState(depth, vocab, seq, batch, kv_heads=kv_heads, resid_scalars=resid_scalars,
-                    backout_layer=backout_layer)
+                    backout_layer=backout_layer, smear=smear)
     st.load_weights(w)
     st.set_windows(windows)
     tok_d = torch.from_numpy(tok).cuda()
@@ -166,9 +169,10 @@ def test_gqa_muon_matches_oracle(normuon):
         np.testing.assert_array_equal(new_w[k], w[k])
 
 
-@pytest.mark.parametrize("depth,vocab,seq,batch,resid,backout", [(2, 2048, 64, 2, True, 1), (3, 2048, 200, 3, True, 0),
-                                                                (4, 2048, 128, 2, False, 2), (4, 2048, 128, 2, True, None)])
-def test_scalars_fwd_bwd_matches_oracle(depth, vocab, seq, batch, resid, backout):
+@pytest.mark.parametrize("depth,vocab,seq,batch,resid,backout,smear", [
+    (2, 2048, 64, 2, True, 1, False), (3, 2048, 200, 3, True, 0, False), (4, 2048, 128, 2, False, 2, False),
+    (4, 2048, 128, 2, True, None, False), (2, 2048, 64, 2, False, None, True), (3, 2048, 200, 3, True, 1, True)])
+def test_scalars_fwd_bwd_matches_oracle(depth, vocab, seq, batch, resid, backout, smear):
     """Residual scalars (random values) and backout at various layers, with a
     ragged length; the scalar gradients are full reductions over tokens, checked
     against their Cauchy-Schwarz scale (gpu_util.assert_scalar_grads). Weights
@@ -176,12 +180,12 @@ def test_scalars_fwd_bwd_matches_oracle(depth, vocab, seq, batch, resid, backout
     the final one, so the backout gradient is not cancelled to noise."""
     st, tok, tgt, loss, grads, ref_loss, ref_grads = _run_case(depth, vocab, seq, batch, seed_w=2, seed_t=3,
                                                                 resid_scalars=resid, backout_layer=backout,
-                                                                std=0.1, backout_value=0.9)
+                                                                std=0.1, backout_value=0.9, smear=smear)
     assert abs(loss - ref_loss) <= LOSS_TOL
-    scalars = ("resid_lambdas", "x0_lambdas", "backout_lambda")
+    scalars = ("resid_lambdas", "x0_lambdas", "backout_lambda", "smear_gate", "smear_lambda")
     _assert_grads(grads, ref_grads, tok, vocab, skip=scalars)
     assert_scalar_grads(grads, ref_grads, _run_case.scales, log)
-    if backout is not None:  # the backout gradient is well above its noise floor here
+    if backout is not None and not smear:  # these cases keep the backout gradient above its noise floor
         assert abs(ref_grads["backout_lambda"][0, 0]) > 1e-3 * _run_case.scales["backout_lambda"][0, 0]
     # Accumulation: a second identical call with accumulate=1 doubles every gradient.
     toks = torch.from_numpy(tok).cuda()
@@ -189,23 +193,27 @@ def test_scalars_fwd_bwd_matches_oracle(depth, vocab, seq, batch, resid, backout
     st.fwd_bwd(toks, tgts, accumulate=True)
     torch.cuda.synchronize()
     g2 = st.to_host(st.grads)
-    for k in ("resid_lambdas", "x0_lambdas", "backout_lambda"):
+    for k in scalars:
         if k in grads:
             np.testing.assert_allclose(g2[k], 2 * grads[k], rtol=1e-5, atol=1e-9)
 
 
 def test_adamw_updates_scalar_tensors():
     depth, vocab = 3, 2048
-    w = _random_scalars(syn.init_weights(depth, vocab, seed=0, resid_scalars=True, backout=True), depth, 1)
-    g = syn.random_like_grads(depth, vocab, seed=7, scale=1e-2, resid_scalars=True, backout=True)
-    st = TrainState(depth, vocab, 64, 1, resid_scalars=True, backout_layer=1)
+    w = _random_scalars(syn.init_weights(depth, vocab, seed=0, resid_scalars=True, backout=True, smear=True),
+                        depth, 1)
+    # (Updates are compared as w - w_new in fp32: weights near 1e-1 keep the
+    # fp32 spacing of w far below the 1e-5 bar for updates of about lr.)
+    w["smear_gate"] *= np.float32(0.05)
+    g = syn.random_like_grads(depth, vocab, seed=7, scale=1e-2, resid_scalars=True, backout=True, smear=True)
+    st = TrainState(depth, vocab, 64, 1, resid_scalars=True, backout_layer=1, smear=True)
     st.load_weights(w)
     st.load_grads(g)
     a = ADAMW
     st.adamw(a["lr"], a["beta1"], a["beta2"], a["eps"], a["weight_decay"], 1)
     torch.cuda.synchronize()
     new_w = st.to_host(st.params)
-    names = ("wte", "lm_head", "resid_lambdas", "x0_lambdas", "backout_lambda")
+    names = ("wte", "lm_head", "resid_lambdas", "x0_lambdas", "backout_lambda", "smear_gate", "smear_lambda")
     f64 = lambda dd: {k: v.astype(np.float64) for k, v in dd.items()}
     z = {k: np.zeros(w[k].shape) for k in names}
     ref_w, _, _ = oracle.adamw_step(f64(w), f64(g), z, z, 1, a["lr"], a["beta1"], a["beta2"], a["eps"],
