@@ -65,10 +65,13 @@ def model_dims(depth: int) -> dict:
     return dict(depth=depth, d=d, heads=d // HEAD_DIM, mlp=4 * d)
 
 
-def tensor_specs(depth: int, vocab: int, kv_heads=None, resid_scalars=False, backout=False, smear=False):
+def tensor_specs(depth: int, vocab: int, kv_heads=None, resid_scalars=False, backout=False, smear=False,
+                 ve_layers=()):
     """Canonical tensor order: wte; per layer wq, wk, wv, wo, wfc, wproj; lm_head;
-    then the optional scalar tensors resid_lambdas [1, depth], x0_lambdas
-    [1, depth], backout_lambda [1, 1], smear_gate [1, 24] and smear_lambda [1, 1].
+    then, for each layer i in ve_layers (ascending), the value embedding
+    h{i}.ve [vocab, kv_heads*128] and its gate h{i}.ve_gate [kv_heads, 32]; then
+    the optional scalar tensors resid_lambdas [1, depth], x0_lambdas [1, depth],
+    backout_lambda [1, 1], smear_gate [1, 24] and smear_lambda [1, 1].
 
     Each entry is (name, rows, cols, kind, layer) with kind in
     {"emb", "matrix", "lm_head", "scalar"}; matrices are [out, in] as in a
@@ -89,6 +92,9 @@ def tensor_specs(depth: int, vocab: int, kv_heads=None, resid_scalars=False, bac
             (f"h{layer}.wproj", d, f, "matrix", layer),
         ]
     specs.append(("lm_head", vocab, d, "lm_head", -1))
+    for layer in sorted(ve_layers):
+        specs += [(f"h{layer}.ve", vocab, dkv, "emb", layer),
+                  (f"h{layer}.ve_gate", dkv // HEAD_DIM, 32, "gate", layer)]
     if resid_scalars:
         specs += [("resid_lambdas", 1, depth, "scalar", -1), ("x0_lambdas", 1, depth, "scalar", -1)]
     if backout:
@@ -105,12 +111,13 @@ SCALAR_INIT = {"resid_lambdas": 1.0, "x0_lambdas": 0.0, "backout_lambda": 0.0, "
 
 
 def init_weights(depth: int, vocab: int, seed: int = 0, std: float = INIT_STD, kv_heads=None,
-                 resid_scalars=False, backout=False, smear=False) -> dict:
+                 resid_scalars=False, backout=False, smear=False, ve_layers=()) -> dict:
     """Every matrix N(0, std^2), float32, drawn in canonical order from one seed;
     scalar tensors take SCALAR_INIT (no draw)."""
     rng = np.random.default_rng(seed)
     out = {}
-    for name, rows, cols, kind, _layer in tensor_specs(depth, vocab, kv_heads, resid_scalars, backout, smear):
+    for name, rows, cols, kind, _layer in tensor_specs(depth, vocab, kv_heads, resid_scalars, backout, smear,
+                                                       ve_layers):
         if kind == "scalar":
             out[name] = np.full((rows, cols), SCALAR_INIT[name], dtype=np.float32)
             continue
@@ -143,11 +150,12 @@ def split_tokens(ids: np.ndarray):
 
 
 def random_like_grads(depth: int, vocab: int, seed: int, scale: float = 1e-3, kv_heads=None,
-                      resid_scalars=False, backout=False, smear=False) -> dict:
+                      resid_scalars=False, backout=False, smear=False, ve_layers=()) -> dict:
     """Seeded Gaussian arrays shaped like the parameters (for optimizer-only cases)."""
     rng = np.random.default_rng(seed)
     out = {}
-    for name, rows, cols, _kind, _layer in tensor_specs(depth, vocab, kv_heads, resid_scalars, backout, smear):
+    for name, rows, cols, _kind, _layer in tensor_specs(depth, vocab, kv_heads, resid_scalars, backout, smear,
+                                                        ve_layers):
         g = rng.standard_normal((rows, cols), dtype=np.float32)
         g *= np.float32(scale)
         out[name] = g

@@ -49,16 +49,18 @@ SCALAR_TENSORS = ("resid_lambdas", "x0_lambdas", "backout_lambda", "smear_gate",
 
 
 def adamw_step(weights, grads, exp_avg, exp_avg_sq, step, lr, beta1, beta2, eps, wd):
-    """AdamW on wte, lm_head and the scalar tensors the model has ([CT50] "2.
-    Otimizador Muon": scalars are in the AdamW group too); every other tensor
-    is copied unchanged.
+    """AdamW on wte, lm_head, the value embeddings and their gates, and the
+    scalar tensors the model has ([CT50] "2. Otimizador Muon": embeddings and
+    scalars are in the AdamW group; the small value-embedding gates join them
+    here); every other tensor is copied unchanged.
 
     exp_avg / exp_avg_sq are dicts holding the moments of those tensors.
     Returns (new weights, new exp_avg, new exp_avg_sq).
     """
     new_w = {k: v.copy() for k, v in weights.items()}
     new_m, new_v = {}, {}
-    for k in ADAMW_TENSORS + tuple(t for t in SCALAR_TENSORS if t in weights):
+    group = ADAMW_TENSORS + tuple(k for k in weights if k.endswith((".ve", ".ve_gate")))
+    for k in group + tuple(t for t in SCALAR_TENSORS if t in weights):
         new_w[k], new_m[k], new_v[k] = adamw_update(weights[k], grads[k], exp_avg[k], exp_avg_sq[k],
                                                     step, lr, beta1, beta2, eps, wd)
     return new_w, new_m, new_v

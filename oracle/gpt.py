@@ -40,6 +40,11 @@ embedding output becomes x_t + smear_lambda * sigmoid(smear_gate . x_t[:24])
 * x_(t-1) (zero before a sequence's first token); this is the x0 that the
 residual scalars mix in.
 
+Value embeddings (optional, per layer): with tensors h{i}.ve [V, Hkv*128]
+and h{i}.ve_gate [Hkv, 32], block i adds to v, per key/value head, the
+token's table row gated by 3 * sigmoid(ve_gate . xn[:32]), xn being the
+block's normalised input (the input of its QKV projection).
+
 Grouped-query attention (optional): the pages list "fewer KV heads". When wk
 and wv have Hkv * 128 rows (Hkv dividing H), query head h attends with key and
 value head h // (H / Hkv); QK-norm and RoPE act per head as before.
@@ -185,6 +190,7 @@ def _scalars(weights):
 
 
 SMEAR_CHANNELS = 24
+VE_GATE_CHANNELS = 32
 
 
 def _smear(x, weights):
@@ -257,6 +263,15 @@ def _forward_sequence(weights, tok, cos, sin, final_norm=True, windows=None, bac
         q = (xn1 @ w["wq"].T).reshape(T, H, HEAD_DIM)
         k = (xn1 @ w["wk"].T).reshape(T, -1, HEAD_DIM)
         v = (xn1 @ w["wv"].T).reshape(T, -1, HEAD_DIM)
+        ve_name = f"h{layer}.ve"
+        ve_logit = None
+        if ve_name in weights:
+            # Value embeddings ([CT50] "Embeddings de Valor (ResFormer)"): a
+            # per-layer table row of the token, gated per key/value head by
+            # 3 sigmoid(ve_gate . xn1[:32]), is added to v.
+            ve = weights[ve_name][tok].reshape(T, -1, HEAD_DIM)
+            ve_logit = xn1[:, :VE_GATE_CHANNELS] @ weights[f"h{layer}.ve_gate"].T
+            v = v + (3.0 / (1.0 + np.exp(-ve_logit)))[:, :, None] * ve
         qn, rq = rms_norm(q)
         kn, rk = rms_norm(k)
         qr, kr = rope(qn, cos, sin), rope(kn, cos, sin)
@@ -268,7 +283,7 @@ def _forward_sequence(weights, tok, cos, sin, final_norm=True, windows=None, bac
         a = np.maximum(u, 0.0) ** 2
         x = x_mid + a @ w["wproj"].T
         layers.append(dict(xn1=xn1, r1=r1, qn=qn, rq=rq, kn=kn, rk=rk, qr=qr, kr=kr,
-                           v=v, p=p, o2=o2, xn2=xn2, r2=r2, u=u, a=a, x_prev=x_prev))
+                           v=v, p=p, o2=o2, xn2=xn2, r2=r2, u=u, a=a, x_prev=x_prev, ve_logit=ve_logit))
     if backout_layer is not None:
         x = x - bl * x_backout
     if final_norm:
@@ -380,11 +395,22 @@ def forward_backward(weights, tokens, targets, final_norm=True, want_grads=True,
             dqr, dkr, dv = causal_attention_bwd(do, s["qr"], s["kr"], s["v"], s["p"])
             dq = rms_norm_bwd(rope_bwd(dqr, cos, sin), s["qn"], s["rq"]).reshape(T, d)
             dk = rms_norm_bwd(rope_bwd(dkr, cos, sin), s["kn"], s["rk"]).reshape(T, -1)
+            dxn1_ve = 0.0
+            if s["ve_logit"] is not None:
+                # v = v_proj + gate * ve, gate = 3 sigmoid(logit), logit = xn1[:32] . ve_gate
+                ve_name = f"h{layer}.ve"
+                ve = weights[ve_name][tok].reshape(T, -1, HEAD_DIM)
+                sig = 1.0 / (1.0 + np.exp(-s["ve_logit"]))
+                np.add.at(grads[ve_name], tok, (3.0 * sig[:, :, None] * dv).reshape(T, -1))
+                dlogit = 3.0 * sig * (1.0 - sig) * np.sum(dv * ve, axis=-1)   # [T, Hkv]
+                grads[f"h{layer}.ve_gate"] += dlogit.T @ s["xn1"][:, :VE_GATE_CHANNELS]
+                dxn1_ve = np.zeros_like(s["xn1"])
+                dxn1_ve[:, :VE_GATE_CHANNELS] = dlogit @ weights[f"h{layer}.ve_gate"]
             dv = dv.reshape(T, -1)
             grads[g["wq"]] += dq.T @ s["xn1"]
             grads[g["wk"]] += dk.T @ s["xn1"]
             grads[g["wv"]] += dv.T @ s["xn1"]
-            dxn1 = dq @ w["wq"] + dk @ w["wk"] + dv @ w["wv"]
+            dxn1 = dq @ w["wq"] + dk @ w["wk"] + dv @ w["wv"] + dxn1_ve
             dx = dx_mid + rms_norm_bwd(dxn1, s["xn1"], s["r1"])
             # dx is now the gradient of the stream entering block `layer`.
             if backout_layer == layer:

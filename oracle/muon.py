@@ -68,7 +68,7 @@ def muon_step(weights, grads, momentum, lr, mu, coeffs, steps=None, names=None):
     prefix, i.e. the block matrices). Other tensors are copied unchanged.
     """
     if names is None:
-        names = [k for k in weights if k.startswith("h")]
+        names = [k for k in weights if k.startswith("h") and not k.endswith((".ve", ".ve_gate"))]
     new_w = {k: v.copy() for k, v in weights.items()}
     new_m = {k: v.copy() for k, v in momentum.items()}
     updates = {}

@@ -70,7 +70,7 @@ def normuon_step(weights, grads, momentum, second_moment, lr, mu, beta2, coeffs,
     are copied unchanged.
     """
     if names is None:
-        names = [k for k in weights if k.startswith("h")]
+        names = [k for k in weights if k.startswith("h") and not k.endswith((".ve", ".ve_gate"))]
     new_w = {k: v.copy() for k, v in weights.items()}
     new_m = {k: v.copy() for k, v in momentum.items()}
     new_v = {k: v.copy() for k, v in second_moment.items()}

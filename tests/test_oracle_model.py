@@ -363,6 +363,77 @@ def test_smear_gradients_match_central_differences():
 
 
 # ----------------------------------------------------------------------------
+# Value embeddings
+# ----------------------------------------------------------------------------
+def _ve_weights(depth, vocab, ve_layers, kv_heads=None, seed=3, std=0.15):
+    w = syn.init_weights(depth, vocab, seed=seed, std=std, kv_heads=kv_heads, ve_layers=ve_layers)
+    return {k: v.astype(np.float64) for k, v in w.items()}
+
+
+def test_zero_value_embedding_is_the_plain_model():
+    depth, vocab, seq = 2, 128, 10
+    w = _tiny_weights(depth, vocab, seed=4, std=0.1)
+    wv = dict(w)
+    wv["h1.ve"] = np.zeros((vocab, 128))
+    wv["h1.ve_gate"] = np.random.default_rng(2).standard_normal((1, 32))
+    tok, tgt = _ids(2, seq, vocab, seed=6)
+    loss, grads = oracle.forward_backward(w, tok, tgt)
+    loss_v, grads_v = oracle.forward_backward(wv, tok, tgt)
+    assert loss_v == loss
+    for k in grads:
+        np.testing.assert_array_equal(grads_v[k], grads[k])
+    assert not np.any(grads_v["h1.ve_gate"])
+    present = np.unique(tok)
+    assert np.all(np.abs(grads_v["h1.ve"][present]).sum(axis=1) > 0)
+    absent = np.setdiff1d(np.arange(vocab), present)
+    assert not np.any(grads_v["h1.ve"][absent])
+
+
+def test_value_embedding_matches_a_head_loop():
+    depth, vocab, seq, kvh = 4, 64, 6, 1  # width 256: 2 query heads, 1 key/value head
+    w = _ve_weights(depth, vocab, (0,), kv_heads=kvh)
+    tok, _ = _ids(1, seq, vocab, seed=2)
+    cos, sin = og.rope_tables(seq)
+    _, c = og._forward_sequence(w, tok[0], cos, sin)
+    s0 = c["layers"][0]
+    v_total = s0["v"]
+    for t in range(seq):
+        xn = s0["xn1"][t]
+        for h in range(kvh):
+            logit = sum(w["h0.ve_gate"][h, j] * xn[j] for j in range(32))
+            gate = 3.0 / (1.0 + math.exp(-logit))
+            for e in range(0, 128, 11):
+                proj = sum(xn[j] * w["h0.wv"][h * 128 + e, j] for j in range(xn.shape[0]))
+                want = proj + gate * w["h0.ve"][tok[0, t], h * 128 + e]
+                assert abs(v_total[t, h, e] - want) < 1e-11
+
+
+@pytest.mark.parametrize("kv_heads,ve_layers", [(None, (0, 1)), (1, (1, 3))])
+def test_value_embedding_gradients_match_central_differences(kv_heads, ve_layers):
+    depth = 2 if kv_heads is None else 4
+    vocab, seq, batch = 96, 10, 2
+    w = _ve_weights(depth, vocab, ve_layers, kv_heads=kv_heads)
+    rng = np.random.default_rng(17)
+    for l in ve_layers:
+        w[f"h{l}.ve_gate"] = rng.standard_normal(w[f"h{l}.ve_gate"].shape) * 0.5
+    tok, tgt = _ids(batch, seq, vocab, seed=5)
+    loss, grads = oracle.forward_backward(w, tok, tgt)
+    h = 1e-5
+
+    def f(ww):
+        return oracle.forward_backward(ww, tok, tgt, want_grads=False)[0]
+
+    for name in w:
+        u = rng.standard_normal(w[name].shape)
+        u /= np.linalg.norm(u)
+        wp = dict(w); wp[name] = w[name] + h * u
+        wm = dict(w); wm[name] = w[name] - h * u
+        fd = (f(wp) - f(wm)) / (2 * h)
+        an = float(np.sum(grads[name] * u))
+        assert abs(fd - an) <= 1e-6 * abs(an) + 1e-9, (name, fd, an)
+
+
+# ----------------------------------------------------------------------------
 # Grouped-query attention: equal to full multi-head attention whose key/value
 # weights repeat each group's rows (an independent path: no head sharing)
 # ----------------------------------------------------------------------------
