@@ -15,7 +15,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgptstep.so")
 
 GPT_OK, GPT_EINVAL, GPT_ESHAPE, GPT_EHIP, GPT_ETOKEN, GPT_EWORKSPACE = 0, -1, -2, -3, -4, -5
-KIND_NAMES = {0: "emb", 1: "matrix", 2: "lm_head", 3: "scalar"}
+KIND_NAMES = {0: "emb", 1: "matrix", 2: "lm_head", 3: "scalar", 4: "gate"}
 
 # gpt_op_gemm out_mode values
 OUT_F32, OUT_F32_ACC, OUT_BF16, OUT_RELU_BF16, OUT_RESID_BF16 = 0, 1, 2, 3, 4
@@ -41,6 +41,7 @@ class GptConfig(C.Structure):
         ("resid_scalars", C.c_int32),
         ("backout_layer", C.c_int32),
         ("smear", C.c_int32),
+        ("ve_layers", C.c_int64),
     ]
 
 
@@ -148,9 +149,9 @@ class GptModel:
     """Host-side plan of a model (no device memory)."""
 
     def __init__(self, depth: int, vocab: int, max_seq: int, kv_heads=None, resid_scalars=False,
-                 backout_layer=None, smear=False):
+                 backout_layer=None, smear=False, ve_layers=()):
         h = C.c_void_p()
-        if not resid_scalars and backout_layer is None and not smear:
+        if not resid_scalars and backout_layer is None and not smear and not ve_layers:
             if kv_heads is None:
                 _check(lib().gpt_create(depth, vocab, max_seq, C.byref(h)), "gpt_create")
             else:
@@ -158,7 +159,7 @@ class GptModel:
         else:
             cfg = GptConfig(depth, vocab, max_seq, 0 if kv_heads is None else int(kv_heads),
                             1 if resid_scalars else 0, -1 if backout_layer is None else int(backout_layer),
-                            1 if smear else 0)
+                            1 if smear else 0, sum(1 << int(l) for l in set(ve_layers)))
             _check(lib().gpt_create_config(C.byref(cfg), C.byref(h)), "gpt_create_config")
         self._h = h
         dims = (C.c_int32 * 6)()

@@ -898,6 +898,122 @@ __global__ void smear_grads_kernel(const float* __restrict__ partials, int nb, f
   *out = accumulate ? *out + t : t;
 }
 
+// Value embeddings ([CT50] "Embeddings de Valor (ResFormer)"): per token
+// row and key/value head h, logit_h = ve_gate[h] . xn[0:32], and
+// v_h += 3 sigmoid(logit_h) * ve[token][h*128 .. h*128+127]. v lives in qkv
+// ([N, (H + 2 Hkv) * 128] bf16, columns d + dkv ..); xn is the block's
+// normalised input (bf16 [N, d]). One wave per row; logits saved [N, Hkv].
+constexpr int VE_CH = 32;
+
+__global__ void __launch_bounds__(256) ve_fwd_kernel(uint16_t* __restrict__ qkv, const uint16_t* __restrict__ xn,
+                                                     const int32_t* __restrict__ tok,
+                                                     const uint16_t* __restrict__ table,
+                                                     const uint16_t* __restrict__ gate, float* __restrict__ logits,
+                                                     long N, int d, int Hkv, int V) {
+  const long row = blockIdx.x * 4L + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= N) return;
+  const int dkv = Hkv * 128;
+  const float xj = lane < VE_CH ? bf2f(xn[row * d + lane]) : 0.f;
+  const int t = tok[row];
+  const bool ok = t >= 0 && t < V;
+  uint16_t* v = qkv + row * (long)(d + 2 * dkv) + d + dkv;
+  const uint16_t* e = table + (long)(ok ? t : 0) * dkv;
+  for (int h = 0; h < Hkv; ++h) {
+    const float lg = warp_sum(lane < VE_CH ? bf2f(gate[h * VE_CH + lane]) * xj : 0.f);
+    if (lane == 0) logits[row * Hkv + h] = lg;
+    const float g = ok ? 3.f / (1.f + __expf(-lg)) : 0.f;
+    // 128 elements of head h: 16 chunks of 8, lanes 0..15.
+    if (lane < 16) {
+      const int c = h * 128 + 8 * lane;
+      float a[8], b[8];
+      unpack8(*reinterpret_cast<const uint4*>(v + c), a);
+      unpack8(*reinterpret_cast<const uint4*>(e + c), b);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) a[k] += g * b[k];
+      *reinterpret_cast<uint4*>(v + c) = pack8(a);
+    }
+  }
+}
+
+// Backward with dv the gradient of v (in dqkv): per row and head,
+// s_h = dv_h . ve_h, dlogit_h = 3 sig (1 - sig) s_h (saved [N, Hkv]);
+// dtable[token] += 3 sig dv_h (fp32 atomics, as the embedding); block partials
+// of d ve_gate[h][j] = sum dlogit_h xn[j] go to partials[blockIdx.x][Hkv*32].
+// Grid-stride over rows, one wave per row, 4 waves per block.
+__global__ void __launch_bounds__(256) ve_bwd_kernel(const uint16_t* __restrict__ dqkv,
+                                                     const uint16_t* __restrict__ xn,
+                                                     const int32_t* __restrict__ tok,
+                                                     const uint16_t* __restrict__ table,
+                                                     const float* __restrict__ logits, float* __restrict__ dtable,
+                                                     float* __restrict__ dlogit, float* __restrict__ partials,
+                                                     long N, int d, int Hkv, int V) {
+  __shared__ float red[4][16 * VE_CH];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int dkv = Hkv * 128;
+  float acc[16];
+#pragma unroll
+  for (int h = 0; h < 16; ++h) acc[h] = 0.f;
+  for (long row = blockIdx.x * 4L + wave; row < N; row += gridDim.x * 4L) {
+    const int t = tok[row];
+    const bool ok = t >= 0 && t < V;
+    const uint16_t* dv = dqkv + row * (long)(d + 2 * dkv) + d + dkv;
+    const uint16_t* e = table + (long)(ok ? t : 0) * dkv;
+    float* dt = dtable + (long)(ok ? t : 0) * dkv;
+    const float xj = lane < VE_CH ? bf2f(xn[row * d + lane]) : 0.f;
+#pragma unroll
+    for (int h = 0; h < 16; ++h) {  // unrolled so that acc[h] stays in registers
+      if (h >= Hkv) break;
+      const float lg = logits[row * Hkv + h];
+      const float sig = 1.f / (1.f + __expf(-lg));
+      float part = 0.f;
+      if (lane < 16) {
+        const int c = h * 128 + 8 * lane;
+        float a[8], b[8];
+        unpack8(*reinterpret_cast<const uint4*>(dv + c), a);
+        unpack8(*reinterpret_cast<const uint4*>(e + c), b);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) part += a[k] * b[k];
+        if (ok) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) unsafeAtomicAdd(dt + c + k, 3.f * sig * a[k]);
+        }
+      }
+      const float sh = warp_sum(part);
+      const float dl = ok ? 3.f * sig * (1.f - sig) * sh : 0.f;
+      if (lane == 0) dlogit[row * Hkv + h] = dl;
+      acc[h] += dl * xj;
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < 16; ++h)
+    if (h < Hkv && lane < VE_CH) red[wave][h * VE_CH + lane] = acc[h];
+  __syncthreads();
+  for (int i = threadIdx.x; i < Hkv * VE_CH; i += blockDim.x)
+    partials[(long)blockIdx.x * Hkv * VE_CH + i] = red[0][i] + red[1][i] + red[2][i] + red[3][i];
+}
+
+// dxn[row][j] += sum_h dlogit[row][h] * ve_gate[h][j], j < 32.
+__global__ void ve_dxn_kernel(float* __restrict__ dxn, const float* __restrict__ dlogit,
+                              const uint16_t* __restrict__ gate, long N, int d, int Hkv) {
+  const long i = blockIdx.x * (long)blockDim.x + threadIdx.x;
+  if (i >= N * VE_CH) return;
+  const long row = i / VE_CH;
+  const int j = (int)(i - row * VE_CH);
+  float a = 0.f;
+  for (int h = 0; h < Hkv; ++h) a += dlogit[row * Hkv + h] * bf2f(gate[h * VE_CH + j]);
+  dxn[row * d + j] += a;
+}
+
+// grads (+)= column sums of partials [nb][n] in block order.
+__global__ void column_sums_kernel(const float* __restrict__ partials, int nb, int n, float* out, int accumulate) {
+  const int k = blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= n) return;
+  float t = 0.f;
+  for (int i = 0; i < nb; ++i) t += partials[(long)i * n + k];
+  out[k] = accumulate ? out[k] + t : t;
+}
+
 // AdamW on one contiguous fp32 tensor and its moments ([CT50] "2. Otimizador
 // Muon": embeddings and lm_head are in the AdamW group). Decoupled decay scaled
 // by lr and taken from the weights before the step; bias corrections
@@ -1233,5 +1349,50 @@ hipError_t launch_smear_bwd(const float* dy, const float* xe, const float* a, fl
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(smear_grads_kernel, dim3(1), dim3(64), 0, s, static_cast<const float*>(partials), kSmearBlocks,
                      gw, glam, accumulate);
+  return hipGetLastError();
+}
+
+// ---- value embeddings
+namespace {
+constexpr int kVeBlocks = 256;
+}
+int ve_partials_floats(int Hkv) { return kVeBlocks * Hkv * VE_CH; }
+
+hipError_t launch_ve_fwd(uint16_t* qkv, const uint16_t* xn, const int32_t* tok, const uint16_t* table,
+                         const uint16_t* gate, float* logits, long N, int d, int Hkv, int V, hipStream_t s) {
+  if (Hkv > 16) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(ve_fwd_kernel, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s, qkv, xn, tok, table, gate,
+                     logits, N, d, Hkv, V);
+  return hipGetLastError();
+}
+
+hipError_t launch_ve_bwd(const uint16_t* dqkv, const uint16_t* xn, const int32_t* tok, const uint16_t* table,
+                         const uint16_t* gate, const float* logits, float* dtable, float* dlogit, float* partials,
+                         float* dgate, float* dxn, long N, int d, int Hkv, int V, int accumulate, hipStream_t s) {
+  if (Hkv > 16) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(ve_bwd_kernel, dim3(kVeBlocks), dim3(256), 0, s, dqkv, xn, tok, table, logits, dtable, dlogit,
+                     partials, N, d, Hkv, V);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n = Hkv * VE_CH;
+  hipLaunchKernelGGL(column_sums_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     static_cast<const float*>(partials), kVeBlocks, n, dgate, accumulate);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(ve_dxn_kernel, dim3((unsigned)((N * VE_CH + 255) / 256)), dim3(256), 0, s, dxn,
+                     static_cast<const float*>(dlogit), gate, N, d, Hkv);
+  return hipGetLastError();
+}
+
+hipError_t launch_adamw_range(float* w, uint16_t* wb, const float* g, float* m, float* v, long n, float lr,
+                              float b1, float b2, float eps, float wd, float bc1, float bc2, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (n % 4 != 0) return hipErrorInvalidValue;
+  AdamwArgs a;
+  a.w = w; a.wb = wb; a.g = g; a.m = m; a.v = v;
+  a.woff[0] = 0; a.woff[1] = 0;
+  a.n = n;
+  a.lr = lr; a.b1 = b1; a.b2 = b2; a.eps = eps; a.wd = wd; a.bc1 = bc1; a.bc2 = bc2;
+  hipLaunchKernelGGL(adamw_kernel, dim3(grid_for(n / 4, 256, 2048), 1), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -37,6 +37,9 @@ struct gpt_model {
   // x0_lambdas [L], backout_lambda (-1 when absent); the backout layer.
   int64_t off_rl = -1, off_xl = -1, off_bl = -1, off_scalars = -1, n_scalars = 0;
   int64_t off_sg = -1, off_sl = -1;  // smear_gate [24], smear_lambda (-1 when absent)
+  // Value embeddings: per layer, offsets of h{l}.ve [V, dkv] and h{l}.ve_gate [Hkv, 32] (-1: none).
+  std::vector<int64_t> ve_off, veg_off;
+  bool any_ve = false;
   int backout_layer = -1;
   std::vector<gpt_tensor> tensors;
   int64_t nparams = 0;
@@ -132,6 +135,7 @@ struct FwdPlan {
   // residual scalars / backout (0 when the model has none)
   size_t x0 = 0, dx0 = 0, red = 0, xprev = 0, xbo = 0, dback = 0;
   size_t xe = 0, sa = 0, sred = 0;  // smear: embedding output, gate logits, partials
+  size_t velog = 0, vedl = 0, vered = 0;  // value embeddings: logits per layer, dlogit, partials
   long nc = 0;       // CE chunk rows
   size_t part_bytes = 0;
   size_t total = 0;
@@ -230,6 +234,11 @@ FwdPlan plan_fwd(const gpt_model& m, int B, int T) {
   if (m.off_bl >= 0) {
     p.xbo = c.take(N * d * 4);
     p.dback = c.take(N * d * 4);
+  }
+  if (m.any_ve) {
+    p.velog = c.take((size_t)m.depth * N * m.Hkv * 4);
+    p.vedl = c.take(N * m.Hkv * 4);
+    p.vered = c.take((size_t)ve_partials_floats(m.Hkv) * 4);
   }
   if (m.off_sg >= 0) {
     p.xe = c.take(N * d * 4);
@@ -522,6 +531,7 @@ gpt_status gpt_create_gqa(int32_t depth, int32_t vocab, int32_t max_seq, int32_t
   c.resid_scalars = 0;
   c.backout_layer = -1;
   c.smear = 0;
+  c.ve_layers = 0;
   return gpt_create_config(&c, out);
 }
 
@@ -536,6 +546,7 @@ gpt_status gpt_create_config(const gpt_config* cfg, gpt_model** out) {
   if (cfg->resid_scalars != 0 && cfg->resid_scalars != 1) return GPT_EINVAL;
   if (cfg->backout_layer < -1 || cfg->backout_layer >= depth) return GPT_EINVAL;
   if (cfg->smear != 0 && cfg->smear != 1) return GPT_EINVAL;
+  if (cfg->ve_layers < 0 || (depth < 63 && (cfg->ve_layers >> depth) != 0)) return GPT_EINVAL;
   if (depth < 1 || depth > 64) return GPT_EINVAL;
   if (vocab < 64 || vocab > 262144 || vocab % 64 != 0) return GPT_EINVAL;
   if (max_seq < 1 || max_seq > 16384) return GPT_EINVAL;
@@ -581,6 +592,23 @@ gpt_status gpt_create_config(const gpt_config* cfg, gpt_model** out) {
   m->layer_stride = 2 * d * d + 2 * dkv * d + 2 * F * d;
   m->off_lm = off;
   add("lm_head", vocab, (int32_t)d, GPT_KIND_LM_HEAD, -1);
+  // Value embeddings (AdamW group, before the scalars so that lm_head and
+  // these tables form one 16-byte aligned run).
+  m->ve_off.assign(depth, -1);
+  m->veg_off.assign(depth, -1);
+  if (cfg->ve_layers != 0 && m->Hkv > 16) {
+    delete m;
+    return GPT_EINVAL;
+  }
+  for (int l = 0; l < depth; ++l) {
+    if (!((cfg->ve_layers >> l) & 1)) continue;
+    const std::string p = "h" + std::to_string(l) + ".";
+    m->ve_off[l] = off;
+    add(p + "ve", vocab, (int32_t)dkv, GPT_KIND_EMB, l);
+    m->veg_off[l] = off;
+    add(p + "ve_gate", m->Hkv, 32, GPT_KIND_GATE, l);
+    m->any_ve = true;
+  }
   m->off_scalars = off;
   if (cfg->resid_scalars) {
     m->off_rl = off;
@@ -695,6 +723,7 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
   const uint16_t* pxl = m->off_xl >= 0 ? pbf + m->off_xl : nullptr;
   const uint16_t* pbl = m->off_bl >= 0 ? pbf + m->off_bl : nullptr;
   if (x0) HIP_TRY(hipMemcpyAsync(x0, x, Nd * 4, hipMemcpyDeviceToDevice, s));
+  auto ve_logits = [&](int l) { return reinterpret_cast<float*>(ws + p.velog) + (size_t)l * N * Hkv; };
 
   // ---- forward through the blocks
   for (int l = 0; l < L; ++l) {
@@ -718,6 +747,9 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
     HIP_TRY(launch_rmsnorm_fwd(x, xn1, rstd1, N, d, s));
     HIP_TRY(gemm_nt(xn1, d, wqkv, d, (int)N, Q, d, qkv, Q, EPI_BF16, s));
     HIP_TRY(launch_qknorm_rope_fwd(qkv, rstdqk, cs, N, T, H, Hkv, s));
+    if (m->ve_off[l] >= 0)
+      HIP_TRY(launch_ve_fwd(qkv, xn1, tokens, pbf + m->ve_off[l], pbf + m->veg_off[l], ve_logits(l), N, d, Hkv, V,
+                            s));
     {
       ProfScope ps(m, s, PROF_ATTN_FWD, 4.0 * batch * H * 128.0 * attn_pairs(T, m->windows[l]));
       HIP_TRY(launch_attention_fwd_window(qkv, o, lse, batch, T, H, Hkv, m->windows[l], s));
@@ -755,6 +787,10 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
   HIP_TRY(launch_loss_reduce(loss_rows, N, n_valid, loss, s));
   HIP_TRY(launch_rmsnorm_bwd(dxn, xnf, rstdf, dx, dxb, N, d, 0, s));
   if (pbl) HIP_TRY(launch_backout_bwd(dx, xbo, dback, Nd, red, grads + m->off_bl, accumulate, s));
+  // Value-embedding table gradients are scatter-adds, started from zero.
+  if (!accumulate)
+    for (int l = 0; l < L; ++l)
+      if (m->ve_off[l] >= 0) HIP_TRY(launch_fill_u32(grads + m->ve_off[l], 0, (long)V * m->dkv, s));
   if (dx0) HIP_TRY(launch_fill_u32(dx0, 0, Nd, s));
 
   // ---- backward through the blocks
@@ -794,6 +830,11 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
     }
     HIP_TRY(launch_qknorm_rope_bwd(dqkv, qkv, rstdqk, cs, N, T, H, Hkv, s));
     HIP_TRY(gemm_nn(dqkv, Q, wqkv, d, (int)N, d, Q, dxn, d, EPI_F32, s));
+    if (m->ve_off[l] >= 0)
+      HIP_TRY(launch_ve_bwd(dqkv, xn1, tokens, pbf + m->ve_off[l], pbf + m->veg_off[l], ve_logits(l),
+                            grads + m->ve_off[l], reinterpret_cast<float*>(ws + p.vedl),
+                            reinterpret_cast<float*>(ws + p.vered), grads + m->veg_off[l], dxn, N, d, Hkv, V,
+                            accumulate, s));
     HIP_TRY(gemm_wgrad(dqkv, Q, xn1, d, Q, d, N, gqkv, accumulate, part, s));
     HIP_TRY(launch_rmsnorm_bwd(dxn, xn1, rstd1, dx, dxb, N, d, 1, s));
     // dx is now the gradient of the stream entering block l.
@@ -904,7 +945,8 @@ gpt_status normuon_step(gpt_model* m, float* params, uint16_t* params_bf16, cons
 
 int64_t adamw_state_elems(const gpt_model* m) {
   if (!m) return 0;
-  return 2L * m->V * m->d + m->n_scalars;
+  // wte, then everything from lm_head on (lm_head, value embeddings, scalars).
+  return (int64_t)m->V * m->d + (m->nparams - m->off_lm);
 }
 
 gpt_status adamw_step(gpt_model* m, float* params, uint16_t* params_bf16, const float* grads,
@@ -919,11 +961,15 @@ gpt_status adamw_step(gpt_model* m, float* params, uint16_t* params_bf16, const 
   if (!(bc1 > 0.0) || !(bc2 > 0.0)) return GPT_EINVAL;
   const long n = (long)m->V * m->d;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  HIP_TRY(launch_adamw(params, params_bf16, grads, exp_avg, exp_avg_sq, (long)m->off_wte, (long)m->off_lm,
-                       n, lr, beta1, beta2, eps, weight_decay, (float)bc1, (float)bc2, s));
+  const long ow = m->off_wte, ol = m->off_lm, os = m->off_scalars;
+  HIP_TRY(launch_adamw_range(params + ow, params_bf16 + ow, grads + ow, exp_avg, exp_avg_sq, n, lr, beta1, beta2,
+                             eps, weight_decay, (float)bc1, (float)bc2, s));
+  // lm_head and the value embeddings: one aligned run (lengths are multiples of 4).
+  HIP_TRY(launch_adamw_range(params + ol, params_bf16 + ol, grads + ol, exp_avg + n, exp_avg_sq + n, os - ol, lr,
+                             beta1, beta2, eps, weight_decay, (float)bc1, (float)bc2, s));
   if (m->n_scalars > 0) {
-    const long o = m->off_scalars;
-    HIP_TRY(launch_adamw_small(params + o, params_bf16 + o, grads + o, exp_avg + 2 * n, exp_avg_sq + 2 * n,
+    const long ms = n + (os - ol);
+    HIP_TRY(launch_adamw_small(params + os, params_bf16 + os, grads + os, exp_avg + ms, exp_avg_sq + ms,
                                (long)m->n_scalars, lr, beta1, beta2, eps, weight_decay, (float)bc1, (float)bc2, s));
   }
   return GPT_OK;

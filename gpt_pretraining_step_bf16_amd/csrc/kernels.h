@@ -93,3 +93,19 @@ hipError_t launch_smear_fwd(const float* xe, float* x, float* a, const uint16_t*
 hipError_t launch_smear_bwd(const float* dy, const float* xe, const float* a, float* dxo, const uint16_t* pw,
                             const uint16_t* plam, long N, int T, int d, float* partials, float* gw, float* glam,
                             int accumulate, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Value embeddings (table bf16 [V, Hkv*128], gate bf16 [Hkv, 32], Hkv <= 16)
+// ---------------------------------------------------------------------------
+int ve_partials_floats(int Hkv);
+// v of qkv += 3 sigmoid(gate . xn[0:32]) * table[token]; logits [N, Hkv]
+hipError_t launch_ve_fwd(uint16_t* qkv, const uint16_t* xn, const int32_t* tok, const uint16_t* table,
+                         const uint16_t* gate, float* logits, long N, int d, int Hkv, int V, hipStream_t s);
+// dtable += (atomics), dgate (+)= (ordered sums), dxn[:, 0:32] += the gate's input gradient;
+// dlogit [N, Hkv] and partials are scratch
+hipError_t launch_ve_bwd(const uint16_t* dqkv, const uint16_t* xn, const int32_t* tok, const uint16_t* table,
+                         const uint16_t* gate, const float* logits, float* dtable, float* dlogit, float* partials,
+                         float* dgate, float* dxn, long N, int d, int Hkv, int V, int accumulate, hipStream_t s);
+// AdamW on n (multiple of 4) contiguous elements, moments at m, v
+hipError_t launch_adamw_range(float* w, uint16_t* wb, const float* g, float* m, float* v, long n, float lr,
+                              float b1, float b2, float eps, float wd, float bc1, float bc2, hipStream_t s);

@@ -29,11 +29,11 @@ def window_pattern(depth: int, seq: int, pattern: str = "SSSL", short_window=Non
 
 class TrainState:
     def __init__(self, depth: int, vocab: int, seq: int, batch: int, device="cuda", kv_heads=None,
-                 resid_scalars=False, backout_layer=None, smear=False):
+                 resid_scalars=False, backout_layer=None, smear=False, ve_layers=()):
         import torch
 
         self.torch = torch
-        self.model = binding.GptModel(depth, vocab, seq, kv_heads, resid_scalars, backout_layer, smear)
+        self.model = binding.GptModel(depth, vocab, seq, kv_heads, resid_scalars, backout_layer, smear, ve_layers)
         self.batch, self.seq = batch, seq
         self.device = device
         n = self.model.num_params

@@ -49,7 +49,7 @@ typedef enum {
   GPT_EWORKSPACE = -5  /* workspace missing or smaller than the *_workspace_bytes() value */
 } gpt_status;
 
-enum { GPT_KIND_EMB = 0, GPT_KIND_MATRIX = 1, GPT_KIND_LM_HEAD = 2, GPT_KIND_SCALAR = 3 };
+enum { GPT_KIND_EMB = 0, GPT_KIND_MATRIX = 1, GPT_KIND_LM_HEAD = 2, GPT_KIND_SCALAR = 3, GPT_KIND_GATE = 4 };
 
 typedef struct {
   char name[32];   /* "wte", "h<l>.wq" ... "h<l>.wproj", "lm_head" */
@@ -101,6 +101,13 @@ int32_t gpt_kv_heads(const gpt_model* m);
  *                  becomes x_t + smear_lambda * sigmoid(smear_gate . x_t[0:24])
  *                  * x_(t-1), x_(-1) = 0 at a sequence's first token (this is
  *                  the x0 of the residual scalars)
+ *   ve_layers      bit l set: layer l has a value embedding ("Embeddings de
+ *                  Valor (ResFormer)"): tensors h{l}.ve [vocab, kv_heads*128]
+ *                  (kind GPT_KIND_EMB) and h{l}.ve_gate [kv_heads, 32] (kind
+ *                  GPT_KIND_GATE); v of each key/value head h gets
+ *                  3 * sigmoid(ve_gate[h] . xn[0:32]) times the token's row,
+ *                  xn being the block's normalised input. kv_heads <= 16.
+ *                  These follow lm_head, before the scalar tensors.
  * Scalar tensors (kind GPT_KIND_SCALAR) follow lm_head in the flat layout and
  * belong to the AdamW group; gpt_fwd_bwd reads them from params_bf16 like
  * every weight and writes their gradients. Returns GPT_EINVAL for values out
@@ -112,6 +119,7 @@ typedef struct {
   int32_t resid_scalars;
   int32_t backout_layer;
   int32_t smear;
+  int64_t ve_layers;
 } gpt_config;
 gpt_status gpt_create_config(const gpt_config* cfg, gpt_model** out);
 /* The backout layer, or -1. */
@@ -224,22 +232,23 @@ gpt_status normuon_step(gpt_model* m, float* params, uint16_t* params_bf16, cons
                         const float* ns_coeffs, int32_t ns_steps, void* workspace, size_t workspace_bytes,
                         void* stream);
 
-/* Elements of each AdamW moment buffer: wte, lm_head, then the scalar tensors
- * (2 * vocab * d + their count). */
+/* Elements of each AdamW moment buffer: wte, then every tensor from lm_head on
+ * (lm_head, value embeddings and gates, scalars), in layout order. */
 int64_t adamw_state_elems(const gpt_model* m);
 
 /*
- * One AdamW step of wte, lm_head and the scalar tensors ([CT50] "2. Otimizador
- * Muon": embeddings, lm_head and scalars are optimised by AdamW; the page gives
- * no hyperparameters, so all of them are arguments). Per element, with t = step:
+ * One AdamW step of wte, lm_head, the value embeddings and their gates, and the
+ * scalar tensors ([CT50] "2. Otimizador Muon": embeddings, lm_head and scalars
+ * are optimised by AdamW; the page gives no hyperparameters, so all of them
+ * are arguments). Per element, with t = step:
  *   m <- beta1 m + (1 - beta1) g;   v <- beta2 v + (1 - beta2) g^2
  *   w <- w - lr * weight_decay * w - lr * (m / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps)
  * (decoupled decay scaled by lr, from the weights before the step).
- *   params, params_bf16, grads  as for muon_step; only wte, lm_head and the
- *                               scalars change, and their bf16 shadow is refreshed
+ *   params, params_bf16, grads  as for muon_step; only the AdamW group changes,
+ *                               and its bf16 shadow is refreshed
  *   exp_avg, exp_avg_sq         device fp32 [adamw_state_elems(m)]: the moments
- *                               of wte, then lm_head, then the scalars (in
- *                               layout order); zero before step 1
+ *                               of wte, then of every tensor from lm_head on,
+ *                               in layout order; zero before step 1
  *   step                        1-based step count (bias correction)
  * Returns GPT_EINVAL for null pointers, step < 1, betas outside [0, 1),
  * eps < 0 or non-finite lr / weight_decay, before any launch.

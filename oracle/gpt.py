@@ -329,9 +329,10 @@ def forward_backward(weights, tokens, targets, final_norm=True, want_grads=True,
     backout_layer: the layer whose input stream the backout subtracts (the
     weights then hold backout_lambda); residual scalars apply when the weights
     hold resid_lambdas and x0_lambdas (see _forward_sequence).
-    scalar_scales: optional dict; for each scalar tensor it receives, shaped
-    like the tensor, the Cauchy-Schwarz bound of the dot product that forms
-    its gradient (a tolerance scale for comparisons; not part of the step).
+    scalar_scales: optional dict; for each scalar tensor and value-embedding
+    gate it receives, shaped like the tensor, the Cauchy-Schwarz bound of the
+    sum that forms its gradient (a tolerance scale for comparisons; not part
+    of the step).
 
     Sequences are independent, so the batch is processed one row at a time and
     the per-row contributions are summed (this bounds memory; it is exact).
@@ -404,6 +405,10 @@ def forward_backward(weights, tokens, targets, final_norm=True, want_grads=True,
                 np.add.at(grads[ve_name], tok, (3.0 * sig[:, :, None] * dv).reshape(T, -1))
                 dlogit = 3.0 * sig * (1.0 - sig) * np.sum(dv * ve, axis=-1)   # [T, Hkv]
                 grads[f"h{layer}.ve_gate"] += dlogit.T @ s["xn1"][:, :VE_GATE_CHANNELS]
+                if scalar_scales is not None:
+                    bound = 3.0 * sig * (1.0 - sig) * np.linalg.norm(dv, axis=-1) * np.linalg.norm(ve, axis=-1)
+                    sk = scalar_scales.setdefault(f"h{layer}.ve_gate", np.zeros_like(weights[f"h{layer}.ve_gate"]))
+                    sk += bound.T @ np.abs(s["xn1"][:, :VE_GATE_CHANNELS])
                 dxn1_ve = np.zeros_like(s["xn1"])
                 dxn1_ve[:, :VE_GATE_CHANNELS] = dlogit @ weights[f"h{layer}.ve_gate"]
             dv = dv.reshape(T, -1)

@@ -37,7 +37,7 @@ def log(msg):
     print(msg, flush=True)
 
 
-def assert_scalar_grads(grads, ref_grads, scales, log=None):
+def assert_scalar_grads(grads, ref_grads, scales, log=None, eps=1e-3):
     """Gradients of the scalar tensors are dot products, over every token and
     channel, of a stream gradient g with a kept stream v. The final norm makes
     the loss insensitive to the stream's scale, so these sums cancel down to a
@@ -47,14 +47,17 @@ def assert_scalar_grads(grads, ref_grads, scales, log=None):
     of the device's stream gradient (bounded by the 2e-2 gradient bar); the
     errors measured on these models stay below 5e-5 S, except the smear gate
     at the end of the backward chain (up to 2.6e-4 S), so per scalar:
-    |delta| <= 2e-2 |ref| + 1e-3 S. A sign error or a wrong kept stream also
-    breaks the matrix and embedding gradients that the same stream gradient
-    feeds, which the rel-L2 checks catch."""
+    |delta| <= 2e-2 |ref| + eps S with eps = 1e-3. A sign error or a wrong
+    kept stream also breaks the matrix and embedding gradients that the same
+    stream gradient feeds, which the rel-L2 checks catch. The value-embedding
+    gates sum products of dv, which comes out of the bf16 attention backward
+    with about 1e-2 relative error (within the 2e-2 bar): they take eps = 1e-2
+    (measured up to 2.9e-3 S)."""
     for k, s in scales.items():
         got = np.asarray(grads[k], dtype=np.float64).ravel()
         ref = np.asarray(ref_grads[k]).ravel()
         sv = np.asarray(s).ravel()
         if log is not None:
             log(f"  {k}: |delta|/S = {np.max(np.abs(got - ref) / sv):.2e}")
-        tol = 2e-2 * np.abs(ref) + 1e-3 * sv
+        tol = 2e-2 * np.abs(ref) + eps * sv
         assert np.all(np.abs(got - ref) <= tol), (k, got, ref, sv)

@@ -234,3 +234,15 @@ def test_config_validation():
     for cfg in bad:
         assert lib.gpt_create_config(C.byref(cfg), C.byref(h)) == binding.GPT_EINVAL
     assert lib.gpt_create_config(None, C.byref(h)) == binding.GPT_EINVAL
+
+
+def test_value_embedding_tensors_and_validation():
+    depth, vocab = 4, 2048
+    m = binding.GptModel(depth, vocab, 128, 1, False, None, False, (1, 3))
+    specs = syn.tensor_specs(depth, vocab, 1, ve_layers=(1, 3))
+    assert [(t["name"], t["rows"], t["cols"], t["kind"]) for t in m.tensors()] == [sp[:4] for sp in specs]
+    assert m.adamw_state_elems() == 2 * vocab * m.d + 2 * (vocab * 128 + 32)
+    lib = binding.lib()
+    h = C.c_void_p()
+    cfg = binding.GptConfig(4, 2048, 128, 0, 0, -1, 0, 1 << 4)  # layer 4 does not exist
+    assert lib.gpt_create_config(C.byref(cfg), C.byref(h)) == binding.GPT_EINVAL
