@@ -513,10 +513,25 @@ __device__ __forceinline__ void split_store(float v, float* x32, uint16_t* xh, u
   xl[i] = (uint16_t)f2bf(v - bf2f(h));
 }
 
+// Four consecutive elements i .. i+3 (i % 4 == 0): fp32 and the bf16 hi/lo
+// split (hi = bf16(v), lo = bf16(v - hi)).
+__device__ __forceinline__ void split_store4(const float (&v)[4], float* x32, uint16_t* xh, uint16_t* xl, long i) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = f2bf(v[e]);
+    l[e] = f2bf(v[e] - bf2f(h[e]));
+  }
+  *reinterpret_cast<float4*>(x32 + i) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<uint2*>(xh + i) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+  *reinterpret_cast<uint2*>(xl + i) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+}
+
 // X = M / (||M||_F + 1e-7) in the tall orientation, as fp32 and bf16 hi/lo.
 // X is [x_rows, x_cols]. A matrix flagged in transposed_mask is stored wide,
 // as [x_cols, x_rows]; it is transposed through a 32x33 LDS tile.
-// Grid: (x_cols / 32, x_rows / 32, count); 256 threads.
+// Grid: (x_cols / 32, x_rows / 32, count); 256 threads, one float4 each:
+// thread t covers row t / 8 and columns 4 (t % 8) .. +3 of the 32x32 tile.
 __global__ void muon_pack_kernel(const MuonGroup g, const float* __restrict__ mom,
                                  const float* __restrict__ partials, int nb, float* __restrict__ x32,
                                  uint16_t* __restrict__ xh, uint16_t* __restrict__ xl) {
@@ -529,29 +544,30 @@ __global__ void muon_pack_kernel(const MuonGroup g, const float* __restrict__ mo
   const long xr = g.x_rows, xc = g.x_cols;
   const long xoff = (long)j * xr * xc;
   const float* src = mom + off;
-  const int tx = threadIdx.x & 31;
-  const int ty = threadIdx.x >> 5;  // 0..7
+  const int q = threadIdx.x & 7;   // float4 column group
+  const int ry = threadIdx.x >> 3;  // 0..31
   const long r0 = blockIdx.y * 32L, c0 = blockIdx.x * 32L;  // X tile origin
+  const long idx = (r0 + ry) * xc + c0 + 4 * q;
+  float v[4];
   if (!tr) {
-    for (int rr = ty; rr < 32; rr += 8) {
-      const long idx = (r0 + rr) * xc + c0 + tx;
-      split_store(src[idx] * inv, x32 + xoff, xh + xoff, xl + xoff, idx);
-    }
+    const float4 m = *reinterpret_cast<const float4*>(src + idx);
+    v[0] = m.x * inv; v[1] = m.y * inv; v[2] = m.z * inv; v[3] = m.w * inv;
   } else {
-    // Stored M[c][r] = X[r][c]; stored rows have x_rows elements.
-    for (int cc = ty; cc < 32; cc += 8) tile[cc][tx] = src[(c0 + cc) * xr + r0 + tx];
+    // Stored M[c][r] = X[r][c]; stored rows have x_rows elements. Thread
+    // (ry, q) loads stored row c0 + ry, X rows r0 + 4q .. +3.
+    const float4 m = *reinterpret_cast<const float4*>(src + (c0 + ry) * xr + r0 + 4 * q);
+    tile[ry][4 * q] = m.x; tile[ry][4 * q + 1] = m.y; tile[ry][4 * q + 2] = m.z; tile[ry][4 * q + 3] = m.w;
     __syncthreads();
-    for (int rr = ty; rr < 32; rr += 8) {
-      const long idx = (r0 + rr) * xc + c0 + tx;
-      split_store(tile[tx][rr] * inv, x32 + xoff, xh + xoff, xl + xoff, idx);
-    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = tile[4 * q + e][ry] * inv;
   }
+  split_store4(v, x32 + xoff, xh + xoff, xl + xoff, idx);
 }
 
 // W <- W - lr * sqrt(max(1, rows/cols)) * X in the stored orientation (rows =
 // fan-out of the stored matrix); refresh bf16. With row_scale (NorMuon), row r
 // of X is first multiplied by row_scale[j * x_rows + r]. Grid as
-// muon_pack_kernel.
+// muon_pack_kernel, one float4 of the stored matrix per thread.
 __global__ void muon_update_kernel(const MuonGroup g, const float* __restrict__ x32,
                                    float* __restrict__ params, uint16_t* __restrict__ pbf, float lr,
                                    const float* __restrict__ row_scale) {
@@ -564,32 +580,39 @@ __global__ void muon_update_kernel(const MuonGroup g, const float* __restrict__ 
   const float srows = (float)(tr ? xc : xr), scols = (float)(tr ? xr : xc);
   const float scale = lr * sqrtf(fmaxf(1.f, srows / scols));
   const long xoff = (long)j * xr * xc;
-  const int tx = threadIdx.x & 31;
-  const int ty = threadIdx.x >> 5;
+  const int q = threadIdx.x & 7;
+  const int ry = threadIdx.x >> 3;
   const long r0 = blockIdx.y * 32L, c0 = blockIdx.x * 32L;  // X tile origin
+  const float* rsc = row_scale ? row_scale + (long)j * xr + r0 : nullptr;
   float* w = params + off;
   uint16_t* wb = pbf + off;
-  const float* rsc = row_scale ? row_scale + (long)j * xr + r0 : nullptr;
+  long widx;
+  float u[4];  // X values for the four stored elements widx .. widx+3
   if (!tr) {
-    for (int rr = ty; rr < 32; rr += 8) {
-      const long idx = (r0 + rr) * xc + c0 + tx;
-      const float sr = rsc ? scale * rsc[rr] : scale;
-      const float v = w[idx] - sr * x32[xoff + idx];
-      w[idx] = v;
-      wb[idx] = (uint16_t)f2bf(v);
-    }
+    widx = (r0 + ry) * xc + c0 + 4 * q;
+    const float4 xv = *reinterpret_cast<const float4*>(x32 + xoff + widx);
+    const float sr = rsc ? rsc[ry] : 1.f;
+    u[0] = sr * xv.x; u[1] = sr * xv.y; u[2] = sr * xv.z; u[3] = sr * xv.w;
   } else {
-    for (int rr = ty; rr < 32; rr += 8)
-      tile[rr][tx] = (rsc ? rsc[rr] : 1.f) * x32[xoff + (r0 + rr) * xc + c0 + tx];
+    // X tile rows r0 + ry, columns c0 + 4q .. +3, into LDS; the stored
+    // matrix W[c][r] is then written along r: stored row c0 + ry, X rows
+    // r0 + 4q .. +3.
+    const float4 xv = *reinterpret_cast<const float4*>(x32 + xoff + (r0 + ry) * xc + c0 + 4 * q);
+    const float sr = rsc ? rsc[ry] : 1.f;
+    tile[ry][4 * q] = sr * xv.x; tile[ry][4 * q + 1] = sr * xv.y;
+    tile[ry][4 * q + 2] = sr * xv.z; tile[ry][4 * q + 3] = sr * xv.w;
     __syncthreads();
-    // Stored W[c][r] with c in the X-column tile, r in the X-row tile.
-    for (int cc = ty; cc < 32; cc += 8) {
-      const long idx = (c0 + cc) * xr + r0 + tx;
-      const float v = w[idx] - scale * tile[tx][cc];
-      w[idx] = v;
-      wb[idx] = (uint16_t)f2bf(v);
-    }
+    widx = (c0 + ry) * xr + r0 + 4 * q;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) u[e] = tile[4 * q + e][ry];
   }
+  float4 wv = *reinterpret_cast<const float4*>(w + widx);
+  wv.x -= scale * u[0];
+  wv.y -= scale * u[1];
+  wv.z -= scale * u[2];
+  wv.w -= scale * u[3];
+  *reinterpret_cast<float4*>(w + widx) = wv;
+  *reinterpret_cast<uint2*>(wb + widx) = make_uint2(pack_bf2(wv.x, wv.y), pack_bf2(wv.z, wv.w));
 }
 
 // NorMuon ([CT50] "2. Otimizador Muon", variance reduction after the
