@@ -165,14 +165,21 @@ __device__ __forceinline__ bf16x8 pack_frag(const f32x16& x, int v0) {
 }
 
 // Work item of a (blocks_per_head x heads) grid, remapped so that the blocks
-// of one head run on the same XCD (they share its K/V or Q/dO in L2).
+// of one head run on the same XCD (they share its K/V or Q/dO in L2). Heads
+// go in pairs whose blocks alternate, block index 0 of both first: callers map
+// block 0 to the most work, so the short blocks of one pair fill the gaps left
+// by the long ones of the next instead of a pair's long block starting last.
 __device__ __forceinline__ void head_block(int& blk, int& bh) {
   const int nb = gridDim.x;
-  const int total = nb * gridDim.y;
+  const int nh = gridDim.y;
+  const int total = nb * nh;
   int lin = blockIdx.x + nb * blockIdx.y;
   if ((total & 7) == 0) lin = (lin & 7) * (total >> 3) + (lin >> 3);
-  bh = lin / nb;
-  blk = lin - bh * nb;
+  const int pair = lin / (2 * nb);
+  const int r = lin - pair * 2 * nb;
+  const int gs = min(2, nh - 2 * pair);  // 1 for the last head of an odd count
+  blk = r / gs;
+  bh = 2 * pair + (r - blk * gs);
 }
 
 // ===========================================================================
