@@ -491,37 +491,6 @@ __global__ void __launch_bounds__(NTHR, 1)
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   };
-  // P and dS of half t of tile n (stage st), packed as B operands.
-  auto softmax = [&](int n, int st, int t, f32x16& s, f32x16& dp, bf16x8 (&pf)[2], bf16x8 (&dsf)[2]) {
-    const float* ls = reinterpret_cast<const float*>(stage(st) + 2 * TILE);
-    const float* ds = ls + QBW;
-    const int qb = qb_first + n % nqt;
-    // s[v]: query qb*64 + 32t + 8(v/4) + 4hl + v%4, key kpos.
-    const bool need_mask = (qb * QBW + 32 * t < k0 + 31) || (qb * QBW + 32 * t + 32 > T) ||
-                           (qb * QBW + 32 * t + 31 > k0 + W);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int ql = 32 * t + 8 * g + 4 * hl;
-      const float4 l4 = *reinterpret_cast<const float4*>(ls + ql);
-      const float4 d4 = *reinterpret_cast<const float4*>(ds + ql);
-      const float lq[4] = {l4.x, l4.y, l4.z, l4.w};
-      const float dq[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int q = qb * QBW + ql + r;
-        const int v = 4 * g + r;
-        float p = fast_exp2(fmaf(s[v], sc, -lq[r]));
-        // Visible iff kpos <= q <= min(T - 1, kpos + W) (one unsigned compare).
-        if (need_mask && (uint32_t)(q - kpos) > (uint32_t)qlim) p = 0.f;
-        s[v] = p;
-        dp[v] = p * (dp[v] - dq[r]);
-      }
-    }
-    pf[0] = pack_frag(s, 0);
-    pf[1] = pack_frag(s, 8);
-    dsf[0] = pack_frag(dp, 0);
-    dsf[1] = pack_frag(dp, 8);
-  };
   // dV^T += dO^T P and dK^T += Q^T dS for half t of the tile in stage st;
   // the transposed fragments of dim tile dt+1 are read during the MFMAs of dt.
   auto dvdk = [&](int st, int t, const bf16x8 (&pf)[2], const bf16x8 (&dsf)[2]) {
@@ -559,6 +528,69 @@ __global__ void __launch_bounds__(NTHR, 1)
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   };
 
+  // P and dS of half t of tile n (stage st), packed as B operands, fused with
+  // sdp(st2, t2): the two are independent, so each k-step's S / dP MFMAs are
+  // followed in program order by the softmax of two of this lane's 16 values
+  // and the MFMAs run while the VALU work issues (8.8% off the backward at
+  // d20 against the softmax as one block). The last tile computes a
+  // throw-away S / dP of the stage after it.
+  auto softmax_sdp = [&](int n, int st, int t, f32x16& s, f32x16& dp, bf16x8 (&pf)[2],
+                         bf16x8 (&dsf)[2], int st2, int t2, f32x16& s2, f32x16& dp2) {
+    const float* ls = reinterpret_cast<const float*>(stage(st) + 2 * TILE);
+    const float* ds = ls + QBW;
+    const int qb = qb_first + n % nqt;
+    const bool need_mask = (qb * QBW + 32 * t < k0 + 31) || (qb * QBW + 32 * t + 32 > T) ||
+                           (qb * QBW + 32 * t + 31 > k0 + W);
+    // Branch-free: with no mask needed the bound admits every offset.
+    const uint32_t lim = need_mask ? (uint32_t)qlim : 0xffffffffu;
+    float lq[16], dq[16];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int ql = 32 * t + 8 * g + 4 * hl;
+      const float4 l4 = *reinterpret_cast<const float4*>(ls + ql);
+      const float4 d4 = *reinterpret_cast<const float4*>(ds + ql);
+      lq[4 * g] = l4.x; lq[4 * g + 1] = l4.y; lq[4 * g + 2] = l4.z; lq[4 * g + 3] = l4.w;
+      dq[4 * g] = d4.x; dq[4 * g + 1] = d4.y; dq[4 * g + 2] = d4.z; dq[4 * g + 3] = d4.w;
+    }
+    const int qrow = qb * QBW + 32 * t + 4 * hl - kpos;  // q - kpos for v = 0
+    auto one = [&](int v) {
+      // s[v]: query qb*64 + 32t + 8(v/4) + 4hl + v%4, key kpos.
+      float p = fast_exp2(fmaf(s[v], sc, -lq[v]));
+      p = (uint32_t)(qrow + 8 * (v >> 2) + (v & 3)) > lim ? 0.f : p;
+      s[v] = p;
+      dp[v] = p * (dp[v] - dq[v]);
+    };
+    const char* qs = stage(st2);
+    const char* gs = qs + TILE;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      s2[v] = 0.f;
+      dp2[v] = 0.f;
+    }
+    bf16x8 fq[8], fg[8];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      fq[k] = row_frag(qs, fa, 32 * t2, k);
+      fg[k] = row_frag(gs, fa, 32 * t2, k);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (k + 2 < 8) {
+        fq[k + 2] = row_frag(qs, fa, 32 * t2, k + 2);
+        fg[k + 2] = row_frag(gs, fa, 32 * t2, k + 2);
+      }
+      s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[k], as_bf16x8(kf[k]), s2, 0, 0, 0);
+      dp2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fg[k], as_bf16x8(vf[k]), dp2, 0, 0, 0);
+      one(2 * k);
+      one(2 * k + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    pf[0] = pack_frag(s, 0);
+    pf[1] = pack_frag(s, 8);
+    dsf[0] = pack_frag(dp, 0);
+    dsf[1] = pack_frag(dp, 8);
+  };
+
   // Pipeline over halves: the S / dP MFMAs of the next half are issued while
   // the softmax of the current half runs (set A holds halves t = 0, set B
   // halves t = 1). Tile n lives in stage n % 4; tile n+2 is loaded during
@@ -575,11 +607,9 @@ __global__ void __launch_bounds__(NTHR, 1)
     if (n > 0) VMCNT_BARRIER(0);  // tile n+1 is in LDS; every wave is past tile n-1
     if (n + 2 < ntile) issue(n + 2, (n + 2) & (DKDV_NST - 1));
     bf16x8 pf[2], dsf[2];
-    softmax(n, st, 0, sa, da, pf, dsf);
-    sdp(st, 1, sb, db);
+    softmax_sdp(n, st, 0, sa, da, pf, dsf, st, 1, sb, db);
     dvdk(st, 0, pf, dsf);
-    softmax(n, st, 1, sb, db, pf, dsf);
-    if (n + 1 < ntile) sdp((n + 1) & (DKDV_NST - 1), 0, sa, da);
+    softmax_sdp(n, st, 1, sb, db, pf, dsf, (n + 1) & (DKDV_NST - 1), 0, sa, da);
     dvdk(st, 1, pf, dsf);
   }
 
