@@ -118,7 +118,10 @@ def test_gemm_epilogues():
                                          (1, 4096, 2, 2048, 2),
                                          # grouped-query attention: groups of 2, 4 and 3 query heads
                                          (1, 333, 4, -1, 2), (2, 200, 4, 37, 1), (1, 1024, 6, -1, 2),
-                                         (1, 2048, 4, 1024, 2)])
+                                         (1, 2048, 4, 1024, 2),
+                                         # more heads than one block-order group, ragged last
+                                         # group, with and without the XCD remap
+                                         (3, 200, 5, -1, 5), (4, 256, 5, -1, 5)])
 def test_attention_fwd_bwd(B, T, H, W, HKV):
     log(f"attention B={B} T={T} H={H} window={W} kv_heads={HKV}")
     rng = np.random.default_rng(T + H)
