@@ -51,8 +51,9 @@ def test_layout_matches_canonical_specs(depth, vocab):
     assert m.num_params == off
 
 
-def test_param_counts_match_survey_table():
-    # Block / embedding / head parameter counts at d20 and d32.
+def test_param_counts_closed_form():
+    # 2·V·d (wte, lm_head) + L·12·d² (q, k, v, o: d² each; fc, proj: 4d² each)
+    # at d20 (d = 1280) and d32 (d = 2048), V = 32768.
     m = binding.GptModel(20, 32768, 2048)
     assert m.num_params == 477_102_080
     m = binding.GptModel(32, 32768, 4096)
