@@ -182,8 +182,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures the single-GPU step only: this build has no multi-GPU path "
-              "(see DESIGN.md for how the step would shard). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures the single-GPU step only: the library has no multi-GPU path "
+              "(each data-parallel rank would run this same step on its share of the batch). "
+              "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
