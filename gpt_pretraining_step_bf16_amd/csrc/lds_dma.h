@@ -67,7 +67,8 @@ __device__ __forceinline__ void dma4(const void* gsrc, uint32_t lds_base) {
 
 // Four 16-byte-per-lane direct loads from one wave-uniform 64-bit base with
 // per-lane byte offsets v[0..3], landing in four consecutive 1 KB LDS blocks
-// from lds_base. M0 is saved once and restored once.
+// from lds_base. M0 is saved once and restored once; the s_add_u32 steps
+// write SCC, which the clobber list declares.
 __device__ __forceinline__ void dma16_sv4(const void* sbase, const uint32_t (&v)[4], uint32_t lds_base) {
   uint32_t saved;
   asm volatile(
@@ -87,5 +88,5 @@ __device__ __forceinline__ void dma16_sv4(const void* sbase, const uint32_t (&v)
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "s"(sbase), "s"(lds_base)
-      : "memory");
+      : "memory", "scc");
 }
