@@ -17,6 +17,8 @@ Parity status of each function is stated in its module header.
 """
 from .gpt import (  # noqa: F401
     EPS_NORM,
+    attention_by_head,
+    attention_by_head_bwd,
     ROPE_BASE,
     causal_attention,
     causal_attention_bwd,

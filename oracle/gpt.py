@@ -161,6 +161,59 @@ def causal_attention_bwd(do, q, k, v, p):
             _sum_kv_groups(dv.transpose(1, 0, 2), hkv))
 
 
+def _head_pool():
+    """Threads for the per-head loops: heads are independent, and NumPy
+    releases the interpreter lock inside its array operations, so running
+    heads side by side changes no arithmetic, only wall time."""
+    global _POOL
+    if _POOL is None:
+        import concurrent.futures
+        import os
+
+        _POOL = concurrent.futures.ThreadPoolExecutor(max_workers=max(1, min(16, len(os.sched_getaffinity(0)))))
+    return _POOL
+
+
+_POOL = None
+
+
+def attention_by_head(q, k, v, window=None):
+    """causal_attention one query head at a time (query head h with key/value
+    head h // (H / Hkv)), so that only one head's T x T probabilities exist per
+    worker; returns o [T, H, hd]."""
+    T, H, hd = q.shape
+    g = H // k.shape[1]
+    o = np.empty_like(q)
+
+    def head(h):
+        o[:, h:h + 1], _ = causal_attention(q[:, h:h + 1], k[:, h // g:h // g + 1], v[:, h // g:h // g + 1], window)
+
+    list(_head_pool().map(head, range(H)))
+    return o
+
+
+def attention_by_head_bwd(do, q, k, v, window=None):
+    """Adjoint of attention_by_head: per query head, the probabilities are
+    recomputed (causal_attention) and causal_attention_bwd applied; the key and
+    value gradients of the query heads that share a key/value head are then
+    summed in head order."""
+    T, H, hd = q.shape
+    g = H // k.shape[1]
+
+    def head(h):
+        qh, kh, vh = q[:, h:h + 1], k[:, h // g:h // g + 1], v[:, h // g:h // g + 1]
+        _, p = causal_attention(qh, kh, vh, window)
+        return causal_attention_bwd(do[:, h:h + 1], qh, kh, vh, p)
+
+    per_head = list(_head_pool().map(head, range(H)))
+    dq, dk, dv = np.empty_like(q), np.zeros_like(k), np.zeros_like(v)
+    for h, (dqh, dkh, dvh) in enumerate(per_head):
+        dq[:, h:h + 1] = dqh
+        dk[:, h // g:h // g + 1] += dkh
+        dv[:, h // g:h // g + 1] += dvh
+    return dq, dk, dv
+
+
 def log_softmax_rows(z):
     """Row-wise logsumexp of z [T, V]."""
     m = z.max(axis=-1, keepdims=True)
@@ -228,7 +281,7 @@ def _smear_bwd(dy, x, a, weights, grads, sc=None):
     return dx
 
 
-def _forward_sequence(weights, tok, cos, sin, final_norm=True, windows=None, backout_layer=None):
+def _forward_sequence(weights, tok, cos, sin, windows=None, backout_layer=None):
     """Forward pass of one sequence; returns the logits and the saved values.
 
     windows: None, or one attention window per layer (an int, or None for the
@@ -275,7 +328,7 @@ def _forward_sequence(weights, tok, cos, sin, final_norm=True, windows=None, bac
         qn, rq = rms_norm(q)
         kn, rk = rms_norm(k)
         qr, kr = rope(qn, cos, sin), rope(kn, cos, sin)
-        o, p = causal_attention(qr, kr, v, _layer_window(windows, layer))
+        o = attention_by_head(qr, kr, v, _layer_window(windows, layer))
         o2 = o.reshape(T, d)
         x_mid = x + o2 @ w["wo"].T
         xn2, r2 = rms_norm(x_mid)
@@ -283,37 +336,22 @@ def _forward_sequence(weights, tok, cos, sin, final_norm=True, windows=None, bac
         a = np.maximum(u, 0.0) ** 2
         x = x_mid + a @ w["wproj"].T
         layers.append(dict(xn1=xn1, r1=r1, qn=qn, rq=rq, kn=kn, rk=rk, qr=qr, kr=kr,
-                           v=v, p=p, o2=o2, xn2=xn2, r2=r2, u=u, a=a, x_prev=x_prev, ve_logit=ve_logit))
+                           v=v, o2=o2, xn2=xn2, r2=r2, u=u, a=a, x_prev=x_prev, ve_logit=ve_logit))
     if backout_layer is not None:
         x = x - bl * x_backout
-    if final_norm:
-        xnf, rf = rms_norm(x)
-    else:
-        xnf, rf = x, None
+    xnf, rf = rms_norm(x)
     z = xnf @ weights["lm_head"].T
     return z, dict(layers=layers, xnf=xnf, rf=rf, x0=x0, x_backout=x_backout, x_emb=x_emb, smear_a=smear_a)
 
 
-def forward_logits(weights, tokens, final_norm=True, windows=None, backout_layer=None):
+def forward_logits(weights, tokens, windows=None, backout_layer=None):
     """Logits [B, T, V] for int tokens [B, T] (no loss, no gradients)."""
     tokens = np.asarray(tokens)
     T = tokens.shape[1]
     dt = weights["wte"].dtype
     cos, sin = rope_tables(T, dtype=dt)
-    return np.stack([_forward_sequence(weights, tokens[b], cos, sin, final_norm, windows, backout_layer)[0]
+    return np.stack([_forward_sequence(weights, tokens[b], cos, sin, windows, backout_layer)[0]
                      for b in range(tokens.shape[0])])
-
-
-def per_position_loss(weights, tokens, targets, final_norm=True, windows=None):
-    """lse(z) - z[target] at every position (0 where the target is ignored)."""
-    z = forward_logits(weights, tokens, final_norm, windows)
-    out = np.zeros(targets.shape, dtype=z.dtype)
-    for b in range(z.shape[0]):
-        lse = log_softmax_rows(z[b])
-        valid = targets[b] >= 0
-        t = np.where(valid, targets[b], 0)
-        out[b] = np.where(valid, lse - z[b][np.arange(z.shape[1]), t], 0.0)
-    return out
 
 
 def _cs(a, b):
@@ -321,8 +359,8 @@ def _cs(a, b):
     return float(np.sum(np.linalg.norm(a, axis=-1) * np.linalg.norm(b, axis=-1)))
 
 
-def forward_backward(weights, tokens, targets, final_norm=True, want_grads=True, windows=None,
-                     backout_layer=None, scalar_scales=None):
+def forward_backward(weights, tokens, targets, want_grads=True, windows=None, backout_layer=None,
+                     scalar_scales=None):
     """Mean cross-entropy loss and the gradient of every tensor.
 
     windows: None, or one attention window per layer (see causal_attention).
@@ -351,7 +389,7 @@ def forward_backward(weights, tokens, targets, final_norm=True, want_grads=True,
     H = d // HEAD_DIM
     for b in range(B):
         tok, tgt = tokens[b], targets[b]
-        z, c = _forward_sequence(weights, tok, cos, sin, final_norm, windows, backout_layer)
+        z, c = _forward_sequence(weights, tok, cos, sin, windows, backout_layer)
         lse = log_softmax_rows(z)
         valid = tgt >= 0
         t = np.where(valid, tgt, 0)
@@ -364,9 +402,7 @@ def forward_backward(weights, tokens, targets, final_norm=True, want_grads=True,
         dz[rows, t] -= 1.0
         dz *= (valid.astype(dt) / n_valid)[:, None]
         grads["lm_head"] += dz.T @ c["xnf"]
-        dx = dz @ weights["lm_head"]
-        if final_norm:
-            dx = rms_norm_bwd(dx, c["xnf"], c["rf"])
+        dx = rms_norm_bwd(dz @ weights["lm_head"], c["xnf"], c["rf"])
         rl, xl, bl = _scalars(weights)
         sc = scalar_scales
         if sc is not None:
@@ -393,7 +429,10 @@ def forward_backward(weights, tokens, targets, final_norm=True, want_grads=True,
             # x_mid = x_in + o Wo^T
             grads[g["wo"]] += dx_mid.T @ s["o2"]
             do = (dx_mid @ w["wo"]).reshape(T, H, HEAD_DIM)
-            dqr, dkr, dv = causal_attention_bwd(do, s["qr"], s["kr"], s["v"], s["p"])
+            # The probabilities are recomputed from the saved q, k, one head at
+            # a time (the forward's definition; keeping them would need H T^2
+            # values per layer).
+            dqr, dkr, dv = attention_by_head_bwd(do, s["qr"], s["kr"], s["v"], _layer_window(windows, layer))
             dq = rms_norm_bwd(rope_bwd(dqr, cos, sin), s["qn"], s["rq"]).reshape(T, d)
             dk = rms_norm_bwd(rope_bwd(dkr, cos, sin), s["kn"], s["rk"]).reshape(T, -1)
             dxn1_ve = 0.0

@@ -575,3 +575,19 @@ def test_depth_rule_matches_configs():
         dm = syn.model_dims(syn.CONFIGS[name]["depth"])
         assert dm["d"] == width and dm["heads"] * 128 == width and dm["mlp"] == 4 * width
     assert syn.model_dims(1)["d"] == 128 and syn.model_dims(3)["d"] == 256
+
+
+@pytest.mark.parametrize("kv_heads,window", [(4, None), (2, 5), (1, None)])
+def test_attention_by_head_equals_all_heads_at_once(kv_heads, window):
+    """The model's head-at-a-time attention and its adjoint are the all-heads
+    attention and adjoint (grouped-query sums included), to fp64 rounding."""
+    rng = np.random.default_rng(31)
+    T, H, hd = 12, 4, 8
+    q = rng.standard_normal((T, H, hd))
+    k = rng.standard_normal((T, kv_heads, hd))
+    v = rng.standard_normal((T, kv_heads, hd))
+    do = rng.standard_normal((T, H, hd))
+    o_ref, p = oracle.causal_attention(q, k, v, window)
+    np.testing.assert_allclose(oracle.attention_by_head(q, k, v, window), o_ref, rtol=0, atol=1e-14)
+    for got, ref in zip(oracle.attention_by_head_bwd(do, q, k, v, window), oracle.causal_attention_bwd(do, q, k, v, p)):
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-13)
