@@ -79,6 +79,7 @@ EXPORTS = {
     "gpt_workspace_bytes": (C.c_size_t, [_P, _I, _I]),
     "gpt_fwd_bwd": (C.c_int, [_P, _P, _P, _P, _I, _I, _P, _P, _I, _P, _S, _P]),
     "muon_workspace_bytes": (C.c_size_t, [_P]),
+    "gpt_ns_default_coeffs": (C.c_int32, [C.POINTER(C.c_float), _I]),
     "muon_step": (C.c_int, [_P, _P, _P, _P, _P, _F, _F, C.POINTER(C.c_float), _I, _P, _S, _P]),
     "normuon_state_elems": (C.c_int64, [_P]),
     "normuon_step": (C.c_int, [_P, _P, _P, _P, _P, _P, _F, _F, _F, C.POINTER(C.c_float), _I, _P, _S, _P]),
@@ -139,10 +140,22 @@ def _stream(stream=None):
     return C.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _coeffs(table):
+def _coeffs(table, steps=None):
+    """(host float buffer, rows) for a Newton-Schulz table; None passes NULL
+    (the library's built-in table) with `steps` rows of it (default 5)."""
+    if table is None:
+        return None, 5 if steps is None else int(steps)
     arr = np.ascontiguousarray(np.asarray(table, dtype=np.float32).reshape(-1, 3))
     buf = (C.c_float * arr.size)(*arr.ravel().tolist())
     return buf, arr.shape[0]
+
+
+def ns_default_coeffs():
+    """The library's built-in Newton-Schulz table as a float32 [rows, 3] array."""
+    rows = lib().gpt_ns_default_coeffs(None, 0)
+    buf = (C.c_float * (3 * rows))()
+    lib().gpt_ns_default_coeffs(buf, rows)
+    return np.array(buf[:], dtype=np.float32).reshape(rows, 3)
 
 
 class GptModel:

@@ -349,6 +349,17 @@ NsPlan plan_ns(long count, long xr, long xc, size_t base) {
   return p;
 }
 
+// Iterations whose products take the hi parts only (one bf16 MFMA product per
+// matrix product). The first iteration's rounding does not survive the rest:
+// with it plain and the others split, the result stays within 5e-5 (Gaussian)
+// to 2e-3 (rank 1 and 2) relative L2 of the fp64 iteration at the block-matrix
+// shapes (at most 8e-3 on small rank-1 matrices), against 3e-5 to 2e-3 with
+// every iteration split. A plain second iteration as well leaves 1e-2 to 6e-2
+// on small well-conditioned matrices, whose singular values reach the region
+// the later polynomials amplify within two steps. Every fp32 master value and
+// hi/lo output is formed as in the split iterations.
+constexpr int kNsPlainIters = 1;
+
 // Run ns_steps iterations on prepared X (x32, xh0, xl0 filled). Result in x32.
 hipError_t run_ns(char* ws, const NsPlan& p, int count, long xr, long xc, const float* coeffs,
                   int steps, hipStream_t s) {
@@ -362,10 +373,11 @@ hipError_t run_ns(char* ws, const NsPlan& p, int count, long xr, long xc, const 
   int cur = 0;
   for (int it = 0; it < steps; ++it) {
     const float a = coeffs[3 * it], b = coeffs[3 * it + 1], c = coeffs[3 * it + 2];
-    // A = X^T X, from hi/lo splits: Xh^T Xh + Xh^T Xl + Xl^T Xh.
+    const int nseg = it < kNsPlainIters ? 1 : 3;
+    // A = X^T X (split iterations: Xh^T Xh + Xh^T Xl + Xl^T Xh).
     GemmArgs g;
     gemm_args_init(g);
-    g.nseg = 3;
+    g.nseg = nseg;
     g.a[0] = xh[cur]; g.b[0] = xh[cur];
     g.a[1] = xh[cur]; g.b[1] = xl[cur];
     g.a[2] = xl[cur]; g.b[2] = xh[cur];
@@ -380,7 +392,7 @@ hipError_t run_ns(char* ws, const NsPlan& p, int count, long xr, long xc, const 
     if (e != hipSuccess) return e;
     // B = b A + c A A (A symmetric, so A A = A A^T).
     gemm_args_init(g);
-    g.nseg = 3;
+    g.nseg = nseg;
     g.a[0] = ah; g.b[0] = ah;
     g.a[1] = ah; g.b[1] = al;
     g.a[2] = al; g.b[2] = ah;
@@ -397,7 +409,7 @@ hipError_t run_ns(char* ws, const NsPlan& p, int count, long xr, long xc, const 
     if (e != hipSuccess) return e;
     // X = a X + X B (B symmetric, so X B = X B^T).
     gemm_args_init(g);
-    g.nseg = 3;
+    g.nseg = nseg;
     g.a[0] = xh[cur]; g.b[0] = bh;
     g.a[1] = xh[cur]; g.b[1] = bl;
     g.a[2] = xl[cur]; g.b[2] = bh;
@@ -888,14 +900,41 @@ int64_t normuon_state_elems(const gpt_model* m) {
   return n;
 }
 
+// Default Newton-Schulz table (rows of a, b, c). Rows 1-2 are the two triples
+// printed in the Polar Express list of "2. Otimizador Muon" ([CT50]); the page
+// stops there. Rows 3-5 continue the list by the same construction: each row
+// is the odd quintic a s + b s^3 + c s^5 minimising max |1 - p(s)| over the
+// interval of singular values the rows before it leave, starting from
+// [1e-3, 1] (rounded to 6 decimals).
+static const float kDefaultNsCoeffs[5][3] = {
+    {8.156f, -22.483f, 15.879f},
+    {4.043f, -2.809f, 0.500f},
+    {3.982257f, -2.970416f, 0.565427f},
+    {3.335133f, -2.500934f, 0.511459f},
+    {2.315341f, -1.682053f, 0.420229f},
+};
+constexpr int kDefaultNsRows = 5;
+
+int32_t gpt_ns_default_coeffs(float* out, int32_t max_rows) {
+  if (out) {
+    for (int r = 0; r < kDefaultNsRows && r < max_rows; ++r)
+      for (int c = 0; c < 3; ++c) out[3 * r + c] = kDefaultNsCoeffs[r][c];
+  }
+  return kDefaultNsRows;
+}
+
 // Momentum, Newton-Schulz and the update for both groups; with second_moment,
 // NorMuon rescales each group's orthogonalised update before the update.
 static gpt_status muon_impl(gpt_model* m, float* params, uint16_t* params_bf16, const float* grads,
                             float* momentum, float* second_moment, float lr, float momentum_coef, float beta2,
                             const float* ns_coeffs, int32_t ns_steps, void* workspace, size_t workspace_bytes,
                             void* stream) {
-  if (!m || !params || !params_bf16 || !grads || !momentum || !ns_coeffs) return GPT_EINVAL;
+  if (!m || !params || !params_bf16 || !grads || !momentum) return GPT_EINVAL;
   if (ns_steps < 1 || ns_steps > 8) return GPT_EINVAL;
+  if (!ns_coeffs) {
+    if (ns_steps > kDefaultNsRows) return GPT_EINVAL;
+    ns_coeffs = &kDefaultNsCoeffs[0][0];
+  }
   size_t nm_off = 0;
   if (!workspace || workspace_bytes < ns_workspace_bytes(*m, &nm_off)) return GPT_EWORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return GPT_EINVAL;
@@ -1070,16 +1109,11 @@ size_t gpt_op_ns_scratch_bytes(int32_t count, int32_t rows, int32_t cols) {
   return plan_ns(count, rows, cols, 0).total;
 }
 
-gpt_status gpt_op_newton_schulz(float* X, int32_t count, int32_t rows, int32_t cols,
-                                const float* ns_coeffs, int32_t ns_steps, void* scratch,
-                                size_t scratch_bytes, void* stream) {
-  if (!X || !ns_coeffs || count < 1 || rows < 1 || cols < 1 || ns_steps < 1 || ns_steps > 8)
-    return GPT_EINVAL;
-  if (rows < cols || cols % 8 != 0 || rows % 8 != 0) return GPT_ESHAPE;
+// The iteration of gpt_op_newton_schulz on a scratch region already checked
+// to hold plan_ns(count, rows, cols).
+static gpt_status ns_op_run(float* X, int32_t count, int32_t rows, int32_t cols, const float* ns_coeffs,
+                            int32_t ns_steps, char* ws, hipStream_t s) {
   const NsPlan p = plan_ns(count, rows, cols, 0);
-  if (!scratch || scratch_bytes < p.total) return GPT_EWORKSPACE;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  char* ws = reinterpret_cast<char*>(scratch);
   g_prof_model = nullptr;
   float* x32 = reinterpret_cast<float*>(ws + p.x32);
   const long n = (long)rows * cols;
@@ -1091,6 +1125,25 @@ gpt_status gpt_op_newton_schulz(float* X, int32_t count, int32_t rows, int32_t c
   HIP_TRY(hipMemcpyAsync(X, x32, (size_t)count * n * 4, hipMemcpyDeviceToDevice, s));
   return GPT_OK;
 }
+
+static gpt_status ns_op_check(const float* X, int32_t count, int32_t rows, int32_t cols,
+                              const float* ns_coeffs, int32_t ns_steps) {
+  if (!X || !ns_coeffs || count < 1 || rows < 1 || cols < 1 || ns_steps < 1 || ns_steps > 8)
+    return GPT_EINVAL;
+  if (rows < cols || cols % 8 != 0 || rows % 8 != 0) return GPT_ESHAPE;
+  return GPT_OK;
+}
+
+gpt_status gpt_op_newton_schulz(float* X, int32_t count, int32_t rows, int32_t cols,
+                                const float* ns_coeffs, int32_t ns_steps, void* scratch,
+                                size_t scratch_bytes, void* stream) {
+  const gpt_status st = ns_op_check(X, count, rows, cols, ns_coeffs, ns_steps);
+  if (st != GPT_OK) return st;
+  if (!scratch || scratch_bytes < plan_ns(count, rows, cols, 0).total) return GPT_EWORKSPACE;
+  return ns_op_run(X, count, rows, cols, ns_coeffs, ns_steps, reinterpret_cast<char*>(scratch),
+                   reinterpret_cast<hipStream_t>(stream));
+}
+
 
 // ---------------------------------------------------------------------------
 // Launch timing

@@ -185,8 +185,9 @@ size_t muon_workspace_bytes(const gpt_model* m);
  *   params_bf16  device bf16 shadow, refreshed for the updated matrices
  *   grads        device fp32 gradients
  *   momentum     device fp32 [gpt_num_params], M <- momentum_coef * M + G
- *   ns_coeffs    HOST pointer to ns_steps rows of (a, b, c) floats
- *   ns_steps     1..8
+ *   ns_coeffs    HOST pointer to ns_steps rows of (a, b, c) floats, or NULL
+ *                for the built-in five-row table (gpt_ns_default_coeffs)
+ *   ns_steps     1..8 (1..5 with the built-in table; GPT_EINVAL otherwise)
  * Per matrix: X0 = M / (||M||_F + 1e-7), oriented so rows >= cols, ns_steps
  * iterations, W <- W - lr * sqrt(max(1, rows/cols)) * X. The iteration runs
  * with fp32 accumulation and fp32 master X; each matrix product is formed
@@ -195,6 +196,19 @@ size_t muon_workspace_bytes(const gpt_model* m);
 gpt_status muon_step(gpt_model* m, float* params, uint16_t* params_bf16, const float* grads,
                      float* momentum, float lr, float momentum_coef, const float* ns_coeffs,
                      int32_t ns_steps, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The built-in Newton-Schulz table that muon_step and normuon_step use when
+ * ns_coeffs is NULL. Rows 1-2: the two (a, b, c) triples the Polar Express
+ * list of [CT50] "2. Otimizador Muon" prints before it breaks off. Rows 3-5:
+ * the list continued by its own construction (each row the odd quintic
+ * a s + b s^3 + c s^5 with the least maximum of |1 - p(s)| over the interval
+ * of singular values the earlier rows leave, from [1e-3, 1]).
+ *   out       HOST buffer of 3 * max_rows floats (may be NULL), filled row by row
+ *   max_rows  rows to copy at most
+ * Returns the number of rows of the table (5). Host only; no GPU call.
+ */
+int32_t gpt_ns_default_coeffs(float* out, int32_t max_rows);
 
 /*
  * Elements of the NorMuon second-moment state: one fp32 per element of the

@@ -111,7 +111,11 @@ def test_muon_and_op_validation():
     need = m.muon_workspace_bytes()
     ws = C.c_void_p(1 << 20)
     assert lib.muon_step(m.handle, fake, fake, fake, fake, 0.02, 0.95, buf, 0, ws, need, None) == binding.GPT_EINVAL
-    assert lib.muon_step(m.handle, fake, fake, fake, fake, 0.02, 0.95, None, 5, ws, need, None) == binding.GPT_EINVAL
+    # NULL coefficients select the built-in five-row table: more rows than it has is rejected,
+    # and the workspace check still comes before any launch.
+    assert lib.muon_step(m.handle, fake, fake, fake, fake, 0.02, 0.95, None, 6, ws, need, None) == binding.GPT_EINVAL
+    assert lib.muon_step(m.handle, fake, fake, fake, fake, 0.02, 0.95, None, 5, ws, need - 1, None) == binding.GPT_EWORKSPACE
+    assert lib.muon_step(m.handle, None, fake, fake, fake, 0.02, 0.95, None, 5, ws, need, None) == binding.GPT_EINVAL
     assert lib.muon_step(m.handle, fake, fake, fake, fake, 0.02, 0.95, buf, 5, ws, need - 1, None) == binding.GPT_EWORKSPACE
     # GEMM shape rules: N % 4, contiguous dims % 8.
     assert lib.gpt_op_gemm(64, 6, 64, 1, fake, 64, 0, 1, fake, 64, 0, 1, fake, 8, 0, 0, None) == binding.GPT_ESHAPE
@@ -119,6 +123,25 @@ def test_muon_and_op_validation():
     assert lib.gpt_op_gemm(64, 64, 64, 1, fake, 64, 0, 1, fake, 64, 0, 1, fake, 64, 0, 9, None) == binding.GPT_EINVAL
     assert lib.gpt_op_newton_schulz(fake, 1, 64, 128, buf, 5, ws, 1 << 30, None) == binding.GPT_ESHAPE
     assert binding.status_str(binding.GPT_ETOKEN).startswith("token")
+
+
+def test_built_in_newton_schulz_table():
+    """muon_step's table for ns_coeffs = NULL: its first two rows are the two
+    triples the page prints (golden file), rows 3-5 follow the greedy minimax
+    rule as the oracle re-derives it, and the whole table is the one the tests
+    and the bench pass explicitly."""
+    import numpy as np
+
+    import oracle
+    from test_oracle_muon import _read_triples
+
+    table = binding.ns_default_coeffs()
+    assert table.shape == (5, 3)
+    printed = _read_triples(os.path.join(ROOT, "tests", "golden", "ns_coeffs_printed.txt"))
+    np.testing.assert_array_equal(table[:2], np.asarray(printed, dtype=np.float32))
+    derived, _ = oracle.greedy_minimax_triples(printed)
+    np.testing.assert_allclose(table[2:], derived[2:], atol=2e-4)
+    np.testing.assert_array_equal(table, syn.NS_COEFFS.astype(np.float32))
 
 
 def test_adamw_state_and_host_validation_precede_any_launch():
