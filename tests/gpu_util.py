@@ -37,27 +37,29 @@ def log(msg):
     print(msg, flush=True)
 
 
-def assert_scalar_grads(grads, ref_grads, scales, log=None, eps=1e-3):
-    """Gradients of the scalar tensors are dot products, over every token and
-    channel, of a stream gradient g with a kept stream v. The final norm makes
-    the loss insensitive to the stream's scale, so these sums cancel down to a
-    small fraction (6e-5 to 4e-3 here) of their Cauchy-Schwarz bound
-    S = sum over rows of |g_row| |v_row| (the oracle reports S per scalar).
-    Their error is at most |delta g| |v| <= eps S, eps being the relative error
-    of the device's stream gradient (bounded by the 2e-2 gradient bar); the
-    errors measured on these models stay below 5e-5 S, except the smear gate
-    at the end of the backward chain (up to 2.6e-4 S), so per scalar:
-    |delta| <= 2e-2 |ref| + eps S with eps = 1e-3. A sign error or a wrong
-    kept stream also breaks the matrix and embedding gradients that the same
-    stream gradient feeds, which the rel-L2 checks catch. The value-embedding
-    gates sum products of dv, which comes out of the bf16 attention backward
-    with about 1e-2 relative error (within the 2e-2 bar): they take eps = 1e-2
-    (measured up to 2.9e-3 S)."""
+def assert_scalar_grads(grads, ref_grads, scales, log=None, eps=2e-4, rel=2e-2):
+    """Gradients of the scalar tensors (and of the value-embedding gates) are
+    dot products, over every token and channel, of a stream gradient g with a
+    kept stream v. For a sum of N*d weakly correlated terms |sum| is of order
+    S / sqrt(N d), S = sum over rows of |g_row| |v_row| being its
+    Cauchy-Schwarz bound (the oracle reports S per element), so at the test
+    sizes the references sit at 1e-4 to 3e-2 of S. The device's error in such
+    a sum is at most |delta g| |v|, a small multiple of S times the relative
+    error of the stream gradient it reads.
+
+    Per element: |delta| <= max(rel |ref|, eps S). A reference above
+    (eps / rel) S is thus held to the plain relative bar, and every reference
+    above eps S to the right sign; eps is a few times the error measured on the
+    device (see the callers)."""
     for k, s in scales.items():
         got = np.asarray(grads[k], dtype=np.float64).ravel()
         ref = np.asarray(ref_grads[k]).ravel()
         sv = np.asarray(s).ravel()
+        e = eps[k] if isinstance(eps, dict) else eps
         if log is not None:
-            log(f"  {k}: |delta|/S = {np.max(np.abs(got - ref) / sv):.2e}")
-        tol = 2e-2 * np.abs(ref) + eps * sv
+            log(f"  {k}: |delta|/S = {np.max(np.abs(got - ref) / sv):.2e} (eps {e:.0e}); "
+                f"|ref|/S in [{np.min(np.abs(ref) / sv):.1e}, {np.max(np.abs(ref) / sv):.1e}]")
+        tol = np.maximum(rel * np.abs(ref), e * sv)
         assert np.all(np.abs(got - ref) <= tol), (k, got, ref, sv)
+        big = np.abs(ref) > e * sv
+        assert np.all(np.sign(got[big]) == np.sign(ref[big])), (k, got, ref)

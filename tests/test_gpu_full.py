@@ -12,10 +12,10 @@ For each depth:
   heads for the 10 query heads plus value embeddings on the odd layers, and
   with residual scalars, a backout at layer 10 and smear): loss |delta| <= 1e-2,
   every gradient tensor rel-L2 <= 2e-2, embedding rows of absent tokens exactly
-  zero. The sequence is the workload's full length except at d32, where it is
-  1024 tokens: the fp64 oracle of a 32-layer model at 4096 tokens needs about
-  80 GB of host memory and minutes; attention at 4096 is compared with the
-  oracle at op level, and the full d32 shape is covered by the checks below.
+  zero. The sequence is the workload's full length, 4096 tokens at d32 (the
+  oracle recomputes each head's probabilities in the backward, so it holds
+  one T x T array per head at a time; about 40 GB of host memory and several
+  minutes at d32).
 * The full microbatch against the same sequences run one at a time and
   accumulated (accumulate=1) in the same workspace. Per token the forward and
   the activation gradients are the same arithmetic (no product is split over
@@ -47,7 +47,13 @@ from gpt_pretraining_step_bf16_amd.step import TrainState, window_pattern  # noq
 LOSS_TOL = 1e-2
 REL_TOL = 2e-2
 ACC_TOL = 1e-5
-ORACLE_SEQ = {"d12": 2048, "d20": 2048, "d26": 2048, "d32": 1024}
+# Scalar and value-embedding-gate gradients: allowed |delta| as a fraction of
+# their Cauchy-Schwarz scale S (gpu_util.assert_scalar_grads), a few times
+# the largest error measured at these sizes.
+SCALAR_EPS = {"resid_lambdas": 2e-4, "x0_lambdas": 2e-4, "backout_lambda": 2e-4, "smear_lambda": 2e-4,
+              "smear_gate": 1e-3}
+VE_GATE_EPS = 1e-3
+ORACLE_SEQ = {"d12": 2048, "d20": 2048, "d26": 2048, "d32": 4096}
 MUON_LAYERS = {"d12": "first_last", "d20": "first_last", "d26": "first", "d32": "first"}
 NAMES = ("wq", "wk", "wv", "wo", "wfc", "wproj")
 
@@ -62,8 +68,8 @@ def _cuda(a):
 
 
 # The fp64 oracle needs from a few seconds (d12) to about a minute (d26) of
-# host time for one sequence.
-@pytest.mark.timeout(900)
+# host time for one sequence, and several minutes for d32's 4096 tokens.
+@pytest.mark.timeout(1000)
 @pytest.mark.parametrize("name,pattern,kv_heads,scalars,ve", [
     ("d12", None, None, False, False), ("d20", None, None, False, False), ("d26", None, None, False, False),
     ("d32", None, None, False, False), ("d12", "SSSL", None, False, False), ("d20", "SSSL", None, False, False),
@@ -122,8 +128,8 @@ def test_one_sequence_matches_oracle(name, pattern, kv_heads, scalars, ve):
     if scales:
         gates = {k: v for k, v in scales.items() if k.endswith(".ve_gate")}
         others = {k: v for k, v in scales.items() if k not in gates}
-        assert_scalar_grads(sg, sref, others, log)
-        assert_scalar_grads(sg, sref, gates, log, eps=1e-2)
+        assert_scalar_grads(sg, sref, others, log, eps=SCALAR_EPS)
+        assert_scalar_grads(sg, sref, gates, log, eps=VE_GATE_EPS)
 
 
 @pytest.mark.timeout(300)
@@ -200,3 +206,28 @@ def test_muon_matches_oracle(name):
     log("  worst update rel-L2 " + " ".join(f"{k}:{e:.2e}" for e, k in sorted(worst)[-3:]))
     np.testing.assert_array_equal(new_w["wte"], w["wte"])
     np.testing.assert_array_equal(new_w["lm_head"], w["lm_head"])
+
+
+@pytest.mark.timeout(300)
+def test_muon_step_is_bit_reproducible_and_takes_the_built_in_table():
+    """muon_step at d20 twice from identical weights, gradients and momenta:
+    identical parameters, bf16 shadow and momenta, bit for bit (the staged
+    Newton-Schulz epilogues included); the NULL table (the library's built-in
+    one) gives the same bits as passing that table explicitly."""
+    L, V, T, _ = _cfg("d20")
+    log("d20 muon repeat")
+    w = syn.init_weights(L, V, seed=0)
+    g = syn.random_like_grads(L, V, seed=7, scale=1e-2)
+    m0 = syn.random_like_grads(L, V, seed=8, scale=1e-2)
+    st = TrainState(L, V, T, 1)
+    st.load_grads(g)
+    outs = []
+    for coeffs in (syn.NS_COEFFS, syn.NS_COEFFS, None):
+        st.load_weights(w)
+        st.load_momentum(m0)
+        st.muon(syn.MUON_LR, syn.MUON_MOMENTUM, coeffs)
+        torch.cuda.synchronize()
+        outs.append((st.params.clone(), st.params_bf16.clone(), st.momentum.clone()))
+    for other in outs[1:]:
+        for a, b in zip(outs[0], other):
+            assert torch.equal(a, b)

@@ -173,24 +173,49 @@ def test_gqa_muon_matches_oracle(normuon):
         np.testing.assert_array_equal(new_w[k], w[k])
 
 
-@pytest.mark.parametrize("depth,vocab,seq,batch,resid,backout,smear", [
-    (2, 2048, 64, 2, True, 1, False), (3, 2048, 200, 3, True, 0, False), (4, 2048, 128, 2, False, 2, False),
-    (4, 2048, 128, 2, True, None, False), (2, 2048, 64, 2, False, None, True), (3, 2048, 200, 3, True, 1, True)])
-def test_scalars_fwd_bwd_matches_oracle(depth, vocab, seq, batch, resid, backout, smear):
+# Error allowance of the scalar and gate gradients, as a fraction of their
+# Cauchy-Schwarz scale S (gpu_util.assert_scalar_grads): a few times the
+# largest |delta|/S measured on the device for these cases (scalars 5e-5 S,
+# the smear gate, last in the backward chain, 2.6e-4 S).
+# Error allowance of the scalar and gate gradients, as a fraction of their
+# Cauchy-Schwarz scale S (gpu_util.assert_scalar_grads): about 2.5 times the
+# largest |delta|/S measured on the device over these cases (scalars 2.1e-4 S,
+# in the 12-token case; the smear gate, last in the backward chain, 8.1e-4 S).
+# The value-embedding gates sum products of dv, which leaves the bf16
+# attention backward with about 1e-2 relative error (measured 2.9e-3 S).
+VE_GATE_EPS = 7e-3
+SCALAR_EPS = {"resid_lambdas": 5e-4, "x0_lambdas": 5e-4, "backout_lambda": 5e-4, "smear_lambda": 5e-4,
+              "smear_gate": 2e-3}
+
+
+@pytest.mark.parametrize("depth,vocab,seq,batch,resid,backout,smear,seeds", [
+    (2, 2048, 64, 2, True, 1, False, (2, 3)), (3, 2048, 200, 3, True, 0, False, (2, 3)),
+    (4, 2048, 128, 2, False, 2, False, (2, 3)), (4, 2048, 128, 2, True, None, False, (2, 3)),
+    (2, 2048, 64, 2, False, None, True, (2, 3)), (3, 2048, 200, 3, True, 1, True, (2, 3)),
+    (2, 2048, 8, 1, True, 1, True, (4, 5)), (3, 2048, 12, 1, True, 1, True, (2, 3))])
+def test_scalars_fwd_bwd_matches_oracle(depth, vocab, seq, batch, resid, backout, smear, seeds):
     """Residual scalars (random values) and backout at various layers, with a
     ragged length; the scalar gradients are full reductions over tokens, checked
     against their Cauchy-Schwarz scale (gpu_util.assert_scalar_grads). Weights
     of std 0.1 and backout_lambda 0.9 keep the kept stream far from parallel to
-    the final one, so the backout gradient is not cancelled to noise."""
-    st, tok, tgt, loss, grads, ref_loss, ref_grads = _run_case(depth, vocab, seq, batch, seed_w=2, seed_t=3,
-                                                                resid_scalars=resid, backout_layer=backout,
-                                                                std=0.1, backout_value=0.9, smear=smear)
+    the final one, so the backout gradient is not cancelled to noise. The two
+    short sequences (8 and 12 tokens) sum few enough terms that several
+    references sit above 1e-2 S, where the plain 2e-2 relative bar applies."""
+    st, tok, tgt, loss, grads, ref_loss, ref_grads = _run_case(depth, vocab, seq, batch, seed_w=seeds[0],
+                                                                seed_t=seeds[1], resid_scalars=resid,
+                                                                backout_layer=backout, std=0.1, backout_value=0.9,
+                                                                smear=smear)
     assert abs(loss - ref_loss) <= LOSS_TOL
     scalars = ("resid_lambdas", "x0_lambdas", "backout_lambda", "smear_gate", "smear_lambda")
     _assert_grads(grads, ref_grads, tok, vocab, skip=scalars)
-    assert_scalar_grads(grads, ref_grads, _run_case.scales, log)
+    assert_scalar_grads(grads, ref_grads, _run_case.scales, log, eps=SCALAR_EPS)
     if backout is not None and not smear:  # these cases keep the backout gradient above its noise floor
         assert abs(ref_grads["backout_lambda"][0, 0]) > 1e-3 * _run_case.scales["backout_lambda"][0, 0]
+    if seq <= 12:
+        # Some references of the short cases are held to the plain relative bar.
+        held = sum(int(np.sum(np.abs(ref_grads[k]) >= 1e-2 * _run_case.scales[k])) for k in _run_case.scales)
+        log(f"  {held} scalar-gradient elements at or above 1e-2 S")
+        assert held >= 5
     # Accumulation: a second identical call with accumulate=1 doubles every gradient.
     toks = torch.from_numpy(tok).cuda()
     tgts = torch.from_numpy(tgt).cuda()
@@ -216,7 +241,7 @@ def test_value_embeddings_fwd_bwd_matches_oracle(depth, kv_heads, seq, batch, ve
     _assert_grads(grads, ref_grads, tok, 2048, skip=gates)
     # Gate gradients are token sums of stream-gradient products, like the
     # scalars: checked against their Cauchy-Schwarz scale.
-    assert_scalar_grads(grads, ref_grads, {k: _run_case.scales[k] for k in gates}, log, eps=1e-2)
+    assert_scalar_grads(grads, ref_grads, {k: _run_case.scales[k] for k in gates}, log, eps=VE_GATE_EPS)
     absent = np.setdiff1d(np.arange(2048), tok.ravel())
     for l in ve_layers:
         assert not np.any(grads[f"h{l}.ve"][absent])
@@ -294,6 +319,43 @@ def test_gradient_accumulation_adds():
     want = (outs[0] + outs[1]).cpu().numpy()
     got = st.grads.cpu().numpy()
     assert rel_l2(got, want) < 1e-5
+
+
+def test_gradient_accumulation_matches_oracle():
+    """The single-GPU accumulation mode ([HADA] "Requisitos do ambiente de
+    computação": one GPU runs the microbatches of eight in sequence): three
+    microbatches of different lengths and ignored targets, accumulated with
+    accumulate=1, against the sum of the oracle's per-microbatch gradients
+    (each the gradient of that microbatch's mean loss over its valid targets).
+    A fourth call without accumulate restarts from zero."""
+    cfg = syn.CONFIGS["tiny"]
+    depth, vocab = cfg["depth"], cfg["vocab"]
+    w = syn.init_weights(depth, vocab, seed=0)
+    w64 = {k: bf16_round(v).astype(np.float64) for k, v in w.items()}
+    st = TrainState(depth, vocab, 64, 3)
+    st.load_weights(w)
+    ref = {k: np.zeros_like(v) for k, v in w64.items()}
+    cases = [(2, 64, 1, [(0, 5)]), (3, 40, 2, [(1, 0), (2, 39), (2, 7)]), (1, 64, 3, [])]
+    seen = []
+    for i, (batch, seq, seed, ignore) in enumerate(cases):
+        tok, tgt = syn.split_tokens(syn.zipf_ids(batch, seq, vocab, seed=seed))
+        tgt = tgt.copy()
+        for (b, t) in ignore:
+            tgt[b, t] = -1
+        seen.append(tok.ravel())
+        st.fwd_bwd(torch.from_numpy(tok).cuda(), torch.from_numpy(tgt).cuda(), accumulate=i > 0)
+        _, g = oracle.forward_backward(w64, tok, tgt)
+        for k in ref:
+            ref[k] += g[k]
+    torch.cuda.synchronize()
+    assert st.check() == 0
+    got = st.to_host(st.grads)
+    _assert_grads(got, ref, np.concatenate(seen), vocab)
+    tok, tgt = syn.split_tokens(syn.zipf_ids(1, 64, vocab, seed=3))
+    st.fwd_bwd(torch.from_numpy(tok).cuda(), torch.from_numpy(tgt).cuda())
+    torch.cuda.synchronize()
+    _, g = oracle.forward_backward(w64, tok, tgt)
+    _assert_grads(st.to_host(st.grads), g, tok, vocab)
 
 
 def test_out_of_range_token_sets_flag():
