@@ -95,6 +95,7 @@ EXPORTS = {
     "gpt_get_attention_windows": (C.c_int, [_P, C.POINTER(C.c_int32), _I]),
     "gpt_op_ns_scratch_bytes": (C.c_size_t, [_I, _I, _I]),
     "gpt_op_newton_schulz": (C.c_int, [_P, _I, _I, _I, C.POINTER(C.c_float), _I, _P, _S, _P]),
+    "gpt_op_newton_schulz_noalloc": (C.c_int, [_P, _I, _I, _I, C.POINTER(C.c_float), _I, _P]),
     "gpt_profile_enable": (C.c_int, [_P, _I]),
     "gpt_profile_reset": (C.c_int, [_P]),
     "gpt_profile_read": (C.c_int, [_P, _I, C.POINTER(C.c_double), C.POINTER(C.c_double),
@@ -315,6 +316,17 @@ def op_attention_bwd(qkv, o, lse, dO, dqkv, scratch, batch, seq, heads, window=-
 
 def ns_scratch_bytes(count, rows, cols) -> int:
     return int(lib().gpt_op_ns_scratch_bytes(count, rows, cols))
+
+
+# Size of the library's fixed device array behind gpt_op_newton_schulz_noalloc
+# (GPT_NS_STATIC_SCRATCH_BYTES in include/gpt.h).
+NS_STATIC_SCRATCH_BYTES = 128 << 20
+
+
+def op_newton_schulz_noalloc(X, count, rows, cols, ns_coeffs, stream=None):
+    buf, steps = _coeffs(ns_coeffs)
+    st = lib().gpt_op_newton_schulz_noalloc(_ptr(X), count, rows, cols, buf, steps, _stream(stream))
+    _check(st, "gpt_op_newton_schulz_noalloc")
 
 
 def op_newton_schulz(X, count, rows, cols, ns_coeffs, scratch, stream=None):

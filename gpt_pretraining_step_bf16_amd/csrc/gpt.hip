@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -1141,6 +1142,48 @@ gpt_status gpt_op_newton_schulz(float* X, int32_t count, int32_t rows, int32_t c
   if (st != GPT_OK) return st;
   if (!scratch || scratch_bytes < plan_ns(count, rows, cols, 0).total) return GPT_EWORKSPACE;
   return ns_op_run(X, count, rows, cols, ns_coeffs, ns_steps, reinterpret_cast<char*>(scratch),
+                   reinterpret_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------
+// Newton-Schulz without a caller-provided scratch: the same kernels on a
+// fixed device array. Each device that runs it holds its own copy of the
+// array until the process ends; its device address is looked up once per
+// device (the host-side name only stands in for the symbol and is never used
+// as an address).
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[GPT_NS_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+gpt_status gpt_op_newton_schulz_noalloc(float* X, int32_t count, int32_t rows, int32_t cols,
+                                        const float* ns_coeffs, int32_t ns_steps, void* stream) {
+  const gpt_status st = ns_op_check(X, count, rows, cols, ns_coeffs, ns_steps);
+  if (st != GPT_OK) return st;
+  if (plan_ns(count, rows, cols, 0).total > (size_t)GPT_NS_STATIC_SCRATCH_BYTES) return GPT_EWORKSPACE;
+  void* ws = nullptr;
+  HIP_TRY(static_scratch(&ws));
+  return ns_op_run(X, count, rows, cols, ns_coeffs, ns_steps, reinterpret_cast<char*>(ws),
                    reinterpret_cast<hipStream_t>(stream));
 }
 

@@ -343,6 +343,22 @@ gpt_status gpt_op_newton_schulz(float* X, int32_t count, int32_t rows, int32_t c
                                 const float* ns_coeffs, int32_t ns_steps, void* scratch,
                                 size_t scratch_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid it):
+ * gpt_op_newton_schulz with its scratch in a fixed device array of
+ * GPT_NS_STATIC_SCRATCH_BYTES that the library holds on each device it runs
+ * on until the process ends. Nothing is allocated; arguments and result as
+ * for gpt_op_newton_schulz (same kernels, same bits). Returns GPT_EWORKSPACE
+ * when gpt_op_ns_scratch_bytes(count, rows, cols) exceeds the array (checked
+ * on the host before any launch; up to four 1280 x 1280 matrices, or one
+ * 5120 x 1280, fit). Every call on a device shares that device's array: calls
+ * that overlap on one device (other streams, other host threads) race and must
+ * be serialised by the caller. The array keeps the last call's contents;
+ * nothing in it needs to start at zero. */
+#define GPT_NS_STATIC_SCRATCH_BYTES (128u << 20)
+gpt_status gpt_op_newton_schulz_noalloc(float* X, int32_t count, int32_t rows, int32_t cols,
+                                        const float* ns_coeffs, int32_t ns_steps, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -125,6 +125,24 @@ def test_muon_and_op_validation():
     assert binding.status_str(binding.GPT_ETOKEN).startswith("token")
 
 
+def test_no_alloc_newton_schulz_host_checks():
+    """The allocation-free Newton-Schulz entry point: its array size in the
+    header equals the binding's, the documented shapes fit, larger requests
+    and bad arguments are refused before any GPU call."""
+    text = open(HEADER).read()
+    m = re.search(r"#define GPT_NS_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == binding.NS_STATIC_SCRATCH_BYTES
+    cap = binding.NS_STATIC_SCRATCH_BYTES
+    assert binding.ns_scratch_bytes(2, 1280, 1280) <= cap and binding.ns_scratch_bytes(1, 5120, 1280) <= cap
+    lib = binding.lib()
+    buf, _ = binding._coeffs(syn.NS_COEFFS)
+    fake = C.c_void_p(4096)
+    assert lib.gpt_op_newton_schulz_noalloc(fake, 6, 1280, 1280, buf, 5, None) == binding.GPT_EWORKSPACE
+    assert lib.gpt_op_newton_schulz_noalloc(None, 1, 256, 256, buf, 5, None) == binding.GPT_EINVAL
+    assert lib.gpt_op_newton_schulz_noalloc(fake, 1, 128, 256, buf, 5, None) == binding.GPT_ESHAPE
+    assert lib.gpt_op_newton_schulz_noalloc(fake, 1, 256, 256, buf, 9, None) == binding.GPT_EINVAL
+
+
 def test_built_in_newton_schulz_table():
     """muon_step's table for ns_coeffs = NULL: its first two rows are the two
     triples the page prints (golden file), rows 3-5 follow the greedy minimax
