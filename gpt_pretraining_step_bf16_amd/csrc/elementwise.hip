@@ -74,22 +74,198 @@ __global__ void embed_fwd_kernel(const int32_t* __restrict__ tok, const uint16_t
   }
 }
 
-// dwte[tok[i]] += dx[i]; rows of absent tokens are untouched (zeroed before).
-__global__ void embed_bwd_kernel(const int32_t* __restrict__ tok, const float* __restrict__ dx,
-                                 float* __restrict__ dwte, long N, int d, int V) {
-  const int chunks = d / 4;
-  for (long c = blockIdx.x * (long)blockDim.x + threadIdx.x; c < N * chunks;
-       c += (long)gridDim.x * blockDim.x) {
-    const long i = c / chunks;
-    const int k = (int)(c - i * chunks);
-    const int t = tok[i];
-    if (t < 0 || t >= V) continue;
-    const float4 g = *reinterpret_cast<const float4*>(dx + i * d + 4 * k);
-    float* dst = dwte + (long)t * d + 4 * k;
-    unsafeAtomicAdd(dst + 0, g.x);
-    unsafeAtomicAdd(dst + 1, g.y);
-    unsafeAtomicAdd(dst + 2, g.z);
-    unsafeAtomicAdd(dst + 3, g.w);
+// ---------------------------------------------------------------------------
+// Row scatter-add with a fixed summation order: out[v] (+)= sum over the
+// positions i with idx[i] = v of src row i ([CT50] "1. Modelo GPT": the untied
+// input table's gradient, and the value-embedding tables'). Rows of ids that do
+// not occur are written as exact zeros (or left as they are when accumulating).
+//   scatter_runs_kernel: one workgroup per group of 256 consecutive positions
+//     sorts the keys (id, position) in LDS (bitonic), splits them into runs of
+//     equal id and sums each run's src rows in position order into a partial
+//     row part[group * 256 + run]; run_ids[group * 256 + run] holds its id
+//     (ascending within the group) and nruns[group] the number of runs.
+//   scatter_merge_kernel: one workgroup per SC_R consecutive ids gathers, for
+//     each id, the partial rows of the groups that hold it and adds them in
+//     group order.
+// No atomics: the result is the same bits on every run. Zipf-skewed ids put
+// at most 256 partial rows (one per group) behind the most frequent id.
+// ---------------------------------------------------------------------------
+constexpr int SC_G = 256;  // positions per group (= threads of the run kernel)
+constexpr int SC_R = 4;    // ids per workgroup of the merge kernel
+
+// Plain fp32 rows [N, ld].
+struct ScatterSrcF32 {
+  const float* p;
+  long ld;
+  __device__ __forceinline__ float4 load(long row, int c4) const {
+    return reinterpret_cast<const float4*>(p + row * ld)[c4];
+  }
+};
+// Gated value rows of the value-embedding backward: 3 sigmoid(logit[row][h])
+// times dv[row][c] (c in head h = c / 128), dv the v block of the bf16 dqkv
+// rows (row stride ld, v at column offset 0 of the pointer).
+struct ScatterSrcVe {
+  const uint16_t* dv;
+  long ld;
+  const float* logits;
+  int Hkv;
+  __device__ __forceinline__ float4 load(long row, int c4) const {
+    const int c = 4 * c4;
+    const float lg = logits[row * Hkv + (c >> 7)];
+    const float g = 3.f * (1.f / (1.f + __expf(-lg)));
+    const uint2 u = *reinterpret_cast<const uint2*>(dv + row * ld + c);
+    return make_float4(g * bf_lo(u.x), g * bf_hi(u.x), g * bf_lo(u.y), g * bf_hi(u.y));
+  }
+};
+
+template <class Src>
+__global__ void __launch_bounds__(SC_G) scatter_runs_kernel(Src src, const int32_t* __restrict__ idx, long N,
+                                                             int V, int W4, float* __restrict__ part,
+                                                             int32_t* __restrict__ run_ids,
+                                                             int32_t* __restrict__ nruns) {
+  __shared__ uint32_t key[SC_G];
+  __shared__ int run_start[SC_G + 1];
+  __shared__ int wave_runs[SC_G / 64], wave_valid[SC_G / 64];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int g = blockIdx.x;
+  const long base = (long)g * SC_G;
+  // Key = id << 8 | position in the group; ids outside [0, V) (flagged by the
+  // forward) and positions past N sort last and are skipped.
+  uint32_t k = 0xffffffffu;
+  if (base + t < N) {
+    const int id = idx[base + t];
+    if (id >= 0 && id < V) k = ((uint32_t)id << 8) | (uint32_t)t;
+  }
+  key[t] = k;
+  __syncthreads();
+  for (int size = 2; size <= SC_G; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const int j = t ^ stride;
+      if (j > t) {
+        const uint32_t a = key[t], b = key[j];
+        if ((a > b) == ((t & size) == 0)) {
+          key[t] = b;
+          key[j] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  k = key[t];
+  const bool valid = k != 0xffffffffu;
+  const bool head = valid && (t == 0 || (key[t - 1] >> 8) != (k >> 8));
+  const unsigned long long mh = __ballot(head), mv = __ballot(valid);
+  if (lane == 0) {
+    wave_runs[wave] = __popcll(mh);
+    wave_valid[wave] = __popcll(mv);
+  }
+  __syncthreads();
+  int before = 0, runs = 0, nvalid = 0;
+#pragma unroll
+  for (int w = 0; w < SC_G / 64; ++w) {
+    before += w < wave ? wave_runs[w] : 0;
+    runs += wave_runs[w];
+    nvalid += wave_valid[w];
+  }
+  if (head) {
+    const int r = before + __popcll(mh & ((1ull << lane) - 1ull));
+    run_start[r] = t;
+    run_ids[base + r] = (int32_t)(k >> 8);
+  }
+  if (t == 0) {
+    run_start[runs] = nvalid;
+    nruns[g] = runs;
+  }
+  __syncthreads();
+  // Each wave sums runs wave, wave + 4, ...; a run's rows in position order.
+  for (int r = wave; r < runs; r += SC_G / 64) {
+    const int s0 = run_start[r], s1 = run_start[r + 1];
+    float4* dst = reinterpret_cast<float4*>(part + (base + r) * (long)(4 * W4));
+    for (int c4 = lane; c4 < W4; c4 += 64) {
+      float4 acc = src.load(base + (key[s0] & 0xffu), c4);
+      for (int j = s0 + 1; j < s1; ++j) {
+        const float4 v = src.load(base + (key[j] & 0xffu), c4);
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+      }
+      dst[c4] = acc;
+    }
+  }
+}
+
+// Ids v0 .. v0 + SC_R - 1; list (dynamic LDS) holds, per id, the partial-row
+// indices of the groups that contain it, in group order.
+__global__ void __launch_bounds__(256) scatter_merge_kernel(const float* __restrict__ part,
+                                                            const int32_t* __restrict__ run_ids,
+                                                            const int32_t* __restrict__ nruns, int G, int V,
+                                                            int W4, float* __restrict__ out, int accumulate) {
+  extern __shared__ int list[];  // [SC_R][G]
+  __shared__ int wave_cnt[4][SC_R];
+  __shared__ int count[SC_R];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int v0 = blockIdx.x * SC_R;
+  if (t < SC_R) count[t] = 0;
+  __syncthreads();
+  for (int c0 = 0; c0 < G; c0 += 256) {
+    const int g = c0 + t;
+    int r_of[SC_R];
+#pragma unroll
+    for (int i = 0; i < SC_R; ++i) r_of[i] = -1;
+    if (g < G) {
+      const int32_t* ids = run_ids + (long)g * SC_G;
+      int lo = 0, hi = nruns[g];
+      while (lo < hi) {  // first run with id >= v0
+        const int mid = (lo + hi) >> 1;
+        if (ids[mid] < v0) lo = mid + 1; else hi = mid;
+      }
+      const int n = nruns[g];
+      for (int r = lo; r < n && ids[r] < v0 + SC_R; ++r) {
+        const int di = ids[r] - v0;
+#pragma unroll
+        for (int i = 0; i < SC_R; ++i)
+          if (di == i) r_of[i] = r;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < SC_R; ++i) {
+      const unsigned long long m = __ballot(r_of[i] >= 0);
+      if (lane == 0) wave_cnt[wave][i] = __popcll(m);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < SC_R; ++i) {
+      const unsigned long long m = __ballot(r_of[i] >= 0);
+      if (r_of[i] >= 0) {
+        int pos = count[i];
+        for (int w = 0; w < wave; ++w) pos += wave_cnt[w][i];
+        pos += __popcll(m & ((1ull << lane) - 1ull));
+        list[i * G + pos] = g * SC_G + r_of[i];
+      }
+    }
+    __syncthreads();
+    if (t < SC_R) count[t] += wave_cnt[0][t] + wave_cnt[1][t] + wave_cnt[2][t] + wave_cnt[3][t];
+    __syncthreads();
+  }
+  for (int i = 0; i < SC_R; ++i) {
+    const int v = v0 + i;
+    if (v >= V) break;
+    const int n = count[i];
+    const int* li = list + i * G;
+    float4* dst = reinterpret_cast<float4*>(out + (long)v * (4 * W4));
+    for (int c4 = t; c4 < W4; c4 += 256) {
+      float4 acc = accumulate ? dst[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+      for (int e = 0; e < n; ++e) {
+        const float4 p = reinterpret_cast<const float4*>(part + (long)li[e] * (4 * W4))[c4];
+        acc.x += p.x;
+        acc.y += p.y;
+        acc.z += p.z;
+        acc.w += p.w;
+      }
+      dst[c4] = acc;
+    }
   }
 }
 
@@ -961,14 +1137,15 @@ __global__ void __launch_bounds__(256) ve_fwd_kernel(uint16_t* __restrict__ qkv,
 
 // Backward with dv the gradient of v (in dqkv): per row and head,
 // s_h = dv_h . ve_h, dlogit_h = 3 sig (1 - sig) s_h (saved [N, Hkv]);
-// dtable[token] += 3 sig dv_h (fp32 atomics, as the embedding); block partials
-// of d ve_gate[h][j] = sum dlogit_h xn[j] go to partials[blockIdx.x][Hkv*32].
+// block partials of d ve_gate[h][j] = sum dlogit_h xn[j] go to
+// partials[blockIdx.x][Hkv*32]. (The table gradient, the rows 3 sig dv_h
+// summed per token, is the ordered scatter below.)
 // Grid-stride over rows, one wave per row, 4 waves per block.
 __global__ void __launch_bounds__(256) ve_bwd_kernel(const uint16_t* __restrict__ dqkv,
                                                      const uint16_t* __restrict__ xn,
                                                      const int32_t* __restrict__ tok,
                                                      const uint16_t* __restrict__ table,
-                                                     const float* __restrict__ logits, float* __restrict__ dtable,
+                                                     const float* __restrict__ logits,
                                                      float* __restrict__ dlogit, float* __restrict__ partials,
                                                      long N, int d, int Hkv, int V) {
   __shared__ float red[4][16 * VE_CH];
@@ -982,7 +1159,6 @@ __global__ void __launch_bounds__(256) ve_bwd_kernel(const uint16_t* __restrict_
     const bool ok = t >= 0 && t < V;
     const uint16_t* dv = dqkv + row * (long)(d + 2 * dkv) + d + dkv;
     const uint16_t* e = table + (long)(ok ? t : 0) * dkv;
-    float* dt = dtable + (long)(ok ? t : 0) * dkv;
     const float xj = lane < VE_CH ? bf2f(xn[row * d + lane]) : 0.f;
 #pragma unroll
     for (int h = 0; h < 16; ++h) {  // unrolled so that acc[h] stays in registers
@@ -997,10 +1173,6 @@ __global__ void __launch_bounds__(256) ve_bwd_kernel(const uint16_t* __restrict_
         unpack8(*reinterpret_cast<const uint4*>(e + c), b);
 #pragma unroll
         for (int k = 0; k < 8; ++k) part += a[k] * b[k];
-        if (ok) {
-#pragma unroll
-          for (int k = 0; k < 8; ++k) unsafeAtomicAdd(dt + c + k, 3.f * sig * a[k]);
-        }
       }
       const float sh = warp_sum(part);
       const float dl = ok ? 3.f * sig * (1.f - sig) * sh : 0.f;
@@ -1152,11 +1324,33 @@ hipError_t launch_embed_fwd(const int32_t* tok, const uint16_t* wte, float* x, i
   return hipGetLastError();
 }
 
-hipError_t launch_embed_bwd(const int32_t* tok, const float* dx, float* dwte, long N, int d, int V,
-                            hipStream_t s) {
-  hipLaunchKernelGGL(embed_bwd_kernel, dim3(grid_for(N * (d / 4), 256)), dim3(256), 0, s, tok, dx,
-                     dwte, N, d, V);
+namespace {
+template <class Src>
+hipError_t launch_scatter(const Src& src, const int32_t* idx, long N, int V, int W, float* out, int accumulate,
+                          const ScatterWs& ws, hipStream_t s) {
+  if (N <= 0) return accumulate ? hipSuccess : launch_fill_u32(out, 0, (long)V * W, s);
+  if (W % 4 != 0 || V >= (1 << 24)) return hipErrorInvalidValue;
+  const int G = (int)((N + SC_G - 1) / SC_G);
+  if (G > kScatterMaxGroups) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(scatter_runs_kernel<Src>, dim3(G), dim3(SC_G), 0, s, src, idx, N, V, W / 4, ws.part,
+                     ws.run_ids, ws.nruns);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(scatter_merge_kernel, dim3((V + SC_R - 1) / SC_R), dim3(256), (size_t)SC_R * G * sizeof(int), s,
+                     static_cast<const float*>(ws.part), static_cast<const int32_t*>(ws.run_ids),
+                     static_cast<const int32_t*>(ws.nruns), G, V, W / 4, out, accumulate);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_embed_bwd(const int32_t* tok, const float* dx, float* dwte, long N, int d, int V, int accumulate,
+                            const ScatterWs& ws, hipStream_t s) {
+  return launch_scatter(ScatterSrcF32{dx, (long)d}, tok, N, V, d, dwte, accumulate, ws, s);
+}
+
+hipError_t launch_ve_table_bwd(const uint16_t* dqkv, long ld, const float* logits, int Hkv, const int32_t* tok,
+                               long N, int V, float* dtable, int accumulate, const ScatterWs& ws, hipStream_t s) {
+  return launch_scatter(ScatterSrcVe{dqkv, ld, logits, Hkv}, tok, N, V, Hkv * 128, dtable, accumulate, ws, s);
 }
 
 hipError_t launch_rmsnorm_fwd(const float* x, uint16_t* xn, float* rstd, long N, int d,
@@ -1391,10 +1585,11 @@ hipError_t launch_ve_fwd(uint16_t* qkv, const uint16_t* xn, const int32_t* tok, 
 
 hipError_t launch_ve_bwd(const uint16_t* dqkv, const uint16_t* xn, const int32_t* tok, const uint16_t* table,
                          const uint16_t* gate, const float* logits, float* dtable, float* dlogit, float* partials,
-                         float* dgate, float* dxn, long N, int d, int Hkv, int V, int accumulate, hipStream_t s) {
+                         float* dgate, float* dxn, long N, int d, int Hkv, int V, int accumulate,
+                         const ScatterWs& ws, hipStream_t s) {
   if (Hkv > 16) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(ve_bwd_kernel, dim3(kVeBlocks), dim3(256), 0, s, dqkv, xn, tok, table, logits, dtable, dlogit,
-                     partials, N, d, Hkv, V);
+  hipLaunchKernelGGL(ve_bwd_kernel, dim3(kVeBlocks), dim3(256), 0, s, dqkv, xn, tok, table, logits, dlogit, partials,
+                     N, d, Hkv, V);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n = Hkv * VE_CH;
@@ -1404,7 +1599,10 @@ hipError_t launch_ve_bwd(const uint16_t* dqkv, const uint16_t* xn, const int32_t
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(ve_dxn_kernel, dim3((unsigned)((N * VE_CH + 255) / 256)), dim3(256), 0, s, dxn,
                      static_cast<const float*>(dlogit), gate, N, d, Hkv);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long dkv = (long)Hkv * 128;
+  return launch_ve_table_bwd(dqkv + d + dkv, d + 2 * dkv, logits, Hkv, tok, N, V, dtable, accumulate, ws, s);
 }
 
 hipError_t launch_adamw_range(float* w, uint16_t* wb, const float* g, float* m, float* v, long n, float lr,

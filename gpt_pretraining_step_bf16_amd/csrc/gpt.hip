@@ -133,6 +133,7 @@ struct FwdPlan {
   size_t layer_bytes = 0;
   size_t x = 0, xnf = 0, rstdf = 0, dx = 0, dxb = 0, dxn = 0, du = 0, dO = 0, delta = 0, dqkv = 0;
   size_t logits = 0, loss_rows = 0, part = 0;
+  size_t sc_ids = 0, sc_nruns = 0;  // run tables of the ordered embedding scatter (partials in du)
   // residual scalars / backout (0 when the model has none)
   size_t x0 = 0, dx0 = 0, red = 0, xprev = 0, xbo = 0, dback = 0;
   size_t xe = 0, sa = 0, sred = 0;  // smear: embedding output, gate logits, partials
@@ -218,7 +219,8 @@ FwdPlan plan_fwd(const gpt_model& m, int B, int T) {
   p.dx = c.take(N * d * 4);
   p.dxb = c.take(N * d * 2);
   p.dxn = c.take(N * d * 4);
-  p.du = c.take(N * F * 2);
+  // du also holds the partial rows of the ordered embedding scatters (free by then).
+  p.du = c.take(std::max<size_t>((size_t)N * F * 2, scatter_part_bytes(N, d)));
   p.dO = c.take(N * d * 2);
   p.delta = c.take(N * H * 4);
   p.dqkv = c.take(N * Q * 2);
@@ -226,6 +228,8 @@ FwdPlan plan_fwd(const gpt_model& m, int B, int T) {
   p.nc = std::min<long>(N, cap_rows);
   p.logits = c.take((size_t)p.nc * V * 2);
   p.loss_rows = c.take(N * 4);
+  p.sc_ids = c.take(scatter_ids_bytes(N));
+  p.sc_nruns = c.take((size_t)scatter_groups(N) * 4);
   if (m.off_rl >= 0 || m.off_bl >= 0) {
     p.x0 = c.take(N * d * 4);
     p.dx0 = c.take(N * d * 4);
@@ -683,6 +687,7 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
   if (!m || !pbf || !tokens || !targets || !loss || !grads) return GPT_EINVAL;
   if (batch < 1 || seq < 1) return GPT_EINVAL;
   if (seq > m->max_seq) return GPT_ESHAPE;
+  if ((long)batch * seq > (long)kScatterMaxGroups * 256) return GPT_ESHAPE;
   if (accumulate != 0 && accumulate != 1) return GPT_EINVAL;
   const FwdPlan p = plan_fwd(*m, batch, seq);
   if (!workspace || workspace_bytes < p.total) return GPT_EWORKSPACE;
@@ -800,10 +805,9 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
   HIP_TRY(launch_loss_reduce(loss_rows, N, n_valid, loss, s));
   HIP_TRY(launch_rmsnorm_bwd(dxn, xnf, rstdf, dx, dxb, N, d, 0, s));
   if (pbl) HIP_TRY(launch_backout_bwd(dx, xbo, dback, Nd, red, grads + m->off_bl, accumulate, s));
-  // Value-embedding table gradients are scatter-adds, started from zero.
-  if (!accumulate)
-    for (int l = 0; l < L; ++l)
-      if (m->ve_off[l] >= 0) HIP_TRY(launch_fill_u32(grads + m->ve_off[l], 0, (long)V * m->dkv, s));
+  // Ordered scatter-adds of the embedding and value-embedding table gradients.
+  const ScatterWs scw{reinterpret_cast<float*>(ws + p.du), reinterpret_cast<int32_t*>(ws + p.sc_ids),
+                      reinterpret_cast<int32_t*>(ws + p.sc_nruns)};
   if (dx0) HIP_TRY(launch_fill_u32(dx0, 0, Nd, s));
 
   // ---- backward through the blocks
@@ -847,7 +851,7 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
       HIP_TRY(launch_ve_bwd(dqkv, xn1, tokens, pbf + m->ve_off[l], pbf + m->veg_off[l], ve_logits(l),
                             grads + m->ve_off[l], reinterpret_cast<float*>(ws + p.vedl),
                             reinterpret_cast<float*>(ws + p.vered), grads + m->veg_off[l], dxn, N, d, Hkv, V,
-                            accumulate, s));
+                            accumulate, scw, s));
     HIP_TRY(gemm_wgrad(dqkv, Q, xn1, d, Q, d, N, gqkv, accumulate, part, s));
     HIP_TRY(launch_rmsnorm_bwd(dxn, xn1, rstd1, dx, dxb, N, d, 1, s));
     // dx is now the gradient of the stream entering block l.
@@ -865,9 +869,7 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
                              grads + m->off_sg, grads + m->off_sl, accumulate, s));
     dx = dxn;
   }
-  float* gwte = grads + m->off_wte;
-  if (!accumulate) HIP_TRY(launch_fill_u32(gwte, 0, (long)V * d, s));
-  HIP_TRY(launch_embed_bwd(tokens, dx, gwte, N, d, V, s));
+  HIP_TRY(launch_embed_bwd(tokens, dx, grads + m->off_wte, N, d, V, accumulate, scw, s));
   return GPT_OK;
 }
 

@@ -11,8 +11,26 @@ hipError_t launch_f32_to_bf16(const float* in, uint16_t* out, long n, hipStream_
 hipError_t launch_rope_table(float* cs, int T, hipStream_t s);  // cs [T][64][2] (cos, sin)
 hipError_t launch_embed_fwd(const int32_t* tok, const uint16_t* wte, float* x, int* err, long N,
                             int d, int V, hipStream_t s);
-hipError_t launch_embed_bwd(const int32_t* tok, const float* dx, float* dwte, long N, int d, int V,
-                            hipStream_t s);
+// Scratch of the ordered row scatter-add (embedding and value-embedding table
+// gradients), for N positions of rows W wide: part >= scatter_part_bytes,
+// run_ids >= scatter_ids_bytes, nruns >= scatter_groups * 4 bytes.
+struct ScatterWs {
+  float* part;
+  int32_t* run_ids;
+  int32_t* nruns;
+};
+constexpr int kScatterMaxGroups = 2048;  // N <= 2048 * 256 positions per call
+inline long scatter_groups(long N) { return (N + 255) / 256; }
+inline size_t scatter_part_bytes(long N, long W) { return (size_t)scatter_groups(N) * 256 * W * 4; }
+inline size_t scatter_ids_bytes(long N) { return (size_t)scatter_groups(N) * 256 * 4; }
+// dwte (+)= per-token sums of the dx rows, in a fixed order; rows of absent
+// tokens are written as 0 (left unchanged with accumulate).
+hipError_t launch_embed_bwd(const int32_t* tok, const float* dx, float* dwte, long N, int d, int V, int accumulate,
+                            const ScatterWs& ws, hipStream_t s);
+// The value-embedding table gradient: dtable (+)= per-token sums of the rows
+// 3 sigmoid(logits[i][h]) dv[i][h*128 .. h*128+127] (dv bf16, row stride ld).
+hipError_t launch_ve_table_bwd(const uint16_t* dv, long ld, const float* logits, int Hkv, const int32_t* tok,
+                               long N, int V, float* dtable, int accumulate, const ScatterWs& ws, hipStream_t s);
 hipError_t launch_rmsnorm_fwd(const float* x, uint16_t* xn, float* rstd, long N, int d,
                               hipStream_t s);
 // dx (+)= rstd * (dxn - xn * mean(dxn * xn)); also writes dx_bf16.
@@ -101,11 +119,12 @@ int ve_partials_floats(int Hkv);
 // v of qkv += 3 sigmoid(gate . xn[0:32]) * table[token]; logits [N, Hkv]
 hipError_t launch_ve_fwd(uint16_t* qkv, const uint16_t* xn, const int32_t* tok, const uint16_t* table,
                          const uint16_t* gate, float* logits, long N, int d, int Hkv, int V, hipStream_t s);
-// dtable += (atomics), dgate (+)= (ordered sums), dxn[:, 0:32] += the gate's input gradient;
-// dlogit [N, Hkv] and partials are scratch
+// dtable (+)= (ordered scatter, ws), dgate (+)= (ordered sums), dxn[:, 0:32] += the gate's
+// input gradient; dlogit [N, Hkv] and partials are scratch
 hipError_t launch_ve_bwd(const uint16_t* dqkv, const uint16_t* xn, const int32_t* tok, const uint16_t* table,
                          const uint16_t* gate, const float* logits, float* dtable, float* dlogit, float* partials,
-                         float* dgate, float* dxn, long N, int d, int Hkv, int V, int accumulate, hipStream_t s);
+                         float* dgate, float* dxn, long N, int d, int Hkv, int V, int accumulate,
+                         const ScatterWs& ws, hipStream_t s);
 // AdamW on n (multiple of 4) contiguous elements, moments at m, v
 hipError_t launch_adamw_range(float* w, uint16_t* wb, const float* g, float* m, float* v, long n, float lr,
                               float b1, float b2, float eps, float wd, float bc1, float bc2, hipStream_t s);

@@ -165,8 +165,12 @@ size_t gpt_workspace_bytes(const gpt_model* m, int32_t batch, int32_t seq);
  *                [HADA] "Requisitos do ambiente de computação" does)
  *   workspace    device, >= gpt_workspace_bytes(m, batch, seq) bytes,
  *                256-byte aligned; holds activations and the sticky error flag
+ * batch * seq is at most 524288 tokens (GPT_ESHAPE otherwise).
  * Ids outside the vocabulary set GPT_ETOKEN in the workspace flag; such tokens
  * embed as zeros and such targets are ignored, so the call still completes.
+ * Every sum runs in a fixed order (no floating-point atomics), so repeated
+ * calls on the same inputs give the same bits; the embedding and
+ * value-embedding rows of ids absent from the batch get exact zeros.
  */
 gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* params_bf16, const int32_t* tokens,
                        const int32_t* targets, int32_t batch, int32_t seq, float* loss,
@@ -358,6 +362,15 @@ gpt_status gpt_op_newton_schulz(float* X, int32_t count, int32_t rows, int32_t c
 #define GPT_NS_STATIC_SCRATCH_BYTES (128u << 20)
 gpt_status gpt_op_newton_schulz_noalloc(float* X, int32_t count, int32_t rows, int32_t cols,
                                         const float* ns_coeffs, int32_t ns_steps, void* stream);
+
+/* Measurement probe, not part of the step: launches `blocks` workgroups of
+ * 4 waves, each issuing 4 independent chains of `iters` dense bf16 MFMAs
+ * (32 x 32 x 16) from registers, and writes the flops the launch performs to
+ * *flops (host). Timing the launch on `stream` gives the matrix-core rate the
+ * chip sustains (a measured peak beside the published one).
+ *   sink  device, >= blocks floats (one value per workgroup, keeps the work live)
+ * Returns GPT_EINVAL for blocks or iters < 1 or null pointers. */
+gpt_status gpt_probe_mfma_bf16(int32_t blocks, int32_t iters, float* sink, double* flops, void* stream);
 
 #ifdef __cplusplus
 }

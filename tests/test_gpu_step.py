@@ -373,6 +373,38 @@ def test_out_of_range_token_sets_flag():
     assert st.check() == 0
 
 
+@pytest.mark.parametrize("ve", [False, True])
+def test_embedding_gradients_are_bit_reproducible(ve):
+    """Repeated calls give the same bits for every gradient, the embedding and
+    value-embedding tables included (ordered scatter, no atomics), on a ragged
+    batch with a head-heavy token mix; rows of absent tokens are exact zeros,
+    also after an accumulating call."""
+    depth, vocab, seq, batch = 3, 2048, 200, 3
+    ve_layers = (0, 2) if ve else ()
+    w = syn.init_weights(depth, vocab, seed=0, ve_layers=ve_layers)
+    st = TrainState(depth, vocab, seq, batch, ve_layers=ve_layers)
+    st.load_weights(w)
+    tok, tgt = syn.split_tokens(syn.zipf_ids(batch, seq, vocab, seed=9))
+    tok_d, tgt_d = torch.from_numpy(tok).cuda(), torch.from_numpy(tgt).cuda()
+    outs = []
+    for _ in range(2):
+        st.fwd_bwd(tok_d, tgt_d)
+        torch.cuda.synchronize()
+        outs.append(st.grads.clone())
+    assert torch.equal(outs[0], outs[1])
+    st.fwd_bwd(tok_d, tgt_d, accumulate=True)
+    torch.cuda.synchronize()
+    g2 = st.to_host(st.grads)
+    g1 = st.to_host(outs[0])
+    absent = np.setdiff1d(np.arange(vocab), tok.ravel())
+    for name in ["wte"] + [f"h{l}.ve" for l in ve_layers]:
+        assert not np.any(g1[name][absent]) and not np.any(g2[name][absent])
+        present = np.unique(tok)
+        # (the second call adds its sums to the first's rows: fp32 reassociation)
+        np.testing.assert_allclose(g2[name][present], 2 * g1[name][present], rtol=1e-5,
+                                   atol=1e-6 * float(np.abs(g1[name]).max()))
+
+
 def test_deterministic_loss_and_causal_invariance():
     cfg = syn.CONFIGS["tiny"]
     st = TrainState(cfg["depth"], cfg["vocab"], cfg["seq"], 1)
