@@ -74,6 +74,46 @@ def test_gemm_layouts_bf16_out(a_kmajor, b_kmajor, N):
     assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-4)
 
 
+@pytest.mark.parametrize("a_kmajor,b_kmajor,mode", [(1, 1, "bf16"), (1, 1, "f32_acc"), (1, 1, "relu"),
+                                                     (1, 0, "f32"), (0, 0, "f32"), (0, 1, "f32")])
+def test_gemm_persistent_many_tiles(a_kmajor, b_kmajor, mode):
+    """More 256 x 256 tiles (9 x 9 x 4 = 324, ragged last row and column)
+    than workgroups (256), so workgroups walk several tiles, interior and
+    edge, and each tile's epilogue runs while the next tile's first k-blocks
+    load."""
+    M = N = 2056
+    K, batch = 320, 4
+    log(f"gemm persistent a_kmajor={a_kmajor} b_kmajor={b_kmajor} mode={mode}")
+    rng = np.random.default_rng(70 + 2 * a_kmajor + b_kmajor)
+    Ab, Af = _rand_bf16(rng, (batch, M, K))
+    Bb, Bf = _rand_bf16(rng, (batch, N, K))
+    A = dev(torch, Ab if a_kmajor else np.ascontiguousarray(Ab.transpose(0, 2, 1)))
+    B = dev(torch, Bb if b_kmajor else np.ascontiguousarray(Bb.transpose(0, 2, 1)))
+    lda, ldb = (K if a_kmajor else M), (K if b_kmajor else N)
+    ref = np.matmul(Af, Bf.transpose(0, 2, 1))
+    if mode in ("bf16", "relu"):
+        C = torch.full((batch, M, N), 0x7FC0, dtype=torch.int16, device="cuda")
+        out = binding.OUT_BF16 if mode == "bf16" else binding.OUT_RELU_BF16
+        binding.op_gemm(M, N, K, A, lda, a_kmajor, B, ldb, b_kmajor, C, N, out, batch=batch,
+                        stride_a=M * K, stride_b=N * K, stride_c=M * N)
+        torch.cuda.synchronize()
+        got = bits_to_f32(C.cpu().numpy()).reshape(batch, M, N)
+        want = ref if mode == "bf16" else np.maximum(ref, 0.0)
+        assert np.all(np.isfinite(got))
+        assert np.all(np.abs(got - want) <= 2.0 ** -8 * np.abs(ref) + 1e-4)
+    else:
+        base = rng.standard_normal((batch, M, N)).astype(np.float32) if mode == "f32_acc" else None
+        C = dev(torch, base) if base is not None else torch.full((batch, M, N), float("nan"), device="cuda")
+        out = binding.OUT_F32_ACC if mode == "f32_acc" else binding.OUT_F32
+        binding.op_gemm(M, N, K, A, lda, a_kmajor, B, ldb, b_kmajor, C, N, out, batch=batch,
+                        stride_a=M * K, stride_b=N * K, stride_c=M * N)
+        torch.cuda.synchronize()
+        got = C.cpu().numpy()
+        want = ref if base is None else base + ref
+        assert np.all(np.isfinite(got))
+        assert np.abs(got - want).max() / np.abs(ref).max() < 2e-6
+
+
 def test_gemm_epilogues():
     M, N, K = 300, 392, 256
     log(f"gemm epilogues M={M} N={N} K={K}")
