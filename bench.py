@@ -15,7 +15,9 @@ JSON line:
                F_tok = 6 (12 L d^2 + V d) + 6 L d T (causal attention once)
   roofline     the GEMM kernel family (the dominant kernel): algorithmic FLOPs
                of its launches / their summed durations, from HIP events
-               recorded around each launch on its stream during the timed steps
+               recorded around each launch on its stream during a second timed
+               pass of the same steps (the headline pass runs without them)
+  measured_peaks  the MFMA rate and copy bandwidth measured on this GPU
   cpu_baseline the CPU oracle on a bounded sample of the same workload
 
 Metric definitions follow the page's train/mfu and train/tok_per_sec
@@ -114,6 +116,51 @@ def gemm_traffic():
     return float(vals["traffic_bytes_per_launch"])
 
 
+def measured_peaks(torch):
+    """Second denominators measured on this GPU: the dense-bf16 MFMA rate the
+    chip sustains (the library's register-only MFMA probe, best of 3) and the
+    bandwidth of a plain 1 GiB device copy (best of 5)."""
+    from gpt_pretraining_step_bf16_amd import binding
+
+    blocks, iters = 2048, 20000
+    sink = torch.empty(blocks, dtype=torch.float32, device="cuda")
+    best = 0.0
+    for _ in range(3):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fl = binding.probe_mfma_bf16(blocks, iters, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, fl / (e0.elapsed_time(e1) / 1e3) / 1e12)
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    bw = 0.0
+    for _ in range(5):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        bw = max(bw, 2.0 * n * 4 / (e0.elapsed_time(e1) / 1e3) / 1e9)
+    del src, dst
+    return {"mfma_bf16_tflops": round(best, 1), "copy_gbs": round(bw, 1),
+            "how": "MFMA: register-only chains of 32x32x16 bf16 MFMAs over 2048 workgroups of 4 waves; "
+                   "copy: torch copy of 1 GiB fp32 (bytes read + written)"}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(cfg, weights, tok, tgt, normuon=False, windows=None):
     """Time the oracle on a bounded sample and scale it to one full step."""
     import oracle  # test infrastructure: used here only for the CPU baseline leg
@@ -149,6 +196,7 @@ def cpu_baseline(cfg, weights, tok, tgt, normuon=False, windows=None):
         "value": round(B * T / t_step, 3),
         "unit": "tokens/s",
         "cores": cores,
+        "cpu": cpu_model(),
         "kind": "oracle",
         "sample": (f"fp32 NumPy oracle: fwd+bwd of 1 of {B} sequences ({T} tokens, {t_seq:.2f} s), "
                    f"{'NorMuon' if normuon else 'Muon'} of 1 of {L} layers ({t_muon_layer:.2f} s) and AdamW of wte and lm_head "
@@ -172,6 +220,8 @@ def main():
     ap.add_argument("--normuon", action="store_true",
                     help="NorMuon variance reduction after Newton-Schulz (normuon_step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peak-probes", action="store_true",
+                    help="skip the measured MFMA-rate and copy-bandwidth probes")
     ap.add_argument("--no-isolated-timings", action="store_true",
                     help="skip the separate AdamW / Muon timings after the timed steps (keeps a "
                          "kernel trace to whole steps)")
@@ -239,60 +289,74 @@ def main():
     if st.check() != 0:
         raise RuntimeError("device reported an out-of-range token")
 
-    st.model.profile_enable(True)
-    torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    t_start.record()
-    for _ in range(args.steps):
-        step()
-    t_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    elapsed_ms = t_start.elapsed_time(t_end)
-    prof = {name: st.model.profile_read(cat) for name, cat in
-            (("gemm", 0), ("attn_fwd", 1), ("attn_bwd", 2), ("ns_gemm", 3))}
-    st.model.profile_enable(False)
+    def timed(nsteps):
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        e0.record()
+        for _ in range(nsteps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1), time.perf_counter() - w0
+
+    # Headline: the timed steps run with no per-launch events.
+    elapsed_ms, wall = timed(args.steps)
     loss = float(st.loss.item())
     if not np.isfinite(loss):
         raise RuntimeError(f"non-finite loss {loss}")
+    # Breakdown: a second timed pass of the same steps with HIP events around
+    # every launch of the GEMM, attention and Newton-Schulz kernels, recorded
+    # on the stream they run on.
+    prof_steps = max(1, min(args.steps, 5))
+    st.model.profile_enable(True)
+    prof_ms, _ = timed(prof_steps)
+    prof = {name: st.model.profile_read(cat) for name, cat in
+            (("gemm", 0), ("attn_fwd", 1), ("attn_bwd", 2), ("ns_gemm", 3))}
+    st.model.profile_enable(False)
 
     ms_step = elapsed_ms / args.steps
     tokens_per_s = accum * B * T * args.steps / (elapsed_ms / 1e3)
     dkv = 128 * st.model.kv_heads
     f_tok = flops_per_token(L, d, V, T, windows, dkv)
     mfu = tokens_per_s * f_tok / PEAK_BF16_FLOPS
-    mfma_work = (tokens_per_s * f_tok + ns_flops(L, d, dkv=dkv) / (ms_step / 1e3)) / PEAK_BF16_FLOPS
-    adamw_ms = block_ms = None
+    ns_alg = ns_flops(L, d, dkv=dkv)
+    mfma_work = (tokens_per_s * f_tok + ns_alg / (ms_step / 1e3)) / PEAK_BF16_FLOPS
+    adamw_ms = block_ms = fwd_bwd_ms = None
     if not args.no_isolated_timings:
-        # The AdamW call alone, timed after the steps (HIP events on the current stream).
-        a0 = torch.cuda.Event(enable_timing=True)
-        a1 = torch.cuda.Event(enable_timing=True)
-        a0.record()
-        for _ in range(5):
+        def iso(fn, n):
+            a0 = torch.cuda.Event(enable_timing=True)
+            a1 = torch.cuda.Event(enable_timing=True)
+            a0.record()
+            for _ in range(n):
+                fn()
+            a1.record()
+            torch.cuda.synchronize()
+            return a0.elapsed_time(a1) / n
+
+        def adamw_once():
             opt_step[0] += 1
             st.adamw(ADAMW["lr"], ADAMW["beta1"], ADAMW["beta2"], ADAMW["eps"], ADAMW["weight_decay"],
                      opt_step[0])
-        a1.record()
-        torch.cuda.synchronize()
-        adamw_ms = a0.elapsed_time(a1) / 5
-        # The block-matrix update alone (muon_step or normuon_step), timed the same way.
-        a0.record()
-        for _ in range(3):
-            block_update()
-        a1.record()
-        torch.cuda.synchronize()
-        block_ms = a0.elapsed_time(a1) / 3
+
+        # Each call alone, timed the same way (HIP events on the current stream).
+        adamw_ms = iso(adamw_once, 5)
+        block_ms = iso(block_update, 3)
+        fwd_bwd_ms = iso(lambda: st.fwd_bwd(tok_d, tgt_d), 3)
     for name, (ms, fl, n) in prof.items():
         tf = fl / (ms / 1e3) / 1e12 if ms > 0 else 0.0
-        print(f"[bench] {name:9s} {ms / args.steps:9.2f} ms/step  {n // max(args.steps, 1):5d} launches/step"
-              f"  {tf:8.1f} TFLOP/s", file=sys.stderr, flush=True)
+        extra = ""
+        if name == "ns_gemm" and ms > 0:
+            extra = f"  (executed; algorithmic {ns_alg * prof_steps / (ms / 1e3) / 1e12:.1f})"
+        print(f"[bench] {name:9s} {ms / prof_steps:9.2f} ms/step  {n // prof_steps:5d} launches/step"
+              f"  {tf:8.1f} TFLOP/s{extra}", file=sys.stderr, flush=True)
     g_ms, g_fl, g_n = prof["gemm"]
     # The head runs over token chunks of at most 1 GiB of bf16 logits (at least 256 rows).
     head_chunk = min(B * T, max(256, (1 << 30) // (2 * V)))
     g_bytes, g_launches = gemm_bytes_per_step(L, d, V, B * T, head_chunk, dkv)
     achieved = g_fl / (g_ms / 1e3) / 1e12 if g_ms > 0 else 0.0
+    peaks = None if args.no_peak_probes else measured_peaks(torch)
     roofline = {
         "kernel": "gemm_pp_kernel + gemm_bf16_kernel (projection, head and weight-gradient GEMMs of fwd+bwd)",
         "bound": "mfma",
@@ -303,9 +367,18 @@ def main():
         "traffic": gemm_traffic(),
         "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
         "algorithmic_bytes_per_launch": round(g_bytes / g_launches),
-        "launches_per_step": g_n // max(args.steps, 1),
-        "ms_per_step": round(g_ms / args.steps, 3),
+        "launches_per_step": g_n // prof_steps,
+        "ms_per_step": round(g_ms / prof_steps, 3),
+        "timing": f"HIP events around each launch over a second timed pass of {prof_steps} steps",
     }
+    if peaks:
+        roofline["frac_of_measured_peak"] = round(achieved / peaks["mfma_bf16_tflops"], 4)
+    ns_ms = prof["ns_gemm"][0] / prof_steps
+    amort = None
+    if fwd_bwd_ms is not None:
+        # The single-GPU accumulation mode: 8 microbatches per optimizer step.
+        t8 = fwd_bwd_ms + (block_ms + adamw_ms) / 8.0
+        amort = round(B * T / (t8 / 1e3) * f_tok / PEAK_BF16_FLOPS, 4)
     out = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -333,11 +406,21 @@ def main():
             "parallelism": "none (1 GPU)",
         },
         "mfu": round(mfu, 4),
+        "mfu_vs_measured_peak": None if not peaks else round(mfu * PEAK_BF16_FLOPS / 1e12
+                                                             / peaks["mfma_bf16_tflops"], 4),
         "mfma_work_utilisation": round(mfma_work, 4),
+        "mfu_amortised_8_microbatches": amort,
         "loss": round(loss, 5),
         "wall_s_timed": round(wall, 3),
+        "ms_per_step_with_launch_events": round(prof_ms / prof_steps, 3),
+        "fwd_bwd_ms": None if fwd_bwd_ms is None else round(fwd_bwd_ms, 3),
         "adamw_ms": None if adamw_ms is None else round(adamw_ms, 3),
         ("normuon_ms" if args.normuon else "muon_ms"): None if block_ms is None else round(block_ms, 3),
+        "newton_schulz": {"ms_per_step": round(ns_ms, 3),
+                          "algorithmic_tflops": round(ns_alg / (ns_ms / 1e3) / 1e12, 1) if ns_ms > 0 else None,
+                          "executed_tflops": round(prof["ns_gemm"][1] / prof_steps / (ns_ms / 1e3) / 1e12, 1)
+                          if ns_ms > 0 else None},
+        "measured_peaks": peaks,
         "roofline": roofline,
         "cpu_baseline": None,
     }

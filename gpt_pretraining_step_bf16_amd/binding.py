@@ -96,6 +96,7 @@ EXPORTS = {
     "gpt_op_ns_scratch_bytes": (C.c_size_t, [_I, _I, _I]),
     "gpt_op_newton_schulz": (C.c_int, [_P, _I, _I, _I, C.POINTER(C.c_float), _I, _P, _S, _P]),
     "gpt_op_newton_schulz_noalloc": (C.c_int, [_P, _I, _I, _I, C.POINTER(C.c_float), _I, _P]),
+    "gpt_probe_mfma_bf16": (C.c_int, [_I, _I, _P, C.POINTER(C.c_double), _P]),
     "gpt_profile_enable": (C.c_int, [_P, _I]),
     "gpt_profile_reset": (C.c_int, [_P]),
     "gpt_profile_read": (C.c_int, [_P, _I, C.POINTER(C.c_double), C.POINTER(C.c_double),
@@ -334,3 +335,11 @@ def op_newton_schulz(X, count, rows, cols, ns_coeffs, scratch, stream=None):
     st = lib().gpt_op_newton_schulz(_ptr(X), count, rows, cols, buf, steps, _ptr(scratch),
                                     scratch.numel() * scratch.element_size(), _stream(stream))
     _check(st, "gpt_op_newton_schulz")
+
+
+def probe_mfma_bf16(blocks, iters, sink, stream=None) -> float:
+    """Launch the MFMA issue-rate probe; returns the flops of the launch."""
+    fl = C.c_double(0.0)
+    st = lib().gpt_probe_mfma_bf16(int(blocks), int(iters), _ptr(sink), C.byref(fl), _stream(stream))
+    _check(st, "gpt_probe_mfma_bf16")
+    return float(fl.value)
