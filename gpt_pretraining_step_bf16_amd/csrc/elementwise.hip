@@ -682,15 +682,16 @@ __device__ __forceinline__ float sum_partials(const float* partials, int j, int 
   return s;
 }
 
+// (xl may be null: the lo half is then not formed.)
 __device__ __forceinline__ void split_store(float v, float* x32, uint16_t* xh, uint16_t* xl, long i) {
   const uint32_t h = f2bf(v);
   x32[i] = v;
   xh[i] = (uint16_t)h;
-  xl[i] = (uint16_t)f2bf(v - bf2f(h));
+  if (xl) xl[i] = (uint16_t)f2bf(v - bf2f(h));
 }
 
 // Four consecutive elements i .. i+3 (i % 4 == 0): fp32 and the bf16 hi/lo
-// split (hi = bf16(v), lo = bf16(v - hi)).
+// split (hi = bf16(v), lo = bf16(v - hi)); xl may be null (no lo half).
 __device__ __forceinline__ void split_store4(const float (&v)[4], float* x32, uint16_t* xh, uint16_t* xl, long i) {
   uint32_t h[4], l[4];
 #pragma unroll
@@ -700,7 +701,7 @@ __device__ __forceinline__ void split_store4(const float (&v)[4], float* x32, ui
   }
   *reinterpret_cast<float4*>(x32 + i) = make_float4(v[0], v[1], v[2], v[3]);
   *reinterpret_cast<uint2*>(xh + i) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-  *reinterpret_cast<uint2*>(xl + i) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+  if (xl) *reinterpret_cast<uint2*>(xl + i) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
 }
 
 // X = M / (||M||_F + 1e-7) in the tall orientation, as fp32 and bf16 hi/lo.
@@ -737,7 +738,7 @@ __global__ void muon_pack_kernel(const MuonGroup g, const float* __restrict__ mo
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = tile[4 * q + e][ry] * inv;
   }
-  split_store4(v, x32 + xoff, xh + xoff, xl + xoff, idx);
+  split_store4(v, x32 + xoff, xh + xoff, xl ? xl + xoff : nullptr, idx);
 }
 
 // W <- W - lr * sqrt(max(1, rows/cols)) * X in the stored orientation (rows =

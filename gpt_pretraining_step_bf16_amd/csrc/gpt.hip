@@ -365,7 +365,14 @@ NsPlan plan_ns(long count, long xr, long xc, size_t base) {
 // hi/lo output is formed as in the split iterations.
 constexpr int kNsPlainIters = 1;
 
-// Run ns_steps iterations on prepared X (x32, xh0, xl0 filled). Result in x32.
+// Where the preparation writes the lo half of X0: nowhere while the first
+// iteration takes the hi parts only (it is never read then).
+inline uint16_t* ns_x0_lo(char* ws, const NsPlan& p) {
+  return kNsPlainIters > 0 ? nullptr : reinterpret_cast<uint16_t*>(ws + p.xl0);
+}
+
+// Run ns_steps iterations on prepared X (x32, xh0 and, when read, xl0 filled).
+// Result in x32.
 hipError_t run_ns(char* ws, const NsPlan& p, int count, long xr, long xc, const float* coeffs,
                   int steps, hipStream_t s) {
   uint16_t* xh[2] = {reinterpret_cast<uint16_t*>(ws + p.xh0), reinterpret_cast<uint16_t*>(ws + p.xh1)};
@@ -954,7 +961,7 @@ static gpt_status muon_impl(gpt_model* m, float* params, uint16_t* params_bf16, 
     float* x32 = reinterpret_cast<float*>(ws + p.x32);
     HIP_TRY(launch_muon_momentum(g, grads, momentum, momentum_coef, part, p.nb, s));
     HIP_TRY(launch_muon_pack(g, momentum, part, p.nb, x32, reinterpret_cast<uint16_t*>(ws + p.xh0),
-                             reinterpret_cast<uint16_t*>(ws + p.xl0), s));
+                             ns_x0_lo(ws, p), s));
     HIP_TRY(run_ns(ws, p, g.count, g.x_rows, g.x_cols, ns_coeffs, ns_steps, s));
     if (state) {
       const long rows = (long)g.count * g.x_rows;
@@ -1121,8 +1128,7 @@ static gpt_status ns_op_run(float* X, int32_t count, int32_t rows, int32_t cols,
   float* x32 = reinterpret_cast<float*>(ws + p.x32);
   const long n = (long)rows * cols;
   HIP_TRY(hipMemcpyAsync(x32, X, (size_t)count * n * 4, hipMemcpyDeviceToDevice, s));
-  HIP_TRY(launch_ns_prepare(x32, reinterpret_cast<uint16_t*>(ws + p.xh0),
-                            reinterpret_cast<uint16_t*>(ws + p.xl0), count, n,
+  HIP_TRY(launch_ns_prepare(x32, reinterpret_cast<uint16_t*>(ws + p.xh0), ns_x0_lo(ws, p), count, n,
                             reinterpret_cast<float*>(ws + p.part), p.nb, s));
   HIP_TRY(run_ns(ws, p, count, rows, cols, ns_coeffs, ns_steps, s));
   HIP_TRY(hipMemcpyAsync(X, x32, (size_t)count * n * 4, hipMemcpyDeviceToDevice, s));
