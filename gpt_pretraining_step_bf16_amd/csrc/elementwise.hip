@@ -682,36 +682,26 @@ __device__ __forceinline__ float sum_partials(const float* partials, int j, int 
   return s;
 }
 
-// (xl may be null: the lo half is then not formed.)
-__device__ __forceinline__ void split_store(float v, float* x32, uint16_t* xh, uint16_t* xl, long i) {
-  const uint32_t h = f2bf(v);
+// X0 element i as fp32 and bf16.
+__device__ __forceinline__ void x0_store(float v, float* x32, uint16_t* xb, long i) {
   x32[i] = v;
-  xh[i] = (uint16_t)h;
-  if (xl) xl[i] = (uint16_t)f2bf(v - bf2f(h));
+  xb[i] = (uint16_t)f2bf(v);
 }
 
-// Four consecutive elements i .. i+3 (i % 4 == 0): fp32 and the bf16 hi/lo
-// split (hi = bf16(v), lo = bf16(v - hi)); xl may be null (no lo half).
-__device__ __forceinline__ void split_store4(const float (&v)[4], float* x32, uint16_t* xh, uint16_t* xl, long i) {
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    h[e] = f2bf(v[e]);
-    l[e] = f2bf(v[e] - bf2f(h[e]));
-  }
+// Four consecutive elements i .. i+3 (i % 4 == 0) of X0 as fp32 and bf16.
+__device__ __forceinline__ void x0_store4(const float (&v)[4], float* x32, uint16_t* xb, long i) {
   *reinterpret_cast<float4*>(x32 + i) = make_float4(v[0], v[1], v[2], v[3]);
-  *reinterpret_cast<uint2*>(xh + i) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-  if (xl) *reinterpret_cast<uint2*>(xl + i) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+  *reinterpret_cast<uint2*>(xb + i) = make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
 }
 
-// X = M / (||M||_F + 1e-7) in the tall orientation, as fp32 and bf16 hi/lo.
+// X = M / (||M||_F + 1e-7) in the tall orientation, as fp32 and bf16.
 // X is [x_rows, x_cols]. A matrix flagged in transposed_mask is stored wide,
 // as [x_cols, x_rows]; it is transposed through a 32x33 LDS tile.
 // Grid: (x_cols / 32, x_rows / 32, count); 256 threads, one float4 each:
 // thread t covers row t / 8 and columns 4 (t % 8) .. +3 of the 32x32 tile.
 __global__ void muon_pack_kernel(const MuonGroup g, const float* __restrict__ mom,
                                  const float* __restrict__ partials, int nb, float* __restrict__ x32,
-                                 uint16_t* __restrict__ xh, uint16_t* __restrict__ xl) {
+                                 uint16_t* __restrict__ xb) {
   __shared__ float tile[32][33];
   const int j = blockIdx.z;
   const long off = muon_mat_offset(g, j);
@@ -738,7 +728,7 @@ __global__ void muon_pack_kernel(const MuonGroup g, const float* __restrict__ mo
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = tile[4 * q + e][ry] * inv;
   }
-  split_store4(v, x32 + xoff, xh + xoff, xl ? xl + xoff : nullptr, idx);
+  x0_store4(v, x32 + xoff, xb + xoff, idx);
 }
 
 // W <- W - lr * sqrt(max(1, rows/cols)) * X in the stored orientation (rows =
@@ -1272,23 +1262,13 @@ __global__ void sumsq_kernel(const float* __restrict__ x, long n, float* __restr
   if (threadIdx.x == 0) partials[(long)j * gridDim.x + blockIdx.x] = red[0] + red[1] + red[2] + red[3];
 }
 
-__global__ void ns_normalize_kernel(float* __restrict__ x32, uint16_t* __restrict__ xh,
-                                    uint16_t* __restrict__ xl, long n, const float* __restrict__ partials,
-                                    int nb) {
+__global__ void ns_normalize_kernel(float* __restrict__ x32, uint16_t* __restrict__ xb, long n,
+                                    const float* __restrict__ partials, int nb) {
   const int j = blockIdx.y;
   const float inv = 1.f / (sqrtf(sum_partials(partials, j, nb)) + 1e-7f);
   const long base = (long)j * n;
   for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x)
-    split_store(x32[base + i] * inv, x32, xh, xl, base + i);
-}
-
-__global__ void split_hilo_kernel(const float* __restrict__ x32, uint16_t* __restrict__ xh,
-                                  uint16_t* __restrict__ xl, long n) {
-  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
-    const uint32_t h = f2bf(x32[i]);
-    xh[i] = (uint16_t)h;
-    xl[i] = (uint16_t)f2bf(x32[i] - bf2f(h));
-  }
+    x0_store(x32[base + i] * inv, x32, xb, base + i);
 }
 
 inline int grid_for(long work, int per_block, int cap = 16384) {
@@ -1431,11 +1411,9 @@ hipError_t launch_muon_momentum(const MuonGroup& g, const float* grads, float* m
 }
 
 hipError_t launch_muon_pack(const MuonGroup& g, const float* mom, const float* partials,
-                            int blocks_per_mat, float* x32, uint16_t* xh, uint16_t* xl,
-                            hipStream_t s) {
+                            int blocks_per_mat, float* x32, uint16_t* xb, hipStream_t s) {
   dim3 grid((unsigned)(g.x_cols / 32), (unsigned)(g.x_rows / 32), g.count);
-  hipLaunchKernelGGL(muon_pack_kernel, grid, dim3(256), 0, s, g, mom, partials, blocks_per_mat, x32, xh,
-                     xl);
+  hipLaunchKernelGGL(muon_pack_kernel, grid, dim3(256), 0, s, g, mom, partials, blocks_per_mat, x32, xb);
   return hipGetLastError();
 }
 
@@ -1477,18 +1455,13 @@ hipError_t launch_adamw(float* w, uint16_t* wb, const float* g, float* m, float*
   return hipGetLastError();
 }
 
-hipError_t launch_ns_prepare(float* x32, uint16_t* xh, uint16_t* xl, int count, long n,
-                             float* partials, int blocks_per_mat, hipStream_t s) {
+hipError_t launch_ns_prepare(float* x32, uint16_t* xb, int count, long n, float* partials,
+                             int blocks_per_mat, hipStream_t s) {
   hipLaunchKernelGGL(sumsq_kernel, dim3(blocks_per_mat, count), dim3(256), 0, s, x32, n, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ns_normalize_kernel, dim3(grid_for(n, 256, 1024), count), dim3(256), 0, s, x32, xh,
-                     xl, n, partials, blocks_per_mat);
-  return hipGetLastError();
-}
-
-hipError_t launch_split_hilo(const float* x32, uint16_t* xh, uint16_t* xl, long n, hipStream_t s) {
-  hipLaunchKernelGGL(split_hilo_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, x32, xh, xl, n);
+  hipLaunchKernelGGL(ns_normalize_kernel, dim3(grid_for(n, 256, 1024), count), dim3(256), 0, s, x32, xb, n,
+                     partials, blocks_per_mat);
   return hipGetLastError();
 }
 

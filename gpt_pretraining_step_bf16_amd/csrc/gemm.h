@@ -1,11 +1,12 @@
-// Host-side interface of the bf16 MFMA GEMM (gemm.hip, gemm_*.hip).
+// Host-side interface of the MFMA GEMM (gemm.hip, gemm_*.hip): bf16 operands,
+// or fp16 ones for the EPI_H_* epilogues.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA GEMM:  C[b](m, n) <- epilogue( sum_k A[b](m, k) * B[b](n, k) )
+// MFMA GEMM:  C[b](m, n) <- epilogue( sum_k A[b](m, k) * B[b](n, k) )
 // ---------------------------------------------------------------------------
 enum GemmEpilogue {
   EPI_F32 = 0,          // C f32 = alpha*acc
@@ -17,19 +18,23 @@ enum GemmEpilogue {
   EPI_SPLITK = 6,       // C f32 [split] = acc (partials, reduced later)
   EPI_HILO = 7,         // v = alpha*acc -> C bf16 hi(v), C2 bf16 lo(v)
   EPI_NS_POLY = 8,      // v = alpha*acc + beta*(D + D2) (D, D2 bf16 hi/lo) -> C hi, C2 lo
-  EPI_NS_UPDATE = 9,    // v = alpha*acc + beta*D (D f32) -> C3 f32 v, C hi, C2 lo
+  EPI_NS_UPDATE = 9,    // v = alpha*acc + beta*D (D f32) -> C3 f32 v, C f16 v
   EPI_RELU2_BF16 = 10,  // C bf16 = max(acc, 0)^2
+  // fp16 operands (v_mfma_f32_32x32x16_f16), fp32 accumulation:
+  EPI_H_GRAM = 11,      // C f16 = alpha*acc
+  EPI_H_NS_POLY = 12,   // v = alpha*acc + beta*D (D f16) -> C f16 v
+  EPI_H_NS_UPDATE = 13, // as EPI_NS_UPDATE
 };
 
 struct GemmArgs {
-  const uint16_t* a[3];  // per K-segment operand bases (bf16 bits); nseg segments are summed
+  const uint16_t* a[3];  // per K-segment operand bases (bf16 or fp16 bits); nseg segments are summed
   const uint16_t* b[3];
   int nseg;
   int M, N, K;
   long lda, ldb;         // leading dimensions (elements)
   long sa, sb;           // batch strides (elements)
   int a_kmajor, b_kmajor;
-  int sym;               // 1: C is symmetric (M == N; HILO / NS_POLY only): only tiles
+  int sym;               // 1: C is symmetric (M == N; HILO, NS_POLY, H_GRAM, H_NS_POLY): only tiles
                          //    tm <= tn are computed, off-diagonal ones also stored transposed
   void* c;
   long ldc, sc;

@@ -1,6 +1,9 @@
 // bf16 MFMA GEMM kernel for gfx950 (device code; instantiated per operand
 // layout in gemm_*.hip): every dense contraction of the step (QKV, O, MLP
 // and head projections forward and backward, weight gradients, Newton-Schulz).
+// The EPI_H_* instantiations (Newton-Schulz after its first iteration) take
+// fp16 operands through v_mfma_f32_32x32x16_f16, the same shape and rate;
+// the operand path (loads, LDS layout, fragment reads) is type-blind.
 //
 // Design
 //  * Macro tile 256 x 256, 256 threads = 4 wave64s in a 2 x 2 grid, each wave
@@ -31,7 +34,7 @@
 //    dealt round-robin over the 8 XCDs), then grouped 4 tile-rows at a time so
 //    an XCD's tiles share A rows and B columns in its L2.
 //  * Up to three K segments with their own operand bases are summed into one
-//    accumulator: Newton-Schulz uses it for hi/lo split products.
+//    accumulator (a sum of products in one pass, e.g. hi/lo split operands).
 #pragma once
 
 #include <type_traits>
@@ -257,7 +260,24 @@ __device__ __forceinline__ void load_bf16x4(const void* p, float* v) {
 template <int E>
 constexpr bool epi_reads() {
   return E == EPI_F32_ACC || E == EPI_RESID_BF16 || E == EPI_DRELU2_BF16 || E == EPI_NS_POLY ||
-         E == EPI_NS_UPDATE;
+         E == EPI_NS_UPDATE || E == EPI_H_NS_POLY || E == EPI_H_NS_UPDATE;
+}
+
+// Whether the operands are fp16 (the EPI_H_* epilogues) rather than bf16.
+template <int E>
+constexpr bool f16_operands() {
+  return E == EPI_H_GRAM || E == EPI_H_NS_POLY || E == EPI_H_NS_UPDATE;
+}
+
+// One 32 x 32 x 16 MFMA of the instantiation's operand type (the fragments
+// hold the operands' 16-bit patterns either way).
+template <int E>
+__device__ __forceinline__ f32x16 mfma16(const bf16x8& b, const bf16x8& a, const f32x16& c) {
+  if constexpr (f16_operands<E>())
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, b), __builtin_bit_cast(f16x8, a), c,
+                                                  0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c, 0, 0, 0);
 }
 
 // Per-lane output pointers of one wave's tile: element (row m, column n) of
@@ -265,7 +285,7 @@ constexpr bool epi_reads() {
 // n = nb + 32 j + 8 g + r (mb, nb the lane's first row and column).
 struct EpiPtrs {
   float* cf;            // C as fp32 (F32, F32_ACC, SPLITK)
-  uint16_t* cb;         // C as bf16
+  uint16_t* cb;         // C as bf16 (fp16 for EPI_NS_UPDATE and EPI_H_*)
   uint16_t* c2;         // lo half of hi/lo outputs
   float* c3;            // fp32 X (NS_UPDATE; D layout)
   const uint16_t* db;   // D as bf16
@@ -298,7 +318,11 @@ __device__ __forceinline__ uint4 epi_load(const EpiPtrs& e, int i, int j, int g)
     const uint2 h = *reinterpret_cast<const uint2*>(e.db + dof);
     const uint2 l = *reinterpret_cast<const uint2*>(e.d2 + dof);
     r = make_uint4(h.x, h.y, l.x, l.y);
-  } else if constexpr (E == EPI_NS_UPDATE) {
+  } else if constexpr (E == EPI_H_NS_POLY) {
+    const uint2 u = *reinterpret_cast<const uint2*>(e.db + dof);
+    r.x = u.x;
+    r.y = u.y;
+  } else if constexpr (E == EPI_NS_UPDATE || E == EPI_H_NS_UPDATE) {
     r = *reinterpret_cast<const uint4*>(e.df + dof);
   }
   return r;
@@ -314,6 +338,20 @@ __device__ __forceinline__ void store_hilo4_t(const EpiPtrs& e, int i, int j, in
     const uint32_t h = f2bf(w[r]);
     e.cbt[o] = (uint16_t)h;
     e.c2t[o] = (uint16_t)f2bf(w[r] - bf2f(h));
+  }
+}
+
+__device__ __forceinline__ void store_h4(void* p, const float* w) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_h2(w[0], w[1]), pack_h2(w[2], w[3]));
+}
+
+// Transposed fp16 store of group (i, j, g) of a symmetric output (as
+// store_hilo4_t, one output).
+__device__ __forceinline__ void store_h4_t(const EpiPtrs& e, int i, int j, int g, const float* w) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const long o = (long)(32 * j + 8 * g + r) * e.ldc + 32 * i;
+    e.cbt[o] = __builtin_bit_cast(uint16_t, (_Float16)w[r]);
   }
 }
 
@@ -358,12 +396,21 @@ __device__ __forceinline__ void epi4(const EpiPtrs& e, int i, int j, int g, cons
     for (int r = 0; r < 4; ++r) w[r] = e.alpha * v[r] + e.beta * (h[r] + l[r]);
     store_hilo4(e.cb + co, e.c2 + co, w);
     if (e.tr) store_hilo4_t(e, i, j, g, w);
-  } else if constexpr (E == EPI_NS_UPDATE) {
+  } else if constexpr (E == EPI_NS_UPDATE || E == EPI_H_NS_UPDATE) {
     const float4 x = __builtin_bit_cast(float4, in);
     float w[4] = {e.alpha * v[0] + e.beta * x.x, e.alpha * v[1] + e.beta * x.y,
                   e.alpha * v[2] + e.beta * x.z, e.alpha * v[3] + e.beta * x.w};
     *reinterpret_cast<float4*>(e.c3 + dof) = make_float4(w[0], w[1], w[2], w[3]);
-    store_hilo4(e.cb + co, e.c2 + co, w);
+    store_h4(e.cb + co, w);
+  } else if constexpr (E == EPI_H_GRAM) {
+    const float w[4] = {e.alpha * v[0], e.alpha * v[1], e.alpha * v[2], e.alpha * v[3]};
+    store_h4(e.cb + co, w);
+    if (e.tr) store_h4_t(e, i, j, g, w);
+  } else if constexpr (E == EPI_H_NS_POLY) {
+    const float w[4] = {e.alpha * v[0] + e.beta * h_lo(in.x), e.alpha * v[1] + e.beta * h_hi(in.x),
+                        e.alpha * v[2] + e.beta * h_lo(in.y), e.alpha * v[3] + e.beta * h_hi(in.y)};
+    store_h4(e.cb + co, w);
+    if (e.tr) store_h4_t(e, i, j, g, w);
   }
 }
 
@@ -412,7 +459,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const f32x16 (&acc
     };
     // 16-byte inputs (fp32 or hi/lo pairs) load block by block; 8-byte ones
     // also prefetch the next block (registers allow it).
-    constexpr bool WIDE = E == EPI_F32_ACC || E == EPI_NS_POLY || E == EPI_NS_UPDATE;
+    constexpr bool WIDE = E == EPI_F32_ACC || E == EPI_NS_POLY || E == EPI_NS_UPDATE || E == EPI_H_NS_UPDATE;
     if constexpr (epi_reads<E>()) load_block(0, in[0]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -517,7 +564,7 @@ template <int E>
 constexpr bool lds_epi_io() {
   // (Plain fp32 outputs and split-K partials measured no faster staged: their
   // GEMMs have long K, and the register path already writes 16 bytes a lane.)
-  return E == EPI_F32_ACC || E == EPI_DRELU2_BF16 || E == EPI_NS_UPDATE;
+  return E == EPI_F32_ACC || E == EPI_DRELU2_BF16 || E == EPI_NS_UPDATE || E == EPI_H_NS_UPDATE;
 }
 constexpr int STG_RS_F = 272;  // padded row stride of an fp32 staging block (bytes)
 static_assert(8 * 32 * STG_RS_F <= NST * STAGE_BYTES, "staging regions must fit in the ring");
@@ -540,6 +587,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void* p) {
 }
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// A buffer store of more than 8 bytes reads its data VGPRs after it issues;
+// a VALU write to those VGPRs right behind it can reach some lanes first (fp32
+// rows were stored holding the fp16 bits that the following conversion wrote
+// into the same registers). The compiler inserts the wait states only for
+// stores whose soffset is not a register, and the staged epilogues pass the
+// row offset in an SGPR, so a store whose registers a VALU may reuse is
+// fenced off alone and followed by the wait written out here.
+__device__ __forceinline__ void wide_store_wait() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 1");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 template <int E, bool FULL>
 __device__ __forceinline__ void store_tile_lds_io(const GemmArgs& p, const f32x16 (&acc)[4][2], int bi,
@@ -611,16 +671,15 @@ __device__ __forceinline__ void store_tile_lds_io(const GemmArgs& p, const f32x1
       }
       wave_lds_order();
     }
-  } else if constexpr (E == EPI_NS_UPDATE) {
-    // v = alpha acc + beta D; fp32 v to C3 (stride ldd), bf16 hi/lo of v to C
-    // and C2 (stride ldc). fp32 rows: 16 lanes per 256-byte segment.
+  } else if constexpr (E == EPI_NS_UPDATE || E == EPI_H_NS_UPDATE) {
+    // v = alpha acc + beta D; fp32 v to C3 (stride ldd), fp16 v to C (stride
+    // ldc). fp32 rows: 16 lanes per 256-byte segment.
     constexpr int RS = STG_RS_F;
     const int ldd = (int)p.ldd;
     const long dbase = (long)bi * p.sd + (long)(m0 + row_off) * p.ldd + (n0 + col_off);
     const auto drs = wave_rsrc(reinterpret_cast<const float*>(p.d) + dbase);
     const auto x3 = wave_rsrc(reinterpret_cast<float*>(p.c3) + dbase);
     const auto hrs = wave_rsrc(reinterpret_cast<uint16_t*>(p.c) + cbase);
-    const auto lrs = wave_rsrc(reinterpret_cast<uint16_t*>(p.c2) + cbase);
     const float alpha = p.alpha, beta = p.beta;
     const int rq = lane >> 4, cc = lane & 15;
     const int dvo = (rq * ldd + cc * 4) * 4, hvo = (rq * ldc + cc * 4) * 2;
@@ -659,14 +718,12 @@ __device__ __forceinline__ void store_tile_lds_io(const GemmArgs& p, const f32x1
         const int row = 32 * i + 4 * q + rq;
         const float4 w = *reinterpret_cast<const float4*>(wreg + (4 * q + rq) * RS + cc * 16);
         if (ok(row)) {
+          const u32x2_t h = u32x2_t{pack_h2(w.x, w.y), pack_h2(w.z, w.w)};
+          __builtin_amdgcn_sched_barrier(0);
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, w), x3, dvo,
                                                  (32 * i + 4 * q) * ldd * 4, 0);
-          const uint32_t h0 = f2bf(w.x), h1 = f2bf(w.y), h2 = f2bf(w.z), h3 = f2bf(w.w);
-          const uint32_t l0 = f2bf(w.x - bf2f(h0)), l1 = f2bf(w.y - bf2f(h1)), l2 = f2bf(w.z - bf2f(h2)),
-                         l3 = f2bf(w.w - bf2f(h3));
-          const int so = (32 * i + 4 * q) * ldc * 2;
-          __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{h0 | (h1 << 16), h2 | (h3 << 16)}, hrs, hvo, so, 0);
-          __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{l0 | (l1 << 16), l2 | (l3 << 16)}, lrs, hvo, so, 0);
+          wide_store_wait();
+          __builtin_amdgcn_raw_buffer_store_b64(h, hrs, hvo, (32 * i + 4 * q) * ldc * 2, 0);
         }
       }
       wave_lds_order();
@@ -835,7 +892,7 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_bf16_kernel(const GemmArgs p) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+        acc[i][j] = mfma16<EPI>(f.b[j], f.a[i], acc[i][j]);
   };
 
   // Interleave a k-step's 16 MFMAs with the NR LDS reads of the next
@@ -931,8 +988,7 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_bf16_kernel(const GemmArgs p) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int t = 2 * q + u;
-        acc[t >> 2][t & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1.b[t & 3], f1.a[t >> 2],
-                                                                     acc[t >> 2][t & 3], 0, 0, 0);
+        acc[t >> 2][t & 3] = mfma16<EPI>(f1.b[t & 3], f1.a[t >> 2], acc[t >> 2][t & 3]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1073,7 +1129,7 @@ __global__ void __launch_bounds__(PP_THR, 1) gemm_pp_kernel(const GemmArgs p) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][j], fa[ks][i], acc[i][j], 0, 0, 0);
+        acc[i][j] = mfma16<EPI>(fb[ks][j], fa[ks][i], acc[i][j]);
   };
   auto compute = [&]() {
     compute_ks(0);
@@ -1133,17 +1189,14 @@ __global__ void __launch_bounds__(PP_THR, 1) gemm_pp_kernel(const GemmArgs p) {
       else
         store_tile_lds<EPI, false>(p, acc, bi, m0, n0, 128 * grp, 64 * w4, lane, wave, smem);
     } else {
-      // Edge tiles of the read-modify-write epilogues keep the register path:
-      // the staged version's edge variant gave wrong Newton-Schulz updates on
-      // a 384 x 128 batch (cause not found), while interior tiles agree.
-      bool staged = false;
       if constexpr (lds_epi_io<EPI>()) {
-        if (interior) {
+        if (interior)
           store_tile_lds_io<EPI, true>(p, acc, bi, m0, n0, 128 * grp, 64 * w4, lane, wave, smem);
-          staged = true;
-        }
+        else
+          store_tile_lds_io<EPI, false>(p, acc, bi, m0, n0, 128 * grp, 64 * w4, lane, wave, smem);
+      } else {
+        store_tile<EPI, 2>(p, acc, bi, si, m0, n0, 128 * grp, 64 * w4, lane);
       }
-      if (!staged) store_tile<EPI, 2>(p, acc, bi, si, m0, n0, 128 * grp, 64 * w4, lane);
     }
     const int lin_next = lin + gridDim.x;
     if (lin_next >= total) break;

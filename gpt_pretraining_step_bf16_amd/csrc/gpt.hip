@@ -328,11 +328,15 @@ constexpr int kMaxMuonGroups = 3;
 
 // Newton-Schulz buffers for `count` matrices of xr x xc.
 struct NsPlan {
-  size_t x32 = 0, xh0 = 0, xl0 = 0, xh1 = 0, xl1 = 0, ah = 0, al = 0, bh = 0, bl = 0, part = 0;
+  size_t x32 = 0, xb = 0, xh0 = 0, xh1 = 0, ah = 0, al = 0, bh = 0, bl = 0, part = 0;
   size_t total = 0;
   int nb = 0;
 };
 
+// Newton-Schulz buffers: x32 the fp32 X, xb the bf16 X0 the preparation
+// writes, xh0 / xh1 the fp16 X of the later iterations (ping-pong), ah / al
+// and bh / bl the first iteration's A and B as bf16 hi / lo (ah and bh hold
+// the fp16 A and B afterwards), part the normalisation partial sums.
 NsPlan plan_ns(long count, long xr, long xc, size_t base) {
   NsPlan p;
   Carve c;
@@ -340,10 +344,9 @@ NsPlan plan_ns(long count, long xr, long xc, size_t base) {
   const long nx = count * xr * xc;
   const long na = count * xc * xc;
   p.x32 = c.take(nx * 4);
+  p.xb = c.take(nx * 2);
   p.xh0 = c.take(nx * 2);
-  p.xl0 = c.take(nx * 2);
   p.xh1 = c.take(nx * 2);
-  p.xl1 = c.take(nx * 2);
   p.ah = c.take(na * 2);
   p.al = c.take(na * 2);
   p.bh = c.take(na * 2);
@@ -354,60 +357,50 @@ NsPlan plan_ns(long count, long xr, long xc, size_t base) {
   return p;
 }
 
-// Iterations whose products take the hi parts only (one bf16 MFMA product per
-// matrix product). The first iteration's rounding does not survive the rest:
-// with it plain and the others split, the result stays within 5e-5 (Gaussian)
-// to 2e-3 (rank 1 and 2) relative L2 of the fp64 iteration at the block-matrix
-// shapes (at most 8e-3 on small rank-1 matrices), against 3e-5 to 2e-3 with
-// every iteration split. A plain second iteration as well leaves 1e-2 to 6e-2
-// on small well-conditioned matrices, whose singular values reach the region
-// the later polynomials amplify within two steps. Every fp32 master value and
-// hi/lo output is formed as in the split iterations.
-constexpr int kNsPlainIters = 1;
-
-// Where the preparation writes the lo half of X0: nowhere while the first
-// iteration takes the hi parts only (it is never read then).
-inline uint16_t* ns_x0_lo(char* ws, const NsPlan& p) {
-  return kNsPlainIters > 0 ? nullptr : reinterpret_cast<uint16_t*>(ws + p.xl0);
-}
-
-// Run ns_steps iterations on prepared X (x32, xh0 and, when read, xl0 filled).
-// Result in x32.
+// Operand precision of the iterations. Every product accumulates in fp32 and
+// X stays in fp32 between iterations; only the MFMA operands are rounded.
+// The first iteration takes bf16 operands: X0 = G / ||G||_F has entries of
+// order 1 / sqrt(rows * cols), where fp16 would be subnormal for the larger
+// matrices; its A is kept as bf16 hi + lo for the linear term of B. The
+// others take fp16 operands (same MFMA rate, 3 more mantissa bits), with A, B
+// and X stored in fp16. A CPU emulation of exactly these roundings against the
+// fp64 iteration gives a relative L2 error of 1.7e-3 to 2.3e-3 for Gaussian,
+// 4e-4 for 1/k-spectrum and 7e-4 to 1e-3 for rank-1-plus-noise matrices at
+// the block shapes (1280 x 1280, 5120 x 1280, 1280 x 5120), and at most
+// 7.7e-3 on a small Gaussian 384 x 128; bf16 operands throughout give 1.5e-2
+// to 2.4e-2 on the same Gaussian matrices.
+//
+// Run ns_steps iterations on prepared X (x32 and xb filled). Result in x32.
 hipError_t run_ns(char* ws, const NsPlan& p, int count, long xr, long xc, const float* coeffs,
                   int steps, hipStream_t s) {
+  const uint16_t* xb = reinterpret_cast<const uint16_t*>(ws + p.xb);
   uint16_t* xh[2] = {reinterpret_cast<uint16_t*>(ws + p.xh0), reinterpret_cast<uint16_t*>(ws + p.xh1)};
-  uint16_t* xl[2] = {reinterpret_cast<uint16_t*>(ws + p.xl0), reinterpret_cast<uint16_t*>(ws + p.xl1)};
   uint16_t* ah = reinterpret_cast<uint16_t*>(ws + p.ah);
   uint16_t* al = reinterpret_cast<uint16_t*>(ws + p.al);
   uint16_t* bh = reinterpret_cast<uint16_t*>(ws + p.bh);
   uint16_t* bl = reinterpret_cast<uint16_t*>(ws + p.bl);
   float* x32 = reinterpret_cast<float*>(ws + p.x32);
-  int cur = 0;
+  int cur = 0;  // xh[cur] holds X in fp16 from the second iteration on
   for (int it = 0; it < steps; ++it) {
     const float a = coeffs[3 * it], b = coeffs[3 * it + 1], c = coeffs[3 * it + 2];
-    const int nseg = it < kNsPlainIters ? 1 : 3;
-    // A = X^T X (split iterations: Xh^T Xh + Xh^T Xl + Xl^T Xh).
+    const bool first = it == 0;
+    const uint16_t* x = first ? xb : xh[cur];
+    // A = X^T X
     GemmArgs g;
     gemm_args_init(g);
-    g.nseg = nseg;
-    g.a[0] = xh[cur]; g.b[0] = xh[cur];
-    g.a[1] = xh[cur]; g.b[1] = xl[cur];
-    g.a[2] = xl[cur]; g.b[2] = xh[cur];
+    g.a[0] = x; g.b[0] = x;
     g.M = (int)xc; g.N = (int)xc; g.K = (int)xr;
     g.lda = xc; g.ldb = xc; g.sa = xr * xc; g.sb = xr * xc;
     g.a_kmajor = 0; g.b_kmajor = 0;
     g.c = ah; g.c2 = al; g.ldc = xc; g.sc = xc * xc;
     g.batch = count;
     g.sym = 1;  // A is symmetric: upper-triangle tiles only, mirrored on store
-    g.epi = EPI_HILO;
+    g.epi = first ? EPI_HILO : EPI_H_GRAM;
     hipError_t e = launch_gemm_prof(g, s, PROF_NS);
     if (e != hipSuccess) return e;
     // B = b A + c A A (A symmetric, so A A = A A^T).
     gemm_args_init(g);
-    g.nseg = nseg;
     g.a[0] = ah; g.b[0] = ah;
-    g.a[1] = ah; g.b[1] = al;
-    g.a[2] = al; g.b[2] = ah;
     g.M = (int)xc; g.N = (int)xc; g.K = (int)xc;
     g.lda = xc; g.ldb = xc; g.sa = xc * xc; g.sb = xc * xc;
     g.a_kmajor = 1; g.b_kmajor = 1;
@@ -416,26 +409,25 @@ hipError_t run_ns(char* ws, const NsPlan& p, int count, long xr, long xc, const 
     g.alpha = c; g.beta = b;
     g.batch = count;
     g.sym = 1;  // B = bA + cA^2 is symmetric too
-    g.epi = EPI_NS_POLY;
+    g.epi = first ? EPI_NS_POLY : EPI_H_NS_POLY;
     e = launch_gemm_prof(g, s, PROF_NS);
     if (e != hipSuccess) return e;
-    // X = a X + X B (B symmetric, so X B = X B^T).
+    // X = a X + X B (B symmetric, so X B = X B^T); the fp16 copy of the new X
+    // goes to the other buffer.
+    uint16_t* xnext = first ? xh[cur] : xh[cur ^ 1];
     gemm_args_init(g);
-    g.nseg = nseg;
-    g.a[0] = xh[cur]; g.b[0] = bh;
-    g.a[1] = xh[cur]; g.b[1] = bl;
-    g.a[2] = xl[cur]; g.b[2] = bh;
+    g.a[0] = x; g.b[0] = bh;
     g.M = (int)xr; g.N = (int)xc; g.K = (int)xc;
     g.lda = xc; g.ldb = xc; g.sa = xr * xc; g.sb = xc * xc;
     g.a_kmajor = 1; g.b_kmajor = 1;
-    g.c = xh[cur ^ 1]; g.c2 = xl[cur ^ 1]; g.c3 = x32; g.ldc = xc; g.sc = xr * xc;
+    g.c = xnext; g.c3 = x32; g.ldc = xc; g.sc = xr * xc;
     g.d = x32; g.ldd = xc; g.sd = xr * xc;
     g.alpha = 1.f; g.beta = a;
     g.batch = count;
-    g.epi = EPI_NS_UPDATE;
+    g.epi = first ? EPI_NS_UPDATE : EPI_H_NS_UPDATE;
     e = launch_gemm_prof(g, s, PROF_NS);
     if (e != hipSuccess) return e;
-    cur ^= 1;
+    if (!first) cur ^= 1;
   }
   return hipSuccess;
 }
@@ -960,8 +952,7 @@ static gpt_status muon_impl(gpt_model* m, float* params, uint16_t* params_bf16, 
     float* part = reinterpret_cast<float*>(ws + p.part);
     float* x32 = reinterpret_cast<float*>(ws + p.x32);
     HIP_TRY(launch_muon_momentum(g, grads, momentum, momentum_coef, part, p.nb, s));
-    HIP_TRY(launch_muon_pack(g, momentum, part, p.nb, x32, reinterpret_cast<uint16_t*>(ws + p.xh0),
-                             ns_x0_lo(ws, p), s));
+    HIP_TRY(launch_muon_pack(g, momentum, part, p.nb, x32, reinterpret_cast<uint16_t*>(ws + p.xb), s));
     HIP_TRY(run_ns(ws, p, g.count, g.x_rows, g.x_cols, ns_coeffs, ns_steps, s));
     if (state) {
       const long rows = (long)g.count * g.x_rows;
@@ -1128,7 +1119,7 @@ static gpt_status ns_op_run(float* X, int32_t count, int32_t rows, int32_t cols,
   float* x32 = reinterpret_cast<float*>(ws + p.x32);
   const long n = (long)rows * cols;
   HIP_TRY(hipMemcpyAsync(x32, X, (size_t)count * n * 4, hipMemcpyDeviceToDevice, s));
-  HIP_TRY(launch_ns_prepare(x32, reinterpret_cast<uint16_t*>(ws + p.xh0), ns_x0_lo(ws, p), count, n,
+  HIP_TRY(launch_ns_prepare(x32, reinterpret_cast<uint16_t*>(ws + p.xb), count, n,
                             reinterpret_cast<float*>(ws + p.part), p.nb, s));
   HIP_TRY(run_ns(ws, p, count, rows, cols, ns_coeffs, ns_steps, s));
   HIP_TRY(hipMemcpyAsync(X, x32, (size_t)count * n * 4, hipMemcpyDeviceToDevice, s));

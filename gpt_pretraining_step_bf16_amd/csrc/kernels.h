@@ -67,14 +67,12 @@ struct MuonGroup {
 hipError_t launch_muon_momentum(const MuonGroup& g, const float* grads, float* mom, float mu,
                                 float* partials, int blocks_per_mat, hipStream_t s);
 hipError_t launch_muon_pack(const MuonGroup& g, const float* mom, const float* partials,
-                            int blocks_per_mat, float* x32, uint16_t* xh, uint16_t* xl,
-                            hipStream_t s);
+                            int blocks_per_mat, float* x32, uint16_t* xb, hipStream_t s);
 hipError_t launch_muon_update(const MuonGroup& g, const float* x32, float* params,
                               uint16_t* params_bf16, float lr, hipStream_t s);
-// Frobenius-normalise count fp32 matrices of n elements in place and split into hi/lo.
-hipError_t launch_ns_prepare(float* x32, uint16_t* xh, uint16_t* xl, int count, long n,
-                             float* partials, int blocks_per_mat, hipStream_t s);
-hipError_t launch_split_hilo(const float* x32, uint16_t* xh, uint16_t* xl, long n, hipStream_t s);
+// Frobenius-normalise count fp32 matrices of n elements in place and write their bf16 copy.
+hipError_t launch_ns_prepare(float* x32, uint16_t* xb, int count, long n, float* partials,
+                             int blocks_per_mat, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Residual scalars and backout (all arrays fp32 [n], n % 4 == 0; scalars are

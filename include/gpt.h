@@ -194,8 +194,11 @@ size_t muon_workspace_bytes(const gpt_model* m);
  *   ns_steps     1..8 (1..5 with the built-in table; GPT_EINVAL otherwise)
  * Per matrix: X0 = M / (||M||_F + 1e-7), oriented so rows >= cols, ns_steps
  * iterations, W <- W - lr * sqrt(max(1, rows/cols)) * X. The iteration runs
- * with fp32 accumulation and fp32 master X; each matrix product is formed
- * from bf16 hi/lo splits of its operands (three MFMA products).
+ * with fp32 accumulation and fp32 master X; the MFMA operands are bf16 in the
+ * first iteration and fp16 in the others (one MFMA product per matrix
+ * product), which keeps the result within about 2e-3 (Gaussian inputs at the
+ * block shapes) to 1e-2 (small Gaussian matrices) relative L2 of the fp64
+ * iteration.
  */
 gpt_status muon_step(gpt_model* m, float* params, uint16_t* params_bf16, const float* grads,
                      float* momentum, float lr, float momentum_coef, const float* ns_coeffs,
@@ -295,7 +298,8 @@ const char* gpt_status_str(gpt_status s);
  * milliseconds, the algorithmic FLOPs and the launch count since the last
  * enable/reset. Categories: 0 projection / head / weight-gradient GEMMs,
  * 1 attention forward, 2 attention backward (causal FLOPs, recompute not
- * counted), 3 Newton-Schulz GEMMs (hi/lo products counted).
+ * counted), 3 Newton-Schulz GEMMs (symmetric products count the
+ * upper-triangle tiles they compute).
  */
 gpt_status gpt_profile_enable(gpt_model* m, int32_t enable);
 gpt_status gpt_profile_reset(gpt_model* m);

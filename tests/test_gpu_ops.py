@@ -216,6 +216,14 @@ def test_attention_fwd_bwd(B, T, H, W, HKV):
 # ----------------------------------------------------------------------------
 # Newton-Schulz against the oracle iteration
 # ----------------------------------------------------------------------------
+# Bars: the update tolerance (rel-L2 2e-2) on small matrices, 5e-3 at a block
+# shape. The first iteration takes bf16 operands, the others fp16, all with
+# fp32 accumulation and an fp32 X; a CPU emulation of those roundings puts
+# Gaussian inputs at 4.5e-3 (256 x 256), 7.7e-3 (384 x 128) and 1.7e-3
+# (1280 x 1280) from the fp64 iteration.
+NS_BAR = {(384, 128): 2e-2, (256, 256): 2e-2, (1280, 1280): 5e-3}
+
+
 @pytest.mark.parametrize("count,rows,cols", [(3, 384, 128), (2, 256, 256), (1, 1280, 1280)])
 def test_newton_schulz(count, rows, cols):
     log(f"newton-schulz count={count} rows={rows} cols={cols}")
@@ -228,7 +236,9 @@ def test_newton_schulz(count, rows, cols):
     got = Xd.cpu().numpy()
     for i in range(count):
         ref = oracle.newton_schulz(X[i].astype(np.float64), syn.NS_COEFFS)
-        assert rel_l2(got[i], ref) < 2e-3, rel_l2(got[i], ref)
+        e = rel_l2(got[i], ref)
+        log(f"  matrix {i}: rel-L2 {e:.2e}")
+        assert e < NS_BAR[(rows, cols)], e
 
 
 @pytest.mark.parametrize("count,rows,cols", [(2, 256, 256), (1, 1280, 1280), (3, 384, 128)])
