@@ -225,6 +225,9 @@ def main():
     ap.add_argument("--no-isolated-timings", action="store_true",
                     help="skip the separate AdamW / Muon timings after the timed steps (keeps a "
                          "kernel trace to whole steps)")
+    ap.add_argument("--packed", action="store_true",
+                    help="feed rows from the library's BOS best-fit packer over seeded synthetic "
+                         "documents instead of independent Zipf rows")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="launch one plain device copy of this many MiB before the steps "
                          "(the calibration kernel for rocprofv3 FETCH_SIZE/WRITE_SIZE counters)")
@@ -248,7 +251,30 @@ def main():
     print(f"[bench] config {args.config}: depth {L} width {d} vocab {V} seq {T} batch {B}",
           file=sys.stderr, flush=True)
     weights = syn.init_weights(L, V, seed=0, kv_heads=args.kv_heads)
-    tok, tgt = syn.split_tokens(syn.zipf_ids(B, T, V, seed=1))
+    packing = None
+    if args.packed:
+        # Rows of T + 1 tokens from the packer (host code in the library). The
+        # buffer is settled for 20 batches first; the timed steps then run on
+        # the next batch, resident in HBM like the Zipf rows.
+        from gpt_pretraining_step_bf16_amd import binding
+
+        doc_tok, doc_off = syn.synthetic_documents(max(4096, 40 * B * (T + 1) // 1000), V, seed=3)
+        pk = binding.BestFitPacker(doc_tok, doc_off, syn.PACK_BUFFER_DOCS)
+        t_pack = time.perf_counter()
+        for _ in range(20):
+            pk.pack(B, T + 1)
+        t_pack = (time.perf_counter() - t_pack) / 20
+        cut0 = pk.tokens_cut
+        rows = pk.pack(B, T + 1)
+        cut = pk.tokens_cut - cut0
+        tok, tgt = syn.split_tokens(rows)
+        packing = {"buffer_docs": syn.PACK_BUFFER_DOCS,
+                   "doc_len": f"round(exp(N({syn.DOC_LEN_MU}, {syn.DOC_LEN_SIGMA}))) tokens, BOS first",
+                   "tokens_cut_frac": round(cut / (B * (T + 1) + cut), 4),
+                   "rows_start_with_bos": bool((rows[:, 0] == V - 1).all()),
+                   "host_pack_ms_per_batch": round(t_pack * 1e3, 3)}
+    else:
+        tok, tgt = syn.split_tokens(syn.zipf_ids(B, T, V, seed=1))
     st = TrainState(L, V, T, B, kv_heads=args.kv_heads)
     st.load_weights(weights)
     windows = window_pattern(L, T, args.window_pattern) if args.window_pattern else None
@@ -391,7 +417,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded Zipf(1.1) token ids, N(0, 0.02) weights)",
+        "data": ("synthetic (seeded documents of Zipf(1.1) token ids, BOS best-fit packed; N(0, 0.02) weights)"
+                 if packing else "synthetic (seeded Zipf(1.1) token ids, N(0, 0.02) weights)"),
         "config": {
             "workload": f"{args.config}: depth {L}, width {d}, {dims['heads']} heads x 128, MLP {4 * d}, "
                         f"vocab {V}, seq {T}, microbatch {B}"
@@ -404,6 +431,7 @@ def main():
             "global_batch": accum * B,
             "seq_len": T,
             "parallelism": "none (1 GPU)",
+            **({"packing": packing} if packing else {}),
         },
         "mfu": round(mfu, 4),
         "mfu_vs_measured_peak": None if not peaks else round(mfu * PEAK_BF16_FLOPS / 1e12

@@ -14,7 +14,7 @@ import numpy as np
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgptstep.so")
 
-GPT_OK, GPT_EINVAL, GPT_ESHAPE, GPT_EHIP, GPT_ETOKEN, GPT_EWORKSPACE = 0, -1, -2, -3, -4, -5
+GPT_OK, GPT_EINVAL, GPT_ESHAPE, GPT_EHIP, GPT_ETOKEN, GPT_EWORKSPACE, GPT_EDATA = 0, -1, -2, -3, -4, -5, -6
 KIND_NAMES = {0: "emb", 1: "matrix", 2: "lm_head", 3: "scalar", 4: "gate"}
 
 # gpt_op_gemm out_mode values
@@ -97,6 +97,8 @@ EXPORTS = {
     "gpt_op_newton_schulz": (C.c_int, [_P, _I, _I, _I, C.POINTER(C.c_float), _I, _P, _S, _P]),
     "gpt_op_newton_schulz_noalloc": (C.c_int, [_P, _I, _I, _I, C.POINTER(C.c_float), _I, _P]),
     "gpt_probe_mfma_bf16": (C.c_int, [_I, _I, _P, C.POINTER(C.c_double), _P]),
+    "gpt_pack_best_fit": (C.c_int, [_P, _P, C.c_int64, _P, C.POINTER(C.c_int32), _I, C.POINTER(C.c_int64), _I,
+                                    _I, _P, C.POINTER(C.c_int64)]),
     "gpt_profile_enable": (C.c_int, [_P, _I]),
     "gpt_profile_reset": (C.c_int, [_P]),
     "gpt_profile_read": (C.c_int, [_P, _I, C.POINTER(C.c_double), C.POINTER(C.c_double),
@@ -343,3 +345,40 @@ def probe_mfma_bf16(blocks, iters, sink, stream=None) -> float:
     st = lib().gpt_probe_mfma_bf16(int(blocks), int(iters), _ptr(sink), C.byref(fl), _stream(stream))
     _check(st, "gpt_probe_mfma_bf16")
     return float(fl.value)
+
+
+class BestFitPacker:
+    """State of gpt_pack_best_fit over one document stream (host arrays).
+
+    tokens: int32 [total], offsets: int64 [n_docs + 1]; every call of pack()
+    fills `rows` rows of `row_len` tokens and carries the buffer to the next.
+    """
+
+    def __init__(self, tokens, offsets, buffer_cap):
+        import numpy as np
+
+        self.tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+        self.offsets = np.ascontiguousarray(offsets, dtype=np.int64)
+        self.n_docs = len(self.offsets) - 1
+        self.buffer = np.zeros(int(buffer_cap), dtype=np.int64)
+        self.count = C.c_int32(0)
+        self.next_doc = C.c_int64(0)
+        self.tokens_cut = 0
+
+    def pack(self, rows, row_len):
+        import numpy as np
+
+        out = np.zeros((int(rows), int(row_len)), dtype=np.int32)
+        cut = C.c_int64(0)
+        vp = lambda a: C.c_void_p(a.ctypes.data)
+        st = lib().gpt_pack_best_fit(vp(self.tokens), vp(self.offsets), self.n_docs, vp(self.buffer),
+                                     C.byref(self.count), len(self.buffer), C.byref(self.next_doc), int(rows),
+                                     int(row_len), vp(out), C.byref(cut))
+        self.tokens_cut += int(cut.value)
+        _check(st, "gpt_pack_best_fit")
+        return out
+
+    @property
+    def state(self):
+        """(buffered document ids in order, next stream document)."""
+        return [int(x) for x in self.buffer[:self.count.value]], int(self.next_doc.value)

@@ -530,6 +530,7 @@ const char* gpt_status_str(gpt_status s) {
     case GPT_EHIP: return "HIP runtime error";
     case GPT_ETOKEN: return "token or target id outside the vocabulary";
     case GPT_EWORKSPACE: return "workspace missing or too small";
+    case GPT_EDATA: return "document data unusable or exhausted";
   }
   return "unknown status";
 }

@@ -144,6 +144,35 @@ def zipf_ids(batch: int, seq: int, vocab: int, seed: int = 1, s: float = ZIPF_S)
     return ids.reshape(batch, seq + 1)
 
 
+# Documents of the packing workload: lengths round(exp(N(DOC_LEN_MU,
+# DOC_LEN_SIGMA))) tokens (mean ~1100), at least 2; with a best-fit buffer of
+# PACK_BUFFER_DOCS documents about 35% of the tokens are cut at sequence length
+# 2048 once the buffer has settled, the figure the pages give.
+DOC_LEN_MU = 6.5
+DOC_LEN_SIGMA = 1.0
+PACK_BUFFER_DOCS = 64
+
+
+def synthetic_documents(n_docs: int, vocab: int, seed: int = 3, mu: float = DOC_LEN_MU,
+                        sigma: float = DOC_LEN_SIGMA, s: float = ZIPF_S):
+    """Seeded documents: (tokens int32 [total], offsets int64 [n_docs + 1]).
+
+    Token 0 of each document is BOS = vocab - 1; the others are Zipf(s) ids over
+    0 .. vocab - 2 (the zipf_ids sampling).
+    """
+    rng = np.random.default_rng(seed)
+    lens = np.maximum(2, np.rint(np.exp(rng.normal(mu, sigma, n_docs)))).astype(np.int64)
+    offsets = np.zeros(n_docs + 1, dtype=np.int64)
+    np.cumsum(lens, out=offsets[1:])
+    ranks = np.arange(1, vocab, dtype=np.float64)
+    cdf = np.cumsum(ranks ** (-s))
+    cdf /= cdf[-1]
+    cdf[-1] = 1.0
+    tokens = np.searchsorted(cdf, rng.random(int(offsets[-1])), side="right").astype(np.int32)
+    tokens[offsets[:-1]] = vocab - 1
+    return tokens, offsets
+
+
 def split_tokens(ids: np.ndarray):
     """Inputs are positions 0..T-1 and targets positions 1..T of each row."""
     return np.ascontiguousarray(ids[:, :-1]), np.ascontiguousarray(ids[:, 1:])

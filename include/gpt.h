@@ -46,7 +46,8 @@ typedef enum {
   GPT_ESHAPE = -2,     /* shape not supported (e.g. seq > the plan's max_seq) */
   GPT_EHIP = -3,       /* a HIP runtime call failed */
   GPT_ETOKEN = -4,     /* a token id or target outside [0, vocab) (target -1 = ignore) */
-  GPT_EWORKSPACE = -5  /* workspace missing or smaller than the *_workspace_bytes() value */
+  GPT_EWORKSPACE = -5, /* workspace missing or smaller than the *_workspace_bytes() value */
+  GPT_EDATA = -6       /* input data unusable: an empty document, or the document stream ran out */
 } gpt_status;
 
 enum { GPT_KIND_EMB = 0, GPT_KIND_MATRIX = 1, GPT_KIND_LM_HEAD = 2, GPT_KIND_SCALAR = 3, GPT_KIND_GATE = 4 };
@@ -366,6 +367,35 @@ gpt_status gpt_op_newton_schulz(float* X, int32_t count, int32_t rows, int32_t c
 #define GPT_NS_STATIC_SCRATCH_BYTES (128u << 20)
 gpt_status gpt_op_newton_schulz_noalloc(float* X, int32_t count, int32_t rows, int32_t cols,
                                         const float* ns_coeffs, int32_t ns_steps, void* stream);
+
+/*
+ * BOS-aligned best-fit packing of a document stream into token rows, on the
+ * host ([CT50] "4. Carregamento de Dados": each row starts with BOS, rows are
+ * filled best-fit with whole documents, and a document is cut to fill a row
+ * when none fits). Before each choice the buffer is topped up from the stream
+ * to buffer_cap documents; the longest buffered document that fits the space
+ * left goes in whole (the earliest among equal lengths); if none fits, the
+ * shortest (earliest among equals) fills the row with its first tokens and its
+ * tail is dropped. A chosen document leaves the buffer; the others keep their
+ * order. Documents carry their own leading BOS; nothing is inserted.
+ *   tokens, offsets  HOST: document d is tokens[offsets[d] .. offsets[d+1]),
+ *                    d < n_docs; every document non-empty
+ *   buffer           HOST int64 [buffer_cap]: ids of the buffered documents in
+ *                    order, *buffer_count of them (in/out; start with 0)
+ *   next_doc         HOST in/out: the next stream document to buffer (start 0)
+ *   rows, row_len    rows to fill and tokens per row (sequence length + 1 for
+ *                    inputs and shifted targets)
+ *   out              HOST int32 [rows, row_len], written row by row
+ *   tokens_cut       HOST out (may be NULL): tokens dropped by cuts in this call
+ * The caller owns every array; nothing is allocated, no GPU is used. Returns
+ * GPT_EINVAL for null pointers, sizes or a state out of range, GPT_EDATA when
+ * an empty document or decreasing offsets reach the buffer or the stream runs
+ * out in mid-row; the state is written back either way (the rows before the
+ * failing one are complete).
+ */
+gpt_status gpt_pack_best_fit(const int32_t* tokens, const int64_t* offsets, int64_t n_docs, int64_t* buffer,
+                             int32_t* buffer_count, int32_t buffer_cap, int64_t* next_doc, int32_t rows,
+                             int32_t row_len, int32_t* out, int64_t* tokens_cut);
 
 /* Measurement probe, not part of the step: launches `blocks` workgroups of
  * 4 waves, each issuing 4 independent chains of `iters` dense bf16 MFMAs

@@ -34,3 +34,4 @@ from .adamw import adamw_step, adamw_update  # noqa: F401
 from .muon import muon_step, newton_schulz, newton_schulz_svd  # noqa: F401
 from .polar_express import greedy_minimax_triples  # noqa: F401
 from .normuon import normuon_step, variance_reduction  # noqa: F401
+from .packing import pack_best_fit  # noqa: F401
