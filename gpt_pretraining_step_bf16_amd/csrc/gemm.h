@@ -23,7 +23,8 @@ enum GemmEpilogue {
   // fp16 operands (v_mfma_f32_32x32x16_f16), fp32 accumulation:
   EPI_H_GRAM = 11,      // C f16 = alpha*acc
   EPI_H_NS_POLY = 12,   // v = alpha*acc + beta*D (D f16) -> C f16 v
-  EPI_H_NS_UPDATE = 13, // as EPI_NS_UPDATE
+  EPI_H_NS_UPDATE = 13, // v = alpha*acc + beta*D (D f16) -> C f16 v
+  EPI_H_NS_LAST = 14,   // v = alpha*acc + beta*D (D f16) -> C3 f32 v (D layout)
 };
 
 struct GemmArgs {

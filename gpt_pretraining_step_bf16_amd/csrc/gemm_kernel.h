@@ -260,13 +260,13 @@ __device__ __forceinline__ void load_bf16x4(const void* p, float* v) {
 template <int E>
 constexpr bool epi_reads() {
   return E == EPI_F32_ACC || E == EPI_RESID_BF16 || E == EPI_DRELU2_BF16 || E == EPI_NS_POLY ||
-         E == EPI_NS_UPDATE || E == EPI_H_NS_POLY || E == EPI_H_NS_UPDATE;
+         E == EPI_NS_UPDATE || E == EPI_H_NS_POLY || E == EPI_H_NS_UPDATE || E == EPI_H_NS_LAST;
 }
 
 // Whether the operands are fp16 (the EPI_H_* epilogues) rather than bf16.
 template <int E>
 constexpr bool f16_operands() {
-  return E == EPI_H_GRAM || E == EPI_H_NS_POLY || E == EPI_H_NS_UPDATE;
+  return E == EPI_H_GRAM || E == EPI_H_NS_POLY || E == EPI_H_NS_UPDATE || E == EPI_H_NS_LAST;
 }
 
 // One 32 x 32 x 16 MFMA of the instantiation's operand type (the fragments
@@ -318,11 +318,11 @@ __device__ __forceinline__ uint4 epi_load(const EpiPtrs& e, int i, int j, int g)
     const uint2 h = *reinterpret_cast<const uint2*>(e.db + dof);
     const uint2 l = *reinterpret_cast<const uint2*>(e.d2 + dof);
     r = make_uint4(h.x, h.y, l.x, l.y);
-  } else if constexpr (E == EPI_H_NS_POLY) {
+  } else if constexpr (E == EPI_H_NS_POLY || E == EPI_H_NS_UPDATE || E == EPI_H_NS_LAST) {
     const uint2 u = *reinterpret_cast<const uint2*>(e.db + dof);
     r.x = u.x;
     r.y = u.y;
-  } else if constexpr (E == EPI_NS_UPDATE || E == EPI_H_NS_UPDATE) {
+  } else if constexpr (E == EPI_NS_UPDATE) {
     r = *reinterpret_cast<const uint4*>(e.df + dof);
   }
   return r;
@@ -396,12 +396,19 @@ __device__ __forceinline__ void epi4(const EpiPtrs& e, int i, int j, int g, cons
     for (int r = 0; r < 4; ++r) w[r] = e.alpha * v[r] + e.beta * (h[r] + l[r]);
     store_hilo4(e.cb + co, e.c2 + co, w);
     if (e.tr) store_hilo4_t(e, i, j, g, w);
-  } else if constexpr (E == EPI_NS_UPDATE || E == EPI_H_NS_UPDATE) {
+  } else if constexpr (E == EPI_NS_UPDATE) {
     const float4 x = __builtin_bit_cast(float4, in);
     float w[4] = {e.alpha * v[0] + e.beta * x.x, e.alpha * v[1] + e.beta * x.y,
                   e.alpha * v[2] + e.beta * x.z, e.alpha * v[3] + e.beta * x.w};
     *reinterpret_cast<float4*>(e.c3 + dof) = make_float4(w[0], w[1], w[2], w[3]);
     store_h4(e.cb + co, w);
+  } else if constexpr (E == EPI_H_NS_UPDATE || E == EPI_H_NS_LAST) {
+    const float w[4] = {e.alpha * v[0] + e.beta * h_lo(in.x), e.alpha * v[1] + e.beta * h_hi(in.x),
+                        e.alpha * v[2] + e.beta * h_lo(in.y), e.alpha * v[3] + e.beta * h_hi(in.y)};
+    if constexpr (E == EPI_H_NS_UPDATE)
+      store_h4(e.cb + co, w);
+    else
+      *reinterpret_cast<float4*>(e.c3 + dof) = make_float4(w[0], w[1], w[2], w[3]);
   } else if constexpr (E == EPI_H_GRAM) {
     const float w[4] = {e.alpha * v[0], e.alpha * v[1], e.alpha * v[2], e.alpha * v[3]};
     store_h4(e.cb + co, w);
@@ -459,7 +466,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const f32x16 (&acc
     };
     // 16-byte inputs (fp32 or hi/lo pairs) load block by block; 8-byte ones
     // also prefetch the next block (registers allow it).
-    constexpr bool WIDE = E == EPI_F32_ACC || E == EPI_NS_POLY || E == EPI_NS_UPDATE || E == EPI_H_NS_UPDATE;
+    constexpr bool WIDE = E == EPI_F32_ACC || E == EPI_NS_POLY || E == EPI_NS_UPDATE;
     if constexpr (epi_reads<E>()) load_block(0, in[0]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -552,7 +559,9 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& p, const f32x16 (
 
 // The same staging for the epilogues that read an operand: the fp32 residual
 // add (read-modify-write of fp32 C), the ReLU^2 backward (reads bf16 D) and
-// the Newton-Schulz update (reads fp32 X, writes fp32 X and its bf16 hi/lo). Per 32-row block: the block's inputs (old C, or D) are read
+// the Newton-Schulz updates (first iteration: reads fp32 X, writes fp32 X and
+// its fp16 copy; later ones: fp16 X in, fp16 X out; the last iteration's fp32
+// output takes the register path). Per 32-row block: the block's inputs (old C, or D) are read
 // row-contiguous into the wave's LDS region; each lane combines its
 // accumulators with the inputs at its own positions, in place; the results
 // leave row-contiguous (256-byte fp32 or 128-byte bf16 row segments). The
@@ -610,10 +619,13 @@ __device__ __forceinline__ void store_tile_lds_io(const GemmArgs& p, const f32x1
   const int r = lane & 31, hl = lane >> 5;
   const int ldc = (int)p.ldc;
   const long cbase = (long)bi * p.sc + (long)(m0 + row_off) * p.ldc + (n0 + col_off);
-  if constexpr (E == EPI_DRELU2_BF16) {
-    // bf16 rows: 8 lanes per 128-byte segment, 8 rows per instruction.
+  if constexpr (E == EPI_DRELU2_BF16 || E == EPI_H_NS_UPDATE) {
+    // 16-bit D in, 16-bit C out (ReLU^2 backward: bf16; Newton-Schulz update
+    // v = alpha acc + beta X: fp16). 8 lanes per 128-byte segment, 8 rows per
+    // instruction.
     constexpr int RS = STG_RS;
     const int ldd = (int)p.ldd;
+    const float alpha = p.alpha, beta = p.beta;
     const auto drs =
         wave_rsrc(reinterpret_cast<const uint16_t*>(p.d) + (long)bi * p.sd + (long)(m0 + row_off) * p.ldd + (n0 + col_off));
     const auto crs = wave_rsrc(reinterpret_cast<uint16_t*>(p.c) + cbase);
@@ -649,13 +661,19 @@ __device__ __forceinline__ void store_tile_lds_io(const GemmArgs& p, const f32x1
         for (int g = 0; g < 4; ++g) {
           char* a = wreg + r * RS + (32 * j + 8 * g + 4 * hl) * 2;
           const uint2 h = *reinterpret_cast<const uint2*>(a);
-          // d relu(u)^2 / du = 2 relu(u) = 2 sqrt(h), h = relu(u)^2 as stored.
           const f32x16& v = acc[i][j];
-          *reinterpret_cast<uint2*>(a) =
-              make_uint2(pack_bf2(2.f * v[4 * g] * __builtin_amdgcn_sqrtf(bf_lo(h.x)),
-                                  2.f * v[4 * g + 1] * __builtin_amdgcn_sqrtf(bf_hi(h.x))),
-                         pack_bf2(2.f * v[4 * g + 2] * __builtin_amdgcn_sqrtf(bf_lo(h.y)),
-                                  2.f * v[4 * g + 3] * __builtin_amdgcn_sqrtf(bf_hi(h.y))));
+          if constexpr (E == EPI_DRELU2_BF16) {
+            // d relu(u)^2 / du = 2 relu(u) = 2 sqrt(h), h = relu(u)^2 as stored.
+            *reinterpret_cast<uint2*>(a) =
+                make_uint2(pack_bf2(2.f * v[4 * g] * __builtin_amdgcn_sqrtf(bf_lo(h.x)),
+                                    2.f * v[4 * g + 1] * __builtin_amdgcn_sqrtf(bf_hi(h.x))),
+                           pack_bf2(2.f * v[4 * g + 2] * __builtin_amdgcn_sqrtf(bf_lo(h.y)),
+                                    2.f * v[4 * g + 3] * __builtin_amdgcn_sqrtf(bf_hi(h.y))));
+          } else {
+            *reinterpret_cast<uint2*>(a) =
+                make_uint2(pack_h2(alpha * v[4 * g] + beta * h_lo(h.x), alpha * v[4 * g + 1] + beta * h_hi(h.x)),
+                           pack_h2(alpha * v[4 * g + 2] + beta * h_lo(h.y), alpha * v[4 * g + 3] + beta * h_hi(h.y)));
+          }
         }
       wave_lds_order();
 #pragma unroll
@@ -671,7 +689,7 @@ __device__ __forceinline__ void store_tile_lds_io(const GemmArgs& p, const f32x1
       }
       wave_lds_order();
     }
-  } else if constexpr (E == EPI_NS_UPDATE || E == EPI_H_NS_UPDATE) {
+  } else if constexpr (E == EPI_NS_UPDATE) {
     // v = alpha acc + beta D; fp32 v to C3 (stride ldd), fp16 v to C (stride
     // ldc). fp32 rows: 16 lanes per 256-byte segment.
     constexpr int RS = STG_RS_F;

@@ -11,6 +11,7 @@ hipError_t launch_gemm_kk_aux(const GemmArgs& g, dim3 grid, hipStream_t s) {
     case EPI_NS_UPDATE: GEMM_LAUNCH(true, true, 0, EPI_NS_UPDATE); break;
     case EPI_H_NS_POLY: GEMM_LAUNCH(true, true, 0, EPI_H_NS_POLY); break;
     case EPI_H_NS_UPDATE: GEMM_LAUNCH(true, true, 0, EPI_H_NS_UPDATE); break;
+    case EPI_H_NS_LAST: GEMM_LAUNCH(true, true, 0, EPI_H_NS_LAST); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -333,8 +333,9 @@ struct NsPlan {
   int nb = 0;
 };
 
-// Newton-Schulz buffers: x32 the fp32 X, xb the bf16 X0 the preparation
-// writes, xh0 / xh1 the fp16 X of the later iterations (ping-pong), ah / al
+// Newton-Schulz buffers: x32 the fp32 X (X0 in, the result out), xb the bf16
+// X0 the preparation writes, xh0 / xh1 the fp16 X between iterations
+// (ping-pong), ah / al
 // and bh / bl the first iteration's A and B as bf16 hi / lo (ah and bh hold
 // the fp16 A and B afterwards), part the normalisation partial sums.
 NsPlan plan_ns(long count, long xr, long xc, size_t base) {
@@ -357,18 +358,18 @@ NsPlan plan_ns(long count, long xr, long xc, size_t base) {
   return p;
 }
 
-// Operand precision of the iterations. Every product accumulates in fp32 and
-// X stays in fp32 between iterations; only the MFMA operands are rounded.
+// Operand precision of the iterations. Every product accumulates in fp32.
 // The first iteration takes bf16 operands: X0 = G / ||G||_F has entries of
 // order 1 / sqrt(rows * cols), where fp16 would be subnormal for the larger
 // matrices; its A is kept as bf16 hi + lo for the linear term of B. The
 // others take fp16 operands (same MFMA rate, 3 more mantissa bits), with A, B
-// and X stored in fp16. A CPU emulation of exactly these roundings against the
-// fp64 iteration gives a relative L2 error of 1.7e-3 to 2.3e-3 for Gaussian,
-// 4e-4 for 1/k-spectrum and 7e-4 to 1e-3 for rank-1-plus-noise matrices at
-// the block shapes (1280 x 1280, 5120 x 1280, 1280 x 5120), and at most
-// 7.7e-3 on a small Gaussian 384 x 128; bf16 operands throughout give 1.5e-2
-// to 2.4e-2 on the same Gaussian matrices.
+// and X stored in fp16 between them: the a X term of a middle iteration reads
+// the same fp16 X its product reads, and only the last writes X in fp32. A CPU
+// emulation of exactly these roundings against the fp64 iteration gives a
+// relative L2 error of 1.3e-3 to 1.7e-3 for Gaussian and 2.1e-3 to 2.6e-3 for
+// 1/k-spectrum matrices at the block shapes (1280 x 1280, 5120 x 1280), and at
+// most 5.8e-3 on a small Gaussian 384 x 128; bf16 operands throughout give
+// 1.5e-2 to 2.4e-2 on the same Gaussian matrices.
 //
 // Run ns_steps iterations on prepared X (x32 and xb filled). Result in x32.
 hipError_t run_ns(char* ws, const NsPlan& p, int count, long xr, long xc, const float* coeffs,
@@ -412,8 +413,10 @@ hipError_t run_ns(char* ws, const NsPlan& p, int count, long xr, long xc, const 
     g.epi = first ? EPI_NS_POLY : EPI_H_NS_POLY;
     e = launch_gemm_prof(g, s, PROF_NS);
     if (e != hipSuccess) return e;
-    // X = a X + X B (B symmetric, so X B = X B^T); the fp16 copy of the new X
-    // goes to the other buffer.
+    // X = a X + X B (B symmetric, so X B = X B^T). The first iteration reads
+    // the fp32 X0 and writes X in fp32 and fp16; the middle ones read and
+    // write fp16 X only (the other buffer); the last writes the fp32 result.
+    const bool last = it == steps - 1;
     uint16_t* xnext = first ? xh[cur] : xh[cur ^ 1];
     gemm_args_init(g);
     g.a[0] = x; g.b[0] = bh;
@@ -421,10 +424,10 @@ hipError_t run_ns(char* ws, const NsPlan& p, int count, long xr, long xc, const 
     g.lda = xc; g.ldb = xc; g.sa = xr * xc; g.sb = xc * xc;
     g.a_kmajor = 1; g.b_kmajor = 1;
     g.c = xnext; g.c3 = x32; g.ldc = xc; g.sc = xr * xc;
-    g.d = x32; g.ldd = xc; g.sd = xr * xc;
+    g.d = first ? (const void*)x32 : (const void*)x; g.ldd = xc; g.sd = xr * xc;
     g.alpha = 1.f; g.beta = a;
     g.batch = count;
-    g.epi = first ? EPI_NS_UPDATE : EPI_H_NS_UPDATE;
+    g.epi = first ? EPI_NS_UPDATE : last ? EPI_H_NS_LAST : EPI_H_NS_UPDATE;
     e = launch_gemm_prof(g, s, PROF_NS);
     if (e != hipSuccess) return e;
     if (!first) cur ^= 1;

@@ -32,7 +32,7 @@ import re
 import sys
 
 # Epilogue ids (GemmEpilogue in csrc/gemm.h) that only Newton-Schulz uses.
-NS_EPILOGUES = {7, 8, 9, 11, 12, 13}
+NS_EPILOGUES = {7, 8, 9, 11, 12, 13, 14}
 GEMM_SOURCES = ("common.h", "lds_dma.h", "gemm.h", "gemm_kernel.h", "gemm.hip",
                 "gemm_kk_fwd.hip", "gemm_kk_aux.hip", "gemm_kt.hip", "gemm_tt.hip")
 

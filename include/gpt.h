@@ -195,11 +195,11 @@ size_t muon_workspace_bytes(const gpt_model* m);
  *   ns_steps     1..8 (1..5 with the built-in table; GPT_EINVAL otherwise)
  * Per matrix: X0 = M / (||M||_F + 1e-7), oriented so rows >= cols, ns_steps
  * iterations, W <- W - lr * sqrt(max(1, rows/cols)) * X. The iteration runs
- * with fp32 accumulation and fp32 master X; the MFMA operands are bf16 in the
- * first iteration and fp16 in the others (one MFMA product per matrix
- * product), which keeps the result within about 2e-3 (Gaussian inputs at the
- * block shapes) to 1e-2 (small Gaussian matrices) relative L2 of the fp64
- * iteration.
+ * with fp32 accumulation; the MFMA operands are bf16 in the first iteration
+ * and fp16 in the others (one MFMA product per matrix product), X is kept in
+ * fp16 between iterations and the last one writes it in fp32, which keeps the
+ * result within about 2e-3 (Gaussian inputs at the block shapes) to 8e-3
+ * (small Gaussian matrices) relative L2 of the fp64 iteration.
  */
 gpt_status muon_step(gpt_model* m, float* params, uint16_t* params_bf16, const float* grads,
                      float* momentum, float lr, float momentum_coef, const float* ns_coeffs,
