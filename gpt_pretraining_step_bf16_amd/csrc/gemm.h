@@ -18,7 +18,7 @@ enum GemmEpilogue {
   EPI_SPLITK = 6,       // C f32 [split] = acc (partials, reduced later)
   EPI_HILO = 7,         // v = alpha*acc -> C bf16 hi(v), C2 bf16 lo(v)
   EPI_NS_POLY = 8,      // v = alpha*acc + beta*(D + D2) (D, D2 bf16 hi/lo) -> C hi, C2 lo
-  EPI_NS_UPDATE = 9,    // v = alpha*acc + beta*D (D f32) -> C3 f32 v, C f16 v
+  EPI_NS_UPDATE = 9,    // v = alpha*acc + beta*D (D f32) -> C3 f32 v (unless C3 is null), C f16 v
   EPI_RELU2_BF16 = 10,  // C bf16 = max(acc, 0)^2
   // fp16 operands (v_mfma_f32_32x32x16_f16), fp32 accumulation:
   EPI_H_GRAM = 11,      // C f16 = alpha*acc

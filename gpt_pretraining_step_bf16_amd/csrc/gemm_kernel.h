@@ -288,6 +288,7 @@ struct EpiPtrs {
   uint16_t* cb;         // C as bf16 (fp16 for EPI_NS_UPDATE and EPI_H_*)
   uint16_t* c2;         // lo half of hi/lo outputs
   float* c3;            // fp32 X (NS_UPDATE; D layout)
+  bool c3ok;            // C3 given (NS_UPDATE may leave it null)
   const uint16_t* db;   // D as bf16
   const uint16_t* d2;   // D2 as bf16
   const float* df;      // D as fp32
@@ -400,7 +401,7 @@ __device__ __forceinline__ void epi4(const EpiPtrs& e, int i, int j, int g, cons
     const float4 x = __builtin_bit_cast(float4, in);
     float w[4] = {e.alpha * v[0] + e.beta * x.x, e.alpha * v[1] + e.beta * x.y,
                   e.alpha * v[2] + e.beta * x.z, e.alpha * v[3] + e.beta * x.w};
-    *reinterpret_cast<float4*>(e.c3 + dof) = make_float4(w[0], w[1], w[2], w[3]);
+    if (e.c3ok) *reinterpret_cast<float4*>(e.c3 + dof) = make_float4(w[0], w[1], w[2], w[3]);
     store_h4(e.cb + co, w);
   } else if constexpr (E == EPI_H_NS_UPDATE || E == EPI_H_NS_LAST) {
     const float w[4] = {e.alpha * v[0] + e.beta * h_lo(in.x), e.alpha * v[1] + e.beta * h_hi(in.x),
@@ -439,7 +440,8 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const f32x16 (&acc
   e.cf = reinterpret_cast<float*>(p.c) + co + (E == EPI_SPLITK ? (long)si * p.s_split : 0L);
   e.cb = reinterpret_cast<uint16_t*>(p.c) + co;
   e.c2 = reinterpret_cast<uint16_t*>(p.c2) + co;
-  e.c3 = reinterpret_cast<float*>(p.c3) + dof;
+  e.c3ok = p.c3 != nullptr;
+  e.c3 = e.c3ok ? reinterpret_cast<float*>(p.c3) + dof : nullptr;
   e.db = reinterpret_cast<const uint16_t*>(p.d) + dof;
   e.d2 = reinterpret_cast<const uint16_t*>(p.d2) + dof;
   e.df = reinterpret_cast<const float*>(p.d) + dof;
@@ -696,6 +698,9 @@ __device__ __forceinline__ void store_tile_lds_io(const GemmArgs& p, const f32x1
     const int ldd = (int)p.ldd;
     const long dbase = (long)bi * p.sd + (long)(m0 + row_off) * p.ldd + (n0 + col_off);
     const auto drs = wave_rsrc(reinterpret_cast<const float*>(p.d) + dbase);
+    // C3 may be null: then only the fp16 copy is written (a run with more
+    // iterations reads X from it).
+    const bool with_x32 = p.c3 != nullptr;
     const auto x3 = wave_rsrc(reinterpret_cast<float*>(p.c3) + dbase);
     const auto hrs = wave_rsrc(reinterpret_cast<uint16_t*>(p.c) + cbase);
     const float alpha = p.alpha, beta = p.beta;
@@ -737,10 +742,12 @@ __device__ __forceinline__ void store_tile_lds_io(const GemmArgs& p, const f32x1
         const float4 w = *reinterpret_cast<const float4*>(wreg + (4 * q + rq) * RS + cc * 16);
         if (ok(row)) {
           const u32x2_t h = u32x2_t{pack_h2(w.x, w.y), pack_h2(w.z, w.w)};
-          __builtin_amdgcn_sched_barrier(0);
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, w), x3, dvo,
-                                                 (32 * i + 4 * q) * ldd * 4, 0);
-          wide_store_wait();
+          if (with_x32) {
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, w), x3, dvo,
+                                                   (32 * i + 4 * q) * ldd * 4, 0);
+            wide_store_wait();
+          }
           __builtin_amdgcn_raw_buffer_store_b64(h, hrs, hvo, (32 * i + 4 * q) * ldc * 2, 0);
         }
       }

@@ -414,8 +414,8 @@ hipError_t run_ns(char* ws, const NsPlan& p, int count, long xr, long xc, const 
     e = launch_gemm_prof(g, s, PROF_NS);
     if (e != hipSuccess) return e;
     // X = a X + X B (B symmetric, so X B = X B^T). The first iteration reads
-    // the fp32 X0 and writes X in fp32 and fp16; the middle ones read and
-    // write fp16 X only (the other buffer); the last writes the fp32 result.
+    // the fp32 X0 and writes X in fp16; the middle ones read and write fp16 X
+    // only (the other buffer); the last writes the fp32 result.
     const bool last = it == steps - 1;
     uint16_t* xnext = first ? xh[cur] : xh[cur ^ 1];
     gemm_args_init(g);
@@ -423,7 +423,8 @@ hipError_t run_ns(char* ws, const NsPlan& p, int count, long xr, long xc, const 
     g.M = (int)xr; g.N = (int)xc; g.K = (int)xc;
     g.lda = xc; g.ldb = xc; g.sa = xr * xc; g.sb = xc * xc;
     g.a_kmajor = 1; g.b_kmajor = 1;
-    g.c = xnext; g.c3 = x32; g.ldc = xc; g.sc = xr * xc;
+    g.c = xnext; g.ldc = xc; g.sc = xr * xc;
+    g.c3 = (first && !last) ? nullptr : x32;  // the first iteration's fp32 X only when it is also the last
     g.d = first ? (const void*)x32 : (const void*)x; g.ldd = xc; g.sd = xr * xc;
     g.alpha = 1.f; g.beta = a;
     g.batch = count;

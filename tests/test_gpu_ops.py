@@ -241,6 +241,28 @@ def test_newton_schulz(count, rows, cols):
         assert e < NS_BAR[(rows, cols)], e
 
 
+@pytest.mark.parametrize("steps", [1, 2, 3])
+def test_newton_schulz_fewer_steps(steps):
+    """Shorter tables: one step is the bf16 first iteration alone (its fp32
+    output is the result), two end with the fp16 iteration that writes fp32,
+    three pass X through fp16 once in between."""
+    count, rows, cols = 2, 512, 256
+    log(f"newton-schulz steps={steps} count={count} rows={rows} cols={cols}")
+    rng = np.random.default_rng(17 + steps)
+    X = rng.standard_normal((count, rows, cols)).astype(np.float32)
+    Xd = dev(torch, X)
+    scratch = torch.empty(binding.ns_scratch_bytes(count, rows, cols), dtype=torch.uint8, device="cuda")
+    table = np.asarray(syn.NS_COEFFS, dtype=np.float32)[:steps]
+    binding.op_newton_schulz(Xd, count, rows, cols, table, scratch)
+    torch.cuda.synchronize()
+    got = Xd.cpu().numpy()
+    for i in range(count):
+        ref = oracle.newton_schulz(X[i].astype(np.float64), syn.NS_COEFFS, steps)
+        e = rel_l2(got[i], ref)
+        log(f"  matrix {i}: rel-L2 {e:.2e}")
+        assert e < (2e-3 if steps == 1 else 2e-2), e
+
+
 @pytest.mark.parametrize("count,rows,cols", [(2, 256, 256), (1, 1280, 1280), (3, 384, 128)])
 def test_newton_schulz_is_bit_reproducible(count, rows, cols):
     """Two runs on identical inputs give identical bits: every sum has a fixed
