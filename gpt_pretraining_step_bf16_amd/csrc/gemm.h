@@ -28,9 +28,8 @@ enum GemmEpilogue {
 };
 
 struct GemmArgs {
-  const uint16_t* a[3];  // per K-segment operand bases (bf16 or fp16 bits); nseg segments are summed
-  const uint16_t* b[3];
-  int nseg;
+  const uint16_t* a;     // operand bases (bf16 or fp16 bits)
+  const uint16_t* b;
   int M, N, K;
   long lda, ldb;         // leading dimensions (elements)
   long sa, sb;           // batch strides (elements)

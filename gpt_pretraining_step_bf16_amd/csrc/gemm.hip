@@ -27,7 +27,6 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, long s_spli
 
 void gemm_args_init(GemmArgs& g) {
   g = GemmArgs{};
-  g.nseg = 1;
   g.alpha = 1.f;
   g.beta = 0.f;
   g.batch = 1;

@@ -33,8 +33,6 @@
 //  * Workgroup ids are remapped so consecutive tiles run on one XCD (ids are
 //    dealt round-robin over the 8 XCDs), then grouped 4 tile-rows at a time so
 //    an XCD's tiles share A rows and B columns in its L2.
-//  * Up to three K segments with their own operand bases are summed into one
-//    accumulator (a sum of products in one pass, e.g. hi/lo split operands).
 #pragma once
 
 #include <type_traits>
@@ -52,11 +50,6 @@ constexpr int NST = 4;                  // stages in the ring
 constexpr int NTHR = 256;
 constexpr int OP_BYTES = BM * BKD * 2;  // one operand's stage: 16 KB
 constexpr int STAGE_BYTES = 2 * OP_BYTES;
-
-__device__ __forceinline__ uint32_t sq2(uint32_t w) {
-  float lo = bf_lo(w), hi = bf_hi(w);
-  return pack_bf2(lo * lo, hi * hi);
-}
 
 // Byte offset of (row r, 16-byte k-chunk c) in a K-contiguous stage [256][32].
 __device__ __forceinline__ int koff(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
@@ -208,12 +201,6 @@ __device__ __forceinline__ bf16x8 read_frag(const char* lds_op, int rb, int ks, 
     const uint2 b = __builtin_bit_cast(uint2, hi);
     return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
   }
-}
-
-__device__ __forceinline__ bf16x8 square_frag(bf16x8 f) {
-  uint4 u = __builtin_bit_cast(uint4, f);
-  u = make_uint4(sq2(u.x), sq2(u.y), sq2(u.z), sq2(u.w));
-  return __builtin_bit_cast(bf16x8, u);
 }
 
 // Wait until at most `n` of this wave's direct loads are outstanding (they
@@ -813,7 +800,7 @@ __device__ __forceinline__ void store_tile_lds_io(const GemmArgs& p, const f32x1
   }
 }
 
-template <bool AK, bool BK_, int SQ, int EPI>
+template <bool AK, bool BK_, int EPI>
 __global__ void __launch_bounds__(NTHR, 1) gemm_bf16_kernel(const GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE_BYTES];
 
@@ -833,7 +820,7 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_bf16_kernel(const GemmArgs p) {
   const int kbeg = si * p.k_chunk;
   const int kend = min(p.K, kbeg + p.k_chunk);
   const int kiters = (kend - kbeg + BKD - 1) / BKD;
-  const int nk = kiters * p.nseg;
+  const int nk = kiters;
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -857,7 +844,7 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_bf16_kernel(const GemmArgs p) {
   block_offsets<BK_>(p.ldb, wave, lane, offb);
   const bool interior = (m0 + BM <= p.M) && (n0 + BN <= p.N);
   struct KBlk {
-    const uint16_t* a;  // operand bases of the block's segment and batch
+    const uint16_t* a;  // operand bases of the block's batch
     const uint16_t* b;
     const uint16_t* sa;  // scalar bases of the block (fast path)
     const uint16_t* sb;
@@ -866,10 +853,9 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_bf16_kernel(const GemmArgs p) {
   };
   auto kblk = [&](int it) {
     KBlk kb;
-    const int seg = it / kiters;
-    kb.k0 = kbeg + (it - seg * kiters) * BKD;
-    kb.a = p.a[seg] + (long)bi * p.sa;
-    kb.b = p.b[seg] + (long)bi * p.sb;
+    kb.k0 = kbeg + it * BKD;
+    kb.a = p.a + (long)bi * p.sa;
+    kb.b = p.b + (long)bi * p.sb;
     kb.sa = AK ? kb.a + (long)m0 * p.lda + kb.k0 : kb.a + (long)kb.k0 * p.lda + m0;
     kb.sb = BK_ ? kb.b + (long)n0 * p.ldb + kb.k0 : kb.b + (long)kb.k0 * p.ldb + n0;
     kb.fast = interior && (kb.k0 + BKD <= kend);
@@ -904,12 +890,10 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_bf16_kernel(const GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       f.a[i] = read_frag<AK>(st, wm * 128 + i * 32, ks, lane);
-      if (SQ == 1) f.a[i] = square_frag(f.a[i]);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       f.b[j] = read_frag<BK_>(st + OP_BYTES, wn * 128 + j * 32, ks, lane);
-      if (SQ == 2) f.b[j] = square_frag(f.b[j]);
     }
   };
   auto mfma_step = [&](const Frags& f) {
@@ -1005,10 +989,8 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_bf16_kernel(const GemmArgs p) {
       if (more) load_q(kb, nst, q);
       if (q < 4) {
         f0.a[q] = read_frag<AK>(rst, wm * 128 + q * 32, 0, lane);
-        if (SQ == 1) f0.a[q] = square_frag(f0.a[q]);
       } else {
         f0.b[q - 4] = read_frag<BK_>(rst + OP_BYTES, wn * 128 + (q - 4) * 32, 0, lane);
-        if (SQ == 2) f0.b[q - 4] = square_frag(f0.b[q - 4]);
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -1088,10 +1070,10 @@ __global__ void __launch_bounds__(PP_THR, 1) gemm_pp_kernel(const GemmArgs p) {
   int m0, n0, bi, si, kbeg, kend, kiters, nk;
   bool interior;
   const uint16_t* nxt;
-  int nxt_seg, nxt_k;
-  auto seg_ptr = [&](int seg) {
+  int nxt_k;
+  auto tile_ptr = [&]() {
     const int rc0 = opA ? m0 : n0;
-    const uint16_t* b = opA ? p.a[seg] + (long)bi * p.sa : p.b[seg] + (long)bi * p.sb;
+    const uint16_t* b = opA ? p.a + (long)bi * p.sa : p.b + (long)bi * p.sb;
     return b + (kmaj ? (long)rc0 * ld + kbeg : (long)kbeg * ld + rc0);
   };
   auto setup = [&](int lin) {
@@ -1104,10 +1086,9 @@ __global__ void __launch_bounds__(PP_THR, 1) gemm_pp_kernel(const GemmArgs p) {
     kbeg = si * p.k_chunk;
     kend = min(p.K, kbeg + p.k_chunk);
     kiters = (kend - kbeg + BKD - 1) / BKD;
-    nk = kiters * p.nseg;
+    nk = kiters;
     interior = (m0 + BM <= p.M) && (n0 + BN <= p.N);
-    nxt = seg_ptr(0);
-    nxt_seg = 0;
+    nxt = tile_ptr();
     nxt_k = 0;
   };
 
@@ -1120,21 +1101,17 @@ __global__ void __launch_bounds__(PP_THR, 1) gemm_pp_kernel(const GemmArgs p) {
     } else {
       const int k0 = kbeg + nxt_k * BKD;
       if (opA) {
-        const uint16_t* a = p.a[nxt_seg] + (long)bi * p.sa;
+        const uint16_t* a = p.a + (long)bi * p.sa;
 #pragma unroll
         for (int q = 0; q < 4; ++q) issue_one<AK>(a, p.lda, m0, p.M, k0, kend, st, w4 * 4 + q, lane);
       } else {
-        const uint16_t* b = p.b[nxt_seg] + (long)bi * p.sb;
+        const uint16_t* b = p.b + (long)bi * p.sb;
 #pragma unroll
         for (int q = 0; q < 4; ++q) issue_one<BK_>(b, p.ldb, n0, p.N, k0, kend, st, w4 * 4 + q, lane);
       }
     }
-    if (++nxt_k == kiters) {
-      nxt_k = 0;
-      if (++nxt_seg < p.nseg) nxt = seg_ptr(nxt_seg);
-    } else {
-      nxt += kstep;
-    }
+    ++nxt_k;
+    nxt += kstep;
   };
 
   f32x16 acc[4][2];
@@ -1248,12 +1225,12 @@ inline unsigned gemm_pp_grid(const dim3& work) {
   const unsigned total = work.x * work.y;
   return total < 256u ? total : 256u;
 }
-#define GEMM_LAUNCH(AK, BK, SQ, EPI)                                                                  \
+#define GEMM_LAUNCH(AK, BK, EPI)                                                                      \
   do {                                                                                                \
     if (gemm_pp_ok(g))                                                                                \
       hipLaunchKernelGGL((gemm_impl::gemm_pp_kernel<AK, BK, EPI>), dim3(gemm_pp_grid(grid)),              \
                          dim3(gemm_impl::PP_THR), 0, s, g);                                                 \
     else                                                                                              \
-      hipLaunchKernelGGL((gemm_impl::gemm_bf16_kernel<AK, BK, SQ, EPI>), grid, dim3(gemm_impl::NTHR), 0, \
+      hipLaunchKernelGGL((gemm_impl::gemm_bf16_kernel<AK, BK, EPI>), grid, dim3(gemm_impl::NTHR), 0,     \
                          s, g);                                                                       \
   } while (0)

@@ -94,10 +94,10 @@ double attn_pairs(long T, long w) {
 // Thread-local current model for the GEMM helpers' profiling.
 thread_local gpt_model* g_prof_model = nullptr;
 
-// MFMA work a launch executes (all K segments; a symmetric launch computes
-// only the T (T + 1) / 2 upper-triangle tiles of its T x T tile grid).
+// MFMA work a launch executes (a symmetric launch computes only the
+// T (T + 1) / 2 upper-triangle tiles of its T x T tile grid).
 inline double gemm_flops(const GemmArgs& g) {
-  double f = 2.0 * g.M * (double)g.N * g.K * g.nseg * g.batch;
+  double f = 2.0 * g.M * (double)g.N * g.K * g.batch;
   if (g.sym) {
     const double t = (g.M + 255) / 256;
     f *= (t + 1) / (2.0 * t);
@@ -389,7 +389,7 @@ hipError_t run_ns(char* ws, const NsPlan& p, int count, long xr, long xc, const 
     // A = X^T X
     GemmArgs g;
     gemm_args_init(g);
-    g.a[0] = x; g.b[0] = x;
+    g.a = x; g.b = x;
     g.M = (int)xc; g.N = (int)xc; g.K = (int)xr;
     g.lda = xc; g.ldb = xc; g.sa = xr * xc; g.sb = xr * xc;
     g.a_kmajor = 0; g.b_kmajor = 0;
@@ -401,7 +401,7 @@ hipError_t run_ns(char* ws, const NsPlan& p, int count, long xr, long xc, const 
     if (e != hipSuccess) return e;
     // B = b A + c A A (A symmetric, so A A = A A^T).
     gemm_args_init(g);
-    g.a[0] = ah; g.b[0] = ah;
+    g.a = ah; g.b = ah;
     g.M = (int)xc; g.N = (int)xc; g.K = (int)xc;
     g.lda = xc; g.ldb = xc; g.sa = xc * xc; g.sb = xc * xc;
     g.a_kmajor = 1; g.b_kmajor = 1;
@@ -419,7 +419,7 @@ hipError_t run_ns(char* ws, const NsPlan& p, int count, long xr, long xc, const 
     const bool last = it == steps - 1;
     uint16_t* xnext = first ? xh[cur] : xh[cur ^ 1];
     gemm_args_init(g);
-    g.a[0] = x; g.b[0] = bh;
+    g.a = x; g.b = bh;
     g.M = (int)xr; g.N = (int)xc; g.K = (int)xc;
     g.lda = xc; g.ldb = xc; g.sa = xr * xc; g.sb = xc * xc;
     g.a_kmajor = 1; g.b_kmajor = 1;
@@ -453,7 +453,7 @@ hipError_t gemm_nt(const uint16_t* A, long lda, const uint16_t* B, long ldb, int
                    void* C, long ldc, int epi, hipStream_t s, const void* D = nullptr, long ldd = 0) {
   GemmArgs g;
   gemm_args_init(g);
-  g.a[0] = A; g.b[0] = B;
+  g.a = A; g.b = B;
   g.M = M; g.N = N; g.K = K;
   g.lda = lda; g.ldb = ldb;
   g.a_kmajor = 1; g.b_kmajor = 1;
@@ -468,7 +468,7 @@ hipError_t gemm_nt_add_f32(const uint16_t* A, long lda, const uint16_t* B, long 
                            int K, float* C, long ldc, hipStream_t s) {
   GemmArgs g;
   gemm_args_init(g);
-  g.a[0] = A; g.b[0] = B;
+  g.a = A; g.b = B;
   g.M = M; g.N = N; g.K = K;
   g.lda = lda; g.ldb = ldb;
   g.a_kmajor = 1; g.b_kmajor = 1;
@@ -483,7 +483,7 @@ hipError_t gemm_nn(const uint16_t* A, long lda, const uint16_t* B, long ldb, int
                    void* C, long ldc, int epi, hipStream_t s, const void* D = nullptr, long ldd = 0) {
   GemmArgs g;
   gemm_args_init(g);
-  g.a[0] = A; g.b[0] = B;
+  g.a = A; g.b = B;
   g.M = M; g.N = N; g.K = K;
   g.lda = lda; g.ldb = ldb;
   g.a_kmajor = 1; g.b_kmajor = 0;
@@ -499,7 +499,7 @@ hipError_t gemm_wgrad(const uint16_t* A, long lda, const uint16_t* B, long ldb, 
   const SplitK sk = plan_splitk(M, N, K);
   GemmArgs g;
   gemm_args_init(g);
-  g.a[0] = A; g.b[0] = B;
+  g.a = A; g.b = B;
   g.M = M; g.N = N; g.K = (int)K;
   g.lda = lda; g.ldb = ldb;
   g.a_kmajor = 0; g.b_kmajor = 0;
@@ -796,7 +796,7 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
     {
       GemmArgs g;
       gemm_args_init(g);
-      g.a[0] = logits; g.b[0] = xnf + r0 * d;
+      g.a = logits; g.b = xnf + r0 * d;
       g.M = V; g.N = d; g.K = nc;
       g.lda = V; g.ldb = d;
       g.a_kmajor = 0; g.b_kmajor = 0;
@@ -1057,7 +1057,7 @@ gpt_status gpt_op_gemm(int32_t M, int32_t N, int32_t K, int32_t batch, const uin
   g_prof_model = nullptr;
   GemmArgs g;
   gemm_args_init(g);
-  g.a[0] = A; g.b[0] = B;
+  g.a = A; g.b = B;
   g.M = M; g.N = N; g.K = K;
   g.lda = lda; g.ldb = ldb; g.sa = stride_a; g.sb = stride_b;
   g.a_kmajor = a_kmajor ? 1 : 0; g.b_kmajor = b_kmajor ? 1 : 0;
