@@ -1094,9 +1094,11 @@ __global__ void __launch_bounds__(PP_THR, 1) gemm_pp_kernel(const GemmArgs p) {
 
   // This wave's 4 blocks of its group's operand of k-block it (the next one
   // in issue order).
-  auto dma_part = [&](int it) {
+  // (INT: the tile is interior, a compile-time tag inside the k-loop.)
+  auto dma_part_t = [&](int it, auto int_tag) __attribute__((always_inline)) {
+    constexpr bool INT = decltype(int_tag)::value;
     const uint32_t st = stage_l(it) + op_off;
-    if (interior) {
+    if constexpr (INT) {
       dma16_sv4(nxt, off, st + (uint32_t)(w4 * 4 * 1024));
     } else {
       const int k0 = kbeg + nxt_k * BKD;
@@ -1112,6 +1114,12 @@ __global__ void __launch_bounds__(PP_THR, 1) gemm_pp_kernel(const GemmArgs p) {
     }
     ++nxt_k;
     nxt += kstep;
+  };
+  auto dma_part = [&](int it) __attribute__((always_inline)) {
+    if (interior)
+      dma_part_t(it, std::true_type{});
+    else
+      dma_part_t(it, std::false_type{});
   };
 
   f32x16 acc[4][2];
@@ -1151,16 +1159,31 @@ __global__ void __launch_bounds__(PP_THR, 1) gemm_pp_kernel(const GemmArgs p) {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto run = [&]() {
+  // The k-loop, with the last two k-blocks (nothing left to load) peeled off
+  // and the interior test hoisted, so the loop body has no branch.
+  auto run_t = [&](auto int_tag) __attribute__((always_inline)) {
+    int j = 0;
 #pragma nounroll
-    for (int j = 0; j < nk; ++j) {
-      const bool more = j + 2 < nk;
+    for (; j + 2 < nk; ++j) {
       load_frags(j);
-      if (more) dma_part(j + 2);
-      wait_bar(more);
+      dma_part_t(j + 2, int_tag);
+      wait_bar(true);
       compute();
-      wait_bar(more);
+      wait_bar(true);
     }
+#pragma nounroll
+    for (; j < nk; ++j) {
+      load_frags(j);
+      wait_bar(false);
+      compute();
+      wait_bar(false);
+    }
+  };
+  auto run = [&]() __attribute__((always_inline)) {
+    if (interior)
+      run_t(std::true_type{});
+    else
+      run_t(std::false_type{});
   };
 
   int lin = blockIdx.x;
