@@ -363,6 +363,71 @@ __global__ void __launch_bounds__(NTHR, 2)
   }
 }
 
+// QK-norm + RoPE backward ([CT50] "1. Modelo GPT": q and k are normalised per
+// head, then rotated) on a head's gradient dy held in the accumulator layout:
+// the lane holds dims 32 dt + 8 g + 4 hl + r (element 4 g + r of a[dt]) of one
+// row, lane ^ 32 the other half, so a RoPE pair (j, j + 64) is a[dt], a[dt + 2]
+// of one lane. y = rope(norm(x)) is the saved bf16 head, given as the row
+// fragments the kernel already holds (yf[k]: dims 16 k + 8 hl .. +7), rstd its
+// saved norm scale, cs the (cos, sin) row of the position. With n = rope^-1(y),
+// dn = rope^-1(dy): dx = rstd (dn - n mean(dy y)) (the rotation keeps dot
+// products). The result replaces a; `scale` multiplies dy first.
+__device__ __forceinline__ void qknorm_rope_bwd_acc(f32x16 (&a)[4], float scale, const uint4 (&yf)[8], float rstd,
+                                                    const float* __restrict__ cs, int hl) {
+  // Dims 32 dt + 8 g + 4 hl + r sit in yf[2 dt + g / 2] of lane half g % 2,
+  // words (x, y) for hl = 0 and (z, w) for hl = 1: half of them come from the
+  // lane ^ 32, which sends the pair this lane needs.
+  // yw[dt][v / 2]: the bf16 pair of dims 32 dt + 8 g + 4 hl + 2 h + {0, 1}
+  // (v = 4 g + 2 h), kept packed to spare registers.
+  uint32_t yw[4][8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t own0 = hl ? yf[k].z : yf[k].x, own1 = hl ? yf[k].w : yf[k].y;
+    const uint32_t give0 = hl ? yf[k].x : yf[k].z, give1 = hl ? yf[k].y : yf[k].w;
+    const uint32_t got0 = (uint32_t)__shfl_xor((int)give0, 32, 64);
+    const uint32_t got1 = (uint32_t)__shfl_xor((int)give1, 32, 64);
+    const int dt = k >> 1;
+    const int w0 = 4 * (k & 1);  // g = 2 (k & 1) (lane half 0's) and g + 1 (lane half 1's)
+    yw[dt][w0 + 0] = hl ? got0 : own0;
+    yw[dt][w0 + 1] = hl ? got1 : own1;
+    yw[dt][w0 + 2] = hl ? own0 : got0;
+    yw[dt][w0 + 3] = hl ? own1 : got1;
+  }
+  float dot = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        a[dt][4 * g + r] *= scale;
+        dot += a[dt][4 * g + r] * ((r & 1) ? bf_hi(yw[dt][2 * g + (r >> 1)]) : bf_lo(yw[dt][2 * g + (r >> 1)]));
+      }
+    }
+  dot += __shfl_xor(dot, 32, 64);
+  dot *= 1.f / 128.f;
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float4* cp = reinterpret_cast<const float4*>(cs + 2 * (32 * dt + 8 * g + 4 * hl));
+      const float4 c01 = cp[0], c23 = cp[1];
+      const float cv[4] = {c01.x, c01.z, c23.x, c23.z};
+      const float sv[4] = {c01.y, c01.w, c23.y, c23.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int v = 4 * g + r;
+        const float g1 = a[dt][v], g2 = a[dt + 2][v];
+        const uint32_t w1 = yw[dt][2 * g + (r >> 1)], w2 = yw[dt + 2][2 * g + (r >> 1)];
+        const float y1 = (r & 1) ? bf_hi(w1) : bf_lo(w1), y2 = (r & 1) ? bf_hi(w2) : bf_lo(w2);
+        const float dn1 = g1 * cv[r] + g2 * sv[r], dn2 = g2 * cv[r] - g1 * sv[r];
+        const float n1 = y1 * cv[r] + y2 * sv[r], n2 = y2 * cv[r] - y1 * sv[r];
+        a[dt][v] = rstd * (dn1 - n1 * dot);
+        a[dt + 2][v] = rstd * (dn2 - n2 * dot);
+      }
+    }
+}
+
 // ===========================================================================
 // Backward: dK, dV
 // ===========================================================================
@@ -379,7 +444,8 @@ constexpr int DKDV_NST = 4;                         // stages of the Q/dO ring
 __global__ void __launch_bounds__(NTHR, 1)
     attn_bwd_dkdv_kernel(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dO,
                          const float* __restrict__ lse2, const float* __restrict__ delta,
-                         uint16_t* __restrict__ dqkv, int T, int H, int Hkv, int W) {
+                         uint16_t* __restrict__ dqkv, const float* __restrict__ rstd_qk,
+                         const float* __restrict__ cs, int T, int H, int Hkv, int W) {
   __shared__ __attribute__((aligned(1024))) char smem[DKDV_NST * DKDV_STAGE + 256];
 
   const int tid = threadIdx.x;
@@ -614,7 +680,14 @@ __global__ void __launch_bounds__(NTHR, 1)
   }
 
   if (kpos < T) {
-    const float scale = 0.08838834764831845f;
+    float scale = 0.08838834764831845f;
+    if (rstd_qk) {  // k's QK-norm + RoPE backward (wave-uniform)
+      int kp = kpos;  // opaque copy: addresses computed here, not before the loop
+      asm volatile("" : "+v"(kp));
+      const long row = (long)b * T + kp;
+      qknorm_rope_bwd_acc(dk, scale, kf, rstd_qk[row * (H + Hkv) + H + hk], cs + 2L * kp * 64, hl);
+      scale = 1.f;
+    }
     uint16_t* krow = dqkv + ((long)b * T + kpos) * ld + d + hk * HD;
     uint16_t* vrow = krow + dkv;
 #pragma unroll
@@ -638,7 +711,8 @@ __global__ void __launch_bounds__(NTHR, 1)
 __global__ void __launch_bounds__(NTHR, 2)
     attn_bwd_dq_kernel(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ o,
                        const uint16_t* __restrict__ dO, const float* __restrict__ lse2,
-                       float* __restrict__ delta, uint16_t* __restrict__ dqkv, int T, int H, int Hkv,
+                       float* __restrict__ delta, uint16_t* __restrict__ dqkv,
+                       const float* __restrict__ rstd_qk, const float* __restrict__ cs, int T, int H, int Hkv,
                        int W) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];  // [stage][K, V]
 
@@ -791,7 +865,16 @@ __global__ void __launch_bounds__(NTHR, 2)
   }
 
   if (qok) {
-    const float scale = 0.08838834764831845f;
+    float scale = 0.08838834764831845f;
+    if (rstd_qk) {  // q's QK-norm + RoPE backward (wave-uniform)
+      // An opaque copy of qpos keeps the compiler from computing these
+      // addresses before the loop (they would be live across it).
+      int qp = qpos;
+      asm volatile("" : "+v"(qp));
+      const long row = (long)b * T + qp;
+      qknorm_rope_bwd_acc(acc, scale, qf, rstd_qk[row * (H + Hkv) + h], cs + 2L * qp * 64, hl);
+      scale = 1.f;
+    }
     uint16_t* qrow = dqkv + ((long)b * T + qpos) * ld + h * HD;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -819,16 +902,17 @@ hipError_t launch_attention_fwd_window(const uint16_t* qkv, uint16_t* o, float* 
 
 hipError_t launch_attention_bwd_window(const uint16_t* qkv, const uint16_t* o, const float* lse2,
                                        const uint16_t* dO, uint16_t* dqkv, float* delta, int B, int T, int H,
-                                       int Hkv, int window, hipStream_t s) {
+                                       int Hkv, int window, hipStream_t s, const float* rstd_qk,
+                                       const float* cs) {
   if (B <= 0 || T <= 0 || H <= 0) return hipSuccess;
   if (Hkv <= 0 || H % Hkv != 0) return hipErrorInvalidValue;
   const int W = (window < 0 || window > T) ? T : window;
   // dQ first: it also writes delta = rowsum(dO * O), which dK/dV reads.
   hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((T + QB - 1) / QB, B * H), dim3(NTHR), 0, s, qkv, o, dO,
-                     lse2, delta, dqkv, T, H, Hkv, W);
+                     lse2, delta, dqkv, rstd_qk, cs, T, H, Hkv, W);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((T + KBW - 1) / KBW, B * Hkv), dim3(NTHR), 0, s, qkv,
-                     dO, lse2, delta, dqkv, T, H, Hkv, W);
+                     dO, lse2, delta, dqkv, rstd_qk, cs, T, H, Hkv, W);
   return hipGetLastError();
 }

@@ -847,9 +847,10 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
     HIP_TRY(gemm_wgrad(dxb, d, o, d, d, d, N, go, accumulate, part, s));
     {
       ProfScope ps(m, s, PROF_ATTN_BWD, 10.0 * batch * H * 128.0 * attn_pairs(T, m->windows[l]));
-      HIP_TRY(launch_attention_bwd_window(qkv, o, lse, dO, dqkv, delta, batch, T, H, Hkv, m->windows[l], s));
+      // dqkv leaves with the QK-norm + RoPE backward applied to its q and k parts.
+      HIP_TRY(launch_attention_bwd_window(qkv, o, lse, dO, dqkv, delta, batch, T, H, Hkv, m->windows[l], s,
+                                          rstdqk, cs));
     }
-    HIP_TRY(launch_qknorm_rope_bwd(dqkv, qkv, rstdqk, cs, N, T, H, Hkv, s));
     HIP_TRY(gemm_nn(dqkv, Q, wqkv, d, (int)N, d, Q, dxn, d, EPI_F32, s));
     if (m->ve_off[l] >= 0)
       HIP_TRY(launch_ve_bwd(dqkv, xn1, tokens, pbf + m->ve_off[l], pbf + m->veg_off[l], ve_logits(l),
