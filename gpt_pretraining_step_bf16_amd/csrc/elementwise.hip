@@ -501,47 +501,6 @@ __global__ void __launch_bounds__(256) qknorm_rope_fwd_kernel(uint16_t* __restri
   if (q == 0) rstd_qk[item] = r;
 }
 
-// Backward of the above. dy = d loss / d rope(norm(x)); y = rope(norm(x)) saved.
-// dn = rope^-1(dy); n = rope^-1(y); dx = rstd * (dn - n * mean(dn * n)), and
-// mean(dn * n) = mean(dy * y) because the rotation preserves dot products.
-__global__ void __launch_bounds__(256) qknorm_rope_bwd_kernel(uint16_t* __restrict__ dqkv,
-                                                             const uint16_t* __restrict__ qkv,
-                                                             const float* __restrict__ rstd_qk,
-                                                             const float* __restrict__ cs, long N, int T,
-                                                             int H, int Hkv) {
-  const int NH = H + Hkv;
-  const long item = (blockIdx.x * (long)blockDim.x + threadIdx.x) >> 3;
-  const int q = threadIdx.x & 7;
-  if (item >= N * NH) return;
-  const long row = item / NH;
-  const int hh = (int)(item - row * NH);
-  const int t = (int)(row % T);
-  const long off = row * (long)(H + 2 * Hkv) * 128 + hh * 128;
-  uint16_t* g = dqkv + off;
-  const uint16_t* y = qkv + off;
-  float g1[8], g2[8], y1[8], y2[8];
-  unpack8(*reinterpret_cast<const uint4*>(g + 8 * q), g1);
-  unpack8(*reinterpret_cast<const uint4*>(g + 64 + 8 * q), g2);
-  unpack8(*reinterpret_cast<const uint4*>(y + 8 * q), y1);
-  unpack8(*reinterpret_cast<const uint4*>(y + 64 + 8 * q), y2);
-  float dot = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) dot += g1[e] * y1[e] + g2[e] * y2[e];
-  dot = group8_sum(dot) / 128.f;
-  const float r = rstd_qk[item];
-  float c[8], sn[8], o1[8], o2[8];
-  rope8(cs, t, q, c, sn);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float dn1 = g1[e] * c[e] + g2[e] * sn[e], dn2 = -g1[e] * sn[e] + g2[e] * c[e];
-    const float n1 = y1[e] * c[e] + y2[e] * sn[e], n2 = -y1[e] * sn[e] + y2[e] * c[e];
-    o1[e] = r * (dn1 - n1 * dot);
-    o2[e] = r * (dn2 - n2 * dot);
-  }
-  *reinterpret_cast<uint4*>(g + 8 * q) = pack8(o1);
-  *reinterpret_cast<uint4*>(g + 64 + 8 * q) = pack8(o2);
-}
-
 __global__ void count_targets_kernel(const int32_t* __restrict__ tgt, long N, int V, int* counter,
                                      int* err) {
   int local = 0;
@@ -1374,13 +1333,6 @@ hipError_t launch_qknorm_rope_fwd(uint16_t* qkv, float* rstd_qk, const float* cs
   return hipGetLastError();
 }
 
-hipError_t launch_qknorm_rope_bwd(uint16_t* dqkv, const uint16_t* qkv, const float* rstd_qk,
-                                  const float* cs, long N, int T, int H, int Hkv, hipStream_t s) {
-  const long items = N * (H + Hkv);
-  hipLaunchKernelGGL(qknorm_rope_bwd_kernel, dim3((unsigned)((items * 8 + 255) / 256)), dim3(256), 0, s, dqkv,
-                     qkv, rstd_qk, cs, N, T, H, Hkv);
-  return hipGetLastError();
-}
 
 hipError_t launch_count_targets(const int32_t* tgt, long N, int V, int* counter, int* err,
                                 hipStream_t s) {

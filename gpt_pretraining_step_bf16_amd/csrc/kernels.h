@@ -40,8 +40,6 @@ hipError_t launch_rmsnorm_bwd(const float* dxn, const uint16_t* xn, const float*
 // rstd_qk is [N, H + Hkv].
 hipError_t launch_qknorm_rope_fwd(uint16_t* qkv, float* rstd_qk, const float* cs, long N, int T,
                                   int H, int Hkv, hipStream_t s);
-hipError_t launch_qknorm_rope_bwd(uint16_t* dqkv, const uint16_t* qkv, const float* rstd_qk,
-                                  const float* cs, long N, int T, int H, int Hkv, hipStream_t s);
 hipError_t launch_count_targets(const int32_t* tgt, long N, int V, int* counter, int* err,
                                 hipStream_t s);
 // Row-wise softmax cross-entropy over bf16 logits [rows, V] in place -> dz bf16,
