@@ -443,64 +443,6 @@ __global__ void rmsnorm_bwd_reg_kernel(const float* __restrict__ dxn, const uint
   }
 }
 
-// Eight lanes per (row, head): lane q of a group holds dims 8q..8q+7 and
-// 64+8q..64+8q+7, i.e. exactly its RoPE pairs (j, j+64), as two 16-byte
-// vectors; the head's sum of squares is reduced over the group's 8 lanes.
-__device__ __forceinline__ float group8_sum(float v) {
-  v += __shfl_xor(v, 1, 64);
-  v += __shfl_xor(v, 2, 64);
-  v += __shfl_xor(v, 4, 64);
-  return v;
-}
-// cos / sin of pairs 8q .. 8q+7 at position t (table rows of 64 (cos, sin)).
-__device__ __forceinline__ void rope8(const float* __restrict__ cs, int t, int q, float* c, float* sn) {
-  const float4* p = reinterpret_cast<const float4*>(cs + 2 * (t * 64 + 8 * q));
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float4 v = p[k];
-    c[2 * k] = v.x;
-    sn[2 * k] = v.y;
-    c[2 * k + 1] = v.z;
-    sn[2 * k + 1] = v.w;
-  }
-}
-
-// In-place QK-norm then RoPE on the q and k heads of qkv ([CT50] "1. Modelo
-// GPT": QK normalisation and rotary embeddings): per (token, head) of 128,
-// n = x * rstd with rstd = (mean x^2 + eps)^-1/2, then pair (j, j+64) is
-// rotated by angle t * 10000^(-j/64). rstd is saved for the backward.
-__global__ void __launch_bounds__(256) qknorm_rope_fwd_kernel(uint16_t* __restrict__ qkv,
-                                                             float* __restrict__ rstd_qk,
-                                                             const float* __restrict__ cs, long N, int T,
-                                                             int H, int Hkv) {
-  const int NH = H + Hkv;  // normalised heads per row: H q heads, then Hkv k heads
-  const long item = (blockIdx.x * (long)blockDim.x + threadIdx.x) >> 3;  // (row, head)
-  const int q = threadIdx.x & 7;
-  if (item >= N * NH) return;  // whole groups of 8 leave together
-  const long row = item / NH;
-  const int hh = (int)(item - row * NH);
-  const int t = (int)(row % T);
-  uint16_t* p = qkv + row * (long)(H + 2 * Hkv) * 128 + hh * 128;
-  float x1[8], x2[8];
-  unpack8(*reinterpret_cast<const uint4*>(p + 8 * q), x1);
-  unpack8(*reinterpret_cast<const uint4*>(p + 64 + 8 * q), x2);
-  float ss = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ss += x1[e] * x1[e] + x2[e] * x2[e];
-  const float r = rsqrtf(group8_sum(ss) / 128.f + RMS_EPS);
-  float c[8], sn[8], o1[8], o2[8];
-  rope8(cs, t, q, c, sn);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float n1 = x1[e] * r, n2 = x2[e] * r;
-    o1[e] = n1 * c[e] - n2 * sn[e];
-    o2[e] = n1 * sn[e] + n2 * c[e];
-  }
-  *reinterpret_cast<uint4*>(p + 8 * q) = pack8(o1);
-  *reinterpret_cast<uint4*>(p + 64 + 8 * q) = pack8(o2);
-  if (q == 0) rstd_qk[item] = r;
-}
-
 __global__ void count_targets_kernel(const int32_t* __restrict__ tgt, long N, int V, int* counter,
                                      int* err) {
   int local = 0;
@@ -1325,13 +1267,6 @@ hipError_t launch_rmsnorm_bwd(const float* dxn, const uint16_t* xn, const float*
   return hipGetLastError();
 }
 
-hipError_t launch_qknorm_rope_fwd(uint16_t* qkv, float* rstd_qk, const float* cs, long N, int T,
-                                  int H, int Hkv, hipStream_t s) {
-  const long items = N * (H + Hkv);
-  hipLaunchKernelGGL(qknorm_rope_fwd_kernel, dim3((unsigned)((items * 8 + 255) / 256)), dim3(256), 0, s, qkv,
-                     rstd_qk, cs, N, T, H, Hkv);
-  return hipGetLastError();
-}
 
 
 hipError_t launch_count_targets(const int32_t* tgt, long N, int V, int* counter, int* err,

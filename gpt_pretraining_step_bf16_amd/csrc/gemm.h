@@ -25,6 +25,9 @@ enum GemmEpilogue {
   EPI_H_NS_POLY = 12,   // v = alpha*acc + beta*D (D f16) -> C f16 v
   EPI_H_NS_UPDATE = 13, // v = alpha*acc + beta*D (D f16) -> C f16 v
   EPI_H_NS_LAST = 14,   // v = alpha*acc + beta*D (D f16) -> C3 f32 v (D layout)
+  // QKV projection: C bf16 = acc, with heads (128 columns) below qk_heads
+  // RMS-normalised and rotated (RoPE) per row, their norm scales to qk_rstd.
+  EPI_QKN_BF16 = 15,
 };
 
 struct GemmArgs {
@@ -49,6 +52,12 @@ struct GemmArgs {
   int k_chunk;           // K per split, multiple of 64
   long s_split;          // element stride between split partials
   int epi;
+  // EPI_QKN_BF16: rstd out [M, qk_heads]; (cos, sin) table [qk_T][64] pairs;
+  // row m is position m % qk_T.
+  float* qk_rstd;
+  const float* qk_cs;
+  int qk_T;
+  int qk_heads;
 };
 
 void gemm_args_init(GemmArgs& g);

@@ -44,7 +44,8 @@ hipError_t launch_gemm(const GemmArgs& g0, hipStream_t s) {
   const int tiles = g.sym ? tside * (tside + 1) / 2 : tside * ((g.N + 255) / 256);
   const dim3 grid(tiles, g.batch * g.splits);
   if (g.a_kmajor && g.b_kmajor) {
-    if (g.epi == EPI_BF16 || g.epi == EPI_RELU_BF16 || g.epi == EPI_RELU2_BF16 || g.epi == EPI_RESID_BF16)
+    if (g.epi == EPI_BF16 || g.epi == EPI_RELU_BF16 || g.epi == EPI_RELU2_BF16 || g.epi == EPI_RESID_BF16 ||
+        g.epi == EPI_QKN_BF16)
       return launch_gemm_kk_fwd(g, grid, s);
     return launch_gemm_kk_aux(g, grid, s);
   }

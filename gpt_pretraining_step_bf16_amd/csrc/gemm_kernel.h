@@ -546,6 +546,121 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& p, const f32x16 (
   }
 }
 
+// QKV projection epilogue with QK-norm and RoPE ([CT50] "1. Modelo GPT": q and
+// k normalised per head, then rotated): the two waves of one group that hold
+// a head's dims 0..63 and 64..127 (waves w, w ^ 1, the same 128 rows) each
+// stage their 32 x 64 block as bf16, plus every row's fp32 sum of squares
+// over its 64 columns; after a workgroup barrier each lane takes 8 columns of
+// a row from both blocks (its RoPE pairs (j, j + 64)), normalises with the
+// summed squares and rotates; a second barrier frees the staging for the
+// next block. A lane's rows within the group are lane / 8 + 8 k (k = 4 i + q),
+// so when the sequence length is a multiple of 256 (a tile never spans two
+// sequences) the (cos, sin) of its pairs advance from row to row by a
+// rotation by 8 positions (table row 8); otherwise they are read per row.
+// Heads at or past qk_heads (v) are stored as they are.
+template <bool FULL>
+__device__ __forceinline__ void store_tile_qkn(const GemmArgs& p, const f32x16 (&acc)[4][2], int m0, int n0,
+                                               int row_off, int col_off, int lane, int wave, char* smem) {
+  const int rows_left = p.M - (m0 + row_off), cols_left = p.N - (n0 + col_off);
+  // Two sets of staging regions, alternating by block, so one barrier per
+  // block suffices: a region is rewritten two blocks later, after the
+  // partner has passed the next block's barrier (its reads done).
+  constexpr int SET = 8 * 32 * STG_RS + 8 * 32 * 4;  // 8 staging blocks + row sums
+  const int r = lane & 31, hl = lane >> 5, cc = lane & 7;
+  const long ldc = p.ldc;
+  uint16_t* cb = reinterpret_cast<uint16_t*>(p.c) + (long)(m0 + row_off) * ldc + (n0 + col_off);
+  const int head = (n0 + col_off) >> 7;
+  const bool normed = head < p.qk_heads;             // wave-uniform, same for both waves of the head
+  const bool lo_half = ((col_off >> 6) & 1) == 0;    // this wave holds dims 0..63 (else 64..127)
+  const int T = p.qk_T;
+  const bool rec = (T & 255) == 0;
+  const long grow0 = (long)m0 + row_off + (lane >> 3);  // the lane's first row
+  float cv[8], sv[8], c8[8], s8[8];
+  auto load_cs = [&](long t, float (&c)[8], float (&sn)[8]) {
+    const float4* q = reinterpret_cast<const float4*>(p.qk_cs + 2 * (t * 64 + 8 * cc));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float4 v = q[k];
+      c[2 * k] = v.x;
+      sn[2 * k] = v.y;
+      c[2 * k + 1] = v.z;
+      sn[2 * k + 1] = v.w;
+    }
+  };
+  if (normed) {
+    load_cs(grow0 % T, cv, sv);
+    if (rec) load_cs(8, c8, s8);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    char* set = smem + (i & 1) * SET;
+    char* wreg = set + wave * (32 * STG_RS);
+    const char* preg = set + (wave ^ 1) * (32 * STG_RS);
+    float* part = reinterpret_cast<float*>(set + 8 * 32 * STG_RS);  // [wave][row]
+    __builtin_amdgcn_sched_barrier(0);
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = 32 * j + 8 * g + 4 * hl;
+        float o[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          o[t] = acc[i][j][4 * g + t];
+          ss += o[t] * o[t];
+        }
+        *reinterpret_cast<uint2*>(wreg + r * STG_RS + col * 2) = make_uint2(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]));
+      }
+    ss += __shfl_xor(ss, 32, 64);
+    if (hl == 0) part[wave * 32 + r] = ss;
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+#pragma nounroll
+    for (int q = 0; q < 4; ++q) {
+      const int rr = 8 * q + (lane >> 3);
+      uint4 val = *reinterpret_cast<const uint4*>(wreg + rr * STG_RS + cc * 16);
+      if (normed) {
+        const long grow = grow0 + 32 * i + 8 * q;
+        if (!rec && (i | q)) load_cs(grow % T, cv, sv);
+        const uint4 oth = *reinterpret_cast<const uint4*>(preg + rr * STG_RS + cc * 16);
+        const float rs = rsqrtf((part[wave * 32 + rr] + part[(wave ^ 1) * 32 + rr]) * (1.f / 128.f) + 1e-6f);
+        const uint32_t ow[4] = {val.x, val.y, val.z, val.w};
+        const uint32_t pw[4] = {oth.x, oth.y, oth.z, oth.w};
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float a = rs * ((e & 1) ? bf_hi(ow[e >> 1]) : bf_lo(ow[e >> 1]));  // this wave's dim
+          const float b = rs * ((e & 1) ? bf_hi(pw[e >> 1]) : bf_lo(pw[e >> 1]));  // the pair's other dim
+          // pair (x1, x2) = (dim j, dim j + 64): (x1 c - x2 s, x1 s + x2 c)
+          y[e] = lo_half ? a * cv[e] - b * sv[e] : b * sv[e] + a * cv[e];
+        }
+        val = make_uint4(pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3]), pack_bf2(y[4], y[5]), pack_bf2(y[6], y[7]));
+        if (lo_half && cc == 0 && (FULL || 32 * i + rr < rows_left))
+          p.qk_rstd[grow * p.qk_heads + head] = rs;
+        if (rec) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float cn = cv[e] * c8[e] - sv[e] * s8[e];
+            sv[e] = sv[e] * c8[e] + cv[e] * s8[e];
+            cv[e] = cn;
+          }
+        }
+      }
+      uint16_t* dst = cb + (long)(32 * i + rr) * ldc + cc * 8;
+      if (FULL || (32 * i + rr < rows_left && cc * 8 + 8 <= cols_left)) {
+        *reinterpret_cast<uint4*>(dst) = val;
+      } else if (32 * i + rr < rows_left && cc * 8 + 4 <= cols_left) {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(val.x, val.y);
+      }
+    }
+  }
+  // The caller's barrier (before the next tile's direct loads) ends the last
+  // block's reads.
+}
+static_assert(2 * (8 * 32 * STG_RS + 8 * 32 * 4) <= NST * STAGE_BYTES, "QK-norm staging must fit in the ring");
+
 // The same staging for the epilogues that read an operand: the fp32 residual
 // add (read-modify-write of fp32 C), the ReLU^2 backward (reads bf16 D) and
 // the Newton-Schulz updates (first iteration: reads fp32 X, writes fp32 X and
@@ -1208,7 +1323,12 @@ __global__ void __launch_bounds__(PP_THR, 1) gemm_pp_kernel(const GemmArgs p) {
       run();
     }
     lds_bar();  // every LDS read of this tile is done
-    if constexpr (lds_epi<EPI>()) {
+    if constexpr (EPI == EPI_QKN_BF16) {
+      if (interior)
+        store_tile_qkn<true>(p, acc, m0, n0, 128 * grp, 64 * w4, lane, wave, smem);
+      else
+        store_tile_qkn<false>(p, acc, m0, n0, 128 * grp, 64 * w4, lane, wave, smem);
+    } else if constexpr (lds_epi<EPI>()) {
       if (interior)
         store_tile_lds<EPI, true>(p, acc, bi, m0, n0, 128 * grp, 64 * w4, lane, wave, smem);
       else

@@ -767,8 +767,20 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
     if (prl) HIP_TRY(launch_resid_mix_fwd(x, x0, xprev(l), prl + l, pxl + l, Nd, s));
     if (l == m->backout_layer) HIP_TRY(hipMemcpyAsync(xbo, x, Nd * 4, hipMemcpyDeviceToDevice, s));
     HIP_TRY(launch_rmsnorm_fwd(x, xn1, rstd1, N, d, s));
-    HIP_TRY(gemm_nt(xn1, d, wqkv, d, (int)N, Q, d, qkv, Q, EPI_BF16, s));
-    HIP_TRY(launch_qknorm_rope_fwd(qkv, rstdqk, cs, N, T, H, Hkv, s));
+    {
+      // qkv = xn1 Wqkv^T with QK-norm and RoPE applied to the q and k heads in
+      // the epilogue (their norm scales to rstdqk).
+      GemmArgs g;
+      gemm_args_init(g);
+      g.a = xn1; g.b = wqkv;
+      g.M = (int)N; g.N = Q; g.K = d;
+      g.lda = d; g.ldb = d;
+      g.a_kmajor = 1; g.b_kmajor = 1;
+      g.c = qkv; g.ldc = Q;
+      g.epi = EPI_QKN_BF16;
+      g.qk_rstd = rstdqk; g.qk_cs = cs; g.qk_T = T; g.qk_heads = H + Hkv;
+      HIP_TRY(launch_gemm_prof(g, s));
+    }
     if (m->ve_off[l] >= 0)
       HIP_TRY(launch_ve_fwd(qkv, xn1, tokens, pbf + m->ve_off[l], pbf + m->veg_off[l], ve_logits(l), N, d, Hkv, V,
                             s));

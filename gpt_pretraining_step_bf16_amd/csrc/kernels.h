@@ -36,10 +36,6 @@ hipError_t launch_rmsnorm_fwd(const float* x, uint16_t* xn, float* rstd, long N,
 // dx (+)= rstd * (dxn - xn * mean(dxn * xn)); also writes dx_bf16.
 hipError_t launch_rmsnorm_bwd(const float* dxn, const uint16_t* xn, const float* rstd, float* dx,
                               uint16_t* dx_bf16, long N, int d, int accumulate, hipStream_t s);
-// QK-norm + RoPE over the H query and Hkv key heads of qkv [N, (H + 2*Hkv)*128];
-// rstd_qk is [N, H + Hkv].
-hipError_t launch_qknorm_rope_fwd(uint16_t* qkv, float* rstd_qk, const float* cs, long N, int T,
-                                  int H, int Hkv, hipStream_t s);
 hipError_t launch_count_targets(const int32_t* tgt, long N, int V, int* counter, int* err,
                                 hipStream_t s);
 // Row-wise softmax cross-entropy over bf16 logits [rows, V] in place -> dz bf16,
