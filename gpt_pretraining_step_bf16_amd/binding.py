@@ -89,6 +89,7 @@ EXPORTS = {
     "gpt_check": (C.c_int, [_P, _P, _P]),
     "gpt_status_str": (C.c_char_p, [C.c_int]),
     "gpt_op_gemm": (C.c_int, [_I, _I, _I, _I, _P, _L, _L, _I, _P, _L, _L, _I, _P, _L, _L, _I, _P]),
+    "gpt_op_qkv_projection": (C.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "gpt_op_attention_fwd": (C.c_int, [_P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "gpt_op_attention_bwd": (C.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "gpt_set_attention_windows": (C.c_int, [_P, C.POINTER(C.c_int32), _I]),
@@ -301,6 +302,12 @@ def op_gemm(M, N, K, A, lda, a_kmajor, B, ldb, b_kmajor, Cout, ldc, out_mode, ba
                            stride_b, int(b_kmajor), _ptr(Cout), ldc, stride_c, out_mode,
                            _stream(stream))
     _check(st, "gpt_op_gemm")
+
+
+def op_qkv_projection(xn, w, qkv, rstd, rope_scratch, batch, seq, d, heads, kv_heads=None, stream=None):
+    kvh = heads if kv_heads is None else int(kv_heads)
+    _check(lib().gpt_op_qkv_projection(_ptr(xn), _ptr(w), _ptr(qkv), _ptr(rstd), _ptr(rope_scratch), batch, seq,
+                                       d, heads, kvh, _stream(stream)), "gpt_op_qkv_projection")
 
 
 def op_attention_fwd(qkv, o, lse, batch, seq, heads, window=-1, kv_heads=None, stream=None):

@@ -1083,6 +1083,29 @@ gpt_status gpt_op_gemm(int32_t M, int32_t N, int32_t K, int32_t batch, const uin
   return GPT_OK;
 }
 
+gpt_status gpt_op_qkv_projection(const uint16_t* xn, const uint16_t* w, uint16_t* qkv, float* rstd,
+                                 float* rope_scratch, int32_t batch, int32_t seq, int32_t d, int32_t heads,
+                                 int32_t kv_heads, void* stream) {
+  if (!xn || !w || !qkv || !rstd || !rope_scratch || batch < 1 || seq < 1 || d < 32 || d % 32 != 0 ||
+      heads < 1 || kv_heads < 1 || heads % kv_heads != 0)
+    return GPT_EINVAL;
+  const long rows = (long)batch * seq;
+  if (rows > INT32_MAX) return GPT_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  HIP_TRY(launch_rope_table(rope_scratch, seq, s));
+  GemmArgs g;
+  gemm_args_init(g);
+  g.a = xn; g.b = w;
+  g.M = (int)rows; g.N = (heads + 2 * kv_heads) * 128; g.K = d;
+  g.lda = d; g.ldb = d;
+  g.a_kmajor = 1; g.b_kmajor = 1;
+  g.c = qkv; g.ldc = g.N;
+  g.epi = EPI_QKN_BF16;
+  g.qk_rstd = rstd; g.qk_cs = rope_scratch; g.qk_T = seq; g.qk_heads = heads + kv_heads;
+  HIP_TRY(launch_gemm_prof(g, s));
+  return GPT_OK;
+}
+
 gpt_status gpt_op_attention_fwd(const uint16_t* qkv, uint16_t* o, float* lse, int32_t batch,
                                 int32_t seq, int32_t heads, int32_t kv_heads, int32_t window, void* stream) {
   if (!qkv || !o || !lse || batch < 1 || seq < 1 || heads < 1 || window < -1) return GPT_EINVAL;

@@ -326,6 +326,21 @@ gpt_status gpt_op_gemm(int32_t M, int32_t N, int32_t K, int32_t batch, const uin
                        int64_t ldb, int64_t stride_b, int32_t b_kmajor, void* C, int64_t ldc,
                        int64_t stride_c, int32_t out_mode, void* stream);
 
+/* QKV projection with QK-norm and RoPE ([CT50] "1. Modelo GPT": q and k are
+ * RMS-normalised per head of 128, then rotated, pair (j, j+64) by angle
+ * t * 10000^(-j/64) at position t = row % seq), the step's first product of
+ * each block in one launch: qkv = xn w^T, then the q and k heads of every row
+ * normalised (eps 1e-6) and rotated, v heads as they are.
+ *   xn [batch*seq, d] bf16; w [(heads + 2*kv_heads)*128, d] bf16 (rows:
+ *   q heads, k heads, v heads); d a multiple of 32.
+ *   Writes qkv [batch*seq, (heads + 2*kv_heads)*128] bf16 and rstd
+ *   [batch*seq, heads + kv_heads] fp32 (the norm scales, for the backward).
+ *   rope_scratch: device, seq*128 floats (the (cos, sin) table is built
+ *   there). All buffers are the caller's; GPT_EINVAL on bad sizes. */
+gpt_status gpt_op_qkv_projection(const uint16_t* xn, const uint16_t* w, uint16_t* qkv, float* rstd,
+                                 float* rope_scratch, int32_t batch, int32_t seq, int32_t d, int32_t heads,
+                                 int32_t kv_heads, void* stream);
+
 /* Causal attention forward over qkv [batch*seq, 3*heads*128] bf16 (q | k | v
  * column blocks, 128 columns per head). Writes o [batch*seq, heads*128] bf16
  * and lse [batch, heads, seq] fp32: the base-2 logarithm of the softmax

@@ -147,6 +147,52 @@ def test_gemm_epilogues():
 
 
 # ----------------------------------------------------------------------------
+# QKV projection with QK-norm and RoPE in the GEMM epilogue
+# ----------------------------------------------------------------------------
+# Ragged rows (M = 400, 1.5 row tiles) and sequence lengths that are not a
+# multiple of 256 take the per-row (cos, sin) path; multiples of 256 take the
+# rotation-by-8-positions path; N not a multiple of 256 leaves half a column
+# tile empty; one case has grouped key/value heads, one the d20 shape.
+@pytest.mark.parametrize("B,T,d,H,HKV", [(2, 200, 256, 2, 2), (1, 512, 384, 3, 1), (3, 256, 128, 1, 1),
+                                         (1, 2048, 1280, 10, 10)])
+def test_qkv_projection_with_qk_norm_and_rope(B, T, d, H, HKV):
+    log(f"qkv projection B={B} T={T} d={d} heads={H} kv_heads={HKV}")
+    rng = np.random.default_rng(B * 1000 + T + d)
+    NH = H + 2 * HKV
+    xb, xf = _rand_bf16(rng, (B * T, d))
+    wb, wf = _rand_bf16(rng, (NH * 128, d), scale=d ** -0.5)
+    qkv = torch.zeros(B * T, NH * 128, dtype=torch.int16, device="cuda")
+    rstd = torch.zeros(B * T, H + HKV, dtype=torch.float32, device="cuda")
+    cs = torch.zeros(T * 128, dtype=torch.float32, device="cuda")
+    binding.op_qkv_projection(dev(torch, xb), dev(torch, wb), qkv, rstd, cs, B, T, d, H, HKV)
+    torch.cuda.synchronize()
+    got = bits_to_f32(qkv.cpu().numpy()).astype(np.float64).reshape(B, T, NH, 128)
+    got_r = rstd.cpu().numpy().reshape(B, T, H + HKV)
+    x = (xf @ wf.T).reshape(B, T, NH, 128)
+    cos, sin = oracle.rope_tables(T)
+    n, r = oracle.rms_norm(x[:, :, :H + HKV])
+    want_qk = np.stack([oracle.rope(n[b], cos, sin) for b in range(B)])
+    # Per element: the kernel rotates bf16(x) * rstd and rounds the result, so
+    # |error| <= 2^-9 (|n_j| + |n_j+64| + |out|); the bar is twice that.
+    pair = np.abs(n) + np.abs(np.concatenate([n[..., 64:], n[..., :64]], axis=-1))
+    err = np.abs(got[:, :, :H + HKV] - want_qk)
+    assert np.all(err <= 2.0 ** -8 * (pair + np.abs(want_qk)) + 1e-6), float(err.max())
+    assert rel_l2(got[:, :, :H + HKV], want_qk) < 5e-3
+    assert np.all(np.abs(got_r - r[..., 0]) <= 1e-4 * np.abs(r[..., 0]))
+    # v heads: the projection rounded once.
+    v = x[:, :, H + HKV:]
+    assert np.all(np.abs(got[:, :, H + HKV:] - v) <= 2.0 ** -8 * np.abs(v) + 1e-6)
+
+
+def test_qkv_projection_rejects_bad_shapes():
+    t = torch.zeros(64, dtype=torch.int16, device="cuda")
+    f = torch.zeros(64, dtype=torch.float32, device="cuda")
+    for args in [(1, 8, 100, 1, 1), (1, 8, 128, 3, 2), (0, 8, 128, 1, 1), (1, 8, 128, 1, 0)]:
+        with pytest.raises(binding.GptError):
+            binding.op_qkv_projection(t, t, t, f, f, *args)
+
+
+# ----------------------------------------------------------------------------
 # Attention forward / backward against the oracle (fp64 on the same bf16 inputs)
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("B,T,H,W,HKV", [(2, 200, 2, -1, 2), (1, 64, 1, -1, 1), (1, 1, 1, -1, 1),
