@@ -90,6 +90,7 @@ EXPORTS = {
     "gpt_status_str": (C.c_char_p, [C.c_int]),
     "gpt_op_gemm": (C.c_int, [_I, _I, _I, _I, _P, _L, _L, _I, _P, _L, _L, _I, _P, _L, _L, _I, _P]),
     "gpt_op_qkv_projection": (C.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "gpt_op_attention_bwd_qknorm": (C.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "gpt_op_attention_fwd": (C.c_int, [_P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "gpt_op_attention_bwd": (C.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "gpt_set_attention_windows": (C.c_int, [_P, C.POINTER(C.c_int32), _I]),
@@ -322,6 +323,15 @@ def op_attention_bwd(qkv, o, lse, dO, dqkv, scratch, batch, seq, heads, window=-
     _check(lib().gpt_op_attention_bwd(_ptr(qkv), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dqkv),
                                       _ptr(scratch), batch, seq, heads, kvh, int(window), _stream(stream)),
            "gpt_op_attention_bwd")
+
+
+def op_attention_bwd_qknorm(qkv, o, lse, dO, rstd, rope_table, dqkv, scratch, batch, seq, heads, window=-1,
+                            kv_heads=None, stream=None):
+    kvh = heads if kv_heads is None else int(kv_heads)
+    _check(lib().gpt_op_attention_bwd_qknorm(_ptr(qkv), _ptr(o), _ptr(lse), _ptr(dO), _ptr(rstd), _ptr(rope_table),
+                                             _ptr(dqkv), _ptr(scratch), batch, seq, heads, kvh, int(window),
+                                             _stream(stream)),
+           "gpt_op_attention_bwd_qknorm")
 
 
 def ns_scratch_bytes(count, rows, cols) -> int:

@@ -1126,6 +1126,19 @@ gpt_status gpt_op_attention_bwd(const uint16_t* qkv, const uint16_t* o, const fl
   return GPT_OK;
 }
 
+gpt_status gpt_op_attention_bwd_qknorm(const uint16_t* qkv, const uint16_t* o, const float* lse,
+                                       const uint16_t* dO, const float* rstd, const float* rope_table,
+                                       uint16_t* dqkv, float* scratch, int32_t batch, int32_t seq, int32_t heads,
+                                       int32_t kv_heads, int32_t window, void* stream) {
+  if (!qkv || !o || !lse || !dO || !rstd || !rope_table || !dqkv || !scratch || batch < 1 || seq < 1 ||
+      heads < 1 || window < -1)
+    return GPT_EINVAL;
+  if (kv_heads < 1 || heads % kv_heads != 0) return GPT_EINVAL;
+  HIP_TRY(launch_attention_bwd_window(qkv, o, lse, dO, dqkv, scratch, batch, seq, heads, kv_heads, window,
+                                      reinterpret_cast<hipStream_t>(stream), rstd, rope_table));
+  return GPT_OK;
+}
+
 gpt_status gpt_set_attention_windows(gpt_model* m, const int32_t* windows, int32_t n) {
   if (!m) return GPT_EINVAL;
   if (!windows) {

@@ -359,6 +359,16 @@ gpt_status gpt_op_attention_bwd(const uint16_t* qkv, const uint16_t* o, const fl
                                 const uint16_t* dO, uint16_t* dqkv, float* scratch, int32_t batch,
                                 int32_t seq, int32_t heads, int32_t kv_heads, int32_t window, void* stream);
 
+/* The same backward through QK-norm and RoPE, as the step runs it: q and k in
+ * qkv are rope(norm(x)) as gpt_op_qkv_projection wrote them, rstd its norm
+ * scales [batch*seq, heads + kv_heads] and rope_table its (cos, sin) table
+ * (seq*128 floats); the q and k parts of dqkv are then gradients w.r.t. the
+ * projections x before the norm ([CT50] "1. Modelo GPT"), v's as above. */
+gpt_status gpt_op_attention_bwd_qknorm(const uint16_t* qkv, const uint16_t* o, const float* lse,
+                                       const uint16_t* dO, const float* rstd, const float* rope_table,
+                                       uint16_t* dqkv, float* scratch, int32_t batch, int32_t seq, int32_t heads,
+                                       int32_t kv_heads, int32_t window, void* stream);
+
 /* Newton-Schulz on `count` fp32 matrices X [count, rows, cols] (rows >= cols)
  * in place: X0 = X / (||X||_F + 1e-7), then ns_steps iterations with the
  * host table ns_coeffs. scratch >= gpt_op_ns_scratch_bytes(count, rows, cols). */

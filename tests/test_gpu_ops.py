@@ -259,6 +259,49 @@ def test_attention_fwd_bwd(B, T, H, W, HKV):
                 assert rel_l2(got, ref) < 2e-2
 
 
+@pytest.mark.parametrize("B,T,H,W,HKV", [(2, 200, 2, -1, 2), (1, 512, 3, 100, 1), (1, 2048, 2, -1, 2)])
+def test_attention_bwd_through_qk_norm_and_rope(B, T, H, W, HKV):
+    """The step's attention backward, whose dQ and dK epilogues carry the
+    QK-norm + RoPE backward, against the oracle's attention backward followed
+    by rope_bwd and rms_norm_bwd, all on the GPU forward's own q, k, v (as
+    the plain attention test feeds both sides the same qkv)."""
+    log(f"attention bwd through qk-norm/rope B={B} T={T} H={H} window={W} kv_heads={HKV}")
+    rng = np.random.default_rng(7 * T + H)
+    d, dkv = H * 128, HKV * 128
+    NH = H + 2 * HKV
+    xb, _ = _rand_bf16(rng, (B * T, d))
+    # Projections of RMS ~2.5, so that rstd ~0.4 matters in the check.
+    wb, _ = _rand_bf16(rng, (NH * 128, d), scale=2.5 * d ** -0.5)
+    qkv = torch.zeros(B * T, NH * 128, dtype=torch.int16, device="cuda")
+    rstd = torch.zeros(B * T, H + HKV, dtype=torch.float32, device="cuda")
+    cs = torch.zeros(T * 128, dtype=torch.float32, device="cuda")
+    binding.op_qkv_projection(dev(torch, xb), dev(torch, wb), qkv, rstd, cs, B, T, d, H, HKV)
+    o = torch.zeros(B * T, d, dtype=torch.int16, device="cuda")
+    lse = torch.zeros(B * H * T, dtype=torch.float32, device="cuda")
+    binding.op_attention_fwd(qkv, o, lse, B, T, H, W, kv_heads=HKV)
+    do_b, do_f = _rand_bf16(rng, (B * T, d))
+    dqkv = torch.zeros_like(qkv)
+    scratch = torch.zeros(B * H * T, dtype=torch.float32, device="cuda")
+    binding.op_attention_bwd_qknorm(qkv, o, lse, dev(torch, do_b), rstd, cs, dqkv, scratch, B, T, H, W,
+                                    kv_heads=HKV)
+    torch.cuda.synchronize()
+    y = bits_to_f32(qkv.cpu().numpy()).astype(np.float64).reshape(B, T, NH, 128)
+    r = rstd.cpu().numpy().astype(np.float64).reshape(B, T, H + HKV, 1)
+    got = bits_to_f32(dqkv.cpu().numpy()).astype(np.float64).reshape(B, T, NH, 128)
+    cos, sin = oracle.rope_tables(T)
+    for b in range(B):
+        q, k, v = y[b, :, :H], y[b, :, H:H + HKV], y[b, :, H + HKV:]
+        _, p = oracle.causal_attention(q, k, v, None if W < 0 else W)
+        dq, dk, dv = oracle.causal_attention_bwd(do_f[b * T:(b + 1) * T].reshape(T, H, 128), q, k, v, p)
+        # Back through the rotation, then the norm (n = the unrotated saved head).
+        dx = [oracle.rms_norm_bwd(oracle.rope_bwd(g, cos, sin), oracle.rope_bwd(yy, cos, sin), rr)
+              for g, yy, rr in ((dq, q, r[b, :, :H]), (dk, k, r[b, :, H:]))]
+        errs = (rel_l2(got[b, :, :H], dx[0]), rel_l2(got[b, :, H:H + HKV], dx[1]),
+                rel_l2(got[b, :, H + HKV:], dv))
+        log(f"  rel-L2 dq {errs[0]:.2e} dk {errs[1]:.2e} dv {errs[2]:.2e}")
+        assert max(errs) < 1e-2  # measured 2.2e-3 to 2.7e-3
+
+
 # ----------------------------------------------------------------------------
 # Newton-Schulz against the oracle iteration
 # ----------------------------------------------------------------------------
