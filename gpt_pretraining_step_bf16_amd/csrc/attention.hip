@@ -600,15 +600,16 @@ __global__ void __launch_bounds__(NTHR, 1)
   // and the MFMAs run while the VALU work issues (8.8% off the backward at
   // d20 against the softmax as one block). The last tile computes a
   // throw-away S / dP of the stage after it.
-  auto softmax_sdp = [&](int n, int st, int t, f32x16& s, f32x16& dp, bf16x8 (&pf)[2],
-                         bf16x8 (&dsf)[2], int st2, int t2, f32x16& s2, f32x16& dp2) {
+  // MASK (a compile-time tag): whether any (query, key) pair of the half is
+  // outside the causal band or past T; halves wholly inside skip the test.
+  auto softmax_sdp = [&](auto mask_tag, int n, int st, int t, f32x16& s, f32x16& dp, bf16x8 (&pf)[2],
+                         bf16x8 (&dsf)[2], int st2, int t2, f32x16& s2, f32x16& dp2)
+                         __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const float* ls = reinterpret_cast<const float*>(stage(st) + 2 * TILE);
     const float* ds = ls + QBW;
     const int qb = qb_first + n % nqt;
-    const bool need_mask = (qb * QBW + 32 * t < k0 + 31) || (qb * QBW + 32 * t + 32 > T) ||
-                           (qb * QBW + 32 * t + 31 > k0 + W);
-    // Branch-free: with no mask needed the bound admits every offset.
-    const uint32_t lim = need_mask ? (uint32_t)qlim : 0xffffffffu;
+    const uint32_t lim = (uint32_t)qlim;
     float lq[16], dq[16];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -622,7 +623,7 @@ __global__ void __launch_bounds__(NTHR, 1)
     auto one = [&](int v) {
       // s[v]: query qb*64 + 32t + 8(v/4) + 4hl + v%4, key kpos.
       float p = fast_exp2(fmaf(s[v], sc, -lq[v]));
-      p = (uint32_t)(qrow + 8 * (v >> 2) + (v & 3)) > lim ? 0.f : p;
+      if constexpr (MASK) p = (uint32_t)(qrow + 8 * (v >> 2) + (v & 3)) > lim ? 0.f : p;
       s[v] = p;
       dp[v] = p * (dp[v] - dq[v]);
     };
@@ -673,9 +674,21 @@ __global__ void __launch_bounds__(NTHR, 1)
     if (n > 0) VMCNT_BARRIER(0);  // tile n+1 is in LDS; every wave is past tile n-1
     if (n + 2 < ntile) issue(n + 2, (n + 2) & (DKDV_NST - 1));
     bf16x8 pf[2], dsf[2];
-    softmax_sdp(n, st, 0, sa, da, pf, dsf, st, 1, sb, db);
+    // Half t of tile n needs the mask when a pair of it is outside the band.
+    auto need_mask = [&](int t) {
+      const int q0 = (qb_first + n % nqt) * QBW + 32 * t;
+      return (q0 < k0 + 31) || (q0 + 32 > T) || (q0 + 31 > k0 + W);
+    };
+    auto half = [&](int t, f32x16& s, f32x16& dp, int st2, int t2, f32x16& s2, f32x16& dp2)
+        __attribute__((always_inline)) {
+      if (need_mask(t))
+        softmax_sdp(std::true_type{}, n, st, t, s, dp, pf, dsf, st2, t2, s2, dp2);
+      else
+        softmax_sdp(std::false_type{}, n, st, t, s, dp, pf, dsf, st2, t2, s2, dp2);
+    };
+    half(0, sa, da, st, 1, sb, db);
     dvdk(st, 0, pf, dsf);
-    softmax_sdp(n, st, 1, sb, db, pf, dsf, (n + 1) & (DKDV_NST - 1), 0, sa, da);
+    half(1, sb, db, (n + 1) & (DKDV_NST - 1), 0, sa, da);
     dvdk(st, 1, pf, dsf);
   }
 
