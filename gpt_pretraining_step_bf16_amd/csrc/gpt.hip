@@ -51,11 +51,20 @@ struct gpt_model {
   bool prof_on = false;
   std::vector<ProfSlot> prof;
   size_t prof_used = 0;
+  // Second stream (default priority) on which the Muon step runs its second
+  // matrix group beside the first, with fork / join events; made on first
+  // use, for the device current then (aux_dev).
+  hipStream_t aux = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  int aux_dev = -1;
   ~gpt_model() {
     for (auto& s : prof) {
       if (s.start) (void)hipEventDestroy(s.start);
       if (s.stop) (void)hipEventDestroy(s.stop);
     }
+    if (ev_fork) (void)hipEventDestroy(ev_fork);
+    if (ev_join) (void)hipEventDestroy(ev_join);
+    if (aux) (void)hipStreamDestroy(aux);
   }
 };
 
@@ -890,20 +899,44 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
   return GPT_OK;
 }
 
-// NorMuon scratch after the Newton-Schulz buffers: per X row of the larger
-// group, the scale and the two norm terms.
+// Each Muon group has Newton-Schulz buffers of its own (the groups run on two
+// streams at once), one after the other; then the NorMuon scratch: per X row
+// of each group, the scale and the two norm terms.
+static size_t ns_region_end(const MuonGroup& g, size_t base) {
+  return (plan_ns(g.count, g.x_rows, g.x_cols, base).total + 255) / 256 * 256;
+}
 static size_t ns_workspace_bytes(const gpt_model& m, size_t* normuon_off) {
   MuonGroup groups[kMaxMuonGroups];
   const int ng = muon_groups(m, groups);
-  size_t ns = 0, rows = 0;
+  size_t off = 0, rows = 0;
   for (int i = 0; i < ng; ++i) {
-    const MuonGroup& g = groups[i];
-    ns = std::max(ns, plan_ns(g.count, g.x_rows, g.x_cols, 0).total);
-    rows = std::max(rows, (size_t)g.count * g.x_rows);
+    off = ns_region_end(groups[i], off);
+    rows += (size_t)groups[i].count * groups[i].x_rows;
   }
-  const size_t off = (ns + 255) / 256 * 256;
   if (normuon_off) *normuon_off = off;
   return off + (3 * rows * 4 + 255) / 256 * 256;
+}
+
+// The second stream and its events, for the current device (false: none,
+// the groups then run one after the other on the caller's stream).
+static bool aux_stream(gpt_model* m) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  if (m->aux) return m->aux_dev == dev;
+  if (hipStreamCreateWithFlags(&m->aux, hipStreamNonBlocking) != hipSuccess) {
+    m->aux = nullptr;
+    return false;
+  }
+  if (hipEventCreateWithFlags(&m->ev_fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&m->ev_join, hipEventDisableTiming) != hipSuccess) {
+    if (m->ev_fork) (void)hipEventDestroy(m->ev_fork);
+    (void)hipStreamDestroy(m->aux);
+    m->aux = nullptr;
+    m->ev_fork = m->ev_join = nullptr;
+    return false;
+  }
+  m->aux_dev = dev;
+  return true;
 }
 
 size_t muon_workspace_bytes(const gpt_model* m) {
@@ -963,26 +996,51 @@ static gpt_status muon_impl(gpt_model* m, float* params, uint16_t* params_bf16, 
   g_prof_model = m;
   MuonGroup groups[kMaxMuonGroups];
   const int ng = muon_groups(*m, groups);
-  float* state = second_moment;
-  for (int gi = 0; gi < ng; ++gi) {
+  // One group's chain: momentum, X0, Newton-Schulz, (NorMuon,) update, in its
+  // own workspace region and stream.
+  auto run_group = [&](int gi, size_t base, float* rs, float* state, hipStream_t sg) -> gpt_status {
     const MuonGroup& g = groups[gi];
-    const NsPlan p = plan_ns(g.count, g.x_rows, g.x_cols, 0);
+    const NsPlan p = plan_ns(g.count, g.x_rows, g.x_cols, base);
     float* part = reinterpret_cast<float*>(ws + p.part);
     float* x32 = reinterpret_cast<float*>(ws + p.x32);
-    HIP_TRY(launch_muon_momentum(g, grads, momentum, momentum_coef, part, p.nb, s));
-    HIP_TRY(launch_muon_pack(g, momentum, part, p.nb, x32, reinterpret_cast<uint16_t*>(ws + p.xb), s));
-    HIP_TRY(run_ns(ws, p, g.count, g.x_rows, g.x_cols, ns_coeffs, ns_steps, s));
+    HIP_TRY(launch_muon_momentum(g, grads, momentum, momentum_coef, part, p.nb, sg));
+    HIP_TRY(launch_muon_pack(g, momentum, part, p.nb, x32, reinterpret_cast<uint16_t*>(ws + p.xb), sg));
+    HIP_TRY(run_ns(ws, p, g.count, g.x_rows, g.x_cols, ns_coeffs, ns_steps, sg));
     if (state) {
       const long rows = (long)g.count * g.x_rows;
-      float* rs = reinterpret_cast<float*>(ws + nm_off);
-      HIP_TRY(launch_normuon(g, x32, state, beta2, rs, rs + rows, s));
-      HIP_TRY(launch_muon_update_scaled(g, x32, params, params_bf16, lr, rs, s));
-      state += rows;
+      HIP_TRY(launch_normuon(g, x32, state, beta2, rs, rs + rows, sg));
+      HIP_TRY(launch_muon_update_scaled(g, x32, params, params_bf16, lr, rs, sg));
     } else {
-      HIP_TRY(launch_muon_update(g, x32, params, params_bf16, lr, s));
+      HIP_TRY(launch_muon_update(g, x32, params, params_bf16, lr, sg));
     }
+    return GPT_OK;
+  };
+  // Group 0 on the caller's stream, the others on the second stream after a
+  // fork; the caller's stream then waits for them (joined on every path).
+  // With launch timing on, the groups run one after the other so that each
+  // launch's events time it alone.
+  const bool two = ng > 1 && !m->prof_on && aux_stream(m);
+  if (two) {
+    HIP_TRY(hipEventRecord(m->ev_fork, s));
+    HIP_TRY(hipStreamWaitEvent(m->aux, m->ev_fork, 0));
   }
-  return GPT_OK;
+  gpt_status st = GPT_OK;
+  size_t base = 0;
+  float* rs = reinterpret_cast<float*>(ws + nm_off);
+  float* state = second_moment;
+  for (int gi = 0; gi < ng && st == GPT_OK; ++gi) {
+    st = run_group(gi, base, rs, state, (two && gi > 0) ? m->aux : s);
+    const long rows = (long)groups[gi].count * groups[gi].x_rows;
+    base = ns_region_end(groups[gi], base);
+    rs += 3 * rows;
+    if (state) state += rows;
+  }
+  if (two) {
+    const hipError_t e1 = hipEventRecord(m->ev_join, m->aux);
+    const hipError_t e2 = e1 == hipSuccess ? hipStreamWaitEvent(s, m->ev_join, 0) : e1;
+    if (st == GPT_OK && e2 != hipSuccess) st = hip_status(e2);
+  }
+  return st;
 }
 
 gpt_status muon_step(gpt_model* m, float* params, uint16_t* params_bf16, const float* grads,

@@ -178,7 +178,8 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* params_bf16, const int32_t*
                        float* grads, int32_t accumulate, void* workspace,
                        size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace muon_step and normuon_step need. */
+/* Bytes of device workspace muon_step and normuon_step need (each matrix
+ * group has its own Newton-Schulz buffers: the groups run concurrently). */
 size_t muon_workspace_bytes(const gpt_model* m);
 
 /*
@@ -200,6 +201,12 @@ size_t muon_workspace_bytes(const gpt_model* m);
  * fp16 between iterations and the last one writes it in fp32, which keeps the
  * result within about 2e-3 (Gaussian inputs at the block shapes) to 8e-3
  * (small Gaussian matrices) relative L2 of the fp64 iteration.
+ * The matrix groups (attention, MLP) run side by side: the first on `stream`,
+ * the others on a second stream of the model's (default priority, made on
+ * the first call for the device current then) after an event recorded on
+ * `stream`; `stream` then waits on an event recorded after them, so work
+ * queued on `stream` afterwards sees the whole update. With launch timing
+ * on (gpt_profile_enable) the groups run one after the other on `stream`.
  */
 gpt_status muon_step(gpt_model* m, float* params, uint16_t* params_bf16, const float* grads,
                      float* momentum, float lr, float momentum_coef, const float* ns_coeffs,
