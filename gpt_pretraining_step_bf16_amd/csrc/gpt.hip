@@ -56,6 +56,7 @@ struct gpt_model {
   // use, for the device current then (aux_dev).
   hipStream_t aux = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  hipEvent_t ev_slot[8] = {};  // weight-gradient partials: 4 GEMM done, 4 reduction done
   int aux_dev = -1;
   ~gpt_model() {
     for (auto& s : prof) {
@@ -64,6 +65,8 @@ struct gpt_model {
     }
     if (ev_fork) (void)hipEventDestroy(ev_fork);
     if (ev_join) (void)hipEventDestroy(ev_join);
+    for (hipEvent_t e : ev_slot)
+      if (e) (void)hipEventDestroy(e);
     if (aux) (void)hipStreamDestroy(aux);
   }
 };
@@ -265,8 +268,10 @@ FwdPlan plan_fwd(const gpt_model& m, int B, int T) {
     const SplitK s = plan_splitk(sh[0], sh[1], N);
     if (s.splits > 1) part = std::max(part, (size_t)s.splits * sh[0] * sh[1] * 4);
   }
-  p.part_bytes = part;
-  p.part = c.take(std::max<size_t>(part, 256));
+  // One partials slot per weight gradient of a block (their reductions may
+  // still run on the second stream when the next one's GEMM starts).
+  p.part_bytes = (std::max<size_t>(part, 256) + 255) / 256 * 256;
+  p.part = c.take(4 * p.part_bytes);
   p.total = c.cur;
   return p;
 }
@@ -503,8 +508,52 @@ hipError_t gemm_nn(const uint16_t* A, long lda, const uint16_t* B, long ldb, int
 }
 
 // Weight gradient: G[M,N] (+)= sum_t A[t][m] * B[t][n], A stored [K][M], B [K][N].
+// The second stream and its events, for the current device (false: none,
+// the groups then run one after the other on the caller's stream).
+bool aux_stream(gpt_model* m) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  if (m->aux) return m->aux_dev == dev;
+  if (hipStreamCreateWithFlags(&m->aux, hipStreamNonBlocking) != hipSuccess) {
+    m->aux = nullptr;
+    return false;
+  }
+  bool ok = hipEventCreateWithFlags(&m->ev_fork, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&m->ev_join, hipEventDisableTiming) == hipSuccess;
+  for (hipEvent_t& e : m->ev_slot) ok = ok && hipEventCreateWithFlags(&e, hipEventDisableTiming) == hipSuccess;
+  if (!ok) {
+    if (m->ev_fork) (void)hipEventDestroy(m->ev_fork);
+    if (m->ev_join) (void)hipEventDestroy(m->ev_join);
+    for (hipEvent_t& e : m->ev_slot) {
+      if (e) (void)hipEventDestroy(e);
+      e = nullptr;
+    }
+    (void)hipStreamDestroy(m->aux);
+    m->aux = nullptr;
+    m->ev_fork = m->ev_join = nullptr;
+    return false;
+  }
+  m->aux_dev = dev;
+  return true;
+}
+
+// Split-K reductions of the weight gradients on the second stream. Each of a
+// block's four weight gradients has its own partials slot; its reduction
+// waits on an event recorded after the GEMM and runs beside the main
+// stream's next kernels (the attention backward leaves registers and LDS for
+// it), and the next GEMM into the same slot waits for it. The caller joins
+// the second stream before it returns.
+struct SideReduce {
+  hipStream_t side = nullptr;
+  hipEvent_t* gemm_done = nullptr;  // [4]
+  hipEvent_t* red_done = nullptr;   // [4]
+  bool used[4] = {};
+  bool any = false;
+};
+
 hipError_t gemm_wgrad(const uint16_t* A, long lda, const uint16_t* B, long ldb, int M, int N, long K,
-                      float* G, int accumulate, float* part, hipStream_t s) {
+                      float* G, int accumulate, float* part, hipStream_t s, SideReduce* side = nullptr,
+                      int slot = 0) {
   const SplitK sk = plan_splitk(M, N, K);
   GemmArgs g;
   gemm_args_init(g);
@@ -517,9 +566,20 @@ hipError_t gemm_wgrad(const uint16_t* A, long lda, const uint16_t* B, long ldb, 
     g.splits = sk.splits; g.k_chunk = sk.k_chunk;
     g.s_split = (long)M * N;
     g.epi = EPI_SPLITK;
-    hipError_t e = launch_gemm_prof(g, s);
-    if (e != hipSuccess) return e;
-    return launch_splitk_reduce(part, (long)M * N, sk.splits, G, (long)M * N, accumulate, s);
+    hipError_t e = hipSuccess;
+    if (side && side->used[slot]) e = hipStreamWaitEvent(s, side->red_done[slot], 0);
+    if (e == hipSuccess) e = launch_gemm_prof(g, s);
+    if (e != hipSuccess || !side) {
+      return e != hipSuccess ? e : launch_splitk_reduce(part, (long)M * N, sk.splits, G, (long)M * N, accumulate, s);
+    }
+    side->any = true;
+    e = hipEventRecord(side->gemm_done[slot], s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side->side, side->gemm_done[slot], 0);
+    if (e == hipSuccess)
+      e = launch_splitk_reduce(part, (long)M * N, sk.splits, G, (long)M * N, accumulate, side->side);
+    if (e == hipSuccess) e = hipEventRecord(side->red_done[slot], side->side);
+    side->used[slot] = true;
+    return e;
   }
   g.c = G; g.ldc = N;
   g.epi = EPI_F32_ACC;
@@ -728,7 +788,26 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
   uint16_t* dqkv = reinterpret_cast<uint16_t*>(ws + p.dqkv);
   uint16_t* logits = reinterpret_cast<uint16_t*>(ws + p.logits);
   float* loss_rows = reinterpret_cast<float*>(ws + p.loss_rows);
-  float* part = reinterpret_cast<float*>(ws + p.part);
+  auto part_slot = [&](int k) { return reinterpret_cast<float*>(ws + p.part + (size_t)k * p.part_bytes); };
+  // Weight-gradient reductions on the second stream (not while launch timing
+  // is on, so that each GEMM launch is timed alone); joined on every return.
+  SideReduce side_r;
+  SideReduce* side = nullptr;
+  if (!m->prof_on && aux_stream(m)) {
+    side_r.side = m->aux;
+    side_r.gemm_done = m->ev_slot;
+    side_r.red_done = m->ev_slot + 4;
+    side = &side_r;
+  }
+  struct JoinSide {
+    gpt_model* m;
+    SideReduce* side;
+    hipStream_t s;
+    ~JoinSide() {
+      if (side && side->any && hipEventRecord(m->ev_join, m->aux) == hipSuccess)
+        (void)hipStreamWaitEvent(s, m->ev_join, 0);
+    }
+  } join_side{m, side, s};
   const uint16_t* wte = pbf + m->off_wte;
   const uint16_t* wlm = pbf + m->off_lm;
 
@@ -859,13 +938,13 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
     const uint16_t* r = reinterpret_cast<const uint16_t*>(lay(p.r, l));
     // MLP: x_out = x_mid + relu(u)^2 Wproj^T
     HIP_TRY(gemm_nn(dxb, d, wproj, F, (int)N, F, d, du, F, EPI_DRELU2_BF16, s, r, F));
-    HIP_TRY(gemm_wgrad(dxb, d, r, F, d, F, N, gproj, accumulate, part, s));
+    HIP_TRY(gemm_wgrad(dxb, d, r, F, d, F, N, gproj, accumulate, part_slot(0), s, side, 0));
     HIP_TRY(gemm_nn(du, F, wfc, d, (int)N, d, F, dxn, d, EPI_F32, s));
-    HIP_TRY(gemm_wgrad(du, F, xn2, d, F, d, N, gfc, accumulate, part, s));
+    HIP_TRY(gemm_wgrad(du, F, xn2, d, F, d, N, gfc, accumulate, part_slot(1), s, side, 1));
     HIP_TRY(launch_rmsnorm_bwd(dxn, xn2, rstd2, dx, dxb, N, d, 1, s));
     // Attention: x_mid = x_in + o Wo^T
     HIP_TRY(gemm_nn(dxb, d, wo, d, (int)N, d, d, dO, d, EPI_BF16, s));
-    HIP_TRY(gemm_wgrad(dxb, d, o, d, d, d, N, go, accumulate, part, s));
+    HIP_TRY(gemm_wgrad(dxb, d, o, d, d, d, N, go, accumulate, part_slot(2), s, side, 2));
     {
       ProfScope ps(m, s, PROF_ATTN_BWD, 10.0 * batch * H * 128.0 * attn_pairs(T, m->windows[l]));
       // dqkv leaves with the QK-norm + RoPE backward applied to its q and k parts.
@@ -878,7 +957,7 @@ gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* pbf, const int32_t* tokens,
                             grads + m->ve_off[l], reinterpret_cast<float*>(ws + p.vedl),
                             reinterpret_cast<float*>(ws + p.vered), grads + m->veg_off[l], dxn, N, d, Hkv, V,
                             accumulate, scw, s));
-    HIP_TRY(gemm_wgrad(dqkv, Q, xn1, d, Q, d, N, gqkv, accumulate, part, s));
+    HIP_TRY(gemm_wgrad(dqkv, Q, xn1, d, Q, d, N, gqkv, accumulate, part_slot(3), s, side, 3));
     HIP_TRY(launch_rmsnorm_bwd(dxn, xn1, rstd1, dx, dxb, N, d, 1, s));
     // dx is now the gradient of the stream entering block l.
     if (l == m->backout_layer) HIP_TRY(launch_backout_add(dx, dxb, dback, pbl, Nd, s));
@@ -917,27 +996,6 @@ static size_t ns_workspace_bytes(const gpt_model& m, size_t* normuon_off) {
   return off + (3 * rows * 4 + 255) / 256 * 256;
 }
 
-// The second stream and its events, for the current device (false: none,
-// the groups then run one after the other on the caller's stream).
-static bool aux_stream(gpt_model* m) {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess) return false;
-  if (m->aux) return m->aux_dev == dev;
-  if (hipStreamCreateWithFlags(&m->aux, hipStreamNonBlocking) != hipSuccess) {
-    m->aux = nullptr;
-    return false;
-  }
-  if (hipEventCreateWithFlags(&m->ev_fork, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&m->ev_join, hipEventDisableTiming) != hipSuccess) {
-    if (m->ev_fork) (void)hipEventDestroy(m->ev_fork);
-    (void)hipStreamDestroy(m->aux);
-    m->aux = nullptr;
-    m->ev_fork = m->ev_join = nullptr;
-    return false;
-  }
-  m->aux_dev = dev;
-  return true;
-}
 
 size_t muon_workspace_bytes(const gpt_model* m) {
   if (!m) return 0;
