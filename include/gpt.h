@@ -172,6 +172,10 @@ size_t gpt_workspace_bytes(const gpt_model* m, int32_t batch, int32_t seq);
  * Every sum runs in a fixed order (no floating-point atomics), so repeated
  * calls on the same inputs give the same bits; the embedding and
  * value-embedding rows of ids absent from the batch get exact zeros.
+ * The weight gradients' split-K reductions run on the model's second stream
+ * (as in muon_step; not while launch timing is on); `stream` waits on it
+ * before the call returns, so work queued on `stream` afterwards sees every
+ * gradient.
  */
 gpt_status gpt_fwd_bwd(gpt_model* m, const uint16_t* params_bf16, const int32_t* tokens,
                        const int32_t* targets, int32_t batch, int32_t seq, float* loss,
