@@ -552,6 +552,8 @@ __device__ __forceinline__ long muon_mat_offset(const MuonGroup& g, int j) {
 }
 
 // M <- mu M + G over matrix blockIdx.y; partial sum of squares of the new M.
+// A thread walks its float4s with stride gridDim.x * 256, four at a time
+// (their loads issued together); the sum of squares keeps the walk's order.
 __global__ void muon_momentum_kernel(const MuonGroup g, const float* __restrict__ grads,
                                      float* __restrict__ mom, float mu, float* __restrict__ partials) {
   __shared__ float red[4];
@@ -560,17 +562,28 @@ __global__ void muon_momentum_kernel(const MuonGroup g, const float* __restrict_
   const long n4 = (long)g.rows * g.cols / 4;
   const float4* gp = reinterpret_cast<const float4*>(grads + off);
   float4* mp = reinterpret_cast<float4*>(mom + off);
+  const long stride = (long)gridDim.x * blockDim.x;
   float ss = 0.f;
-  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n4; i += (long)gridDim.x * blockDim.x) {
-    float4 m = mp[i];
-    const float4 gv = gp[i];
+  auto step = [&](float4 m, const float4 gv, long i) {
     m.x = mu * m.x + gv.x;
     m.y = mu * m.y + gv.y;
     m.z = mu * m.z + gv.z;
     m.w = mu * m.w + gv.w;
     mp[i] = m;
     ss += m.x * m.x + m.y * m.y + m.z * m.z + m.w * m.w;
+  };
+  long i = blockIdx.x * (long)blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n4; i += 4 * stride) {
+    float4 m[4], gv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      m[u] = mp[i + u * stride];
+      gv[u] = gp[i + u * stride];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) step(m[u], gv[u], i + u * stride);
   }
+  for (; i < n4; i += stride) step(mp[i], gp[i], i);
   ss = warp_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
@@ -597,13 +610,15 @@ __device__ __forceinline__ void x0_store4(const float (&v)[4], float* x32, uint1
 
 // X = M / (||M||_F + 1e-7) in the tall orientation, as fp32 and bf16.
 // X is [x_rows, x_cols]. A matrix flagged in transposed_mask is stored wide,
-// as [x_cols, x_rows]; it is transposed through a 32x33 LDS tile.
-// Grid: (x_cols / 32, x_rows / 32, count); 256 threads, one float4 each:
-// thread t covers row t / 8 and columns 4 (t % 8) .. +3 of the 32x32 tile.
+// as [x_cols, x_rows]; it is transposed through 32x33 LDS tiles.
+// Grid: (ceil(x_cols / 128), x_rows / 32, count); 256 threads. A workgroup
+// covers 32 rows and up to four 32-column tiles of X; thread t covers row
+// t / 8 and columns 4 (t % 8) .. +3 of each tile, its four loads issued
+// together.
 __global__ void muon_pack_kernel(const MuonGroup g, const float* __restrict__ mom,
                                  const float* __restrict__ partials, int nb, float* __restrict__ x32,
                                  uint16_t* __restrict__ xb) {
-  __shared__ float tile[32][33];
+  __shared__ float tile[4][32][33];
   const int j = blockIdx.z;
   const long off = muon_mat_offset(g, j);
   const int k = j % g.per_layer;
@@ -614,32 +629,50 @@ __global__ void muon_pack_kernel(const MuonGroup g, const float* __restrict__ mo
   const float* src = mom + off;
   const int q = threadIdx.x & 7;   // float4 column group
   const int ry = threadIdx.x >> 3;  // 0..31
-  const long r0 = blockIdx.y * 32L, c0 = blockIdx.x * 32L;  // X tile origin
-  const long idx = (r0 + ry) * xc + c0 + 4 * q;
-  float v[4];
+  const long r0 = blockIdx.y * 32L, c0 = blockIdx.x * 128L;  // X block origin
+  const int nsub = (int)min(4L, (xc - c0) / 32);               // workgroup-uniform
+  float4 m[4];
   if (!tr) {
-    const float4 m = *reinterpret_cast<const float4*>(src + idx);
-    v[0] = m.x * inv; v[1] = m.y * inv; v[2] = m.z * inv; v[3] = m.w * inv;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if (t < nsub) m[t] = *reinterpret_cast<const float4*>(src + (r0 + ry) * xc + c0 + 32 * t + 4 * q);
   } else {
     // Stored M[c][r] = X[r][c]; stored rows have x_rows elements. Thread
-    // (ry, q) loads stored row c0 + ry, X rows r0 + 4q .. +3.
-    const float4 m = *reinterpret_cast<const float4*>(src + (c0 + ry) * xr + r0 + 4 * q);
-    tile[ry][4 * q] = m.x; tile[ry][4 * q + 1] = m.y; tile[ry][4 * q + 2] = m.z; tile[ry][4 * q + 3] = m.w;
+    // (ry, q) loads stored row c0 + 32 t + ry, X rows r0 + 4q .. +3.
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if (t < nsub) m[t] = *reinterpret_cast<const float4*>(src + (c0 + 32 * t + ry) * xr + r0 + 4 * q);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if (t < nsub) {
+        tile[t][ry][4 * q] = m[t].x;
+        tile[t][ry][4 * q + 1] = m[t].y;
+        tile[t][ry][4 * q + 2] = m[t].z;
+        tile[t][ry][4 * q + 3] = m[t].w;
+      }
     __syncthreads();
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = tile[4 * q + e][ry] * inv;
+    for (int t = 0; t < 4; ++t)
+      if (t < nsub) m[t] = make_float4(tile[t][4 * q][ry], tile[t][4 * q + 1][ry], tile[t][4 * q + 2][ry],
+                                       tile[t][4 * q + 3][ry]);
   }
-  x0_store4(v, x32 + xoff, xb + xoff, idx);
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    if (t < nsub) {
+      const float v[4] = {m[t].x * inv, m[t].y * inv, m[t].z * inv, m[t].w * inv};
+      x0_store4(v, x32 + xoff, xb + xoff, (r0 + ry) * xc + c0 + 32 * t + 4 * q);
+    }
 }
 
 // W <- W - lr * sqrt(max(1, rows/cols)) * X in the stored orientation (rows =
 // fan-out of the stored matrix); refresh bf16. With row_scale (NorMuon), row r
-// of X is first multiplied by row_scale[j * x_rows + r]. Grid as
-// muon_pack_kernel, one float4 of the stored matrix per thread.
+// of X is first multiplied by row_scale[j * x_rows + r]. Grid and thread
+// mapping as muon_pack_kernel (up to four 32x32 tiles of X per workgroup,
+// one float4 of each per thread, loads issued together).
 __global__ void muon_update_kernel(const MuonGroup g, const float* __restrict__ x32,
                                    float* __restrict__ params, uint16_t* __restrict__ pbf, float lr,
                                    const float* __restrict__ row_scale) {
-  __shared__ float tile[32][33];
+  __shared__ float tile[4][32][33];
   const int j = blockIdx.z;
   const long off = muon_mat_offset(g, j);
   const int k = j % g.per_layer;
@@ -650,37 +683,54 @@ __global__ void muon_update_kernel(const MuonGroup g, const float* __restrict__ 
   const long xoff = (long)j * xr * xc;
   const int q = threadIdx.x & 7;
   const int ry = threadIdx.x >> 3;
-  const long r0 = blockIdx.y * 32L, c0 = blockIdx.x * 32L;  // X tile origin
+  const long r0 = blockIdx.y * 32L, c0 = blockIdx.x * 128L;  // X block origin
+  const int nsub = (int)min(4L, (xc - c0) / 32);               // workgroup-uniform
   const float* rsc = row_scale ? row_scale + (long)j * xr + r0 : nullptr;
   float* w = params + off;
   uint16_t* wb = pbf + off;
-  long widx;
-  float u[4];  // X values for the four stored elements widx .. widx+3
-  if (!tr) {
-    widx = (r0 + ry) * xc + c0 + 4 * q;
-    const float4 xv = *reinterpret_cast<const float4*>(x32 + xoff + widx);
-    const float sr = rsc ? rsc[ry] : 1.f;
-    u[0] = sr * xv.x; u[1] = sr * xv.y; u[2] = sr * xv.z; u[3] = sr * xv.w;
-  } else {
-    // X tile rows r0 + ry, columns c0 + 4q .. +3, into LDS; the stored
-    // matrix W[c][r] is then written along r: stored row c0 + ry, X rows
-    // r0 + 4q .. +3.
-    const float4 xv = *reinterpret_cast<const float4*>(x32 + xoff + (r0 + ry) * xc + c0 + 4 * q);
-    const float sr = rsc ? rsc[ry] : 1.f;
-    tile[ry][4 * q] = sr * xv.x; tile[ry][4 * q + 1] = sr * xv.y;
-    tile[ry][4 * q + 2] = sr * xv.z; tile[ry][4 * q + 3] = sr * xv.w;
-    __syncthreads();
-    widx = (c0 + ry) * xr + r0 + 4 * q;
+  long widx[4];
+  float4 xv[4], wv[4];
+  // X tile t: rows r0 + ry, columns c0 + 32 t + 4q .. +3.
 #pragma unroll
-    for (int e = 0; e < 4; ++e) u[e] = tile[4 * q + e][ry];
+  for (int t = 0; t < 4; ++t) {
+    widx[t] = tr ? (c0 + 32 * t + ry) * xr + r0 + 4 * q : (r0 + ry) * xc + c0 + 32 * t + 4 * q;
+    if (t < nsub) {
+      xv[t] = *reinterpret_cast<const float4*>(x32 + xoff + (r0 + ry) * xc + c0 + 32 * t + 4 * q);
+      wv[t] = *reinterpret_cast<const float4*>(w + widx[t]);
+    }
   }
-  float4 wv = *reinterpret_cast<const float4*>(w + widx);
-  wv.x -= scale * u[0];
-  wv.y -= scale * u[1];
-  wv.z -= scale * u[2];
-  wv.w -= scale * u[3];
-  *reinterpret_cast<float4*>(w + widx) = wv;
-  *reinterpret_cast<uint2*>(wb + widx) = make_uint2(pack_bf2(wv.x, wv.y), pack_bf2(wv.z, wv.w));
+  const float sr = rsc ? rsc[ry] : 1.f;
+  if (tr) {
+    // The stored matrix W[c][r] is written along r: stored row c0 + 32 t +
+    // ry, X rows r0 + 4q .. +3, through the LDS tile.
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if (t < nsub) {
+        tile[t][ry][4 * q] = sr * xv[t].x;
+        tile[t][ry][4 * q + 1] = sr * xv[t].y;
+        tile[t][ry][4 * q + 2] = sr * xv[t].z;
+        tile[t][ry][4 * q + 3] = sr * xv[t].w;
+      }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    if (t < nsub) {
+      float u[4];  // X values for the four stored elements widx .. widx+3
+      if (!tr) {
+        u[0] = sr * xv[t].x; u[1] = sr * xv[t].y; u[2] = sr * xv[t].z; u[3] = sr * xv[t].w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[e] = tile[t][4 * q + e][ry];
+      }
+      float4 nv = wv[t];
+      nv.x -= scale * u[0];
+      nv.y -= scale * u[1];
+      nv.z -= scale * u[2];
+      nv.w -= scale * u[3];
+      *reinterpret_cast<float4*>(w + widx[t]) = nv;
+      *reinterpret_cast<uint2*>(wb + widx[t]) = make_uint2(pack_bf2(nv.x, nv.y), pack_bf2(nv.z, nv.w));
+    }
 }
 
 // NorMuon ([CT50] "2. Otimizador Muon", variance reduction after the
@@ -1299,14 +1349,14 @@ hipError_t launch_muon_momentum(const MuonGroup& g, const float* grads, float* m
 
 hipError_t launch_muon_pack(const MuonGroup& g, const float* mom, const float* partials,
                             int blocks_per_mat, float* x32, uint16_t* xb, hipStream_t s) {
-  dim3 grid((unsigned)(g.x_cols / 32), (unsigned)(g.x_rows / 32), g.count);
+  dim3 grid((unsigned)((g.x_cols + 127) / 128), (unsigned)(g.x_rows / 32), g.count);
   hipLaunchKernelGGL(muon_pack_kernel, grid, dim3(256), 0, s, g, mom, partials, blocks_per_mat, x32, xb);
   return hipGetLastError();
 }
 
 hipError_t launch_muon_update(const MuonGroup& g, const float* x32, float* params,
                               uint16_t* params_bf16, float lr, hipStream_t s) {
-  dim3 grid((unsigned)(g.x_cols / 32), (unsigned)(g.x_rows / 32), g.count);
+  dim3 grid((unsigned)((g.x_cols + 127) / 128), (unsigned)(g.x_rows / 32), g.count);
   hipLaunchKernelGGL(muon_update_kernel, grid, dim3(256), 0, s, g, x32, params, params_bf16, lr,
                      static_cast<const float*>(nullptr));
   return hipGetLastError();
@@ -1325,7 +1375,7 @@ hipError_t launch_normuon(const MuonGroup& g, const float* x32, float* state, fl
 
 hipError_t launch_muon_update_scaled(const MuonGroup& g, const float* x32, float* params,
                                      uint16_t* params_bf16, float lr, const float* row_scale, hipStream_t s) {
-  dim3 grid((unsigned)(g.x_cols / 32), (unsigned)(g.x_rows / 32), g.count);
+  dim3 grid((unsigned)((g.x_cols + 127) / 128), (unsigned)(g.x_rows / 32), g.count);
   hipLaunchKernelGGL(muon_update_kernel, grid, dim3(256), 0, s, g, x32, params, params_bf16, lr, row_scale);
   return hipGetLastError();
 }
