@@ -177,21 +177,36 @@ __global__ void __launch_bounds__(SC_G) scatter_runs_kernel(Src src, const int32
     nruns[g] = runs;
   }
   __syncthreads();
-  // Each wave sums runs wave, wave + 4, ...; a run's rows in position order.
-  for (int r = wave; r < runs; r += SC_G / 64) {
+  // Work items are (run, 64-float4 column chunk) pairs, dealt round-robin to
+  // the waves, so a long run (the most frequent id) spreads over all of them.
+  // A run's rows are added in position order, four loads in flight.
+  const int nch = (W4 + 63) / 64;
+  for (int item = wave; item < runs * nch; item += SC_G / 64) {
+    const int r = item / nch;
+    const int c4 = (item - r * nch) * 64 + lane;
+    if (c4 >= W4) continue;
     const int s0 = run_start[r], s1 = run_start[r + 1];
     float4* dst = reinterpret_cast<float4*>(part + (base + r) * (long)(4 * W4));
-    for (int c4 = lane; c4 < W4; c4 += 64) {
-      float4 acc = src.load(base + (key[s0] & 0xffu), c4);
-      for (int j = s0 + 1; j < s1; ++j) {
-        const float4 v = src.load(base + (key[j] & 0xffu), c4);
-        acc.x += v.x;
-        acc.y += v.y;
-        acc.z += v.z;
-        acc.w += v.w;
-      }
-      dst[c4] = acc;
+    auto add = [](float4& acc, const float4 v) {
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    };
+    float4 acc = src.load(base + (key[s0] & 0xffu), c4);
+    int j = s0 + 1;
+    for (; j + 3 < s1; j += 4) {
+      const float4 v0 = src.load(base + (key[j] & 0xffu), c4);
+      const float4 v1 = src.load(base + (key[j + 1] & 0xffu), c4);
+      const float4 v2 = src.load(base + (key[j + 2] & 0xffu), c4);
+      const float4 v3 = src.load(base + (key[j + 3] & 0xffu), c4);
+      add(acc, v0);
+      add(acc, v1);
+      add(acc, v2);
+      add(acc, v3);
     }
+    for (; j < s1; ++j) add(acc, src.load(base + (key[j] & 0xffu), c4));
+    dst[c4] = acc;
   }
 }
 
