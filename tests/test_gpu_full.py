@@ -53,7 +53,7 @@ SCALAR_EPS = {"resid_lambdas": 2e-4, "x0_lambdas": 2e-4, "backout_lambda": 2e-4,
               "smear_gate": 1e-3}
 VE_GATE_EPS = 1e-3
 ORACLE_SEQ = {"d12": 2048, "d20": 2048, "d26": 2048, "d32": 4096}
-MUON_LAYERS = {"d12": "first_last", "d20": "first_last", "d26": "first", "d32": "first"}
+MUON_LAYERS = {"d12": "first_last", "d20": "first_last", "d26": "first_last", "d32": "first_last"}
 NAMES = ("wq", "wk", "wv", "wo", "wfc", "wproj")
 
 
