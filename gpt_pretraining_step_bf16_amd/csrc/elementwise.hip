@@ -542,16 +542,27 @@ __global__ void __launch_bounds__(256) ce_softmax_kernel(uint16_t* __restrict__ 
 }
 
 // loss = sum(loss_rows) / n_valid, one workgroup, fixed order.
-__global__ void loss_reduce_kernel(const float* __restrict__ rows, long N, const int* n_valid,
-                                   float* loss) {
-  __shared__ float red[4];
+__global__ void __launch_bounds__(1024) loss_reduce_kernel(const float* __restrict__ rows, long N,
+                                                          const int* n_valid, float* loss) {
+  __shared__ float red[16];
+  // rows is 256-byte aligned (a workspace region): float4 loads, then the tail.
+  const long n4 = N / 4;
+  const float4* r4 = reinterpret_cast<const float4*>(rows);
   float s = 0.f;
-  for (long i = threadIdx.x; i < N; i += blockDim.x) s += rows[i];
+  for (long i = threadIdx.x; i < n4; i += blockDim.x) {
+    const float4 v = r4[i];
+    s += v.x;
+    s += v.y;
+    s += v.z;
+    s += v.w;
+  }
+  for (long i = 4 * n4 + threadIdx.x; i < N; i += blockDim.x) s += rows[i];
   s = warp_sum(s);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
   __syncthreads();
   if (threadIdx.x == 0) {
-    const float tot = red[0] + red[1] + red[2] + red[3];
+    float tot = 0.f;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) tot += red[w];
     const int nv = *n_valid;
     *loss = nv > 0 ? tot / (float)nv : 0.f;
   }
@@ -1351,7 +1362,7 @@ hipError_t launch_ce_softmax(uint16_t* logits, const int32_t* tgt, float* loss_r
 
 hipError_t launch_loss_reduce(const float* loss_rows, long N, const int* n_valid, float* loss,
                               hipStream_t s) {
-  hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(256), 0, s, loss_rows, N, n_valid, loss);
+  hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(1024), 0, s, loss_rows, N, n_valid, loss);
   return hipGetLastError();
 }
 
