@@ -506,13 +506,16 @@ __global__ void __launch_bounds__(256) ce_softmax_kernel(uint16_t* __restrict__ 
     s = s * exp2f((m - nm) * GPT_LOG2E) + acc;
     m = nm;
   }
-  // Combine (m, s) across the wave, then across the 4 waves.
+  // Combine (m, s) across the wave, then across the 4 waves. A thread with
+  // no chunk (V < 2048) holds (-inf, 0): it adds nothing (exp2 of -inf minus
+  // -inf would be NaN).
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float om = __shfl_xor(m, o, 64);
     const float os = __shfl_xor(s, o, 64);
     const float nm = fmaxf(m, om);
-    s = s * exp2f((m - nm) * GPT_LOG2E) + os * exp2f((om - nm) * GPT_LOG2E);
+    s = (m == -INFINITY ? 0.f : s * exp2f((m - nm) * GPT_LOG2E)) +
+        (om == -INFINITY ? 0.f : os * exp2f((om - nm) * GPT_LOG2E));
     m = nm;
   }
   if (lane == 0) {
@@ -522,7 +525,8 @@ __global__ void __launch_bounds__(256) ce_softmax_kernel(uint16_t* __restrict__ 
   __syncthreads();
   float M = red[0][0], S = 0.f;
   for (int w = 1; w < 4; ++w) M = fmaxf(M, red[0][w]);
-  for (int w = 0; w < 4; ++w) S += red[1][w] * exp2f((red[0][w] - M) * GPT_LOG2E);
+  for (int w = 0; w < 4; ++w)
+    if (red[0][w] != -INFINITY) S += red[1][w] * exp2f((red[0][w] - M) * GPT_LOG2E);
   const float lse = M + logf(S);
   const int nv = *n_valid;
   const float scale = (valid && nv > 0) ? 1.f / (float)nv : 0.f;

@@ -103,6 +103,17 @@ def test_tiny_fwd_bwd_matches_oracle():
     _assert_grads(grads, ref_grads, tok, cfg["vocab"])
 
 
+@pytest.mark.parametrize("vocab", [64, 512, 1984])
+def test_small_vocab_fwd_bwd_matches_oracle(vocab):
+    """Vocabularies narrower than the cross-entropy workgroup's 256 threads x 8
+    logits (V < 2048): threads that hold no part of the row must add nothing
+    to its max and sum (the loss was NaN before that was handled)."""
+    st, tok, tgt, loss, grads, ref_loss, ref_grads = _run_case(2, vocab, 64, 2)
+    log(f"  V={vocab} loss gpu={loss:.6f} oracle={ref_loss:.6f}")
+    assert abs(loss - ref_loss) <= LOSS_TOL
+    _assert_grads(grads, ref_grads, tok, vocab)
+
+
 @pytest.mark.parametrize("windows", [[0, 20], [63, -1], [7, 1]])
 def test_windowed_fwd_bwd_matches_oracle(windows):
     """Per-layer attention windows: the degenerate window 0 (each token sees
