@@ -103,6 +103,18 @@ def test_tiny_fwd_bwd_matches_oracle():
     _assert_grads(grads, ref_grads, tok, cfg["vocab"])
 
 
+@pytest.mark.parametrize("depth,vocab,seq,batch", [(1, 128, 37, 3), (3, 320, 100, 2), (5, 192, 130, 1),
+                                                   (2, 2048, 1, 5)])
+def test_unusual_shapes_fwd_bwd_matches_oracle(depth, vocab, seq, batch):
+    """Shapes the boundary accepts beyond the workloads': depth 1, 3 and 5
+    (width 128, 256 and 384: one, two and three heads), token counts that are
+    not multiples of 4 or of a 256-row tile, one-token sequences."""
+    st, tok, tgt, loss, grads, ref_loss, ref_grads = _run_case(depth, vocab, seq, batch)
+    log(f"  loss gpu={loss:.6f} oracle={ref_loss:.6f}")
+    assert abs(loss - ref_loss) <= LOSS_TOL
+    _assert_grads(grads, ref_grads, tok, vocab)
+
+
 @pytest.mark.parametrize("vocab", [64, 512, 1984])
 def test_small_vocab_fwd_bwd_matches_oracle(vocab):
     """Vocabularies narrower than the cross-entropy workgroup's 256 threads x 8
