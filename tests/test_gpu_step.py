@@ -205,10 +205,6 @@ def test_gqa_muon_matches_oracle(normuon):
 
 
 # Error allowance of the scalar and gate gradients, as a fraction of their
-# Cauchy-Schwarz scale S (gpu_util.assert_scalar_grads): a few times the
-# largest |delta|/S measured on the device for these cases (scalars 5e-5 S,
-# the smear gate, last in the backward chain, 2.6e-4 S).
-# Error allowance of the scalar and gate gradients, as a fraction of their
 # Cauchy-Schwarz scale S (gpu_util.assert_scalar_grads): about 2.5 times the
 # largest |delta|/S measured on the device over these cases (scalars 2.1e-4 S,
 # in the 12-token case; the smear gate, last in the backward chain, 8.1e-4 S).
@@ -256,6 +252,25 @@ def test_scalars_fwd_bwd_matches_oracle(depth, vocab, seq, batch, resid, backout
     for k in scalars:
         if k in grads:
             np.testing.assert_allclose(g2[k], 2 * grads[k], rtol=1e-5, atol=1e-9)
+
+
+def test_all_options_together_match_oracle():
+    """Every optional feature in one model: grouped-query attention with one
+    key/value head for three query heads, a mix of windows, value embeddings,
+    residual scalars with backout and smear, at width 384, 100 tokens and a
+    512-token vocabulary."""
+    ve = (0, 3)
+    st, tok, tgt, loss, grads, ref_loss, ref_grads = _run_case(5, 512, 100, 2, seed_w=2, seed_t=3,
+                                                                windows=[-1, 30, -1, 7, 60], kv_heads=1,
+                                                                resid_scalars=True, backout_layer=2, smear=True,
+                                                                ve_layers=ve)
+    log(f"  loss gpu={loss:.6f} oracle={ref_loss:.6f}")
+    assert abs(loss - ref_loss) <= LOSS_TOL
+    scalars = ("resid_lambdas", "x0_lambdas", "backout_lambda", "smear_gate", "smear_lambda")
+    gates = tuple(f"h{l}.ve_gate" for l in ve)
+    _assert_grads(grads, ref_grads, tok, 512, skip=scalars + gates)
+    assert_scalar_grads(grads, ref_grads, {k: _run_case.scales[k] for k in scalars}, log, eps=SCALAR_EPS)
+    assert_scalar_grads(grads, ref_grads, {k: _run_case.scales[k] for k in gates}, log, eps=VE_GATE_EPS)
 
 
 @pytest.mark.parametrize("depth,kv_heads,seq,batch,ve_layers,windows", [
