@@ -152,11 +152,14 @@ def test_gqa_fwd_bwd_matches_oracle(depth, kv_heads, seq, batch, windows):
     _assert_grads(grads, ref_grads, tok, 2048)
 
 
+@pytest.mark.parametrize("depth", [8, 5])
 @pytest.mark.parametrize("normuon", [False, True])
-def test_gqa_muon_matches_oracle(normuon):
-    """Muon / NorMuon on a grouped-query model: wk and wv ([128, 512], wide)
-    form their own Newton-Schulz batch, apart from wq and wo."""
-    depth, vocab, kvh = 8, 2048, 1
+def test_gqa_muon_matches_oracle(normuon, depth):
+    """Muon / NorMuon on a grouped-query model: wk and wv ([128, d], wide)
+    form their own Newton-Schulz batch, apart from wq and wo. Depth 5 gives
+    width 384: 384 x 384, 384 x 128 and 1536 x 384 iterations, none a whole
+    number of 256 x 256 tiles."""
+    vocab, kvh = 2048, 1
     log(f"gqa {'normuon' if normuon else 'muon'} depth={depth} kv_heads={kvh}")
     w = syn.init_weights(depth, vocab, seed=0, kv_heads=kvh)
     g = syn.random_like_grads(depth, vocab, seed=7, scale=1e-2, kv_heads=kvh)
