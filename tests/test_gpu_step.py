@@ -104,13 +104,15 @@ def test_tiny_fwd_bwd_matches_oracle():
 
 
 @pytest.mark.parametrize("depth,vocab,seq,batch", [(1, 128, 37, 3), (3, 320, 100, 2), (5, 192, 130, 1),
-                                                   (2, 2048, 1, 5), (2, 65536, 64, 2), (1, 262144, 33, 2)])
+                                                   (2, 2048, 1, 5), (2, 65536, 64, 2), (1, 262144, 33, 2),
+                                                   (1, 2048, 16384, 1)])
 def test_unusual_shapes_fwd_bwd_matches_oracle(depth, vocab, seq, batch):
     """Shapes the boundary accepts beyond the workloads': depth 1, 3 and 5
     (width 128, 256 and 384: one, two and three heads), token counts that are
     not multiples of 4 or of a 256-row tile, one-token sequences, and the
     largest vocabularies (65536 and the 262144 maximum: wider cross-entropy
-    rows, head chunks of 8192 and 2048 tokens)."""
+    rows, head chunks of 8192 and 2048 tokens) and the longest sequence
+    (16384 positions: attention, the RoPE table and its rotation recurrence)."""
     st, tok, tgt, loss, grads, ref_loss, ref_grads = _run_case(depth, vocab, seq, batch)
     log(f"  loss gpu={loss:.6f} oracle={ref_loss:.6f}")
     assert abs(loss - ref_loss) <= LOSS_TOL
