@@ -119,6 +119,16 @@ def test_unusual_shapes_fwd_bwd_matches_oracle(depth, vocab, seq, batch):
     _assert_grads(grads, ref_grads, tok, vocab)
 
 
+@pytest.mark.timeout(900)
+def test_maximum_token_count_matches_oracle():
+    """The most tokens one call accepts (batch * seq = 524288: 2048 groups of
+    256 positions in the embedding scatter, two head chunks), at depth 1."""
+    st, tok, tgt, loss, grads, ref_loss, ref_grads = _run_case(1, 2048, 2048, 256)
+    log(f"  loss gpu={loss:.6f} oracle={ref_loss:.6f}")
+    assert abs(loss - ref_loss) <= LOSS_TOL
+    _assert_grads(grads, ref_grads, tok, 2048)
+
+
 @pytest.mark.parametrize("vocab", [64, 512, 1984])
 def test_small_vocab_fwd_bwd_matches_oracle(vocab):
     """Vocabularies narrower than the cross-entropy workgroup's 256 threads x 8
