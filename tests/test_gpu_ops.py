@@ -310,10 +310,15 @@ def test_attention_bwd_through_qk_norm_and_rope(B, T, H, W, HKV):
 # fp32 accumulation, X kept in fp16 between iterations; a CPU emulation of
 # those roundings puts Gaussian inputs at 3.0e-3 (256 x 256), 5.8e-3
 # (384 x 128) and 1.3e-3 (1280 x 1280) from the fp64 iteration.
-NS_BAR = {(384, 128): 2e-2, (256, 256): 2e-2, (1280, 1280): 5e-3}
+NS_BAR = {(384, 128): 2e-2, (256, 256): 2e-2, (1280, 1280): 5e-3, (40, 24): 2e-2, (72, 72): 2e-2,
+          (200, 56): 2e-2, (96, 96): 2e-2, (136, 136): 2e-2}
 
 
-@pytest.mark.parametrize("count,rows,cols", [(3, 384, 128), (2, 256, 256), (1, 1280, 1280)])
+# The last five shapes are multiples of 8 but not of 128 (the op's contract):
+# single partial tiles, K not a multiple of 32 (the single-group kernel with
+# its zeroed partial k-block) and symmetric products over ragged tiles.
+@pytest.mark.parametrize("count,rows,cols", [(3, 384, 128), (2, 256, 256), (1, 1280, 1280), (2, 40, 24),
+                                             (1, 72, 72), (2, 200, 56), (1, 96, 96), (1, 136, 136)])
 def test_newton_schulz(count, rows, cols):
     log(f"newton-schulz count={count} rows={rows} cols={cols}")
     rng = np.random.default_rng(rows + cols)
