@@ -50,6 +50,28 @@ def test_gemm_layouts_fp32_out(a_kmajor, b_kmajor, K):
     assert err < 2e-6, err
 
 
+# The smallest shapes the contract allows (multiples of 8 along the
+# K-contiguous dimensions, N a multiple of 4): a single partial tile, K below
+# one k-block or off the 32 grid (single-group kernel) or on it (ping-pong).
+@pytest.mark.parametrize("M,N,K", [(8, 8, 8), (24, 16, 40), (40, 8, 1000), (8, 8, 64)])
+@pytest.mark.parametrize("a_kmajor,b_kmajor", [(1, 1), (1, 0), (0, 1), (0, 0)])
+def test_gemm_tiny_shapes(a_kmajor, b_kmajor, M, N, K):
+    batch = 3
+    rng = np.random.default_rng(M + N + K + 2 * a_kmajor + b_kmajor)
+    Ab, Af = _rand_bf16(rng, (batch, M, K))
+    Bb, Bf = _rand_bf16(rng, (batch, N, K))
+    A_store = Ab if a_kmajor else np.ascontiguousarray(Ab.transpose(0, 2, 1))
+    B_store = Bb if b_kmajor else np.ascontiguousarray(Bb.transpose(0, 2, 1))
+    C = torch.zeros(batch, M, N, dtype=torch.float32, device="cuda")
+    binding.op_gemm(M, N, K, dev(torch, A_store), K if a_kmajor else M, a_kmajor, dev(torch, B_store),
+                    K if b_kmajor else N, b_kmajor, C, N, binding.OUT_F32, batch=batch, stride_a=M * K,
+                    stride_b=N * K, stride_c=M * N)
+    torch.cuda.synchronize()
+    ref = np.matmul(Af, Bf.transpose(0, 2, 1))
+    err = np.abs(C.cpu().numpy() - ref).max() / np.abs(ref).max()
+    assert err < 2e-6, err
+
+
 # bf16 outputs go through the LDS-staged epilogue (interior tiles, and edge
 # tiles with a column count that is a multiple of 8 or only of 4), in a
 # persistent launch that walks several tiles per workgroup.
